@@ -1,0 +1,178 @@
+"""Seeded synthetic inputs for the AWQ int4 MoE expert stage.
+
+This module only draws random numbers. It holds none of the stage's
+arithmetic (no dequantisation, no packing, no routing, no products), so both
+the CPU oracle and the GPU path can take their inputs from it.
+
+Shapes follow the layer share described on the pages (PR #520 "Narrow
+Qwen3.8 AWQ active grouped decode", Purpose: 512 experts, top-k 10, hidden
+2560, local intermediate 160, group 32). The pages measured on real layer-1
+AWQ weights that are not available; the draws below stand in for them:
+
+* packed values q ~ U{0..15}
+* scales s = fp16(|N(0,1)| * 0.02)
+* zeros z ~ U{0..15} (stored as u8)
+* activations x = fp16(N(0,1))
+* router weights = fp32 softmax of N(0,1) logits over the k selected experts
+
+Every expert draws from its own stream, ``PCG64(SeedSequence([seed, e]))``,
+in the fixed order q_gate, q_up, q_down, s_gate, s_up, s_down, z_gate, z_up,
+z_down, so one expert can be regenerated without drawing the others.
+"""
+
+from __future__ import annotations
+
+import math
+from dataclasses import dataclass
+
+import numpy as np
+
+GROUP = 32
+
+# Layer shapes used by tests and the benchmark.
+RANK_SHAPE = dict(num_experts=512, topk=10, hidden=2560, inter=160)
+TINY_SHAPE = dict(num_experts=16, topk=2, hidden=256, inter=32)
+
+
+@dataclass
+class ExpertWeights:
+    """Logical (unpacked) AWQ weights of one expert.
+
+    Orientation is y = x @ W, i.e. W is [K][N]:
+      q_gate, q_up : uint8 [hidden][inter]   values 0..15
+      q_down       : uint8 [inter][hidden]   values 0..15
+      s_*          : float16 [K/32][N]       group scales (group along K)
+      z_*          : uint8  [K/32][N]        group zeros
+    """
+
+    q_gate: np.ndarray
+    q_up: np.ndarray
+    q_down: np.ndarray
+    s_gate: np.ndarray
+    s_up: np.ndarray
+    s_down: np.ndarray
+    z_gate: np.ndarray
+    z_up: np.ndarray
+    z_down: np.ndarray
+
+
+def _expert_rng(seed: int, e: int) -> np.random.Generator:
+    return np.random.Generator(np.random.PCG64(np.random.SeedSequence([int(seed), int(e)])))
+
+
+def expert_weights(seed: int, e: int, hidden: int, inter: int,
+                   scale_std: float = 0.02, zero_hi: int = 16) -> ExpertWeights:
+    """Draw the logical weights of expert ``e`` from its own seeded stream."""
+    rng = _expert_rng(seed, e)
+    H, I = hidden, inter
+    q_gate = rng.integers(0, 16, size=(H, I), dtype=np.uint8)
+    q_up = rng.integers(0, 16, size=(H, I), dtype=np.uint8)
+    q_down = rng.integers(0, 16, size=(I, H), dtype=np.uint8)
+    s_gate = (np.abs(rng.standard_normal((H // GROUP, I))) * scale_std).astype(np.float16)
+    s_up = (np.abs(rng.standard_normal((H // GROUP, I))) * scale_std).astype(np.float16)
+    s_down = (np.abs(rng.standard_normal((I // GROUP, H))) * scale_std).astype(np.float16)
+    z_gate = rng.integers(0, zero_hi, size=(H // GROUP, I), dtype=np.uint8)
+    z_up = rng.integers(0, zero_hi, size=(H // GROUP, I), dtype=np.uint8)
+    z_down = rng.integers(0, zero_hi, size=(I // GROUP, H), dtype=np.uint8)
+    return ExpertWeights(q_gate, q_up, q_down, s_gate, s_up, s_down, z_gate, z_up, z_down)
+
+
+@dataclass
+class BankInputs:
+    """Stacked logical weights of all experts of one layer (leading axis E)."""
+
+    q_gate: np.ndarray
+    q_up: np.ndarray
+    q_down: np.ndarray
+    s_gate: np.ndarray
+    s_up: np.ndarray
+    s_down: np.ndarray
+    z_gate: np.ndarray
+    z_up: np.ndarray
+    z_down: np.ndarray
+
+    def expert(self, e: int) -> ExpertWeights:
+        return ExpertWeights(*(getattr(self, f)[e] for f in _FIELDS))
+
+
+_FIELDS = ("q_gate", "q_up", "q_down", "s_gate", "s_up", "s_down", "z_gate", "z_up", "z_down")
+
+
+def bank_inputs(seed: int, num_experts: int, hidden: int, inter: int, **kw) -> BankInputs:
+    """Draw all experts of one layer (expert e from stream [seed, e])."""
+    E, H, I = num_experts, hidden, inter
+    out = {
+        "q_gate": np.empty((E, H, I), np.uint8), "q_up": np.empty((E, H, I), np.uint8),
+        "q_down": np.empty((E, I, H), np.uint8),
+        "s_gate": np.empty((E, H // GROUP, I), np.float16), "s_up": np.empty((E, H // GROUP, I), np.float16),
+        "s_down": np.empty((E, I // GROUP, H), np.float16),
+        "z_gate": np.empty((E, H // GROUP, I), np.uint8), "z_up": np.empty((E, H // GROUP, I), np.uint8),
+        "z_down": np.empty((E, I // GROUP, H), np.uint8),
+    }
+    for e in range(E):
+        w = expert_weights(seed, e, H, I, **kw)
+        for f in _FIELDS:
+            out[f][e] = getattr(w, f)
+    return BankInputs(**out)
+
+
+def activations(rng: np.random.Generator, M: int, hidden: int) -> np.ndarray:
+    """x = fp16(N(0,1)), shape [M][hidden]."""
+    return rng.standard_normal((M, hidden)).astype(np.float16)
+
+
+def router_weights(rng: np.random.Generator, M: int, k: int) -> np.ndarray:
+    """fp32 softmax of N(0,1) logits over the k selected experts, [M][k].
+
+    This only shapes the synthetic input distribution; the stage itself uses
+    the weights exactly as given.
+    """
+    logits = rng.standard_normal((M, k))
+    logits -= logits.max(axis=1, keepdims=True)
+    p = np.exp(logits)
+    p /= p.sum(axis=1, keepdims=True)
+    return p.astype(np.float32)
+
+
+def ids_distinct(rng: np.random.Generator, M: int, k: int, E: int) -> np.ndarray:
+    """Each token picks k distinct experts uniformly; tokens are independent."""
+    return np.stack([rng.choice(E, size=k, replace=False) for _ in range(M)]).astype(np.int32)
+
+
+def ids_shared_pool(rng: np.random.Generator, M: int, k: int, E: int, frac: float = 0.6) -> np.ndarray:
+    """Tokens draw k distinct experts from a common pool of ceil(frac*M*k).
+
+    This gives multi-row segments (experts shared by several tokens), the
+    grouped-decode case of PR #520 (Purpose: multi-row active-expert segments).
+    """
+    pool_n = max(k, min(E, int(math.ceil(frac * M * k))))
+    pool = rng.choice(E, size=pool_n, replace=False)
+    return np.stack([rng.choice(pool, size=k, replace=False) for _ in range(M)]).astype(np.int32)
+
+
+def ids_all_distinct(rng: np.random.Generator, M: int, k: int, E: int) -> np.ndarray:
+    """All M*k slots pick different experts (upper bound on touched bytes)."""
+    return rng.choice(E, size=M * k, replace=False).reshape(M, k).astype(np.int32)
+
+
+def hot_experts(seed: int, k: int, E: int) -> np.ndarray:
+    """The fixed set of k experts reused by every call of the hot workload."""
+    rng = np.random.Generator(np.random.PCG64(np.random.SeedSequence([int(seed), 0xA0])))
+    return rng.choice(E, size=k, replace=False).astype(np.int32)
+
+
+def rotating_ids(seed: int, calls: int, k: int, E: int) -> np.ndarray:
+    """Call c uses experts perm[c*k:(c+1)*k] of one seeded permutation, [calls][1][k]."""
+    rng = np.random.Generator(np.random.PCG64(np.random.SeedSequence([int(seed), 0xB0])))
+    perm = rng.permutation(E)
+    assert calls * k <= E
+    return perm[: calls * k].reshape(calls, 1, k).astype(np.int32)
+
+
+def router_logits(rng: np.random.Generator, M: int, E: int) -> np.ndarray:
+    """fp32 router logits ~ N(0,1), [M][E]."""
+    return rng.standard_normal((M, E)).astype(np.float32)
+
+
+def call_rng(seed: int, tag: int) -> np.random.Generator:
+    return np.random.Generator(np.random.PCG64(np.random.SeedSequence([int(seed), 0xC0, int(tag)])))
