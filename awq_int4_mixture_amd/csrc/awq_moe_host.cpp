@@ -1,0 +1,369 @@
+// Host side of the C ABI declared in include/awq_moe.h: argument checks
+// (fail closed before any write or launch), the bank packer, layout and
+// workspace queries, and the kernel launch sequence of the decode stage.
+
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+
+#include "../../include/awq_moe.h"
+#include "kernels.h"
+
+namespace {
+
+thread_local std::string g_err;
+
+int fail(int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return code;
+}
+
+int ok() {
+  g_err.clear();
+  return AWQ_MOE_OK;
+}
+
+uint64_t pad256(uint64_t n) { return (n + 255u) / 256u * 256u; }
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+int check_dims(const awq_moe_dims* d) {
+  if (!d) return fail(AWQ_MOE_EINVAL, "dims is null");
+  if (d->group_size != 32) return fail(AWQ_MOE_EUNSUPPORTED, "group_size %d: only 32 is served", d->group_size);
+  if (d->meta_bytes != 3 && d->meta_bytes != 4)
+    return fail(AWQ_MOE_EUNSUPPORTED, "meta_bytes %d: only 3 or 4", d->meta_bytes);
+  if (d->num_experts < 1) return fail(AWQ_MOE_EINVAL, "num_experts %d < 1", d->num_experts);
+  if (d->hidden < 32 || d->hidden % 32 || d->hidden > AWQ_MOE_MAX_HIDDEN)
+    return fail(AWQ_MOE_EUNSUPPORTED, "hidden %d: must be a multiple of 32 in [32, %d]", d->hidden,
+                AWQ_MOE_MAX_HIDDEN);
+  if (d->inter < 32 || d->inter % 32 || d->inter > AWQ_MOE_MAX_INTER)
+    return fail(AWQ_MOE_EUNSUPPORTED, "inter %d: must be a multiple of 32 in [32, %d]", d->inter, AWQ_MOE_MAX_INTER);
+  return AWQ_MOE_OK;
+}
+
+struct Layout {
+  uint64_t w13_units, w13_meta, w2_units, w2_meta;
+  awq_moe_bank_layout pub;
+};
+
+Layout make_layout(const awq_moe_dims* d) {
+  const uint64_t H = (uint64_t)d->hidden, I = (uint64_t)d->inter, RB = (uint64_t)d->meta_bytes;
+  Layout L;
+  L.w13_units = (H / 32) * (2 * I) * 16;
+  L.w13_meta = (H / 32) * (2 * I) * RB;
+  L.w2_units = (I / 32) * H * 16;
+  L.w2_meta = (I / 32) * H * RB;
+  L.pub.w13_off = 0;
+  L.pub.w13_meta_off = pad256(L.w13_units);
+  L.pub.w2_off = L.pub.w13_meta_off + pad256(L.w13_meta);
+  L.pub.w2_meta_off = L.pub.w2_off + pad256(L.w2_units);
+  L.pub.expert_bytes = L.pub.w2_meta_off + pad256(L.w2_meta);
+  L.pub.total_bytes = L.pub.expert_bytes * (uint64_t)d->num_experts;
+  return L;
+}
+
+// Workspace: [status u32 | num_active i32 | pad] then routing arrays, then act.
+struct WsLayout {
+  uint64_t ids_off, offsets_off, slots_off, act_off, total;
+};
+
+WsLayout make_ws(const awq_moe_dims* d, int max_tokens, int topk) {
+  const uint64_t n = (uint64_t)max_tokens * (uint64_t)topk;
+  WsLayout w;
+  w.ids_off = 256;
+  w.offsets_off = w.ids_off + pad256(n * 4);
+  w.slots_off = w.offsets_off + pad256((n + 1) * 4);
+  w.act_off = w.slots_off + pad256(n * 4);
+  w.total = w.act_off + pad256(n * (uint64_t)d->inter * 2);
+  return w;
+}
+
+int check_tokens(int M, int topk) {
+  if (M < 1 || M > AWQ_MOE_MAX_TOKENS) return fail(AWQ_MOE_EINVAL, "M %d outside [1, %d]", M, AWQ_MOE_MAX_TOKENS);
+  if (topk < 1 || topk > AWQ_MOE_MAX_TOPK) return fail(AWQ_MOE_EINVAL, "topk %d outside [1, %d]", topk, AWQ_MOE_MAX_TOPK);
+  return AWQ_MOE_OK;
+}
+
+// The kernels are built for gfx950 only; remember the answer per device.
+std::atomic<int> g_arch_state[64];  // 0 unknown, 1 gfx950, 2 other
+
+int check_device() {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(AWQ_MOE_EHIP, "hipGetDevice: %s", hipGetErrorString(e));
+  if (dev < 0 || dev >= 64) return fail(AWQ_MOE_EUNSUPPORTED, "device index %d", dev);
+  int st = g_arch_state[dev].load(std::memory_order_relaxed);
+  if (st == 0) {
+    hipDeviceProp_t prop;
+    e = hipGetDeviceProperties(&prop, dev);
+    if (e != hipSuccess) return fail(AWQ_MOE_EHIP, "hipGetDeviceProperties: %s", hipGetErrorString(e));
+    st = (std::strncmp(prop.gcnArchName, "gfx950", 6) == 0) ? 1 : 2;
+    g_arch_state[dev].store(st, std::memory_order_relaxed);
+    if (st == 2) return fail(AWQ_MOE_EUNSUPPORTED, "device %d is %s; kernels are built for gfx950", dev, prop.gcnArchName);
+  }
+  if (st == 2) return fail(AWQ_MOE_EUNSUPPORTED, "device %d is not gfx950", dev);
+  return AWQ_MOE_OK;
+}
+
+int hip_status(hipError_t e, const char* what) {
+  if (e != hipSuccess) return fail(AWQ_MOE_EHIP, "%s: %s", what, hipGetErrorString(e));
+  return ok();
+}
+
+awq_moe::StageArgs stage_args(const awq_moe_dims* d, const void* bank, int M, int topk,
+                              const int32_t* ids, const int32_t* offsets, const int32_t* slots,
+                              const int32_t* num_active) {
+  const Layout L = make_layout(d);
+  awq_moe::StageArgs a;
+  a.bank = static_cast<const uint8_t*>(bank);
+  a.expert_bytes = L.pub.expert_bytes;
+  a.w13_off = L.pub.w13_off;
+  a.w13_meta_off = L.pub.w13_meta_off;
+  a.w2_off = L.pub.w2_off;
+  a.w2_meta_off = L.pub.w2_meta_off;
+  a.H = d->hidden;
+  a.I = d->inter;
+  a.RB = d->meta_bytes;
+  a.M = M;
+  a.topk = topk;
+  a.active_ids = ids;
+  a.offsets = offsets;
+  a.sorted_slots = slots;
+  a.num_active = num_active;
+  return a;
+}
+
+int check_route_ptrs(const int32_t* ids, const int32_t* offsets, const int32_t* slots, const int32_t* na) {
+  if (!ids || !offsets || !slots || !na) return fail(AWQ_MOE_EINVAL, "routing array is null");
+  if (!aligned(ids, 4) || !aligned(offsets, 4) || !aligned(slots, 4) || !aligned(na, 4))
+    return fail(AWQ_MOE_EINVAL, "routing arrays must be 4-byte aligned");
+  return AWQ_MOE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* awq_moe_last_error(void) { return g_err.c_str(); }
+
+int awq_moe_bank_layout_query(const awq_moe_dims* dims, awq_moe_bank_layout* out) {
+  int rc = check_dims(dims);
+  if (rc) return rc;
+  if (!out) return fail(AWQ_MOE_EINVAL, "out is null");
+  *out = make_layout(dims).pub;
+  return ok();
+}
+
+int awq_moe_workspace_bytes(const awq_moe_dims* dims, int32_t max_tokens, int32_t topk, uint64_t* out) {
+  int rc = check_dims(dims);
+  if (rc) return rc;
+  if ((rc = check_tokens(max_tokens, topk))) return rc;
+  if (!out) return fail(AWQ_MOE_EINVAL, "out is null");
+  *out = make_ws(dims, max_tokens, topk).total;
+  return ok();
+}
+
+int awq_moe_prepare(const awq_moe_dims* dims, const uint8_t* q_gate, const uint8_t* q_up,
+                    const uint8_t* q_down, const uint16_t* s_gate, const uint16_t* s_up,
+                    const uint16_t* s_down, const uint8_t* z_gate, const uint8_t* z_up,
+                    const uint8_t* z_down, void* bank, uint64_t bank_bytes) {
+  int rc = check_dims(dims);
+  if (rc) return rc;
+  if (!q_gate || !q_up || !q_down || !s_gate || !s_up || !s_down || !z_gate || !z_up || !z_down || !bank)
+    return fail(AWQ_MOE_EINVAL, "null input or bank pointer");
+  const Layout L = make_layout(dims);
+  if (bank_bytes < L.pub.total_bytes)
+    return fail(AWQ_MOE_ENOSPC, "bank_bytes %llu < %llu", (unsigned long long)bank_bytes,
+                (unsigned long long)L.pub.total_bytes);
+  const uint64_t E = (uint64_t)dims->num_experts, H = (uint64_t)dims->hidden, I = (uint64_t)dims->inter;
+  const int RB = dims->meta_bytes;
+  // validate everything before writing anything
+  const uint64_t nq13 = E * H * I, nq2 = E * I * H;
+  for (uint64_t i = 0; i < nq13; ++i)
+    if (q_gate[i] > 15 || q_up[i] > 15) return fail(AWQ_MOE_EINVAL, "q_gate/q_up value > 15 at %llu", (unsigned long long)i);
+  for (uint64_t i = 0; i < nq2; ++i)
+    if (q_down[i] > 15) return fail(AWQ_MOE_EINVAL, "q_down value > 15 at %llu", (unsigned long long)i);
+  const uint64_t ns13 = E * (H / 32) * I, ns2 = E * (I / 32) * H;
+  auto finite = [](uint16_t b) { return (b & 0x7C00u) != 0x7C00u; };
+  for (uint64_t i = 0; i < ns13; ++i)
+    if (!finite(s_gate[i]) || !finite(s_up[i])) return fail(AWQ_MOE_EINVAL, "non-finite W13 scale at %llu", (unsigned long long)i);
+  for (uint64_t i = 0; i < ns2; ++i)
+    if (!finite(s_down[i])) return fail(AWQ_MOE_EINVAL, "non-finite W2 scale at %llu", (unsigned long long)i);
+
+  uint8_t* out = static_cast<uint8_t*>(bank);
+  std::memset(out, 0, L.pub.total_bytes);
+  const uint64_t G13 = H / 32, L13 = 4 * G13, G2 = I / 32, L2 = 2 * G2;
+
+  // Pack 32 values v(k), k = 0..31 into a 16-byte unit.
+  auto put_unit = [](uint8_t* dst, auto value_at) {
+    for (int d = 0; d < 4; ++d) {
+      uint32_t w = 0;
+      for (int p = 0; p < 8; ++p) w |= (uint32_t)value_at(8 * d + p) << (4 * (p >> 1) + 16 * (p & 1));
+      dst[4 * d + 0] = (uint8_t)(w);
+      dst[4 * d + 1] = (uint8_t)(w >> 8);
+      dst[4 * d + 2] = (uint8_t)(w >> 16);
+      dst[4 * d + 3] = (uint8_t)(w >> 24);
+    }
+  };
+  auto put_record = [RB](uint8_t* dst, uint16_t s, uint8_t z) {
+    dst[0] = (uint8_t)(s & 0xFF);
+    dst[1] = (uint8_t)(s >> 8);
+    dst[2] = z;
+    if (RB == 4) dst[3] = 0;
+  };
+
+  for (uint64_t e = 0; e < E; ++e) {
+    uint8_t* blk = out + e * L.pub.expert_bytes;
+    const uint8_t* qg = q_gate + e * H * I;
+    const uint8_t* qu = q_up + e * H * I;
+    const uint8_t* qd = q_down + e * I * H;
+    const uint16_t* sg = s_gate + e * G13 * I;
+    const uint16_t* su = s_up + e * G13 * I;
+    const uint16_t* sd = s_down + e * G2 * H;
+    const uint8_t* zg = z_gate + e * G13 * I;
+    const uint8_t* zu = z_up + e * G13 * I;
+    const uint8_t* zd = z_down + e * G2 * H;
+    // W13: column n = 2i (gate i) or 2i + 1 (up i)
+    for (uint64_t n = 0; n < 2 * I; ++n) {
+      const uint64_t i = n >> 1;
+      const bool up = n & 1;
+      const uint8_t* q = up ? qu : qg;
+      const uint64_t nt = n / 16, c = n % 16, quad = c / 4, j = c % 4;
+      for (uint64_t g = 0; g < G13; ++g) {
+        const uint64_t t = 4 * g + quad;
+        put_unit(blk + L.pub.w13_off + nt * 256 * G13 + (j * L13 + t) * 16,
+                 [&](int k) { return q[(32 * g + k) * I + i]; });
+        put_record(blk + L.pub.w13_meta_off + nt * 16 * G13 * RB + (4 * t + j) * RB,
+                   (up ? su : sg)[g * I + i], (up ? zu : zg)[g * I + i]);
+      }
+    }
+    // W2: column n of hidden
+    for (uint64_t n = 0; n < H; ++n) {
+      const uint64_t nt = n / 8, c = n % 8, quad = c / 4, j = c % 4;
+      for (uint64_t g = 0; g < G2; ++g) {
+        const uint64_t t = 2 * g + quad;
+        put_unit(blk + L.pub.w2_off + nt * 128 * G2 + (j * L2 + t) * 16,
+                 [&](int k) { return qd[(32 * g + k) * H + n]; });
+        put_record(blk + L.pub.w2_meta_off + nt * 8 * G2 * RB + (4 * t + j) * RB, sd[g * H + n], zd[g * H + n]);
+      }
+    }
+  }
+  return ok();
+}
+
+int awq_moe_route_compact(const int32_t* topk_ids, int32_t M, int32_t topk, int32_t num_experts,
+                          int32_t* active_expert_ids, int32_t* active_expert_offsets,
+                          int32_t* sorted_slots, int32_t* num_active, uint32_t* status, void* stream) {
+  int rc = check_tokens(M, topk);
+  if (rc) return rc;
+  if (num_experts < 1) return fail(AWQ_MOE_EINVAL, "num_experts %d < 1", num_experts);
+  if (!topk_ids || !aligned(topk_ids, 4)) return fail(AWQ_MOE_EINVAL, "topk_ids null or misaligned");
+  if ((rc = check_route_ptrs(active_expert_ids, active_expert_offsets, sorted_slots, num_active))) return rc;
+  if (!status || !aligned(status, 4)) return fail(AWQ_MOE_EINVAL, "status null or misaligned");
+  if ((rc = check_device())) return rc;
+  return hip_status(awq_moe::launch_route_compact(topk_ids, M * topk, num_experts, active_expert_ids,
+                                                  active_expert_offsets, sorted_slots, num_active, status,
+                                                  static_cast<hipStream_t>(stream)),
+                    "route_compact launch");
+}
+
+int awq_moe_w13_swiglu(const awq_moe_dims* dims, const void* bank, const uint16_t* x, int32_t M,
+                       int32_t topk, const int32_t* active_expert_ids, const int32_t* active_expert_offsets,
+                       const int32_t* sorted_slots, const int32_t* num_active, uint16_t* act, void* stream) {
+  int rc = check_dims(dims);
+  if (rc) return rc;
+  if ((rc = check_tokens(M, topk))) return rc;
+  if (!bank || !aligned(bank, 256)) return fail(AWQ_MOE_EINVAL, "bank null or not 256-byte aligned");
+  if (!x || !aligned(x, 16)) return fail(AWQ_MOE_EINVAL, "x null or not 16-byte aligned");
+  if (!act || !aligned(act, 16)) return fail(AWQ_MOE_EINVAL, "act null or not 16-byte aligned");
+  if ((rc = check_route_ptrs(active_expert_ids, active_expert_offsets, sorted_slots, num_active))) return rc;
+  if ((rc = check_device())) return rc;
+  const awq_moe::StageArgs a = stage_args(dims, bank, M, topk, active_expert_ids, active_expert_offsets,
+                                          sorted_slots, num_active);
+  return hip_status(awq_moe::launch_w13_swiglu(a, x, act, static_cast<hipStream_t>(stream)), "w13 launch");
+}
+
+int awq_moe_w2_reduce(const awq_moe_dims* dims, const void* bank, const uint16_t* act, const float* topk_w,
+                      int32_t M, int32_t topk, const int32_t* active_expert_ids,
+                      const int32_t* active_expert_offsets, const int32_t* sorted_slots,
+                      const int32_t* num_active, uint16_t* out, void* stream) {
+  int rc = check_dims(dims);
+  if (rc) return rc;
+  if ((rc = check_tokens(M, topk))) return rc;
+  if (!bank || !aligned(bank, 256)) return fail(AWQ_MOE_EINVAL, "bank null or not 256-byte aligned");
+  if (!act || !aligned(act, 16)) return fail(AWQ_MOE_EINVAL, "act null or not 16-byte aligned");
+  if (!topk_w || !aligned(topk_w, 4)) return fail(AWQ_MOE_EINVAL, "topk_w null or misaligned");
+  if (!out || !aligned(out, 16)) return fail(AWQ_MOE_EINVAL, "out null or not 16-byte aligned");
+  if ((rc = check_route_ptrs(active_expert_ids, active_expert_offsets, sorted_slots, num_active))) return rc;
+  if ((rc = check_device())) return rc;
+  const awq_moe::StageArgs a = stage_args(dims, bank, M, topk, active_expert_ids, active_expert_offsets,
+                                          sorted_slots, num_active);
+  return hip_status(awq_moe::launch_w2_reduce(a, act, topk_w, out, static_cast<hipStream_t>(stream)),
+                    "w2 launch");
+}
+
+int awq_moe_decode(const awq_moe_dims* dims, const void* bank, const uint16_t* x, const int32_t* topk_ids,
+                   const float* topk_w, int32_t M, int32_t topk, uint16_t* out, void* workspace,
+                   uint64_t workspace_bytes, void* stream) {
+  int rc = check_dims(dims);
+  if (rc) return rc;
+  if ((rc = check_tokens(M, topk))) return rc;
+  if (!bank || !aligned(bank, 256)) return fail(AWQ_MOE_EINVAL, "bank null or not 256-byte aligned");
+  if (!x || !aligned(x, 16)) return fail(AWQ_MOE_EINVAL, "x null or not 16-byte aligned");
+  if (!topk_ids || !aligned(topk_ids, 4)) return fail(AWQ_MOE_EINVAL, "topk_ids null or misaligned");
+  if (!topk_w || !aligned(topk_w, 4)) return fail(AWQ_MOE_EINVAL, "topk_w null or misaligned");
+  if (!out || !aligned(out, 16)) return fail(AWQ_MOE_EINVAL, "out null or not 16-byte aligned");
+  if (!workspace || !aligned(workspace, 256)) return fail(AWQ_MOE_EINVAL, "workspace null or not 256-byte aligned");
+  const WsLayout W = make_ws(dims, M, topk);
+  if (workspace_bytes < W.total)
+    return fail(AWQ_MOE_ENOSPC, "workspace_bytes %llu < %llu", (unsigned long long)workspace_bytes,
+                (unsigned long long)W.total);
+  if ((rc = check_device())) return rc;
+  uint8_t* ws = static_cast<uint8_t*>(workspace);
+  uint32_t* status = reinterpret_cast<uint32_t*>(ws + AWQ_MOE_WS_STATUS_OFFSET);
+  int32_t* num_active = reinterpret_cast<int32_t*>(ws + 4);
+  int32_t* ids = reinterpret_cast<int32_t*>(ws + W.ids_off);
+  int32_t* offsets = reinterpret_cast<int32_t*>(ws + W.offsets_off);
+  int32_t* slots = reinterpret_cast<int32_t*>(ws + W.slots_off);
+  uint16_t* act = reinterpret_cast<uint16_t*>(ws + W.act_off);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e = awq_moe::launch_route_compact(topk_ids, M * topk, dims->num_experts, ids, offsets, slots,
+                                               num_active, status, s);
+  if (e != hipSuccess) return hip_status(e, "route_compact launch");
+  const awq_moe::StageArgs a = stage_args(dims, bank, M, topk, ids, offsets, slots, num_active);
+  if ((e = awq_moe::launch_w13_swiglu(a, x, act, s)) != hipSuccess) return hip_status(e, "w13 launch");
+  return hip_status(awq_moe::launch_w2_reduce(a, act, topk_w, out, s), "w2 launch");
+}
+
+int awq_moe_dequant(const awq_moe_dims* dims, const void* bank, int32_t expert_begin, int32_t expert_count,
+                    int32_t which, float* out, void* stream) {
+  int rc = check_dims(dims);
+  if (rc) return rc;
+  if (!bank || !aligned(bank, 256)) return fail(AWQ_MOE_EINVAL, "bank null or not 256-byte aligned");
+  if (!out || !aligned(out, 4)) return fail(AWQ_MOE_EINVAL, "out null or misaligned");
+  if (which != 0 && which != 1) return fail(AWQ_MOE_EINVAL, "which %d: 0 (W13) or 1 (W2)", which);
+  if (expert_count < 1 || expert_begin < 0 || (int64_t)expert_begin + expert_count > dims->num_experts)
+    return fail(AWQ_MOE_EINVAL, "expert range [%d, %d) outside [0, %d)", expert_begin,
+                expert_begin + expert_count, dims->num_experts);
+  if ((rc = check_device())) return rc;
+  const Layout L = make_layout(dims);
+  const int K = which == 0 ? dims->hidden : dims->inter;
+  const int N = which == 0 ? 2 * dims->inter : dims->hidden;
+  const uint64_t uo = which == 0 ? L.pub.w13_off : L.pub.w2_off;
+  const uint64_t mo = which == 0 ? L.pub.w13_meta_off : L.pub.w2_meta_off;
+  return hip_status(awq_moe::launch_dequant(static_cast<const uint8_t*>(bank), L.pub.expert_bytes, uo, mo,
+                                            dims->meta_bytes, which, K, N, expert_begin, expert_count, out,
+                                            static_cast<hipStream_t>(stream)),
+                    "dequant launch");
+}
+
+}  // extern "C"

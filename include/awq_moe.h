@@ -1,0 +1,185 @@
+/*
+ * awq_moe.h -- C ABI of the AWQ int4 MoE expert stage for small-batch decode
+ * (gfx950 / MI355X).
+ *
+ * The stage (PR #520 "[Perf][SM70] Narrow Qwen3.8 AWQ active grouped decode",
+ * Purpose and Implementation; fork PR #12 "Add opt-in native-g32 AWQ QPN M1
+ * dispatch", Purpose and stack): for M = 1..8 decode tokens, each with top-k
+ * routed experts, compact the routed ids into active-expert segments, run
+ * W13 (gate/up interleaved, K = hidden, N = 2*inter) with SwiGLU, run W2
+ * (K = inter, N = hidden) and sum the expert outputs weighted by the router
+ * weights. Weights are AWQ int4 with one {fp16 scale, u8 zero} record per
+ * group of 32 along K, stored as 4-byte padded or 3-byte compact records
+ * (PR #522 "Coalesce AWQ QPN W13 compact metadata loads and enable compact
+ * metadata by default", Purpose).
+ *
+ * Conventions for every entry point:
+ *  - Return AWQ_MOE_OK (0) or a negative error code. Arguments are checked on
+ *    the host before anything is written or launched; on error nothing is
+ *    written and nothing is launched (fail closed, as the pages' explicit
+ *    requests do: PR #522, Default switch). awq_moe_last_error() then holds a
+ *    message for the calling thread.
+ *  - "device" pointers are HIP device memory owned by the caller; "host"
+ *    pointers are ordinary host memory owned by the caller. The library never
+ *    allocates device memory, never synchronises a stream and reads no
+ *    environment variables, so the launching calls can be captured in a HIP
+ *    graph.
+ *  - stream is a hipStream_t passed as void* (NULL = the null stream). Kernels
+ *    run asynchronously on it; a launch failure returns AWQ_MOE_EHIP.
+ *  - Concurrent calls that share an output or workspace buffer race.
+ *
+ * Bank layout (version 1; also stated in oracle/layout.py):
+ *   Per expert block, four sections, each padded to 256 bytes: W13 units,
+ *   W13 records, W2 units, W2 records (offsets from awq_moe_bank_layout_query).
+ *   A unit = 16 bytes = the 32 4-bit values of group g of one output column:
+ *   dword d (LE) holds k = 32g + 8d + p, p = 0..7, value p at bit
+ *   4*(p>>1) + 16*(p&1). A record = bytes {scale lo, scale hi, zero} (+ a
+ *   zero pad byte for 4-byte records). W13 column 2i is gate i, 2i+1 is up i.
+ *   W13: tiles of 16 columns, G13 = H/32, L13 = 4*G13; column n, group g:
+ *     nt = n/16, c = n%16, quad = c/4, j = c%4, t = 4g + quad,
+ *     unit at nt*256*G13 + (j*L13 + t)*16, record at nt*16*G13*RB + (4t + j)*RB.
+ *   W2: tiles of 8 columns, G2 = I/32, L2 = 2*G2:
+ *     nt = n/8, c = n%8, quad = c/4, j = c%4, t = 2g + quad,
+ *     unit at nt*128*G2 + (j*L2 + t)*16, record at nt*8*G2*RB + (4t + j)*RB.
+ *
+ * Routing arrays (n = M*topk slots, flat slot s = t*topk + j):
+ *   active_expert_ids[n]      segment -> expert id, ascending; -1 past num_active
+ *   active_expert_offsets[n+1] row ranges of the segments; entries past
+ *                             num_active hold V, the number of valid slots
+ *   sorted_slots[n]           row -> flat slot; rows of one segment in
+ *                             ascending slot order; invalid slots last
+ *   num_active[1]             number of segments
+ *   status[1]                 bit 0 set when some id was outside [0, E)
+ *   Ids outside [0, E) are not an error of the call: their rows are left out
+ *   of every segment and contribute 0 to the output.
+ */
+#ifndef AWQ_MOE_H
+#define AWQ_MOE_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define AWQ_MOE_OK 0
+#define AWQ_MOE_EINVAL (-1)       /* null pointer, misalignment, bad size or value */
+#define AWQ_MOE_EUNSUPPORTED (-2) /* group size, record size or shape not served */
+#define AWQ_MOE_ENOSPC (-3)       /* buffer smaller than the layout needs */
+#define AWQ_MOE_EHIP (-4)         /* HIP runtime error (message has hipGetErrorString) */
+
+#define AWQ_MOE_MAX_TOKENS 8      /* decode tokens per call, M in [1, 8] */
+#define AWQ_MOE_MAX_TOPK 32
+#define AWQ_MOE_MAX_HIDDEN 8192
+#define AWQ_MOE_MAX_INTER 2048
+#define AWQ_MOE_STATUS_BAD_ID 1u
+
+typedef struct awq_moe_dims {
+  int32_t num_experts; /* E >= 1 */
+  int32_t hidden;      /* H: multiple of 32, <= AWQ_MOE_MAX_HIDDEN */
+  int32_t inter;       /* I: local intermediate size, multiple of 32, <= AWQ_MOE_MAX_INTER */
+  int32_t group_size;  /* must be 32 */
+  int32_t meta_bytes;  /* 3 (compact records) or 4 (padded records) */
+} awq_moe_dims;
+
+typedef struct awq_moe_bank_layout {
+  uint64_t w13_off;      /* section offsets inside one expert block */
+  uint64_t w13_meta_off;
+  uint64_t w2_off;
+  uint64_t w2_meta_off;
+  uint64_t expert_bytes; /* one expert block (multiple of 256) */
+  uint64_t total_bytes;  /* num_experts * expert_bytes */
+} awq_moe_bank_layout;
+
+/* Fill *out with the bank layout of dims (host only). EINVAL on a null
+ * pointer, EUNSUPPORTED on a shape this layout does not serve. */
+int awq_moe_bank_layout_query(const awq_moe_dims* dims, awq_moe_bank_layout* out);
+
+/* Pack logical AWQ weights into the bank layout (host -> host; pure,
+ * deterministic, thread-safe). Builds the prepared banks the pages call
+ * awq_sm70_prepare_compact for 3-byte records (PR #522, Default switch).
+ * Orientation y = x W, all arrays C-contiguous host memory:
+ *   q_gate, q_up [E][H][I] and q_down [E][I][H]: uint8, values 0..15
+ *   s_gate, s_up [E][H/32][I], s_down [E][I/32][H]: fp16 bit patterns (finite)
+ *   z_gate, z_up [E][H/32][I], z_down [E][I/32][H]: uint8 zeros (0..255)
+ * bank: host buffer of bank_bytes >= total_bytes; every byte of the first
+ * total_bytes is written (padding zero). The caller uploads it to device.
+ * EINVAL on a q value > 15 or a non-finite scale (nothing written),
+ * ENOSPC when bank_bytes is too small. */
+int awq_moe_prepare(const awq_moe_dims* dims,
+                    const uint8_t* q_gate, const uint8_t* q_up, const uint8_t* q_down,
+                    const uint16_t* s_gate, const uint16_t* s_up, const uint16_t* s_down,
+                    const uint8_t* z_gate, const uint8_t* z_up, const uint8_t* z_down,
+                    void* bank, uint64_t bank_bytes);
+
+/* Bytes of decode workspace for up to max_tokens tokens with topk experts
+ * each (host only). */
+int awq_moe_workspace_bytes(const awq_moe_dims* dims, int32_t max_tokens, int32_t topk,
+                            uint64_t* out);
+
+/* Byte offset, inside the decode workspace, of the uint32 status word that
+ * awq_moe_decode writes (bit 0: some id was outside [0, E)). Always 0. */
+#define AWQ_MOE_WS_STATUS_OFFSET 0
+
+/* Compact routed ids into active-expert segments (PR #520, Purpose: multi-row
+ * active-expert segments with offsets-based scheduling; Implementation: the op
+ * writes active_expert_ids and active_expert_offsets). All pointers device,
+ * int32 topk_ids [M][topk] C-contiguous; outputs as described above, sized
+ * for n = M*topk. M in [1, 8], topk in [1, 32]. */
+int awq_moe_route_compact(const int32_t* topk_ids, int32_t M, int32_t topk, int32_t num_experts,
+                          int32_t* active_expert_ids, int32_t* active_expert_offsets,
+                          int32_t* sorted_slots, int32_t* num_active, uint32_t* status,
+                          void* stream);
+
+/* The whole stage for M = 1..8 tokens (PR #520 Purpose: 2 to 8 tokens; fork
+ * PR #12 Purpose and stack: physical M = 1 with fp16 (1, hidden) x, int32
+ * (1, k) ids and fp32 router weights).
+ *   bank     device, 256-byte aligned, awq_moe_bank_layout_query(dims).total_bytes
+ *   x        device fp16 [M][H], 16-byte aligned
+ *   topk_ids device int32 [M][topk]; topk_w device fp32 [M][topk] (used as given)
+ *   out      device fp16 [M][H], 16-byte aligned, overwritten:
+ *            out[t] = fp16_rne(sum_j topk_w[t][j] * W2_e(silu(x_t Wg_e) * (x_t Wu_e))),
+ *            e = topk_ids[t][j], accumulated in fp32 in a fixed order that
+ *            depends only on the compacted segments.
+ *   workspace device, 256-byte aligned, >= awq_moe_workspace_bytes(dims, M, topk);
+ *            holds the routing arrays, the fp16 intermediate and the status word.
+ * Launches three kernels on stream. */
+int awq_moe_decode(const awq_moe_dims* dims, const void* bank, const uint16_t* x,
+                   const int32_t* topk_ids, const float* topk_w, int32_t M, int32_t topk,
+                   uint16_t* out, void* workspace, uint64_t workspace_bytes, void* stream);
+
+/* --- stage exports, for stage-pair checks (fork PR #12, Numerical acceptance:
+ * W2 checked on its own intermediate) and per-kernel timing ------------- */
+
+/* W13 + SwiGLU over compacted segments. act: device fp16 [M*topk][I]; row r
+ * of act belongs to sorted row r (rows past the valid count are not written).
+ * Routing arrays as produced by awq_moe_route_compact for the same M, topk. */
+int awq_moe_w13_swiglu(const awq_moe_dims* dims, const void* bank, const uint16_t* x,
+                       int32_t M, int32_t topk, const int32_t* active_expert_ids,
+                       const int32_t* active_expert_offsets, const int32_t* sorted_slots,
+                       const int32_t* num_active, uint16_t* act, void* stream);
+
+/* W2 + router-weighted reduction from a given fp16 act [M*topk][I] (sorted
+ * rows). out device fp16 [M][H], overwritten. */
+int awq_moe_w2_reduce(const awq_moe_dims* dims, const void* bank, const uint16_t* act,
+                      const float* topk_w, int32_t M, int32_t topk,
+                      const int32_t* active_expert_ids, const int32_t* active_expert_offsets,
+                      const int32_t* sorted_slots, const int32_t* num_active,
+                      uint16_t* out, void* stream);
+
+/* Dequantise experts [expert_begin, expert_begin + expert_count) of the bank
+ * into fp32 (diagnostic; the result is exact, see the design notes):
+ *   which = 0: W13 [count][H][2I] (column 2i gate, 2i+1 up)
+ *   which = 1: W2  [count][I][H]
+ * out device fp32, C-contiguous. */
+int awq_moe_dequant(const awq_moe_dims* dims, const void* bank, int32_t expert_begin,
+                    int32_t expert_count, int32_t which, float* out, void* stream);
+
+/* Message for the last error returned on the calling thread ("" if none). */
+const char* awq_moe_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* AWQ_MOE_H */

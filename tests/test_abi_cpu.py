@@ -1,0 +1,152 @@
+"""C-ABI checks that need no GPU: the library loads and exports every declared
+symbol; the host packer matches the oracle packer byte for byte; invalid
+arguments are rejected before anything is written or launched."""
+
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+from awq_int4_mixture_amd import inputs
+from oracle import layout as OL
+
+abi = pytest.importorskip("awq_int4_mixture_amd.abi", reason="libawq_moe.so not built")
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(__file__)), "include", "awq_moe.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(awq_moe_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_every_declared_symbol_is_exported():
+    names = declared_functions()
+    assert set(names) == set(abi.EXPORTED), names
+    lib = ctypes.CDLL(abi.LIB_PATH)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+@pytest.mark.parametrize("E,H,I,rb", [(512, 2560, 160, 3), (512, 2560, 160, 4), (16, 256, 32, 4), (3, 96, 64, 3)])
+def test_layout_query_matches_oracle(E, H, I, rb):
+    L = abi.awq_moe_bank_layout_query(abi.make_dims(E, H, I, rb))
+    O = OL.layout(OL.Dims(E, H, I, rb))
+    assert (L.w13_off, L.w13_meta_off, L.w2_off, L.w2_meta_off, L.expert_bytes, L.total_bytes) == \
+           (O.w13_off, O.w13_meta_off, O.w2_off, O.w2_meta_off, O.expert_bytes, O.total_bytes)
+
+
+@pytest.mark.parametrize("rb", [3, 4])
+@pytest.mark.parametrize("E,H,I", [(4, 256, 32), (2, 96, 64), (2, 2560, 160)])
+def test_prepare_bytes_equal_oracle_pack(rb, E, H, I):
+    bi = inputs.bank_inputs(21, E, H, I, zero_hi=256)
+    got = abi.prepare_from_inputs(abi.make_dims(E, H, I, rb), bi)
+    want = OL.pack_bank(OL.Dims(E, H, I, rb), bi)
+    assert got.tobytes() == want.tobytes()
+
+
+@pytest.mark.parametrize("rb", [3, 4])
+def test_prepare_worked_example(rb):
+    from tests.test_oracle_layout import golden_entries, worked_example_weights
+    w = worked_example_weights()
+    bank = abi.awq_moe_prepare(abi.make_dims(1, 64, 32, rb), *(a[None] for a in (
+        w.q_gate, w.q_up, w.q_down, w.s_gate, w.s_up, w.s_down, w.z_gate, w.z_up, w.z_down)))
+    for r, off, want in golden_entries():
+        if r == rb:
+            assert bytes(bank[off:off + len(want)]) == want
+
+
+def _small_inputs():
+    return inputs.bank_inputs(2, 2, 64, 32)
+
+
+def test_prepare_rejects_bad_values_and_writes_nothing():
+    dims = abi.make_dims(2, 64, 32, 3)
+    total = abi.awq_moe_bank_layout_query(dims).total_bytes
+    bi = _small_inputs()
+    bad_q = bi.q_up.copy()
+    bad_q[1, 5, 7] = 16
+    bank = np.full(total, 0xAB, np.uint8)
+    with pytest.raises(abi.AwqMoeError) as ei:
+        abi.awq_moe_prepare(dims, bi.q_gate, bad_q, bi.q_down, bi.s_gate, bi.s_up, bi.s_down,
+                            bi.z_gate, bi.z_up, bi.z_down, bank=bank)
+    assert ei.value.code == abi.EINVAL and (bank == 0xAB).all()
+    for bits in (0x7C00, 0xFC00, 0x7E00):          # +inf, -inf, NaN
+        s = bi.s_down.copy().view(np.uint16)
+        s[0, 0, 3] = bits
+        with pytest.raises(abi.AwqMoeError) as ei:
+            abi.awq_moe_prepare(dims, bi.q_gate, bi.q_up, bi.q_down, bi.s_gate, bi.s_up, s.view(np.float16),
+                                bi.z_gate, bi.z_up, bi.z_down, bank=bank)
+        assert ei.value.code == abi.EINVAL and (bank == 0xAB).all()
+    small = np.zeros(total - 1, np.uint8)
+    with pytest.raises(abi.AwqMoeError) as ei:
+        abi.awq_moe_prepare(dims, bi.q_gate, bi.q_up, bi.q_down, bi.s_gate, bi.s_up, bi.s_down,
+                            bi.z_gate, bi.z_up, bi.z_down, bank=small)
+    assert ei.value.code == abi.ENOSPC and not small.any()
+
+
+@pytest.mark.parametrize("dims,code", [
+    ((512, 2560, 160, 32, 5), abi.EUNSUPPORTED),
+    ((512, 2560, 160, 64, 4), abi.EUNSUPPORTED),
+    ((512, 2560, 160, 16, 3), abi.EUNSUPPORTED),
+    ((512, 2570, 160, 32, 3), abi.EUNSUPPORTED),
+    ((512, 2560, 150, 32, 3), abi.EUNSUPPORTED),
+    ((512, 16384, 160, 32, 3), abi.EUNSUPPORTED),
+    ((512, 2560, 4096, 32, 3), abi.EUNSUPPORTED),
+    ((0, 2560, 160, 32, 3), abi.EINVAL),
+])
+def test_unsupported_dims_fail_closed(dims, code):
+    d = abi.awq_moe_dims(dims[0], dims[1], dims[2], dims[3], dims[4])
+    with pytest.raises(abi.AwqMoeError) as ei:
+        abi.awq_moe_bank_layout_query(d)
+    assert ei.value.code == code
+
+
+@pytest.mark.parametrize("M,k", [(0, 10), (9, 10), (1, 0), (1, 33), (-1, 2), (127, 10), (128, 10)])
+def test_token_and_topk_bounds(M, k):
+    """PR #520 (Tests) checks 1/2/8/9/127/128-token boundaries: only M in 1..8 is served."""
+    d = abi.make_dims(512, 2560, 160, 3)
+    with pytest.raises(abi.AwqMoeError) as ei:
+        abi.awq_moe_workspace_bytes(d, M, k)
+    assert ei.value.code == abi.EINVAL
+
+
+def test_device_calls_reject_bad_arguments_before_launch():
+    """Host validation returns before any HIP call, so these run without a GPU."""
+    lib = abi._lib
+    d = abi.make_dims(512, 2560, 160, 3)
+    buf = (ctypes.c_uint8 * 4096)()
+    base = (ctypes.addressof(buf) + 255) // 256 * 256
+    p = ctypes.c_void_p(base)
+    mis = ctypes.c_void_p(base + 2)
+    ws_need = abi.awq_moe_workspace_bytes(d, 1, 10)
+    cases = [
+        (lambda: lib.awq_moe_decode(ctypes.byref(d), p, p, p, p, 9, 10, p, p, ws_need, None), abi.EINVAL),
+        (lambda: lib.awq_moe_decode(ctypes.byref(d), p, p, p, p, 1, 10, p, p, ws_need - 1, None), abi.ENOSPC),
+        (lambda: lib.awq_moe_decode(ctypes.byref(d), mis, p, p, p, 1, 10, p, p, ws_need, None), abi.EINVAL),
+        (lambda: lib.awq_moe_decode(ctypes.byref(d), p, mis, p, p, 1, 10, p, p, ws_need, None), abi.EINVAL),
+        (lambda: lib.awq_moe_decode(ctypes.byref(d), p, p, None, p, 1, 10, p, p, ws_need, None), abi.EINVAL),
+        (lambda: lib.awq_moe_decode(ctypes.byref(d), p, p, p, p, 1, 10, mis, p, ws_need, None), abi.EINVAL),
+        (lambda: lib.awq_moe_decode(None, p, p, p, p, 1, 10, p, p, ws_need, None), abi.EINVAL),
+        (lambda: lib.awq_moe_route_compact(p, 0, 10, 512, p, p, p, p, p, None), abi.EINVAL),
+        (lambda: lib.awq_moe_route_compact(p, 1, 10, 0, p, p, p, p, p, None), abi.EINVAL),
+        (lambda: lib.awq_moe_route_compact(p, 1, 10, 512, p, p, None, p, p, None), abi.EINVAL),
+        (lambda: lib.awq_moe_w13_swiglu(ctypes.byref(d), p, p, 1, 10, p, p, p, p, mis, None), abi.EINVAL),
+        (lambda: lib.awq_moe_w2_reduce(ctypes.byref(d), p, p, p, 1, 10, p, p, p, p, mis, None), abi.EINVAL),
+        (lambda: lib.awq_moe_dequant(ctypes.byref(d), p, 510, 3, 0, p, None), abi.EINVAL),
+        (lambda: lib.awq_moe_dequant(ctypes.byref(d), p, 0, 1, 2, p, None), abi.EINVAL),
+    ]
+    for i, (call, code) in enumerate(cases):
+        assert call() == code, (i, abi.awq_moe_last_error())
+        assert abi.awq_moe_last_error() != ""
+    assert bytes(buf) == bytes(4096)
+
+
+def test_workspace_grows_with_tokens():
+    d = abi.make_dims(512, 2560, 160, 3)
+    sizes = [abi.awq_moe_workspace_bytes(d, M, 10) for M in range(1, 9)]
+    assert all(b > a for a, b in zip(sizes, sizes[1:]))
+    assert sizes[-1] >= 80 * 160 * 2

@@ -1,0 +1,316 @@
+"""GPU parity of the HIP path against the float64 oracle, through the C ABI.
+
+Integer work (routing arrays, dequantised fp32 weights) must match bit for
+bit; floating outputs must satisfy max|gpu - ref| <= 4e-3 max|ref| and
+||gpu - ref|| / ||ref|| <= 2e-3.
+"""
+
+import itertools
+
+import numpy as np
+import pytest
+
+from awq_int4_mixture_amd import inputs
+from oracle import ref as R
+from tests.gpu_helpers import bank_case, f16_to_np, say, to_dev, torch_mod
+
+pytestmark = pytest.mark.gpu
+
+torch = torch_mod()
+if not torch.cuda.is_available():
+    pytest.skip("no GPU", allow_module_level=True)
+
+from awq_int4_mixture_amd import abi  # noqa: E402  (fails loudly when the library is missing)
+
+RANK = (2560, 160)
+TINY = (256, 32)
+
+
+def oracle_route(ids, E):
+    return R.route_compact(ids, E)
+
+
+def gpu_route(ids, E):
+    r = abi.awq_moe_route_compact(to_dev(ids), E)
+    torch.cuda.synchronize()
+    return {k: getattr(r, k).cpu().numpy() for k in
+            ("active_expert_ids", "active_expert_offsets", "sorted_slots", "num_active", "status")}, r
+
+
+def assert_route_equal(g, o):
+    assert g["active_expert_ids"].tolist() == o["active_ids"].tolist()
+    assert g["active_expert_offsets"].tolist() == o["offsets"].tolist()
+    assert g["sorted_slots"].tolist() == o["sorted_slots"].tolist()
+    assert int(g["num_active"][0]) == o["num_active"]
+    assert int(g["status"][0]) == o["status"]
+
+
+# ---------------------------------------------------------------------------
+# integer work: dequantised weights and routing arrays, bit-exact
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("rb", [3, 4])
+@pytest.mark.parametrize("shape", [TINY, RANK])
+def test_dequant_bit_exact(rb, shape):
+    H, I = shape
+    say("dequant", rb, shape)
+    dims, bank, bi = bank_case(31, 6, H, I, rb, 256)
+    for which in (0, 1):
+        got = abi.awq_moe_dequant(dims, bank, 1, 4, which).cpu().numpy()
+        for el in range(4):
+            w = bi.expert(1 + el)
+            want = R.w13_interleaved(w) if which == 0 else R.dequant(w.q_down, w.s_down, w.z_down)
+            assert R.isclose_exact_fp32(want)
+            np.testing.assert_array_equal(got[el], want.astype(np.float32))
+
+
+def test_route_exhaustive_small():
+    """Every id tensor with E=4, k=2, M=1..3."""
+    say("route exhaustive")
+    for M in (1, 2, 3):
+        for flat in itertools.product(range(4), repeat=2 * M):
+            ids = np.array(flat, np.int32).reshape(M, 2)
+            g, _ = gpu_route(ids, 4)
+            assert_route_equal(g, oracle_route(ids, 4))
+
+
+def test_route_random_and_edges():
+    rng = np.random.default_rng(4)
+    cases = []
+    for _ in range(150):
+        M = int(rng.integers(1, 9))
+        k = int(rng.integers(1, 33))
+        E = int(rng.integers(1, 1024))
+        cases.append((rng.integers(-3, E + 3, size=(M, k)).astype(np.int32), E))
+    cases += [
+        (np.full((8, 32), 7, np.int32), 512),                 # one expert takes every slot (256 rows)
+        (np.full((8, 32), -1, np.int32), 512),                # every id invalid
+        (np.arange(256, dtype=np.int32).reshape(8, 32), 256),  # all distinct, max slots
+        (np.array([[511, 0, 255, 256, 1, 510, 2, 509, 3, 508]], np.int32), 512),
+    ]
+    for ids, E in cases:
+        say("route", ids.shape, E)
+        g, _ = gpu_route(ids, E)
+        assert_route_equal(g, oracle_route(ids, E))
+
+
+# ---------------------------------------------------------------------------
+# stages and the whole decode
+# ---------------------------------------------------------------------------
+
+def run_decode(dims, bank, x, ids, w):
+    out = abi.awq_moe_decode(dims, bank, to_dev(x), to_dev(ids), to_dev(w))
+    torch.cuda.synchronize()
+    return f16_to_np(out)
+
+
+def check(got, want, what):
+    ok, e = R.within_gate(got, want)
+    say(what, e)
+    assert ok, (what, e)
+    return e
+
+
+@pytest.mark.parametrize("rb", [3, 4])
+@pytest.mark.parametrize("M", [1, 2, 8])
+def test_w13_stage_and_w2_stage_pair(rb, M):
+    """W13+SwiGLU against the oracle; W2+reduction checked on the GPU's own
+    intermediate (fork PR #12, Numerical acceptance)."""
+    H, I = RANK
+    dims, bank, bi = bank_case(7, 64, H, I, rb)
+    rng = inputs.call_rng(7, 100 + M)
+    x = inputs.activations(rng, M, H)
+    ids = inputs.ids_shared_pool(rng, M, 10, 64)
+    w = inputs.router_weights(rng, M, 10)
+    route_o = oracle_route(ids, 64)
+    _, route_g = gpu_route(ids, 64)
+    act = abi.awq_moe_w13_swiglu(dims, bank, to_dev(x), M, 10, route_g)
+    torch.cuda.synchronize()
+    act_np = f16_to_np(act)
+    V = route_o["num_valid"]
+    act_ref = R.w13_swiglu_rows(x, route_o, 10, bi.expert)
+    check(act_np[:V], act_ref[:V], f"w13 M={M} rb={rb}")
+    out = abi.awq_moe_w2_reduce(dims, bank, act, to_dev(w), M, 10, route_g)
+    torch.cuda.synchronize()
+    out_ref = R.w2_reduce(act_np, w, route_o, 10, bi.expert, M, H)
+    check(f16_to_np(out), out_ref, f"w2 on own act M={M} rb={rb}")
+
+
+@pytest.mark.parametrize("rb", [3, 4])
+def test_tiny_config(rb):
+    """E=16, top-k 2, hidden 256, inter 32, M=1."""
+    dims, bank, bi = bank_case(1, 16, 256, 32, rb)
+    for c in range(4):
+        rng = inputs.call_rng(1, c)
+        x = inputs.activations(rng, 1, 256)
+        ids = inputs.ids_distinct(rng, 1, 2, 16)
+        w = inputs.router_weights(rng, 1, 2)
+        check(run_decode(dims, bank, x, ids, w), R.moe_stage(x, ids, w, 16, bi.expert), f"tiny rb={rb} c={c}")
+
+
+@pytest.mark.parametrize("rb", [3, 4])
+@pytest.mark.parametrize("M,mode", [(1, "distinct"), (2, "pool"), (4, "pool"), (8, "pool"), (8, "all"),
+                                    (3, "pool"), (5, "distinct")])
+def test_decode_rank_shape(rb, M, mode):
+    H, I = RANK
+    dims, bank, bi = bank_case(7, 128, H, I, rb)
+    rng = inputs.call_rng(8, M * 10 + len(mode))
+    x = inputs.activations(rng, M, H)
+    draw = {"distinct": inputs.ids_distinct, "pool": inputs.ids_shared_pool, "all": inputs.ids_all_distinct}[mode]
+    ids = draw(rng, M, 10, 128)
+    w = inputs.router_weights(rng, M, 10)
+    check(run_decode(dims, bank, x, ids, w), R.moe_stage(x, ids, w, 128, bi.expert), f"rank M={M} {mode} rb={rb}")
+
+
+def test_decode_full_bank_rank_shape_m1_and_m8():
+    """The benchmark's layer: E=512, hidden 2560, inter 160, top-k 10, 3-byte records."""
+    H, I = RANK
+    dims, bank, bi = bank_case(2026, 512, H, I, 3)
+    for M in (1, 8):
+        rng = inputs.call_rng(2026, M)
+        x = inputs.activations(rng, M, H)
+        ids = inputs.ids_shared_pool(rng, M, 10, 512) if M > 1 else inputs.ids_distinct(rng, 1, 10, 512)
+        w = inputs.router_weights(rng, M, 10)
+        check(run_decode(dims, bank, x, ids, w), R.moe_stage(x, ids, w, 512, bi.expert), f"full E512 M={M}")
+
+
+def test_duplicate_and_invalid_ids_and_status():
+    H, I = RANK
+    dims, bank, bi = bank_case(7, 64, H, I, 3)
+    rng = inputs.call_rng(9, 0)
+    M, k = 3, 10
+    x = inputs.activations(rng, M, H)
+    w = inputs.router_weights(rng, M, k)
+    ids = inputs.ids_distinct(rng, M, k, 64)
+    ids[0, 3] = ids[0, 1]          # duplicate inside one token
+    ids[1, :] = 5                  # every slot of a token on one expert
+    ids[2, 4] = 64                 # out of range
+    ids[2, 7] = -1
+    dec = abi.Decoder(dims, bank, k)
+    out = dec(to_dev(x), to_dev(ids), to_dev(w))
+    torch.cuda.synchronize()
+    check(f16_to_np(out), R.moe_stage(x, ids, w, 64, bi.expert), "dup/invalid")
+    assert dec.status() == abi.STATUS_BAD_ID
+    ok_ids = inputs.ids_distinct(rng, M, k, 64)
+    dec(to_dev(x), to_dev(ok_ids), to_dev(w))
+    assert dec.status() == 0
+
+
+def test_three_and_four_byte_records_give_identical_bytes():
+    """PR #522 (Default switch): outputs of the two layouts are byte-identical."""
+    H, I = RANK
+    _, b3, _ = bank_case(7, 64, H, I, 3)
+    d3 = abi.make_dims(64, H, I, 3)
+    _, b4, _ = bank_case(7, 64, H, I, 4)
+    d4 = abi.make_dims(64, H, I, 4)
+    for M in (1, 4, 8):
+        rng = inputs.call_rng(10, M)
+        x = inputs.activations(rng, M, H)
+        ids = inputs.ids_shared_pool(rng, M, 10, 64)
+        w = inputs.router_weights(rng, M, 10)
+        a = run_decode(d3, b3, x, ids, w)
+        b = run_decode(d4, b4, x, ids, w)
+        assert a.view(np.uint16).tolist() == b.view(np.uint16).tolist()
+
+
+# ---------------------------------------------------------------------------
+# exact cases and invariants (bit-exact on the GPU)
+# ---------------------------------------------------------------------------
+
+def test_w2_exact_integer_case_bit_exact():
+    """s = 1, z = 8, act in {-1, 0, 1}, weights 1: every value is an integer with
+    |y| <= 2048, so fp32 accumulation and the fp16 output are exact."""
+    H, I, E = 2560, 160, 16
+    bi = inputs.bank_inputs(12, E, H, I)
+    bi.s_down[:] = np.float16(1.0)
+    bi.z_down[:] = 8
+    dims = abi.make_dims(E, H, I, 3)
+    bank = to_dev(abi.prepare_from_inputs(dims, bi))
+    rng = np.random.default_rng(5)
+    M, k = 2, 10
+    ids = np.stack([rng.choice(E, k, replace=False) for _ in range(M)]).astype(np.int32)
+    w = np.zeros((M, k), np.float32)
+    w[:, 0] = 1.0
+    route_o = oracle_route(ids, E)
+    _, route_g = gpu_route(ids, E)
+    act = rng.integers(-1, 2, size=(M * k, I)).astype(np.float16)
+    out = abi.awq_moe_w2_reduce(dims, bank, to_dev(act), to_dev(w), M, k, route_g)
+    torch.cuda.synchronize()
+    want = R.w2_reduce(act, w, route_o, k, bi.expert, M, H)
+    assert np.abs(want).max() <= 2048 and np.array_equal(want, np.round(want))
+    np.testing.assert_array_equal(f16_to_np(out).astype(np.float64), want)
+
+
+def test_invariants_bit_exact():
+    H, I = RANK
+    dims, bank, bi = bank_case(7, 64, H, I, 3)
+    rng = inputs.call_rng(11, 0)
+    M, k = 4, 10
+    x = inputs.activations(rng, M, H)
+    ids = inputs.ids_shared_pool(rng, M, k, 64)
+    w = inputs.router_weights(rng, M, k)
+    base = run_decode(dims, bank, x, ids, w)
+    # run to run (PR #520 addendum: same-arm teacher-forced A/A was exact)
+    assert run_decode(dims, bank, x, ids, w).view(np.uint16).tolist() == base.view(np.uint16).tolist()
+    # permuting a token's (id, weight) pairs
+    perm = rng.permutation(k)
+    p = run_decode(dims, bank, x, ids[:, perm], w[:, perm])
+    assert p.view(np.uint16).tolist() == base.view(np.uint16).tolist()
+    # power-of-two scaling of the router weights scales the output exactly
+    s = run_decode(dims, bank, x, ids, (w * np.float32(0.25)).astype(np.float32))
+    assert np.array_equal(s.astype(np.float64) * 4, base.astype(np.float64)) or \
+        np.abs(s.astype(np.float64) * 4 - base).max() <= 2.0 ** -14 * 4
+    # zero weights give +0, zero activations give 0
+    z = run_decode(dims, bank, x, ids, np.zeros_like(w))
+    assert not z.view(np.uint16).any()
+    z2 = run_decode(dims, bank, np.zeros_like(x), ids, w)
+    assert not (z2.astype(np.float64) != 0).any()
+
+
+def test_batch_independence_within_tolerance():
+    """A token alone and inside a batch: the pages record cross-batch sensitivity
+    as a known property (PR #520, Precision); here report bit-equality and gate
+    on the tolerance."""
+    H, I = RANK
+    dims, bank, bi = bank_case(7, 64, H, I, 3)
+    rng = inputs.call_rng(12, 0)
+    M, k = 8, 10
+    x = inputs.activations(rng, M, H)
+    ids = inputs.ids_shared_pool(rng, M, k, 64)
+    w = inputs.router_weights(rng, M, k)
+    batch = run_decode(dims, bank, x, ids, w)
+    same = 0
+    for t in range(M):
+        alone = run_decode(dims, bank, x[t:t + 1], ids[t:t + 1], w[t:t + 1])
+        same += int(alone.view(np.uint16).tolist() == batch[t:t + 1].view(np.uint16).tolist())
+        ok, _ = R.within_gate(alone[0], batch[t])
+        assert ok
+    say("batch-independent tokens (bit-equal)", same, "of", M)
+
+
+def test_graph_capture_replays_match_eager():
+    H, I = RANK
+    dims, bank, bi = bank_case(7, 64, H, I, 3)
+    rng = inputs.call_rng(13, 0)
+    M, k = 2, 10
+    x = to_dev(inputs.activations(rng, M, H))
+    ids = to_dev(inputs.ids_shared_pool(rng, M, k, 64))
+    w = to_dev(inputs.router_weights(rng, M, k))
+    dec = abi.Decoder(dims, bank, k)
+    eager = dec(x, ids, w).clone()
+    torch.cuda.synchronize()
+    out = torch.empty_like(eager)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        dec(x, ids, w, out=out)            # warm up on the capture stream
+    torch.cuda.current_stream().wait_stream(s)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        dec(x, ids, w, out=out)
+    for rep in range(4):
+        out.fill_(float("nan"))
+        _ = torch.randn(1000, device="cuda").sum()      # unrelated eager work between replays
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, eager), rep
