@@ -1,0 +1,294 @@
+"""Benchmark of the AWQ int4 MoE expert stage for small-batch decode on one MI355X.
+
+Headline workload: the 512-expert rank-share layer (hidden 2560, local
+intermediate 160, top-k 10, int4 group 32, 4-byte records), M = 1 token,
+the same 10 hot experts on every call, 48 calls per HIP-graph replay with a
+fresh fp16 x ~ N(0,1) and softmax router weights per call (PR #522,
+Operator results: 48 calls per graph replay). One *step* is one replay: 48
+passes of route-compact -> W13+SwiGLU -> W2+reduction.
+
+Printed: one JSON line with the layer's achieved weight bandwidth (touched
+weight + record bytes / layer time), per-kernel times, the roofline of the
+dominant kernel (W13+SwiGLU) from HIP events on its stream, side
+measurements (cold M=1 with 3-byte records over 480 rotating experts; M=8
+with a shared expert pool), and the CPU oracle timed on a bounded sample.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--only NAME] [--no-cpu]
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+from awq_int4_mixture_amd import inputs  # noqa: E402
+
+HBM_PEAK_GBS = 8000.0
+CALLS = 48
+SEED = 2026
+E, K_TOP, H, I = 512, 10, 2560, 160
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=200)
+    p.add_argument("--warmup", type=int, default=20)
+    p.add_argument("--only", default="", help="comma list of workloads: m1_hot,m1_cold,m8_pool")
+    p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    return p.parse_args()
+
+
+class Workload:
+    """48 calls of one configuration, all inputs resident on the device."""
+
+    def __init__(self, name, abi, torch, dims, bank, ids_calls, M, rng, per_expert):
+        self.name, self.dims, self.bank, self.M = name, dims, bank, M
+        dev = bank.device
+        self.x = [torch.from_numpy(inputs.activations(rng, M, H)).to(dev) for _ in range(CALLS)]
+        self.ids = [torch.from_numpy(np.ascontiguousarray(ids_calls[c])).to(dev) for c in range(CALLS)]
+        self.w = [torch.from_numpy(inputs.router_weights(rng, M, K_TOP)).to(dev) for _ in range(CALLS)]
+        self.out = torch.empty((M, H), dtype=torch.float16, device=dev)
+        self.act = torch.empty((M * K_TOP, I), dtype=torch.float16, device=dev)
+        self.dec = abi.Decoder(dims, bank, K_TOP, max_tokens=M)
+        self.routes = [abi.alloc_route(M * K_TOP, dev) for _ in range(CALLS)]
+        self.ids_np = [np.asarray(ids_calls[c]) for c in range(CALLS)]
+        distinct = [len(np.unique(a)) for a in self.ids_np]
+        self.distinct_mean = float(np.mean(distinct))
+        self.w13_bytes = [d * per_expert["w13"] for d in distinct]
+        self.w2_bytes = [d * per_expert["w2"] for d in distinct]
+
+
+def per_expert_bytes(abi, dims):
+    L = abi.awq_moe_bank_layout_query(dims)
+    return {"w13": int(L.w2_off - L.w13_off), "w2": int(L.expert_bytes - L.w2_off)}
+
+
+def capture(torch, fn):
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        fn()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        fn()
+    torch.cuda.synchronize()
+    return g
+
+
+def time_graph(torch, g, reps, warmup):
+    """Mean ms per replay, from HIP events recorded on the replay stream."""
+    s = torch.cuda.current_stream()
+    for _ in range(warmup):
+        g.replay()
+    torch.cuda.synchronize()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    t0.record(s)
+    for _ in range(reps):
+        g.replay()
+    t1.record(s)
+    t1.synchronize()
+    return t0.elapsed_time(t1) / reps
+
+
+def measure(abi, torch, wl: Workload, steps, warmup):
+    def full():
+        for c in range(CALLS):
+            wl.dec(wl.x[c], wl.ids[c], wl.w[c], out=wl.out)
+
+    def route():
+        for c in range(CALLS):
+            abi.awq_moe_route_compact(wl.ids[c], E, out=wl.routes[c])
+
+    def w13():
+        for c in range(CALLS):
+            abi.awq_moe_w13_swiglu(wl.dims, wl.bank, wl.x[c], wl.M, K_TOP, wl.routes[c], act=wl.act)
+
+    def w2():
+        for c in range(CALLS):
+            abi.awq_moe_w2_reduce(wl.dims, wl.bank, wl.act, wl.w[c], wl.M, K_TOP, wl.routes[c], out=wl.out)
+
+    route()
+    torch.cuda.synchronize()
+    res = {}
+    for name, fn in (("layer", full), ("route", route), ("w13", w13), ("w2", w2)):
+        g = capture(torch, fn)
+        ms = time_graph(torch, g, steps, warmup)
+        res[name + "_us"] = ms * 1e3 / CALLS
+        if name == "layer":
+            res["step_ms"] = ms
+        del g
+    w13b = float(np.mean(wl.w13_bytes))
+    w2b = float(np.mean(wl.w2_bytes))
+    res.update(
+        M=wl.M, distinct_experts_per_call=wl.distinct_mean,
+        w13_bytes_per_call=w13b, w2_bytes_per_call=w2b,
+        w13_gbs=w13b / (res["w13_us"] * 1e3), w2_gbs=w2b / (res["w2_us"] * 1e3),
+        layer_gbs=(w13b + w2b) / (res["layer_us"] * 1e3),
+    )
+    for k in ("w13", "w2", "layer"):
+        res[k + "_pct_peak"] = 100.0 * res[k + "_gbs"] / HBM_PEAK_GBS
+    return res
+
+
+def recorded_traffic(kernel: str, summary: str = "pmc_traffic_m1_hot_4b.txt"):
+    """HBM bytes per launch of ``kernel`` from the committed rocprofv3 counter summary
+    (FETCH_SIZE and WRITE_SIZE, each scaled by a 1 GiB copy in the same run), or None
+    when the summary is missing or the kernel source changed since it was taken."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", summary)
+    src = os.path.join(ROOT, "awq_int4_mixture_amd", "csrc", "kernels.hip")
+    if not os.path.exists(path):
+        return None
+    h = hashlib.sha256(open(src, "rb").read()).hexdigest()[:16]
+    for line in open(path):
+        parts = [p.strip() for p in line.split("|")]
+        if len(parts) == 4 and parts[0] == "TRAFFIC" and kernel in parts[1] and parts[3] == f"source {h}":
+            return float(parts[2].split()[0])
+    return None
+
+
+def copy_ceiling(torch, nbytes=1 << 30, reps=20):
+    """Device-to-device copy of a known size: a reference read+write rate."""
+    a = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    b = torch.empty_like(a)
+    b.copy_(a)
+    torch.cuda.synchronize()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    t0.record()
+    for _ in range(reps):
+        b.copy_(a)
+    t1.record()
+    t1.synchronize()
+    ms = t0.elapsed_time(t1) / reps
+    del a, b
+    return {"bytes_moved": 2 * nbytes, "us": ms * 1e3, "gbs": 2 * nbytes / (ms * 1e6)}
+
+
+def cpu_baseline(bi, ids_calls, rng_seed, budget_s=12.0):
+    """The float64 oracle on the headline workload's calls, as many as fit in ~budget_s."""
+    from threadpoolctl import threadpool_limits
+
+    from oracle import ref as R
+    rng = inputs.call_rng(rng_seed, 77)
+    per_call = K_TOP * (409_600 + 102_400 + 204_800 + 51_200)
+    done = 0
+    with threadpool_limits(limits=1):
+        t0 = time.perf_counter()
+        while done < CALLS:
+            x = inputs.activations(rng, 1, H)
+            w = inputs.router_weights(rng, 1, K_TOP)
+            R.moe_stage(x, ids_calls[done], w, E, bi.expert)
+            done += 1
+            if time.perf_counter() - t0 > budget_s:
+                break
+        dt = time.perf_counter() - t0
+    return {"value": round(per_call * done / dt / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": f"{done} of the 48 M=1 hot-expert calls (4-byte records), float64 NumPy on one "
+                      f"thread, dequantisation of the touched experts included, {dt:.1f} s",
+            "layer_us": round(dt / done * 1e6, 1)}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); "
+              "this build has no multi-GPU path.", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    from awq_int4_mixture_amd import abi
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    torch.cuda.set_device(0)
+    only = set(filter(None, args.only.split(","))) or {"m1_hot", "m1_cold", "m8_pool"}
+
+    t_gen = time.perf_counter()
+    bi = inputs.bank_inputs(SEED, E, H, I)
+    banks = {}
+    for rb in (4, 3):
+        if rb == 4 and "m1_hot" not in only:
+            continue
+        if rb == 3 and not ({"m1_cold", "m8_pool"} & only):
+            continue
+        dims = abi.make_dims(E, H, I, rb)
+        banks[rb] = (dims, torch.from_numpy(abi.prepare_from_inputs(dims, bi)).to("cuda"))
+    t_gen = time.perf_counter() - t_gen
+
+    rng = inputs.call_rng(SEED, 1)
+    hot = inputs.hot_experts(SEED, K_TOP, E)
+    hot_calls = [hot[None, :].copy() for _ in range(CALLS)]
+    results = {}
+    stream = torch.cuda.Stream()
+    with torch.cuda.stream(stream):
+        if "m1_hot" in only:
+            dims, bank = banks[4]
+            wl = Workload("m1_hot", abi, torch, dims, bank, hot_calls, 1, rng, per_expert_bytes(abi, dims))
+            results["m1_hot"] = measure(abi, torch, wl, args.steps, args.warmup)
+        if "m1_cold" in only:
+            dims, bank = banks[3]
+            rot = inputs.rotating_ids(SEED, CALLS, K_TOP, E)
+            wl = Workload("m1_cold", abi, torch, dims, bank, [rot[c] for c in range(CALLS)], 1, rng,
+                          per_expert_bytes(abi, dims))
+            results["m1_cold"] = measure(abi, torch, wl, args.steps, args.warmup)
+        if "m8_pool" in only:
+            dims, bank = banks[3]
+            ids = [inputs.ids_shared_pool(inputs.call_rng(SEED, 300 + c), 8, K_TOP, E) for c in range(CALLS)]
+            wl = Workload("m8_pool", abi, torch, dims, bank, ids, 8, rng, per_expert_bytes(abi, dims))
+            results["m8_pool"] = measure(abi, torch, wl, args.steps, args.warmup)
+        ceiling = copy_ceiling(torch)
+
+    head = results.get("m1_hot") or next(iter(results.values()))
+    line = {
+        "metric": "MoE layer decode µs and achieved weight HBM GB/s (% of peak) at M=1 and M=8",
+        "value": round(head["layer_gbs"], 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(head["step_ms"], 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp16 x int4 -> fp32 accumulate",
+        "data": "synthetic (seeded int4 weights, fp16 scales |N(0,1)|*0.02, zeros U{0..15}, x ~ N(0,1))",
+        "config": {
+            "workload": "AWQ int4 MoE expert stage, 512 experts, hidden 2560, inter 160, top-k 10, group 32, "
+                        "M=1, 4-byte records, same 10 hot experts on all 48 calls of a graph replay",
+            "layer_us": round(head["layer_us"], 3),
+            "calls_per_step": CALLS,
+        },
+        "roofline": {
+            "bound": "hbm",
+            "kernel": "w13_swiglu_kernel<4>",
+            "achieved": round(head["w13_gbs"], 2),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(head["w13_gbs"] / HBM_PEAK_GBS, 4),
+            "traffic": recorded_traffic("w13_swiglu_kernel<4>"),
+            "algorithmic_bytes_per_launch": head["w13_bytes_per_call"],
+            "avg_launch_us": round(head["w13_us"], 3),
+        },
+        "per_config": {k: {kk: (round(vv, 4) if isinstance(vv, float) else vv) for kk, vv in v.items()}
+                       for k, v in results.items()},
+        "copy_reference": ceiling,
+        "setup_s": round(t_gen, 1),
+    }
+    if not args.no_cpu and "m1_hot" in results:
+        line["cpu_baseline"] = cpu_baseline(bi, hot_calls, SEED)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()
