@@ -22,6 +22,7 @@ OK, EINVAL, EUNSUPPORTED, ENOSPC, EHIP = 0, -1, -2, -3, -4
 MAX_TOKENS, MAX_TOPK = 8, 32
 STATUS_BAD_ID = 1
 WS_STATUS_OFFSET = 0
+WS_ACT_OFFSET = 4608
 
 EXPORTED = (
     "awq_moe_bank_layout_query", "awq_moe_prepare", "awq_moe_workspace_bytes",
@@ -67,8 +68,8 @@ def _load() -> ctypes.CDLL:
         "awq_moe_workspace_bytes": [D, I32, I32, ctypes.POINTER(ctypes.c_uint64)],
         "awq_moe_route_compact": [P, I32, I32, I32, P, P, P, P, P, V],
         "awq_moe_decode": [D, P, P, P, P, I32, I32, P, P, U64, V],
-        "awq_moe_w13_swiglu": [D, P, P, I32, I32, P, P, P, P, P, V],
-        "awq_moe_w2_reduce": [D, P, P, P, I32, I32, P, P, P, P, P, V],
+        "awq_moe_w13_swiglu": [D, P, P, P, I32, I32, P, U64, V],
+        "awq_moe_w2_reduce": [D, P, P, I32, I32, P, U64, P, V],
         "awq_moe_dequant": [D, P, I32, I32, I32, P, V],
     }
     for name, args in sig.items():
@@ -219,27 +220,40 @@ def awq_moe_decode(dims: awq_moe_dims, bank, x, topk_ids, topk_w, out=None, work
     return out
 
 
-def awq_moe_w13_swiglu(dims: awq_moe_dims, bank, x, M: int, topk: int, route: Route, act=None, stream=None):
+def alloc_workspace(dims: awq_moe_dims, max_tokens: int, topk: int, device="cuda"):
     torch = _torch()
-    if act is None:
-        act = torch.zeros((M * topk, dims.inter), dtype=torch.float16, device=x.device)
+    return torch.zeros(awq_moe_workspace_bytes(dims, max_tokens, topk), dtype=torch.uint8, device=device)
+
+
+def workspace_act(workspace, M: int, topk: int, inter: int):
+    """View of the fp16 intermediate act[M*topk][inter] (indexed by slot) inside a workspace."""
+    torch = _torch()
+    nbytes = M * topk * inter * 2
+    return workspace[WS_ACT_OFFSET:WS_ACT_OFFSET + nbytes].view(torch.float16).view(M * topk, inter)
+
+
+def awq_moe_w13_swiglu(dims: awq_moe_dims, bank, x, topk_ids, workspace=None, stream=None):
+    """Runs W13 + SwiGLU; returns the workspace holding act, the plan and the status."""
+    torch = _torch()
+    M, k = topk_ids.shape
+    if workspace is None:
+        workspace = alloc_workspace(dims, M, k, x.device)
     _check(_lib.awq_moe_w13_swiglu(
         ctypes.byref(dims), _dev(bank, torch.uint8, name="bank"), _dev(x, torch.float16, (M, dims.hidden), "x"),
-        M, topk, _dev(route.active_expert_ids, torch.int32), _dev(route.active_expert_offsets, torch.int32),
-        _dev(route.sorted_slots, torch.int32), _dev(route.num_active, torch.int32),
-        _dev(act, torch.float16, (M * topk, dims.inter), "act"), _stream(stream)), "awq_moe_w13_swiglu")
-    return act
+        _dev(topk_ids, torch.int32, (M, k), "topk_ids"), M, k,
+        _dev(workspace, torch.uint8, name="workspace"), workspace.numel(), _stream(stream)), "awq_moe_w13_swiglu")
+    return workspace
 
 
-def awq_moe_w2_reduce(dims: awq_moe_dims, bank, act, topk_w, M: int, topk: int, route: Route, out=None, stream=None):
+def awq_moe_w2_reduce(dims: awq_moe_dims, bank, topk_w, workspace, out=None, stream=None):
+    """W2 + reduction from the act and plan left in ``workspace`` by awq_moe_w13_swiglu."""
     torch = _torch()
+    M, k = topk_w.shape
     if out is None:
-        out = torch.empty((M, dims.hidden), dtype=torch.float16, device=act.device)
+        out = torch.empty((M, dims.hidden), dtype=torch.float16, device=topk_w.device)
     _check(_lib.awq_moe_w2_reduce(
-        ctypes.byref(dims), _dev(bank, torch.uint8, name="bank"),
-        _dev(act, torch.float16, (M * topk, dims.inter), "act"), _dev(topk_w, torch.float32, (M, topk), "topk_w"),
-        M, topk, _dev(route.active_expert_ids, torch.int32), _dev(route.active_expert_offsets, torch.int32),
-        _dev(route.sorted_slots, torch.int32), _dev(route.num_active, torch.int32),
+        ctypes.byref(dims), _dev(bank, torch.uint8, name="bank"), _dev(topk_w, torch.float32, (M, k), "topk_w"),
+        M, k, _dev(workspace, torch.uint8, name="workspace"), workspace.numel(),
         _dev(out, torch.float16, (M, dims.hidden), "out"), _stream(stream)), "awq_moe_w2_reduce")
     return out
 
@@ -269,8 +283,7 @@ class Decoder:
     def __init__(self, dims: awq_moe_dims, bank, topk: int, max_tokens: int = MAX_TOKENS):
         torch = _torch()
         self.dims, self.bank, self.topk = dims, bank, topk
-        self.workspace = torch.empty(awq_moe_workspace_bytes(dims, max_tokens, topk), dtype=torch.uint8,
-                                     device=bank.device)
+        self.workspace = alloc_workspace(dims, max_tokens, topk, bank.device)
 
     def __call__(self, x, topk_ids, topk_w, out=None, stream=None):
         return awq_moe_decode(self.dims, self.bank, x, topk_ids, topk_w, out=out, workspace=self.workspace,

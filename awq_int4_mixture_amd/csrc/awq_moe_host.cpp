@@ -71,20 +71,14 @@ Layout make_layout(const awq_moe_dims* d) {
   return L;
 }
 
-// Workspace: [status u32 | num_active i32 | pad] then routing arrays, then act.
-struct WsLayout {
-  uint64_t ids_off, offsets_off, slots_off, act_off, total;
-};
+// Workspace: [status u32 | pad] [routing plan] [fp16 act[n][I]].
+constexpr uint64_t kPlanOffset = 256;
+static_assert(kPlanOffset + sizeof(awq_moe::Plan) <= AWQ_MOE_WS_ACT_OFFSET, "plan overlaps act");
+static_assert(AWQ_MOE_WS_ACT_OFFSET % 256 == 0, "act must stay 256-byte aligned");
 
-WsLayout make_ws(const awq_moe_dims* d, int max_tokens, int topk) {
+uint64_t ws_total(const awq_moe_dims* d, int max_tokens, int topk) {
   const uint64_t n = (uint64_t)max_tokens * (uint64_t)topk;
-  WsLayout w;
-  w.ids_off = 256;
-  w.offsets_off = w.ids_off + pad256(n * 4);
-  w.slots_off = w.offsets_off + pad256((n + 1) * 4);
-  w.act_off = w.slots_off + pad256(n * 4);
-  w.total = w.act_off + pad256(n * (uint64_t)d->inter * 2);
-  return w;
+  return AWQ_MOE_WS_ACT_OFFSET + pad256(n * (uint64_t)d->inter * 2);
 }
 
 int check_tokens(int M, int topk) {
@@ -119,9 +113,8 @@ int hip_status(hipError_t e, const char* what) {
   return ok();
 }
 
-awq_moe::StageArgs stage_args(const awq_moe_dims* d, const void* bank, int M, int topk,
-                              const int32_t* ids, const int32_t* offsets, const int32_t* slots,
-                              const int32_t* num_active) {
+awq_moe::StageArgs stage_args(const awq_moe_dims* d, const void* bank, const int32_t* topk_ids, int M,
+                              int topk) {
   const Layout L = make_layout(d);
   awq_moe::StageArgs a;
   a.bank = static_cast<const uint8_t*>(bank);
@@ -130,15 +123,13 @@ awq_moe::StageArgs stage_args(const awq_moe_dims* d, const void* bank, int M, in
   a.w13_meta_off = L.pub.w13_meta_off;
   a.w2_off = L.pub.w2_off;
   a.w2_meta_off = L.pub.w2_meta_off;
+  a.topk_ids = topk_ids;
   a.H = d->hidden;
   a.I = d->inter;
   a.RB = d->meta_bytes;
   a.M = M;
   a.topk = topk;
-  a.active_ids = ids;
-  a.offsets = offsets;
-  a.sorted_slots = slots;
-  a.num_active = num_active;
+  a.E = d->num_experts;
   return a;
 }
 
@@ -168,7 +159,7 @@ int awq_moe_workspace_bytes(const awq_moe_dims* dims, int32_t max_tokens, int32_
   if (rc) return rc;
   if ((rc = check_tokens(max_tokens, topk))) return rc;
   if (!out) return fail(AWQ_MOE_EINVAL, "out is null");
-  *out = make_ws(dims, max_tokens, topk).total;
+  *out = ws_total(dims, max_tokens, topk);
   return ok();
 }
 
@@ -270,78 +261,80 @@ int awq_moe_route_compact(const int32_t* topk_ids, int32_t M, int32_t topk, int3
   if ((rc = check_route_ptrs(active_expert_ids, active_expert_offsets, sorted_slots, num_active))) return rc;
   if (!status || !aligned(status, 4)) return fail(AWQ_MOE_EINVAL, "status null or misaligned");
   if ((rc = check_device())) return rc;
-  return hip_status(awq_moe::launch_route_compact(topk_ids, M * topk, num_experts, active_expert_ids,
-                                                  active_expert_offsets, sorted_slots, num_active, status,
-                                                  static_cast<hipStream_t>(stream)),
+  const awq_moe::RouteOut o{active_expert_ids, active_expert_offsets, sorted_slots, num_active, status};
+  return hip_status(awq_moe::launch_route_compact(topk_ids, M * topk, num_experts, o, static_cast<hipStream_t>(stream)),
                     "route_compact launch");
 }
 
-int awq_moe_w13_swiglu(const awq_moe_dims* dims, const void* bank, const uint16_t* x, int32_t M,
-                       int32_t topk, const int32_t* active_expert_ids, const int32_t* active_expert_offsets,
-                       const int32_t* sorted_slots, const int32_t* num_active, uint16_t* act, void* stream) {
+int check_stage(const awq_moe_dims* dims, const void* bank, int32_t M, int32_t topk, const void* workspace,
+                uint64_t workspace_bytes) {
   int rc = check_dims(dims);
   if (rc) return rc;
   if ((rc = check_tokens(M, topk))) return rc;
   if (!bank || !aligned(bank, 256)) return fail(AWQ_MOE_EINVAL, "bank null or not 256-byte aligned");
-  if (!x || !aligned(x, 16)) return fail(AWQ_MOE_EINVAL, "x null or not 16-byte aligned");
-  if (!act || !aligned(act, 16)) return fail(AWQ_MOE_EINVAL, "act null or not 16-byte aligned");
-  if ((rc = check_route_ptrs(active_expert_ids, active_expert_offsets, sorted_slots, num_active))) return rc;
-  if ((rc = check_device())) return rc;
-  const awq_moe::StageArgs a = stage_args(dims, bank, M, topk, active_expert_ids, active_expert_offsets,
-                                          sorted_slots, num_active);
-  return hip_status(awq_moe::launch_w13_swiglu(a, x, act, static_cast<hipStream_t>(stream)), "w13 launch");
+  if (!workspace || !aligned(workspace, 256)) return fail(AWQ_MOE_EINVAL, "workspace null or not 256-byte aligned");
+  const uint64_t need = ws_total(dims, M, topk);
+  if (workspace_bytes < need)
+    return fail(AWQ_MOE_ENOSPC, "workspace_bytes %llu < %llu", (unsigned long long)workspace_bytes,
+                (unsigned long long)need);
+  return AWQ_MOE_OK;
 }
 
-int awq_moe_w2_reduce(const awq_moe_dims* dims, const void* bank, const uint16_t* act, const float* topk_w,
-                      int32_t M, int32_t topk, const int32_t* active_expert_ids,
-                      const int32_t* active_expert_offsets, const int32_t* sorted_slots,
-                      const int32_t* num_active, uint16_t* out, void* stream) {
-  int rc = check_dims(dims);
+struct WsPtrs {
+  uint32_t* status;
+  awq_moe::Plan* plan;
+  uint16_t* act;
+};
+
+WsPtrs ws_ptrs(void* workspace) {
+  uint8_t* ws = static_cast<uint8_t*>(workspace);
+  return WsPtrs{reinterpret_cast<uint32_t*>(ws + AWQ_MOE_WS_STATUS_OFFSET),
+                reinterpret_cast<awq_moe::Plan*>(ws + kPlanOffset),
+                reinterpret_cast<uint16_t*>(ws + AWQ_MOE_WS_ACT_OFFSET)};
+}
+
+int awq_moe_w13_swiglu(const awq_moe_dims* dims, const void* bank, const uint16_t* x, const int32_t* topk_ids,
+                       int32_t M, int32_t topk, void* workspace, uint64_t workspace_bytes, void* stream) {
+  int rc = check_stage(dims, bank, M, topk, workspace, workspace_bytes);
   if (rc) return rc;
-  if ((rc = check_tokens(M, topk))) return rc;
-  if (!bank || !aligned(bank, 256)) return fail(AWQ_MOE_EINVAL, "bank null or not 256-byte aligned");
-  if (!act || !aligned(act, 16)) return fail(AWQ_MOE_EINVAL, "act null or not 16-byte aligned");
+  if (!x || !aligned(x, 16)) return fail(AWQ_MOE_EINVAL, "x null or not 16-byte aligned");
+  if (!topk_ids || !aligned(topk_ids, 4)) return fail(AWQ_MOE_EINVAL, "topk_ids null or misaligned");
+  if ((rc = check_device())) return rc;
+  const WsPtrs w = ws_ptrs(workspace);
+  return hip_status(awq_moe::launch_w13_swiglu(stage_args(dims, bank, topk_ids, M, topk), x, w.act, w.plan,
+                                               w.status, static_cast<hipStream_t>(stream)),
+                    "w13 launch");
+}
+
+int awq_moe_w2_reduce(const awq_moe_dims* dims, const void* bank, const float* topk_w, int32_t M, int32_t topk,
+                      const void* workspace, uint64_t workspace_bytes, uint16_t* out, void* stream) {
+  int rc = check_stage(dims, bank, M, topk, workspace, workspace_bytes);
+  if (rc) return rc;
   if (!topk_w || !aligned(topk_w, 4)) return fail(AWQ_MOE_EINVAL, "topk_w null or misaligned");
   if (!out || !aligned(out, 16)) return fail(AWQ_MOE_EINVAL, "out null or not 16-byte aligned");
-  if ((rc = check_route_ptrs(active_expert_ids, active_expert_offsets, sorted_slots, num_active))) return rc;
   if ((rc = check_device())) return rc;
-  const awq_moe::StageArgs a = stage_args(dims, bank, M, topk, active_expert_ids, active_expert_offsets,
-                                          sorted_slots, num_active);
-  return hip_status(awq_moe::launch_w2_reduce(a, act, topk_w, out, static_cast<hipStream_t>(stream)),
+  const WsPtrs w = ws_ptrs(const_cast<void*>(workspace));
+  return hip_status(awq_moe::launch_w2_reduce(stage_args(dims, bank, nullptr, M, topk), w.act, topk_w, w.plan, out,
+                                              static_cast<hipStream_t>(stream)),
                     "w2 launch");
 }
 
 int awq_moe_decode(const awq_moe_dims* dims, const void* bank, const uint16_t* x, const int32_t* topk_ids,
                    const float* topk_w, int32_t M, int32_t topk, uint16_t* out, void* workspace,
                    uint64_t workspace_bytes, void* stream) {
-  int rc = check_dims(dims);
+  int rc = check_stage(dims, bank, M, topk, workspace, workspace_bytes);
   if (rc) return rc;
-  if ((rc = check_tokens(M, topk))) return rc;
-  if (!bank || !aligned(bank, 256)) return fail(AWQ_MOE_EINVAL, "bank null or not 256-byte aligned");
   if (!x || !aligned(x, 16)) return fail(AWQ_MOE_EINVAL, "x null or not 16-byte aligned");
   if (!topk_ids || !aligned(topk_ids, 4)) return fail(AWQ_MOE_EINVAL, "topk_ids null or misaligned");
   if (!topk_w || !aligned(topk_w, 4)) return fail(AWQ_MOE_EINVAL, "topk_w null or misaligned");
   if (!out || !aligned(out, 16)) return fail(AWQ_MOE_EINVAL, "out null or not 16-byte aligned");
-  if (!workspace || !aligned(workspace, 256)) return fail(AWQ_MOE_EINVAL, "workspace null or not 256-byte aligned");
-  const WsLayout W = make_ws(dims, M, topk);
-  if (workspace_bytes < W.total)
-    return fail(AWQ_MOE_ENOSPC, "workspace_bytes %llu < %llu", (unsigned long long)workspace_bytes,
-                (unsigned long long)W.total);
   if ((rc = check_device())) return rc;
-  uint8_t* ws = static_cast<uint8_t*>(workspace);
-  uint32_t* status = reinterpret_cast<uint32_t*>(ws + AWQ_MOE_WS_STATUS_OFFSET);
-  int32_t* num_active = reinterpret_cast<int32_t*>(ws + 4);
-  int32_t* ids = reinterpret_cast<int32_t*>(ws + W.ids_off);
-  int32_t* offsets = reinterpret_cast<int32_t*>(ws + W.offsets_off);
-  int32_t* slots = reinterpret_cast<int32_t*>(ws + W.slots_off);
-  uint16_t* act = reinterpret_cast<uint16_t*>(ws + W.act_off);
+  const WsPtrs w = ws_ptrs(workspace);
   hipStream_t s = static_cast<hipStream_t>(stream);
-  hipError_t e = awq_moe::launch_route_compact(topk_ids, M * topk, dims->num_experts, ids, offsets, slots,
-                                               num_active, status, s);
-  if (e != hipSuccess) return hip_status(e, "route_compact launch");
-  const awq_moe::StageArgs a = stage_args(dims, bank, M, topk, ids, offsets, slots, num_active);
-  if ((e = awq_moe::launch_w13_swiglu(a, x, act, s)) != hipSuccess) return hip_status(e, "w13 launch");
-  return hip_status(awq_moe::launch_w2_reduce(a, act, topk_w, out, s), "w2 launch");
+  const awq_moe::StageArgs a = stage_args(dims, bank, topk_ids, M, topk);
+  hipError_t e = awq_moe::launch_w13_swiglu(a, x, w.act, w.plan, w.status, s);
+  if (e != hipSuccess) return hip_status(e, "w13 launch");
+  return hip_status(awq_moe::launch_w2_reduce(a, w.act, topk_w, w.plan, out, s), "w2 launch");
 }
 
 int awq_moe_dequant(const awq_moe_dims* dims, const void* bank, int32_t expert_begin, int32_t expert_count,

@@ -129,227 +129,486 @@ __device__ __forceinline__ float silu_mul(float g, float u) {
 }
 
 // ---------------------------------------------------------------------------
-// routing compaction: one workgroup, one thread per slot (n <= 256)
+// routing compaction of n <= 256 slots inside one workgroup (LDS only).
+// Canonical order: experts ascending, rows of a segment by ascending slot,
+// invalid slots (ids outside [0, E)) after all valid ones in slot order.
+// Every stage kernel runs this in its prologue, so the only global-memory
+// round trip before the weight loads is the read of the n routed ids.
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void route_compact_kernel(
-    const int32_t* __restrict__ ids, int n, int E, int32_t* __restrict__ active_ids,
-    int32_t* __restrict__ offsets, int32_t* __restrict__ sorted_slots,
-    int32_t* __restrict__ num_active, uint32_t* __restrict__ status) {
-  __shared__ int key[256];    // id of a valid slot, -1 for an invalid one
-  __shared__ int first[256];  // 1 when the slot is the first valid slot of its id
-  const int s = threadIdx.x;
-  int id = -1;
-  if (s < n) {
-    const int v = ids[s];
-    id = (v >= 0 && v < E) ? v : -1;
-    key[s] = id;
-  }
-  __syncthreads();
-  int before = 0, inv_before = 0, nvalid = 0, is_first = 1;
-  for (int s2 = 0; s2 < n; ++s2) {
-    const int k2 = key[s2];
-    nvalid += (k2 >= 0);
-    if (id >= 0) {
-      before += (k2 >= 0) && (k2 < id || (k2 == id && s2 < s));
-      if (k2 == id && s2 < s) is_first = 0;
-    } else {
-      inv_before += (k2 < 0) && (s2 < s);
+constexpr int kMaxSlots = AWQ_MOE_KMAX_SLOTS;
+constexpr int kNoKey = 0x7FFFFFFF;
+
+struct __attribute__((aligned(16))) Compact {
+  int key[kMaxSlots + 4];       // valid id, -1 invalid, -2 padding
+  int firstkey[kMaxSlots + 4];  // id when the slot is its id's first valid slot, else kNoKey
+  int rank[kMaxSlots];          // slot -> row
+  int sorted[kMaxSlots];        // row -> slot
+  int seg_e[kMaxSlots];         // segment -> expert
+  int seg_off[kMaxSlots + 1];   // segment -> first row; [num_active] = number of valid slots
+  int num_active, nvalid;
+};
+
+__device__ void block_compact(const int32_t* __restrict__ ids, int n, int E, Compact& C) {
+  const int t = threadIdx.x, bd = blockDim.x;
+  const int n4 = (n + 3) & ~3;
+  for (int s = t; s < n4; s += bd) {
+    int k = -2;
+    if (s < n) {
+      const int v = ids[s];
+      k = (v >= 0 && v < E) ? v : -1;
     }
+    C.key[s] = k;
+    C.firstkey[s] = kNoKey;
   }
-  if (s < n) first[s] = (id >= 0) && is_first;
   __syncthreads();
-  int seg = 0, nseg = 0;
-  for (int s2 = 0; s2 < n; ++s2) {
-    const int f = first[s2];
-    nseg += f;
-    seg += f && (key[s2] < id);
-  }
-  if (s < n) {
-    if (id >= 0) {
-      sorted_slots[before] = s;
-      if (is_first) {
-        active_ids[seg] = id;
-        offsets[seg] = before;
+  for (int s = t; s < n; s += bd) {
+    const int id = C.key[s];
+    int before = 0, inv_before = 0, nvalid = 0, dup_before = 0;
+    for (int s2 = 0; s2 < n4; s2 += 4) {
+      const int4 k4 = *reinterpret_cast<const int4*>(&C.key[s2]);
+      const int kk[4] = {k4.x, k4.y, k4.z, k4.w};
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int k2 = kk[q];
+        const bool earlier = (s2 + q) < s;
+        nvalid += (k2 >= 0);
+        before += (k2 >= 0) & ((k2 < id) | ((k2 == id) & earlier));
+        dup_before += (k2 == id) & earlier;
+        inv_before += (k2 == -1) & earlier;
       }
-    } else {
-      sorted_slots[nvalid + inv_before] = s;
     }
-    if (s >= nseg) active_ids[s] = -1;
+    const int r = (id >= 0) ? before : nvalid + inv_before;
+    C.rank[s] = r;
+    C.sorted[r] = s;
+    if (id >= 0 && dup_before == 0) C.firstkey[s] = id;
+    if (s == 0) C.nvalid = nvalid;
   }
-  for (int i = s; i <= n; i += blockDim.x)
-    if (i >= nseg) offsets[i] = nvalid;
-  if (s == 0) {
-    *num_active = nseg;
-    *status = (nvalid == n) ? 0u : 1u;
+  __syncthreads();
+  for (int s = t; s < n; s += bd) {
+    const int fk = C.firstkey[s];
+    int below = 0, nseg = 0;
+    for (int s2 = 0; s2 < n4; s2 += 4) {
+      const int4 f4 = *reinterpret_cast<const int4*>(&C.firstkey[s2]);
+      const int ff[4] = {f4.x, f4.y, f4.z, f4.w};
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        below += ff[q] < fk;
+        nseg += ff[q] != kNoKey;
+      }
+    }
+    if (fk != kNoKey) {
+      C.seg_e[below] = fk;
+      C.seg_off[below] = C.rank[s];
+    }
+    if (s == 0) {
+      C.num_active = nseg;
+      C.seg_off[nseg] = C.nvalid;
+    }
+  }
+  __syncthreads();
+}
+
+// Write the compacted arrays of the workgroup to global memory.
+__device__ void store_route(const Compact& C, int n, const RouteOut& o) {
+  const int t = threadIdx.x, bd = blockDim.x;
+  const int A = C.num_active, V = C.nvalid;
+  for (int i = t; i < n; i += bd) {
+    o.sorted_slots[i] = C.sorted[i];
+    o.active_ids[i] = i < A ? C.seg_e[i] : -1;
+  }
+  for (int i = t; i <= n; i += bd) o.offsets[i] = i <= A ? C.seg_off[i] : V;
+  if (t == 0) {
+    *o.num_active = A;
+    *o.status = (V == n) ? 0u : AWQ_MOE_STATUS_BAD_ID_BIT;
+  }
+}
+
+__global__ __launch_bounds__(256) void route_compact_kernel(const int32_t* __restrict__ ids, int n, int E,
+                                                            RouteOut o) {
+  __shared__ Compact C;
+  block_compact(ids, n, E, C);
+  store_route(C, n, o);
+}
+
+// ---------------------------------------------------------------------------
+// Segment discovery inside the stage kernels, without sorting. Each wave
+// holds the routed ids of up to 256 slots in registers (slot c*64 + lane in
+// chunk c); a ballot gives the 64-bit mask of slots that share an id, so the
+// rows of a segment come out in ascending slot order for free.
+// ---------------------------------------------------------------------------
+struct SlotIds {
+  int v[4];  // id of slot c*64 + lane, -1 when invalid or past n
+};
+
+__device__ __forceinline__ SlotIds load_slot_ids(const int32_t* __restrict__ ids, int n, int E) {
+  SlotIds r;
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    const int l = c * 64 + lane;
+    int v = -1;
+    if (l < n) {
+      v = ids[l];
+      if (v < 0 || v >= E) v = -1;
+    }
+    r.v[c] = v;
+  }
+  return r;
+}
+
+__device__ __forceinline__ void same_id_masks(const SlotIds& ids, int id, int n, uint64_t (&m)[4]) {
+#pragma unroll
+  for (int c = 0; c < 4; ++c) m[c] = (c * 64 < n) ? __ballot(ids.v[c] == id) : 0ull;
+}
+
+// Pop the lowest slot of a 256-bit mask (-1 when empty). Uniform.
+__device__ __forceinline__ int pop_slot(uint64_t (&m)[4]) {
+  int res = -1;
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    if (res < 0 && m[c] != 0ull) {
+      res = c * 64 + __builtin_ctzll(m[c]);
+      m[c] &= m[c] - 1;
+    }
+  }
+  return res;
+}
+
+// ---------------------------------------------------------------------------
+// The routing plan for W2, built by one workgroup of the W13 launch while the
+// other workgroups stream W13. All phases are parallel over slots:
+//  1. insert every valid slot's expert into an LDS hash table (open
+//     addressing, atomicCAS), keeping the lowest slot and the count per expert;
+//  2. wave 0 numbers the segments in order of their lowest slot (ballots) and
+//     turns the counts into offsets (wave prefix sums);
+//  3. every slot takes a place in its segment's slot list (atomic fill; the
+//     order inside a segment does not change any result, since every slot is
+//     computed independently) and ranks itself inside its token by
+//     (expert, slot), which fixes the order of the token's final sum.
+// ---------------------------------------------------------------------------
+constexpr int kHashBits = 9;
+constexpr int kHash = 1 << kHashBits;  // > kMaxSlots, so probing always ends
+static_assert(kHash > kMaxSlots, "hash table must exceed the slot count");
+
+struct PlanLds {
+  int tab_key[kHash];   // expert id, -1 empty
+  int tab_min[kHash];   // lowest slot of the expert; then its segment index
+  int tab_cnt[kHash];   // slots of the expert
+  int tab_fill[kHash];  // placement counter
+  int entry[kMaxSlots];  // slot -> table entry, -1 invalid
+  int key[kMaxSlots];    // slot -> expert id, -1 invalid
+  int seg_off[kMaxSlots + 1];
+};
+
+__device__ __forceinline__ int hash_slot(int k) {
+  return (int)(((uint32_t)k * 2654435761u) >> (32 - kHashBits));
+}
+
+__device__ __forceinline__ int wave_inclusive_sum(int v) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int u = __shfl_up(v, o);
+    if (lane >= o) v += u;
+  }
+  return v;
+}
+
+__device__ void build_plan(const int32_t* __restrict__ topk_ids, int M, int topk, int E, Plan* __restrict__ plan,
+                           uint32_t* __restrict__ status, PlanLds& P) {
+  const int n = M * topk;
+  const int t = threadIdx.x, lane = t & 63, bd = blockDim.x;
+  for (int i = t; i < kHash; i += bd) {
+    P.tab_key[i] = -1;
+    P.tab_min[i] = 0x7FFFFFFF;
+    P.tab_cnt[i] = 0;
+    P.tab_fill[i] = 0;
+  }
+  __syncthreads();
+  int bad = 0;
+  for (int s = t; s < n; s += bd) {
+    const int v = topk_ids[s];
+    const int k = (v >= 0 && v < E) ? v : -1;
+    P.key[s] = k;
+    int h = -1;
+    if (k >= 0) {
+      h = hash_slot(k);
+      for (;;) {
+        const int old = atomicCAS(&P.tab_key[h], -1, k);
+        if (old == -1 || old == k) break;
+        h = (h + 1) & (kHash - 1);
+      }
+      atomicMin(&P.tab_min[h], s);
+      atomicAdd(&P.tab_cnt[h], 1);
+    } else {
+      bad = 1;
+    }
+    P.entry[s] = h;
+  }
+  bad = __syncthreads_or(bad);
+  if (t == 0 && status != nullptr) *status = bad ? AWQ_MOE_STATUS_BAD_ID_BIT : 0u;
+  if (t < 64) {
+    int nseg = 0, off = 0;
+    for (int c = 0; c * 64 < n; ++c) {
+      const int sl = c * 64 + lane;
+      const int h = sl < n ? P.entry[sl] : -1;
+      const bool leader = h >= 0 && P.tab_min[h] == sl;
+      const uint64_t lm = __ballot(leader);
+      const int cnt = leader ? P.tab_cnt[h] : 0;
+      const int incl = wave_inclusive_sum(cnt);
+      if (leader) {
+        const int seg = nseg + (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(lm >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)lm, 0));
+        const int o = off + incl - cnt;
+        P.tab_min[h] = seg;  // from here on: the expert's segment index
+        P.seg_off[seg] = o;
+        plan->seg_off[seg] = o;
+        plan->seg_e[seg] = P.key[sl];
+      }
+      nseg += __builtin_popcountll(lm);
+      off += __shfl(incl, 63);
+    }
+    if (lane == 0) {
+      P.seg_off[nseg] = off;
+      plan->seg_off[nseg] = off;
+      plan->num_segments = nseg;
+    }
+  }
+  __syncthreads();
+  for (int s = t; s < n; s += bd) {
+    const int h = P.entry[s];
+    const int tok = s / topk, j = s - tok * topk, base = tok * topk;
+    if (h >= 0) {
+      const int pos = P.seg_off[P.tab_min[h]] + atomicAdd(&P.tab_fill[h], 1);
+      plan->seg_slots[pos] = s;
+      const int id = P.key[s];
+      int r = 0;
+      for (int j2 = 0; j2 < topk; ++j2) {
+        const int k2 = P.key[base + j2];
+        r += (k2 >= 0) & ((k2 < id) | ((k2 == id) & (j2 < j)));
+      }
+      plan->order[base + r] = s;
+    }
+    if (j == 0) {
+      int c = 0;
+      for (int j2 = 0; j2 < topk; ++j2) c += P.key[base + j2] >= 0;
+      plan->cnt[tok] = c;
+    }
   }
 }
 
 // ---------------------------------------------------------------------------
-// W13 + SwiGLU: grid (2I/16 column tiles, n segment slots); one workgroup
-// streams one 16-column tile of one active expert over all of K once and
-// applies it to every row of the segment.
+// W13 + SwiGLU: grid (2I/16 column tiles, 1 + n). Row 0 of the grid builds
+// the routing plan (tile 0 only). The workgroup of slot s = blockIdx.y - 1
+// works only when s is the lowest slot routed to its expert: it streams one
+// 16-column tile of that expert over all of K once and applies it to every
+// slot routed to the expert (a multi-row segment). act is indexed by slot.
 // ---------------------------------------------------------------------------
 template <int RB>
-__global__ __launch_bounds__(1024) void w13_swiglu_kernel(
-    const uint8_t* __restrict__ bank, uint64_t expert_bytes, uint64_t w13_off,
-    uint64_t w13_meta_off, int H, int I, const uint16_t* __restrict__ x, int topk,
-    const int32_t* __restrict__ active_ids, const int32_t* __restrict__ offsets,
-    const int32_t* __restrict__ sorted_slots, const int32_t* __restrict__ num_active,
-    uint16_t* __restrict__ act) {
+__global__ __launch_bounds__(1024) void w13_swiglu_kernel(StageArgs a, const uint16_t* __restrict__ x,
+                                                          uint16_t* __restrict__ act, Plan* __restrict__ plan,
+                                                          uint32_t* __restrict__ status) {
   constexpr int R = 4;  // rows per pass
   __shared__ float red[16][R][16];  // [wave][row][column]
-  const int seg = blockIdx.y;
-  if (seg >= *num_active) return;
+  __shared__ PlanLds plan_lds;
+  const int n = a.M * a.topk;
   const int nt = blockIdx.x;
-  const int e = active_ids[seg];
-  const int r_begin = offsets[seg], r_end = offsets[seg + 1];
-  const int G = H >> 5;
-  const int L = 4 * G;
+  if (blockIdx.y == 0) {
+    if (nt == 0) build_plan(a.topk_ids, a.M, a.topk, a.E, plan, status, plan_lds);
+    return;
+  }
+  const int s = blockIdx.y - 1;
   const int t = threadIdx.x;
   const int lane = t & 63, wave = t >> 6, nwaves = blockDim.x >> 6;
+  const int my = a.topk_ids[s];
+  const SlotIds ids = load_slot_ids(a.topk_ids, n, a.E);
+  if (my < 0 || my >= a.E) return;
+  uint64_t rows[4];
+  same_id_masks(ids, my, n, rows);
+  {
+    uint64_t probe[4] = {rows[0], rows[1], rows[2], rows[3]};
+    if (pop_slot(probe) != s) return;  // another slot leads this expert
+  }
+  const int H = a.H, I = a.I, topk = a.topk;
+  const int G = H >> 5;
+  const int L = 4 * G;
   const bool active = t < L;
   const int g = t >> 2;
 
-  const uint8_t* blk = bank + (uint64_t)e * expert_bytes;
+  const uint8_t* blk = a.bank + (uint64_t)my * a.expert_bytes;
   uint4 w[4];
   Records<RB> rec;
   if (active) {
-    const uint8_t* units = blk + w13_off + (uint64_t)nt * 256u * G;
+    const uint8_t* units = blk + a.w13_off + (uint64_t)nt * 256u * G;
 #pragma unroll
     for (int j = 0; j < 4; ++j) w[j] = *reinterpret_cast<const uint4*>(units + ((uint64_t)j * L + t) * 16u);
-    rec = load_records<RB>(blk + w13_meta_off + (uint64_t)nt * 16u * G * RB + (uint64_t)t * 4u * RB);
+    rec = load_records<RB>(blk + a.w13_meta_off + (uint64_t)nt * 16u * G * RB + (uint64_t)t * 4u * RB);
   }
 
-  for (int r0 = r_begin; r0 < r_end; r0 += R) {
+  for (;;) {
+    int slot[R];
+    int rowsn = 0;
+#pragma unroll
+    for (int rr = 0; rr < R; ++rr) {
+      slot[rr] = pop_slot(rows);
+      rowsn += slot[rr] >= 0;
+    }
+    if (rowsn == 0) break;
     float part[R][4];
 #pragma unroll
     for (int rr = 0; rr < R; ++rr) {
 #pragma unroll
       for (int j = 0; j < 4; ++j) part[rr][j] = 0.f;
-      if (active && r0 + rr < r_end) {
-        const int tok = sorted_slots[r0 + rr] / topk;
-        const Act32 a = load_act32(x + (uint64_t)tok * H + 32 * g);
-        float S, C;
-        group_sums(a, S, C);
+      if (active && rr < rowsn) {
+        const int tok = slot[rr] / topk;
+        const Act32 av = load_act32(x + (uint64_t)tok * H + 32 * g);
+        float S, Cs;
+        group_sums(av, S, Cs);
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          const float acc = unit_dot(w[j], a);
-          part[rr][j] = rec.s[j] * (acc - fmaf(rec.z[j], S, C));
+          const float acc = unit_dot(w[j], av);
+          part[rr][j] = rec.s[j] * (acc - fmaf(rec.z[j], S, Cs));
         }
       }
     }
     // reduce over the 16 groups of this wave: lanes with equal (lane & 3)
 #pragma unroll
-    for (int rr = 0; rr < R; ++rr)
+    for (int rr = 0; rr < R; ++rr) {
+      if (rr < rowsn) {
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        float v = part[rr][j];
-        v += __shfl_xor(v, 4);
-        v += __shfl_xor(v, 8);
-        v += __shfl_xor(v, 16);
-        v += __shfl_xor(v, 32);
-        part[rr][j] = v;
+        for (int j = 0; j < 4; ++j) {
+          float v = part[rr][j];
+          v += __shfl_xor(v, 4);
+          v += __shfl_xor(v, 8);
+          v += __shfl_xor(v, 16);
+          v += __shfl_xor(v, 32);
+          if (lane < 4) red[wave][rr][4 * lane + j] = v;
+        }
       }
-    if (lane < 4) {
-#pragma unroll
-      for (int rr = 0; rr < R; ++rr)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) red[wave][rr][4 * lane + j] = part[rr][j];
     }
     __syncthreads();
-    if (t < 16 * R) {
+    if (t < 16 * R) {  // exactly wave 0
       const int col = t & 15, rr = t >> 4;
       float h = 0.f;
       for (int wv = 0; wv < nwaves; ++wv) h += red[wv][rr][col];
       const float other = __shfl_xor(h, 1);  // partner column: gate <-> up
-      if (!(col & 1) && r0 + rr < r_end) {
+      int sl = -1;
+#pragma unroll
+      for (int q = 0; q < R; ++q)
+        if (q == rr) sl = slot[q];
+      if (!(col & 1) && rr < rowsn) {
         const float v = silu_mul(h, other);
-        act[(uint64_t)(r0 + rr) * I + nt * 8 + (col >> 1)] = __builtin_bit_cast(uint16_t, (_Float16)v);
+        act[(uint64_t)sl * I + nt * 8 + (col >> 1)] = __builtin_bit_cast(uint16_t, (_Float16)v);
       }
     }
+    if (rowsn < R) break;
     __syncthreads();
   }
 }
 
 // ---------------------------------------------------------------------------
-// W2 + router-weighted reduction: grid (H/8 column tiles); one workgroup owns
-// 8 output columns for all tokens and walks every active segment, so a
-// token's sum over its experts never leaves the workgroup.
+// W2 + router-weighted reduction: grid (H/8 column tiles). One workgroup owns
+// 8 output columns for all tokens. It loads the routing plan in one round
+// trip; lane groups stream each segment's W2 tile once and apply it to every
+// slot of the segment; the K groups of a slot are summed by shuffles into one
+// partial per slot; each token then sums its slots' partials in ascending
+// expert order (ties by slot), so the result depends only on the set of
+// (expert, weight) pairs of the token.
+// Lanes: slot group sl (SS of them) x column quad (2) x group gp (GP, the
+// power of two >= I/32; lanes with gp >= I/32 idle at the loads).
 // ---------------------------------------------------------------------------
 template <int RB>
-__global__ __launch_bounds__(512) void w2_reduce_kernel(
-    const uint8_t* __restrict__ bank, uint64_t expert_bytes, uint64_t w2_off,
-    uint64_t w2_meta_off, int H, int I, const uint16_t* __restrict__ act,
-    const float* __restrict__ topk_w, int M, int topk, int SS,
-    const int32_t* __restrict__ active_ids, const int32_t* __restrict__ offsets,
-    const int32_t* __restrict__ sorted_slots, const int32_t* __restrict__ num_active,
-    uint16_t* __restrict__ out) {
-  extern __shared__ float red[];  // [M][8][SS*G2] then [M][8][G2]
+__global__ __launch_bounds__(512) void w2_reduce_kernel(StageArgs a, const uint16_t* __restrict__ act,
+                                                        const float* __restrict__ topk_w,
+                                                        const Plan* __restrict__ plan, int SS, int GP,
+                                                        uint16_t* __restrict__ out) {
+  constexpr int R = 4;  // rows per pass
+  __shared__ int seg_e[kMaxSlots];
+  __shared__ int seg_off[kMaxSlots + 1];
+  __shared__ int seg_slots[kMaxSlots];
+  __shared__ int order[kMaxSlots];
+  __shared__ float wts[kMaxSlots];
+  __shared__ float ybuf[kMaxSlots][8];
+  __shared__ int cnt[AWQ_MOE_KMAX_TOKENS];
+  __shared__ int nseg_s;
+  const int M = a.M, topk = a.topk, H = a.H, I = a.I;
+  const int n = M * topk;
   const int nt = blockIdx.x;
-  const int G2 = I >> 5;
-  const int L2 = 2 * G2;
   const int t = threadIdx.x;
-  const int sl = t / L2, tl = t - sl * L2;
-  const int g = tl >> 1, quad = tl & 1;
-  const int nseg = *num_active;
 
-  float acc[AWQ_MOE_KMAX_TOKENS][4];
-#pragma unroll
-  for (int tt = 0; tt < AWQ_MOE_KMAX_TOKENS; ++tt)
-#pragma unroll
-    for (int j = 0; j < 4; ++j) acc[tt][j] = 0.f;
+  for (int i = t; i < n; i += blockDim.x) {
+    seg_e[i] = plan->seg_e[i];
+    seg_off[i] = plan->seg_off[i];
+    seg_slots[i] = plan->seg_slots[i];
+    order[i] = plan->order[i];
+    wts[i] = topk_w[i];
+  }
+  if (t == 0) {
+    seg_off[n] = plan->seg_off[n];
+    nseg_s = plan->num_segments;
+  }
+  if (t < M) cnt[t] = plan->cnt[t];
+  __syncthreads();
 
+  const int G2 = I >> 5;
+  const int L2p = 2 * GP;
+  const int sl = t / L2p, tl = t - sl * L2p;
+  const int quad = tl / GP, gp = tl - quad * GP;
+  const int nseg = nseg_s;
+  const bool loader = (sl < SS) && (gp < G2);
   if (sl < SS) {
     for (int seg = sl; seg < nseg; seg += SS) {
-      const int e = active_ids[seg];
-      const uint8_t* blk = bank + (uint64_t)e * expert_bytes;
-      const uint8_t* units = blk + w2_off + (uint64_t)nt * 128u * G2;
+      const int e = seg_e[seg];
+      const int r_end = seg_off[seg + 1];
       uint4 w[4];
+      Records<RB> rec;
+      if (loader) {
+        const uint8_t* blk = a.bank + (uint64_t)e * a.expert_bytes;
+        const int tli = 2 * gp + quad;  // lane of the bank layout
+        const uint8_t* units = blk + a.w2_off + (uint64_t)nt * 128u * G2;
 #pragma unroll
-      for (int j = 0; j < 4; ++j) w[j] = *reinterpret_cast<const uint4*>(units + ((uint64_t)j * L2 + tl) * 16u);
-      const Records<RB> rec =
-          load_records<RB>(blk + w2_meta_off + (uint64_t)nt * 8u * G2 * RB + (uint64_t)tl * 4u * RB);
-      const int r_end = offsets[seg + 1];
-      for (int r = offsets[seg]; r < r_end; ++r) {
-        const int slot = sorted_slots[r];
-        const int tok = slot / topk;
-        const float wr = topk_w[slot];
-        const Act32 a = load_act32(act + (uint64_t)r * I + 32 * g);
-        float S, C;
-        group_sums(a, S, C);
+        for (int j = 0; j < 4; ++j) w[j] = *reinterpret_cast<const uint4*>(units + ((uint64_t)j * (2 * G2) + tli) * 16u);
+        rec = load_records<RB>(blk + a.w2_meta_off + (uint64_t)nt * 8u * G2 * RB + (uint64_t)tli * 4u * RB);
+      }
+      for (int r0 = seg_off[seg]; r0 < r_end; r0 += R) {
+        const int rows = min(R, r_end - r0);
+        Act32 av[R];
+        int slot[R];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const float y = rec.s[j] * (unit_dot(w[j], a) - fmaf(rec.z[j], S, C));
+        for (int rr = 0; rr < R; ++rr) {
+          slot[rr] = rr < rows ? seg_slots[r0 + rr] : 0;
+          if (loader && rr < rows) av[rr] = load_act32(act + (uint64_t)slot[rr] * I + 32 * gp);
+        }
 #pragma unroll
-          for (int tt = 0; tt < AWQ_MOE_KMAX_TOKENS; ++tt)
-            if (tt == tok) acc[tt][j] = fmaf(wr, y, acc[tt][j]);
+        for (int rr = 0; rr < R; ++rr) {
+          if (rr < rows) {
+            float y[4] = {0.f, 0.f, 0.f, 0.f};
+            if (loader) {
+              float S, Cs;
+              group_sums(av[rr], S, Cs);
+#pragma unroll
+              for (int j = 0; j < 4; ++j) y[j] = rec.s[j] * (unit_dot(w[j], av[rr]) - fmaf(rec.z[j], S, Cs));
+            }
+            for (int o = 1; o < GP; o <<= 1)
+#pragma unroll
+              for (int j = 0; j < 4; ++j) y[j] += __shfl_xor(y[j], o);
+            if (gp == 0) {
+#pragma unroll
+              for (int j = 0; j < 4; ++j) ybuf[slot[rr]][4 * quad + j] = y[j];
+            }
+          }
         }
       }
     }
   }
-  // reduction over (segment slot, group) in a fixed order
-  const int P = SS * G2;
-  float* red2 = red + (size_t)M * 8 * P;
-  if (sl < SS) {
-#pragma unroll
-    for (int tt = 0; tt < AWQ_MOE_KMAX_TOKENS; ++tt)
-      if (tt < M) {
-#pragma unroll
-        for (int j = 0; j < 4; ++j) red[((size_t)tt * 8 + 4 * quad + j) * P + sl * G2 + g] = acc[tt][j];
-      }
-  }
-  __syncthreads();
-  for (int i = t; i < M * 8 * G2; i += blockDim.x) {
-    const int gg = i % G2, tc = i / G2;  // tc = token*8 + column
-    float v = 0.f;
-    for (int s2 = 0; s2 < SS; ++s2) v += red[(size_t)tc * P + s2 * G2 + gg];
-    red2[(size_t)tc * G2 + gg] = v;
-  }
   __syncthreads();
   for (int i = t; i < M * 8; i += blockDim.x) {
-    float v = 0.f;
-    for (int gg = 0; gg < G2; ++gg) v += red2[(size_t)i * G2 + gg];
     const int tt = i >> 3, col = i & 7;
+    float v = 0.f;
+    const int c = cnt[tt];
+    for (int r = 0; r < c; ++r) {
+      const int slot = order[tt * topk + r];
+      v = fmaf(wts[slot], ybuf[slot][col], v);
+    }
     out[(uint64_t)tt * H + nt * 8 + col] = __builtin_bit_cast(uint16_t, (_Float16)v);
   }
 }
@@ -398,58 +657,47 @@ __global__ void dequant_kernel(const uint8_t* __restrict__ bank, uint64_t expert
 // ---------------------------------------------------------------------------
 // launchers
 // ---------------------------------------------------------------------------
-hipError_t launch_route_compact(const int32_t* ids, int n, int E, int32_t* active_ids,
-                                int32_t* offsets, int32_t* sorted_slots, int32_t* num_active,
-                                uint32_t* status, hipStream_t stream) {
-  hipLaunchKernelGGL(route_compact_kernel, dim3(1), dim3(256), 0, stream, ids, n, E, active_ids,
-                     offsets, sorted_slots, num_active, status);
+hipError_t launch_route_compact(const int32_t* ids, int n, int E, const RouteOut& o, hipStream_t stream) {
+  hipLaunchKernelGGL(route_compact_kernel, dim3(1), dim3(256), 0, stream, ids, n, E, o);
   return hipGetLastError();
 }
 
-hipError_t launch_w13_swiglu(const StageArgs& a, const uint16_t* x, uint16_t* act, hipStream_t stream) {
+hipError_t launch_w13_swiglu(const StageArgs& a, const uint16_t* x, uint16_t* act, Plan* plan, uint32_t* status,
+                             hipStream_t stream) {
   const int L = 4 * (a.H / 32);
   const dim3 block(((L + 63) / 64) * 64);
-  const dim3 grid((2 * a.I) / 16, a.M * a.topk);
+  const dim3 grid((2 * a.I) / 16, 1 + a.M * a.topk);
   if (a.RB == 4)
-    hipLaunchKernelGGL(w13_swiglu_kernel<4>, grid, block, 0, stream, a.bank, a.expert_bytes,
-                       a.w13_off, a.w13_meta_off, a.H, a.I, x, a.topk, a.active_ids, a.offsets,
-                       a.sorted_slots, a.num_active, act);
+    hipLaunchKernelGGL(w13_swiglu_kernel<4>, grid, block, 0, stream, a, x, act, plan, status);
   else
-    hipLaunchKernelGGL(w13_swiglu_kernel<3>, grid, block, 0, stream, a.bank, a.expert_bytes,
-                       a.w13_off, a.w13_meta_off, a.H, a.I, x, a.topk, a.active_ids, a.offsets,
-                       a.sorted_slots, a.num_active, act);
+    hipLaunchKernelGGL(w13_swiglu_kernel<3>, grid, block, 0, stream, a, x, act, plan, status);
   return hipGetLastError();
 }
 
-int w2_segment_slots(int I) {
-  const int L2 = 2 * (I / 32);
-  int ss = 320 / L2;
-  if (ss > 32) ss = 32;
-  if (ss < 1) ss = 1;
-  return ss;
-}
-
-size_t w2_lds_bytes(int M, int I) {
+W2Shape w2_shape(int I, int n) {
+  W2Shape sh;
   const int G2 = I / 32;
-  const int SS = w2_segment_slots(I);
-  return (size_t)M * 8 * (SS * G2 + G2) * sizeof(float);
+  sh.GP = 1;
+  while (sh.GP < G2) sh.GP <<= 1;
+  const int L2p = 2 * sh.GP;
+  int ss = 512 / L2p;
+  if (ss > 32) ss = 32;
+  if (ss > n) ss = n;
+  if (ss < 1) ss = 1;
+  sh.SS = ss;
+  sh.threads = ((ss * L2p + 63) / 64) * 64;
+  return sh;
 }
 
-hipError_t launch_w2_reduce(const StageArgs& a, const uint16_t* act, const float* topk_w,
+hipError_t launch_w2_reduce(const StageArgs& a, const uint16_t* act, const float* topk_w, const Plan* plan,
                             uint16_t* out, hipStream_t stream) {
-  const int SS = w2_segment_slots(a.I);
-  const int L2 = 2 * (a.I / 32);
-  const dim3 block(((SS * L2 + 63) / 64) * 64);
+  const W2Shape sh = w2_shape(a.I, a.M * a.topk);
+  const dim3 block(sh.threads);
   const dim3 grid(a.H / 8);
-  const size_t lds = w2_lds_bytes(a.M, a.I);
   if (a.RB == 4)
-    hipLaunchKernelGGL(w2_reduce_kernel<4>, grid, block, lds, stream, a.bank, a.expert_bytes,
-                       a.w2_off, a.w2_meta_off, a.H, a.I, act, topk_w, a.M, a.topk, SS,
-                       a.active_ids, a.offsets, a.sorted_slots, a.num_active, out);
+    hipLaunchKernelGGL(w2_reduce_kernel<4>, grid, block, 0, stream, a, act, topk_w, plan, sh.SS, sh.GP, out);
   else
-    hipLaunchKernelGGL(w2_reduce_kernel<3>, grid, block, lds, stream, a.bank, a.expert_bytes,
-                       a.w2_off, a.w2_meta_off, a.H, a.I, act, topk_w, a.M, a.topk, SS,
-                       a.active_ids, a.offsets, a.sorted_slots, a.num_active, out);
+    hipLaunchKernelGGL(w2_reduce_kernel<3>, grid, block, 0, stream, a, act, topk_w, plan, sh.SS, sh.GP, out);
   return hipGetLastError();
 }
 

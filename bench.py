@@ -58,7 +58,7 @@ class Workload:
         self.ids = [torch.from_numpy(np.ascontiguousarray(ids_calls[c])).to(dev) for c in range(CALLS)]
         self.w = [torch.from_numpy(inputs.router_weights(rng, M, K_TOP)).to(dev) for _ in range(CALLS)]
         self.out = torch.empty((M, H), dtype=torch.float16, device=dev)
-        self.act = torch.empty((M * K_TOP, I), dtype=torch.float16, device=dev)
+        self.ws = [abi.alloc_workspace(dims, M, K_TOP, dev) for _ in range(CALLS)]
         self.dec = abi.Decoder(dims, bank, K_TOP, max_tokens=M)
         self.routes = [abi.alloc_route(M * K_TOP, dev) for _ in range(CALLS)]
         self.ids_np = [np.asarray(ids_calls[c]) for c in range(CALLS)]
@@ -114,15 +114,17 @@ def measure(abi, torch, wl: Workload, steps, warmup):
 
     def w13():
         for c in range(CALLS):
-            abi.awq_moe_w13_swiglu(wl.dims, wl.bank, wl.x[c], wl.M, K_TOP, wl.routes[c], act=wl.act)
+            abi.awq_moe_w13_swiglu(wl.dims, wl.bank, wl.x[c], wl.ids[c], workspace=wl.ws[c])
 
     def w2():
         for c in range(CALLS):
-            abi.awq_moe_w2_reduce(wl.dims, wl.bank, wl.act, wl.w[c], wl.M, K_TOP, wl.routes[c], out=wl.out)
+            abi.awq_moe_w2_reduce(wl.dims, wl.bank, wl.w[c], wl.ws[c], out=wl.out)
 
     route()
     torch.cuda.synchronize()
     res = {}
+    # "layer" = awq_moe_decode (the stage kernels compact the ids themselves);
+    # "route" = the standalone awq_moe_route_compact kernel, not part of the layer.
     for name, fn in (("layer", full), ("route", route), ("w13", w13), ("w2", w2)):
         g = capture(torch, fn)
         ms = time_graph(torch, g, steps, warmup)

@@ -117,9 +117,12 @@ int awq_moe_prepare(const awq_moe_dims* dims,
 int awq_moe_workspace_bytes(const awq_moe_dims* dims, int32_t max_tokens, int32_t topk,
                             uint64_t* out);
 
-/* Byte offset, inside the decode workspace, of the uint32 status word that
- * awq_moe_decode writes (bit 0: some id was outside [0, E)). Always 0. */
+/* Decode workspace layout (bytes): the uint32 status word at
+ * AWQ_MOE_WS_STATUS_OFFSET (bit 0: some id was outside [0, E)); the routing
+ * plan the W13 launch leaves for W2 (library-private, 256..4607); the fp16
+ * intermediate act[M*topk][I], indexed by flat slot, at AWQ_MOE_WS_ACT_OFFSET. */
 #define AWQ_MOE_WS_STATUS_OFFSET 0
+#define AWQ_MOE_WS_ACT_OFFSET 4608
 
 /* Compact routed ids into active-expert segments (PR #520, Purpose: multi-row
  * active-expert segments with offsets-based scheduling; Implementation: the op
@@ -142,29 +145,35 @@ int awq_moe_route_compact(const int32_t* topk_ids, int32_t M, int32_t topk, int3
  *            e = topk_ids[t][j], accumulated in fp32 in a fixed order that
  *            depends only on the compacted segments.
  *   workspace device, 256-byte aligned, >= awq_moe_workspace_bytes(dims, M, topk);
- *            holds the routing arrays, the fp16 intermediate and the status word.
- * Launches three kernels on stream. */
+ *            receives the status word (offset AWQ_MOE_WS_STATUS_OFFSET) and
+ *            the fp16 intermediate.
+ * Launches two kernels on stream (W13 + SwiGLU, then W2 + reduction); each
+ * groups the routed slots by expert itself, so no separate routing launch
+ * precedes them. */
 int awq_moe_decode(const awq_moe_dims* dims, const void* bank, const uint16_t* x,
                    const int32_t* topk_ids, const float* topk_w, int32_t M, int32_t topk,
                    uint16_t* out, void* workspace, uint64_t workspace_bytes, void* stream);
 
 /* --- stage exports, for stage-pair checks (fork PR #12, Numerical acceptance:
- * W2 checked on its own intermediate) and per-kernel timing ------------- */
+ * W2 checked on its own intermediate) and per-kernel timing. awq_moe_decode
+ * is exactly awq_moe_w13_swiglu followed by awq_moe_w2_reduce on the same
+ * workspace. */
 
-/* W13 + SwiGLU over compacted segments. act: device fp16 [M*topk][I]; row r
- * of act belongs to sorted row r (rows past the valid count are not written).
- * Routing arrays as produced by awq_moe_route_compact for the same M, topk. */
+/* W13 + SwiGLU for the routed ids topk_ids [M][topk] (device int32). Writes
+ * the status word, the routing plan and act into workspace: act[s] =
+ * fp16(silu(x_t Wg_e) * (x_t Wu_e)) for each valid flat slot s = t*topk + j
+ * (rows of invalid slots are not written). Each expert's W13 is streamed once
+ * and applied to all its slots. One launch. */
 int awq_moe_w13_swiglu(const awq_moe_dims* dims, const void* bank, const uint16_t* x,
-                       int32_t M, int32_t topk, const int32_t* active_expert_ids,
-                       const int32_t* active_expert_offsets, const int32_t* sorted_slots,
-                       const int32_t* num_active, uint16_t* act, void* stream);
+                       const int32_t* topk_ids, int32_t M, int32_t topk,
+                       void* workspace, uint64_t workspace_bytes, void* stream);
 
-/* W2 + router-weighted reduction from a given fp16 act [M*topk][I] (sorted
- * rows). out device fp16 [M][H], overwritten. */
-int awq_moe_w2_reduce(const awq_moe_dims* dims, const void* bank, const uint16_t* act,
-                      const float* topk_w, int32_t M, int32_t topk,
-                      const int32_t* active_expert_ids, const int32_t* active_expert_offsets,
-                      const int32_t* sorted_slots, const int32_t* num_active,
+/* W2 + router-weighted reduction from the act and routing plan that
+ * awq_moe_w13_swiglu left in workspace for the same M and topk (the caller
+ * may overwrite act in between). topk_w device fp32 [M][topk]; out device
+ * fp16 [M][H], overwritten. One launch. */
+int awq_moe_w2_reduce(const awq_moe_dims* dims, const void* bank, const float* topk_w,
+                      int32_t M, int32_t topk, const void* workspace, uint64_t workspace_bytes,
                       uint16_t* out, void* stream);
 
 /* Dequantise experts [expert_begin, expert_begin + expert_count) of the bank

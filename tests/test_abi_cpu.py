@@ -134,8 +134,12 @@ def test_device_calls_reject_bad_arguments_before_launch():
         (lambda: lib.awq_moe_route_compact(p, 0, 10, 512, p, p, p, p, p, None), abi.EINVAL),
         (lambda: lib.awq_moe_route_compact(p, 1, 10, 0, p, p, p, p, p, None), abi.EINVAL),
         (lambda: lib.awq_moe_route_compact(p, 1, 10, 512, p, p, None, p, p, None), abi.EINVAL),
-        (lambda: lib.awq_moe_w13_swiglu(ctypes.byref(d), p, p, 1, 10, p, p, p, p, mis, None), abi.EINVAL),
-        (lambda: lib.awq_moe_w2_reduce(ctypes.byref(d), p, p, p, 1, 10, p, p, p, p, mis, None), abi.EINVAL),
+        (lambda: lib.awq_moe_w13_swiglu(ctypes.byref(d), p, p, p, 1, 10, mis, ws_need, None), abi.EINVAL),
+        (lambda: lib.awq_moe_w13_swiglu(ctypes.byref(d), p, p, None, 1, 10, p, ws_need, None), abi.EINVAL),
+        (lambda: lib.awq_moe_w13_swiglu(ctypes.byref(d), p, p, p, 1, 10, p, ws_need - 1, None), abi.ENOSPC),
+        (lambda: lib.awq_moe_w2_reduce(ctypes.byref(d), p, p, 1, 10, p, ws_need, mis, None), abi.EINVAL),
+        (lambda: lib.awq_moe_w2_reduce(ctypes.byref(d), p, p, 9, 10, p, ws_need, p, None), abi.EINVAL),
+        (lambda: lib.awq_moe_w2_reduce(ctypes.byref(d), p, None, 1, 10, p, ws_need, p, None), abi.EINVAL),
         (lambda: lib.awq_moe_dequant(ctypes.byref(d), p, 510, 3, 0, p, None), abi.EINVAL),
         (lambda: lib.awq_moe_dequant(ctypes.byref(d), p, 0, 1, 2, p, None), abi.EINVAL),
     ]

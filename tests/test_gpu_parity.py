@@ -123,16 +123,15 @@ def test_w13_stage_and_w2_stage_pair(rb, M):
     ids = inputs.ids_shared_pool(rng, M, 10, 64)
     w = inputs.router_weights(rng, M, 10)
     route_o = oracle_route(ids, 64)
-    _, route_g = gpu_route(ids, 64)
-    act = abi.awq_moe_w13_swiglu(dims, bank, to_dev(x), M, 10, route_g)
+    ws = abi.awq_moe_w13_swiglu(dims, bank, to_dev(x), to_dev(ids))
     torch.cuda.synchronize()
-    act_np = f16_to_np(act)
     V = route_o["num_valid"]
+    act_sorted = f16_to_np(abi.workspace_act(ws, M, 10, I))[route_o["sorted_slots"]]   # by slot -> sorted rows
     act_ref = R.w13_swiglu_rows(x, route_o, 10, bi.expert)
-    check(act_np[:V], act_ref[:V], f"w13 M={M} rb={rb}")
-    out = abi.awq_moe_w2_reduce(dims, bank, act, to_dev(w), M, 10, route_g)
+    check(act_sorted[:V], act_ref[:V], f"w13 M={M} rb={rb}")
+    out = abi.awq_moe_w2_reduce(dims, bank, to_dev(w), ws)
     torch.cuda.synchronize()
-    out_ref = R.w2_reduce(act_np, w, route_o, 10, bi.expert, M, H)
+    out_ref = R.w2_reduce(act_sorted, w, route_o, 10, bi.expert, M, H)
     check(f16_to_np(out), out_ref, f"w2 on own act M={M} rb={rb}")
 
 
@@ -232,11 +231,12 @@ def test_w2_exact_integer_case_bit_exact():
     w = np.zeros((M, k), np.float32)
     w[:, 0] = 1.0
     route_o = oracle_route(ids, E)
-    _, route_g = gpu_route(ids, E)
-    act = rng.integers(-1, 2, size=(M * k, I)).astype(np.float16)
-    out = abi.awq_moe_w2_reduce(dims, bank, to_dev(act), to_dev(w), M, k, route_g)
+    act = rng.integers(-1, 2, size=(M * k, I)).astype(np.float16)      # indexed by slot
+    ws = abi.awq_moe_w13_swiglu(dims, bank, to_dev(np.zeros((M, H), np.float16)), to_dev(ids))
+    abi.workspace_act(ws, M, k, I).copy_(to_dev(act))                  # replace the intermediate
+    out = abi.awq_moe_w2_reduce(dims, bank, to_dev(w), ws)
     torch.cuda.synchronize()
-    want = R.w2_reduce(act, w, route_o, k, bi.expert, M, H)
+    want = R.w2_reduce(act[route_o["sorted_slots"]], w, route_o, k, bi.expert, M, H)
     assert np.abs(want).max() <= 2048 and np.array_equal(want, np.round(want))
     np.testing.assert_array_equal(f16_to_np(out).astype(np.float64), want)
 
