@@ -128,6 +128,49 @@ __device__ __forceinline__ float silu_mul(float g, float u) {
   return g / (1.0f + __expf(-g)) * u;
 }
 
+// Cross-lane sums in the VALU (DPP and gfx950 permlane swaps), no LDS round trip.
+template <int CTRL>
+__device__ __forceinline__ float dpp(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
+}
+constexpr int kRowRor4 = 0x124, kRowRor8 = 0x128;
+constexpr int kQuadSwap1 = 0xB1;  // quad_perm [1,0,3,2]
+constexpr int kQuadSwap2 = 0x4E;  // quad_perm [2,3,0,1]
+constexpr int kRowHalfMirror = 0x141;
+
+// Sum four per-lane values over the 16 lanes that share lane bits 0..1 (one
+// column quad of a wave): two DPP row rotations sum within each 16-lane row
+// in the VALU; then a reduce-scatter across rows: the xor-16 exchange trades
+// two of the four values, the xor-32 exchange one, so lane l ends with the
+// full sum of value 2*b4 + b5 (b4, b5 = lane bits 4, 5). The lanes with
+// (lane & 12) == 0 carry the four results of their quad.
+__device__ __forceinline__ float sum4_lane_bits_2to5(float p0, float p1, float p2, float p3) {
+  p0 += dpp<kRowRor4>(p0);
+  p1 += dpp<kRowRor4>(p1);
+  p2 += dpp<kRowRor4>(p2);
+  p3 += dpp<kRowRor4>(p3);
+  p0 += dpp<kRowRor8>(p0);
+  p1 += dpp<kRowRor8>(p1);
+  p2 += dpp<kRowRor8>(p2);
+  p3 += dpp<kRowRor8>(p3);
+  const int lane = threadIdx.x & 63;
+  const bool b4 = (lane & 16) != 0, b5 = (lane & 32) != 0;
+  float k0 = b4 ? p2 : p0, k1 = b4 ? p3 : p1;
+  k0 += __shfl_xor(b4 ? p0 : p2, 16);
+  k1 += __shfl_xor(b4 ? p1 : p3, 16);
+  float k = b5 ? k1 : k0;
+  k += __shfl_xor(b5 ? k0 : k1, 32);
+  return k;
+}
+
+// Sum over aligned groups of 8 lanes (lane bits 0..2); every lane gets the sum.
+__device__ __forceinline__ float sum_lane_bits_0to2(float v) {
+  v += dpp<kQuadSwap1>(v);
+  v += dpp<kQuadSwap2>(v);
+  v += dpp<kRowHalfMirror>(v);
+  return v;
+}
+
 // ---------------------------------------------------------------------------
 // routing compaction of n <= 256 slots inside one workgroup (LDS only).
 // Canonical order: experts ascending, rows of a segment by ascending slot,
@@ -407,7 +450,7 @@ template <int RB>
 __global__ __launch_bounds__(1024) void w13_swiglu_kernel(StageArgs a, const uint16_t* __restrict__ x,
                                                           uint16_t* __restrict__ act, Plan* __restrict__ plan,
                                                           uint32_t* __restrict__ status) {
-  constexpr int R = 4;  // rows per pass
+  constexpr int R = 2;  // rows per pass
   __shared__ float red[16][R][16];  // [wave][row][column]
   __shared__ PlanLds plan_lds;
   const int n = a.M * a.topk;
@@ -419,31 +462,41 @@ __global__ __launch_bounds__(1024) void w13_swiglu_kernel(StageArgs a, const uin
   const int s = blockIdx.y - 1;
   const int t = threadIdx.x;
   const int lane = t & 63, wave = t >> 6, nwaves = blockDim.x >> 6;
+  const int H = a.H, I = a.I, topk = a.topk;
+  const int G = H >> 5;
+  const int L = 4 * G;
+  const bool active = t < L;
+  const int g = t >> 2;
   const int my = a.topk_ids[s];
   const SlotIds ids = load_slot_ids(a.topk_ids, n, a.E);
   if (my < 0 || my >= a.E) return;
+  const uint8_t* blk = a.bank + (uint64_t)my * a.expert_bytes;
+  uint4 w[4];
+  Records<RB> rec;
+  Act32 x0;
+  // With one token every slot reads the same activation row and an expert
+  // repeats only when the caller passes duplicate ids, so the tile and the
+  // row are requested before the leader check (which needs all n ids).
+  const bool early = (a.M == 1);
+  if (early && active) {
+    const uint8_t* units = blk + a.w13_off + (uint64_t)nt * 256u * G;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) w[j] = *reinterpret_cast<const uint4*>(units + ((uint64_t)j * L + t) * 16u);
+    rec = load_records<RB>(blk + a.w13_meta_off + (uint64_t)nt * 16u * G * RB + (uint64_t)t * 4u * RB);
+    x0 = load_act32(x + 32 * g);
+  }
   uint64_t rows[4];
   same_id_masks(ids, my, n, rows);
   {
     uint64_t probe[4] = {rows[0], rows[1], rows[2], rows[3]};
     if (pop_slot(probe) != s) return;  // another slot leads this expert
   }
-  const int H = a.H, I = a.I, topk = a.topk;
-  const int G = H >> 5;
-  const int L = 4 * G;
-  const bool active = t < L;
-  const int g = t >> 2;
-
-  const uint8_t* blk = a.bank + (uint64_t)my * a.expert_bytes;
-  uint4 w[4];
-  Records<RB> rec;
-  if (active) {
+  if (!early && active) {
     const uint8_t* units = blk + a.w13_off + (uint64_t)nt * 256u * G;
 #pragma unroll
     for (int j = 0; j < 4; ++j) w[j] = *reinterpret_cast<const uint4*>(units + ((uint64_t)j * L + t) * 16u);
     rec = load_records<RB>(blk + a.w13_meta_off + (uint64_t)nt * 16u * G * RB + (uint64_t)t * 4u * RB);
   }
-
   for (;;) {
     int slot[R];
     int rowsn = 0;
@@ -459,8 +512,7 @@ __global__ __launch_bounds__(1024) void w13_swiglu_kernel(StageArgs a, const uin
 #pragma unroll
       for (int j = 0; j < 4; ++j) part[rr][j] = 0.f;
       if (active && rr < rowsn) {
-        const int tok = slot[rr] / topk;
-        const Act32 av = load_act32(x + (uint64_t)tok * H + 32 * g);
+        const Act32 av = early ? x0 : load_act32(x + (uint64_t)(slot[rr] / topk) * H + 32 * g);
         float S, Cs;
         group_sums(av, S, Cs);
 #pragma unroll
@@ -470,23 +522,17 @@ __global__ __launch_bounds__(1024) void w13_swiglu_kernel(StageArgs a, const uin
         }
       }
     }
-    // reduce over the 16 groups of this wave: lanes with equal (lane & 3)
+    // Sum over the 16 groups of this wave (lane bits 2..5): lane l ends with
+    // column 4*(l & 3) + 2*b4 + b5 of the tile.
 #pragma unroll
     for (int rr = 0; rr < R; ++rr) {
       if (rr < rowsn) {
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          float v = part[rr][j];
-          v += __shfl_xor(v, 4);
-          v += __shfl_xor(v, 8);
-          v += __shfl_xor(v, 16);
-          v += __shfl_xor(v, 32);
-          if (lane < 4) red[wave][rr][4 * lane + j] = v;
-        }
+        const float v = sum4_lane_bits_2to5(part[rr][0], part[rr][1], part[rr][2], part[rr][3]);
+        if ((lane & 12) == 0) red[wave][rr][4 * (lane & 3) + 2 * ((lane >> 4) & 1) + (lane >> 5)] = v;
       }
     }
     __syncthreads();
-    if (t < 16 * R) {  // exactly wave 0
+    if (t < 16 * R) {  // wave 0 (R <= 4)
       const int col = t & 15, rr = t >> 4;
       float h = 0.f;
       for (int wv = 0; wv < nwaves; ++wv) h += red[wv][rr][col];
@@ -521,7 +567,6 @@ __global__ __launch_bounds__(512) void w2_reduce_kernel(StageArgs a, const uint1
                                                         const float* __restrict__ topk_w,
                                                         const Plan* __restrict__ plan, int SS, int GP,
                                                         uint16_t* __restrict__ out) {
-  constexpr int R = 4;  // rows per pass
   __shared__ int seg_e[kMaxSlots];
   __shared__ int seg_off[kMaxSlots + 1];
   __shared__ int seg_slots[kMaxSlots];
@@ -555,48 +600,54 @@ __global__ __launch_bounds__(512) void w2_reduce_kernel(StageArgs a, const uint1
   const int quad = tl / GP, gp = tl - quad * GP;
   const int nseg = nseg_s;
   const bool loader = (sl < SS) && (gp < G2);
+  // Segment tiles are software-pipelined: the next segment's W2 tile and first
+  // activation row are requested before the current segment is computed.
+  const int tli = 2 * gp + quad;  // lane of the bank layout
+  auto issue = [&](int seg, uint4 (&w)[4], Records<RB>& rec, Act32& first) {
+    const uint8_t* blk = a.bank + (uint64_t)seg_e[seg] * a.expert_bytes;
+    const uint8_t* units = blk + a.w2_off + (uint64_t)nt * 128u * G2;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) w[j] = *reinterpret_cast<const uint4*>(units + ((uint64_t)j * (2 * G2) + tli) * 16u);
+    rec = load_records<RB>(blk + a.w2_meta_off + (uint64_t)nt * 8u * G2 * RB + (uint64_t)tli * 4u * RB);
+    first = load_act32(act + (uint64_t)seg_slots[seg_off[seg]] * I + 32 * gp);
+  };
   if (sl < SS) {
+    uint4 w[4], wn[4];
+    Records<RB> rec, recn;
+    Act32 cur, curn;
+    if (loader && sl < nseg) issue(sl, w, rec, cur);
     for (int seg = sl; seg < nseg; seg += SS) {
-      const int e = seg_e[seg];
-      const int r_end = seg_off[seg + 1];
-      uint4 w[4];
-      Records<RB> rec;
-      if (loader) {
-        const uint8_t* blk = a.bank + (uint64_t)e * a.expert_bytes;
-        const int tli = 2 * gp + quad;  // lane of the bank layout
-        const uint8_t* units = blk + a.w2_off + (uint64_t)nt * 128u * G2;
+      const int r_begin = seg_off[seg], r_end = seg_off[seg + 1];
+      const bool more = seg + SS < nseg;
+      if (loader && more) issue(seg + SS, wn, recn, curn);
+      for (int r = r_begin; r < r_end; ++r) {
+        const int slot = seg_slots[r];
+        if (loader && r > r_begin) cur = load_act32(act + (uint64_t)slot * I + 32 * gp);
+        float y[4] = {0.f, 0.f, 0.f, 0.f};
+        if (loader) {
+          float S, Cs;
+          group_sums(cur, S, Cs);
 #pragma unroll
-        for (int j = 0; j < 4; ++j) w[j] = *reinterpret_cast<const uint4*>(units + ((uint64_t)j * (2 * G2) + tli) * 16u);
-        rec = load_records<RB>(blk + a.w2_meta_off + (uint64_t)nt * 8u * G2 * RB + (uint64_t)tli * 4u * RB);
+          for (int j = 0; j < 4; ++j) y[j] = rec.s[j] * (unit_dot(w[j], cur) - fmaf(rec.z[j], S, Cs));
+        }
+        if (GP == 8) {
+#pragma unroll
+          for (int j = 0; j < 4; ++j) y[j] = sum_lane_bits_0to2(y[j]);
+        } else {
+          for (int o = 1; o < GP; o <<= 1)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) y[j] += __shfl_xor(y[j], o);
+        }
+        if (gp == 0) {
+#pragma unroll
+          for (int j = 0; j < 4; ++j) ybuf[slot][4 * quad + j] = y[j];
+        }
       }
-      for (int r0 = seg_off[seg]; r0 < r_end; r0 += R) {
-        const int rows = min(R, r_end - r0);
-        Act32 av[R];
-        int slot[R];
+      if (more) {
 #pragma unroll
-        for (int rr = 0; rr < R; ++rr) {
-          slot[rr] = rr < rows ? seg_slots[r0 + rr] : 0;
-          if (loader && rr < rows) av[rr] = load_act32(act + (uint64_t)slot[rr] * I + 32 * gp);
-        }
-#pragma unroll
-        for (int rr = 0; rr < R; ++rr) {
-          if (rr < rows) {
-            float y[4] = {0.f, 0.f, 0.f, 0.f};
-            if (loader) {
-              float S, Cs;
-              group_sums(av[rr], S, Cs);
-#pragma unroll
-              for (int j = 0; j < 4; ++j) y[j] = rec.s[j] * (unit_dot(w[j], av[rr]) - fmaf(rec.z[j], S, Cs));
-            }
-            for (int o = 1; o < GP; o <<= 1)
-#pragma unroll
-              for (int j = 0; j < 4; ++j) y[j] += __shfl_xor(y[j], o);
-            if (gp == 0) {
-#pragma unroll
-              for (int j = 0; j < 4; ++j) ybuf[slot[rr]][4 * quad + j] = y[j];
-            }
-          }
-        }
+        for (int j = 0; j < 4; ++j) w[j] = wn[j];
+        rec = recn;
+        cur = curn;
       }
     }
   }
@@ -680,8 +731,8 @@ W2Shape w2_shape(int I, int n) {
   sh.GP = 1;
   while (sh.GP < G2) sh.GP <<= 1;
   const int L2p = 2 * sh.GP;
-  int ss = 512 / L2p;
-  if (ss > 32) ss = 32;
+  int ss = 256 / L2p;
+  if (ss > 16) ss = 16;
   if (ss > n) ss = n;
   if (ss < 1) ss = 1;
   sh.SS = ss;
