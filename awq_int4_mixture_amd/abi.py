@@ -22,7 +22,7 @@ OK, EINVAL, EUNSUPPORTED, ENOSPC, EHIP = 0, -1, -2, -3, -4
 MAX_TOKENS, MAX_TOPK = 8, 32
 STATUS_BAD_ID = 1
 WS_STATUS_OFFSET = 0
-WS_ACT_OFFSET = 4608
+WS_ACT_OFFSET = 256
 
 EXPORTED = (
     "awq_moe_bank_layout_query", "awq_moe_prepare", "awq_moe_workspace_bytes",
@@ -69,7 +69,7 @@ def _load() -> ctypes.CDLL:
         "awq_moe_route_compact": [P, I32, I32, I32, P, P, P, P, P, V],
         "awq_moe_decode": [D, P, P, P, P, I32, I32, P, P, U64, V],
         "awq_moe_w13_swiglu": [D, P, P, P, I32, I32, P, U64, V],
-        "awq_moe_w2_reduce": [D, P, P, I32, I32, P, U64, P, V],
+        "awq_moe_w2_reduce": [D, P, P, P, I32, I32, P, U64, P, V],
         "awq_moe_dequant": [D, P, I32, I32, I32, P, V],
     }
     for name, args in sig.items():
@@ -211,7 +211,7 @@ def awq_moe_decode(dims: awq_moe_dims, bank, x, topk_ids, topk_w, out=None, work
     if out is None:
         out = torch.empty((M, H), dtype=torch.float16, device=x.device)
     if workspace is None:
-        workspace = torch.empty(awq_moe_workspace_bytes(dims, M, k), dtype=torch.uint8, device=x.device)
+        workspace = alloc_workspace(dims, M, k, x.device)
     _check(_lib.awq_moe_decode(
         ctypes.byref(dims), _dev(bank, torch.uint8, name="bank"), _dev(x, torch.float16, (M, dims.hidden), "x"),
         _dev(topk_ids, torch.int32, (M, k), "topk_ids"), _dev(topk_w, torch.float32, (M, k), "topk_w"), M, k,
@@ -221,6 +221,7 @@ def awq_moe_decode(dims: awq_moe_dims, bank, x, topk_ids, topk_w, out=None, work
 
 
 def alloc_workspace(dims: awq_moe_dims, max_tokens: int, topk: int, device="cuda"):
+    """A decode workspace (zero-filled so that unused rows read as zero)."""
     torch = _torch()
     return torch.zeros(awq_moe_workspace_bytes(dims, max_tokens, topk), dtype=torch.uint8, device=device)
 
@@ -233,7 +234,7 @@ def workspace_act(workspace, M: int, topk: int, inter: int):
 
 
 def awq_moe_w13_swiglu(dims: awq_moe_dims, bank, x, topk_ids, workspace=None, stream=None):
-    """Runs W13 + SwiGLU; returns the workspace holding act, the plan and the status."""
+    """Runs W13 + SwiGLU; returns the workspace holding act and the status."""
     torch = _torch()
     M, k = topk_ids.shape
     if workspace is None:
@@ -245,16 +246,16 @@ def awq_moe_w13_swiglu(dims: awq_moe_dims, bank, x, topk_ids, workspace=None, st
     return workspace
 
 
-def awq_moe_w2_reduce(dims: awq_moe_dims, bank, topk_w, workspace, out=None, stream=None):
-    """W2 + reduction from the act and plan left in ``workspace`` by awq_moe_w13_swiglu."""
+def awq_moe_w2_reduce(dims: awq_moe_dims, bank, topk_ids, topk_w, workspace, out=None, stream=None):
+    """W2 + reduction from the act in ``workspace`` (as awq_moe_w13_swiglu left it)."""
     torch = _torch()
     M, k = topk_w.shape
     if out is None:
         out = torch.empty((M, dims.hidden), dtype=torch.float16, device=topk_w.device)
     _check(_lib.awq_moe_w2_reduce(
-        ctypes.byref(dims), _dev(bank, torch.uint8, name="bank"), _dev(topk_w, torch.float32, (M, k), "topk_w"),
-        M, k, _dev(workspace, torch.uint8, name="workspace"), workspace.numel(),
-        _dev(out, torch.float16, (M, dims.hidden), "out"), _stream(stream)), "awq_moe_w2_reduce")
+        ctypes.byref(dims), _dev(bank, torch.uint8, name="bank"), _dev(topk_ids, torch.int32, (M, k), "topk_ids"),
+        _dev(topk_w, torch.float32, (M, k), "topk_w"), M, k, _dev(workspace, torch.uint8, name="workspace"),
+        workspace.numel(), _dev(out, torch.float16, (M, dims.hidden), "out"), _stream(stream)), "awq_moe_w2_reduce")
     return out
 
 

@@ -71,9 +71,7 @@ Layout make_layout(const awq_moe_dims* d) {
   return L;
 }
 
-// Workspace: [status u32 | pad] [routing plan] [fp16 act[n][I]].
-constexpr uint64_t kPlanOffset = 256;
-static_assert(kPlanOffset + sizeof(awq_moe::Plan) <= AWQ_MOE_WS_ACT_OFFSET, "plan overlaps act");
+// Workspace: [status u32 | pad] [fp16 act[n][I]].
 static_assert(AWQ_MOE_WS_ACT_OFFSET % 256 == 0, "act must stay 256-byte aligned");
 
 uint64_t ws_total(const awq_moe_dims* d, int max_tokens, int topk) {
@@ -192,7 +190,7 @@ int awq_moe_prepare(const awq_moe_dims* dims, const uint8_t* q_gate, const uint8
 
   uint8_t* out = static_cast<uint8_t*>(bank);
   std::memset(out, 0, L.pub.total_bytes);
-  const uint64_t G13 = H / 32, L13 = 4 * G13, G2 = I / 32, L2 = 2 * G2;
+  const uint64_t G13 = H / 32, L13 = 4 * G13, G2 = I / 32, L2 = 4 * G2;
 
   // Pack 32 values v(k), k = 0..31 into a 16-byte unit.
   auto put_unit = [](uint8_t* dst, auto value_at) {
@@ -239,12 +237,12 @@ int awq_moe_prepare(const awq_moe_dims* dims, const uint8_t* q_gate, const uint8
     }
     // W2: column n of hidden
     for (uint64_t n = 0; n < H; ++n) {
-      const uint64_t nt = n / 8, c = n % 8, quad = c / 4, j = c % 4;
+      const uint64_t nt = n / 16, c = n % 16, quad = c / 4, j = c % 4;
       for (uint64_t g = 0; g < G2; ++g) {
-        const uint64_t t = 2 * g + quad;
-        put_unit(blk + L.pub.w2_off + nt * 128 * G2 + (j * L2 + t) * 16,
+        const uint64_t t = 4 * g + quad;
+        put_unit(blk + L.pub.w2_off + nt * 256 * G2 + (j * L2 + t) * 16,
                  [&](int k) { return qd[(32 * g + k) * H + n]; });
-        put_record(blk + L.pub.w2_meta_off + nt * 8 * G2 * RB + (4 * t + j) * RB, sd[g * H + n], zd[g * H + n]);
+        put_record(blk + L.pub.w2_meta_off + nt * 16 * G2 * RB + (4 * t + j) * RB, sd[g * H + n], zd[g * H + n]);
       }
     }
   }
@@ -282,14 +280,12 @@ int check_stage(const awq_moe_dims* dims, const void* bank, int32_t M, int32_t t
 
 struct WsPtrs {
   uint32_t* status;
-  awq_moe::Plan* plan;
   uint16_t* act;
 };
 
-WsPtrs ws_ptrs(void* workspace) {
-  uint8_t* ws = static_cast<uint8_t*>(workspace);
+WsPtrs ws_ptrs(const void* workspace) {
+  uint8_t* ws = static_cast<uint8_t*>(const_cast<void*>(workspace));
   return WsPtrs{reinterpret_cast<uint32_t*>(ws + AWQ_MOE_WS_STATUS_OFFSET),
-                reinterpret_cast<awq_moe::Plan*>(ws + kPlanOffset),
                 reinterpret_cast<uint16_t*>(ws + AWQ_MOE_WS_ACT_OFFSET)};
 }
 
@@ -301,20 +297,22 @@ int awq_moe_w13_swiglu(const awq_moe_dims* dims, const void* bank, const uint16_
   if (!topk_ids || !aligned(topk_ids, 4)) return fail(AWQ_MOE_EINVAL, "topk_ids null or misaligned");
   if ((rc = check_device())) return rc;
   const WsPtrs w = ws_ptrs(workspace);
-  return hip_status(awq_moe::launch_w13_swiglu(stage_args(dims, bank, topk_ids, M, topk), x, w.act, w.plan,
-                                               w.status, static_cast<hipStream_t>(stream)),
+  return hip_status(awq_moe::launch_w13_swiglu(stage_args(dims, bank, topk_ids, M, topk), x, w.act, w.status,
+                                               static_cast<hipStream_t>(stream)),
                     "w13 launch");
 }
 
-int awq_moe_w2_reduce(const awq_moe_dims* dims, const void* bank, const float* topk_w, int32_t M, int32_t topk,
-                      const void* workspace, uint64_t workspace_bytes, uint16_t* out, void* stream) {
+int awq_moe_w2_reduce(const awq_moe_dims* dims, const void* bank, const int32_t* topk_ids, const float* topk_w,
+                      int32_t M, int32_t topk, const void* workspace, uint64_t workspace_bytes, uint16_t* out,
+                      void* stream) {
   int rc = check_stage(dims, bank, M, topk, workspace, workspace_bytes);
   if (rc) return rc;
+  if (!topk_ids || !aligned(topk_ids, 4)) return fail(AWQ_MOE_EINVAL, "topk_ids null or misaligned");
   if (!topk_w || !aligned(topk_w, 4)) return fail(AWQ_MOE_EINVAL, "topk_w null or misaligned");
   if (!out || !aligned(out, 16)) return fail(AWQ_MOE_EINVAL, "out null or not 16-byte aligned");
   if ((rc = check_device())) return rc;
-  const WsPtrs w = ws_ptrs(const_cast<void*>(workspace));
-  return hip_status(awq_moe::launch_w2_reduce(stage_args(dims, bank, nullptr, M, topk), w.act, topk_w, w.plan, out,
+  const WsPtrs w = ws_ptrs(workspace);
+  return hip_status(awq_moe::launch_w2_reduce(stage_args(dims, bank, topk_ids, M, topk), w.act, topk_w, out,
                                               static_cast<hipStream_t>(stream)),
                     "w2 launch");
 }
@@ -332,9 +330,9 @@ int awq_moe_decode(const awq_moe_dims* dims, const void* bank, const uint16_t* x
   const WsPtrs w = ws_ptrs(workspace);
   hipStream_t s = static_cast<hipStream_t>(stream);
   const awq_moe::StageArgs a = stage_args(dims, bank, topk_ids, M, topk);
-  hipError_t e = awq_moe::launch_w13_swiglu(a, x, w.act, w.plan, w.status, s);
+  hipError_t e = awq_moe::launch_w13_swiglu(a, x, w.act, w.status, s);
   if (e != hipSuccess) return hip_status(e, "w13 launch");
-  return hip_status(awq_moe::launch_w2_reduce(a, w.act, topk_w, w.plan, out, s), "w2 launch");
+  return hip_status(awq_moe::launch_w2_reduce(a, w.act, topk_w, out, s), "w2 launch");
 }
 
 int awq_moe_dequant(const awq_moe_dims* dims, const void* bank, int32_t expert_begin, int32_t expert_count,
@@ -349,12 +347,10 @@ int awq_moe_dequant(const awq_moe_dims* dims, const void* bank, int32_t expert_b
                 expert_begin + expert_count, dims->num_experts);
   if ((rc = check_device())) return rc;
   const Layout L = make_layout(dims);
-  const int K = which == 0 ? dims->hidden : dims->inter;
-  const int N = which == 0 ? 2 * dims->inter : dims->hidden;
   const uint64_t uo = which == 0 ? L.pub.w13_off : L.pub.w2_off;
   const uint64_t mo = which == 0 ? L.pub.w13_meta_off : L.pub.w2_meta_off;
   return hip_status(awq_moe::launch_dequant(static_cast<const uint8_t*>(bank), L.pub.expert_bytes, uo, mo,
-                                            dims->meta_bytes, which, K, N, expert_begin, expert_count, out,
+                                            dims->meta_bytes, which, dims->hidden, dims->inter, expert_begin, expert_count, out,
                                             static_cast<hipStream_t>(stream)),
                     "dequant launch");
 }

@@ -7,22 +7,10 @@
 
 #define AWQ_MOE_KMAX_TOKENS 8
 #define AWQ_MOE_KMAX_SLOTS 256
+#define AWQ_MOE_KMAX_TOPK 32
 #define AWQ_MOE_STATUS_BAD_ID_BIT 1u
 
 namespace awq_moe {
-
-// Routing plan that the W13 launch writes for W2 (inside the decode
-// workspace): segments = distinct valid experts in order of their lowest
-// slot, each with its slots in ascending order, and, per token, its valid
-// slots in ascending (expert, slot) order.
-struct Plan {
-  int32_t num_segments;
-  int32_t cnt[AWQ_MOE_KMAX_TOKENS];           // valid slots of token t
-  int32_t seg_e[AWQ_MOE_KMAX_SLOTS];          // expert of segment
-  int32_t seg_off[AWQ_MOE_KMAX_SLOTS + 1];    // segment -> first entry of seg_slots
-  int32_t seg_slots[AWQ_MOE_KMAX_SLOTS];      // slots grouped by segment
-  int32_t order[AWQ_MOE_KMAX_SLOTS];          // [t*topk + r]: token t's r-th slot
-};
 
 // Everything a stage kernel needs besides its activation input and output.
 // Passed by value as a kernel argument.
@@ -44,18 +32,12 @@ struct RouteOut {
 };
 
 hipError_t launch_route_compact(const int32_t* ids, int n, int E, const RouteOut& o, hipStream_t stream);
-hipError_t launch_w13_swiglu(const StageArgs& a, const uint16_t* x, uint16_t* act, Plan* plan, uint32_t* status,
+hipError_t launch_w13_swiglu(const StageArgs& a, const uint16_t* x, uint16_t* act, uint32_t* status,
                              hipStream_t stream);
-hipError_t launch_w2_reduce(const StageArgs& a, const uint16_t* act, const float* topk_w, const Plan* plan,
-                            uint16_t* out, hipStream_t stream);
+hipError_t launch_w2_reduce(const StageArgs& a, const uint16_t* act, const float* topk_w, uint16_t* out,
+                            hipStream_t stream);
 hipError_t launch_dequant(const uint8_t* bank, uint64_t expert_bytes, uint64_t units_off,
-                          uint64_t meta_off, int RB, int which, int K, int N, int expert_begin,
+                          uint64_t meta_off, int RB, int which, int H, int I, int expert_begin,
                           int expert_count, float* out, hipStream_t stream);
-// Workgroup shape of the W2 kernel: SS slot groups x 2 column quads x GP
-// group lanes (GP = power of two >= I/32).
-struct W2Shape {
-  int SS, GP, threads;
-};
-W2Shape w2_shape(int I, int n);
 
 }  // namespace awq_moe

@@ -35,8 +35,6 @@ typedef uint32_t u32x3_a4 __attribute__((ext_vector_type(3), aligned(4)));
 // Bit pattern constants of the nibble -> fp16 conversion.
 constexpr uint32_t kLoMask = 0x000F000Fu;   // values at bits 0 and 16
 constexpr uint32_t kHiMask = 0x00F000F0u;   // values at bits 4 and 20
-constexpr uint32_t kMagic1024 = 0x64006400u; // fp16 1024.0 twice: mantissa ulp 1
-constexpr uint32_t kMagic64 = 0x54005400u;   // fp16 64.0 twice: ulp 1/16, so bits 4..7 count 1 each
 
 __device__ __forceinline__ h2_t as_h2(uint32_t v) { return __builtin_bit_cast(h2_t, v); }
 
@@ -108,18 +106,34 @@ __device__ __forceinline__ void group_sums(const Act32& a, float& S, float& C) {
   C = fmaf(1024.f, s1024, 64.f * s64);
 }
 
+// The two exponent patterns live in VGPRs: with the masks in SGPRs each
+// (v & mask) | magic is then a single v_and_or_b32 (a VOP3 instruction here
+// takes at most one scalar operand and no literal).
+struct Magic {
+  uint32_t m1024, m64;
+};
+
+// 0x6400 is fp16 1024.0 (mantissa ulp 1: a value at bits 0..3 adds itself);
+// 0x5400 is fp16 64.0 (ulp 1/16: a value at bits 4..7 adds itself).
+__device__ __forceinline__ Magic make_magic() {
+  Magic m;
+  asm volatile("v_mov_b32 %0, 0x64006400" : "=v"(m.m1024));
+  asm volatile("v_mov_b32 %0, 0x54005400" : "=v"(m.m64));
+  return m;
+}
+
 // acc = sum_k x_k * (offset_k + q_k) over one unit (4 dwords = 32 values).
-__device__ __forceinline__ float unit_dot(const uint4& w, const Act32& a) {
+__device__ __forceinline__ float unit_dot(const uint4& w, const Act32& a, const Magic& mg) {
   float acc = 0.f;
   const uint32_t wd[4] = {w.x, w.y, w.z, w.w};
 #pragma unroll
   for (int d = 0; d < 4; ++d) {
     const uint32_t v = wd[d];
     const uint32_t v8 = v >> 8;
-    acc = dot2(a.px[4 * d + 0], (v & kLoMask) | kMagic1024, acc);
-    acc = dot2(a.px[4 * d + 1], (v & kHiMask) | kMagic64, acc);
-    acc = dot2(a.px[4 * d + 2], (v8 & kLoMask) | kMagic1024, acc);
-    acc = dot2(a.px[4 * d + 3], (v8 & kHiMask) | kMagic64, acc);
+    acc = dot2(a.px[4 * d + 0], (v & kLoMask) | mg.m1024, acc);
+    acc = dot2(a.px[4 * d + 1], (v & kHiMask) | mg.m64, acc);
+    acc = dot2(a.px[4 * d + 2], (v8 & kLoMask) | mg.m1024, acc);
+    acc = dot2(a.px[4 * d + 3], (v8 & kHiMask) | mg.m64, acc);
   }
   return acc;
 }
@@ -128,7 +142,7 @@ __device__ __forceinline__ float silu_mul(float g, float u) {
   return g / (1.0f + __expf(-g)) * u;
 }
 
-// Cross-lane sums in the VALU (DPP and gfx950 permlane swaps), no LDS round trip.
+// Cross-lane sums in the VALU (DPP row operations and lane shuffles), no LDS round trip.
 template <int CTRL>
 __device__ __forceinline__ float dpp(float v) {
   return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
@@ -175,8 +189,6 @@ __device__ __forceinline__ float sum_lane_bits_0to2(float v) {
 // routing compaction of n <= 256 slots inside one workgroup (LDS only).
 // Canonical order: experts ascending, rows of a segment by ascending slot,
 // invalid slots (ids outside [0, E)) after all valid ones in slot order.
-// Every stage kernel runs this in its prologue, so the only global-memory
-// round trip before the weight loads is the read of the n routed ids.
 // ---------------------------------------------------------------------------
 constexpr int kMaxSlots = AWQ_MOE_KMAX_SLOTS;
 constexpr int kNoKey = 0x7FFFFFFF;
@@ -274,393 +286,153 @@ __global__ __launch_bounds__(256) void route_compact_kernel(const int32_t* __res
 }
 
 // ---------------------------------------------------------------------------
-// Segment discovery inside the stage kernels, without sorting. Each wave
-// holds the routed ids of up to 256 slots in registers (slot c*64 + lane in
-// chunk c); a ballot gives the 64-bit mask of slots that share an id, so the
-// rows of a segment come out in ascending slot order for free.
-// ---------------------------------------------------------------------------
-struct SlotIds {
-  int v[4];  // id of slot c*64 + lane, -1 when invalid or past n
-};
-
-__device__ __forceinline__ SlotIds load_slot_ids(const int32_t* __restrict__ ids, int n, int E) {
-  SlotIds r;
-  const int lane = threadIdx.x & 63;
-#pragma unroll
-  for (int c = 0; c < 4; ++c) {
-    const int l = c * 64 + lane;
-    int v = -1;
-    if (l < n) {
-      v = ids[l];
-      if (v < 0 || v >= E) v = -1;
-    }
-    r.v[c] = v;
-  }
-  return r;
-}
-
-__device__ __forceinline__ void same_id_masks(const SlotIds& ids, int id, int n, uint64_t (&m)[4]) {
-#pragma unroll
-  for (int c = 0; c < 4; ++c) m[c] = (c * 64 < n) ? __ballot(ids.v[c] == id) : 0ull;
-}
-
-// Pop the lowest slot of a 256-bit mask (-1 when empty). Uniform.
-__device__ __forceinline__ int pop_slot(uint64_t (&m)[4]) {
-  int res = -1;
-#pragma unroll
-  for (int c = 0; c < 4; ++c) {
-    if (res < 0 && m[c] != 0ull) {
-      res = c * 64 + __builtin_ctzll(m[c]);
-      m[c] &= m[c] - 1;
-    }
-  }
-  return res;
-}
-
-// ---------------------------------------------------------------------------
-// The routing plan for W2, built by one workgroup of the W13 launch while the
-// other workgroups stream W13. All phases are parallel over slots:
-//  1. insert every valid slot's expert into an LDS hash table (open
-//     addressing, atomicCAS), keeping the lowest slot and the count per expert;
-//  2. wave 0 numbers the segments in order of their lowest slot (ballots) and
-//     turns the counts into offsets (wave prefix sums);
-//  3. every slot takes a place in its segment's slot list (atomic fill; the
-//     order inside a segment does not change any result, since every slot is
-//     computed independently) and ranks itself inside its token by
-//     (expert, slot), which fixes the order of the token's final sum.
-// ---------------------------------------------------------------------------
-constexpr int kHashBits = 9;
-constexpr int kHash = 1 << kHashBits;  // > kMaxSlots, so probing always ends
-static_assert(kHash > kMaxSlots, "hash table must exceed the slot count");
-
-struct PlanLds {
-  int tab_key[kHash];   // expert id, -1 empty
-  int tab_min[kHash];   // lowest slot of the expert; then its segment index
-  int tab_cnt[kHash];   // slots of the expert
-  int tab_fill[kHash];  // placement counter
-  int entry[kMaxSlots];  // slot -> table entry, -1 invalid
-  int key[kMaxSlots];    // slot -> expert id, -1 invalid
-  int seg_off[kMaxSlots + 1];
-};
-
-__device__ __forceinline__ int hash_slot(int k) {
-  return (int)(((uint32_t)k * 2654435761u) >> (32 - kHashBits));
-}
-
-__device__ __forceinline__ int wave_inclusive_sum(int v) {
-  const int lane = threadIdx.x & 63;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const int u = __shfl_up(v, o);
-    if (lane >= o) v += u;
-  }
-  return v;
-}
-
-__device__ void build_plan(const int32_t* __restrict__ topk_ids, int M, int topk, int E, Plan* __restrict__ plan,
-                           uint32_t* __restrict__ status, PlanLds& P) {
-  const int n = M * topk;
-  const int t = threadIdx.x, lane = t & 63, bd = blockDim.x;
-  for (int i = t; i < kHash; i += bd) {
-    P.tab_key[i] = -1;
-    P.tab_min[i] = 0x7FFFFFFF;
-    P.tab_cnt[i] = 0;
-    P.tab_fill[i] = 0;
-  }
-  __syncthreads();
-  int bad = 0;
-  for (int s = t; s < n; s += bd) {
-    const int v = topk_ids[s];
-    const int k = (v >= 0 && v < E) ? v : -1;
-    P.key[s] = k;
-    int h = -1;
-    if (k >= 0) {
-      h = hash_slot(k);
-      for (;;) {
-        const int old = atomicCAS(&P.tab_key[h], -1, k);
-        if (old == -1 || old == k) break;
-        h = (h + 1) & (kHash - 1);
-      }
-      atomicMin(&P.tab_min[h], s);
-      atomicAdd(&P.tab_cnt[h], 1);
-    } else {
-      bad = 1;
-    }
-    P.entry[s] = h;
-  }
-  bad = __syncthreads_or(bad);
-  if (t == 0 && status != nullptr) *status = bad ? AWQ_MOE_STATUS_BAD_ID_BIT : 0u;
-  if (t < 64) {
-    int nseg = 0, off = 0;
-    for (int c = 0; c * 64 < n; ++c) {
-      const int sl = c * 64 + lane;
-      const int h = sl < n ? P.entry[sl] : -1;
-      const bool leader = h >= 0 && P.tab_min[h] == sl;
-      const uint64_t lm = __ballot(leader);
-      const int cnt = leader ? P.tab_cnt[h] : 0;
-      const int incl = wave_inclusive_sum(cnt);
-      if (leader) {
-        const int seg = nseg + (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(lm >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)lm, 0));
-        const int o = off + incl - cnt;
-        P.tab_min[h] = seg;  // from here on: the expert's segment index
-        P.seg_off[seg] = o;
-        plan->seg_off[seg] = o;
-        plan->seg_e[seg] = P.key[sl];
-      }
-      nseg += __builtin_popcountll(lm);
-      off += __shfl(incl, 63);
-    }
-    if (lane == 0) {
-      P.seg_off[nseg] = off;
-      plan->seg_off[nseg] = off;
-      plan->num_segments = nseg;
-    }
-  }
-  __syncthreads();
-  for (int s = t; s < n; s += bd) {
-    const int h = P.entry[s];
-    const int tok = s / topk, j = s - tok * topk, base = tok * topk;
-    if (h >= 0) {
-      const int pos = P.seg_off[P.tab_min[h]] + atomicAdd(&P.tab_fill[h], 1);
-      plan->seg_slots[pos] = s;
-      const int id = P.key[s];
-      int r = 0;
-      for (int j2 = 0; j2 < topk; ++j2) {
-        const int k2 = P.key[base + j2];
-        r += (k2 >= 0) & ((k2 < id) | ((k2 == id) & (j2 < j)));
-      }
-      plan->order[base + r] = s;
-    }
-    if (j == 0) {
-      int c = 0;
-      for (int j2 = 0; j2 < topk; ++j2) c += P.key[base + j2] >= 0;
-      plan->cnt[tok] = c;
-    }
-  }
-}
-
-// ---------------------------------------------------------------------------
-// W13 + SwiGLU: grid (2I/16 column tiles, 1 + n). Row 0 of the grid builds
-// the routing plan (tile 0 only). The workgroup of slot s = blockIdx.y - 1
-// works only when s is the lowest slot routed to its expert: it streams one
-// 16-column tile of that expert over all of K once and applies it to every
-// slot routed to the expert (a multi-row segment). act is indexed by slot.
+// W13 + SwiGLU: grid (2I/16 column tiles, n slots). The workgroup of slot s
+// reads its expert id with one scalar load and at once requests its expert's
+// 16-column tile (all of K) and its token's activation row, then writes
+// act[s] for that tile. Slots that share an expert read the same tile; the
+// second and later reads are served by L2 or the MALL (all of them request
+// it within the same few hundred nanoseconds), which measured faster than
+// first electing one workgroup per expert from the routed ids.
+// Workgroup (0, 0) also writes the status word.
 // ---------------------------------------------------------------------------
 template <int RB>
 __global__ __launch_bounds__(1024) void w13_swiglu_kernel(StageArgs a, const uint16_t* __restrict__ x,
-                                                          uint16_t* __restrict__ act, Plan* __restrict__ plan,
-                                                          uint32_t* __restrict__ status) {
-  constexpr int R = 2;  // rows per pass
-  __shared__ float red[16][R][16];  // [wave][row][column]
-  __shared__ PlanLds plan_lds;
-  const int n = a.M * a.topk;
-  const int nt = blockIdx.x;
-  if (blockIdx.y == 0) {
-    if (nt == 0) build_plan(a.topk_ids, a.M, a.topk, a.E, plan, status, plan_lds);
-    return;
-  }
-  const int s = blockIdx.y - 1;
+                                                          uint16_t* __restrict__ act, uint32_t* __restrict__ status) {
+  __shared__ float red[16][16];  // [wave][column]
+  const int nt = blockIdx.x, s = blockIdx.y;
   const int t = threadIdx.x;
   const int lane = t & 63, wave = t >> 6, nwaves = blockDim.x >> 6;
-  const int H = a.H, I = a.I, topk = a.topk;
+  const int H = a.H, I = a.I;
   const int G = H >> 5;
   const int L = 4 * G;
-  const bool active = t < L;
   const int g = t >> 2;
-  const int my = a.topk_ids[s];
-  const SlotIds ids = load_slot_ids(a.topk_ids, n, a.E);
-  if (my < 0 || my >= a.E) return;
-  const uint8_t* blk = a.bank + (uint64_t)my * a.expert_bytes;
-  uint4 w[4];
-  Records<RB> rec;
-  Act32 x0;
-  // With one token every slot reads the same activation row and an expert
-  // repeats only when the caller passes duplicate ids, so the tile and the
-  // row are requested before the leader check (which needs all n ids).
-  const bool early = (a.M == 1);
-  if (early && active) {
+  if (status != nullptr && nt == 0 && s == 0) {
+    int bad = 0;
+    for (int i = t; i < a.M * a.topk; i += blockDim.x) {
+      const int v = a.topk_ids[i];
+      bad |= (v < 0 || v >= a.E);
+    }
+    bad = __syncthreads_or(bad);
+    if (t == 0) *status = bad ? AWQ_MOE_STATUS_BAD_ID_BIT : 0u;
+  }
+  const int e = a.topk_ids[s];
+  if (e < 0 || e >= a.E) return;  // invalid slot: no row
+  float part[4] = {0.f, 0.f, 0.f, 0.f};
+  if (t < L) {
+    const uint8_t* blk = a.bank + (uint64_t)e * a.expert_bytes;
     const uint8_t* units = blk + a.w13_off + (uint64_t)nt * 256u * G;
+    uint4 w[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) w[j] = *reinterpret_cast<const uint4*>(units + ((uint64_t)j * L + t) * 16u);
-    rec = load_records<RB>(blk + a.w13_meta_off + (uint64_t)nt * 16u * G * RB + (uint64_t)t * 4u * RB);
-    x0 = load_act32(x + 32 * g);
+    const Records<RB> rec = load_records<RB>(blk + a.w13_meta_off + (uint64_t)nt * 16u * G * RB + (uint64_t)t * 4u * RB);
+    const Act32 av = load_act32(x + (uint64_t)(s / a.topk) * H + 32 * g);
+    float S, Cs;
+    group_sums(av, S, Cs);
+    const Magic mg = make_magic();
+#pragma unroll
+    for (int j = 0; j < 4; ++j) part[j] = rec.s[j] * (unit_dot(w[j], av, mg) - fmaf(rec.z[j], S, Cs));
   }
-  uint64_t rows[4];
-  same_id_masks(ids, my, n, rows);
-  {
-    uint64_t probe[4] = {rows[0], rows[1], rows[2], rows[3]};
-    if (pop_slot(probe) != s) return;  // another slot leads this expert
-  }
-  if (!early && active) {
-    const uint8_t* units = blk + a.w13_off + (uint64_t)nt * 256u * G;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) w[j] = *reinterpret_cast<const uint4*>(units + ((uint64_t)j * L + t) * 16u);
-    rec = load_records<RB>(blk + a.w13_meta_off + (uint64_t)nt * 16u * G * RB + (uint64_t)t * 4u * RB);
-  }
-  for (;;) {
-    int slot[R];
-    int rowsn = 0;
-#pragma unroll
-    for (int rr = 0; rr < R; ++rr) {
-      slot[rr] = pop_slot(rows);
-      rowsn += slot[rr] >= 0;
-    }
-    if (rowsn == 0) break;
-    float part[R][4];
-#pragma unroll
-    for (int rr = 0; rr < R; ++rr) {
-#pragma unroll
-      for (int j = 0; j < 4; ++j) part[rr][j] = 0.f;
-      if (active && rr < rowsn) {
-        const Act32 av = early ? x0 : load_act32(x + (uint64_t)(slot[rr] / topk) * H + 32 * g);
-        float S, Cs;
-        group_sums(av, S, Cs);
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const float acc = unit_dot(w[j], av);
-          part[rr][j] = rec.s[j] * (acc - fmaf(rec.z[j], S, Cs));
-        }
-      }
-    }
-    // Sum over the 16 groups of this wave (lane bits 2..5): lane l ends with
-    // column 4*(l & 3) + 2*b4 + b5 of the tile.
-#pragma unroll
-    for (int rr = 0; rr < R; ++rr) {
-      if (rr < rowsn) {
-        const float v = sum4_lane_bits_2to5(part[rr][0], part[rr][1], part[rr][2], part[rr][3]);
-        if ((lane & 12) == 0) red[wave][rr][4 * (lane & 3) + 2 * ((lane >> 4) & 1) + (lane >> 5)] = v;
-      }
-    }
-    __syncthreads();
-    if (t < 16 * R) {  // wave 0 (R <= 4)
-      const int col = t & 15, rr = t >> 4;
-      float h = 0.f;
-      for (int wv = 0; wv < nwaves; ++wv) h += red[wv][rr][col];
-      const float other = __shfl_xor(h, 1);  // partner column: gate <-> up
-      int sl = -1;
-#pragma unroll
-      for (int q = 0; q < R; ++q)
-        if (q == rr) sl = slot[q];
-      if (!(col & 1) && rr < rowsn) {
-        const float v = silu_mul(h, other);
-        act[(uint64_t)sl * I + nt * 8 + (col >> 1)] = __builtin_bit_cast(uint16_t, (_Float16)v);
-      }
-    }
-    if (rowsn < R) break;
-    __syncthreads();
+  // Sum over the 16 groups of this wave (lane bits 2..5): lane l ends with
+  // column 4*(l & 3) + 2*b4 + b5 of the tile.
+  const float v = sum4_lane_bits_2to5(part[0], part[1], part[2], part[3]);
+  if ((lane & 12) == 0) red[wave][4 * (lane & 3) + 2 * ((lane >> 4) & 1) + (lane >> 5)] = v;
+  __syncthreads();
+  if (t < 16) {
+    float h = 0.f;
+    for (int wv = 0; wv < nwaves; ++wv) h += red[wv][t];
+    const float other = __shfl_xor(h, 1);  // partner column: gate <-> up
+    if (!(t & 1)) act[(uint64_t)s * I + nt * 8 + (t >> 1)] = __builtin_bit_cast(uint16_t, (_Float16)silu_mul(h, other));
   }
 }
 
 // ---------------------------------------------------------------------------
-// W2 + router-weighted reduction: grid (H/8 column tiles). One workgroup owns
-// 8 output columns for all tokens. It loads the routing plan in one round
-// trip; lane groups stream each segment's W2 tile once and apply it to every
-// slot of the segment; the K groups of a slot are summed by shuffles into one
-// partial per slot; each token then sums its slots' partials in ascending
-// expert order (ties by slot), so the result depends only on the set of
-// (expert, weight) pairs of the token.
-// Lanes: slot group sl (SS of them) x column quad (2) x group gp (GP, the
-// power of two >= I/32; lanes with gp >= I/32 idle at the loads).
+// W2 + router-weighted reduction: grid (H/16 column tiles, M tokens). The
+// workgroup of (tile, token) streams the 16-column W2 tile of each of the
+// token's routed experts (all of K = I) and sums the slots in LDS, so no
+// partial result crosses workgroups and no workspace is written.
+// Lanes: u = slot*LS + t with LS = 4*G2 lanes per slot and t = 4g + quad as
+// in the layout; slots beyond what one block holds are taken in passes.
+// Slot order of the final sum: ascending (expert, slot) over the valid slots,
+// so the result depends only on the set of (expert, weight) pairs and not on
+// the order of the token's top-k list. Wave 0 ranks the slots with lane
+// shuffles while the weight loads are in flight.
 // ---------------------------------------------------------------------------
 template <int RB>
-__global__ __launch_bounds__(512) void w2_reduce_kernel(StageArgs a, const uint16_t* __restrict__ act,
-                                                        const float* __restrict__ topk_w,
-                                                        const Plan* __restrict__ plan, int SS, int GP,
-                                                        uint16_t* __restrict__ out) {
-  __shared__ int seg_e[kMaxSlots];
-  __shared__ int seg_off[kMaxSlots + 1];
-  __shared__ int seg_slots[kMaxSlots];
-  __shared__ int order[kMaxSlots];
-  __shared__ float wts[kMaxSlots];
-  __shared__ float ybuf[kMaxSlots][8];
-  __shared__ int cnt[AWQ_MOE_KMAX_TOKENS];
-  __shared__ int nseg_s;
-  const int M = a.M, topk = a.topk, H = a.H, I = a.I;
-  const int n = M * topk;
-  const int nt = blockIdx.x;
+__global__ __launch_bounds__(1024) void w2_reduce_kernel(StageArgs a, const uint16_t* __restrict__ act,
+                                                         const float* __restrict__ topk_w,
+                                                         uint16_t* __restrict__ out) {
+  __shared__ float red[4096];                      // [slot in pass][g][16]; SPP*G2*16 <= 4096
+  __shared__ float ys[AWQ_MOE_KMAX_TOPK * 16];     // [slot][16]: the slot's 16 column results
+  __shared__ int ord[AWQ_MOE_KMAX_TOPK];           // rank -> slot
+  __shared__ float wr[AWQ_MOE_KMAX_TOPK];          // rank -> router weight
+  __shared__ int nvalid_s;
+  const int nt = blockIdx.x, tok = blockIdx.y;
   const int t = threadIdx.x;
+  const int H = a.H, I = a.I, topk = a.topk, E = a.E;
+  const int G2 = I >> 5, LS = 4 * G2;
+  const int spp = blockDim.x / LS;                 // slots per pass (>= 1)
+  const int32_t* ids = a.topk_ids + tok * topk;
 
-  for (int i = t; i < n; i += blockDim.x) {
-    seg_e[i] = plan->seg_e[i];
-    seg_off[i] = plan->seg_off[i];
-    seg_slots[i] = plan->seg_slots[i];
-    order[i] = plan->order[i];
-    wts[i] = topk_w[i];
-  }
-  if (t == 0) {
-    seg_off[n] = plan->seg_off[n];
-    nseg_s = plan->num_segments;
-  }
-  if (t < M) cnt[t] = plan->cnt[t];
-  __syncthreads();
-
-  const int G2 = I >> 5;
-  const int L2p = 2 * GP;
-  const int sl = t / L2p, tl = t - sl * L2p;
-  const int quad = tl / GP, gp = tl - quad * GP;
-  const int nseg = nseg_s;
-  const bool loader = (sl < SS) && (gp < G2);
-  // Segment tiles are software-pipelined: the next segment's W2 tile and first
-  // activation row are requested before the current segment is computed.
-  const int tli = 2 * gp + quad;  // lane of the bank layout
-  auto issue = [&](int seg, uint4 (&w)[4], Records<RB>& rec, Act32& first) {
-    const uint8_t* blk = a.bank + (uint64_t)seg_e[seg] * a.expert_bytes;
-    const uint8_t* units = blk + a.w2_off + (uint64_t)nt * 128u * G2;
+  for (int s0 = 0; s0 < topk; s0 += spp) {
+    const int sp = t / LS, tl = t - sp * LS;
+    const int slot = s0 + sp;
+    const bool lane_on = sp < spp && slot < topk;
+    const int e = lane_on ? ids[slot] : -1;
+    const bool live = lane_on && e >= 0 && e < E;
+    uint4 w[4];
+    Records<RB> rec;
+    Act32 av;
+    const int g = tl >> 2, quad = tl & 3;
+    if (live) {
+      const uint8_t* blk = a.bank + (uint64_t)e * a.expert_bytes;
+      const uint8_t* units = blk + a.w2_off + (uint64_t)nt * 256u * G2;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) w[j] = *reinterpret_cast<const uint4*>(units + ((uint64_t)j * (2 * G2) + tli) * 16u);
-    rec = load_records<RB>(blk + a.w2_meta_off + (uint64_t)nt * 8u * G2 * RB + (uint64_t)tli * 4u * RB);
-    first = load_act32(act + (uint64_t)seg_slots[seg_off[seg]] * I + 32 * gp);
-  };
-  if (sl < SS) {
-    uint4 w[4], wn[4];
-    Records<RB> rec, recn;
-    Act32 cur, curn;
-    if (loader && sl < nseg) issue(sl, w, rec, cur);
-    for (int seg = sl; seg < nseg; seg += SS) {
-      const int r_begin = seg_off[seg], r_end = seg_off[seg + 1];
-      const bool more = seg + SS < nseg;
-      if (loader && more) issue(seg + SS, wn, recn, curn);
-      for (int r = r_begin; r < r_end; ++r) {
-        const int slot = seg_slots[r];
-        if (loader && r > r_begin) cur = load_act32(act + (uint64_t)slot * I + 32 * gp);
-        float y[4] = {0.f, 0.f, 0.f, 0.f};
-        if (loader) {
-          float S, Cs;
-          group_sums(cur, S, Cs);
-#pragma unroll
-          for (int j = 0; j < 4; ++j) y[j] = rec.s[j] * (unit_dot(w[j], cur) - fmaf(rec.z[j], S, Cs));
-        }
-        if (GP == 8) {
-#pragma unroll
-          for (int j = 0; j < 4; ++j) y[j] = sum_lane_bits_0to2(y[j]);
-        } else {
-          for (int o = 1; o < GP; o <<= 1)
-#pragma unroll
-            for (int j = 0; j < 4; ++j) y[j] += __shfl_xor(y[j], o);
-        }
-        if (gp == 0) {
-#pragma unroll
-          for (int j = 0; j < 4; ++j) ybuf[slot][4 * quad + j] = y[j];
-        }
+      for (int j = 0; j < 4; ++j) w[j] = *reinterpret_cast<const uint4*>(units + ((uint64_t)j * LS + tl) * 16u);
+      rec = load_records<RB>(blk + a.w2_meta_off + (uint64_t)nt * 16u * G2 * RB + (uint64_t)tl * 4u * RB);
+      av = load_act32(act + (uint64_t)(tok * topk + slot) * I + 32 * g);
+    }
+    if (s0 == 0 && t < 64) {
+      const int id = t < topk ? ids[t] : -1;
+      const float wt = t < topk ? topk_w[tok * topk + t] : 0.f;
+      const bool v = t < topk && id >= 0 && id < E;
+      int r = 0;
+      for (int j2 = 0; j2 < topk; ++j2) {
+        const int k2 = __shfl(id, j2);
+        r += (k2 >= 0 && k2 < E) & ((k2 < id) | ((k2 == id) & (j2 < t)));
       }
-      if (more) {
+      if (v) {
+        ord[r] = t;
+        wr[r] = wt;
+      }
+      const unsigned long long b = __ballot(v);
+      if (t == 0) nvalid_s = (int)__popcll(b);
+    }
+    if (live) {
+      float S, Cs;
+      group_sums(av, S, Cs);
+      const Magic mg = make_magic();
 #pragma unroll
-        for (int j = 0; j < 4; ++j) w[j] = wn[j];
-        rec = recn;
-        cur = curn;
+      for (int j = 0; j < 4; ++j)
+        red[(sp * G2 + g) * 16 + 4 * quad + j] = rec.s[j] * (unit_dot(w[j], av, mg) - fmaf(rec.z[j], S, Cs));
+    }
+    __syncthreads();
+    // per-slot column results of this pass, groups summed in ascending g
+    // (rows of invalid slots hold stale values and are never read)
+    for (int u = t; u < spp * 16; u += blockDim.x) {
+      const int ps = u >> 4, c = u & 15;
+      if (s0 + ps < topk) {
+        float y = 0.f;
+        for (int gg = 0; gg < G2; ++gg) y += red[(ps * G2 + gg) * 16 + c];
+        ys[(s0 + ps) * 16 + c] = y;
       }
     }
+    __syncthreads();
   }
-  __syncthreads();
-  for (int i = t; i < M * 8; i += blockDim.x) {
-    const int tt = i >> 3, col = i & 7;
-    float v = 0.f;
-    const int c = cnt[tt];
-    for (int r = 0; r < c; ++r) {
-      const int slot = order[tt * topk + r];
-      v = fmaf(wts[slot], ybuf[slot][col], v);
-    }
-    out[(uint64_t)tt * H + nt * 8 + col] = __builtin_bit_cast(uint16_t, (_Float16)v);
+  if (t < 16) {
+    const int nv = nvalid_s;
+    float acc = 0.f;
+    for (int r = 0; r < nv; ++r) acc = fmaf(wr[r], ys[ord[r] * 16 + t], acc);
+    out[(uint64_t)tok * H + nt * 16 + t] = __builtin_bit_cast(uint16_t, (_Float16)acc);
   }
 }
 
@@ -669,7 +441,7 @@ __global__ __launch_bounds__(512) void w2_reduce_kernel(StageArgs a, const uint1
 // ---------------------------------------------------------------------------
 template <int RB>
 __global__ void dequant_kernel(const uint8_t* __restrict__ bank, uint64_t expert_bytes,
-                               uint64_t units_off, uint64_t meta_off, int which, int K, int N,
+                               uint64_t units_off, uint64_t meta_off, int K, int N,
                                int expert_begin, int expert_count, float* __restrict__ out) {
   const int G = K >> 5;
   const uint64_t per_expert = (uint64_t)G * N;
@@ -678,16 +450,10 @@ __global__ void dequant_kernel(const uint8_t* __restrict__ bank, uint64_t expert
   const int el = (int)(idx / per_expert);
   const int rem = (int)(idx - (uint64_t)el * per_expert);
   const int g = rem / N, n = rem - g * N;
-  uint64_t uo, ro;
-  if (which == 0) {
-    const int L = 4 * G, nt = n >> 4, c = n & 15, quad = c >> 2, j = c & 3, t = 4 * g + quad;
-    uo = (uint64_t)nt * 256u * G + ((uint64_t)j * L + t) * 16u;
-    ro = (uint64_t)nt * 16u * G * RB + (uint64_t)(4 * t + j) * RB;
-  } else {
-    const int L = 2 * G, nt = n >> 3, c = n & 7, quad = c >> 2, j = c & 3, t = 2 * g + quad;
-    uo = (uint64_t)nt * 128u * G + ((uint64_t)j * L + t) * 16u;
-    ro = (uint64_t)nt * 8u * G * RB + (uint64_t)(4 * t + j) * RB;
-  }
+  // W13 and W2 share the tiled placement (16-column tiles, t = 4g + quad).
+  const int L = 4 * G, nt = n >> 4, c = n & 15, quad = c >> 2, j = c & 3, t = 4 * g + quad;
+  const uint64_t uo = (uint64_t)nt * 256u * G + ((uint64_t)j * L + t) * 16u;
+  const uint64_t ro = (uint64_t)nt * 16u * G * RB + (uint64_t)(4 * t + j) * RB;
   const uint8_t* blk = bank + (uint64_t)(expert_begin + el) * expert_bytes;
   const uint4 w = *reinterpret_cast<const uint4*>(blk + units_off + uo);
   const uint8_t* rp = blk + meta_off + ro;
@@ -713,57 +479,45 @@ hipError_t launch_route_compact(const int32_t* ids, int n, int E, const RouteOut
   return hipGetLastError();
 }
 
-hipError_t launch_w13_swiglu(const StageArgs& a, const uint16_t* x, uint16_t* act, Plan* plan, uint32_t* status,
+hipError_t launch_w13_swiglu(const StageArgs& a, const uint16_t* x, uint16_t* act, uint32_t* status,
                              hipStream_t stream) {
   const int L = 4 * (a.H / 32);
   const dim3 block(((L + 63) / 64) * 64);
-  const dim3 grid((2 * a.I) / 16, 1 + a.M * a.topk);
+  const dim3 grid((2 * a.I) / 16, a.M * a.topk);
   if (a.RB == 4)
-    hipLaunchKernelGGL(w13_swiglu_kernel<4>, grid, block, 0, stream, a, x, act, plan, status);
+    hipLaunchKernelGGL(w13_swiglu_kernel<4>, grid, block, 0, stream, a, x, act, status);
   else
-    hipLaunchKernelGGL(w13_swiglu_kernel<3>, grid, block, 0, stream, a, x, act, plan, status);
+    hipLaunchKernelGGL(w13_swiglu_kernel<3>, grid, block, 0, stream, a, x, act, status);
   return hipGetLastError();
 }
 
-W2Shape w2_shape(int I, int n) {
-  W2Shape sh;
-  const int G2 = I / 32;
-  sh.GP = 1;
-  while (sh.GP < G2) sh.GP <<= 1;
-  const int L2p = 2 * sh.GP;
-  int ss = 256 / L2p;
-  if (ss > 16) ss = 16;
-  if (ss > n) ss = n;
-  if (ss < 1) ss = 1;
-  sh.SS = ss;
-  sh.threads = ((ss * L2p + 63) / 64) * 64;
-  return sh;
-}
-
-hipError_t launch_w2_reduce(const StageArgs& a, const uint16_t* act, const float* topk_w, const Plan* plan,
-                            uint16_t* out, hipStream_t stream) {
-  const W2Shape sh = w2_shape(a.I, a.M * a.topk);
-  const dim3 block(sh.threads);
-  const dim3 grid(a.H / 8);
+hipError_t launch_w2_reduce(const StageArgs& a, const uint16_t* act, const float* topk_w, uint16_t* out,
+                            hipStream_t stream) {
+  const int LS = 4 * (a.I / 32);
+  const int lanes = a.topk * LS;
+  const dim3 block(lanes >= 1024 ? 1024 : ((lanes + 63) / 64) * 64);
+  const dim3 grid(a.H / 16, a.M);
   if (a.RB == 4)
-    hipLaunchKernelGGL(w2_reduce_kernel<4>, grid, block, 0, stream, a, act, topk_w, plan, sh.SS, sh.GP, out);
+    hipLaunchKernelGGL(w2_reduce_kernel<4>, grid, block, 0, stream, a, act, topk_w, out);
   else
-    hipLaunchKernelGGL(w2_reduce_kernel<3>, grid, block, 0, stream, a, act, topk_w, plan, sh.SS, sh.GP, out);
+    hipLaunchKernelGGL(w2_reduce_kernel<3>, grid, block, 0, stream, a, act, topk_w, out);
   return hipGetLastError();
 }
 
 hipError_t launch_dequant(const uint8_t* bank, uint64_t expert_bytes, uint64_t units_off,
-                          uint64_t meta_off, int RB, int which, int K, int N, int expert_begin,
+                          uint64_t meta_off, int RB, int which, int H, int I, int expert_begin,
                           int expert_count, float* out, hipStream_t stream) {
+  const int K = which == 0 ? H : I;
+  const int N = which == 0 ? 2 * I : H;
   const uint64_t total = (uint64_t)(K / 32) * N * expert_count;
   const dim3 block(256);
   const dim3 grid((unsigned)((total + 255) / 256));
   if (RB == 4)
     hipLaunchKernelGGL(dequant_kernel<4>, grid, block, 0, stream, bank, expert_bytes, units_off,
-                       meta_off, which, K, N, expert_begin, expert_count, out);
+                       meta_off, K, N, expert_begin, expert_count, out);
   else
     hipLaunchKernelGGL(dequant_kernel<3>, grid, block, 0, stream, bank, expert_bytes, units_off,
-                       meta_off, which, K, N, expert_begin, expert_count, out);
+                       meta_off, K, N, expert_begin, expert_count, out);
   return hipGetLastError();
 }
 

@@ -43,7 +43,7 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=200)
     p.add_argument("--warmup", type=int, default=20)
-    p.add_argument("--only", default="", help="comma list of workloads: m1_hot,m1_cold,m8_pool")
+    p.add_argument("--only", default="", help="comma list of workloads: m1_hot,m1_cold,m8_pool,m8_distinct")
     p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     return p.parse_args()
 
@@ -118,12 +118,12 @@ def measure(abi, torch, wl: Workload, steps, warmup):
 
     def w2():
         for c in range(CALLS):
-            abi.awq_moe_w2_reduce(wl.dims, wl.bank, wl.w[c], wl.ws[c], out=wl.out)
+            abi.awq_moe_w2_reduce(wl.dims, wl.bank, wl.ids[c], wl.w[c], wl.ws[c], out=wl.out)
 
     route()
     torch.cuda.synchronize()
     res = {}
-    # "layer" = awq_moe_decode (the stage kernels compact the ids themselves);
+    # "layer" = awq_moe_decode (two launches, one workgroup per slot and tile);
     # "route" = the standalone awq_moe_route_compact kernel, not part of the layer.
     for name, fn in (("layer", full), ("route", route), ("w13", w13), ("w2", w2)):
         g = capture(torch, fn)
@@ -214,7 +214,7 @@ def main():
     from awq_int4_mixture_amd import abi
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     torch.cuda.set_device(0)
-    only = set(filter(None, args.only.split(","))) or {"m1_hot", "m1_cold", "m8_pool"}
+    only = set(filter(None, args.only.split(","))) or {"m1_hot", "m1_cold", "m8_pool", "m8_distinct"}
 
     t_gen = time.perf_counter()
     bi = inputs.bank_inputs(SEED, E, H, I)
@@ -222,7 +222,7 @@ def main():
     for rb in (4, 3):
         if rb == 4 and "m1_hot" not in only:
             continue
-        if rb == 3 and not ({"m1_cold", "m8_pool"} & only):
+        if rb == 3 and not ({"m1_cold", "m8_pool", "m8_distinct"} & only):
             continue
         dims = abi.make_dims(E, H, I, rb)
         banks[rb] = (dims, torch.from_numpy(abi.prepare_from_inputs(dims, bi)).to("cuda"))
@@ -249,6 +249,11 @@ def main():
             ids = [inputs.ids_shared_pool(inputs.call_rng(SEED, 300 + c), 8, K_TOP, E) for c in range(CALLS)]
             wl = Workload("m8_pool", abi, torch, dims, bank, ids, 8, rng, per_expert_bytes(abi, dims))
             results["m8_pool"] = measure(abi, torch, wl, args.steps, args.warmup)
+        if "m8_distinct" in only:
+            dims, bank = banks[3]
+            ids = [inputs.ids_all_distinct(inputs.call_rng(SEED, 400 + c), 8, K_TOP, E) for c in range(CALLS)]
+            wl = Workload("m8_distinct", abi, torch, dims, bank, ids, 8, rng, per_expert_bytes(abi, dims))
+            results["m8_distinct"] = measure(abi, torch, wl, args.steps, args.warmup)
         ceiling = copy_ceiling(torch)
 
     head = results.get("m1_hot") or next(iter(results.values()))

@@ -35,12 +35,10 @@
  *   dword d (LE) holds k = 32g + 8d + p, p = 0..7, value p at bit
  *   4*(p>>1) + 16*(p&1). A record = bytes {scale lo, scale hi, zero} (+ a
  *   zero pad byte for 4-byte records). W13 column 2i is gate i, 2i+1 is up i.
- *   W13: tiles of 16 columns, G13 = H/32, L13 = 4*G13; column n, group g:
+ *   W13 (K = H, N = 2I) and W2 (K = I, N = H) use one tiled placement; with
+ *   G = K/32 and L = 4*G, column n, group g:
  *     nt = n/16, c = n%16, quad = c/4, j = c%4, t = 4g + quad,
- *     unit at nt*256*G13 + (j*L13 + t)*16, record at nt*16*G13*RB + (4t + j)*RB.
- *   W2: tiles of 8 columns, G2 = I/32, L2 = 2*G2:
- *     nt = n/8, c = n%8, quad = c/4, j = c%4, t = 2g + quad,
- *     unit at nt*128*G2 + (j*L2 + t)*16, record at nt*8*G2*RB + (4t + j)*RB.
+ *     unit at nt*256*G + (j*L + t)*16, record at nt*16*G*RB + (4t + j)*RB.
  *
  * Routing arrays (n = M*topk slots, flat slot s = t*topk + j):
  *   active_expert_ids[n]      segment -> expert id, ascending; -1 past num_active
@@ -117,12 +115,14 @@ int awq_moe_prepare(const awq_moe_dims* dims,
 int awq_moe_workspace_bytes(const awq_moe_dims* dims, int32_t max_tokens, int32_t topk,
                             uint64_t* out);
 
-/* Decode workspace layout (bytes): the uint32 status word at
- * AWQ_MOE_WS_STATUS_OFFSET (bit 0: some id was outside [0, E)); the routing
- * plan the W13 launch leaves for W2 (library-private, 256..4607); the fp16
- * intermediate act[M*topk][I], indexed by flat slot, at AWQ_MOE_WS_ACT_OFFSET. */
+/* Decode workspace layout (bytes), for n = M*topk slots: the uint32 status
+ * word at AWQ_MOE_WS_STATUS_OFFSET (bit 0: some id was outside [0, E)),
+ * written by every W13 launch; the fp16 intermediate act[n][I], indexed by
+ * flat slot, at AWQ_MOE_WS_ACT_OFFSET. A workspace sized for (max_tokens,
+ * topk) serves any M <= max_tokens with the same topk; it needs no
+ * initialisation. */
 #define AWQ_MOE_WS_STATUS_OFFSET 0
-#define AWQ_MOE_WS_ACT_OFFSET 4608
+#define AWQ_MOE_WS_ACT_OFFSET 256
 
 /* Compact routed ids into active-expert segments (PR #520, Purpose: multi-row
  * active-expert segments with offsets-based scheduling; Implementation: the op
@@ -142,14 +142,16 @@ int awq_moe_route_compact(const int32_t* topk_ids, int32_t M, int32_t topk, int3
  *   topk_ids device int32 [M][topk]; topk_w device fp32 [M][topk] (used as given)
  *   out      device fp16 [M][H], 16-byte aligned, overwritten:
  *            out[t] = fp16_rne(sum_j topk_w[t][j] * W2_e(silu(x_t Wg_e) * (x_t Wu_e))),
- *            e = topk_ids[t][j], accumulated in fp32 in a fixed order that
- *            depends only on the compacted segments.
+ *            e = topk_ids[t][j] over the valid ids, accumulated in fp32 over
+ *            the token's slots in ascending (expert, slot) order, so the
+ *            result does not depend on the order of a token's top-k list.
  *   workspace device, 256-byte aligned, >= awq_moe_workspace_bytes(dims, M, topk);
- *            receives the status word (offset AWQ_MOE_WS_STATUS_OFFSET) and
- *            the fp16 intermediate.
- * Launches two kernels on stream (W13 + SwiGLU, then W2 + reduction); each
- * groups the routed slots by expert itself, so no separate routing launch
- * precedes them. */
+ *            receives the status word and the fp16 intermediate.
+ * Launches two kernels on stream: W13 + SwiGLU with one workgroup per
+ * (slot, 16-column tile), then W2 + reduction with one workgroup per
+ * (token, 16-column tile) that sums the token's slots itself. Slots that
+ * share an expert read its tiles at about the same moment and all but the
+ * first read are served from cache, so no routing launch precedes them. */
 int awq_moe_decode(const awq_moe_dims* dims, const void* bank, const uint16_t* x,
                    const int32_t* topk_ids, const float* topk_w, int32_t M, int32_t topk,
                    uint16_t* out, void* workspace, uint64_t workspace_bytes, void* stream);
@@ -160,24 +162,26 @@ int awq_moe_decode(const awq_moe_dims* dims, const void* bank, const uint16_t* x
  * workspace. */
 
 /* W13 + SwiGLU for the routed ids topk_ids [M][topk] (device int32). Writes
- * the status word, the routing plan and act into workspace: act[s] =
+ * the status word and act into workspace: act[s] =
  * fp16(silu(x_t Wg_e) * (x_t Wu_e)) for each valid flat slot s = t*topk + j
- * (rows of invalid slots are not written). Each expert's W13 is streamed once
- * and applied to all its slots. One launch. */
+ * (rows of invalid slots are not written). One launch. */
 int awq_moe_w13_swiglu(const awq_moe_dims* dims, const void* bank, const uint16_t* x,
                        const int32_t* topk_ids, int32_t M, int32_t topk,
                        void* workspace, uint64_t workspace_bytes, void* stream);
 
-/* W2 + router-weighted reduction from the act and routing plan that
- * awq_moe_w13_swiglu left in workspace for the same M and topk (the caller
- * may overwrite act in between). topk_w device fp32 [M][topk]; out device
- * fp16 [M][H], overwritten. One launch. */
-int awq_moe_w2_reduce(const awq_moe_dims* dims, const void* bank, const float* topk_w,
-                      int32_t M, int32_t topk, const void* workspace, uint64_t workspace_bytes,
-                      uint16_t* out, void* stream);
+/* W2 + router-weighted reduction from the act in workspace (left there by
+ * awq_moe_w13_swiglu for the same M and topk, or written by the caller;
+ * workspace is only read). topk_ids device int32 [M][topk] and topk_w device
+ * fp32 [M][topk] as for awq_moe_decode; out device fp16 [M][H], overwritten.
+ * One launch. */
+int awq_moe_w2_reduce(const awq_moe_dims* dims, const void* bank, const int32_t* topk_ids,
+                      const float* topk_w, int32_t M, int32_t topk, const void* workspace,
+                      uint64_t workspace_bytes, uint16_t* out, void* stream);
 
 /* Dequantise experts [expert_begin, expert_begin + expert_count) of the bank
- * into fp32 (diagnostic; the result is exact, see the design notes):
+ * into fp32 (diagnostic). Each value s * (q - z) is exact in fp32: q - z is an
+ * integer in [-255, 15] and s an fp16, so the product needs at most 19
+ * significant bits.
  *   which = 0: W13 [count][H][2I] (column 2i gate, 2i+1 up)
  *   which = 1: W2  [count][I][H]
  * out device fp32, C-contiguous. */

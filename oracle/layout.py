@@ -29,19 +29,18 @@ for p = 0..7, value p at bit 4*(p >> 1) + 16*(p & 1).
 A *record* is RB bytes: bytes 0-1 the fp16 scale (little endian), byte 2
 the zero; for RB = 4, byte 3 is 0.
 
-W13 (K = H, N = 2I): column n = 2i is gate column i, n = 2i + 1 is up
-column i. Columns form tiles of 16; with G13 = H/32, L13 = 4*G13:
+Both matrices use one tiled placement, for a matrix with K rows (K = H for
+W13, K = I for W2), G = K/32 groups and N columns. For W13 (N = 2I) column
+n = 2i is gate column i and n = 2i + 1 is up column i; for W2, N = H.
+Columns form tiles of 16; with L = 4*G:
   nt = n // 16, c = n % 16, quad = c // 4, j = c % 4, t = 4*g + quad
-  unit offset   = nt*256*G13 + (j*L13 + t)*16
-  record offset = nt*16*G13*RB + (4*t + j)*RB
-W2 (K = I, N = H): tiles of 8 columns; with G2 = I/32, L2 = 2*G2:
-  nt = n // 8, c = n % 8, quad = c // 4, j = c % 4, t = 2*g + quad
-  unit offset   = nt*128*G2 + (j*L2 + t)*16
-  record offset = nt*8*G2*RB + (4*t + j)*RB
+  unit offset   = nt*256*G + (j*L + t)*16
+  record offset = nt*16*G*RB + (4*t + j)*RB
 
-So lane t of a tile owns units j = 0..3 (four adjacent columns of one
-group), its four unit loads are each contiguous across lanes, and its four
-records are one aligned 12- or 16-byte run.
+Lane t of a tile owns units j = 0..3 (four adjacent columns of one group),
+its four unit loads are each contiguous across the tile's lanes, and its
+four records are one aligned 12- or 16-byte run. One tile is one contiguous
+run of 256*G unit bytes and one of 16*G*RB record bytes.
 """
 
 from __future__ import annotations
@@ -112,38 +111,39 @@ def layout(d: Dims) -> Layout:
 # unit / record placement
 # ---------------------------------------------------------------------------
 
-def w13_unit_offset(H: int, g, n):
-    G13 = H // GROUP
-    L13 = 4 * G13
+def tile_unit_offset(K: int, g, n):
+    """Byte offset of the unit of (group g, column n) in a section whose
+    matrix has K rows."""
+    G = K // GROUP
+    L = 4 * G
     nt, c = n // 16, n % 16
     quad, j = c // 4, c % 4
     t = 4 * g + quad
-    return nt * 256 * G13 + (j * L13 + t) * 16
+    return nt * 256 * G + (j * L + t) * 16
+
+
+def tile_record_offset(K: int, RB: int, g, n):
+    G = K // GROUP
+    nt, c = n // 16, n % 16
+    quad, j = c // 4, c % 4
+    t = 4 * g + quad
+    return nt * 16 * G * RB + (4 * t + j) * RB
+
+
+def w13_unit_offset(H: int, g, n):
+    return tile_unit_offset(H, g, n)
 
 
 def w13_record_offset(H: int, RB: int, g, n):
-    G13 = H // GROUP
-    nt, c = n // 16, n % 16
-    quad, j = c // 4, c % 4
-    t = 4 * g + quad
-    return nt * 16 * G13 * RB + (4 * t + j) * RB
+    return tile_record_offset(H, RB, g, n)
 
 
 def w2_unit_offset(I: int, g, n):
-    G2 = I // GROUP
-    L2 = 2 * G2
-    nt, c = n // 8, n % 8
-    quad, j = c // 4, c % 4
-    t = 2 * g + quad
-    return nt * 128 * G2 + (j * L2 + t) * 16
+    return tile_unit_offset(I, g, n)
 
 
 def w2_record_offset(I: int, RB: int, g, n):
-    G2 = I // GROUP
-    nt, c = n // 8, n % 8
-    quad, j = c // 4, c % 4
-    t = 2 * g + quad
-    return nt * 8 * G2 * RB + (4 * t + j) * RB
+    return tile_record_offset(I, RB, g, n)
 
 
 # ---------------------------------------------------------------------------

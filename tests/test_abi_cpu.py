@@ -137,9 +137,11 @@ def test_device_calls_reject_bad_arguments_before_launch():
         (lambda: lib.awq_moe_w13_swiglu(ctypes.byref(d), p, p, p, 1, 10, mis, ws_need, None), abi.EINVAL),
         (lambda: lib.awq_moe_w13_swiglu(ctypes.byref(d), p, p, None, 1, 10, p, ws_need, None), abi.EINVAL),
         (lambda: lib.awq_moe_w13_swiglu(ctypes.byref(d), p, p, p, 1, 10, p, ws_need - 1, None), abi.ENOSPC),
-        (lambda: lib.awq_moe_w2_reduce(ctypes.byref(d), p, p, 1, 10, p, ws_need, mis, None), abi.EINVAL),
-        (lambda: lib.awq_moe_w2_reduce(ctypes.byref(d), p, p, 9, 10, p, ws_need, p, None), abi.EINVAL),
-        (lambda: lib.awq_moe_w2_reduce(ctypes.byref(d), p, None, 1, 10, p, ws_need, p, None), abi.EINVAL),
+        (lambda: lib.awq_moe_w2_reduce(ctypes.byref(d), p, p, p, 1, 10, p, ws_need, mis, None), abi.EINVAL),
+        (lambda: lib.awq_moe_w2_reduce(ctypes.byref(d), p, p, p, 9, 10, p, ws_need, p, None), abi.EINVAL),
+        (lambda: lib.awq_moe_w2_reduce(ctypes.byref(d), p, None, p, 1, 10, p, ws_need, p, None), abi.EINVAL),
+        (lambda: lib.awq_moe_w2_reduce(ctypes.byref(d), p, p, p, 1, 10, p, ws_need - 1, p, None), abi.ENOSPC),
+        (lambda: lib.awq_moe_w2_reduce(ctypes.byref(d), p, p, None, 1, 10, p, ws_need, p, None), abi.EINVAL),
         (lambda: lib.awq_moe_dequant(ctypes.byref(d), p, 510, 3, 0, p, None), abi.EINVAL),
         (lambda: lib.awq_moe_dequant(ctypes.byref(d), p, 0, 1, 2, p, None), abi.EINVAL),
     ]

@@ -129,7 +129,7 @@ def test_w13_stage_and_w2_stage_pair(rb, M):
     act_sorted = f16_to_np(abi.workspace_act(ws, M, 10, I))[route_o["sorted_slots"]]   # by slot -> sorted rows
     act_ref = R.w13_swiglu_rows(x, route_o, 10, bi.expert)
     check(act_sorted[:V], act_ref[:V], f"w13 M={M} rb={rb}")
-    out = abi.awq_moe_w2_reduce(dims, bank, to_dev(w), ws)
+    out = abi.awq_moe_w2_reduce(dims, bank, to_dev(ids), to_dev(w), ws)
     torch.cuda.synchronize()
     out_ref = R.w2_reduce(act_sorted, w, route_o, 10, bi.expert, M, H)
     check(f16_to_np(out), out_ref, f"w2 on own act M={M} rb={rb}")
@@ -159,6 +159,29 @@ def test_decode_rank_shape(rb, M, mode):
     ids = draw(rng, M, 10, 128)
     w = inputs.router_weights(rng, M, 10)
     check(run_decode(dims, bank, x, ids, w), R.moe_stage(x, ids, w, 128, bi.expert), f"rank M={M} {mode} rb={rb}")
+
+
+@pytest.mark.parametrize("E,H,I,k,M", [
+    (8, 512, 2048, 10, 2),     # W2: 256 lanes per slot, 4 slots per pass -> 3 passes
+    (16, 256, 32, 32, 8),      # top-k 32, 256 slots; 4 lanes per slot
+    (6, 96, 64, 3, 5),         # hidden 96: 6 column tiles
+    (12, 128, 96, 1, 3),       # top-k 1
+    (64, 2560, 160, 10, 8),    # a token whose ids are all invalid, next to valid ones
+])
+def test_decode_other_shapes(E, H, I, k, M):
+    dims, bank, bi = bank_case(40 + I, E, H, I, 3)
+    rng = inputs.call_rng(41, H + k)
+    x = inputs.activations(rng, M, H)
+    ids = inputs.ids_shared_pool(rng, M, k, E) if k <= E else rng.integers(0, E, size=(M, k)).astype(np.int32)
+    if E == 64:
+        ids[3, :] = -7
+    w = inputs.router_weights(rng, M, k)
+    say("other shape", E, H, I, k, M)
+    got = run_decode(dims, bank, x, ids, w)
+    want = R.moe_stage(x, ids, w, E, bi.expert)
+    if E == 64:
+        assert not got[3].any()
+    check(got, want, f"shape E={E} H={H} I={I} k={k} M={M}")
 
 
 def test_decode_full_bank_rank_shape_m1_and_m8():
@@ -234,7 +257,7 @@ def test_w2_exact_integer_case_bit_exact():
     act = rng.integers(-1, 2, size=(M * k, I)).astype(np.float16)      # indexed by slot
     ws = abi.awq_moe_w13_swiglu(dims, bank, to_dev(np.zeros((M, H), np.float16)), to_dev(ids))
     abi.workspace_act(ws, M, k, I).copy_(to_dev(act))                  # replace the intermediate
-    out = abi.awq_moe_w2_reduce(dims, bank, to_dev(w), ws)
+    out = abi.awq_moe_w2_reduce(dims, bank, to_dev(ids), to_dev(w), ws)
     torch.cuda.synchronize()
     want = R.w2_reduce(act[route_o["sorted_slots"]], w, route_o, k, bi.expert, M, H)
     assert np.abs(want).max() <= 2048 and np.array_equal(want, np.round(want))

@@ -140,12 +140,12 @@ def test_byte_accounting_matches_pages():
         assert L.expert_bytes == L.w13_units + L.w13_meta + L.w2_units + L.w2_meta
 
 
-@pytest.mark.parametrize("H,I,rb", [(2560, 160, 3), (2560, 160, 4), (256, 32, 3)])
+@pytest.mark.parametrize("H,I,rb", [(2560, 160, 3), (2560, 160, 4), (256, 32, 3), (8192, 2048, 3), (96, 64, 4)])
 def test_placement_is_a_bijection_with_coalesced_lanes(H, I, rb):
     L = OL.layout(OL.Dims(1, H, I, rb))
-    for (unit_off, rec_off, G, N, NT) in (
-        (lambda g, n: OL.w13_unit_offset(H, g, n), lambda g, n: OL.w13_record_offset(H, rb, g, n), H // 32, 2 * I, 16),
-        (lambda g, n: OL.w2_unit_offset(I, g, n), lambda g, n: OL.w2_record_offset(I, rb, g, n), I // 32, H, 8),
+    for (unit_off, rec_off, G, N) in (
+        (lambda g, n: OL.w13_unit_offset(H, g, n), lambda g, n: OL.w13_record_offset(H, rb, g, n), H // 32, 2 * I),
+        (lambda g, n: OL.w2_unit_offset(I, g, n), lambda g, n: OL.w2_record_offset(I, rb, g, n), I // 32, H),
     ):
         g = np.arange(G)[:, None]
         n = np.arange(N)[None, :]
@@ -153,12 +153,15 @@ def test_placement_is_a_bijection_with_coalesced_lanes(H, I, rb):
         ro = np.broadcast_to(rec_off(g, n), (G, N)).ravel()
         assert np.array_equal(np.sort(uo), np.arange(G * N) * 16)
         assert np.array_equal(np.sort(ro), np.arange(G * N) * rb)
-        # within one tile, load j of lanes t = 0..L-1 reads one contiguous range
-        lanes = G * NT // 4
-        for j in range(4):
-            offs = []
+        # within a tile, load j of lanes t = 0..4G-1 reads one contiguous range,
+        # and the four records of lane t are one run starting on a dword boundary
+        lanes = 4 * G
+        for nt in (0, N // 16 - 1):
+            for j in range(4):
+                offs = [unit_off(t // 4, 16 * nt + 4 * (t % 4) + j) for t in range(lanes)]
+                assert offs == list(range(offs[0], offs[0] + 16 * lanes, 16))
+                assert offs[0] == nt * 256 * G + j * 16 * lanes
             for t in range(lanes):
-                gg, quad = t // (NT // 4), t % (NT // 4)
-                offs.append(unit_off(gg, 4 * quad + j))
-            assert offs == list(range(offs[0], offs[0] + 16 * lanes, 16))
+                r = [rec_off(t // 4, 16 * nt + 4 * (t % 4) + j) for j in range(4)]
+                assert r == list(range(r[0], r[0] + 4 * rb, rb)) and r[0] % 4 == 0
     assert L.total_bytes == L.expert_bytes
