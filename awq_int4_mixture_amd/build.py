@@ -24,6 +24,8 @@ COMMON = [
     f"--offload-arch={ARCH}",
     # no packed-fp32 VALU instructions anywhere in the device code
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # the first 16 dwords of kernel arguments arrive in SGPRs at wave launch
+    "-mllvm", "-amdgpu-kernarg-preload-count=16",
     f"-I{INCLUDE}", f"-I{CSRC}",
 ]
 SOURCES = ["kernels.hip", "awq_moe_host.cpp"]

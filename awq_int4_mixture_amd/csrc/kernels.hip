@@ -296,36 +296,41 @@ __global__ __launch_bounds__(256) void route_compact_kernel(const int32_t* __res
 // Workgroup (0, 0) also writes the status word.
 // ---------------------------------------------------------------------------
 template <int RB>
-__global__ __launch_bounds__(1024) void w13_swiglu_kernel(StageArgs a, const uint16_t* __restrict__ x,
-                                                          uint16_t* __restrict__ act, uint32_t* __restrict__ status) {
+__global__ __launch_bounds__(1024) void w13_swiglu_kernel(const int32_t* __restrict__ ids,
+                                                          const uint8_t* __restrict__ units_base,
+                                                          const uint8_t* __restrict__ recs_base,
+                                                          const uint16_t* __restrict__ x, uint64_t expert_bytes, int H,
+                                                          int I, int topk, int E, uint16_t* __restrict__ act,
+                                                          uint32_t* __restrict__ status, int M) {
   __shared__ float red[16][16];  // [wave][column]
   const int nt = blockIdx.x, s = blockIdx.y;
+  // First request: the slot's expert id (a scalar load; nothing depends on
+  // anything else before the weight loads).
+  const int e = ids[s];
   const int t = threadIdx.x;
   const int lane = t & 63, wave = t >> 6, nwaves = blockDim.x >> 6;
-  const int H = a.H, I = a.I;
   const int G = H >> 5;
   const int L = 4 * G;
   const int g = t >> 2;
-  if (status != nullptr && nt == 0 && s == 0) {
+  if (nt == 0 && s == 0 && status != nullptr) {
     int bad = 0;
-    for (int i = t; i < a.M * a.topk; i += blockDim.x) {
-      const int v = a.topk_ids[i];
-      bad |= (v < 0 || v >= a.E);
+    for (int i = t; i < M * topk; i += blockDim.x) {
+      const int v = ids[i];
+      bad |= (v < 0 || v >= E);
     }
     bad = __syncthreads_or(bad);
     if (t == 0) *status = bad ? AWQ_MOE_STATUS_BAD_ID_BIT : 0u;
   }
-  const int e = a.topk_ids[s];
-  if (e < 0 || e >= a.E) return;  // invalid slot: no row
+  if (e < 0 || e >= E) return;  // invalid slot: no row
   float part[4] = {0.f, 0.f, 0.f, 0.f};
   if (t < L) {
-    const uint8_t* blk = a.bank + (uint64_t)e * a.expert_bytes;
-    const uint8_t* units = blk + a.w13_off + (uint64_t)nt * 256u * G;
+    const uint8_t* units = units_base + (uint64_t)e * expert_bytes + (uint64_t)nt * 256u * G;
     uint4 w[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) w[j] = *reinterpret_cast<const uint4*>(units + ((uint64_t)j * L + t) * 16u);
-    const Records<RB> rec = load_records<RB>(blk + a.w13_meta_off + (uint64_t)nt * 16u * G * RB + (uint64_t)t * 4u * RB);
-    const Act32 av = load_act32(x + (uint64_t)(s / a.topk) * H + 32 * g);
+    const Records<RB> rec = load_records<RB>(recs_base + (uint64_t)e * expert_bytes + (uint64_t)nt * 16u * G * RB +
+                                             (uint64_t)t * 4u * RB);
+    const Act32 av = load_act32(x + (uint64_t)(s / topk) * H + 32 * g);
     float S, Cs;
     group_sums(av, S, Cs);
     const Magic mg = make_magic();
@@ -358,20 +363,28 @@ __global__ __launch_bounds__(1024) void w13_swiglu_kernel(StageArgs a, const uin
 // shuffles while the weight loads are in flight.
 // ---------------------------------------------------------------------------
 template <int RB>
-__global__ __launch_bounds__(1024) void w2_reduce_kernel(StageArgs a, const uint16_t* __restrict__ act,
-                                                         const float* __restrict__ topk_w,
+__global__ __launch_bounds__(1024) void w2_reduce_kernel(const int32_t* __restrict__ topk_ids,
+                                                         const uint8_t* __restrict__ units_base,
+                                                         const uint8_t* __restrict__ recs_base,
+                                                         const uint16_t* __restrict__ act, uint64_t expert_bytes, int H,
+                                                         int I, int topk, int E, const float* __restrict__ topk_w,
                                                          uint16_t* __restrict__ out) {
   __shared__ float red[4096];                      // [slot in pass][g][16]; SPP*G2*16 <= 4096
   __shared__ float ys[AWQ_MOE_KMAX_TOPK * 16];     // [slot][16]: the slot's 16 column results
   __shared__ int ord[AWQ_MOE_KMAX_TOPK];           // rank -> slot
   __shared__ float wr[AWQ_MOE_KMAX_TOPK];          // rank -> router weight
   __shared__ int nvalid_s;
-  const int nt = blockIdx.x, tok = blockIdx.y;
+  // Workgroups are handed to the 8 XCDs round robin by linear id, so with
+  // H/16 a multiple of 8 the x index bx runs on XCD bx % 8 for every token.
+  // Give each XCD a contiguous run of tiles: the record runs of neighbouring
+  // tiles share cache lines, which are then fetched into one L2 only.
+  const int T2 = H >> 4;
+  const int nt = (T2 & 7) ? (int)blockIdx.x : (int)((blockIdx.x & 7) * (T2 >> 3) + (blockIdx.x >> 3));
+  const int tok = blockIdx.y;
   const int t = threadIdx.x;
-  const int H = a.H, I = a.I, topk = a.topk, E = a.E;
   const int G2 = I >> 5, LS = 4 * G2;
   const int spp = blockDim.x / LS;                 // slots per pass (>= 1)
-  const int32_t* ids = a.topk_ids + tok * topk;
+  const int32_t* ids = topk_ids + tok * topk;
 
   for (int s0 = 0; s0 < topk; s0 += spp) {
     const int sp = t / LS, tl = t - sp * LS;
@@ -384,11 +397,11 @@ __global__ __launch_bounds__(1024) void w2_reduce_kernel(StageArgs a, const uint
     Act32 av;
     const int g = tl >> 2, quad = tl & 3;
     if (live) {
-      const uint8_t* blk = a.bank + (uint64_t)e * a.expert_bytes;
-      const uint8_t* units = blk + a.w2_off + (uint64_t)nt * 256u * G2;
+      const uint8_t* units = units_base + (uint64_t)e * expert_bytes + (uint64_t)nt * 256u * G2;
 #pragma unroll
       for (int j = 0; j < 4; ++j) w[j] = *reinterpret_cast<const uint4*>(units + ((uint64_t)j * LS + tl) * 16u);
-      rec = load_records<RB>(blk + a.w2_meta_off + (uint64_t)nt * 16u * G2 * RB + (uint64_t)tl * 4u * RB);
+      rec = load_records<RB>(recs_base + (uint64_t)e * expert_bytes + (uint64_t)nt * 16u * G2 * RB +
+                             (uint64_t)tl * 4u * RB);
       av = load_act32(act + (uint64_t)(tok * topk + slot) * I + 32 * g);
     }
     if (s0 == 0 && t < 64) {
@@ -485,9 +498,11 @@ hipError_t launch_w13_swiglu(const StageArgs& a, const uint16_t* x, uint16_t* ac
   const dim3 block(((L + 63) / 64) * 64);
   const dim3 grid((2 * a.I) / 16, a.M * a.topk);
   if (a.RB == 4)
-    hipLaunchKernelGGL(w13_swiglu_kernel<4>, grid, block, 0, stream, a, x, act, status);
+    hipLaunchKernelGGL(w13_swiglu_kernel<4>, grid, block, 0, stream, a.topk_ids, a.bank + a.w13_off,
+                       a.bank + a.w13_meta_off, x, a.expert_bytes, a.H, a.I, a.topk, a.E, act, status, a.M);
   else
-    hipLaunchKernelGGL(w13_swiglu_kernel<3>, grid, block, 0, stream, a, x, act, status);
+    hipLaunchKernelGGL(w13_swiglu_kernel<3>, grid, block, 0, stream, a.topk_ids, a.bank + a.w13_off,
+                       a.bank + a.w13_meta_off, x, a.expert_bytes, a.H, a.I, a.topk, a.E, act, status, a.M);
   return hipGetLastError();
 }
 
@@ -498,9 +513,11 @@ hipError_t launch_w2_reduce(const StageArgs& a, const uint16_t* act, const float
   const dim3 block(lanes >= 1024 ? 1024 : ((lanes + 63) / 64) * 64);
   const dim3 grid(a.H / 16, a.M);
   if (a.RB == 4)
-    hipLaunchKernelGGL(w2_reduce_kernel<4>, grid, block, 0, stream, a, act, topk_w, out);
+    hipLaunchKernelGGL(w2_reduce_kernel<4>, grid, block, 0, stream, a.topk_ids, a.bank + a.w2_off, a.bank + a.w2_meta_off,
+                       act, a.expert_bytes, a.H, a.I, a.topk, a.E, topk_w, out);
   else
-    hipLaunchKernelGGL(w2_reduce_kernel<3>, grid, block, 0, stream, a, act, topk_w, out);
+    hipLaunchKernelGGL(w2_reduce_kernel<3>, grid, block, 0, stream, a.topk_ids, a.bank + a.w2_off, a.bank + a.w2_meta_off,
+                       act, a.expert_bytes, a.H, a.I, a.topk, a.E, topk_w, out);
   return hipGetLastError();
 }
 
