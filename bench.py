@@ -5,13 +5,15 @@ intermediate 160, top-k 10, int4 group 32, 4-byte records), M = 1 token,
 the same 10 hot experts on every call, 48 calls per HIP-graph replay with a
 fresh fp16 x ~ N(0,1) and softmax router weights per call (PR #522,
 Operator results: 48 calls per graph replay). One *step* is one replay: 48
-passes of route-compact -> W13+SwiGLU -> W2+reduction.
+awq_moe_decode calls (W13+SwiGLU, then W2+reduction; two launches each).
 
 Printed: one JSON line with the layer's achieved weight bandwidth (touched
-weight + record bytes / layer time), per-kernel times, the roofline of the
-dominant kernel (W13+SwiGLU) from HIP events on its stream, side
-measurements (cold M=1 with 3-byte records over 480 rotating experts; M=8
-with a shared expert pool), and the CPU oracle timed on a bounded sample.
+weight + record bytes / layer time), per-kernel times from graphs of one
+kernel, the roofline of the dominant (longer) kernel from HIP events on its
+stream, side measurements (cold M=1 with 3-byte records over 480 rotating
+experts; M=8 with a shared expert pool and with 80 distinct experts), two
+live references (a 1 GiB streaming read and the per-launch floor of a
+graph of empty launches), and the CPU oracle timed on a bounded sample.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--only NAME] [--no-cpu]
 """
@@ -145,7 +147,7 @@ def measure(abi, torch, wl: Workload, steps, warmup):
     return res
 
 
-def recorded_traffic(kernel: str, summary: str = "pmc_traffic_m1_hot_4b.txt"):
+def recorded_traffic(kernel: str, summary: str = "pmc_traffic_m1_hot.txt"):
     """HBM bytes per launch of ``kernel`` from the committed rocprofv3 counter summary
     (FETCH_SIZE and WRITE_SIZE, each scaled by a 1 GiB copy in the same run), or None
     when the summary is missing or the kernel source changed since it was taken."""
@@ -180,8 +182,45 @@ def copy_ceiling(torch, nbytes=1 << 30, reps=20):
     return {"bytes_moved": 2 * nbytes, "us": ms * 1e3, "gbs": 2 * nbytes / (ms * 1e6)}
 
 
+def read_ceiling(torch, nbytes=1 << 30, reps=20):
+    """1 GiB streaming reads (row sums of float32 tiles of 1, 4 and 16 KiB, and
+    a full sum): the best rate is reported as a reference read rate."""
+    a = torch.ones(nbytes // 4, dtype=torch.float32, device="cuda")
+    best = None
+    for cols in (256, 1024, 4096, None):
+        fn = (lambda: a.sum()) if cols is None else (lambda c=cols: a.view(-1, c).sum(dim=1))
+        r = fn()
+        torch.cuda.synchronize()
+        t0 = torch.cuda.Event(enable_timing=True)
+        t1 = torch.cuda.Event(enable_timing=True)
+        t0.record()
+        for _ in range(reps):
+            r = fn()
+        t1.record()
+        t1.synchronize()
+        ms = t0.elapsed_time(t1) / reps
+        gbs = nbytes / (ms * 1e6)
+        if best is None or gbs > best["gbs"]:
+            best = {"bytes_read": nbytes, "us": ms * 1e3, "gbs": gbs,
+                    "op": "sum" if cols is None else f"row sums of {cols} float32"}
+        del r
+    del a
+    return best
+
+
+def launch_floor(torch, steps=50, warmup=5):
+    """Per-launch time of a HIP graph of 48 launches that do (almost) nothing:
+    the floor under any one-launch kernel timed the same way."""
+    t = torch.zeros(64, dtype=torch.float32, device="cuda")
+    g = capture(torch, lambda: [t.add_(1.0) for _ in range(CALLS)])
+    ms = time_graph(torch, g, steps, warmup)
+    del g
+    return {"us_per_launch": ms * 1e3 / CALLS}
+
+
 def cpu_baseline(bi, ids_calls, rng_seed, budget_s=12.0):
-    """The float64 oracle on the headline workload's calls, as many as fit in ~budget_s."""
+    """The float64 oracle on the headline workload's calls (cycling through the
+    48 expert sets with fresh inputs) for about budget_s seconds."""
     from threadpoolctl import threadpool_limits
 
     from oracle import ref as R
@@ -190,18 +229,36 @@ def cpu_baseline(bi, ids_calls, rng_seed, budget_s=12.0):
     done = 0
     with threadpool_limits(limits=1):
         t0 = time.perf_counter()
-        while done < CALLS:
+        while True:
             x = inputs.activations(rng, 1, H)
             w = inputs.router_weights(rng, 1, K_TOP)
-            R.moe_stage(x, ids_calls[done], w, E, bi.expert)
+            R.moe_stage(x, ids_calls[done % CALLS], w, E, bi.expert)
             done += 1
             if time.perf_counter() - t0 > budget_s:
                 break
         dt = time.perf_counter() - t0
     return {"value": round(per_call * done / dt / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
-            "sample": f"{done} of the 48 M=1 hot-expert calls (4-byte records), float64 NumPy on one "
+            "sample": f"{done} M=1 calls on the hot-expert sets (4-byte records), float64 NumPy on one "
                       f"thread, dequantisation of the touched experts included, {dt:.1f} s",
             "layer_us": round(dt / done * 1e6, 1)}
+
+
+def roofline(head):
+    """HBM roofline of the longer of the two stage kernels at the headline workload."""
+    k = "w2" if head["w2_us"] >= head["w13_us"] else "w13"
+    name = {"w13": "w13_swiglu_kernel<4>", "w2": "w2_reduce_kernel<4>"}[k]
+    gbs = head[k + "_gbs"]
+    return {
+        "bound": "hbm",
+        "kernel": name,
+        "achieved": round(gbs, 2),
+        "peak": HBM_PEAK_GBS,
+        "unit": "GB/s",
+        "frac": round(gbs / HBM_PEAK_GBS, 4),
+        "traffic": recorded_traffic(name),
+        "algorithmic_bytes_per_launch": head[k + "_bytes_per_call"],
+        "avg_launch_us": round(head[k + "_us"], 3),
+    }
 
 
 def main():
@@ -255,6 +312,8 @@ def main():
             wl = Workload("m8_distinct", abi, torch, dims, bank, ids, 8, rng, per_expert_bytes(abi, dims))
             results["m8_distinct"] = measure(abi, torch, wl, args.steps, args.warmup)
         ceiling = copy_ceiling(torch)
+        read_ref = read_ceiling(torch)
+        floor = launch_floor(torch)
 
     head = results.get("m1_hot") or next(iter(results.values()))
     line = {
@@ -276,20 +335,12 @@ def main():
             "layer_us": round(head["layer_us"], 3),
             "calls_per_step": CALLS,
         },
-        "roofline": {
-            "bound": "hbm",
-            "kernel": "w13_swiglu_kernel<4>",
-            "achieved": round(head["w13_gbs"], 2),
-            "peak": HBM_PEAK_GBS,
-            "unit": "GB/s",
-            "frac": round(head["w13_gbs"] / HBM_PEAK_GBS, 4),
-            "traffic": recorded_traffic("w13_swiglu_kernel<4>"),
-            "algorithmic_bytes_per_launch": head["w13_bytes_per_call"],
-            "avg_launch_us": round(head["w13_us"], 3),
-        },
+        "roofline": roofline(head),
         "per_config": {k: {kk: (round(vv, 4) if isinstance(vv, float) else vv) for kk, vv in v.items()}
                        for k, v in results.items()},
         "copy_reference": ceiling,
+        "read_reference": read_ref,
+        "launch_floor": floor,
         "setup_s": round(t_gen, 1),
     }
     if not args.no_cpu and "m1_hot" in results:
