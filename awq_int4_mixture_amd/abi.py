@@ -27,7 +27,7 @@ WS_ACT_OFFSET = 256
 EXPORTED = (
     "awq_moe_bank_layout_query", "awq_moe_prepare", "awq_moe_workspace_bytes",
     "awq_moe_route_compact", "awq_moe_decode", "awq_moe_w13_swiglu", "awq_moe_w2_reduce",
-    "awq_moe_dequant", "awq_moe_last_error",
+    "awq_moe_dequant", "awq_moe_router_topk", "awq_moe_residual_rmsnorm", "awq_moe_last_error",
 )
 
 
@@ -71,6 +71,8 @@ def _load() -> ctypes.CDLL:
         "awq_moe_w13_swiglu": [D, P, P, P, I32, I32, P, U64, V],
         "awq_moe_w2_reduce": [D, P, P, P, I32, I32, P, U64, P, V],
         "awq_moe_dequant": [D, P, I32, I32, I32, P, V],
+        "awq_moe_router_topk": [P, I32, I32, I32, P, P, V],
+        "awq_moe_residual_rmsnorm": [P, P, I32, I32, ctypes.c_float, P, P, V],
     }
     for name, args in sig.items():
         f = getattr(lib, name)
@@ -268,6 +270,36 @@ def awq_moe_dequant(dims: awq_moe_dims, bank, expert_begin: int, expert_count: i
                                 expert_count, which, _dev(out, torch.float32, (expert_count, K, N), "out"),
                                 _stream(stream)), "awq_moe_dequant")
     return out
+
+
+def awq_moe_router_topk(logits, topk: int, ids=None, w=None, stream=None):
+    """Top-k + softmax of fp32 logits [M][E] -> (ids int32 [M][k], w fp32 [M][k])."""
+    torch = _torch()
+    M, E = logits.shape
+    if ids is None:
+        ids = torch.empty((M, topk), dtype=torch.int32, device=logits.device)
+    if w is None:
+        w = torch.empty((M, topk), dtype=torch.float32, device=logits.device)
+    _check(_lib.awq_moe_router_topk(_dev(logits, torch.float32, (M, E), "logits"), M, E, topk,
+                                    _dev(ids, torch.int32, (M, topk), "ids"), _dev(w, torch.float32, (M, topk), "w"),
+                                    _stream(stream)), "awq_moe_router_topk")
+    return ids, w
+
+
+def awq_moe_residual_rmsnorm(r, delta=None, eps: float = 1e-6, r_next=None, x=None, stream=None):
+    """r_next = fp16(r + delta); x = fp16(rms_norm(r_next)). Returns (r_next, x)."""
+    torch = _torch()
+    M, H = r.shape
+    if r_next is None:
+        r_next = torch.empty_like(r)
+    if x is None:
+        x = torch.empty_like(r)
+    dp = None if delta is None else _dev(delta, torch.float16, (M, H), "delta")
+    _check(_lib.awq_moe_residual_rmsnorm(_dev(r, torch.float16, (M, H), "r"), dp, M, H, eps,
+                                         _dev(r_next, torch.float16, (M, H), "r_next"),
+                                         _dev(x, torch.float16, (M, H), "x"), _stream(stream)),
+           "awq_moe_residual_rmsnorm")
+    return r_next, x
 
 
 def awq_moe_last_error() -> str:

@@ -8,6 +8,8 @@
 #define AWQ_MOE_KMAX_TOKENS 8
 #define AWQ_MOE_KMAX_SLOTS 256
 #define AWQ_MOE_KMAX_TOPK 32
+#define AWQ_MOE_KMAX_ROUTER_E 4096
+#define AWQ_MOE_KMAX_HIDDEN 8192
 #define AWQ_MOE_STATUS_BAD_ID_BIT 1u
 
 namespace awq_moe {
@@ -36,6 +38,10 @@ hipError_t launch_w13_swiglu(const StageArgs& a, const uint16_t* x, uint16_t* ac
                              hipStream_t stream);
 hipError_t launch_w2_reduce(const StageArgs& a, const uint16_t* act, const float* topk_w, uint16_t* out,
                             hipStream_t stream);
+hipError_t launch_router_topk(const float* logits, int M, int E, int k, int32_t* ids, float* w, hipStream_t stream);
+// r_next and x may not alias r or delta.
+hipError_t launch_residual_rmsnorm(const uint16_t* r, const uint16_t* delta, int M, int H, float eps,
+                                   uint16_t* r_next, uint16_t* x, hipStream_t stream);
 hipError_t launch_dequant(const uint8_t* bank, uint64_t expert_bytes, uint64_t units_off,
                           uint64_t meta_off, int RB, int which, int H, int I, int expert_begin,
                           int expert_count, float* out, hipStream_t stream);

@@ -351,43 +351,48 @@ __global__ __launch_bounds__(1024) void w13_swiglu_kernel(const int32_t* __restr
 }
 
 // ---------------------------------------------------------------------------
-// W2 + router-weighted reduction: grid (H/16 column tiles, M tokens). The
-// workgroup of (tile, token) streams the 16-column W2 tile of each of the
-// token's routed experts (all of K = I) and sums the slots in LDS, so no
-// partial result crosses workgroups and no workspace is written.
-// Lanes: u = slot*LS + t with LS = 4*G2 lanes per slot and t = 4g + quad as
-// in the layout; slots beyond what one block holds are taken in passes.
-// Slot order of the final sum: ascending (expert, slot) over the valid slots,
-// so the result depends only on the set of (expert, weight) pairs and not on
-// the order of the token's top-k list. Wave 0 ranks the slots with lane
-// shuffles while the weight loads are in flight.
+// W2 + router-weighted reduction: grid (H/(16*TPW) column groups, M tokens).
+// The workgroup of (group, token) streams TPW adjacent 16-column W2 tiles
+// (one contiguous run per expert, all of K = I) of each of the token's
+// routed experts and sums the slots in LDS, so no partial result crosses
+// workgroups and no workspace is written.
+// Lanes: u = slot*(TPW*LS) + tile*LS + t with LS = 4*G2 lanes per tile and
+// t = 4g + quad as in the layout; slots beyond what one block holds are
+// taken in passes. Slot order of the final sum: ascending (expert, slot)
+// over the valid slots, so the result depends only on the set of
+// (expert, weight) pairs and not on the order of the token's top-k list.
+// Wave 0 ranks the slots with lane shuffles while the weight loads are in
+// flight.
 // ---------------------------------------------------------------------------
-template <int RB>
+template <int RB, int TPW>
 __global__ __launch_bounds__(1024) void w2_reduce_kernel(const int32_t* __restrict__ topk_ids,
                                                          const uint8_t* __restrict__ units_base,
                                                          const uint8_t* __restrict__ recs_base,
                                                          const uint16_t* __restrict__ act, uint64_t expert_bytes, int H,
                                                          int I, int topk, int E, const float* __restrict__ topk_w,
                                                          uint16_t* __restrict__ out) {
-  __shared__ float red[4096];                      // [slot in pass][g][16]; SPP*G2*16 <= 4096
-  __shared__ float ys[AWQ_MOE_KMAX_TOPK * 16];     // [slot][16]: the slot's 16 column results
+  constexpr int NC = 16 * TPW;                     // columns per workgroup
+  __shared__ float red[4096];                      // [slot in pass][tile][g][16]; <= 4*blockDim
+  __shared__ float ys[AWQ_MOE_KMAX_TOPK * NC];     // [slot][NC]: the slot's column results
   __shared__ int ord[AWQ_MOE_KMAX_TOPK];           // rank -> slot
   __shared__ float wr[AWQ_MOE_KMAX_TOPK];          // rank -> router weight
   __shared__ int nvalid_s;
   // Workgroups are handed to the 8 XCDs round robin by linear id, so with
-  // H/16 a multiple of 8 the x index bx runs on XCD bx % 8 for every token.
-  // Give each XCD a contiguous run of tiles: the record runs of neighbouring
-  // tiles share cache lines, which are then fetched into one L2 only.
-  const int T2 = H >> 4;
-  const int nt = (T2 & 7) ? (int)blockIdx.x : (int)((blockIdx.x & 7) * (T2 >> 3) + (blockIdx.x >> 3));
+  // the group count a multiple of 8 the x index bx runs on XCD bx % 8 for
+  // every token. Give each XCD a contiguous run of groups: the record runs
+  // of neighbouring tiles share cache lines, which are then fetched into
+  // one L2 only.
+  const int NG = H / NC;
+  const int grp = (NG & 7) ? (int)blockIdx.x : (int)((blockIdx.x & 7) * (NG >> 3) + (blockIdx.x >> 3));
+  const int nt0 = grp * TPW;
   const int tok = blockIdx.y;
   const int t = threadIdx.x;
-  const int G2 = I >> 5, LS = 4 * G2;
-  const int spp = blockDim.x / LS;                 // slots per pass (>= 1)
+  const int G2 = I >> 5, LS = 4 * G2, LSW = TPW * LS;
+  const int spp = blockDim.x / LSW;                // slots per pass (>= 1)
   const int32_t* ids = topk_ids + tok * topk;
-
   for (int s0 = 0; s0 < topk; s0 += spp) {
-    const int sp = t / LS, tl = t - sp * LS;
+    const int sp = t / LSW, rem = t - sp * LSW;
+    const int tt = TPW == 1 ? 0 : rem / LS, tl = rem - tt * LS;
     const int slot = s0 + sp;
     const bool lane_on = sp < spp && slot < topk;
     const int e = lane_on ? ids[slot] : -1;
@@ -397,11 +402,11 @@ __global__ __launch_bounds__(1024) void w2_reduce_kernel(const int32_t* __restri
     Act32 av;
     const int g = tl >> 2, quad = tl & 3;
     if (live) {
-      const uint8_t* units = units_base + (uint64_t)e * expert_bytes + (uint64_t)nt * 256u * G2;
+      const uint64_t eo = (uint64_t)e * expert_bytes;
+      const uint8_t* units = units_base + eo + (uint64_t)(nt0 + tt) * 256u * G2;
 #pragma unroll
       for (int j = 0; j < 4; ++j) w[j] = *reinterpret_cast<const uint4*>(units + ((uint64_t)j * LS + tl) * 16u);
-      rec = load_records<RB>(recs_base + (uint64_t)e * expert_bytes + (uint64_t)nt * 16u * G2 * RB +
-                             (uint64_t)tl * 4u * RB);
+      rec = load_records<RB>(recs_base + eo + (uint64_t)(nt0 + tt) * 16u * G2 * RB + (uint64_t)tl * 4u * RB);
       av = load_act32(act + (uint64_t)(tok * topk + slot) * I + 32 * g);
     }
     if (s0 == 0 && t < 64) {
@@ -426,26 +431,28 @@ __global__ __launch_bounds__(1024) void w2_reduce_kernel(const int32_t* __restri
       const Magic mg = make_magic();
 #pragma unroll
       for (int j = 0; j < 4; ++j)
-        red[(sp * G2 + g) * 16 + 4 * quad + j] = rec.s[j] * (unit_dot(w[j], av, mg) - fmaf(rec.z[j], S, Cs));
+        red[((sp * TPW + tt) * G2 + g) * 16 + 4 * quad + j] =
+            rec.s[j] * (unit_dot(w[j], av, mg) - fmaf(rec.z[j], S, Cs));
     }
     __syncthreads();
     // per-slot column results of this pass, groups summed in ascending g
     // (rows of invalid slots hold stale values and are never read)
-    for (int u = t; u < spp * 16; u += blockDim.x) {
-      const int ps = u >> 4, c = u & 15;
+    for (int u = t; u < spp * NC; u += blockDim.x) {
+      const int ps = u / NC, cc = u - ps * NC;
+      const int t2 = cc >> 4, c = cc & 15;
       if (s0 + ps < topk) {
         float y = 0.f;
-        for (int gg = 0; gg < G2; ++gg) y += red[(ps * G2 + gg) * 16 + c];
-        ys[(s0 + ps) * 16 + c] = y;
+        for (int gg = 0; gg < G2; ++gg) y += red[((ps * TPW + t2) * G2 + gg) * 16 + c];
+        ys[(s0 + ps) * NC + cc] = y;
       }
     }
     __syncthreads();
   }
-  if (t < 16) {
+  if (t < NC) {
     const int nv = nvalid_s;
     float acc = 0.f;
-    for (int r = 0; r < nv; ++r) acc = fmaf(wr[r], ys[ord[r] * 16 + t], acc);
-    out[(uint64_t)tok * H + nt * 16 + t] = __builtin_bit_cast(uint16_t, (_Float16)acc);
+    for (int r = 0; r < nv; ++r) acc = fmaf(wr[r], ys[ord[r] * NC + t], acc);
+    out[(uint64_t)tok * H + nt0 * 16 + t] = __builtin_bit_cast(uint16_t, (_Float16)acc);
   }
 }
 
@@ -487,6 +494,155 @@ __global__ void dequant_kernel(const uint8_t* __restrict__ bank, uint64_t expert
 // ---------------------------------------------------------------------------
 // launchers
 // ---------------------------------------------------------------------------
+// ---------------------------------------------------------------------------
+// Router top-k + softmax (the layer-stack workload's per-layer router; the
+// pages leave the router unchanged, fork PR #12, Purpose and stack).
+// One workgroup per token. Each logit becomes a 64-bit key that orders by
+// value (exact fp32 order, -0 == +0, NaN below every number) and then by
+// lower id:  key = ord(value) << 32 | (0xFFFFFFFF - id), ord mapping the
+// float bit pattern to an order-preserving uint32. Keys are distinct, so
+// the number of larger keys is an element's rank. The softmax over the k
+// winners is fp32, summed in rank order.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ uint64_t router_key(float v, int id) {
+  uint32_t ord;
+  if (v != v) {
+    ord = 0u;  // NaN: below every number
+  } else {
+    const uint32_t u = __builtin_bit_cast(uint32_t, v == 0.f ? 0.f : v);
+    ord = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+  }
+  return ((uint64_t)ord << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)id);
+}
+
+__device__ __forceinline__ uint64_t readlane_u64(uint64_t v, int lane) {
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)v, lane);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(v >> 32), lane);
+  return ((uint64_t)hi << 32) | lo;
+}
+
+// Two stages. (1) Each wave ranks the keys of a 64-element chunk among
+// themselves with lane reads (no memory round trips) and keeps its k best
+// as candidates at fixed places chunk*k + rank. (2) Each candidate is
+// ranked among all candidates in LDS; rank < k is the answer.
+__global__ __launch_bounds__(1024) void router_topk_kernel(const float* __restrict__ logits, int E, int k,
+                                                           int32_t* __restrict__ ids, float* __restrict__ w) {
+  __shared__ uint64_t cand[AWQ_MOE_KMAX_ROUTER_E / 64 * AWQ_MOE_KMAX_TOPK];
+  __shared__ float cand_v[AWQ_MOE_KMAX_ROUTER_E / 64 * AWQ_MOE_KMAX_TOPK];
+  __shared__ float sel_v[AWQ_MOE_KMAX_TOPK];
+  __shared__ float sel_p[AWQ_MOE_KMAX_TOPK];
+  const int tok = blockIdx.x, t = threadIdx.x, nt = blockDim.x;
+  const int lane = t & 63, wave = t >> 6, nwaves = nt >> 6;
+  const float* lg = logits + (uint64_t)tok * E;
+  const int nchunks = (E + 63) >> 6;
+  const int ncand = nchunks * k;
+  for (int c = t; c < ncand; c += nt) cand[c] = 0;  // 0 sorts below every key
+  __syncthreads();
+  for (int chunk = wave; chunk < nchunks; chunk += nwaves) {
+    const int i = chunk * 64 + lane;
+    const float v = i < E ? lg[i] : 0.f;
+    const uint64_t key = i < E ? router_key(v, i) : 0;
+    int r = 0;
+#pragma unroll
+    for (int j = 0; j < 64; ++j) r += readlane_u64(key, j) > key;
+    if (i < E && r < k) {
+      cand[chunk * k + r] = key;
+      cand_v[chunk * k + r] = v;
+    }
+  }
+  __syncthreads();
+  for (int c = t; c < ncand; c += nt) {
+    const uint64_t kc = cand[c];
+    if (kc == 0) continue;
+    int r = 0;
+#pragma unroll 8
+    for (int j = 0; j < ncand; ++j) r += cand[j] > kc;
+    if (r < k) {
+      ids[tok * k + r] = (int)(0xFFFFFFFFu - (uint32_t)kc);
+      sel_v[r] = cand_v[c];
+    }
+  }
+  __syncthreads();
+  if (t < 64) {  // one wave: LDS writes are visible to its own later reads
+    const float m = sel_v[0];
+    const float p = t < k ? expf(sel_v[t] - m) : 0.f;
+    if (t < k) sel_p[t] = p;
+    float sum = 0.f;  // in rank order
+    for (int r = 0; r < k; ++r) sum += sel_p[r];
+    if (t < k) w[tok * k + t] = p / sum;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Residual update and parameter-free RMS norm for the layer-stack workload:
+// r_next = fp16(r + delta) (delta may be null: r_next = r), and
+// x = fp16(r_next / sqrt(mean(r_next^2) + eps)), all in fp32. One workgroup
+// per row; each thread owns runs of 8 values (16-byte loads and stores) and
+// keeps them in registers across the reduction.
+// ---------------------------------------------------------------------------
+typedef _Float16 h8_t __attribute__((ext_vector_type(8)));
+
+__global__ __launch_bounds__(1024) void residual_rmsnorm_kernel(const uint16_t* __restrict__ r,
+                                                                const uint16_t* __restrict__ delta, int H, float eps,
+                                                                uint16_t* __restrict__ r_next,
+                                                                uint16_t* __restrict__ x) {
+  __shared__ float part[16];
+  const int row = blockIdx.x, t = threadIdx.x;
+  const int nv = H >> 3;  // runs of 8 (H % 8 == 0 on this path)
+  constexpr int kRuns = 1;  // blockDim = min(1024, H/8 rounded up to 64) and H <= 8192: one run per thread
+  h8_t v[kRuns];
+  float ss = 0.f;
+#pragma unroll
+  for (int q = 0; q < kRuns; ++q) {
+    const int i = t + q * (int)blockDim.x;
+    if (i < nv) {
+      h8_t a = *reinterpret_cast<const h8_t*>(r + (uint64_t)row * H + 8 * i);
+      if (delta) {
+        const h8_t b = *reinterpret_cast<const h8_t*>(delta + (uint64_t)row * H + 8 * i);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) a[e] = (_Float16)((float)a[e] + (float)b[e]);
+      }
+      v[q] = a;
+      *reinterpret_cast<h8_t*>(r_next + (uint64_t)row * H + 8 * i) = a;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) ss = fmaf((float)a[e], (float)a[e], ss);
+    }
+  }
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) ss += __shfl_xor(ss, off);
+  if ((t & 63) == 0) part[t >> 6] = ss;
+  __syncthreads();
+  float tot = 0.f;
+  for (int i = 0; i < (int)(blockDim.x >> 6); ++i) tot += part[i];
+  const float inv = 1.0f / sqrtf(tot / (float)H + eps);
+#pragma unroll
+  for (int q = 0; q < kRuns; ++q) {
+    const int i = t + q * (int)blockDim.x;
+    if (i < nv) {
+      h8_t o;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) o[e] = (_Float16)((float)v[q][e] * inv);
+      *reinterpret_cast<h8_t*>(x + (uint64_t)row * H + 8 * i) = o;
+    }
+  }
+}
+
+hipError_t launch_router_topk(const float* logits, int M, int E, int k, int32_t* ids, float* w, hipStream_t stream) {
+  // E <= 4096 over at most 1024 threads: at most 4 keys per thread
+  int threads = ((E + 63) / 64) * 64;
+  if (threads > 1024) threads = 1024;
+  hipLaunchKernelGGL(router_topk_kernel, dim3(M), dim3(threads), 0, stream, logits, E, k, ids, w);
+  return hipGetLastError();
+}
+
+hipError_t launch_residual_rmsnorm(const uint16_t* r, const uint16_t* delta, int M, int H, float eps,
+                                   uint16_t* r_next, uint16_t* x, hipStream_t stream) {
+  int threads = ((H / 8 + 63) / 64) * 64;
+  if (threads > 1024) threads = 1024;
+  hipLaunchKernelGGL(residual_rmsnorm_kernel, dim3(M), dim3(threads), 0, stream, r, delta, H, eps, r_next, x);
+  return hipGetLastError();
+}
+
 hipError_t launch_route_compact(const int32_t* ids, int n, int E, const RouteOut& o, hipStream_t stream) {
   hipLaunchKernelGGL(route_compact_kernel, dim3(1), dim3(256), 0, stream, ids, n, E, o);
   return hipGetLastError();
@@ -506,18 +662,25 @@ hipError_t launch_w13_swiglu(const StageArgs& a, const uint16_t* x, uint16_t* ac
   return hipGetLastError();
 }
 
+template <int RB, int TPW>
+static void launch_w2_t(const StageArgs& a, const uint16_t* act, const float* topk_w, uint16_t* out,
+                        hipStream_t stream) {
+  const int lanes = a.topk * TPW * 4 * (a.I / 32);
+  const dim3 block(lanes >= 1024 ? 1024 : ((lanes + 63) / 64) * 64);
+  const dim3 grid(a.H / (16 * TPW), a.M);
+  hipLaunchKernelGGL((w2_reduce_kernel<RB, TPW>), grid, block, 0, stream, a.topk_ids, a.bank + a.w2_off,
+                     a.bank + a.w2_meta_off, act, a.expert_bytes, a.H, a.I, a.topk, a.E, topk_w, out);
+}
+
+// One 16-column tile per workgroup: groups of 2 or 4 adjacent tiles (longer
+// contiguous runs per expert) measured no faster, at 4 slower, on hot and
+// on cold weights.
 hipError_t launch_w2_reduce(const StageArgs& a, const uint16_t* act, const float* topk_w, uint16_t* out,
                             hipStream_t stream) {
-  const int LS = 4 * (a.I / 32);
-  const int lanes = a.topk * LS;
-  const dim3 block(lanes >= 1024 ? 1024 : ((lanes + 63) / 64) * 64);
-  const dim3 grid(a.H / 16, a.M);
   if (a.RB == 4)
-    hipLaunchKernelGGL(w2_reduce_kernel<4>, grid, block, 0, stream, a.topk_ids, a.bank + a.w2_off, a.bank + a.w2_meta_off,
-                       act, a.expert_bytes, a.H, a.I, a.topk, a.E, topk_w, out);
+    launch_w2_t<4, 1>(a, act, topk_w, out, stream);
   else
-    hipLaunchKernelGGL(w2_reduce_kernel<3>, grid, block, 0, stream, a.topk_ids, a.bank + a.w2_off, a.bank + a.w2_meta_off,
-                       act, a.expert_bytes, a.H, a.I, a.topk, a.E, topk_w, out);
+    launch_w2_t<3, 1>(a, act, topk_w, out, stream);
   return hipGetLastError();
 }
 

@@ -176,3 +176,32 @@ def router_logits(rng: np.random.Generator, M: int, E: int) -> np.ndarray:
 
 def call_rng(seed: int, tag: int) -> np.random.Generator:
     return np.random.Generator(np.random.PCG64(np.random.SeedSequence([int(seed), 0xC0, int(tag)])))
+
+
+def device_bank(seed: int, num_experts: int, record_sections, expert_bytes: int, meta_bytes: int,
+                device="cuda"):
+    """A packed bank drawn directly on the device (for many-layer workloads).
+
+    Uniform random bytes are uniform 4-bit values, so every byte of the bank
+    is first drawn U{0..255}. Each record section ``(offset, count)`` of
+    every expert block is then overwritten with ``count`` records of
+    ``meta_bytes`` bytes: scale = fp16(|N(0,1)| * 0.02) (little endian),
+    zero ~ U{0..15}, and a zero pad byte for 4-byte records. The draws come
+    from one seeded torch generator in the order: bank bytes, then for each
+    section the normals and then the zeros. Returns a uint8 device tensor.
+    """
+    import torch
+    g = torch.Generator(device=device)
+    g.manual_seed(int(seed))
+    total = num_experts * expert_bytes
+    bank = torch.randint(0, 256, (total,), dtype=torch.uint8, device=device, generator=g)
+    blocks = bank.view(num_experts, expert_bytes)
+    for off, count in record_sections:
+        s = (torch.randn((num_experts, count), device=device, generator=g).abs() * 0.02).to(torch.float16)
+        z = torch.randint(0, 16, (num_experts, count), dtype=torch.uint8, device=device, generator=g)
+        rec = blocks[:, off:off + count * meta_bytes].view(num_experts, count, meta_bytes)
+        rec[:, :, 0:2] = s.view(torch.uint8).view(num_experts, count, 2)
+        rec[:, :, 2] = z
+        if meta_bytes == 4:
+            rec[:, :, 3] = 0
+    return bank

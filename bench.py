@@ -45,7 +45,7 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=200)
     p.add_argument("--warmup", type=int, default=20)
-    p.add_argument("--only", default="", help="comma list of workloads: m1_hot,m1_cold,m8_pool,m8_distinct")
+    p.add_argument("--only", default="", help="comma list of workloads: m1_hot,m1_cold,m8_pool,m8_distinct,stack48")
     p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     return p.parse_args()
 
@@ -68,6 +68,49 @@ class Workload:
         self.distinct_mean = float(np.mean(distinct))
         self.w13_bytes = [d * per_expert["w13"] for d in distinct]
         self.w2_bytes = [d * per_expert["w2"] for d in distinct]
+
+
+def measure_stack(abi, torch, steps, warmup, layers=48, M=8):
+    """One decode step of a stack of 512-expert layers (3-byte records, banks
+    drawn on the device): per layer, residual update + RMS norm, router top-k
+    over fp32 N(0,1) logits, then the stage. One graph replay = one step."""
+    dims = abi.make_dims(E, H, I, 3)
+    Lq = abi.awq_moe_bank_layout_query(dims)
+    sections = [(int(Lq.w13_meta_off), (H // 32) * 2 * I), (int(Lq.w2_meta_off), (I // 32) * H)]
+    banks = [inputs.device_bank(SEED + 9000 + l, E, sections, int(Lq.expert_bytes), 3) for l in range(layers)]
+    rng = inputs.call_rng(SEED, 900)
+    logits = [torch.from_numpy(inputs.router_logits(rng, M, E)).to("cuda") for _ in range(layers)]
+    r0 = torch.from_numpy(inputs.activations(rng, M, H)).to("cuda")
+    rbuf = [torch.empty_like(r0) for _ in range(2)]
+    xbuf = torch.empty_like(r0)
+    outs = [torch.empty_like(r0) for _ in range(layers)]
+    ids = [torch.empty((M, K_TOP), dtype=torch.int32, device="cuda") for _ in range(layers)]
+    wts = [torch.empty((M, K_TOP), dtype=torch.float32, device="cuda") for _ in range(layers)]
+    ws = abi.alloc_workspace(dims, M, K_TOP, "cuda")
+
+    def step():
+        r = r0
+        for l in range(layers):
+            rn = rbuf[l % 2]
+            abi.awq_moe_residual_rmsnorm(r, None if l == 0 else outs[l - 1], r_next=rn, x=xbuf)
+            abi.awq_moe_router_topk(logits[l], K_TOP, ids=ids[l], w=wts[l])
+            abi.awq_moe_decode(dims, banks[l], xbuf, ids[l], wts[l], out=outs[l], workspace=ws)
+            r = rn
+
+    step()
+    torch.cuda.synchronize()
+    distinct = [len(np.unique(t.cpu().numpy())) for t in ids]
+    g = capture(torch, step)
+    ms = time_graph(torch, g, steps, warmup)
+    del g
+    touched = float(sum(distinct)) * float(Lq.expert_bytes)
+    out = {"layers": layers, "M": M, "step_us": ms * 1e3, "layer_us": ms * 1e3 / layers,
+           "distinct_experts_per_layer": float(np.mean(distinct)), "touched_bytes_per_step": touched,
+           "gbs": touched / (ms * 1e6), "pct_peak": 100.0 * touched / (ms * 1e6) / HBM_PEAK_GBS,
+           "resident_bank_bytes": int(Lq.total_bytes) * layers, "launches_per_layer": 4}
+    del banks
+    torch.cuda.empty_cache()
+    return out
 
 
 def per_expert_bytes(abi, dims):
@@ -271,7 +314,7 @@ def main():
     from awq_int4_mixture_amd import abi
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     torch.cuda.set_device(0)
-    only = set(filter(None, args.only.split(","))) or {"m1_hot", "m1_cold", "m8_pool", "m8_distinct"}
+    only = set(filter(None, args.only.split(","))) or {"m1_hot", "m1_cold", "m8_pool", "m8_distinct", "stack48"}
 
     t_gen = time.perf_counter()
     bi = inputs.bank_inputs(SEED, E, H, I)
@@ -311,10 +354,17 @@ def main():
             ids = [inputs.ids_all_distinct(inputs.call_rng(SEED, 400 + c), 8, K_TOP, E) for c in range(CALLS)]
             wl = Workload("m8_distinct", abi, torch, dims, bank, ids, 8, rng, per_expert_bytes(abi, dims))
             results["m8_distinct"] = measure(abi, torch, wl, args.steps, args.warmup)
+        if "stack48" in only:
+            del banks
+            torch.cuda.empty_cache()
+            stack = measure_stack(abi, torch, max(args.steps // 4, 10), max(args.warmup // 4, 2))
         ceiling = copy_ceiling(torch)
         read_ref = read_ceiling(torch)
         floor = launch_floor(torch)
 
+    if not results:
+        print(json.dumps({"stack48": stack}), flush=True)
+        return
     head = results.get("m1_hot") or next(iter(results.values()))
     line = {
         "metric": "MoE layer decode µs and achieved weight HBM GB/s (% of peak) at M=1 and M=8",
@@ -338,6 +388,7 @@ def main():
         "roofline": roofline(head),
         "per_config": {k: {kk: (round(vv, 4) if isinstance(vv, float) else vv) for kk, vv in v.items()}
                        for k, v in results.items()},
+        "stack48": stack if "stack48" in only else None,
         "copy_reference": ceiling,
         "read_reference": read_ref,
         "launch_floor": floor,

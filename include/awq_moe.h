@@ -70,6 +70,7 @@ extern "C" {
 #define AWQ_MOE_MAX_TOPK 32
 #define AWQ_MOE_MAX_HIDDEN 8192
 #define AWQ_MOE_MAX_INTER 2048
+#define AWQ_MOE_MAX_ROUTER_EXPERTS 4096
 #define AWQ_MOE_STATUS_BAD_ID 1u
 
 typedef struct awq_moe_dims {
@@ -177,6 +178,32 @@ int awq_moe_w13_swiglu(const awq_moe_dims* dims, const void* bank, const uint16_
 int awq_moe_w2_reduce(const awq_moe_dims* dims, const void* bank, const int32_t* topk_ids,
                       const float* topk_w, int32_t M, int32_t topk, const void* workspace,
                       uint64_t workspace_bytes, uint16_t* out, void* stream);
+
+/* --- support for a stack of MoE layers (not part of the stage itself) --- */
+
+/* Router top-k + softmax for M = 1..8 tokens. The pages leave the router
+ * unchanged (fork PR #12, Purpose and stack); this is the library's reading:
+ * per token, the topk largest fp32 logits, compared exactly (-0 == +0, NaN
+ * below every number, ties to the lower expert id), listed by descending
+ * logit, and w = softmax over the topk selected logits in fp32
+ * (max-subtracted). All pointers device:
+ *   logits   fp32 [M][num_experts], C-contiguous, 4-byte aligned
+ *   topk_ids int32 [M][topk] out; topk_w fp32 [M][topk] out
+ * num_experts in [1, AWQ_MOE_MAX_ROUTER_EXPERTS]; topk in [1, min(32,
+ * num_experts)]. One launch (one wave per token). */
+int awq_moe_router_topk(const float* logits, int32_t M, int32_t num_experts, int32_t topk,
+                        int32_t* topk_ids, float* topk_w, void* stream);
+
+/* Residual update and parameter-free RMS norm between stacked layers (not on
+ * the pages: fp16 residuals chained through many layers overflow without a
+ * norm). Per row t of M = 1..8 rows, in fp32:
+ *   r_next[t] = fp16_rne(r[t] + delta[t])      (delta NULL: r_next[t] = r[t])
+ *   x[t]      = fp16_rne(r_next[t] / sqrt(mean(r_next[t]^2) + eps))
+ * r, delta, r_next, x: device fp16 [M][hidden], 16-byte aligned; hidden a
+ * multiple of 8 in [8, AWQ_MOE_MAX_HIDDEN]; r_next and x must not overlap r,
+ * delta or each other. eps in (0, 1]. One launch. */
+int awq_moe_residual_rmsnorm(const uint16_t* r, const uint16_t* delta, int32_t M, int32_t hidden,
+                             float eps, uint16_t* r_next, uint16_t* x, void* stream);
 
 /* Dequantise experts [expert_begin, expert_begin + expert_count) of the bank
  * into fp32 (diagnostic). Each value s * (q - z) is exact in fp32: q - z is an

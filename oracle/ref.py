@@ -190,8 +190,9 @@ def topk_softmax(logits: np.ndarray, k: int):
         sel = order[:k]
         ids[t] = sel
         v = lg[t, sel].astype(np.float64)
-        p = np.exp(v - v.max())
-        w[t] = p / p.sum()
+        with np.errstate(invalid="ignore"):      # inf - inf and NaN give NaN weights, as in fp32
+            p = np.exp(v - v.max())
+            w[t] = p / p.sum()
     return ids, w
 
 

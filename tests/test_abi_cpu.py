@@ -122,6 +122,8 @@ def test_device_calls_reject_bad_arguments_before_launch():
     base = (ctypes.addressof(buf) + 255) // 256 * 256
     p = ctypes.c_void_p(base)
     mis = ctypes.c_void_p(base + 2)
+    q1 = ctypes.c_void_p(base + 1024)       # two disjoint 1 KiB row buffers
+    q2 = ctypes.c_void_p(base + 2048)
     ws_need = abi.awq_moe_workspace_bytes(d, 1, 10)
     cases = [
         (lambda: lib.awq_moe_decode(ctypes.byref(d), p, p, p, p, 9, 10, p, p, ws_need, None), abi.EINVAL),
@@ -144,6 +146,21 @@ def test_device_calls_reject_bad_arguments_before_launch():
         (lambda: lib.awq_moe_w2_reduce(ctypes.byref(d), p, p, None, 1, 10, p, ws_need, p, None), abi.EINVAL),
         (lambda: lib.awq_moe_dequant(ctypes.byref(d), p, 510, 3, 0, p, None), abi.EINVAL),
         (lambda: lib.awq_moe_dequant(ctypes.byref(d), p, 0, 1, 2, p, None), abi.EINVAL),
+        (lambda: lib.awq_moe_router_topk(p, 0, 512, 10, p, p, None), abi.EINVAL),
+        (lambda: lib.awq_moe_router_topk(p, 9, 512, 10, p, p, None), abi.EINVAL),
+        (lambda: lib.awq_moe_router_topk(p, 1, 4097, 10, p, p, None), abi.EINVAL),
+        (lambda: lib.awq_moe_router_topk(p, 1, 8, 9, p, p, None), abi.EINVAL),
+        (lambda: lib.awq_moe_router_topk(p, 1, 512, 33, p, p, None), abi.EINVAL),
+        (lambda: lib.awq_moe_router_topk(None, 1, 512, 10, p, p, None), abi.EINVAL),
+        (lambda: lib.awq_moe_router_topk(mis, 1, 512, 10, p, p, None), abi.EINVAL),
+        (lambda: lib.awq_moe_residual_rmsnorm(p, None, 1, 2560, 0.0, q1, q2, None), abi.EINVAL),
+        (lambda: lib.awq_moe_residual_rmsnorm(p, None, 9, 256, 1e-6, q1, q2, None), abi.EINVAL),
+        (lambda: lib.awq_moe_residual_rmsnorm(p, None, 1, 256, 1e-6, p, q2, None), abi.EINVAL),
+        (lambda: lib.awq_moe_residual_rmsnorm(p, q2, 1, 256, 1e-6, q1, q2, None), abi.EINVAL),
+        (lambda: lib.awq_moe_residual_rmsnorm(p, None, 1, 256, 1e-6, q1, q1, None), abi.EINVAL),
+        (lambda: lib.awq_moe_residual_rmsnorm(p, None, 1, 8193, 1e-6, q1, q2, None), abi.EINVAL),
+        (lambda: lib.awq_moe_residual_rmsnorm(p, None, 1, 100, 1e-6, q1, q2, None), abi.EINVAL),
+        (lambda: lib.awq_moe_residual_rmsnorm(mis, None, 1, 256, 1e-6, q1, q2, None), abi.EINVAL),
     ]
     for i, (call, code) in enumerate(cases):
         assert call() == code, (i, abi.awq_moe_last_error())
