@@ -373,8 +373,8 @@ __global__ __launch_bounds__(1024) void w2_reduce_kernel(const int32_t* __restri
                                                          uint16_t* __restrict__ out) {
   constexpr int NC = 16 * TPW;                     // columns per workgroup
   __shared__ float red[4096];                      // [slot in pass][tile][g][16]; <= 4*blockDim
-  __shared__ float ys[AWQ_MOE_KMAX_TOPK * NC];     // [slot][NC]: the slot's column results
-  __shared__ int ord[AWQ_MOE_KMAX_TOPK];           // rank -> slot
+  __shared__ float ys[AWQ_MOE_KMAX_TOPK * NC];     // [rank][NC]: a valid slot's column results
+  __shared__ int rk[AWQ_MOE_KMAX_TOPK];            // slot -> rank (-1: invalid slot)
   __shared__ float wr[AWQ_MOE_KMAX_TOPK];          // rank -> router weight
   __shared__ int nvalid_s;
   // Workgroups are handed to the 8 XCDs round robin by linear id, so with
@@ -415,13 +415,11 @@ __global__ __launch_bounds__(1024) void w2_reduce_kernel(const int32_t* __restri
       const bool v = t < topk && id >= 0 && id < E;
       int r = 0;
       for (int j2 = 0; j2 < topk; ++j2) {
-        const int k2 = __shfl(id, j2);
+        const int k2 = __builtin_amdgcn_readlane(id, j2);
         r += (k2 >= 0 && k2 < E) & ((k2 < id) | ((k2 == id) & (j2 < t)));
       }
-      if (v) {
-        ord[r] = t;
-        wr[r] = wt;
-      }
+      if (t < topk) rk[t] = v ? r : -1;
+      if (v) wr[r] = wt;
       const unsigned long long b = __ballot(v);
       if (t == 0) nvalid_s = (int)__popcll(b);
     }
@@ -435,15 +433,16 @@ __global__ __launch_bounds__(1024) void w2_reduce_kernel(const int32_t* __restri
             rec.s[j] * (unit_dot(w[j], av, mg) - fmaf(rec.z[j], S, Cs));
     }
     __syncthreads();
-    // per-slot column results of this pass, groups summed in ascending g
-    // (rows of invalid slots hold stale values and are never read)
+    // per-slot column results of this pass, groups summed in ascending g,
+    // stored at the slot's rank (invalid slots are skipped)
     for (int u = t; u < spp * NC; u += blockDim.x) {
       const int ps = u / NC, cc = u - ps * NC;
       const int t2 = cc >> 4, c = cc & 15;
-      if (s0 + ps < topk) {
+      const int r = s0 + ps < topk ? rk[s0 + ps] : -1;
+      if (r >= 0) {
         float y = 0.f;
         for (int gg = 0; gg < G2; ++gg) y += red[((ps * TPW + t2) * G2 + gg) * 16 + c];
-        ys[(s0 + ps) * NC + cc] = y;
+        ys[r * NC + cc] = y;
       }
     }
     __syncthreads();
@@ -451,7 +450,8 @@ __global__ __launch_bounds__(1024) void w2_reduce_kernel(const int32_t* __restri
   if (t < NC) {
     const int nv = nvalid_s;
     float acc = 0.f;
-    for (int r = 0; r < nv; ++r) acc = fmaf(wr[r], ys[ord[r] * NC + t], acc);
+#pragma unroll 4
+    for (int r = 0; r < nv; ++r) acc = fmaf(wr[r], ys[r * NC + t], acc);
     out[(uint64_t)tok * H + nt0 * 16 + t] = __builtin_bit_cast(uint16_t, (_Float16)acc);
   }
 }
