@@ -203,6 +203,16 @@ struct __attribute__((aligned(16))) Compact {
   int num_active, nvalid;
 };
 
+// Sum over the 4 lanes of a quad (DPP quad permutes); every lane gets the sum.
+__device__ __forceinline__ int quad_sum(int v) {
+  v += __builtin_amdgcn_update_dpp(0, v, 0xB1, 0xF, 0xF, false);  // quad_perm [1,0,3,2]
+  v += __builtin_amdgcn_update_dpp(0, v, 0x4E, 0xF, 0xF, false);  // quad_perm [2,3,0,1]
+  return v;
+}
+
+// Each slot's comparisons against all n keys are split over the 4 lanes of
+// a quad (lane p takes every 4th group of four keys), and the counts are
+// summed with quad permutes. blockDim is a multiple of 64 and at least 4n.
 __device__ void block_compact(const int32_t* __restrict__ ids, int n, int E, Compact& C) {
   const int t = threadIdx.x, bd = blockDim.x;
   const int n4 = (n + 3) & ~3;
@@ -216,10 +226,12 @@ __device__ void block_compact(const int32_t* __restrict__ ids, int n, int E, Com
     C.firstkey[s] = kNoKey;
   }
   __syncthreads();
-  for (int s = t; s < n; s += bd) {
-    const int id = C.key[s];
+  const int p = t & 3;
+  const int s = t >> 2;  // every lane of a quad has the same slot
+  {
+    const int id = s < n ? C.key[s] : -2;
     int before = 0, inv_before = 0, nvalid = 0, dup_before = 0;
-    for (int s2 = 0; s2 < n4; s2 += 4) {
+    for (int s2 = 4 * p; s2 < n4; s2 += 16) {
       const int4 k4 = *reinterpret_cast<const int4*>(&C.key[s2]);
       const int kk[4] = {k4.x, k4.y, k4.z, k4.w};
 #pragma unroll
@@ -232,17 +244,23 @@ __device__ void block_compact(const int32_t* __restrict__ ids, int n, int E, Com
         inv_before += (k2 == -1) & earlier;
       }
     }
-    const int r = (id >= 0) ? before : nvalid + inv_before;
-    C.rank[s] = r;
-    C.sorted[r] = s;
-    if (id >= 0 && dup_before == 0) C.firstkey[s] = id;
-    if (s == 0) C.nvalid = nvalid;
+    before = quad_sum(before);
+    inv_before = quad_sum(inv_before);
+    nvalid = quad_sum(nvalid);
+    dup_before = quad_sum(dup_before);
+    if (s < n && p == 0) {
+      const int r = (id >= 0) ? before : nvalid + inv_before;
+      C.rank[s] = r;
+      C.sorted[r] = s;
+      if (id >= 0 && dup_before == 0) C.firstkey[s] = id;
+      if (s == 0) C.nvalid = nvalid;
+    }
   }
   __syncthreads();
-  for (int s = t; s < n; s += bd) {
-    const int fk = C.firstkey[s];
+  {
+    const int fk = s < n ? C.firstkey[s] : kNoKey;
     int below = 0, nseg = 0;
-    for (int s2 = 0; s2 < n4; s2 += 4) {
+    for (int s2 = 4 * p; s2 < n4; s2 += 16) {
       const int4 f4 = *reinterpret_cast<const int4*>(&C.firstkey[s2]);
       const int ff[4] = {f4.x, f4.y, f4.z, f4.w};
 #pragma unroll
@@ -251,13 +269,17 @@ __device__ void block_compact(const int32_t* __restrict__ ids, int n, int E, Com
         nseg += ff[q] != kNoKey;
       }
     }
-    if (fk != kNoKey) {
-      C.seg_e[below] = fk;
-      C.seg_off[below] = C.rank[s];
-    }
-    if (s == 0) {
-      C.num_active = nseg;
-      C.seg_off[nseg] = C.nvalid;
+    below = quad_sum(below);
+    nseg = quad_sum(nseg);
+    if (s < n && p == 0) {
+      if (fk != kNoKey) {
+        C.seg_e[below] = fk;
+        C.seg_off[below] = C.rank[s];
+      }
+      if (s == 0) {
+        C.num_active = nseg;
+        C.seg_off[nseg] = C.nvalid;
+      }
     }
   }
   __syncthreads();
@@ -278,7 +300,7 @@ __device__ void store_route(const Compact& C, int n, const RouteOut& o) {
   }
 }
 
-__global__ __launch_bounds__(256) void route_compact_kernel(const int32_t* __restrict__ ids, int n, int E,
+__global__ __launch_bounds__(1024) void route_compact_kernel(const int32_t* __restrict__ ids, int n, int E,
                                                             RouteOut o) {
   __shared__ Compact C;
   block_compact(ids, n, E, C);
@@ -644,7 +666,9 @@ hipError_t launch_residual_rmsnorm(const uint16_t* r, const uint16_t* delta, int
 }
 
 hipError_t launch_route_compact(const int32_t* ids, int n, int E, const RouteOut& o, hipStream_t stream) {
-  hipLaunchKernelGGL(route_compact_kernel, dim3(1), dim3(256), 0, stream, ids, n, E, o);
+  // four lanes per slot, at least one wave
+  const int threads = ((4 * n + 63) / 64) * 64;
+  hipLaunchKernelGGL(route_compact_kernel, dim3(1), dim3(threads), 0, stream, ids, n, E, o);
   return hipGetLastError();
 }
 
