@@ -289,7 +289,7 @@ def cpu_baseline(bi, ids_calls, rng_seed, budget_s=12.0):
 def roofline(head):
     """HBM roofline of the longer of the two stage kernels at the headline workload."""
     k = "w2" if head["w2_us"] >= head["w13_us"] else "w13"
-    name = {"w13": "w13_swiglu_kernel<4>", "w2": "w2_reduce_kernel<4>"}[k]
+    name = {"w13": "w13_swiglu_kernel<4>", "w2": "w2_reduce_kernel<4, 1>"}[k]
     gbs = head[k + "_gbs"]
     return {
         "bound": "hbm",

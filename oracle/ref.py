@@ -160,6 +160,35 @@ def w2_reduce(act_rows: np.ndarray, topk_w: np.ndarray, route: dict, topk: int,
     return out
 
 
+def w2_rounding_bound(act_rows: np.ndarray, topk_w: np.ndarray, route: dict, topk: int,
+                      weights_of, M: int, H: int):
+    """Informational bound on |fp16 out - exact out| for W2 + reduction from a
+    given act (the pages print no bound formula; this is the standard one).
+
+    An fp32 evaluation that accumulates the n products w * act[i] * Wd[i][c]
+    of token t in any order errs by at most gamma_n * sum of their magnitudes
+    (Higham's dot-product bound), and the final rounding to fp16 adds at most
+    half an fp16 ulp, 2^-11 * |out|. Here n = (valid rows of the token) * I,
+    plus one per row for the weighting. Returns (bound [M][H], exact out).
+    """
+    a64 = np.asarray(act_rows).astype(np.float64)
+    w64 = np.asarray(topk_w).astype(np.float64).reshape(-1)
+    out = np.zeros((M, H))
+    mag = np.zeros((M, H))
+    nterms = np.zeros(M, dtype=np.int64)
+    for a in range(route["num_active"]):
+        e = int(route["active_ids"][a])
+        _, _, Wd = expert_dense(weights_of(e))
+        for r in range(route["offsets"][a], route["offsets"][a + 1]):
+            slot = int(route["sorted_slots"][r])
+            t = slot // topk
+            out[t] += w64[slot] * (a64[r] @ Wd)
+            mag[t] += abs(w64[slot]) * (np.abs(a64[r]) @ np.abs(Wd))
+            nterms[t] += Wd.shape[0] + 1
+    gam = np.array([higham_gamma(int(n)) for n in nterms])
+    return gam[:, None] * mag + 2.0 ** -11 * np.abs(out), out
+
+
 def moe_stage(x: np.ndarray, topk_ids: np.ndarray, topk_w: np.ndarray, num_experts: int,
               weights_of) -> np.ndarray:
     """The whole stage for M tokens, float64 [M][H] (no intermediate rounding)."""

@@ -133,6 +133,11 @@ def test_w13_stage_and_w2_stage_pair(rb, M):
     torch.cuda.synchronize()
     out_ref = R.w2_reduce(act_sorted, w, route_o, 10, bi.expert, M, H)
     check(f16_to_np(out), out_ref, f"w2 on own act M={M} rb={rb}")
+    # informational rounding bound of the W2 step on its own act
+    bound, exact = R.w2_rounding_bound(act_sorted, w, route_o, 10, bi.expert, M, H)
+    frac = np.abs(f16_to_np(out).astype(np.float64) - exact) / bound
+    say(f"w2 rounding bound M={M} rb={rb}: max |gpu - exact| / bound = {frac.max():.3f}")
+    assert frac.max() <= 1.0
 
 
 @pytest.mark.parametrize("rb", [3, 4])

@@ -268,3 +268,47 @@ def test_planted_oracle_mistakes_are_caught(mistake, monkeypatch):
     want = np.array(LP.stage_loops(x.astype(np.float64).tolist(), ids.tolist(),
                                    w.astype(np.float64).tolist(), 4, bi.expert))
     assert np.abs(got - want).max() > 1e-6 * np.abs(want).max()
+
+
+def test_rms_norm_worked_values_and_closed_forms():
+    """[3, 4] has mean square 12.5: [3, 4] / sqrt(12.5) = [0.848528137..., 1.131370849...];
+    a constant row c maps to sign(c) / sqrt(1 + eps / c^2); a positive scale of
+    the row changes the result only through eps."""
+    got = R.rms_norm(np.array([[3.0, 4.0]], np.float16), eps=0.0)
+    np.testing.assert_allclose(got, [[0.8485281374238570, 1.1313708498984760]], rtol=1e-15)
+    got = R.rms_norm(np.full((1, 8), -2.0), eps=1e-6)
+    np.testing.assert_allclose(got, np.full((1, 8), -1.0 / np.sqrt(1.0 + 1e-6 / 4.0)), rtol=1e-15)
+    rng = np.random.default_rng(3)
+    r = rng.standard_normal((3, 64))
+    np.testing.assert_allclose(R.rms_norm(r * 8.0, eps=0.0), R.rms_norm(r, eps=0.0), rtol=1e-13)
+    # every row of the output has mean square ms / (ms + eps)
+    out = R.rms_norm(r, eps=1e-2)
+    ms = (r * r).mean(axis=1)
+    np.testing.assert_allclose((out * out).mean(axis=1), ms / (ms + 1e-2), rtol=1e-13)
+
+
+def test_w2_rounding_bound_covers_a_float32_evaluation():
+    """A plain fp32 evaluation (sequential sums in NumPy float32, then fp16)
+    must fall inside the bound; the bound must not be vacuous (it is below
+    the output magnitude for most elements)."""
+    E, H, I, M, k = 6, 64, 64, 3, 4
+    bi = inputs.bank_inputs(9, E, H, I)
+    rng = inputs.call_rng(9, 1)
+    ids = inputs.ids_distinct(rng, M, k, E)
+    wts = inputs.router_weights(rng, M, k)
+    route = R.route_compact(ids, E)
+    act = rng.standard_normal((M * k, I)).astype(np.float16)
+    bound, exact = R.w2_rounding_bound(act, wts, route, k, bi.expert, M, H)
+    f32 = np.zeros((M, H), np.float32)
+    for a in range(route["num_active"]):
+        e = int(route["active_ids"][a])
+        Wd = R.expert_dense(bi.expert(e))[2].astype(np.float32)
+        for r in range(route["offsets"][a], route["offsets"][a + 1]):
+            slot = int(route["sorted_slots"][r])
+            acc = np.zeros(H, np.float32)
+            for i in range(I):
+                acc = acc + np.float32(act[r, i]) * Wd[i]
+            f32[slot // k] = f32[slot // k] + np.float32(wts.reshape(-1)[slot]) * acc
+    got = f32.astype(np.float16).astype(np.float64)
+    assert np.all(np.abs(got - exact) <= bound)
+    assert np.mean(bound < np.abs(exact)) > 0.9
