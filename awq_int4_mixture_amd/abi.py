@@ -27,7 +27,8 @@ WS_ACT_OFFSET = 256
 EXPORTED = (
     "awq_moe_bank_layout_query", "awq_moe_prepare", "awq_moe_workspace_bytes",
     "awq_moe_route_compact", "awq_moe_decode", "awq_moe_w13_swiglu", "awq_moe_w2_reduce",
-    "awq_moe_dequant", "awq_moe_router_topk", "awq_moe_residual_rmsnorm", "awq_moe_last_error",
+    "awq_moe_dequant", "awq_moe_router_topk", "awq_moe_residual_rmsnorm", "awq_moe_router_residual",
+    "awq_moe_last_error",
 )
 
 
@@ -73,6 +74,7 @@ def _load() -> ctypes.CDLL:
         "awq_moe_dequant": [D, P, I32, I32, I32, P, V],
         "awq_moe_router_topk": [P, I32, I32, I32, P, P, V],
         "awq_moe_residual_rmsnorm": [P, P, I32, I32, ctypes.c_float, P, P, V],
+        "awq_moe_router_residual": [P, I32, I32, I32, P, P, P, P, I32, ctypes.c_float, P, P, V],
     }
     for name, args in sig.items():
         f = getattr(lib, name)
@@ -300,6 +302,30 @@ def awq_moe_residual_rmsnorm(r, delta=None, eps: float = 1e-6, r_next=None, x=No
                                          _dev(x, torch.float16, (M, H), "x"), _stream(stream)),
            "awq_moe_residual_rmsnorm")
     return r_next, x
+
+
+def awq_moe_router_residual(logits, topk: int, r, delta=None, eps: float = 1e-6, ids=None, w=None, r_next=None,
+                            x=None, stream=None):
+    """Router top-k + softmax and the residual/RMS-norm step in one launch.
+    Returns (ids, w, r_next, x)."""
+    torch = _torch()
+    M, E = logits.shape
+    H = r.shape[1]
+    if ids is None:
+        ids = torch.empty((M, topk), dtype=torch.int32, device=logits.device)
+    if w is None:
+        w = torch.empty((M, topk), dtype=torch.float32, device=logits.device)
+    if r_next is None:
+        r_next = torch.empty_like(r)
+    if x is None:
+        x = torch.empty_like(r)
+    dp = None if delta is None else _dev(delta, torch.float16, (M, H), "delta")
+    _check(_lib.awq_moe_router_residual(
+        _dev(logits, torch.float32, (M, E), "logits"), M, E, topk, _dev(ids, torch.int32, (M, topk), "ids"),
+        _dev(w, torch.float32, (M, topk), "w"), _dev(r, torch.float16, (M, H), "r"), dp, H, eps,
+        _dev(r_next, torch.float16, (M, H), "r_next"), _dev(x, torch.float16, (M, H), "x"), _stream(stream)),
+        "awq_moe_router_residual")
+    return ids, w, r_next, x
 
 
 def awq_moe_last_error() -> str:

@@ -264,8 +264,8 @@ int awq_moe_route_compact(const int32_t* topk_ids, int32_t M, int32_t topk, int3
                     "route_compact launch");
 }
 
-int awq_moe_router_topk(const float* logits, int32_t M, int32_t num_experts, int32_t topk, int32_t* topk_ids,
-                        float* topk_w, void* stream) {
+int check_router_args(const float* logits, int32_t M, int32_t num_experts, int32_t topk, const int32_t* topk_ids,
+                      const float* topk_w) {
   if (M < 1 || M > AWQ_MOE_MAX_TOKENS) return fail(AWQ_MOE_EINVAL, "M %d outside [1, %d]", M, AWQ_MOE_MAX_TOKENS);
   if (num_experts < 1 || num_experts > AWQ_MOE_MAX_ROUTER_EXPERTS)
     return fail(AWQ_MOE_EINVAL, "num_experts %d outside [1, %d]", num_experts, AWQ_MOE_MAX_ROUTER_EXPERTS);
@@ -274,15 +274,11 @@ int awq_moe_router_topk(const float* logits, int32_t M, int32_t num_experts, int
   if (!logits || !aligned(logits, 4)) return fail(AWQ_MOE_EINVAL, "logits null or misaligned");
   if (!topk_ids || !aligned(topk_ids, 4)) return fail(AWQ_MOE_EINVAL, "topk_ids null or misaligned");
   if (!topk_w || !aligned(topk_w, 4)) return fail(AWQ_MOE_EINVAL, "topk_w null or misaligned");
-  int rc = check_device();
-  if (rc) return rc;
-  return hip_status(awq_moe::launch_router_topk(logits, M, num_experts, topk, topk_ids, topk_w,
-                                                static_cast<hipStream_t>(stream)),
-                    "router launch");
+  return AWQ_MOE_OK;
 }
 
-int awq_moe_residual_rmsnorm(const uint16_t* r, const uint16_t* delta, int32_t M, int32_t hidden, float eps,
-                             uint16_t* r_next, uint16_t* x, void* stream) {
+int check_residual_args(const uint16_t* r, const uint16_t* delta, int32_t M, int32_t hidden, float eps,
+                        const uint16_t* r_next, const uint16_t* x) {
   if (M < 1 || M > AWQ_MOE_MAX_TOKENS) return fail(AWQ_MOE_EINVAL, "M %d outside [1, %d]", M, AWQ_MOE_MAX_TOKENS);
   if (hidden < 8 || hidden > AWQ_MOE_MAX_HIDDEN || hidden % 8)
     return fail(AWQ_MOE_EINVAL, "hidden %d: a multiple of 8 in [8, %d]", hidden, AWQ_MOE_MAX_HIDDEN);
@@ -297,11 +293,39 @@ int awq_moe_residual_rmsnorm(const uint16_t* r, const uint16_t* delta, int32_t M
   };
   if (overlap(r_next, r) || overlap(r_next, delta) || overlap(x, r) || overlap(x, delta) || overlap(x, r_next))
     return fail(AWQ_MOE_EINVAL, "r_next and x must not overlap r, delta or each other");
-  int rc = check_device();
+  return AWQ_MOE_OK;
+}
+
+int awq_moe_router_topk(const float* logits, int32_t M, int32_t num_experts, int32_t topk, int32_t* topk_ids,
+                        float* topk_w, void* stream) {
+  int rc = check_router_args(logits, M, num_experts, topk, topk_ids, topk_w);
   if (rc) return rc;
+  if ((rc = check_device())) return rc;
+  return hip_status(awq_moe::launch_router_topk(logits, M, num_experts, topk, topk_ids, topk_w,
+                                                static_cast<hipStream_t>(stream)),
+                    "router launch");
+}
+
+int awq_moe_residual_rmsnorm(const uint16_t* r, const uint16_t* delta, int32_t M, int32_t hidden, float eps,
+                             uint16_t* r_next, uint16_t* x, void* stream) {
+  int rc = check_residual_args(r, delta, M, hidden, eps, r_next, x);
+  if (rc) return rc;
+  if ((rc = check_device())) return rc;
   return hip_status(awq_moe::launch_residual_rmsnorm(r, delta, M, hidden, eps, r_next, x,
                                                      static_cast<hipStream_t>(stream)),
                     "residual_rmsnorm launch");
+}
+
+int awq_moe_router_residual(const float* logits, int32_t M, int32_t num_experts, int32_t topk, int32_t* topk_ids,
+                            float* topk_w, const uint16_t* r, const uint16_t* delta, int32_t hidden, float eps,
+                            uint16_t* r_next, uint16_t* x, void* stream) {
+  int rc = check_router_args(logits, M, num_experts, topk, topk_ids, topk_w);
+  if (rc) return rc;
+  if ((rc = check_residual_args(r, delta, M, hidden, eps, r_next, x))) return rc;
+  if ((rc = check_device())) return rc;
+  return hip_status(awq_moe::launch_router_residual(logits, M, num_experts, topk, topk_ids, topk_w, r, delta, hidden,
+                                                    eps, r_next, x, static_cast<hipStream_t>(stream)),
+                    "router_residual launch");
 }
 
 int check_stage(const awq_moe_dims* dims, const void* bank, int32_t M, int32_t topk, const void* workspace,

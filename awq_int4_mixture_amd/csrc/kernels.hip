@@ -547,15 +547,14 @@ __device__ __forceinline__ uint64_t readlane_u64(uint64_t v, int lane) {
 // themselves with lane reads (no memory round trips) and keeps its k best
 // as candidates at fixed places chunk*k + rank. (2) Each candidate is
 // ranked among all candidates in LDS; rank < k is the answer.
-__global__ __launch_bounds__(1024) void router_topk_kernel(const float* __restrict__ logits, int E, int k,
-                                                           int32_t* __restrict__ ids, float* __restrict__ w) {
+__device__ void router_topk_row(const float* __restrict__ lg, int E, int k, int32_t* __restrict__ ids,
+                                float* __restrict__ w) {
   __shared__ uint64_t cand[AWQ_MOE_KMAX_ROUTER_E / 64 * AWQ_MOE_KMAX_TOPK];
   __shared__ float cand_v[AWQ_MOE_KMAX_ROUTER_E / 64 * AWQ_MOE_KMAX_TOPK];
   __shared__ float sel_v[AWQ_MOE_KMAX_TOPK];
   __shared__ float sel_p[AWQ_MOE_KMAX_TOPK];
-  const int tok = blockIdx.x, t = threadIdx.x, nt = blockDim.x;
+  const int t = threadIdx.x, nt = blockDim.x;
   const int lane = t & 63, wave = t >> 6, nwaves = nt >> 6;
-  const float* lg = logits + (uint64_t)tok * E;
   const int nchunks = (E + 63) >> 6;
   const int ncand = nchunks * k;
   for (int c = t; c < ncand; c += nt) cand[c] = 0;  // 0 sorts below every key
@@ -580,7 +579,7 @@ __global__ __launch_bounds__(1024) void router_topk_kernel(const float* __restri
 #pragma unroll 8
     for (int j = 0; j < ncand; ++j) r += cand[j] > kc;
     if (r < k) {
-      ids[tok * k + r] = (int)(0xFFFFFFFFu - (uint32_t)kc);
+      ids[r] = (int)(0xFFFFFFFFu - (uint32_t)kc);
       sel_v[r] = cand_v[c];
     }
   }
@@ -591,8 +590,14 @@ __global__ __launch_bounds__(1024) void router_topk_kernel(const float* __restri
     if (t < k) sel_p[t] = p;
     float sum = 0.f;  // in rank order
     for (int r = 0; r < k; ++r) sum += sel_p[r];
-    if (t < k) w[tok * k + t] = p / sum;
+    if (t < k) w[t] = p / sum;
   }
+}
+
+__global__ __launch_bounds__(1024) void router_topk_kernel(const float* __restrict__ logits, int E, int k,
+                                                           int32_t* __restrict__ ids, float* __restrict__ w) {
+  const int tok = blockIdx.x;
+  router_topk_row(logits + (uint64_t)tok * E, E, k, ids + tok * k, w + tok * k);
 }
 
 // ---------------------------------------------------------------------------
@@ -604,31 +609,38 @@ __global__ __launch_bounds__(1024) void router_topk_kernel(const float* __restri
 // ---------------------------------------------------------------------------
 typedef _Float16 h8_t __attribute__((ext_vector_type(8)));
 
-__global__ __launch_bounds__(1024) void residual_rmsnorm_kernel(const uint16_t* __restrict__ r,
-                                                                const uint16_t* __restrict__ delta, int H, float eps,
-                                                                uint16_t* __restrict__ r_next,
-                                                                uint16_t* __restrict__ x) {
+// One run of 8 values per thread (blockDim >= H/8, H <= 8192, H % 8 == 0).
+struct ResRow {
+  h8_t a, b;
+};
+
+// Issue the loads of row r (and delta) for this thread's run.
+__device__ __forceinline__ ResRow residual_load(const uint16_t* __restrict__ r, const uint16_t* __restrict__ delta,
+                                                int H) {
+  ResRow rr;
+  const int i = threadIdx.x;
+  if (i < (H >> 3)) {
+    rr.a = *reinterpret_cast<const h8_t*>(r + 8 * i);
+    if (delta) rr.b = *reinterpret_cast<const h8_t*>(delta + 8 * i);
+  }
+  return rr;
+}
+
+__device__ void residual_finish(const ResRow& rr, bool has_delta, int H, float eps, uint16_t* __restrict__ r_next,
+                                uint16_t* __restrict__ x) {
   __shared__ float part[16];
-  const int row = blockIdx.x, t = threadIdx.x;
-  const int nv = H >> 3;  // runs of 8 (H % 8 == 0 on this path)
-  constexpr int kRuns = 1;  // blockDim = min(1024, H/8 rounded up to 64) and H <= 8192: one run per thread
-  h8_t v[kRuns];
+  const int t = threadIdx.x;
+  const bool on = t < (H >> 3);
+  h8_t a = rr.a;
   float ss = 0.f;
+  if (on) {
+    if (has_delta) {
 #pragma unroll
-  for (int q = 0; q < kRuns; ++q) {
-    const int i = t + q * (int)blockDim.x;
-    if (i < nv) {
-      h8_t a = *reinterpret_cast<const h8_t*>(r + (uint64_t)row * H + 8 * i);
-      if (delta) {
-        const h8_t b = *reinterpret_cast<const h8_t*>(delta + (uint64_t)row * H + 8 * i);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) a[e] = (_Float16)((float)a[e] + (float)b[e]);
-      }
-      v[q] = a;
-      *reinterpret_cast<h8_t*>(r_next + (uint64_t)row * H + 8 * i) = a;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) ss = fmaf((float)a[e], (float)a[e], ss);
+      for (int e = 0; e < 8; ++e) a[e] = (_Float16)((float)a[e] + (float)rr.b[e]);
     }
+    *reinterpret_cast<h8_t*>(r_next + 8 * t) = a;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) ss = fmaf((float)a[e], (float)a[e], ss);
   }
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) ss += __shfl_xor(ss, off);
@@ -637,16 +649,37 @@ __global__ __launch_bounds__(1024) void residual_rmsnorm_kernel(const uint16_t* 
   float tot = 0.f;
   for (int i = 0; i < (int)(blockDim.x >> 6); ++i) tot += part[i];
   const float inv = 1.0f / sqrtf(tot / (float)H + eps);
+  if (on) {
+    h8_t o;
 #pragma unroll
-  for (int q = 0; q < kRuns; ++q) {
-    const int i = t + q * (int)blockDim.x;
-    if (i < nv) {
-      h8_t o;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) o[e] = (_Float16)((float)v[q][e] * inv);
-      *reinterpret_cast<h8_t*>(x + (uint64_t)row * H + 8 * i) = o;
-    }
+    for (int e = 0; e < 8; ++e) o[e] = (_Float16)((float)a[e] * inv);
+    *reinterpret_cast<h8_t*>(x + 8 * t) = o;
   }
+}
+
+__global__ __launch_bounds__(1024) void residual_rmsnorm_kernel(const uint16_t* __restrict__ r,
+                                                                const uint16_t* __restrict__ delta, int H, float eps,
+                                                                uint16_t* __restrict__ r_next,
+                                                                uint16_t* __restrict__ x) {
+  const uint64_t o = (uint64_t)blockIdx.x * H;
+  const ResRow rr = residual_load(r + o, delta ? delta + o : nullptr, H);
+  residual_finish(rr, delta != nullptr, H, eps, r_next + o, x + o);
+}
+
+// Both per-token steps between two stacked layers in one launch: the
+// residual rows' loads are issued first, the router runs while they are in
+// flight, then the norm finishes.
+__global__ __launch_bounds__(1024) void router_residual_kernel(const float* __restrict__ logits, int E, int k,
+                                                               int32_t* __restrict__ ids, float* __restrict__ w,
+                                                               const uint16_t* __restrict__ r,
+                                                               const uint16_t* __restrict__ delta, int H, float eps,
+                                                               uint16_t* __restrict__ r_next,
+                                                               uint16_t* __restrict__ x) {
+  const int tok = blockIdx.x;
+  const uint64_t o = (uint64_t)tok * H;
+  const ResRow rr = residual_load(r + o, delta ? delta + o : nullptr, H);
+  router_topk_row(logits + (uint64_t)tok * E, E, k, ids + tok * k, w + tok * k);
+  residual_finish(rr, delta != nullptr, H, eps, r_next + o, x + o);
 }
 
 hipError_t launch_router_topk(const float* logits, int M, int E, int k, int32_t* ids, float* w, hipStream_t stream) {
@@ -662,6 +695,18 @@ hipError_t launch_residual_rmsnorm(const uint16_t* r, const uint16_t* delta, int
   int threads = ((H / 8 + 63) / 64) * 64;
   if (threads > 1024) threads = 1024;
   hipLaunchKernelGGL(residual_rmsnorm_kernel, dim3(M), dim3(threads), 0, stream, r, delta, H, eps, r_next, x);
+  return hipGetLastError();
+}
+
+hipError_t launch_router_residual(const float* logits, int M, int E, int k, int32_t* ids, float* w,
+                                  const uint16_t* r, const uint16_t* delta, int H, float eps, uint16_t* r_next,
+                                  uint16_t* x, hipStream_t stream) {
+  int threads = ((E + 63) / 64) * 64;
+  const int rt = ((H / 8 + 63) / 64) * 64;
+  if (rt > threads) threads = rt;
+  if (threads > 1024) threads = 1024;
+  hipLaunchKernelGGL(router_residual_kernel, dim3(M), dim3(threads), 0, stream, logits, E, k, ids, w, r, delta, H,
+                     eps, r_next, x);
   return hipGetLastError();
 }
 

@@ -72,8 +72,9 @@ class Workload:
 
 def measure_stack(abi, torch, steps, warmup, layers=48, M=8):
     """One decode step of a stack of 512-expert layers (3-byte records, banks
-    drawn on the device): per layer, residual update + RMS norm, router top-k
-    over fp32 N(0,1) logits, then the stage. One graph replay = one step."""
+    drawn on the device): per layer, residual update + RMS norm and router
+    top-k over fp32 N(0,1) logits (one launch), then the stage (two
+    launches). One graph replay = one step."""
     dims = abi.make_dims(E, H, I, 3)
     Lq = abi.awq_moe_bank_layout_query(dims)
     sections = [(int(Lq.w13_meta_off), (H // 32) * 2 * I), (int(Lq.w2_meta_off), (I // 32) * H)]
@@ -92,8 +93,8 @@ def measure_stack(abi, torch, steps, warmup, layers=48, M=8):
         r = r0
         for l in range(layers):
             rn = rbuf[l % 2]
-            abi.awq_moe_residual_rmsnorm(r, None if l == 0 else outs[l - 1], r_next=rn, x=xbuf)
-            abi.awq_moe_router_topk(logits[l], K_TOP, ids=ids[l], w=wts[l])
+            abi.awq_moe_router_residual(logits[l], K_TOP, r, None if l == 0 else outs[l - 1], ids=ids[l], w=wts[l],
+                                        r_next=rn, x=xbuf)
             abi.awq_moe_decode(dims, banks[l], xbuf, ids[l], wts[l], out=outs[l], workspace=ws)
             r = rn
 
@@ -107,7 +108,7 @@ def measure_stack(abi, torch, steps, warmup, layers=48, M=8):
     out = {"layers": layers, "M": M, "step_us": ms * 1e3, "layer_us": ms * 1e3 / layers,
            "distinct_experts_per_layer": float(np.mean(distinct)), "touched_bytes_per_step": touched,
            "gbs": touched / (ms * 1e6), "pct_peak": 100.0 * touched / (ms * 1e6) / HBM_PEAK_GBS,
-           "resident_bank_bytes": int(Lq.total_bytes) * layers, "launches_per_layer": 4}
+           "resident_bank_bytes": int(Lq.total_bytes) * layers, "launches_per_layer": 3}
     del banks
     torch.cuda.empty_cache()
     return out

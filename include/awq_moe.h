@@ -205,6 +205,15 @@ int awq_moe_router_topk(const float* logits, int32_t M, int32_t num_experts, int
 int awq_moe_residual_rmsnorm(const uint16_t* r, const uint16_t* delta, int32_t M, int32_t hidden,
                              float eps, uint16_t* r_next, uint16_t* x, void* stream);
 
+/* awq_moe_residual_rmsnorm and awq_moe_router_topk in one launch (the two
+ * per-token steps between stacked layers; one workgroup per token). The
+ * results are bit-identical to the two calls; arguments and errors are the
+ * union of theirs, with one M for both. */
+int awq_moe_router_residual(const float* logits, int32_t M, int32_t num_experts, int32_t topk,
+                            int32_t* topk_ids, float* topk_w, const uint16_t* r,
+                            const uint16_t* delta, int32_t hidden, float eps, uint16_t* r_next,
+                            uint16_t* x, void* stream);
+
 /* Dequantise experts [expert_begin, expert_begin + expert_count) of the bank
  * into fp32 (diagnostic). Each value s * (q - z) is exact in fp32: q - z is an
  * integer in [-255, 15] and s an fp16, so the product needs at most 19

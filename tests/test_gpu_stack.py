@@ -81,6 +81,22 @@ def test_residual_rmsnorm():
     assert np.max(np.abs(f16_to_np(x2) - R.rms_norm(r)) / np.maximum(np.abs(R.rms_norm(r)), 2.0 ** -14)) <= 2.0 ** -10
 
 
+@pytest.mark.parametrize("E,H,k", [(512, 2560, 10), (4096, 256, 32), (64, 8192, 4)])
+def test_router_residual_equals_the_two_calls(E, H, k):
+    rng = inputs.call_rng(504, E + H)
+    M = 8
+    logits = to_dev(inputs.router_logits(rng, M, E))
+    r = to_dev((rng.standard_normal((M, H)) * 2).astype(np.float16))
+    d = to_dev(rng.standard_normal((M, H)).astype(np.float16))
+    ids1, w1 = abi.awq_moe_router_topk(logits, k)
+    rn1, x1 = abi.awq_moe_residual_rmsnorm(r, d)
+    ids2, w2, rn2, x2 = abi.awq_moe_router_residual(logits, k, r, d)
+    torch.cuda.synchronize()
+    for a, b in ((ids1, ids2), (w1, w2), (rn1, rn2), (x1, x2)):
+        assert torch.equal(a.view(torch.uint8) if a.dtype != torch.int32 else a,
+                           b.view(torch.uint8) if b.dtype != torch.int32 else b)
+
+
 def experts_from_bank(d, bank_np):
     """weights_of(e) for the oracle, decoded by the oracle from the bank bytes."""
     cache = {}
@@ -113,8 +129,7 @@ def test_stack_teacher_forced_four_layers():
             dec = abi.Decoder(dims, bank, K, max_tokens=M)
         dec.bank = bank
         logits = inputs.router_logits(rng, M, E)
-        r_next, x = abi.awq_moe_residual_rmsnorm(r, None if layer == 0 else out)
-        ids, w = abi.awq_moe_router_topk(to_dev(logits), K)
+        ids, w, r_next, x = abi.awq_moe_router_residual(to_dev(logits), K, r, None if layer == 0 else out)
         out = dec(x, ids, w)
         torch.cuda.synchronize()
         want_ids, want_w = R.topk_softmax(logits, K)
