@@ -91,6 +91,25 @@ __device__ __forceinline__ Act32 load_act32(const uint16_t* p) {
   return a;
 }
 
+// The same 32 values for a quad of lanes (4 adjacent lanes, one group): lane
+// q of the quad loads quarter q (16 bytes) and DPP quad broadcasts hand every
+// lane all four quarters, so the quad issues one load per lane instead of four.
+// All four lanes of the quad must be active.
+template <int Q>
+__device__ __forceinline__ uint32_t quad_bcast(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, Q | (Q << 2) | (Q << 4) | (Q << 6), 0xF, 0xF, false);
+}
+
+__device__ __forceinline__ Act32 load_act32_quad(const uint16_t* p, int quad) {
+  const uint4 v = *reinterpret_cast<const uint4*>(p + 8 * quad);
+  Act32 a;
+  a.px[0] = quad_bcast<0>(v.x); a.px[1] = quad_bcast<0>(v.y); a.px[2] = quad_bcast<0>(v.z); a.px[3] = quad_bcast<0>(v.w);
+  a.px[4] = quad_bcast<1>(v.x); a.px[5] = quad_bcast<1>(v.y); a.px[6] = quad_bcast<1>(v.z); a.px[7] = quad_bcast<1>(v.w);
+  a.px[8] = quad_bcast<2>(v.x); a.px[9] = quad_bcast<2>(v.y); a.px[10] = quad_bcast<2>(v.z); a.px[11] = quad_bcast<2>(v.w);
+  a.px[12] = quad_bcast<3>(v.x); a.px[13] = quad_bcast<3>(v.y); a.px[14] = quad_bcast<3>(v.z); a.px[15] = quad_bcast<3>(v.w);
+  return a;
+}
+
 // Per-group sums: S = sum x, C = 1024 * (x at 1024-offset slots) + 64 * (x at 64-offset slots).
 __device__ __forceinline__ void group_sums(const Act32& a, float& S, float& C) {
   const uint32_t one2 = 0x3C003C00u;  // fp16 (1.0, 1.0)
@@ -429,7 +448,7 @@ __global__ __launch_bounds__(1024) void w2_reduce_kernel(const int32_t* __restri
 #pragma unroll
       for (int j = 0; j < 4; ++j) w[j] = *reinterpret_cast<const uint4*>(units + ((uint64_t)j * LS + tl) * 16u);
       rec = load_records<RB>(recs_base + eo + (uint64_t)(nt0 + tt) * 16u * G2 * RB + (uint64_t)tl * 4u * RB);
-      av = load_act32(act + (uint64_t)(tok * topk + slot) * I + 32 * g);
+      av = load_act32_quad(act + (uint64_t)(tok * topk + slot) * I + 32 * g, quad);
     }
     if (s0 == 0 && t < 64) {
       const int id = t < topk ? ids[t] : -1;
