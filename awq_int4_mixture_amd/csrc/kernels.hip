@@ -498,6 +498,105 @@ __global__ __launch_bounds__(1024) void w2_reduce_kernel(const int32_t* __restri
 }
 
 // ---------------------------------------------------------------------------
+// W2 + router-weighted reduction for I <= 256 (at most 32 lanes per slot):
+// grid (H/16 tiles, M tokens) as above, but every slot owns one 32-lane half
+// of a wave, so a wave holds two slots. The two ids arrive as wave-uniform
+// scalar loads, and the sum over the slot's groups runs in registers (DPP
+// row rotations within 16 lanes, one exchange across the two rows of the
+// half), which leaves a single LDS round for the router-weighted sum in
+// ascending (expert, slot) order.
+// ---------------------------------------------------------------------------
+template <int RB>
+__global__ __launch_bounds__(1024) void w2_reduce32_kernel(const int32_t* __restrict__ topk_ids,
+                                                           const uint8_t* __restrict__ units_base,
+                                                           const uint8_t* __restrict__ recs_base,
+                                                           const uint16_t* __restrict__ act, uint64_t expert_bytes,
+                                                           int H, int I, int topk, int E,
+                                                           const float* __restrict__ topk_w,
+                                                           uint16_t* __restrict__ out) {
+  __shared__ float ys[AWQ_MOE_KMAX_TOPK * 16];     // [rank][16]
+  __shared__ int rk[AWQ_MOE_KMAX_TOPK];            // slot -> rank (-1: invalid slot)
+  __shared__ float wr[AWQ_MOE_KMAX_TOPK];          // rank -> router weight
+  __shared__ int nvalid_s;
+  const int T2 = H >> 4;
+  const int nt = (T2 & 7) ? (int)blockIdx.x : (int)((blockIdx.x & 7) * (T2 >> 3) + (blockIdx.x >> 3));
+  const int tok = blockIdx.y;
+  const int t = threadIdx.x, lane = t & 63;
+  const int G2 = I >> 5, LS = 4 * G2;  // LS <= 32
+  const int32_t* ids = topk_ids + tok * topk;
+  // the wave's two slots; indexes clamped into the token's ids (unused past topk)
+  const int w2 = __builtin_amdgcn_readfirstlane(t >> 6) * 2;
+  const int e0 = ids[w2 < topk ? w2 : topk - 1];
+  const int e1 = ids[w2 + 1 < topk ? w2 + 1 : topk - 1];
+  const int slot = t >> 5, tl = t & 31;
+  const int e = (t & 32) ? e1 : e0;
+  const bool live = slot < topk && tl < LS && e >= 0 && e < E;
+  const int g = tl >> 2, quad = tl & 3;
+  float part[4] = {0.f, 0.f, 0.f, 0.f};
+  uint4 w[4];
+  Records<RB> rec;
+  Act32 av;
+  if (live) {
+    const uint64_t eo = (uint64_t)e * expert_bytes;
+    const uint8_t* units = units_base + eo + (uint64_t)nt * 256u * G2;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) w[j] = *reinterpret_cast<const uint4*>(units + ((uint64_t)j * LS + tl) * 16u);
+    rec = load_records<RB>(recs_base + eo + (uint64_t)nt * 16u * G2 * RB + (uint64_t)tl * 4u * RB);
+    av = load_act32_quad(act + (uint64_t)(tok * topk + slot) * I + 32 * g, quad);
+  }
+  if (t < 64) {
+    // rank of slot t among the valid slots by (id, slot), while the loads fly
+    const int id = t < topk ? ids[t] : -1;
+    const bool v = t < topk && id >= 0 && id < E;
+    int r = 0;
+    for (int j2 = 0; j2 < topk; ++j2) {
+      const int k2 = __builtin_amdgcn_readlane(id, j2);
+      r += (k2 >= 0 && k2 < E) & ((k2 < id) | ((k2 == id) & (j2 < t)));
+    }
+    if (t < topk) rk[t] = v ? r : -1;
+    if (v) wr[r] = topk_w[tok * topk + t];
+    const unsigned long long b = __ballot(v);
+    if (t == 0) nvalid_s = (int)__popcll(b);
+  }
+  if (live) {
+    float S, Cs;
+    group_sums(av, S, Cs);
+    const Magic mg = make_magic();
+#pragma unroll
+    for (int j = 0; j < 4; ++j) part[j] = rec.s[j] * (unit_dot(w[j], av, mg) - fmaf(rec.z[j], S, Cs));
+  }
+  // sum over the groups of the half (lane bits 2..4): rotations by 4 and 8
+  // inside each 16-lane row, then the two rows of the half trade two values
+  // each, so lane l ends with columns 4*(l & 3) + 2*b4 and + 1 (b4 = bit 4).
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    part[j] += dpp<kRowRor4>(part[j]);
+    part[j] += dpp<kRowRor8>(part[j]);
+  }
+  const bool b4 = (lane & 16) != 0;
+  float k0 = b4 ? part[2] : part[0], k1 = b4 ? part[3] : part[1];
+  k0 += __shfl_xor(b4 ? part[0] : part[2], 16);
+  k1 += __shfl_xor(b4 ? part[1] : part[3], 16);
+  __syncthreads();  // rk is ready
+  if ((lane & 12) == 0 && slot < topk) {
+    const int r = rk[slot];
+    if (r >= 0) {
+      const int c = 4 * (lane & 3) + 2 * (int)b4;
+      ys[r * 16 + c] = k0;
+      ys[r * 16 + c + 1] = k1;
+    }
+  }
+  __syncthreads();
+  if (t < 16) {
+    const int nv = nvalid_s;
+    float acc = 0.f;
+#pragma unroll 4
+    for (int r = 0; r < nv; ++r) acc = fmaf(wr[r], ys[r * 16 + t], acc);
+    out[(uint64_t)tok * H + nt * 16 + t] = __builtin_bit_cast(uint16_t, (_Float16)acc);
+  }
+}
+
+// ---------------------------------------------------------------------------
 // dequantisation (diagnostic): one thread per unit, writes 32 fp32 values
 // ---------------------------------------------------------------------------
 template <int RB>
@@ -765,6 +864,18 @@ static void launch_w2_t(const StageArgs& a, const uint16_t* act, const float* to
 // on cold weights.
 hipError_t launch_w2_reduce(const StageArgs& a, const uint16_t* act, const float* topk_w, uint16_t* out,
                             hipStream_t stream) {
+  if (a.I <= 256) {
+    // one 32-lane half per slot, two slots per wave
+    const dim3 block(((a.topk * 32 + 63) / 64) * 64);
+    const dim3 grid(a.H / 16, a.M);
+    if (a.RB == 4)
+      hipLaunchKernelGGL(w2_reduce32_kernel<4>, grid, block, 0, stream, a.topk_ids, a.bank + a.w2_off,
+                         a.bank + a.w2_meta_off, act, a.expert_bytes, a.H, a.I, a.topk, a.E, topk_w, out);
+    else
+      hipLaunchKernelGGL(w2_reduce32_kernel<3>, grid, block, 0, stream, a.topk_ids, a.bank + a.w2_off,
+                         a.bank + a.w2_meta_off, act, a.expert_bytes, a.H, a.I, a.topk, a.E, topk_w, out);
+    return hipGetLastError();
+  }
   if (a.RB == 4)
     launch_w2_t<4, 1>(a, act, topk_w, out, stream);
   else
