@@ -290,7 +290,8 @@ def cpu_baseline(bi, ids_calls, rng_seed, budget_s=12.0):
 def roofline(head):
     """HBM roofline of the longer of the two stage kernels at the headline workload."""
     k = "w2" if head["w2_us"] >= head["w13_us"] else "w13"
-    name = {"w13": "w13_swiglu_kernel<4>", "w2": "w2_reduce_kernel<4, 1>"}[k]
+    # at inter <= 256 the W2 launch is the two-slots-per-wave kernel
+    name = {"w13": "w13_swiglu_kernel<4>", "w2": "w2_reduce32_kernel<4>" if I <= 256 else "w2_reduce_kernel<4, 1>"}[k]
     gbs = head[k + "_gbs"]
     return {
         "bound": "hbm",
