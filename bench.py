@@ -171,13 +171,23 @@ def measure(abi, torch, wl: Workload, steps, warmup):
     res = {}
     # "layer" = awq_moe_decode (two launches, one workgroup per slot and tile);
     # "route" = the standalone awq_moe_route_compact kernel, not part of the layer.
-    for name, fn in (("layer", full), ("route", route), ("w13", w13), ("w2", w2)):
-        g = capture(torch, fn)
+    graphs = {name: capture(torch, fn) for name, fn in (("layer", full), ("route", route), ("w13", w13), ("w2", w2))}
+    for name, g in graphs.items():
         ms = time_graph(torch, g, steps, warmup)
         res[name + "_us"] = ms * 1e3 / CALLS
         if name == "layer":
             res["step_ms"] = ms
-        del g
+    # 7 further samples per graph, in alternating (ABBA) order, for the median and the minimum
+    per_sample = max(steps // 7, 10)
+    samples = {name: [] for name in graphs}
+    names = list(graphs)
+    for r in range(7):
+        for name in (names if r % 2 == 0 else names[::-1]):
+            samples[name].append(time_graph(torch, graphs[name], per_sample, 2) * 1e3 / CALLS)
+    for name, v in samples.items():
+        res[name + "_us_median7"] = float(np.median(v))
+        res[name + "_us_min7"] = float(np.min(v))
+    del graphs
     w13b = float(np.mean(wl.w13_bytes))
     w2b = float(np.mean(wl.w2_bytes))
     res.update(
