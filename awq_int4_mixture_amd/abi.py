@@ -28,7 +28,7 @@ EXPORTED = (
     "awq_moe_bank_layout_query", "awq_moe_prepare", "awq_moe_workspace_bytes",
     "awq_moe_route_compact", "awq_moe_decode", "awq_moe_w13_swiglu", "awq_moe_w2_reduce",
     "awq_moe_dequant", "awq_moe_router_topk", "awq_moe_residual_rmsnorm", "awq_moe_router_residual",
-    "awq_moe_last_error",
+    "awq_moe_router_gemv", "awq_moe_last_error",
 )
 
 
@@ -75,6 +75,7 @@ def _load() -> ctypes.CDLL:
         "awq_moe_router_topk": [P, I32, I32, I32, P, P, V],
         "awq_moe_residual_rmsnorm": [P, P, I32, I32, ctypes.c_float, P, P, V],
         "awq_moe_router_residual": [P, I32, I32, I32, P, P, P, P, I32, ctypes.c_float, P, P, V],
+        "awq_moe_router_gemv": [P, P, I32, I32, ctypes.c_float, P, I32, P, P, P, V],
     }
     for name, args in sig.items():
         f = getattr(lib, name)
@@ -326,6 +327,26 @@ def awq_moe_router_residual(logits, topk: int, r, delta=None, eps: float = 1e-6,
         _dev(r_next, torch.float16, (M, H), "r_next"), _dev(x, torch.float16, (M, H), "x"), _stream(stream)),
         "awq_moe_router_residual")
     return ids, w, r_next, x
+
+
+def awq_moe_router_gemv(r, router_w, delta=None, eps: float = 1e-6, r_next=None, x=None, logits=None, stream=None):
+    """Residual + RMS norm, then fp32 logits = x . router_w^T (router_w fp16 [E][H]).
+    Returns (r_next, x, logits)."""
+    torch = _torch()
+    M, H = r.shape
+    E = router_w.shape[0]
+    if r_next is None:
+        r_next = torch.empty_like(r)
+    if x is None:
+        x = torch.empty_like(r)
+    if logits is None:
+        logits = torch.empty((M, E), dtype=torch.float32, device=r.device)
+    dp = None if delta is None else _dev(delta, torch.float16, (M, H), "delta")
+    _check(_lib.awq_moe_router_gemv(
+        _dev(r, torch.float16, (M, H), "r"), dp, M, H, eps, _dev(router_w, torch.float16, (E, H), "router_w"), E,
+        _dev(r_next, torch.float16, (M, H), "r_next"), _dev(x, torch.float16, (M, H), "x"),
+        _dev(logits, torch.float32, (M, E), "logits"), _stream(stream)), "awq_moe_router_gemv")
+    return r_next, x, logits
 
 
 def awq_moe_last_error() -> str:

@@ -328,6 +328,21 @@ int awq_moe_router_residual(const float* logits, int32_t M, int32_t num_experts,
                     "router_residual launch");
 }
 
+int awq_moe_router_gemv(const uint16_t* r, const uint16_t* delta, int32_t M, int32_t hidden, float eps,
+                        const uint16_t* router_w, int32_t num_experts, uint16_t* r_next, uint16_t* x, float* logits,
+                        void* stream) {
+  int rc = check_residual_args(r, delta, M, hidden, eps, r_next, x);
+  if (rc) return rc;
+  if (num_experts < 1 || num_experts > AWQ_MOE_MAX_ROUTER_EXPERTS)
+    return fail(AWQ_MOE_EINVAL, "num_experts %d outside [1, %d]", num_experts, AWQ_MOE_MAX_ROUTER_EXPERTS);
+  if (!router_w || !aligned(router_w, 16)) return fail(AWQ_MOE_EINVAL, "router_w null or not 16-byte aligned");
+  if (!logits || !aligned(logits, 4)) return fail(AWQ_MOE_EINVAL, "logits null or misaligned");
+  if ((rc = check_device())) return rc;
+  return hip_status(awq_moe::launch_router_gemv(r, delta, M, hidden, eps, router_w, num_experts, r_next, x, logits,
+                                                static_cast<hipStream_t>(stream)),
+                    "router_gemv launch");
+}
+
 int check_stage(const awq_moe_dims* dims, const void* bank, int32_t M, int32_t topk, const void* workspace,
                 uint64_t workspace_bytes) {
   int rc = check_dims(dims);

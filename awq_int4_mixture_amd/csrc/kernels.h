@@ -45,6 +45,10 @@ hipError_t launch_residual_rmsnorm(const uint16_t* r, const uint16_t* delta, int
 hipError_t launch_router_residual(const float* logits, int M, int E, int k, int32_t* ids, float* w,
                                   const uint16_t* r, const uint16_t* delta, int H, float eps, uint16_t* r_next,
                                   uint16_t* x, hipStream_t stream);
+// Residual update + RMS norm of M rows, then fp32 logits = x . wr^T
+// (wr fp16 [E][H]).
+hipError_t launch_router_gemv(const uint16_t* r, const uint16_t* delta, int M, int H, float eps, const uint16_t* wr,
+                              int E, uint16_t* r_next, uint16_t* x, float* logits, hipStream_t stream);
 hipError_t launch_dequant(const uint8_t* bank, uint64_t expert_bytes, uint64_t units_off,
                           uint64_t meta_off, int RB, int which, int H, int I, int expert_begin,
                           int expert_count, float* out, hipStream_t stream);

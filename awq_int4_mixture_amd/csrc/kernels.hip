@@ -25,22 +25,16 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "device_util.h"
 #include "kernels.h"
 
 namespace awq_moe {
 
-typedef _Float16 h2_t __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x3_a4 __attribute__((ext_vector_type(3), aligned(4)));
 
 // Bit pattern constants of the nibble -> fp16 conversion.
 constexpr uint32_t kLoMask = 0x000F000Fu;   // values at bits 0 and 16
 constexpr uint32_t kHiMask = 0x00F000F0u;   // values at bits 4 and 20
-
-__device__ __forceinline__ h2_t as_h2(uint32_t v) { return __builtin_bit_cast(h2_t, v); }
-
-__device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c) {
-  return __builtin_amdgcn_fdot2(as_h2(a), as_h2(b), c, false);
-}
 
 // Records of a lane's four columns: scale (fp16 -> fp32, exact) and zero.
 template <int RB>
@@ -159,49 +153,6 @@ __device__ __forceinline__ float unit_dot(const uint4& w, const Act32& a, const 
 
 __device__ __forceinline__ float silu_mul(float g, float u) {
   return g / (1.0f + __expf(-g)) * u;
-}
-
-// Cross-lane sums in the VALU (DPP row operations and lane shuffles), no LDS round trip.
-template <int CTRL>
-__device__ __forceinline__ float dpp(float v) {
-  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
-}
-constexpr int kRowRor4 = 0x124, kRowRor8 = 0x128;
-constexpr int kQuadSwap1 = 0xB1;  // quad_perm [1,0,3,2]
-constexpr int kQuadSwap2 = 0x4E;  // quad_perm [2,3,0,1]
-constexpr int kRowHalfMirror = 0x141;
-
-// Sum four per-lane values over the 16 lanes that share lane bits 0..1 (one
-// column quad of a wave): two DPP row rotations sum within each 16-lane row
-// in the VALU; then a reduce-scatter across rows: the xor-16 exchange trades
-// two of the four values, the xor-32 exchange one, so lane l ends with the
-// full sum of value 2*b4 + b5 (b4, b5 = lane bits 4, 5). The lanes with
-// (lane & 12) == 0 carry the four results of their quad.
-__device__ __forceinline__ float sum4_lane_bits_2to5(float p0, float p1, float p2, float p3) {
-  p0 += dpp<kRowRor4>(p0);
-  p1 += dpp<kRowRor4>(p1);
-  p2 += dpp<kRowRor4>(p2);
-  p3 += dpp<kRowRor4>(p3);
-  p0 += dpp<kRowRor8>(p0);
-  p1 += dpp<kRowRor8>(p1);
-  p2 += dpp<kRowRor8>(p2);
-  p3 += dpp<kRowRor8>(p3);
-  const int lane = threadIdx.x & 63;
-  const bool b4 = (lane & 16) != 0, b5 = (lane & 32) != 0;
-  float k0 = b4 ? p2 : p0, k1 = b4 ? p3 : p1;
-  k0 += __shfl_xor(b4 ? p0 : p2, 16);
-  k1 += __shfl_xor(b4 ? p1 : p3, 16);
-  float k = b5 ? k1 : k0;
-  k += __shfl_xor(b5 ? k0 : k1, 32);
-  return k;
-}
-
-// Sum over aligned groups of 8 lanes (lane bits 0..2); every lane gets the sum.
-__device__ __forceinline__ float sum_lane_bits_0to2(float v) {
-  v += dpp<kQuadSwap1>(v);
-  v += dpp<kQuadSwap2>(v);
-  v += dpp<kRowHalfMirror>(v);
-  return v;
 }
 
 // ---------------------------------------------------------------------------
@@ -634,200 +585,6 @@ __global__ void dequant_kernel(const uint8_t* __restrict__ bank, uint64_t expert
 // ---------------------------------------------------------------------------
 // launchers
 // ---------------------------------------------------------------------------
-// ---------------------------------------------------------------------------
-// Router top-k + softmax (the layer-stack workload's per-layer router; the
-// pages leave the router unchanged, fork PR #12, Purpose and stack).
-// One workgroup per token. Each logit becomes a 64-bit key that orders by
-// value (exact fp32 order, -0 == +0, NaN below every number) and then by
-// lower id:  key = ord(value) << 32 | (0xFFFFFFFF - id), ord mapping the
-// float bit pattern to an order-preserving uint32. Keys are distinct, so
-// the number of larger keys is an element's rank. The softmax over the k
-// winners is fp32, summed in rank order.
-// ---------------------------------------------------------------------------
-__device__ __forceinline__ uint64_t router_key(float v, int id) {
-  uint32_t ord;
-  if (v != v) {
-    ord = 0u;  // NaN: below every number
-  } else {
-    const uint32_t u = __builtin_bit_cast(uint32_t, v == 0.f ? 0.f : v);
-    ord = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
-  }
-  return ((uint64_t)ord << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)id);
-}
-
-__device__ __forceinline__ uint64_t readlane_u64(uint64_t v, int lane) {
-  const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)v, lane);
-  const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(v >> 32), lane);
-  return ((uint64_t)hi << 32) | lo;
-}
-
-// Two stages. (1) Each wave ranks the keys of a 64-element chunk among
-// themselves with lane reads (no memory round trips) and keeps its k best
-// as candidates at fixed places chunk*k + rank. (2) Each candidate is
-// ranked among all candidates in LDS; rank < k is the answer.
-__device__ void router_topk_row(const float* __restrict__ lg, int E, int k, int32_t* __restrict__ ids,
-                                float* __restrict__ w) {
-  __shared__ uint64_t cand[AWQ_MOE_KMAX_ROUTER_E / 64 * AWQ_MOE_KMAX_TOPK];
-  __shared__ float cand_v[AWQ_MOE_KMAX_ROUTER_E / 64 * AWQ_MOE_KMAX_TOPK];
-  __shared__ float sel_v[AWQ_MOE_KMAX_TOPK];
-  __shared__ float sel_p[AWQ_MOE_KMAX_TOPK];
-  const int t = threadIdx.x, nt = blockDim.x;
-  const int lane = t & 63, wave = t >> 6, nwaves = nt >> 6;
-  const int nchunks = (E + 63) >> 6;
-  const int ncand = nchunks * k;
-  for (int c = t; c < ncand; c += nt) cand[c] = 0;  // 0 sorts below every key
-  __syncthreads();
-  for (int chunk = wave; chunk < nchunks; chunk += nwaves) {
-    const int i = chunk * 64 + lane;
-    const float v = i < E ? lg[i] : 0.f;
-    const uint64_t key = i < E ? router_key(v, i) : 0;
-    int r = 0;
-#pragma unroll
-    for (int j = 0; j < 64; ++j) r += readlane_u64(key, j) > key;
-    if (i < E && r < k) {
-      cand[chunk * k + r] = key;
-      cand_v[chunk * k + r] = v;
-    }
-  }
-  __syncthreads();
-  for (int c = t; c < ncand; c += nt) {
-    const uint64_t kc = cand[c];
-    if (kc == 0) continue;
-    int r = 0;
-#pragma unroll 8
-    for (int j = 0; j < ncand; ++j) r += cand[j] > kc;
-    if (r < k) {
-      ids[r] = (int)(0xFFFFFFFFu - (uint32_t)kc);
-      sel_v[r] = cand_v[c];
-    }
-  }
-  __syncthreads();
-  if (t < 64) {  // one wave: LDS writes are visible to its own later reads
-    const float m = sel_v[0];
-    const float p = t < k ? expf(sel_v[t] - m) : 0.f;
-    if (t < k) sel_p[t] = p;
-    float sum = 0.f;  // in rank order
-    for (int r = 0; r < k; ++r) sum += sel_p[r];
-    if (t < k) w[t] = p / sum;
-  }
-}
-
-__global__ __launch_bounds__(1024) void router_topk_kernel(const float* __restrict__ logits, int E, int k,
-                                                           int32_t* __restrict__ ids, float* __restrict__ w) {
-  const int tok = blockIdx.x;
-  router_topk_row(logits + (uint64_t)tok * E, E, k, ids + tok * k, w + tok * k);
-}
-
-// ---------------------------------------------------------------------------
-// Residual update and parameter-free RMS norm for the layer-stack workload:
-// r_next = fp16(r + delta) (delta may be null: r_next = r), and
-// x = fp16(r_next / sqrt(mean(r_next^2) + eps)), all in fp32. One workgroup
-// per row; each thread owns runs of 8 values (16-byte loads and stores) and
-// keeps them in registers across the reduction.
-// ---------------------------------------------------------------------------
-typedef _Float16 h8_t __attribute__((ext_vector_type(8)));
-
-// One run of 8 values per thread (blockDim >= H/8, H <= 8192, H % 8 == 0).
-struct ResRow {
-  h8_t a, b;
-};
-
-// Issue the loads of row r (and delta) for this thread's run.
-__device__ __forceinline__ ResRow residual_load(const uint16_t* __restrict__ r, const uint16_t* __restrict__ delta,
-                                                int H) {
-  ResRow rr;
-  const int i = threadIdx.x;
-  if (i < (H >> 3)) {
-    rr.a = *reinterpret_cast<const h8_t*>(r + 8 * i);
-    if (delta) rr.b = *reinterpret_cast<const h8_t*>(delta + 8 * i);
-  }
-  return rr;
-}
-
-__device__ void residual_finish(const ResRow& rr, bool has_delta, int H, float eps, uint16_t* __restrict__ r_next,
-                                uint16_t* __restrict__ x) {
-  __shared__ float part[16];
-  const int t = threadIdx.x;
-  const bool on = t < (H >> 3);
-  h8_t a = rr.a;
-  float ss = 0.f;
-  if (on) {
-    if (has_delta) {
-#pragma unroll
-      for (int e = 0; e < 8; ++e) a[e] = (_Float16)((float)a[e] + (float)rr.b[e]);
-    }
-    *reinterpret_cast<h8_t*>(r_next + 8 * t) = a;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) ss = fmaf((float)a[e], (float)a[e], ss);
-  }
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) ss += __shfl_xor(ss, off);
-  if ((t & 63) == 0) part[t >> 6] = ss;
-  __syncthreads();
-  float tot = 0.f;
-  for (int i = 0; i < (int)(blockDim.x >> 6); ++i) tot += part[i];
-  const float inv = 1.0f / sqrtf(tot / (float)H + eps);
-  if (on) {
-    h8_t o;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) o[e] = (_Float16)((float)a[e] * inv);
-    *reinterpret_cast<h8_t*>(x + 8 * t) = o;
-  }
-}
-
-__global__ __launch_bounds__(1024) void residual_rmsnorm_kernel(const uint16_t* __restrict__ r,
-                                                                const uint16_t* __restrict__ delta, int H, float eps,
-                                                                uint16_t* __restrict__ r_next,
-                                                                uint16_t* __restrict__ x) {
-  const uint64_t o = (uint64_t)blockIdx.x * H;
-  const ResRow rr = residual_load(r + o, delta ? delta + o : nullptr, H);
-  residual_finish(rr, delta != nullptr, H, eps, r_next + o, x + o);
-}
-
-// Both per-token steps between two stacked layers in one launch: the
-// residual rows' loads are issued first, the router runs while they are in
-// flight, then the norm finishes.
-__global__ __launch_bounds__(1024) void router_residual_kernel(const float* __restrict__ logits, int E, int k,
-                                                               int32_t* __restrict__ ids, float* __restrict__ w,
-                                                               const uint16_t* __restrict__ r,
-                                                               const uint16_t* __restrict__ delta, int H, float eps,
-                                                               uint16_t* __restrict__ r_next,
-                                                               uint16_t* __restrict__ x) {
-  const int tok = blockIdx.x;
-  const uint64_t o = (uint64_t)tok * H;
-  const ResRow rr = residual_load(r + o, delta ? delta + o : nullptr, H);
-  router_topk_row(logits + (uint64_t)tok * E, E, k, ids + tok * k, w + tok * k);
-  residual_finish(rr, delta != nullptr, H, eps, r_next + o, x + o);
-}
-
-hipError_t launch_router_topk(const float* logits, int M, int E, int k, int32_t* ids, float* w, hipStream_t stream) {
-  // E <= 4096 over at most 1024 threads: at most 4 keys per thread
-  int threads = ((E + 63) / 64) * 64;
-  if (threads > 1024) threads = 1024;
-  hipLaunchKernelGGL(router_topk_kernel, dim3(M), dim3(threads), 0, stream, logits, E, k, ids, w);
-  return hipGetLastError();
-}
-
-hipError_t launch_residual_rmsnorm(const uint16_t* r, const uint16_t* delta, int M, int H, float eps,
-                                   uint16_t* r_next, uint16_t* x, hipStream_t stream) {
-  int threads = ((H / 8 + 63) / 64) * 64;
-  if (threads > 1024) threads = 1024;
-  hipLaunchKernelGGL(residual_rmsnorm_kernel, dim3(M), dim3(threads), 0, stream, r, delta, H, eps, r_next, x);
-  return hipGetLastError();
-}
-
-hipError_t launch_router_residual(const float* logits, int M, int E, int k, int32_t* ids, float* w,
-                                  const uint16_t* r, const uint16_t* delta, int H, float eps, uint16_t* r_next,
-                                  uint16_t* x, hipStream_t stream) {
-  int threads = ((E + 63) / 64) * 64;
-  const int rt = ((H / 8 + 63) / 64) * 64;
-  if (rt > threads) threads = rt;
-  if (threads > 1024) threads = 1024;
-  hipLaunchKernelGGL(router_residual_kernel, dim3(M), dim3(threads), 0, stream, logits, E, k, ids, w, r, delta, H,
-                     eps, r_next, x);
-  return hipGetLastError();
-}
-
 hipError_t launch_route_compact(const int32_t* ids, int n, int E, const RouteOut& o, hipStream_t stream) {
   // four lanes per slot, at least one wave
   const int threads = ((4 * n + 63) / 64) * 64;

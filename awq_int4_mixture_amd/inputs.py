@@ -205,3 +205,14 @@ def device_bank(seed: int, num_experts: int, record_sections, expert_bytes: int,
         if meta_bytes == 4:
             rec[:, :, 3] = 0
     return bank
+
+
+def device_router_weights(seed: int, num_experts: int, hidden: int, device="cuda"):
+    """Router weights for a many-layer workload, drawn on the device: fp16
+    [num_experts][hidden] with entries N(0,1) / sqrt(hidden), so that a
+    unit-RMS input row gives logits of about unit variance."""
+    import torch
+    g = torch.Generator(device=device)
+    g.manual_seed(int(seed))
+    w = torch.randn((num_experts, hidden), device=device, generator=g) / float(np.sqrt(hidden))
+    return w.to(torch.float16)

@@ -45,7 +45,7 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=200)
     p.add_argument("--warmup", type=int, default=20)
-    p.add_argument("--only", default="", help="comma list of workloads: m1_hot,m1_cold,m8_pool,m8_distinct,stack48")
+    p.add_argument("--only", default="", help="comma list of workloads: m1_hot,m1_cold,m8_pool,m8_distinct,stack48,stack48_gemv")
     p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     return p.parse_args()
 
@@ -70,17 +70,23 @@ class Workload:
         self.w2_bytes = [d * per_expert["w2"] for d in distinct]
 
 
-def measure_stack(abi, torch, steps, warmup, layers=48, M=8):
+def measure_stack(abi, torch, steps, warmup, layers=48, M=8, router="given"):
     """One decode step of a stack of 512-expert layers (3-byte records, banks
-    drawn on the device): per layer, residual update + RMS norm and router
-    top-k over fp32 N(0,1) logits (one launch), then the stage (two
-    launches). One graph replay = one step."""
+    drawn on the device). Per layer, with router="given": residual update +
+    RMS norm and router top-k over fp32 N(0,1) logits (one launch), then the
+    stage (two launches). With router="gemv": residual update + RMS norm +
+    logits = x . Wr^T from fp16 router weights N(0,1)/sqrt(H) (one launch),
+    router top-k (one launch), then the stage. One graph replay = one step."""
     dims = abi.make_dims(E, H, I, 3)
     Lq = abi.awq_moe_bank_layout_query(dims)
     sections = [(int(Lq.w13_meta_off), (H // 32) * 2 * I), (int(Lq.w2_meta_off), (I // 32) * H)]
     banks = [inputs.device_bank(SEED + 9000 + l, E, sections, int(Lq.expert_bytes), 3) for l in range(layers)]
     rng = inputs.call_rng(SEED, 900)
-    logits = [torch.from_numpy(inputs.router_logits(rng, M, E)).to("cuda") for _ in range(layers)]
+    if router == "gemv":
+        wr = [inputs.device_router_weights(SEED + 9500 + l, E, H) for l in range(layers)]
+        logits = [torch.empty((M, E), dtype=torch.float32, device="cuda") for _ in range(layers)]
+    else:
+        logits = [torch.from_numpy(inputs.router_logits(rng, M, E)).to("cuda") for _ in range(layers)]
     r0 = torch.from_numpy(inputs.activations(rng, M, H)).to("cuda")
     rbuf = [torch.empty_like(r0) for _ in range(2)]
     xbuf = torch.empty_like(r0)
@@ -93,8 +99,12 @@ def measure_stack(abi, torch, steps, warmup, layers=48, M=8):
         r = r0
         for l in range(layers):
             rn = rbuf[l % 2]
-            abi.awq_moe_router_residual(logits[l], K_TOP, r, None if l == 0 else outs[l - 1], ids=ids[l], w=wts[l],
-                                        r_next=rn, x=xbuf)
+            delta = None if l == 0 else outs[l - 1]
+            if router == "gemv":
+                abi.awq_moe_router_gemv(r, wr[l], delta, r_next=rn, x=xbuf, logits=logits[l])
+                abi.awq_moe_router_topk(logits[l], K_TOP, ids=ids[l], w=wts[l])
+            else:
+                abi.awq_moe_router_residual(logits[l], K_TOP, r, delta, ids=ids[l], w=wts[l], r_next=rn, x=xbuf)
             abi.awq_moe_decode(dims, banks[l], xbuf, ids[l], wts[l], out=outs[l], workspace=ws)
             r = rn
 
@@ -108,7 +118,11 @@ def measure_stack(abi, torch, steps, warmup, layers=48, M=8):
     out = {"layers": layers, "M": M, "step_us": ms * 1e3, "layer_us": ms * 1e3 / layers,
            "distinct_experts_per_layer": float(np.mean(distinct)), "touched_bytes_per_step": touched,
            "gbs": touched / (ms * 1e6), "pct_peak": 100.0 * touched / (ms * 1e6) / HBM_PEAK_GBS,
-           "resident_bank_bytes": int(Lq.total_bytes) * layers, "launches_per_layer": 3}
+           "resident_bank_bytes": int(Lq.total_bytes) * layers, "launches_per_layer": 4 if router == "gemv" else 3,
+           "router": router}
+    if router == "gemv":
+        out["router_weight_bytes_per_step"] = layers * E * H * 2
+        del wr
     del banks
     torch.cuda.empty_cache()
     return out
@@ -201,16 +215,23 @@ def measure(abi, torch, wl: Workload, steps, warmup):
     return res
 
 
+def stage_source_hash() -> str:
+    """sha256[:16] over the stage kernels' device sources (kernels.hip, then device_util.h)."""
+    import hashlib
+    h = hashlib.sha256()
+    for name in ("kernels.hip", "device_util.h"):
+        h.update(open(os.path.join(ROOT, "awq_int4_mixture_amd", "csrc", name), "rb").read())
+    return h.hexdigest()[:16]
+
+
 def recorded_traffic(kernel: str, summary: str = "pmc_traffic_m1_hot.txt"):
     """HBM bytes per launch of ``kernel`` from the committed rocprofv3 counter summary
     (FETCH_SIZE and WRITE_SIZE, each scaled by a 1 GiB copy in the same run), or None
     when the summary is missing or the kernel source changed since it was taken."""
-    import hashlib
     path = os.path.join(ROOT, "profiles", summary)
-    src = os.path.join(ROOT, "awq_int4_mixture_amd", "csrc", "kernels.hip")
     if not os.path.exists(path):
         return None
-    h = hashlib.sha256(open(src, "rb").read()).hexdigest()[:16]
+    h = stage_source_hash()
     for line in open(path):
         parts = [p.strip() for p in line.split("|")]
         if len(parts) == 4 and parts[0] == "TRAFFIC" and kernel in parts[1] and parts[3] == f"source {h}":
@@ -326,7 +347,8 @@ def main():
     from awq_int4_mixture_amd import abi
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     torch.cuda.set_device(0)
-    only = set(filter(None, args.only.split(","))) or {"m1_hot", "m1_cold", "m8_pool", "m8_distinct", "stack48"}
+    only = set(filter(None, args.only.split(","))) or {"m1_hot", "m1_cold", "m8_pool", "m8_distinct", "stack48",
+                                                       "stack48_gemv"}
 
     t_gen = time.perf_counter()
     bi = inputs.bank_inputs(SEED, E, H, I)
@@ -366,16 +388,20 @@ def main():
             ids = [inputs.ids_all_distinct(inputs.call_rng(SEED, 400 + c), 8, K_TOP, E) for c in range(CALLS)]
             wl = Workload("m8_distinct", abi, torch, dims, bank, ids, 8, rng, per_expert_bytes(abi, dims))
             results["m8_distinct"] = measure(abi, torch, wl, args.steps, args.warmup)
-        if "stack48" in only:
+        stack = stack_gemv = None
+        if {"stack48", "stack48_gemv"} & only:
             del banks
             torch.cuda.empty_cache()
+        if "stack48" in only:
             stack = measure_stack(abi, torch, max(args.steps // 4, 10), max(args.warmup // 4, 2))
+        if "stack48_gemv" in only:
+            stack_gemv = measure_stack(abi, torch, max(args.steps // 4, 10), max(args.warmup // 4, 2), router="gemv")
         ceiling = copy_ceiling(torch)
         read_ref = read_ceiling(torch)
         floor = launch_floor(torch)
 
     if not results:
-        print(json.dumps({"stack48": stack}), flush=True)
+        print(json.dumps({"stack48": stack, "stack48_gemv": stack_gemv}), flush=True)
         return
     head = results.get("m1_hot") or next(iter(results.values()))
     line = {
@@ -400,7 +426,8 @@ def main():
         "roofline": roofline(head),
         "per_config": {k: {kk: (round(vv, 4) if isinstance(vv, float) else vv) for kk, vv in v.items()}
                        for k, v in results.items()},
-        "stack48": stack if "stack48" in only else None,
+        "stack48": stack,
+        "stack48_gemv": stack_gemv,
         "copy_reference": ceiling,
         "read_reference": read_ref,
         "launch_floor": floor,

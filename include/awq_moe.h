@@ -214,6 +214,18 @@ int awq_moe_router_residual(const float* logits, int32_t M, int32_t num_experts,
                             const uint16_t* delta, int32_t hidden, float eps, uint16_t* r_next,
                             uint16_t* x, void* stream);
 
+/* Router GEMV between stacked layers (the router is not on the pages; fork PR
+ * #12, Purpose and stack, leaves it unchanged): the residual step of
+ * awq_moe_residual_rmsnorm (r_next, x, same arguments and rules), then
+ *   logits[t][e] = sum_k x[t][k] * router_w[e][k]   (fp16 products, fp32 sums)
+ * router_w: device fp16 [num_experts][hidden] (expert-major), 16-byte aligned;
+ * logits: device fp32 [M][num_experts]. r_next and x are bit-identical to
+ * awq_moe_residual_rmsnorm's. One launch; awq_moe_router_topk on logits then
+ * gives the routing. */
+int awq_moe_router_gemv(const uint16_t* r, const uint16_t* delta, int32_t M, int32_t hidden, float eps,
+                        const uint16_t* router_w, int32_t num_experts, uint16_t* r_next, uint16_t* x,
+                        float* logits, void* stream);
+
 /* Dequantise experts [expert_begin, expert_begin + expert_count) of the bank
  * into fp32 (diagnostic). Each value s * (q - z) is exact in fp32: q - z is an
  * integer in [-255, 15] and s an fp16, so the product needs at most 19

@@ -164,6 +164,10 @@ def test_device_calls_reject_bad_arguments_before_launch():
         (lambda: lib.awq_moe_router_residual(p, 1, 512, 33, p, p, p, None, 256, 1e-6, q1, q2, None), abi.EINVAL),
         (lambda: lib.awq_moe_router_residual(p, 1, 512, 10, p, p, p, None, 256, 1e-6, p, q2, None), abi.EINVAL),
         (lambda: lib.awq_moe_router_residual(p, 9, 512, 10, p, p, p, None, 256, 1e-6, q1, q2, None), abi.EINVAL),
+        (lambda: lib.awq_moe_router_gemv(p, None, 9, 256, 1e-6, p, 512, q1, q2, p, None), abi.EINVAL),
+        (lambda: lib.awq_moe_router_gemv(p, None, 1, 256, 1e-6, None, 512, q1, q2, p, None), abi.EINVAL),
+        (lambda: lib.awq_moe_router_gemv(p, None, 1, 256, 1e-6, p, 0, q1, q2, p, None), abi.EINVAL),
+        (lambda: lib.awq_moe_router_gemv(p, None, 1, 256, 1e-6, p, 512, q1, q2, None, None), abi.EINVAL),
     ]
     for i, (call, code) in enumerate(cases):
         assert call() == code, (i, abi.awq_moe_last_error())

@@ -295,6 +295,30 @@ def test_invariants_bit_exact():
     assert not (z2.astype(np.float64) != 0).any()
 
 
+def test_linearity_in_router_weights_and_duplicate_merging():
+    """out(w_a + w_b) ~ out(w_a) + out(w_b) within the gate, and a token that
+    lists one expert twice, (e, w1) and (e, w2), matches (e, w1 + w2)."""
+    H, I = RANK
+    dims, bank, bi = bank_case(7, 64, H, I, 3)
+    rng = inputs.call_rng(13, 0)
+    M, k = 3, 10
+    x = inputs.activations(rng, M, H)
+    ids = inputs.ids_distinct(rng, M, k, 64)
+    wa = inputs.router_weights(rng, M, k)
+    wb = inputs.router_weights(rng, M, k)
+    sum_out = run_decode(dims, bank, x, ids, (wa + wb).astype(np.float32))
+    parts = run_decode(dims, bank, x, ids, wa).astype(np.float64) + run_decode(dims, bank, x, ids, wb)
+    check(sum_out, parts, "linearity in w")
+    dup = ids.copy()
+    dup[:, 1] = dup[:, 0]                     # expert of slot 0 listed twice
+    wd = wa.copy()
+    merged = wa.copy()
+    merged[:, 0] = wa[:, 0] + wa[:, 1]
+    merged[:, 1] = 0.0                        # the second listing carries no weight
+    check(run_decode(dims, bank, x, dup, wd), run_decode(dims, bank, x, dup, merged).astype(np.float64),
+          "duplicate merging")
+
+
 def test_batch_independence_within_tolerance():
     """A token alone and inside a batch: the pages record cross-batch sensitivity
     as a known property (PR #520, Precision); here report bit-equality and gate

@@ -97,6 +97,37 @@ def test_router_residual_equals_the_two_calls(E, H, k):
                            b.view(torch.uint8) if b.dtype != torch.int32 else b)
 
 
+@pytest.mark.parametrize("M,H,E", [(8, 2560, 512), (3, 256, 64), (1, 4096, 130), (5, 8192, 37), (2, 6144, 9),
+                                   (7, 560, 513)])
+def test_router_gemv(M, H, E):
+    """The residual step bit-identical to awq_moe_residual_rmsnorm; logits
+    against float64 x . W^T on the GPU's own x. The fp32 sums form a tree of
+    depth well under 100 (a chain over each thread's runs, then lane and wave
+    sums), so |err| <= gamma_100 * sum |x w| < 1e-5 * sum |x w| (Higham's
+    bound for a summation tree; fp16 products are exact in fp32). The top-k
+    of the GPU's logits equals the oracle's top-k of them."""
+    rng = inputs.call_rng(505, M * H + E)
+    r = to_dev((rng.standard_normal((M, H)) * 2).astype(np.float16))
+    d = to_dev(rng.standard_normal((M, H)).astype(np.float16))
+    wr_np = (rng.standard_normal((E, H)) / np.sqrt(H)).astype(np.float16)
+    rn, x, logits = abi.awq_moe_router_gemv(r, to_dev(wr_np), d)
+    rn1, x1 = abi.awq_moe_residual_rmsnorm(r, d)
+    torch.cuda.synchronize()
+    assert torch.equal(rn.view(torch.int16), rn1.view(torch.int16)) and torch.equal(x.view(torch.int16), x1.view(torch.int16))
+    x64 = f16_to_np(x).astype(np.float64)
+    w64 = wr_np.astype(np.float64)
+    want = x64 @ w64.T
+    mag = np.abs(x64) @ np.abs(w64).T
+    got = logits.cpu().numpy().astype(np.float64)
+    assert np.all(np.abs(got - want) <= 1e-5 * mag + 1e-30), np.max(np.abs(got - want) / mag)
+    k = min(10, E)
+    ids, w = abi.awq_moe_router_topk(logits, k)
+    torch.cuda.synchronize()
+    want_ids, want_w = R.topk_softmax(logits.cpu().numpy(), k)
+    np.testing.assert_array_equal(ids.cpu().numpy(), want_ids)
+    np.testing.assert_allclose(w.cpu().numpy().astype(np.float64), want_w, rtol=1e-5, atol=1e-7)
+
+
 def experts_from_bank(d, bank_np):
     """weights_of(e) for the oracle, decoded by the oracle from the bank bytes."""
     cache = {}
