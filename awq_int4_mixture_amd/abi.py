@@ -28,7 +28,7 @@ EXPORTED = (
     "awq_moe_bank_layout_query", "awq_moe_prepare", "awq_moe_workspace_bytes",
     "awq_moe_route_compact", "awq_moe_decode", "awq_moe_w13_swiglu", "awq_moe_w2_reduce",
     "awq_moe_dequant", "awq_moe_router_topk", "awq_moe_residual_rmsnorm", "awq_moe_router_residual",
-    "awq_moe_router_gemv", "awq_moe_last_error",
+    "awq_moe_router_gemv", "awq_moe_prefill_workspace_bytes", "awq_moe_prefill", "awq_moe_last_error",
 )
 
 
@@ -69,6 +69,8 @@ def _load() -> ctypes.CDLL:
         "awq_moe_workspace_bytes": [D, I32, I32, ctypes.POINTER(ctypes.c_uint64)],
         "awq_moe_route_compact": [P, I32, I32, I32, P, P, P, P, P, V],
         "awq_moe_decode": [D, P, P, P, P, I32, I32, P, P, U64, V],
+        "awq_moe_prefill_workspace_bytes": [D, I32, I32, ctypes.POINTER(ctypes.c_uint64)],
+        "awq_moe_prefill": [D, P, P, P, P, I32, I32, P, P, U64, V],
         "awq_moe_w13_swiglu": [D, P, P, P, I32, I32, P, U64, V],
         "awq_moe_w2_reduce": [D, P, P, P, I32, I32, P, U64, P, V],
         "awq_moe_dequant": [D, P, I32, I32, I32, P, V],
@@ -222,6 +224,36 @@ def awq_moe_decode(dims: awq_moe_dims, bank, x, topk_ids, topk_w, out=None, work
         _dev(topk_ids, torch.int32, (M, k), "topk_ids"), _dev(topk_w, torch.float32, (M, k), "topk_w"), M, k,
         _dev(out, torch.float16, (M, dims.hidden), "out"), _dev(workspace, torch.uint8, name="workspace"),
         workspace.numel(), _stream(stream)), "awq_moe_decode")
+    return out
+
+
+def awq_moe_prefill_workspace_bytes(dims: awq_moe_dims, max_tokens: int, topk: int) -> int:
+    out = ctypes.c_uint64()
+    _check(_lib.awq_moe_prefill_workspace_bytes(ctypes.byref(dims), max_tokens, topk, ctypes.byref(out)),
+           "awq_moe_prefill_workspace_bytes")
+    return out.value
+
+
+def alloc_prefill_workspace(dims: awq_moe_dims, max_tokens: int, topk: int, device="cuda"):
+    """An indexed-prefill workspace (needs no initialisation)."""
+    torch = _torch()
+    return torch.empty(awq_moe_prefill_workspace_bytes(dims, max_tokens, topk), dtype=torch.uint8, device=device)
+
+
+def awq_moe_prefill(dims: awq_moe_dims, bank, x, topk_ids, topk_w, out=None, workspace=None, stream=None):
+    """The stage for M in [9, 4096] tokens (expert-major, matrix cores)."""
+    torch = _torch()
+    M, H = x.shape
+    k = topk_ids.shape[1]
+    if out is None:
+        out = torch.empty((M, H), dtype=torch.float16, device=x.device)
+    if workspace is None:
+        workspace = alloc_prefill_workspace(dims, M, k, x.device)
+    _check(_lib.awq_moe_prefill(
+        ctypes.byref(dims), _dev(bank, torch.uint8, name="bank"), _dev(x, torch.float16, (M, dims.hidden), "x"),
+        _dev(topk_ids, torch.int32, (M, k), "topk_ids"), _dev(topk_w, torch.float32, (M, k), "topk_w"), M, k,
+        _dev(out, torch.float16, (M, dims.hidden), "out"), _dev(workspace, torch.uint8, name="workspace"),
+        workspace.numel(), _stream(stream)), "awq_moe_prefill")
     return out
 
 

@@ -28,7 +28,7 @@ COMMON = [
     "-mllvm", "-amdgpu-kernarg-preload-count=16",
     f"-I{INCLUDE}", f"-I{CSRC}",
 ]
-SOURCES = ["kernels.hip", "router.hip", "awq_moe_host.cpp"]
+SOURCES = ["kernels.hip", "router.hip", "prefill.hip", "awq_moe_host.cpp"]
 
 
 def _hipcc() -> str:

@@ -396,6 +396,84 @@ int awq_moe_w2_reduce(const awq_moe_dims* dims, const void* bank, const int32_t*
                     "w2 launch");
 }
 
+namespace {
+
+struct PrefillLayout {
+  uint64_t slot_row, row_slot, items, act, y, total;
+};
+
+PrefillLayout prefill_layout(const awq_moe_dims* d, int M, int topk) {
+  const uint64_t n = (uint64_t)M * (uint64_t)topk;
+  const uint64_t mi = (uint64_t)awq_moe::prefill_max_items((int)n, d->num_experts);
+  PrefillLayout L;
+  uint64_t off = 256;  // status u32 at 0, num_items i32 at 4
+  L.slot_row = off;
+  off += pad256(n * 4);
+  L.row_slot = off;
+  off += pad256(n * 4);
+  L.items = off;
+  off += pad256(mi * 8);
+  L.act = off;
+  off += pad256(n * (uint64_t)d->inter * 2);
+  L.y = off;
+  off += pad256(n * (uint64_t)d->hidden * 4);
+  L.total = off;
+  return L;
+}
+
+int check_prefill_shape(const awq_moe_dims* dims, int M, int topk) {
+  int rc = check_dims(dims);
+  if (rc) return rc;
+  if (dims->num_experts > AWQ_MOE_PREFILL_MAX_EXPERTS)
+    return fail(AWQ_MOE_EUNSUPPORTED, "num_experts %d > %d for prefill", dims->num_experts,
+                AWQ_MOE_PREFILL_MAX_EXPERTS);
+  if (M < AWQ_MOE_PREFILL_MIN_TOKENS || M > AWQ_MOE_PREFILL_MAX_TOKENS)
+    return fail(AWQ_MOE_EINVAL, "M %d outside [%d, %d] (1..8 tokens go to awq_moe_decode)", M,
+                AWQ_MOE_PREFILL_MIN_TOKENS, AWQ_MOE_PREFILL_MAX_TOKENS);
+  if (topk < 1 || topk > AWQ_MOE_MAX_TOPK) return fail(AWQ_MOE_EINVAL, "topk %d outside [1, %d]", topk, AWQ_MOE_MAX_TOPK);
+  return AWQ_MOE_OK;
+}
+
+}  // namespace
+
+int awq_moe_prefill_workspace_bytes(const awq_moe_dims* dims, int32_t max_tokens, int32_t topk, uint64_t* out) {
+  int rc = check_prefill_shape(dims, max_tokens, topk);
+  if (rc) return rc;
+  if (!out) return fail(AWQ_MOE_EINVAL, "out is null");
+  *out = prefill_layout(dims, max_tokens, topk).total;
+  return ok();
+}
+
+int awq_moe_prefill(const awq_moe_dims* dims, const void* bank, const uint16_t* x, const int32_t* topk_ids,
+                    const float* topk_w, int32_t M, int32_t topk, uint16_t* out, void* workspace,
+                    uint64_t workspace_bytes, void* stream) {
+  int rc = check_prefill_shape(dims, M, topk);
+  if (rc) return rc;
+  if (!bank || !aligned(bank, 256)) return fail(AWQ_MOE_EINVAL, "bank null or not 256-byte aligned");
+  if (!workspace || !aligned(workspace, 256)) return fail(AWQ_MOE_EINVAL, "workspace null or not 256-byte aligned");
+  const PrefillLayout L = prefill_layout(dims, M, topk);
+  if (workspace_bytes < L.total)
+    return fail(AWQ_MOE_ENOSPC, "workspace_bytes %llu < %llu", (unsigned long long)workspace_bytes,
+                (unsigned long long)L.total);
+  if (!x || !aligned(x, 16)) return fail(AWQ_MOE_EINVAL, "x null or not 16-byte aligned");
+  if (!topk_ids || !aligned(topk_ids, 4)) return fail(AWQ_MOE_EINVAL, "topk_ids null or misaligned");
+  if (!topk_w || !aligned(topk_w, 4)) return fail(AWQ_MOE_EINVAL, "topk_w null or misaligned");
+  if (!out || !aligned(out, 16)) return fail(AWQ_MOE_EINVAL, "out null or not 16-byte aligned");
+  if ((rc = check_device())) return rc;
+  uint8_t* ws = static_cast<uint8_t*>(workspace);
+  awq_moe::PrefillWs w;
+  w.status = reinterpret_cast<uint32_t*>(ws);
+  w.num_items = reinterpret_cast<int32_t*>(ws + 4);
+  w.slot_row = reinterpret_cast<int32_t*>(ws + L.slot_row);
+  w.row_slot = reinterpret_cast<int32_t*>(ws + L.row_slot);
+  w.items = reinterpret_cast<int32_t*>(ws + L.items);
+  w.act = reinterpret_cast<uint16_t*>(ws + L.act);
+  w.y = reinterpret_cast<float*>(ws + L.y);
+  return hip_status(awq_moe::launch_prefill(stage_args(dims, bank, topk_ids, M, topk), x, topk_w, out, w,
+                                            static_cast<hipStream_t>(stream)),
+                    "prefill launch");
+}
+
 int awq_moe_decode(const awq_moe_dims* dims, const void* bank, const uint16_t* x, const int32_t* topk_ids,
                    const float* topk_w, int32_t M, int32_t topk, uint16_t* out, void* workspace,
                    uint64_t workspace_bytes, void* stream) {

@@ -49,6 +49,20 @@ hipError_t launch_router_residual(const float* logits, int M, int E, int k, int3
 // (wr fp16 [E][H]).
 hipError_t launch_router_gemv(const uint16_t* r, const uint16_t* delta, int M, int H, float eps, const uint16_t* wr,
                               int E, uint16_t* r_next, uint16_t* x, float* logits, hipStream_t stream);
+// Indexed prefill workspace (all device pointers inside the caller's workspace).
+struct PrefillWs {
+  uint32_t* status;
+  int32_t* num_items;
+  int32_t* slot_row;  // [n] row of each slot, -1 for an invalid id
+  int32_t* row_slot;  // [n] slot of each row
+  int32_t* items;     // [max_items][2] {expert, row0 | rows << 24}
+  uint16_t* act;      // fp16 [n][I] by row
+  float* y;           // fp32 [n][H] by row
+};
+// Upper bound on the number of work items (expert row chunks of 32) for n slots.
+int prefill_max_items(int n, int E);
+hipError_t launch_prefill(const StageArgs& a, const uint16_t* x, const float* topk_w, uint16_t* out,
+                          const PrefillWs& w, hipStream_t stream);
 hipError_t launch_dequant(const uint8_t* bank, uint64_t expert_bytes, uint64_t units_off,
                           uint64_t meta_off, int RB, int which, int H, int I, int expert_begin,
                           int expert_count, float* out, hipStream_t stream);

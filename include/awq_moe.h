@@ -72,6 +72,9 @@ extern "C" {
 #define AWQ_MOE_MAX_INTER 2048
 #define AWQ_MOE_MAX_ROUTER_EXPERTS 4096
 #define AWQ_MOE_STATUS_BAD_ID 1u
+#define AWQ_MOE_PREFILL_MIN_TOKENS 9      /* indexed prefill tokens per call, M in [9, 4096] */
+#define AWQ_MOE_PREFILL_MAX_TOKENS 4096
+#define AWQ_MOE_PREFILL_MAX_EXPERTS 4096
 
 typedef struct awq_moe_dims {
   int32_t num_experts; /* E >= 1 */
@@ -225,6 +228,34 @@ int awq_moe_router_residual(const float* logits, int32_t M, int32_t num_experts,
 int awq_moe_router_gemv(const uint16_t* r, const uint16_t* delta, int32_t M, int32_t hidden, float eps,
                         const uint16_t* router_w, int32_t num_experts, uint16_t* r_next, uint16_t* x,
                         float* logits, void* stream);
+
+/* Indexed prefill: the same stage as awq_moe_decode (route, W13 + SwiGLU, W2,
+ * router-weighted reduction; every reading of the decode stage holds) for
+ * M in [9, 4096] tokens. PR #520 "[Perf][SM70] Narrow Qwen3.8 AWQ active
+ * grouped decode", Tests: indexed prefill and grouped decode have disjoint
+ * admission (boundary cases 8 and 9 tokens), so M <= 8 is EINVAL here and
+ * M >= 9 is EINVAL in awq_moe_decode.
+ *
+ * Work is expert-major: each distinct expert's weights are read once per
+ * call and applied to all of its rows with matrix-core products, the
+ * dequantised weight kept exact as the integer (q - z) and the group scale
+ * applied to the fp32 group result. Row results go to an fp32 workspace and
+ * each token's rows are summed in ascending (expert id, slot) order, so the
+ * output is deterministic, bit-invariant to permuting a token's (id, weight)
+ * pairs, and independent of which other tokens share the call.
+ *
+ * Arguments as in awq_moe_decode, with num_experts <= 4096 and
+ * workspace_bytes >= awq_moe_prefill_workspace_bytes(dims, M, topk).
+ * Workspace layout (all offsets 256-aligned): status u32 at 0 (bit 0: an id
+ * outside [0, E); its slot contributes 0), then slot -> row, row -> slot,
+ * work items, fp16 act [M*topk][inter] and fp32 y [M*topk][hidden]. The
+ * workspace needs no initialisation. Four launches on `stream`; nothing is
+ * allocated and nothing synchronises, so the call can be captured in a HIP
+ * graph. Calls that share a workspace must not overlap. */
+int awq_moe_prefill_workspace_bytes(const awq_moe_dims* dims, int32_t max_tokens, int32_t topk, uint64_t* out);
+int awq_moe_prefill(const awq_moe_dims* dims, const void* bank, const uint16_t* x, const int32_t* topk_ids,
+                    const float* topk_w, int32_t M, int32_t topk, uint16_t* out, void* workspace,
+                    uint64_t workspace_bytes, void* stream);
 
 /* Dequantise experts [expert_begin, expert_begin + expert_count) of the bank
  * into fp32 (diagnostic). Each value s * (q - z) is exact in fp32: q - z is an

@@ -125,6 +125,8 @@ def test_device_calls_reject_bad_arguments_before_launch():
     q1 = ctypes.c_void_p(base + 1024)       # two disjoint 1 KiB row buffers
     q2 = ctypes.c_void_p(base + 2048)
     ws_need = abi.awq_moe_workspace_bytes(d, 1, 10)
+    pws_need = abi.awq_moe_prefill_workspace_bytes(d, 9, 10)
+    d_big = abi.make_dims(4097, 256, 32, 3)
     cases = [
         (lambda: lib.awq_moe_decode(ctypes.byref(d), p, p, p, p, 9, 10, p, p, ws_need, None), abi.EINVAL),
         (lambda: lib.awq_moe_decode(ctypes.byref(d), p, p, p, p, 1, 10, p, p, ws_need - 1, None), abi.ENOSPC),
@@ -168,6 +170,19 @@ def test_device_calls_reject_bad_arguments_before_launch():
         (lambda: lib.awq_moe_router_gemv(p, None, 1, 256, 1e-6, None, 512, q1, q2, p, None), abi.EINVAL),
         (lambda: lib.awq_moe_router_gemv(p, None, 1, 256, 1e-6, p, 0, q1, q2, p, None), abi.EINVAL),
         (lambda: lib.awq_moe_router_gemv(p, None, 1, 256, 1e-6, p, 512, q1, q2, None, None), abi.EINVAL),
+        (lambda: lib.awq_moe_prefill(ctypes.byref(d), p, p, p, p, 8, 10, p, p, pws_need, None), abi.EINVAL),
+        (lambda: lib.awq_moe_prefill(ctypes.byref(d), p, p, p, p, 4097, 10, p, p, 1 << 62, None), abi.EINVAL),
+        (lambda: lib.awq_moe_prefill(ctypes.byref(d), p, p, p, p, 9, 33, p, p, 1 << 62, None), abi.EINVAL),
+        (lambda: lib.awq_moe_prefill(ctypes.byref(d), p, p, p, p, 9, 10, p, p, pws_need - 1, None), abi.ENOSPC),
+        (lambda: lib.awq_moe_prefill(ctypes.byref(d), mis, p, p, p, 9, 10, p, p, pws_need, None), abi.EINVAL),
+        (lambda: lib.awq_moe_prefill(ctypes.byref(d), p, mis, p, p, 9, 10, p, p, pws_need, None), abi.EINVAL),
+        (lambda: lib.awq_moe_prefill(ctypes.byref(d), p, p, None, p, 9, 10, p, p, pws_need, None), abi.EINVAL),
+        (lambda: lib.awq_moe_prefill(ctypes.byref(d), p, p, p, None, 9, 10, p, p, pws_need, None), abi.EINVAL),
+        (lambda: lib.awq_moe_prefill(ctypes.byref(d), p, p, p, p, 9, 10, mis, p, pws_need, None), abi.EINVAL),
+        (lambda: lib.awq_moe_prefill(ctypes.byref(d), p, p, p, p, 9, 10, p, mis, pws_need, None), abi.EINVAL),
+        (lambda: lib.awq_moe_prefill(ctypes.byref(d_big), p, p, p, p, 9, 10, p, p, 1 << 62, None),
+         abi.EUNSUPPORTED),
+        (lambda: lib.awq_moe_prefill(None, p, p, p, p, 9, 10, p, p, pws_need, None), abi.EINVAL),
     ]
     for i, (call, code) in enumerate(cases):
         assert call() == code, (i, abi.awq_moe_last_error())
@@ -180,3 +195,19 @@ def test_workspace_grows_with_tokens():
     sizes = [abi.awq_moe_workspace_bytes(d, M, 10) for M in range(1, 9)]
     assert all(b > a for a, b in zip(sizes, sizes[1:]))
     assert sizes[-1] >= 80 * 160 * 2
+
+
+def test_prefill_workspace_bounds():
+    """The prefill workspace holds the row maps, the work items, fp16 act and
+    fp32 y for every slot; admission is M in [9, 4096] (1..8 go to decode)."""
+    d = abi.make_dims(512, 2560, 160, 3)
+    for M in (9, 128, 4096):
+        n = M * 10
+        need = abi.awq_moe_prefill_workspace_bytes(d, M, 10)
+        assert need >= 256 + 8 * n + n * 160 * 2 + n * 2560 * 4
+        assert need % 256 == 0
+    for M in (8, 4097):
+        with pytest.raises(abi.AwqMoeError):
+            abi.awq_moe_prefill_workspace_bytes(d, M, 10)
+    with pytest.raises(abi.AwqMoeError):
+        abi.awq_moe_workspace_bytes(d, 9, 10)

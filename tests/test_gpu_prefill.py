@@ -1,0 +1,168 @@
+"""GPU parity of the indexed prefill stage (M >= 9 tokens) against the
+float64 oracle, through the C ABI, plus its bit-exact invariants.
+
+The oracle is the same whole-stage definition as for decode (PR #520,
+Tests: indexed prefill serves the token counts above the grouped decode's
+1..8); the gates are max|gpu - ref| <= 4e-3 max|ref| and
+||gpu - ref|| / ||ref|| <= 2e-3.
+"""
+
+import numpy as np
+import pytest
+
+from awq_int4_mixture_amd import inputs
+from oracle import ref as R
+from tests.gpu_helpers import bank_case, f16_to_np, say, to_dev, torch_mod
+
+pytestmark = pytest.mark.gpu
+
+torch = torch_mod()
+if not torch.cuda.is_available():
+    pytest.skip("no GPU", allow_module_level=True)
+
+from awq_int4_mixture_amd import abi  # noqa: E402  (fails loudly when the library is missing)
+
+
+def run_prefill(dims, bank, x, ids, w, workspace=None):
+    out = abi.awq_moe_prefill(dims, bank, to_dev(x), to_dev(ids), to_dev(w), workspace=workspace)
+    torch.cuda.synchronize()
+    return f16_to_np(out)
+
+
+def check(got, want, what):
+    ok, e = R.within_gate(got, want)
+    say(what, e)
+    assert ok, (what, e)
+    return e
+
+
+@pytest.mark.parametrize("E,H,I,k,M,rb", [
+    (16, 256, 32, 2, 9, 3),        # the admission boundary, tiny shape
+    (16, 256, 32, 4, 128, 4),      # 32 rows per expert on average: several items, two 16-row tiles
+    (6, 96, 64, 3, 17, 3),         # hidden 96: 6 W2 column tiles in one block; 3 W13 groups for 4 waves
+    (16, 512, 2048, 10, 40, 3),    # inter 2048: 256 W13 column tiles, 64 W2 groups
+    (12, 128, 96, 1, 33, 4),       # top-k 1
+    (64, 2560, 160, 10, 127, 3),   # rank shape with 64 experts, ~20 rows each
+    (4, 8192, 32, 2, 9, 3),        # hidden 8192: 256 W13 groups, 64 per wave
+    (16, 256, 32, 2, 4096, 3),     # the largest M: 8192 slots, ~512 rows per expert
+])
+def test_prefill_shapes(E, H, I, k, M, rb):
+    dims, bank, bi = bank_case(60 + I, E, H, I, rb)
+    rng = inputs.call_rng(61, M + H + k)
+    x = inputs.activations(rng, M, H)
+    ids = inputs.ids_distinct(rng, M, k, E)
+    w = inputs.router_weights(rng, M, k)
+    say("prefill shape", E, H, I, k, M, rb)
+    check(run_prefill(dims, bank, x, ids, w), R.moe_stage(x, ids, w, E, bi.expert),
+          f"prefill E={E} H={H} I={I} k={k} M={M} rb={rb}")
+
+
+@pytest.mark.parametrize("rb", [3, 4])
+@pytest.mark.parametrize("M", [9, 128])
+def test_prefill_rank_shape_full_bank(rb, M):
+    """The decode benchmark's layer (512 experts, hidden 2560, inter 160,
+    top-k 10) with M tokens that pick their experts independently."""
+    H, I = 2560, 160
+    dims, bank, bi = bank_case(2026, 512, H, I, rb)
+    rng = inputs.call_rng(2027, M)
+    x = inputs.activations(rng, M, H)
+    ids = inputs.ids_distinct(rng, M, 10, 512)
+    w = inputs.router_weights(rng, M, 10)
+    say("prefill rank", M, rb)
+    check(run_prefill(dims, bank, x, ids, w), R.moe_stage(x, ids, w, 512, bi.expert), f"prefill rank M={M} rb={rb}")
+
+
+def test_prefill_invalid_and_duplicate_ids():
+    """Ids outside [0, E) set status bit 0 and contribute nothing; a token
+    may route to one expert twice (two rows); a token with no valid id gives
+    an all-zero row."""
+    E, H, I, k, M = 16, 256, 32, 4, 20
+    dims, bank, bi = bank_case(62, E, H, I, 3)
+    rng = inputs.call_rng(63, 0)
+    x = inputs.activations(rng, M, H)
+    ids = inputs.ids_distinct(rng, M, k, E)
+    ids[2, 1] = -1
+    ids[5, 3] = E
+    ids[7, :] = [3, 3, 9, 3]
+    ids[11, :] = -5
+    w = inputs.router_weights(rng, M, k)
+    ws = abi.alloc_prefill_workspace(dims, M, k)
+    got = run_prefill(dims, bank, x, ids, w, workspace=ws)
+    assert int(ws[:4].view(torch.int32).cpu()[0]) & 1 == 1
+    assert not got[11].any()
+    check(got, R.moe_stage(x, ids, w, E, bi.expert), "prefill invalid/duplicate ids")
+    ok_ids = inputs.ids_distinct(rng, M, k, E)
+    run_prefill(dims, bank, x, ok_ids, w, workspace=ws)
+    assert int(ws[:4].view(torch.int32).cpu()[0]) == 0
+
+
+def test_prefill_bit_exact_invariants():
+    """Each token's result depends only on its own (id, weight) pairs: two
+    calls give identical bytes; permuting a token's pairs gives identical
+    bytes (ascending (expert, slot) summation); a token gives identical bytes
+    inside a 9-token call and inside a 40-token call with other tokens
+    (a row's matrix-core result does not depend on the rows sharing its
+    tile); router weights scaled by 2 give exactly twice the output."""
+    E, H, I, k = 24, 512, 64, 6
+    dims, bank, bi = bank_case(64, E, H, I, 3)
+    rng = inputs.call_rng(65, 0)
+    M = 40
+    x = inputs.activations(rng, M, H)
+    ids = inputs.ids_shared_pool(rng, M, k, E, frac=0.3)
+    w = inputs.router_weights(rng, M, k)
+    a = run_prefill(dims, bank, x, ids, w)
+    b = run_prefill(dims, bank, x, ids, w)
+    assert a.tobytes() == b.tobytes()
+    perm = np.stack([rng.permutation(k) for _ in range(M)])
+    ids_p = np.take_along_axis(ids, perm, 1)
+    w_p = np.take_along_axis(w, perm, 1)
+    c = run_prefill(dims, bank, x, ids_p, w_p)
+    assert a.tobytes() == c.tobytes()
+    sub = run_prefill(dims, bank, x[:9], ids[:9], w[:9])
+    assert sub.tobytes() == a[:9].tobytes()
+    d = run_prefill(dims, bank, x, ids, (w * 2).astype(np.float32))
+    mag = np.abs(a.astype(np.float64))
+    normal = (mag >= 2.0 ** -14) & (mag < 3e4)  # doubling is exact there, subnormals excluded
+    assert np.array_equal(d[normal].astype(np.float64), 2.0 * a[normal].astype(np.float64))
+    check(a, R.moe_stage(x, ids, w, E, bi.expert), "prefill invariants case")
+
+
+def test_prefill_close_to_decode():
+    """The prefill and decode paths compute the same stage: 16 tokens in one
+    prefill call against two 8-token decode calls, within the gate."""
+    H, I = 2560, 160
+    dims, bank, bi = bank_case(7, 128, H, I, 3)
+    rng = inputs.call_rng(66, 0)
+    x = inputs.activations(rng, 16, H)
+    ids = inputs.ids_shared_pool(rng, 16, 10, 128)
+    w = inputs.router_weights(rng, 16, 10)
+    p = run_prefill(dims, bank, x, ids, w)
+    d = np.concatenate([f16_to_np(abi.awq_moe_decode(dims, bank, to_dev(x[h:h + 8]), to_dev(ids[h:h + 8]),
+                                                     to_dev(w[h:h + 8]))) for h in (0, 8)])
+    torch.cuda.synchronize()
+    check(p, d.astype(np.float64), "prefill vs decode")
+
+
+def test_prefill_graph_capture_replays_match_eager():
+    E, H, I, k, M = 32, 256, 64, 4, 64
+    dims, bank, bi = bank_case(67, E, H, I, 4)
+    rng = inputs.call_rng(68, 0)
+    x = to_dev(inputs.activations(rng, M, H))
+    ids = to_dev(inputs.ids_distinct(rng, M, k, E))
+    w = to_dev(inputs.router_weights(rng, M, k))
+    ws = abi.alloc_prefill_workspace(dims, M, k)
+    out = torch.empty((M, H), dtype=torch.float16, device="cuda")
+    abi.awq_moe_prefill(dims, bank, x, ids, w, out=out, workspace=ws)
+    torch.cuda.synchronize()
+    eager = out.clone()
+    s = torch.cuda.Stream()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(g, stream=s):
+            abi.awq_moe_prefill(dims, bank, x, ids, w, out=out, workspace=ws)
+    for _ in range(3):
+        out.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out.view(torch.int16), eager.view(torch.int16))
