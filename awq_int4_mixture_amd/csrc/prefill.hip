@@ -122,28 +122,27 @@ __global__ __launch_bounds__(1024) void prefill_route_kernel(const int32_t* __re
 // group) for B, and row l % 16 with the same K block for A; the result
 // holds rows 4kb .. 4kb + 3 of column c.
 // ---------------------------------------------------------------------------
-template <int RB>
-__device__ __forceinline__ uint32_t load_record1(const uint8_t* p) {
-  if constexpr (RB == 4) {
-    return *reinterpret_cast<const uint32_t*>(p);
-  } else {
-    return (uint32_t)p[0] | ((uint32_t)p[1] << 8) | ((uint32_t)p[2] << 16);
-  }
+// Eight (q - z) values in fp16 from one dword of a unit (value p of the dword
+// at bits 4*(p/2) + 16*(p%2)) and the record's zero point. Each pair of
+// nibbles is shifted to bits 0..3 and 16..19 and OR-ed into the mantissas of
+// a packed 1024.0 (exponent pattern m1024, kept in a VGPR so the mask and
+// the OR are one v_and_or_b32), giving 1024 + q exactly; adding the packed
+// fp16 -(1024 + z), whose bit pattern is 0xE400 + z for z <= 255, leaves
+// q - z exactly (an integer of magnitude <= 255).
+__device__ __forceinline__ uint32_t magic1024() {
+  uint32_t m;
+  asm volatile("v_mov_b32 %0, 0x64006400" : "=v"(m));
+  return m;
 }
 
-// Eight (q - z) values in fp16 from one dword of a unit (value p of the dword
-// at bits 4*(p/2) + 16*(p%2)) and the record's zero point. The nibbles become
-// 1024 + q or 64 + q by OR-ing them into those numbers' mantissas; subtracting
-// 1024 + z or 64 + z (integers below 2048, exact in fp16) leaves q - z exactly.
-__device__ __forceinline__ h8_t qz_operand(uint32_t w, uint32_t z) {
-  const _Float16 z1024 = (_Float16)(-(1024.0f + (float)z));
-  const _Float16 z64 = (_Float16)(-(64.0f + (float)z));
-  const h2_t c1024 = {z1024, z1024}, c64 = {z64, z64};
-  const h2_t p0 = as_h2((w & 0x000F000Fu) | 0x64006400u) + c1024;
-  const h2_t p1 = as_h2((w & 0x00F000F0u) | 0x54005400u) + c64;
-  const h2_t p2 = as_h2(((w >> 8) & 0x000F000Fu) | 0x64006400u) + c1024;
-  const h2_t p3 = as_h2(((w >> 8) & 0x00F000F0u) | 0x54005400u) + c64;
-  return h8_t{p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
+__device__ __forceinline__ h8_t qz_operand(uint32_t w, uint32_t z, uint32_t m1024) {
+  const h2_t cz = as_h2(0xE400E400u + z * 0x10001u);
+  const h2_t p0 = as_h2((w & 0x000F000Fu) | m1024) + cz;
+  const h2_t p1 = as_h2(((w >> 4) & 0x000F000Fu) | m1024) + cz;
+  const h2_t p2 = as_h2(((w >> 8) & 0x000F000Fu) | m1024) + cz;
+  const h2_t p3 = as_h2(((w >> 12) & 0x000F000Fu) | m1024) + cz;
+  return __builtin_bit_cast(h8_t, make_uint4(__builtin_bit_cast(uint32_t, p0), __builtin_bit_cast(uint32_t, p1),
+                                             __builtin_bit_cast(uint32_t, p2), __builtin_bit_cast(uint32_t, p3)));
 }
 
 __device__ __forceinline__ f4_t mfma16(const h8_t& a, const h8_t& b) {
@@ -164,26 +163,146 @@ __device__ __forceinline__ void item_of(const int32_t* __restrict__ items, int i
 }
 
 // ---------------------------------------------------------------------------
-// W13 + SwiGLU: grid (2I/16 column tiles, work items), 4 waves; wave w takes
-// the groups g = w, w + 4, ... and the waves' partial tiles are summed in
-// LDS in wave order. Gate and up of intermediate i are columns 2i and 2i + 1,
-// i.e. neighbouring lanes of the result.
+// Weight staging. A chunk of kc groups of T adjacent column tiles is copied
+// from the bank into LDS with 16-byte loads, all issued before the first LDS
+// write. In the bank a tile holds, for each j = column % 4, a run of 4G
+// units ordered (group, quad); the chunk is the units of groups
+// [g0, g0 + kc) of each run and the records of those groups, which are
+// contiguous. In LDS the runs are padded to a stride of 16 (mod 64) dwords,
+// so the 64 lanes of an operand read (column c = 4 quad + j, dword kb) hit
+// 64 different banks.
 // ---------------------------------------------------------------------------
+constexpr int run_stride(int kc) { return 16 * kc + ((16 - 16 * kc) % 64 + 64) % 64; }
+
+// Piece p of a chunk: 16 bytes of tile tt at bank offset src and LDS offset
+// dst. Pieces are numbered against the full chunk size KC (compile-time
+// divisors); a shorter last chunk leaves the pieces past kc groups off.
+struct Piece {
+  bool on;
+  uint64_t src;
+  int dst;
+};
+
+template <int KC>
+__device__ __forceinline__ Piece weight_piece(int p, int T, int G, int g0, int kc, int tile_dw) {
+  constexpr int kPerTile = 16 * KC, kRun = 4 * KC;
+  const int tt = p / kPerTile, rem = p - tt * kPerTile, j = rem / kRun, u = rem - j * kRun;
+  Piece r;
+  r.on = tt < T && u < 4 * kc;
+  r.src = (uint64_t)tt * 256 * G + (uint64_t)j * 64 * G + 64 * g0 + 16 * u;
+  r.dst = 4 * (tt * tile_dw + j * run_stride(KC) + 4 * u);  // bytes
+  return r;
+}
+
+template <int RB, int KC>
+__device__ __forceinline__ Piece record_piece(int p, int T, int G, int g0, int kc, int tile_rb) {
+  constexpr int kPerTile = KC * RB;  // 16-byte pieces of a full chunk's records
+  const int tt = p / kPerTile, rem = p - tt * kPerTile;
+  Piece r;
+  r.on = tt < T && rem < kc * RB;
+  r.src = (uint64_t)tt * 16 * G * RB + 16 * g0 * RB + 16 * rem;
+  r.dst = tt * tile_rb + 16 * rem;
+  return r;
+}
+
+__device__ __forceinline__ uint4 load_piece(const uint8_t* __restrict__ base, const Piece& pc) {
+  return pc.on ? *reinterpret_cast<const uint4*>(base + pc.src) : make_uint4(0, 0, 0, 0);
+}
+
+// A chunk's staging in two halves: issue() requests up to 5 * 256 weight
+// pieces and 256 record pieces; store() writes them to LDS (and so waits for
+// them). Other work can run in between; only the LDS destinations (-1: no
+// piece) and the data stay in registers.
+template <int RB, int KC, int MAXW, int NTHREADS = 256>
+struct Stager {
+  int d0, d1, d2, d3, d4, dr;
+  uint4 v0, v1, v2, v3, v4, vr;
+
+  __device__ __forceinline__ static int fetch(const uint8_t* __restrict__ base, const Piece& pc, uint4& v) {
+    v = load_piece(base, pc);
+    return pc.on ? pc.dst : -1;
+  }
+
+  __device__ __forceinline__ void issue(const uint8_t* __restrict__ units, const uint8_t* __restrict__ recs, int G,
+                                        int T, int g0, int kc, int tile_dw, int tile_rb) {
+    static_assert(MAXW >= 1 && MAXW <= 5, "pieces per thread");
+    const int t = threadIdx.x;
+    d0 = fetch(units, weight_piece<KC>(t, T, G, g0, kc, tile_dw), v0);
+    if constexpr (MAXW > 1) d1 = fetch(units, weight_piece<KC>(t + NTHREADS, T, G, g0, kc, tile_dw), v1);
+    if constexpr (MAXW > 2) d2 = fetch(units, weight_piece<KC>(t + 2 * NTHREADS, T, G, g0, kc, tile_dw), v2);
+    if constexpr (MAXW > 3) d3 = fetch(units, weight_piece<KC>(t + 3 * NTHREADS, T, G, g0, kc, tile_dw), v3);
+    if constexpr (MAXW > 4) d4 = fetch(units, weight_piece<KC>(t + 4 * NTHREADS, T, G, g0, kc, tile_dw), v4);
+    dr = fetch(recs, record_piece<RB, KC>(t, T, G, g0, kc, tile_rb), vr);
+  }
+
+  __device__ __forceinline__ static void put(uint8_t* lds, int d, const uint4& v) {
+    if (d >= 0) *reinterpret_cast<uint4*>(lds + d) = v;
+  }
+
+  __device__ __forceinline__ void store(uint32_t* __restrict__ wl, uint8_t* __restrict__ rl) const {
+    uint8_t* wb = reinterpret_cast<uint8_t*>(wl);
+    put(wb, d0, v0);
+    if constexpr (MAXW > 1) put(wb, d1, v1);
+    if constexpr (MAXW > 2) put(wb, d2, v2);
+    if constexpr (MAXW > 3) put(wb, d3, v3);
+    if constexpr (MAXW > 4) put(wb, d4, v4);
+    put(rl, dr, vr);
+  }
+};
+
+// Operand of lane (column c = 4 quad + j, block kb) for chunk-local group gl.
+template <int RB>
+__device__ __forceinline__ void lds_operand(const uint32_t* __restrict__ wl, const uint8_t* __restrict__ rl, int rs,
+                                            int gl, int quad, int j, int kb, uint32_t m1024, h8_t& b, float& s) {
+  const uint32_t w = wl[j * rs + (4 * gl + quad) * 4 + kb];
+  const uint8_t* rp = rl + (16 * gl + 4 * quad + j) * RB;
+  const uint32_t sb = (uint32_t)rp[0] | ((uint32_t)rp[1] << 8);
+  s = (float)__builtin_bit_cast(_Float16, (uint16_t)sb);
+  b = qz_operand(w, rp[2], m1024);
+}
+
+// ---------------------------------------------------------------------------
+// W13 + SwiGLU: grid (2I/16 column tiles, work items), 4 waves. The tile is
+// staged in chunks of up to 40 groups (16-byte loads into LDS); within a
+// chunk wave w takes the groups gl = w, w + 4, ... in batches of kW13Batch:
+// a batch's activation loads are issued together (unconditionally, from
+// clamped groups) and then consumed, so a wave waits once per batch while
+// few registers stay live. Groups past the chunk get a zero scale. At the
+// end the waves' partial tiles are summed in LDS in wave order. Gate and up
+// of intermediate i are columns 2i and 2i + 1, i.e. neighbouring lanes.
+// ---------------------------------------------------------------------------
+constexpr int kW13Chunk = 40;
+constexpr int kW13Batch = 2;
+constexpr int kW13PerWave = kW13Chunk / 4;
+constexpr int kW13Pieces = (16 * kW13Chunk + 255) / 256;
+constexpr int kW13WlDw = 4 * run_stride(kW13Chunk);
+static_assert(kW13PerWave % kW13Batch == 0, "batches tile the wave's groups");
+static_assert(kW13Pieces <= 5 && kW13Chunk * 4 <= 256, "staging capacity");
+static_assert(kW13WlDw >= 4 * 2 * 64 * 4, "the partial tiles reuse the weight buffer");
+
 template <int RB, int NRT>
-__device__ __forceinline__ void w13_groups(const uint8_t* __restrict__ ub, const uint8_t* __restrict__ rbp,
-                                           const uint16_t* __restrict__ xr0, const uint16_t* __restrict__ xr1,
-                                           int G, int wave, int kb, f4_t (&acc)[2]) {
-#pragma unroll 4
-  for (int g = wave; g < G; g += 4) {
-    const uint32_t w = *reinterpret_cast<const uint32_t*>(ub + 64 * g);
-    const uint32_t r = load_record1<RB>(rbp + 16 * g * RB);
-    const float s = (float)__builtin_bit_cast(_Float16, (uint16_t)(r & 0xFFFFu));
-    const h8_t b = qz_operand(w, (r >> 16) & 0xFFu);
-    const h8_t a0 = *reinterpret_cast<const h8_t*>(xr0 + 32 * g + 8 * kb);
-    scale_add(acc[0], s, mfma16(a0, b));
-    if constexpr (NRT == 2) {
-      const h8_t a1 = *reinterpret_cast<const h8_t*>(xr1 + 32 * g + 8 * kb);
-      scale_add(acc[1], s, mfma16(a1, b));
+__device__ __forceinline__ void w13_chunk(const uint32_t* wl, const uint8_t* rl, const uint16_t* __restrict__ xr0,
+                                          const uint16_t* __restrict__ xr1, int g0, int kc, int wave, int quad,
+                                          int j, int kb, uint32_t m1024, f4_t& acc0, f4_t& acc1) {
+  constexpr int rs = run_stride(kW13Chunk);
+#pragma unroll 1
+  for (int i0 = 0; i0 < kW13PerWave; i0 += kW13Batch) {
+    h8_t a0[kW13Batch], a1[kW13Batch];
+#pragma unroll
+    for (int u = 0; u < kW13Batch; ++u) {
+      const int g = g0 + min(wave + 4 * (i0 + u), kc - 1);
+      a0[u] = *reinterpret_cast<const h8_t*>(xr0 + 32 * g + 8 * kb);
+      if constexpr (NRT == 2) a1[u] = *reinterpret_cast<const h8_t*>(xr1 + 32 * g + 8 * kb);
+    }
+#pragma unroll
+    for (int u = 0; u < kW13Batch; ++u) {
+      const int gl = wave + 4 * (i0 + u);
+      h8_t b;
+      float sc;
+      lds_operand<RB>(wl, rl, rs, min(gl, kW13Chunk - 1), quad, j, kb, m1024, b, sc);
+      sc = gl < kc ? sc : 0.f;  // past the chunk: stale LDS, finite operand, zero weight
+      scale_add(acc0, sc, mfma16(a0[u], b));
+      if constexpr (NRT == 2) scale_add(acc1, sc, mfma16(a1[u], b));
     }
   }
 }
@@ -196,34 +315,45 @@ __global__ __launch_bounds__(256) void prefill_w13_kernel(const int32_t* __restr
                                                           const uint16_t* __restrict__ x, uint64_t expert_bytes,
                                                           uint64_t units_off, uint64_t meta_off, int H, int I,
                                                           int topk, uint16_t* __restrict__ act) {
-  __shared__ f4_t red[4][2][64];
+  // staged weights, then (after the last chunk) the waves' partial tiles
+  __shared__ __attribute__((aligned(16))) uint32_t wl[kW13WlDw];
+  __shared__ __attribute__((aligned(16))) uint8_t rl[16 * kW13Chunk * 4];
   const int it = blockIdx.y;
   if (it >= *num_items) return;
   int e, row0, rows;
   item_of(items, it, e, row0, rows);
   const int nt = blockIdx.x, G = H >> 5;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const uint32_t m1024 = magic1024();
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int c = lane & 15, kb = lane >> 4, quad = c >> 2, j = c & 3;
   const uint8_t* blk = bank + (uint64_t)e * expert_bytes;
-  // unit (g, column c) dword kb at nt*256G + (j*4G + 4g + quad)*16 + 4kb
-  const uint8_t* ub = blk + units_off + (uint64_t)nt * 256 * G + (uint64_t)j * 64 * G + 16 * quad + 4 * kb;
-  // record (g, column c) at nt*16G*RB + (16g + 4quad + j)*RB
-  const uint8_t* rbp = blk + meta_off + (uint64_t)nt * 16 * G * RB + (uint64_t)(4 * quad + j) * RB;
-  const int ra = min(c, rows - 1), rb = min(16 + c, rows - 1);
-  const uint16_t* xr0 = x + (uint64_t)(row_slot[row0 + ra] / topk) * H;
-  const uint16_t* xr1 = x + (uint64_t)(row_slot[row0 + rb] / topk) * H;
-  f4_t acc[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
-  if (rows > 16)
-    w13_groups<RB, 2>(ub, rbp, xr0, xr1, G, wave, kb, acc);
-  else
-    w13_groups<RB, 1>(ub, rbp, xr0, xr1, G, wave, kb, acc);
-  red[wave][0][lane] = acc[0];
-  red[wave][1][lane] = acc[1];
+  const uint8_t* units = blk + units_off + (uint64_t)nt * 256 * G;
+  const uint8_t* recs = blk + meta_off + (uint64_t)nt * 16 * G * RB;
+  const int nrt = rows > 16 ? 2 : 1;
+  const uint16_t* xr0 = x + (uint64_t)(row_slot[row0 + min(c, rows - 1)] / topk) * H;
+  const uint16_t* xr1 = x + (uint64_t)(row_slot[row0 + min(16 + c, rows - 1)] / topk) * H;
+  f4_t acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
+  for (int g0 = 0; g0 < G; g0 += kW13Chunk) {
+    const int kc = min(kW13Chunk, G - g0);
+    Stager<RB, kW13Chunk, kW13Pieces> st;
+    st.issue(units, recs, G, 1, g0, kc, 0, 0);
+    if (g0 > 0) __syncthreads();  // the previous chunk's LDS reads are done
+    st.store(wl, rl);
+    __syncthreads();
+    if (nrt == 2)
+      w13_chunk<RB, 2>(wl, rl, xr0, xr1, g0, kc, wave, quad, j, kb, m1024, acc0, acc1);
+    else
+      w13_chunk<RB, 1>(wl, rl, xr0, xr1, g0, kc, wave, quad, j, kb, m1024, acc0, acc1);
+  }
+  f4_t* red = reinterpret_cast<f4_t*>(wl);  // [wave][rt][lane]
+  __syncthreads();                          // every wave is done with the staged weights
+  red[(2 * wave + 0) * 64 + lane] = acc0;
+  red[(2 * wave + 1) * 64 + lane] = acc1;
   __syncthreads();
   if (wave != 0) return;
-  const int nrt = rows > 16 ? 2 : 1;
   for (int rt = 0; rt < nrt; ++rt) {
-    const f4_t d = red[0][rt][lane] + red[1][rt][lane] + red[2][rt][lane] + red[3][rt][lane];
+    const f4_t d = red[rt * 64 + lane] + red[(2 + rt) * 64 + lane] + red[(4 + rt) * 64 + lane] +
+                   red[(6 + rt) * 64 + lane];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const float up = dpp<kQuadSwap1>(d[i]);  // column c ^ 1
@@ -238,30 +368,49 @@ __global__ __launch_bounds__(256) void prefill_w13_kernel(const int32_t* __restr
 }
 
 // ---------------------------------------------------------------------------
-// W2: grid (ceil(H/16 / 8) column blocks, work items), 4 waves; wave w takes
-// column tiles 8b + w and 8b + w + 4 over all I/32 groups; fp32 row results.
+// W2: grid (ceil(H/16 / 8) column blocks, work items), 4 waves. The 8 tiles
+// of the block are staged in chunks of up to 5 groups (all of K at inter
+// 160), the activations of the chunk are requested first, and wave w takes
+// tiles w and w + 4 over the chunk's groups, writing fp32 row results.
 // ---------------------------------------------------------------------------
+constexpr int kW2Chunk = 5;
+constexpr int kW2TileDw = 4 * run_stride(kW2Chunk);
+
 template <int RB, int NRT>
-__device__ __forceinline__ void w2_tiles(const uint8_t* __restrict__ blk, uint64_t units_off, uint64_t meta_off,
+__device__ __forceinline__ void w2_block(const uint8_t* __restrict__ units, const uint8_t* __restrict__ recs,
                                          const uint16_t* __restrict__ ar0, const uint16_t* __restrict__ ar1, int G,
-                                         int NT, int nt0, int lane, f4_t (&acc)[2][2]) {
+                                         int T, uint32_t* wl, uint8_t* rl, f4_t (&acc)[2][2]) {
+  const uint32_t m1024 = magic1024();
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int c = lane & 15, kb = lane >> 4, quad = c >> 2, j = c & 3;
-  for (int g = 0; g < G; ++g) {
-    const h8_t a0 = *reinterpret_cast<const h8_t*>(ar0 + 32 * g + 8 * kb);
-    h8_t a1;
-    if constexpr (NRT == 2) a1 = *reinterpret_cast<const h8_t*>(ar1 + 32 * g + 8 * kb);
+  constexpr int rs = run_stride(kW2Chunk);
+  for (int g0 = 0; g0 < G; g0 += kW2Chunk) {
+    const int kc = min(kW2Chunk, G - g0);
+    Stager<RB, kW2Chunk, 3> st;
+    st.issue(units, recs, G, T, g0, kc, kW2TileDw, 16 * kW2Chunk * RB);
+    h8_t a0[kW2Chunk], a1[kW2Chunk];
 #pragma unroll
-    for (int q = 0; q < 2; ++q) {
-      const int nt = nt0 + 4 * q;
-      if (nt < NT) {
-        const uint32_t w = *reinterpret_cast<const uint32_t*>(
-            blk + units_off + (uint64_t)nt * 256 * G + (uint64_t)j * 64 * G + 64 * g + 16 * quad + 4 * kb);
-        const uint32_t r =
-            load_record1<RB>(blk + meta_off + (uint64_t)nt * 16 * G * RB + (uint64_t)(16 * g + 4 * quad + j) * RB);
-        const float s = (float)__builtin_bit_cast(_Float16, (uint16_t)(r & 0xFFFFu));
-        const h8_t b = qz_operand(w, (r >> 16) & 0xFFu);
-        scale_add(acc[q][0], s, mfma16(a0, b));
-        if constexpr (NRT == 2) scale_add(acc[q][1], s, mfma16(a1, b));
+    for (int i = 0; i < kW2Chunk; ++i) {
+      const int g = g0 + min(i, kc - 1);
+      a0[i] = *reinterpret_cast<const h8_t*>(ar0 + 32 * g + 8 * kb);
+      if constexpr (NRT == 2) a1[i] = *reinterpret_cast<const h8_t*>(ar1 + 32 * g + 8 * kb);
+    }
+    if (g0 > 0) __syncthreads();
+    st.store(wl, rl);
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < kW2Chunk; ++i) {
+#pragma unroll
+      for (int q = 0; q < 2; ++q) {
+        const int tt = wave + 4 * q;
+        if (tt < T) {
+          h8_t b;
+          float sc;
+          lds_operand<RB>(wl + tt * kW2TileDw, rl + tt * 16 * kW2Chunk * RB, rs, i, quad, j, kb, m1024, b, sc);
+          sc = i < kc ? sc : 0.f;
+          scale_add(acc[q][0], sc, mfma16(a0[i], b));
+          if constexpr (NRT == 2) scale_add(acc[q][1], sc, mfma16(a1[i], b));
+        }
       }
     }
   }
@@ -273,28 +422,33 @@ __global__ __launch_bounds__(256) void prefill_w2_kernel(const int32_t* __restri
                                                          const uint8_t* __restrict__ bank, uint64_t expert_bytes,
                                                          uint64_t units_off, uint64_t meta_off, int H, int I,
                                                          const uint16_t* __restrict__ act, float* __restrict__ y) {
+  __shared__ __attribute__((aligned(16))) uint32_t wl[8 * kW2TileDw];
+  __shared__ __attribute__((aligned(16))) uint8_t rl[8 * 16 * kW2Chunk * 4];
   const int it = blockIdx.y;
   if (it >= *num_items) return;
   int e, row0, rows;
   item_of(items, it, e, row0, rows);
   const int G = I >> 5, NT = H >> 4;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int c = lane & 15, kb = lane >> 4;
-  const int nt0 = blockIdx.x * 8 + wave;
-  if (nt0 >= NT) return;
+  const int nt0 = blockIdx.x * 8;
+  const int T = min(8, NT - nt0);  // 8, or the last block's 2, 4 or 6 tiles
   const uint8_t* blk = bank + (uint64_t)e * expert_bytes;
+  const uint8_t* units = blk + units_off + (uint64_t)nt0 * 256 * G;
+  const uint8_t* recs = blk + meta_off + (uint64_t)nt0 * 16 * G * RB;
   const uint16_t* ar0 = act + (uint64_t)(row0 + min(c, rows - 1)) * I;
   const uint16_t* ar1 = act + (uint64_t)(row0 + min(16 + c, rows - 1)) * I;
   f4_t acc[2][2] = {};
   if (rows > 16)
-    w2_tiles<RB, 2>(blk, units_off, meta_off, ar0, ar1, G, NT, nt0, lane, acc);
+    w2_block<RB, 2>(units, recs, ar0, ar1, G, T, wl, rl, acc);
   else
-    w2_tiles<RB, 1>(blk, units_off, meta_off, ar0, ar1, G, NT, nt0, lane, acc);
+    w2_block<RB, 1>(units, recs, ar0, ar1, G, T, wl, rl, acc);
   const int nrt = rows > 16 ? 2 : 1;
 #pragma unroll
   for (int q = 0; q < 2; ++q) {
-    const int nt = nt0 + 4 * q;
-    if (nt >= NT) break;
+    const int tt = wave + 4 * q;
+    if (tt >= T) break;
+    const int nt = nt0 + tt;
     for (int rt = 0; rt < nrt; ++rt) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {

@@ -45,7 +45,7 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=200)
     p.add_argument("--warmup", type=int, default=20)
-    p.add_argument("--only", default="", help="comma list of workloads: m1_hot,m1_cold,m8_pool,m8_distinct,stack48,stack48_gemv")
+    p.add_argument("--only", default="", help="comma list of workloads: m1_hot,m1_cold,m8_pool,m8_distinct,p128,p1024,p4096,stack48,stack48_gemv")
     p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     return p.parse_args()
 
@@ -215,6 +215,44 @@ def measure(abi, torch, wl: Workload, steps, warmup):
     return res
 
 
+def measure_prefill(abi, torch, dims, bank, M, steps, warmup, per_expert, calls=8):
+    """Indexed prefill of M tokens (awq_moe_prefill, four launches) on the
+    512-expert rank layer: each token picks 10 distinct experts uniformly.
+    One graph replays `calls` calls with different inputs; reported per call."""
+    dev = bank.device
+    xs, idss, ws_, distinct = [], [], [], []
+    for c in range(calls):
+        rng = inputs.call_rng(SEED, 700 + 16 * M + c)
+        xs.append(torch.from_numpy(inputs.activations(rng, M, H)).to(dev))
+        ids = inputs.ids_distinct(rng, M, K_TOP, E)
+        distinct.append(len(np.unique(ids)))
+        idss.append(torch.from_numpy(ids).to(dev))
+        ws_.append(torch.from_numpy(inputs.router_weights(rng, M, K_TOP)).to(dev))
+    out = torch.empty((M, H), dtype=torch.float16, device=dev)
+    work = abi.alloc_prefill_workspace(dims, M, K_TOP, dev)
+
+    def run():
+        for c in range(calls):
+            abi.awq_moe_prefill(dims, bank, xs[c], idss[c], ws_[c], out=out, workspace=work)
+
+    g = capture(torch, run)
+    ms = time_graph(torch, g, steps, warmup)
+    samples = [time_graph(torch, g, max(steps // 7, 5), 2) for _ in range(7)]
+    del g
+    n = M * K_TOP
+    wbytes = float(np.mean(distinct)) * (per_expert["w13"] + per_expert["w2"])
+    flops = 6.0 * n * H * I
+    us = ms * 1e3 / calls
+    res = {"M": M, "call_us": us, "call_us_median7": float(np.median(samples)) * 1e3 / calls,
+           "call_us_min7": float(np.min(samples)) * 1e3 / calls,
+           "distinct_experts_per_call": float(np.mean(distinct)), "weight_bytes_per_call": wbytes,
+           "weight_gbs": wbytes / (us * 1e3), "weight_pct_peak": 100.0 * wbytes / (us * 1e3) / HBM_PEAK_GBS,
+           "row_result_bytes_per_call": float(n * H * 4 * 2 + n * I * 2 * 2),
+           "tflops": flops / (us * 1e-6) / 1e12, "tokens_per_s": M / (us * 1e-6)}
+    del work
+    return res
+
+
 def stage_source_hash() -> str:
     """sha256[:16] over the stage kernels' device sources (kernels.hip, then device_util.h)."""
     import hashlib
@@ -347,8 +385,9 @@ def main():
     from awq_int4_mixture_amd import abi
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     torch.cuda.set_device(0)
+    prefill_wls = {"p128": 128, "p1024": 1024, "p4096": 4096}
     only = set(filter(None, args.only.split(","))) or {"m1_hot", "m1_cold", "m8_pool", "m8_distinct", "stack48",
-                                                       "stack48_gemv"}
+                                                       "stack48_gemv", *prefill_wls}
 
     t_gen = time.perf_counter()
     bi = inputs.bank_inputs(SEED, E, H, I)
@@ -356,7 +395,7 @@ def main():
     for rb in (4, 3):
         if rb == 4 and "m1_hot" not in only:
             continue
-        if rb == 3 and not ({"m1_cold", "m8_pool", "m8_distinct"} & only):
+        if rb == 3 and not ({"m1_cold", "m8_pool", "m8_distinct", *prefill_wls} & only):
             continue
         dims = abi.make_dims(E, H, I, rb)
         banks[rb] = (dims, torch.from_numpy(abi.prepare_from_inputs(dims, bi)).to("cuda"))
@@ -388,6 +427,11 @@ def main():
             ids = [inputs.ids_all_distinct(inputs.call_rng(SEED, 400 + c), 8, K_TOP, E) for c in range(CALLS)]
             wl = Workload("m8_distinct", abi, torch, dims, bank, ids, 8, rng, per_expert_bytes(abi, dims))
             results["m8_distinct"] = measure(abi, torch, wl, args.steps, args.warmup)
+        for name, Mp in prefill_wls.items():
+            if name in only:
+                dims, bank = banks[3]
+                results[name] = measure_prefill(abi, torch, dims, bank, Mp, max(args.steps // 4, 10),
+                                                max(args.warmup // 4, 2), per_expert_bytes(abi, dims))
         stack = stack_gemv = None
         if {"stack48", "stack48_gemv"} & only:
             del banks
@@ -400,10 +444,11 @@ def main():
         read_ref = read_ceiling(torch)
         floor = launch_floor(torch)
 
-    if not results:
-        print(json.dumps({"stack48": stack, "stack48_gemv": stack_gemv}), flush=True)
+    decode_results = {k: v for k, v in results.items() if k not in prefill_wls}
+    if not decode_results:
+        print(json.dumps({"per_config": results, "stack48": stack, "stack48_gemv": stack_gemv}), flush=True)
         return
-    head = results.get("m1_hot") or next(iter(results.values()))
+    head = decode_results.get("m1_hot") or next(iter(decode_results.values()))
     line = {
         "metric": "MoE layer decode µs and achieved weight HBM GB/s (% of peak) at M=1 and M=8",
         "value": round(head["layer_gbs"], 2),
