@@ -155,6 +155,18 @@ __device__ __forceinline__ void scale_add(f4_t& acc, float s, const f4_t& d) {
   for (int i = 0; i < 4; ++i) acc[i] = fmaf(s, d[i], acc[i]);
 }
 
+// Linear workgroup ids are dealt to the 8 XCDs round robin. With a grid of
+// (NT tiles, items rounded up to a multiple of 8) this maps linear id L so
+// that an item's NT tiles are consecutive ids of one XCD, which then reads
+// the item's activation rows into its L2 once: item = 8 (L / 8NT) + L % 8,
+// tile = (L / 8) % NT (a bijection on the grid).
+__device__ __forceinline__ void xcd_item_tile(int& item, int& tile) {
+  const int NT = gridDim.x;
+  const int L = blockIdx.y * NT + blockIdx.x;
+  item = 8 * (L / (8 * NT)) + (L & 7);
+  tile = (L >> 3) % NT;
+}
+
 __device__ __forceinline__ void item_of(const int32_t* __restrict__ items, int it, int& e, int& row0, int& rows) {
   e = items[2 * it];
   const int rp = items[2 * it + 1];
@@ -318,11 +330,12 @@ __global__ __launch_bounds__(256) void prefill_w13_kernel(const int32_t* __restr
   // staged weights, then (after the last chunk) the waves' partial tiles
   __shared__ __attribute__((aligned(16))) uint32_t wl[kW13WlDw];
   __shared__ __attribute__((aligned(16))) uint8_t rl[16 * kW13Chunk * 4];
-  const int it = blockIdx.y;
+  int it, nt;
+  xcd_item_tile(it, nt);
   if (it >= *num_items) return;
   int e, row0, rows;
   item_of(items, it, e, row0, rows);
-  const int nt = blockIdx.x, G = H >> 5;
+  const int G = H >> 5;
   const uint32_t m1024 = magic1024();
   const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int c = lane & 15, kb = lane >> 4, quad = c >> 2, j = c & 3;
@@ -424,14 +437,15 @@ __global__ __launch_bounds__(256) void prefill_w2_kernel(const int32_t* __restri
                                                          const uint16_t* __restrict__ act, float* __restrict__ y) {
   __shared__ __attribute__((aligned(16))) uint32_t wl[8 * kW2TileDw];
   __shared__ __attribute__((aligned(16))) uint8_t rl[8 * 16 * kW2Chunk * 4];
-  const int it = blockIdx.y;
+  int it, nb;
+  xcd_item_tile(it, nb);
   if (it >= *num_items) return;
   int e, row0, rows;
   item_of(items, it, e, row0, rows);
   const int G = I >> 5, NT = H >> 4;
   const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int c = lane & 15, kb = lane >> 4;
-  const int nt0 = blockIdx.x * 8;
+  const int nt0 = nb * 8;
   const int T = min(8, NT - nt0);  // 8, or the last block's 2, 4 or 6 tiles
   const uint8_t* blk = bank + (uint64_t)e * expert_bytes;
   const uint8_t* units = blk + units_off + (uint64_t)nt0 * 256 * G;
@@ -521,7 +535,8 @@ hipError_t launch_prefill(const StageArgs& a, const uint16_t* x, const float* to
                      w.row_slot, w.items, w.num_items, w.status);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
-  const dim3 g13((2 * a.I) / 16, max_items), g2(((a.H / 16) + 7) / 8, max_items);
+  const int items8 = (max_items + 7) / 8 * 8;  // whole XCD rounds (see xcd_item_tile)
+  const dim3 g13((2 * a.I) / 16, items8), g2(((a.H / 16) + 7) / 8, items8);
   if (a.RB == 4) {
     hipLaunchKernelGGL(prefill_w13_kernel<4>, g13, dim3(256), 0, stream, w.items, w.num_items, w.row_slot, a.bank, x,
                        a.expert_bytes, a.w13_off, a.w13_meta_off, a.H, a.I, a.topk, w.act);
