@@ -246,12 +246,23 @@ int awq_moe_router_gemv(const uint16_t* r, const uint16_t* delta, int32_t M, int
  *
  * Arguments as in awq_moe_decode, with num_experts <= 4096 and
  * workspace_bytes >= awq_moe_prefill_workspace_bytes(dims, M, topk).
- * Workspace layout (all offsets 256-aligned): status u32 at 0 (bit 0: an id
- * outside [0, E); its slot contributes 0), then slot -> row, row -> slot,
- * work items, fp16 act [M*topk][inter] and fp32 y [M*topk][hidden]. The
- * workspace needs no initialisation. Four launches on `stream`; nothing is
- * allocated and nothing synchronises, so the call can be captured in a HIP
- * graph. Calls that share a workspace must not overlap. */
+ * Workspace layout, with n = M*topk, X = ceil(n/32) + min(E, n) and P(b) =
+ * b rounded up to a multiple of 256, each part starting where the previous
+ * one ends:
+ *   [0, 256)   status u32 at 0 (bit 0: an id outside [0, E); its slot
+ *              contributes 0), number of work items i32 at 4;
+ *   P(4n)      slot_row i32[n]: row of each slot, -1 for an invalid id;
+ *   P(4n)      row_slot i32[n]: slot of each row (rows 0 .. valid slots - 1);
+ *   P(8X)      work items i32[X][2]: {expert, first row | rows << 24}, rows
+ *              <= 32, in ascending expert order, each expert's rows cut
+ *              into chunks of 32 from its first row;
+ *   P(2n*I)    fp16 act [n][inter] by row;  P(4n*H) fp32 y [n][hidden] by row.
+ * The rows of expert e are the contiguous range after the rows of all
+ * lower experts (ascending expert order, as route_compact's segments); the
+ * order of the rows inside that range is unspecified and no output depends
+ * on it. The workspace needs no initialisation. Four launches on `stream`;
+ * nothing is allocated and nothing synchronises, so the call can be
+ * captured in a HIP graph. Calls that share a workspace must not overlap. */
 int awq_moe_prefill_workspace_bytes(const awq_moe_dims* dims, int32_t max_tokens, int32_t topk, uint64_t* out);
 int awq_moe_prefill(const awq_moe_dims* dims, const void* bank, const uint16_t* x, const int32_t* topk_ids,
                     const float* topk_w, int32_t M, int32_t topk, uint16_t* out, void* workspace,

@@ -166,3 +166,63 @@ def test_prefill_graph_capture_replays_match_eager():
         g.replay()
         torch.cuda.synchronize()
         assert torch.equal(out.view(torch.int16), eager.view(torch.int16))
+
+
+def _pad256(b):
+    return (b + 255) // 256 * 256
+
+
+@pytest.mark.parametrize("E,k,M,hot", [(16, 4, 128, False), (512, 10, 128, False), (8, 2, 300, True),
+                                       (64, 10, 9, False)])
+def test_prefill_routing_arrays(E, k, M, hot):
+    """The routing arrays in the workspace (layout as documented in the
+    header). Unique parts, bit-exact against the oracle's compaction: the
+    number of work items and each item (expert, first row, rows), the status
+    word, the segment of every slot. The rest checked for validity: slot ->
+    row and row -> slot are inverse bijections on the valid slots, and every
+    slot's row lies inside its expert's segment."""
+    H, I = 256, 32
+    dims, bank, bi = bank_case(70, E, H, I, 3)
+    rng = inputs.call_rng(71, E + M)
+    x = inputs.activations(rng, M, H)
+    if hot:  # a few experts take most rows: several 32-row items per expert
+        ids = np.stack([rng.choice(3, size=k, replace=False) for _ in range(M)]).astype(np.int32)
+    else:
+        ids = inputs.ids_distinct(rng, M, k, E)
+    ids[M // 2, 0] = -3  # one invalid slot
+    w = inputs.router_weights(rng, M, k)
+    ws = abi.alloc_prefill_workspace(dims, M, k)
+    run_prefill(dims, bank, x, ids, w, workspace=ws)
+    raw = ws.cpu().numpy()
+    n = M * k
+    X = (n + 31) // 32 + min(E, n)
+    o_slot_row = 256
+    o_row_slot = o_slot_row + _pad256(4 * n)
+    o_items = o_row_slot + _pad256(4 * n)
+    status, n_items = raw[:8].view(np.int32)
+    slot_row = raw[o_slot_row:o_slot_row + 4 * n].view(np.int32)
+    row_slot = raw[o_row_slot:o_row_slot + 4 * n].view(np.int32)
+    items = raw[o_items:o_items + 8 * X].view(np.int32).reshape(X, 2)
+
+    ro = R.route_compact(ids, E)
+    flat = ids.reshape(-1)
+    valid = (flat >= 0) & (flat < E)
+    V = int(valid.sum())
+    assert status == 1 and V == ro["num_valid"]
+    # segments (unique): expert e owns rows [off, off + cnt) in ascending expert order
+    seg = {int(e): (int(ro["offsets"][a]), int(ro["offsets"][a + 1])) for a, e in
+           enumerate(ro["active_ids"][:ro["num_active"]])}
+    want_items = []
+    for e, (lo, hi) in sorted(seg.items()):
+        for r0 in range(lo, hi, 32):
+            want_items.append((e, r0 | (min(32, hi - r0) << 24)))
+    assert n_items == len(want_items)
+    assert [tuple(v) for v in items[:n_items].tolist()] == want_items
+    # rows (valid placement): bijection, each slot inside its expert's segment
+    assert (slot_row[~valid] == -1).all()
+    rows_of_valid = slot_row[valid]
+    assert sorted(rows_of_valid.tolist()) == list(range(V))
+    assert (row_slot[rows_of_valid] == np.flatnonzero(valid)).all()
+    for s in np.flatnonzero(valid):
+        lo, hi = seg[int(flat[s])]
+        assert lo <= slot_row[s] < hi
