@@ -29,6 +29,9 @@ COMMON = [
     f"-I{INCLUDE}", f"-I{CSRC}",
 ]
 SOURCES = ["kernels.hip", "router.hip", "prefill.hip", "awq_moe_host.cpp"]
+# matrix-core results straight into VGPRs (no accumulator-register copies),
+# for the file whose kernels use MFMA
+EXTRA = {"prefill.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 
 
 def _hipcc() -> str:
@@ -45,7 +48,7 @@ def build(verbose: bool = False) -> str:
     objs = []
     for src in SOURCES:
         obj = os.path.join(OBJDIR, src + ".o")
-        cmd = [hipcc, *COMMON, "-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj]
+        cmd = [hipcc, *COMMON, *EXTRA.get(src, []), "-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj]
         if verbose:
             print(" ".join(cmd), flush=True)
         subprocess.run(cmd, check=True)

@@ -206,15 +206,31 @@ __device__ __forceinline__ Piece weight_piece(int p, int T, int G, int g0, int k
   return r;
 }
 
+// Record piece p: 4 consecutive records (12 or 16 bytes, 4-byte aligned) of
+// tile tt, stored in LDS as 4 dwords (a 3-byte record becomes its 4-byte
+// form), so that an operand read takes one aligned dword.
 template <int RB, int KC>
 __device__ __forceinline__ Piece record_piece(int p, int T, int G, int g0, int kc, int tile_rb) {
-  constexpr int kPerTile = KC * RB;  // 16-byte pieces of a full chunk's records
+  constexpr int kPerTile = 4 * KC;  // record quads of a full chunk
   const int tt = p / kPerTile, rem = p - tt * kPerTile;
   Piece r;
-  r.on = tt < T && rem < kc * RB;
-  r.src = (uint64_t)tt * 16 * G * RB + 16 * g0 * RB + 16 * rem;
+  r.on = tt < T && rem < 4 * kc;
+  r.src = (uint64_t)tt * 16 * G * RB + (16 * g0 + 4 * rem) * RB;
   r.dst = tt * tile_rb + 16 * rem;
   return r;
+}
+
+template <int RB>
+__device__ __forceinline__ uint4 load_records4(const uint8_t* __restrict__ base, const Piece& pc) {
+  if (!pc.on) return make_uint4(0, 0, 0, 0);
+  if constexpr (RB == 4) {
+    return *reinterpret_cast<const uint4*>(base + pc.src);
+  } else {
+    typedef uint32_t u32x3 __attribute__((ext_vector_type(3), aligned(4)));
+    const u32x3 d = *reinterpret_cast<const u32x3*>(base + pc.src);
+    return make_uint4(d.x & 0xFFFFFFu, (d.x >> 24) | ((d.y & 0xFFFFu) << 8), (d.y >> 16) | ((d.z & 0xFFu) << 16),
+                      d.z >> 8);
+  }
 }
 
 __device__ __forceinline__ uint4 load_piece(const uint8_t* __restrict__ base, const Piece& pc) {
@@ -244,7 +260,9 @@ struct Stager {
     if constexpr (MAXW > 2) d2 = fetch(units, weight_piece<KC>(t + 2 * NTHREADS, T, G, g0, kc, tile_dw), v2);
     if constexpr (MAXW > 3) d3 = fetch(units, weight_piece<KC>(t + 3 * NTHREADS, T, G, g0, kc, tile_dw), v3);
     if constexpr (MAXW > 4) d4 = fetch(units, weight_piece<KC>(t + 4 * NTHREADS, T, G, g0, kc, tile_dw), v4);
-    dr = fetch(recs, record_piece<RB, KC>(t, T, G, g0, kc, tile_rb), vr);
+    const Piece prc = record_piece<RB, KC>(t, T, G, g0, kc, tile_rb);
+    vr = load_records4<RB>(recs, prc);
+    dr = prc.on ? prc.dst : -1;
   }
 
   __device__ __forceinline__ static void put(uint8_t* lds, int d, const uint4& v) {
@@ -267,10 +285,9 @@ template <int RB>
 __device__ __forceinline__ void lds_operand(const uint32_t* __restrict__ wl, const uint8_t* __restrict__ rl, int rs,
                                             int gl, int quad, int j, int kb, uint32_t m1024, h8_t& b, float& s) {
   const uint32_t w = wl[j * rs + (4 * gl + quad) * 4 + kb];
-  const uint8_t* rp = rl + (16 * gl + 4 * quad + j) * RB;
-  const uint32_t sb = (uint32_t)rp[0] | ((uint32_t)rp[1] << 8);
-  s = (float)__builtin_bit_cast(_Float16, (uint16_t)sb);
-  b = qz_operand(w, rp[2], m1024);
+  const uint32_t r = reinterpret_cast<const uint32_t*>(rl)[16 * gl + 4 * quad + j];
+  s = (float)__builtin_bit_cast(_Float16, (uint16_t)(r & 0xFFFFu));
+  b = qz_operand(w, (r >> 16) & 0xFFu, m1024);
 }
 
 // ---------------------------------------------------------------------------
@@ -289,7 +306,7 @@ constexpr int kW13PerWave = kW13Chunk / 4;
 constexpr int kW13Pieces = (16 * kW13Chunk + 255) / 256;
 constexpr int kW13WlDw = 4 * run_stride(kW13Chunk);
 static_assert(kW13PerWave % kW13Batch == 0, "batches tile the wave's groups");
-static_assert(kW13Pieces <= 5 && kW13Chunk * 4 <= 256, "staging capacity");
+static_assert(kW13Pieces <= 5 && kW13Chunk * 4 <= 256, "staging capacity (record quads: one per thread)");
 static_assert(kW13WlDw >= 4 * 2 * 64 * 4, "the partial tiles reuse the weight buffer");
 
 template <int RB, int NRT>
@@ -329,7 +346,7 @@ __global__ __launch_bounds__(256) void prefill_w13_kernel(const int32_t* __restr
                                                           int topk, uint16_t* __restrict__ act) {
   // staged weights, then (after the last chunk) the waves' partial tiles
   __shared__ __attribute__((aligned(16))) uint32_t wl[kW13WlDw];
-  __shared__ __attribute__((aligned(16))) uint8_t rl[16 * kW13Chunk * 4];
+  __shared__ __attribute__((aligned(16))) uint8_t rl[16 * kW13Chunk * 4];  // records as dwords
   int it, nt;
   xcd_item_tile(it, nt);
   if (it >= *num_items) return;
@@ -346,13 +363,15 @@ __global__ __launch_bounds__(256) void prefill_w13_kernel(const int32_t* __restr
   const uint16_t* xr0 = x + (uint64_t)(row_slot[row0 + min(c, rows - 1)] / topk) * H;
   const uint16_t* xr1 = x + (uint64_t)(row_slot[row0 + min(16 + c, rows - 1)] / topk) * H;
   f4_t acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
+  // one chunk ahead: the next chunk's loads are in flight while this one is computed
+  Stager<RB, kW13Chunk, kW13Pieces> st;
+  st.issue(units, recs, G, 1, 0, min(kW13Chunk, G), 0, 0);
   for (int g0 = 0; g0 < G; g0 += kW13Chunk) {
     const int kc = min(kW13Chunk, G - g0);
-    Stager<RB, kW13Chunk, kW13Pieces> st;
-    st.issue(units, recs, G, 1, g0, kc, 0, 0);
     if (g0 > 0) __syncthreads();  // the previous chunk's LDS reads are done
     st.store(wl, rl);
     __syncthreads();
+    if (g0 + kW13Chunk < G) st.issue(units, recs, G, 1, g0 + kW13Chunk, min(kW13Chunk, G - g0 - kW13Chunk), 0, 0);
     if (nrt == 2)
       w13_chunk<RB, 2>(wl, rl, xr0, xr1, g0, kc, wave, quad, j, kb, m1024, acc0, acc1);
     else
@@ -400,7 +419,7 @@ __device__ __forceinline__ void w2_block(const uint8_t* __restrict__ units, cons
   for (int g0 = 0; g0 < G; g0 += kW2Chunk) {
     const int kc = min(kW2Chunk, G - g0);
     Stager<RB, kW2Chunk, 3> st;
-    st.issue(units, recs, G, T, g0, kc, kW2TileDw, 16 * kW2Chunk * RB);
+    st.issue(units, recs, G, T, g0, kc, kW2TileDw, 16 * kW2Chunk * 4);
     h8_t a0[kW2Chunk], a1[kW2Chunk];
 #pragma unroll
     for (int i = 0; i < kW2Chunk; ++i) {
@@ -419,7 +438,7 @@ __device__ __forceinline__ void w2_block(const uint8_t* __restrict__ units, cons
         if (tt < T) {
           h8_t b;
           float sc;
-          lds_operand<RB>(wl + tt * kW2TileDw, rl + tt * 16 * kW2Chunk * RB, rs, i, quad, j, kb, m1024, b, sc);
+          lds_operand<RB>(wl + tt * kW2TileDw, rl + tt * 16 * kW2Chunk * 4, rs, i, quad, j, kb, m1024, b, sc);
           sc = i < kc ? sc : 0.f;
           scale_add(acc[q][0], sc, mfma16(a0[i], b));
           if constexpr (NRT == 2) scale_add(acc[q][1], sc, mfma16(a1[i], b));
