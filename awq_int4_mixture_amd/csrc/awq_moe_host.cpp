@@ -73,6 +73,8 @@ Layout make_layout(const awq_moe_dims* d) {
 
 // Workspace: [status u32 | pad] [fp16 act[n][I]].
 static_assert(AWQ_MOE_WS_ACT_OFFSET % 256 == 0, "act must stay 256-byte aligned");
+static_assert(AWQ_MOE_WS_ACT_OFFSET == AWQ_MOE_KWS_ACT_OFFSET && AWQ_MOE_WS_STATUS_OFFSET == AWQ_MOE_KWS_STATUS_OFFSET,
+              "kernels and header agree on the workspace layout");
 
 uint64_t ws_total(const awq_moe_dims* d, int max_tokens, int topk) {
   const uint64_t n = (uint64_t)max_tokens * (uint64_t)topk;
@@ -375,8 +377,7 @@ int awq_moe_w13_swiglu(const awq_moe_dims* dims, const void* bank, const uint16_
   if (!x || !aligned(x, 16)) return fail(AWQ_MOE_EINVAL, "x null or not 16-byte aligned");
   if (!topk_ids || !aligned(topk_ids, 4)) return fail(AWQ_MOE_EINVAL, "topk_ids null or misaligned");
   if ((rc = check_device())) return rc;
-  const WsPtrs w = ws_ptrs(workspace);
-  return hip_status(awq_moe::launch_w13_swiglu(stage_args(dims, bank, topk_ids, M, topk), x, w.act, w.status,
+  return hip_status(awq_moe::launch_w13_swiglu(stage_args(dims, bank, topk_ids, M, topk), x, workspace,
                                                static_cast<hipStream_t>(stream)),
                     "w13 launch");
 }
@@ -487,7 +488,7 @@ int awq_moe_decode(const awq_moe_dims* dims, const void* bank, const uint16_t* x
   const WsPtrs w = ws_ptrs(workspace);
   hipStream_t s = static_cast<hipStream_t>(stream);
   const awq_moe::StageArgs a = stage_args(dims, bank, topk_ids, M, topk);
-  hipError_t e = awq_moe::launch_w13_swiglu(a, x, w.act, w.status, s);
+  hipError_t e = awq_moe::launch_w13_swiglu(a, x, workspace, s);
   if (e != hipSuccess) return hip_status(e, "w13 launch");
   return hip_status(awq_moe::launch_w2_reduce(a, w.act, topk_w, out, s), "w2 launch");
 }

@@ -11,6 +11,9 @@
 #define AWQ_MOE_KMAX_ROUTER_E 4096
 #define AWQ_MOE_KMAX_HIDDEN 8192
 #define AWQ_MOE_STATUS_BAD_ID_BIT 1u
+// decode workspace: status word, then fp16 act [M*topk][I]
+#define AWQ_MOE_KWS_STATUS_OFFSET 0
+#define AWQ_MOE_KWS_ACT_OFFSET 256
 
 namespace awq_moe {
 
@@ -34,8 +37,8 @@ struct RouteOut {
 };
 
 hipError_t launch_route_compact(const int32_t* ids, int n, int E, const RouteOut& o, hipStream_t stream);
-hipError_t launch_w13_swiglu(const StageArgs& a, const uint16_t* x, uint16_t* act, uint32_t* status,
-                             hipStream_t stream);
+// ws: the decode workspace (status word and act at the offsets above).
+hipError_t launch_w13_swiglu(const StageArgs& a, const uint16_t* x, void* ws, hipStream_t stream);
 hipError_t launch_w2_reduce(const StageArgs& a, const uint16_t* act, const float* topk_w, uint16_t* out,
                             hipStream_t stream);
 hipError_t launch_router_topk(const float* logits, int M, int E, int k, int32_t* ids, float* w, hipStream_t stream);

@@ -49,23 +49,46 @@ __device__ __forceinline__ void decode_record(uint32_t r, float& s, float& z) {
   z = (float)((r >> 16) & 0xFFu);
 }
 
+// A lane's four records as loaded (one 16- or 12-byte load), decoded only
+// where they are used, so that the wait for them can come late.
 template <int RB>
-__device__ __forceinline__ Records<RB> load_records(const uint8_t* p) {
+struct RawRecords {
+  uint32_t d[RB];
+};
+
+template <int RB>
+__device__ __forceinline__ RawRecords<RB> load_records_raw(const uint8_t* p) {
+  RawRecords<RB> r;
+  if constexpr (RB == 4) {
+    const uint4 v = *reinterpret_cast<const uint4*>(p);
+    r.d[0] = v.x; r.d[1] = v.y; r.d[2] = v.z; r.d[3] = v.w;
+  } else {
+    const u32x3_a4 v = *reinterpret_cast<const u32x3_a4*>(p);
+    r.d[0] = v.x; r.d[1] = v.y; r.d[2] = v.z;
+  }
+  return r;
+}
+
+template <int RB>
+__device__ __forceinline__ Records<RB> decode_records(const RawRecords<RB>& v) {
   Records<RB> out;
   uint32_t r[4];
   if constexpr (RB == 4) {
-    uint4 v = *reinterpret_cast<const uint4*>(p);
-    r[0] = v.x; r[1] = v.y; r[2] = v.z; r[3] = v.w;
+    r[0] = v.d[0]; r[1] = v.d[1]; r[2] = v.d[2]; r[3] = v.d[3];
   } else {
-    u32x3_a4 v = *reinterpret_cast<const u32x3_a4*>(p);
-    r[0] = v.x;
-    r[1] = __builtin_amdgcn_alignbyte(v.y, v.x, 3);
-    r[2] = __builtin_amdgcn_alignbyte(v.z, v.y, 2);
-    r[3] = v.z >> 8;
+    r[0] = v.d[0];
+    r[1] = __builtin_amdgcn_alignbyte(v.d[1], v.d[0], 3);
+    r[2] = __builtin_amdgcn_alignbyte(v.d[2], v.d[1], 2);
+    r[3] = v.d[2] >> 8;
   }
 #pragma unroll
   for (int j = 0; j < 4; ++j) decode_record(r[j], out.s[j], out.z[j]);
   return out;
+}
+
+template <int RB>
+__device__ __forceinline__ Records<RB> load_records(const uint8_t* p) {
+  return decode_records<RB>(load_records_raw<RB>(p));
 }
 
 // 32 fp16 activations of one group as 16 packed pairs: px[4d + p] holds
@@ -278,53 +301,79 @@ __global__ __launch_bounds__(1024) void route_compact_kernel(const int32_t* __re
 }
 
 // ---------------------------------------------------------------------------
-// W13 + SwiGLU: grid (2I/16 column tiles, n slots). The workgroup of slot s
-// reads its expert id with one scalar load and at once requests its expert's
-// 16-column tile (all of K) and its token's activation row, then writes
-// act[s] for that tile. Slots that share an expert read the same tile; the
-// second and later reads are served by L2 or the MALL (all of them request
-// it within the same few hundred nanoseconds), which measured faster than
-// first electing one workgroup per expert from the routed ids.
-// Workgroup (0, 0) also writes the status word.
+// Shape word of the decode kernels: G = H/32 in bits 0..8, G2 = I/32 in bits
+// 9..15, topk in bits 16..21, M in bits 22..25. Together with 32-bit expert
+// strides it keeps every argument a kernel needs before its first weight
+// load inside the 14 dwords that arrive preloaded in SGPRs, so no wave waits
+// on a kernel-argument load.
+// ---------------------------------------------------------------------------
+__host__ __device__ constexpr uint32_t pack_dims(int H, int I, int topk, int M) {
+  return (uint32_t)(H >> 5) | ((uint32_t)(I >> 5) << 9) | ((uint32_t)topk << 16) | ((uint32_t)M << 22);
+}
+__device__ __forceinline__ int dims_G(uint32_t d) { return (int)(d & 0x1FFu); }
+__device__ __forceinline__ int dims_G2(uint32_t d) { return (int)((d >> 9) & 0x7Fu); }
+__device__ __forceinline__ int dims_topk(uint32_t d) { return (int)((d >> 16) & 0x3Fu); }
+__device__ __forceinline__ int dims_M(uint32_t d) { return (int)((d >> 22) & 0xFu); }
+
+// ---------------------------------------------------------------------------
+// W13 + SwiGLU: grid (2I/16 column tiles, n slots), ceil(H/8 / 64) waves.
+// The workgroup of slot s reads its expert id with one scalar load; its
+// token's activations are requested before that load returns, and the
+// expert's 16-column tile (all of K) right after it, so the slot's chain is
+// two memory round trips. It then writes act[s] for that tile. Slots that
+// share an expert read the same tile; the second and later reads are served
+// by L2 or the MALL (all of them request it within the same few hundred
+// nanoseconds), which measured faster than first electing one workgroup per
+// expert from the routed ids.
+// The workspace holds the status word at offset 0 and act at offset 256.
+// Wave 0 of workgroup (0, 0) also writes the status word; its id loads are
+// issued first and consumed after the weight loads are in flight.
 // ---------------------------------------------------------------------------
 template <int RB>
 __global__ __launch_bounds__(1024) void w13_swiglu_kernel(const int32_t* __restrict__ ids,
                                                           const uint8_t* __restrict__ units_base,
-                                                          const uint8_t* __restrict__ recs_base,
-                                                          const uint16_t* __restrict__ x, uint64_t expert_bytes, int H,
-                                                          int I, int topk, int E, uint16_t* __restrict__ act,
-                                                          uint32_t* __restrict__ status, int M) {
+                                                          const uint16_t* __restrict__ x, uint8_t* __restrict__ ws,
+                                                          uint32_t expert_bytes, uint32_t meta_delta, uint32_t dims,
+                                                          int E) {
   __shared__ float red[16][16];  // [wave][column]
   const int nt = blockIdx.x, s = blockIdx.y;
-  // First request: the slot's expert id (a scalar load; nothing depends on
-  // anything else before the weight loads).
-  const int e = ids[s];
-  const int t = threadIdx.x;
-  const int lane = t & 63, wave = t >> 6, nwaves = blockDim.x >> 6;
-  const int G = H >> 5;
-  const int L = 4 * G;
+  const int e = ids[s];  // scalar load
+  const int G = dims_G(dims), I = 32 * dims_G2(dims), topk = dims_topk(dims);
+  const int H = 32 * G, L = 4 * G, nwaves = (L + 63) >> 6;
+  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
   const int g = t >> 2;
-  if (nt == 0 && s == 0 && status != nullptr) {
-    int bad = 0;
-    for (int i = t; i < M * topk; i += blockDim.x) {
-      const int v = ids[i];
-      bad |= (v < 0 || v >= E);
-    }
-    bad = __syncthreads_or(bad);
-    if (t == 0) *status = bad ? AWQ_MOE_STATUS_BAD_ID_BIT : 0u;
+  const bool status_wave = nt == 0 && s == 0 && wave == 0;
+  const int n = topk * dims_M(dims);  // <= 256 slots: four per lane of one wave
+  int sid[4];
+  if (status_wave) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) sid[q] = lane + 64 * q < n ? ids[lane + 64 * q] : 0;
   }
-  if (e < 0 || e >= E) return;  // invalid slot: no row
-  float part[4] = {0.f, 0.f, 0.f, 0.f};
-  if (t < L) {
-    const uint8_t* units = units_base + (uint64_t)e * expert_bytes + (uint64_t)nt * 256u * G;
-    uint4 w[4];
+  Act32 av;
+  if (t < L) av = load_act32(x + (uint64_t)(s / topk) * H + 32 * g);
+  const bool live = e >= 0 && e < E;
+  const uint64_t eo = (uint64_t)(uint32_t)e * expert_bytes;
+  uint4 w[4];
+  RawRecords<RB> rraw;
+  if (live && t < L) {
+    const uint8_t* units = units_base + eo + (uint64_t)nt * 256u * G;
+    rraw = load_records_raw<RB>(units_base + eo + meta_delta + (uint64_t)nt * 16u * G * RB + (uint64_t)t * 4u * RB);
 #pragma unroll
     for (int j = 0; j < 4; ++j) w[j] = *reinterpret_cast<const uint4*>(units + ((uint64_t)j * L + t) * 16u);
-    const Records<RB> rec = load_records<RB>(recs_base + (uint64_t)e * expert_bytes + (uint64_t)nt * 16u * G * RB +
-                                             (uint64_t)t * 4u * RB);
-    const Act32 av = load_act32(x + (uint64_t)(s / topk) * H + 32 * g);
+  }
+  if (status_wave) {
+    bool bad = false;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) bad |= lane + 64 * q < n && (sid[q] < 0 || sid[q] >= E);
+    const unsigned long long b = __ballot(bad);
+    if (lane == 0) *reinterpret_cast<uint32_t*>(ws + AWQ_MOE_KWS_STATUS_OFFSET) = b ? AWQ_MOE_STATUS_BAD_ID_BIT : 0u;
+  }
+  if (!live) return;  // invalid slot: no row (uniform over the workgroup)
+  float part[4] = {0.f, 0.f, 0.f, 0.f};
+  if (t < L) {
     float S, Cs;
     group_sums(av, S, Cs);
+    const Records<RB> rec = decode_records<RB>(rraw);
     const Magic mg = make_magic();
 #pragma unroll
     for (int j = 0; j < 4; ++j) part[j] = rec.s[j] * (unit_dot(w[j], av, mg) - fmaf(rec.z[j], S, Cs));
@@ -338,6 +387,7 @@ __global__ __launch_bounds__(1024) void w13_swiglu_kernel(const int32_t* __restr
     float h = 0.f;
     for (int wv = 0; wv < nwaves; ++wv) h += red[wv][t];
     const float other = __shfl_xor(h, 1);  // partner column: gate <-> up
+    uint16_t* act = reinterpret_cast<uint16_t*>(ws + AWQ_MOE_KWS_ACT_OFFSET);
     if (!(t & 1)) act[(uint64_t)s * I + nt * 8 + (t >> 1)] = __builtin_bit_cast(uint16_t, (_Float16)silu_mul(h, other));
   }
 }
@@ -456,62 +506,88 @@ __global__ __launch_bounds__(1024) void w2_reduce_kernel(const int32_t* __restri
 // row rotations within 16 lanes, one exchange across the two rows of the
 // half), which leaves a single LDS round for the router-weighted sum in
 // ascending (expert, slot) order.
+// Every load that does not depend on an id (the token's ids and the wave's
+// two router weights for the ranking, every lane's activations) is issued
+// before the scalar id loads are waited for, so each wave's chain is the id
+// load and then one round trip for the weights; the ranking (two ballots per
+// wave) runs while the weights are in flight.
 // ---------------------------------------------------------------------------
 template <int RB>
 __global__ __launch_bounds__(1024) void w2_reduce32_kernel(const int32_t* __restrict__ topk_ids,
                                                            const uint8_t* __restrict__ units_base,
-                                                           const uint8_t* __restrict__ recs_base,
-                                                           const uint16_t* __restrict__ act, uint64_t expert_bytes,
-                                                           int H, int I, int topk, int E,
+                                                           const uint16_t* __restrict__ act,
                                                            const float* __restrict__ topk_w,
-                                                           uint16_t* __restrict__ out) {
+                                                           uint16_t* __restrict__ out, uint32_t expert_bytes,
+                                                           uint32_t meta_delta, uint32_t dims, int E) {
   __shared__ float ys[AWQ_MOE_KMAX_TOPK * 16];     // [rank][16]
   __shared__ int rk[AWQ_MOE_KMAX_TOPK];            // slot -> rank (-1: invalid slot)
   __shared__ float wr[AWQ_MOE_KMAX_TOPK];          // rank -> router weight
   __shared__ int nvalid_s;
+  const int G2 = dims_G2(dims), LS = 4 * G2;  // LS <= 32
+  const int H = 32 * dims_G(dims), I = 32 * G2, topk = dims_topk(dims);
   const int T2 = H >> 4;
   const int nt = (T2 & 7) ? (int)blockIdx.x : (int)((blockIdx.x & 7) * (T2 >> 3) + (blockIdx.x >> 3));
   const int tok = blockIdx.y;
   const int t = threadIdx.x, lane = t & 63;
-  const int G2 = I >> 5, LS = 4 * G2;  // LS <= 32
   const int32_t* ids = topk_ids + tok * topk;
   // the wave's two slots; indexes clamped into the token's ids (unused past topk)
   const int w2 = __builtin_amdgcn_readfirstlane(t >> 6) * 2;
   const int e0 = ids[w2 < topk ? w2 : topk - 1];
   const int e1 = ids[w2 + 1 < topk ? w2 + 1 : topk - 1];
+  // Every load below is unconditional, with clamped indexes (a dead lane
+  // reads what a live lane of its half reads, inside the bank), so the code
+  // is straight-line and each value is waited for just before its first use
+  // (exec-masked loads measured slower: the waits after the branch cover all
+  // of them). The ranking inputs come first.
+  const int rid = ids[lane < topk ? lane : topk - 1];
+  const float wt0 = topk_w[tok * topk + (w2 < topk ? w2 : topk - 1)];
+  const float wt1 = topk_w[tok * topk + (w2 + 1 < topk ? w2 + 1 : topk - 1)];
   const int slot = t >> 5, tl = t & 31;
+  const bool lane_on = slot < topk && tl < LS;
+  const int slotc = slot < topk ? slot : topk - 1;
+  const int tlc = tl < LS ? tl : LS - 1, gc = tlc >> 2, quadc = tlc & 3;
+  const uint4 araw = *reinterpret_cast<const uint4*>(act + (uint64_t)(tok * topk + slotc) * I + 32 * gc + 8 * quadc);
   const int e = (t & 32) ? e1 : e0;
-  const bool live = slot < topk && tl < LS && e >= 0 && e < E;
-  const int g = tl >> 2, quad = tl & 3;
+  const bool valid_e = e >= 0 && e < E;
+  const bool live = lane_on && valid_e;
   float part[4] = {0.f, 0.f, 0.f, 0.f};
+  const uint64_t eo = (uint64_t)(uint32_t)(valid_e ? e : 0) * expert_bytes;
+  const uint8_t* units = units_base + eo + (uint64_t)nt * 256u * G2;
+  const RawRecords<RB> rraw =
+      load_records_raw<RB>(units_base + eo + meta_delta + (uint64_t)nt * 16u * G2 * RB + (uint64_t)tlc * 4u * RB);
   uint4 w[4];
-  Records<RB> rec;
-  Act32 av;
-  if (live) {
-    const uint64_t eo = (uint64_t)e * expert_bytes;
-    const uint8_t* units = units_base + eo + (uint64_t)nt * 256u * G2;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) w[j] = *reinterpret_cast<const uint4*>(units + ((uint64_t)j * LS + tl) * 16u);
-    rec = load_records<RB>(recs_base + eo + (uint64_t)nt * 16u * G2 * RB + (uint64_t)tl * 4u * RB);
-    av = load_act32_quad(act + (uint64_t)(tok * topk + slot) * I + 32 * g, quad);
-  }
-  if (t < 64) {
-    // rank of slot t among the valid slots by (id, slot), while the loads fly
-    const int id = t < topk ? ids[t] : -1;
-    const bool v = t < topk && id >= 0 && id < E;
-    int r = 0;
-    for (int j2 = 0; j2 < topk; ++j2) {
-      const int k2 = __builtin_amdgcn_readlane(id, j2);
-      r += (k2 >= 0 && k2 < E) & ((k2 < id) | ((k2 == id) & (j2 < t)));
+  for (int j = 0; j < 4; ++j) w[j] = *reinterpret_cast<const uint4*>(units + ((uint64_t)j * LS + tlc) * 16u);
+  // Keep the ranking below the weight loads: it runs while they are in flight.
+  __builtin_amdgcn_sched_barrier(0);
+  {
+    // Ranks of the wave's two slots among the token's valid slots by (id,
+    // slot): lane j holds slot j's id, so each rank is the population count
+    // of one ballot against the wave-uniform ids e0 and e1.
+    const bool vj = lane < topk && rid >= 0 && rid < E;
+    const unsigned long long b0 = __ballot(vj && (rid < e0 || (rid == e0 && lane < w2)));
+    const unsigned long long b1 = __ballot(vj && (rid < e1 || (rid == e1 && lane < w2 + 1)));
+    const unsigned long long bv = __ballot(vj);
+    if (lane == 0) {
+      const bool v0 = w2 < topk && e0 >= 0 && e0 < E, v1 = w2 + 1 < topk && e1 >= 0 && e1 < E;
+      const int r0 = (int)__popcll(b0), r1 = (int)__popcll(b1);
+      if (w2 < topk) rk[w2] = v0 ? r0 : -1;
+      if (w2 + 1 < topk) rk[w2 + 1] = v1 ? r1 : -1;
+      if (v0) wr[r0] = wt0;
+      if (v1) wr[r1] = wt1;
+      if (w2 == 0) nvalid_s = (int)__popcll(bv);
     }
-    if (t < topk) rk[t] = v ? r : -1;
-    if (v) wr[r] = topk_w[tok * topk + t];
-    const unsigned long long b = __ballot(v);
-    if (t == 0) nvalid_s = (int)__popcll(b);
   }
+  // the quad's four 16-byte quarters of the group's activations, to every lane of the quad
+  Act32 av;
+  av.px[0] = quad_bcast<0>(araw.x); av.px[1] = quad_bcast<0>(araw.y); av.px[2] = quad_bcast<0>(araw.z); av.px[3] = quad_bcast<0>(araw.w);
+  av.px[4] = quad_bcast<1>(araw.x); av.px[5] = quad_bcast<1>(araw.y); av.px[6] = quad_bcast<1>(araw.z); av.px[7] = quad_bcast<1>(araw.w);
+  av.px[8] = quad_bcast<2>(araw.x); av.px[9] = quad_bcast<2>(araw.y); av.px[10] = quad_bcast<2>(araw.z); av.px[11] = quad_bcast<2>(araw.w);
+  av.px[12] = quad_bcast<3>(araw.x); av.px[13] = quad_bcast<3>(araw.y); av.px[14] = quad_bcast<3>(araw.z); av.px[15] = quad_bcast<3>(araw.w);
   if (live) {
     float S, Cs;
     group_sums(av, S, Cs);
+    const Records<RB> rec = decode_records<RB>(rraw);
     const Magic mg = make_magic();
 #pragma unroll
     for (int j = 0; j < 4; ++j) part[j] = rec.s[j] * (unit_dot(w[j], av, mg) - fmaf(rec.z[j], S, Cs));
@@ -592,17 +668,27 @@ hipError_t launch_route_compact(const int32_t* ids, int n, int E, const RouteOut
   return hipGetLastError();
 }
 
-hipError_t launch_w13_swiglu(const StageArgs& a, const uint16_t* x, uint16_t* act, uint32_t* status,
-                             hipStream_t stream) {
+// The decode kernels take 32-bit expert strides and record offsets; the
+// largest admitted shape (hidden 8192, inter 2048) needs about 34 MB per
+// expert, so a wider value means the arguments are corrupt.
+static bool fits32(const StageArgs& a, uint64_t meta_delta) {
+  return a.expert_bytes <= 0xFFFFFFFFull && meta_delta <= 0xFFFFFFFFull;
+}
+
+hipError_t launch_w13_swiglu(const StageArgs& a, const uint16_t* x, void* ws, hipStream_t stream) {
+  const uint64_t md = a.w13_meta_off - a.w13_off;
+  if (!fits32(a, md)) return hipErrorInvalidValue;
   const int L = 4 * (a.H / 32);
   const dim3 block(((L + 63) / 64) * 64);
   const dim3 grid((2 * a.I) / 16, a.M * a.topk);
+  const uint32_t dims = pack_dims(a.H, a.I, a.topk, a.M);
+  uint8_t* w = static_cast<uint8_t*>(ws);
   if (a.RB == 4)
-    hipLaunchKernelGGL(w13_swiglu_kernel<4>, grid, block, 0, stream, a.topk_ids, a.bank + a.w13_off,
-                       a.bank + a.w13_meta_off, x, a.expert_bytes, a.H, a.I, a.topk, a.E, act, status, a.M);
+    hipLaunchKernelGGL(w13_swiglu_kernel<4>, grid, block, 0, stream, a.topk_ids, a.bank + a.w13_off, x, w,
+                       (uint32_t)a.expert_bytes, (uint32_t)md, dims, a.E);
   else
-    hipLaunchKernelGGL(w13_swiglu_kernel<3>, grid, block, 0, stream, a.topk_ids, a.bank + a.w13_off,
-                       a.bank + a.w13_meta_off, x, a.expert_bytes, a.H, a.I, a.topk, a.E, act, status, a.M);
+    hipLaunchKernelGGL(w13_swiglu_kernel<3>, grid, block, 0, stream, a.topk_ids, a.bank + a.w13_off, x, w,
+                       (uint32_t)a.expert_bytes, (uint32_t)md, dims, a.E);
   return hipGetLastError();
 }
 
@@ -625,12 +711,15 @@ hipError_t launch_w2_reduce(const StageArgs& a, const uint16_t* act, const float
     // one 32-lane half per slot, two slots per wave
     const dim3 block(((a.topk * 32 + 63) / 64) * 64);
     const dim3 grid(a.H / 16, a.M);
+    const uint64_t md = a.w2_meta_off - a.w2_off;
+    if (!fits32(a, md)) return hipErrorInvalidValue;
+    const uint32_t dims = pack_dims(a.H, a.I, a.topk, a.M);
     if (a.RB == 4)
-      hipLaunchKernelGGL(w2_reduce32_kernel<4>, grid, block, 0, stream, a.topk_ids, a.bank + a.w2_off,
-                         a.bank + a.w2_meta_off, act, a.expert_bytes, a.H, a.I, a.topk, a.E, topk_w, out);
+      hipLaunchKernelGGL(w2_reduce32_kernel<4>, grid, block, 0, stream, a.topk_ids, a.bank + a.w2_off, act, topk_w,
+                         out, (uint32_t)a.expert_bytes, (uint32_t)md, dims, a.E);
     else
-      hipLaunchKernelGGL(w2_reduce32_kernel<3>, grid, block, 0, stream, a.topk_ids, a.bank + a.w2_off,
-                         a.bank + a.w2_meta_off, act, a.expert_bytes, a.H, a.I, a.topk, a.E, topk_w, out);
+      hipLaunchKernelGGL(w2_reduce32_kernel<3>, grid, block, 0, stream, a.topk_ids, a.bank + a.w2_off, act, topk_w,
+                         out, (uint32_t)a.expert_bytes, (uint32_t)md, dims, a.E);
     return hipGetLastError();
   }
   if (a.RB == 4)
