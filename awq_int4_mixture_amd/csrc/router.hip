@@ -47,16 +47,19 @@ __device__ void router_topk_row(const float* __restrict__ lg, int E, int k, int3
   __shared__ uint64_t cand[AWQ_MOE_KMAX_ROUTER_E / 64 * AWQ_MOE_KMAX_TOPK];
   __shared__ float cand_v[AWQ_MOE_KMAX_ROUTER_E / 64 * AWQ_MOE_KMAX_TOPK];
   __shared__ float sel_v[AWQ_MOE_KMAX_TOPK];
-  __shared__ float sel_p[AWQ_MOE_KMAX_TOPK];
   const int t = threadIdx.x, nt = blockDim.x;
   const int lane = t & 63, wave = t >> 6, nwaves = nt >> 6;
   const int nchunks = (E + 63) >> 6;
   const int ncand = nchunks * k;
+  // the wave's first chunk is requested before anything waits
+  const int i0 = wave * 64 + lane;
+  float v0 = 0.f;
+  if (i0 < E) v0 = lg[i0];
   for (int c = t; c < ncand; c += nt) cand[c] = 0;  // 0 sorts below every key
   __syncthreads();
   for (int chunk = wave; chunk < nchunks; chunk += nwaves) {
     const int i = chunk * 64 + lane;
-    const float v = i < E ? lg[i] : 0.f;
+    const float v = chunk == wave ? v0 : (i < E ? lg[i] : 0.f);
     const uint64_t key = i < E ? router_key(v, i) : 0;
     int r = 0;
 #pragma unroll
@@ -79,12 +82,11 @@ __device__ void router_topk_row(const float* __restrict__ lg, int E, int k, int3
     }
   }
   __syncthreads();
-  if (t < 64) {  // one wave: LDS writes are visible to its own later reads
+  if (t < 64) {
     const float m = sel_v[0];
     const float p = t < k ? expf(sel_v[t] - m) : 0.f;
-    if (t < k) sel_p[t] = p;
-    float sum = 0.f;  // in rank order
-    for (int r = 0; r < k; ++r) sum += sel_p[r];
+    float sum = 0.f;  // in rank order, from the lanes' registers
+    for (int r = 0; r < k; ++r) sum += __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, p), r));
     if (t < k) w[t] = p / sum;
   }
 }
