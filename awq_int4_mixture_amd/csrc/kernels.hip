@@ -499,119 +499,127 @@ __global__ __launch_bounds__(1024) void w2_reduce_kernel(const int32_t* __restri
 }
 
 // ---------------------------------------------------------------------------
-// W2 + router-weighted reduction for I <= 256 (at most 32 lanes per slot):
-// grid (H/16 tiles, M tokens) as above, but every slot owns one 32-lane half
-// of a wave, so a wave holds two slots. The two ids arrive as wave-uniform
-// scalar loads, and the sum over the slot's groups runs in registers (DPP
-// row rotations within 16 lanes, one exchange across the two rows of the
-// half), which leaves a single LDS round for the router-weighted sum in
-// ascending (expert, slot) order.
-// Every load that does not depend on an id (the token's ids and the wave's
-// two router weights for the ranking, every lane's activations) is issued
-// before the scalar id loads are waited for, so each wave's chain is the id
-// load and then one round trip for the weights; the ranking (two ballots per
-// wave) runs while the weights are in flight.
+// W2 + router-weighted reduction for I <= 256: grid (H/16 tiles, M tokens)
+// as above. A slot owns LS = 4*I/32 <= 32 adjacent lanes of a wave (lane =
+// 4g + quad inside its segment), and a wave holds SPW = floor(64 / LS)
+// slots, so a token's slots take ceil(topk / SPW) waves: 4 at I = 160 and
+// top-k 10, one per SIMD of the CU (with 5 waves one SIMD runs two, and at
+// M = 1, one workgroup per CU, that SIMD sets the kernel's time).
+// The wave's ids and router weights arrive as scalar loads; the token's
+// ids (for the ranking) and the activations are requested before they
+// return, and every load is unconditional with clamped indexes, so the
+// code is straight-line and each value is waited for just before its first
+// use (exec-masked loads measured slower: the waits after the branch cover
+// all of them). Each wave ranks its own slots by (id, slot) with one ballot
+// per slot while its weights are in flight and keeps the ranks in SGPRs.
+// A slot's groups are summed in ascending g through the wave's own LDS
+// rows (no barrier: a wave's LDS operations complete in order), and the
+// slot's 16 column results go to LDS at its rank; one barrier, then the
+// router-weighted sum in ascending (expert, slot) order.
 // ---------------------------------------------------------------------------
-template <int RB>
-__global__ __launch_bounds__(1024) void w2_reduce32_kernel(const int32_t* __restrict__ topk_ids,
-                                                           const uint8_t* __restrict__ units_base,
-                                                           const uint16_t* __restrict__ act,
-                                                           const float* __restrict__ topk_w,
-                                                           uint16_t* __restrict__ out, uint32_t expert_bytes,
-                                                           uint32_t meta_delta, uint32_t dims, int E) {
-  __shared__ float ys[AWQ_MOE_KMAX_TOPK * 16];     // [rank][16]
-  __shared__ int rk[AWQ_MOE_KMAX_TOPK];            // slot -> rank (-1: invalid slot)
-  __shared__ float wr[AWQ_MOE_KMAX_TOPK];          // rank -> router weight
+template <int RB, int SPW>
+__global__ __launch_bounds__(1024) void w2_reduce_seg_kernel(const int32_t* __restrict__ topk_ids,
+                                                             const uint8_t* __restrict__ units_base,
+                                                             const uint16_t* __restrict__ act,
+                                                             const float* __restrict__ topk_w,
+                                                             uint16_t* __restrict__ out, uint32_t expert_bytes,
+                                                             uint32_t meta_delta, uint32_t dims, int E) {
+  __shared__ __attribute__((aligned(16))) float red[AWQ_MOE_KMAX_TOPK * 8 * 16];  // [slot][g][16]
+  __shared__ __attribute__((aligned(16))) float ys[AWQ_MOE_KMAX_TOPK * 16];       // [rank][16]
+  __shared__ float wr[AWQ_MOE_KMAX_TOPK];                                         // rank -> router weight
   __shared__ int nvalid_s;
-  const int G2 = dims_G2(dims), LS = 4 * G2;  // LS <= 32
+  const int G2 = dims_G2(dims), LS = 4 * G2;  // LS <= 32, SPW * LS <= 64
   const int H = 32 * dims_G(dims), I = 32 * G2, topk = dims_topk(dims);
   const int T2 = H >> 4;
   const int nt = (T2 & 7) ? (int)blockIdx.x : (int)((blockIdx.x & 7) * (T2 >> 3) + (blockIdx.x >> 3));
   const int tok = blockIdx.y;
   const int t = threadIdx.x, lane = t & 63;
+  const int s0 = __builtin_amdgcn_readfirstlane(t >> 6) * SPW;  // the wave's first slot
   const int32_t* ids = topk_ids + tok * topk;
-  // the wave's two slots; indexes clamped into the token's ids (unused past topk)
-  const int w2 = __builtin_amdgcn_readfirstlane(t >> 6) * 2;
-  const int e0 = ids[w2 < topk ? w2 : topk - 1];
-  const int e1 = ids[w2 + 1 < topk ? w2 + 1 : topk - 1];
-  // Every load below is unconditional, with clamped indexes (a dead lane
-  // reads what a live lane of its half reads, inside the bank), so the code
-  // is straight-line and each value is waited for just before its first use
-  // (exec-masked loads measured slower: the waits after the branch cover all
-  // of them). The ranking inputs come first.
+  // the wave's ids and router weights, indexes clamped into the token's slots
+  int ek[SPW];
+  float wk[SPW];
+#pragma unroll
+  for (int k = 0; k < SPW; ++k) {
+    const int sk = s0 + k < topk ? s0 + k : topk - 1;
+    ek[k] = ids[sk];
+    wk[k] = topk_w[tok * topk + sk];
+  }
+  // ranking input: lane j holds slot j's id
   const int rid = ids[lane < topk ? lane : topk - 1];
-  const float wt0 = topk_w[tok * topk + (w2 < topk ? w2 : topk - 1)];
-  const float wt1 = topk_w[tok * topk + (w2 + 1 < topk ? w2 + 1 : topk - 1)];
-  const int slot = t >> 5, tl = t & 31;
-  const bool lane_on = slot < topk && tl < LS;
+  // the lane's slot inside the wave (kk == SPW: a lane past the segments)
+  int kk = 0;
+#pragma unroll
+  for (int k = 1; k <= SPW; ++k) kk += lane >= k * LS;
+  const int tl = lane - kk * LS;  // in [0, LS) for every lane
+  const int slot = s0 + kk;
+  const bool lane_on = kk < SPW && slot < topk;
   const int slotc = slot < topk ? slot : topk - 1;
-  const int tlc = tl < LS ? tl : LS - 1, gc = tlc >> 2, quadc = tlc & 3;
-  const uint4 araw = *reinterpret_cast<const uint4*>(act + (uint64_t)(tok * topk + slotc) * I + 32 * gc + 8 * quadc);
-  const int e = (t & 32) ? e1 : e0;
+  const int g = tl >> 2, quad = tl & 3;
+  const uint4 araw = *reinterpret_cast<const uint4*>(act + (uint64_t)(tok * topk + slotc) * I + 32 * g + 8 * quad);
+  int e = ek[0];
+#pragma unroll
+  for (int k = 1; k < SPW; ++k) e = kk == k ? ek[k] : e;
   const bool valid_e = e >= 0 && e < E;
   const bool live = lane_on && valid_e;
-  float part[4] = {0.f, 0.f, 0.f, 0.f};
   const uint64_t eo = (uint64_t)(uint32_t)(valid_e ? e : 0) * expert_bytes;
   const uint8_t* units = units_base + eo + (uint64_t)nt * 256u * G2;
   const RawRecords<RB> rraw =
-      load_records_raw<RB>(units_base + eo + meta_delta + (uint64_t)nt * 16u * G2 * RB + (uint64_t)tlc * 4u * RB);
+      load_records_raw<RB>(units_base + eo + meta_delta + (uint64_t)nt * 16u * G2 * RB + (uint64_t)tl * 4u * RB);
   uint4 w[4];
 #pragma unroll
-  for (int j = 0; j < 4; ++j) w[j] = *reinterpret_cast<const uint4*>(units + ((uint64_t)j * LS + tlc) * 16u);
+  for (int j = 0; j < 4; ++j) w[j] = *reinterpret_cast<const uint4*>(units + ((uint64_t)j * LS + tl) * 16u);
   // Keep the ranking below the weight loads: it runs while they are in flight.
   __builtin_amdgcn_sched_barrier(0);
-  {
-    // Ranks of the wave's two slots among the token's valid slots by (id,
-    // slot): lane j holds slot j's id, so each rank is the population count
-    // of one ballot against the wave-uniform ids e0 and e1.
-    const bool vj = lane < topk && rid >= 0 && rid < E;
-    const unsigned long long b0 = __ballot(vj && (rid < e0 || (rid == e0 && lane < w2)));
-    const unsigned long long b1 = __ballot(vj && (rid < e1 || (rid == e1 && lane < w2 + 1)));
-    const unsigned long long bv = __ballot(vj);
-    if (lane == 0) {
-      const bool v0 = w2 < topk && e0 >= 0 && e0 < E, v1 = w2 + 1 < topk && e1 >= 0 && e1 < E;
-      const int r0 = (int)__popcll(b0), r1 = (int)__popcll(b1);
-      if (w2 < topk) rk[w2] = v0 ? r0 : -1;
-      if (w2 + 1 < topk) rk[w2 + 1] = v1 ? r1 : -1;
-      if (v0) wr[r0] = wt0;
-      if (v1) wr[r1] = wt1;
-      if (w2 == 0) nvalid_s = (int)__popcll(bv);
-    }
+  // Ranks of the wave's slots among the token's valid slots by (id, slot):
+  // each is the population count of one ballot against a wave-uniform id.
+  const bool vj = lane < topk && rid >= 0 && rid < E;
+  int rk[SPW];
+#pragma unroll
+  for (int k = 0; k < SPW; ++k)
+    rk[k] = (int)__popcll(__ballot(vj && (rid < ek[k] || (rid == ek[k] && lane < s0 + k))));
+  const unsigned long long bv = __ballot(vj);
+  if (lane == 0) {
+#pragma unroll
+    for (int k = 0; k < SPW; ++k)
+      if (s0 + k < topk && ek[k] >= 0 && ek[k] < E) wr[rk[k]] = wk[k];
+    if (s0 == 0) nvalid_s = (int)__popcll(bv);
   }
+  int rank = rk[0];
+#pragma unroll
+  for (int k = 1; k < SPW; ++k) rank = kk == k ? rk[k] : rank;
   // the quad's four 16-byte quarters of the group's activations, to every lane of the quad
   Act32 av;
   av.px[0] = quad_bcast<0>(araw.x); av.px[1] = quad_bcast<0>(araw.y); av.px[2] = quad_bcast<0>(araw.z); av.px[3] = quad_bcast<0>(araw.w);
   av.px[4] = quad_bcast<1>(araw.x); av.px[5] = quad_bcast<1>(araw.y); av.px[6] = quad_bcast<1>(araw.z); av.px[7] = quad_bcast<1>(araw.w);
   av.px[8] = quad_bcast<2>(araw.x); av.px[9] = quad_bcast<2>(araw.y); av.px[10] = quad_bcast<2>(araw.z); av.px[11] = quad_bcast<2>(araw.w);
   av.px[12] = quad_bcast<3>(araw.x); av.px[13] = quad_bcast<3>(araw.y); av.px[14] = quad_bcast<3>(araw.z); av.px[15] = quad_bcast<3>(araw.w);
+  float* rrow = red + (slotc * 8) * 16 + 4 * quad;  // + 16 g: this lane's four columns in group g
   if (live) {
     float S, Cs;
     group_sums(av, S, Cs);
     const Records<RB> rec = decode_records<RB>(rraw);
     const Magic mg = make_magic();
-#pragma unroll
-    for (int j = 0; j < 4; ++j) part[j] = rec.s[j] * (unit_dot(w[j], av, mg) - fmaf(rec.z[j], S, Cs));
+    float4 part;
+    part.x = rec.s[0] * (unit_dot(w[0], av, mg) - fmaf(rec.z[0], S, Cs));
+    part.y = rec.s[1] * (unit_dot(w[1], av, mg) - fmaf(rec.z[1], S, Cs));
+    part.z = rec.s[2] * (unit_dot(w[2], av, mg) - fmaf(rec.z[2], S, Cs));
+    part.w = rec.s[3] * (unit_dot(w[3], av, mg) - fmaf(rec.z[3], S, Cs));
+    *reinterpret_cast<float4*>(rrow + 16 * g) = part;
   }
-  // sum over the groups of the half (lane bits 2..4): rotations by 4 and 8
-  // inside each 16-lane row, then the two rows of the half trade two values
-  // each, so lane l ends with columns 4*(l & 3) + 2*b4 and + 1 (b4 = bit 4).
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    part[j] += dpp<kRowRor4>(part[j]);
-    part[j] += dpp<kRowRor8>(part[j]);
-  }
-  const bool b4 = (lane & 16) != 0;
-  float k0 = b4 ? part[2] : part[0], k1 = b4 ? part[3] : part[1];
-  k0 += __shfl_xor(b4 ? part[0] : part[2], 16);
-  k1 += __shfl_xor(b4 ? part[1] : part[3], 16);
-  __syncthreads();  // rk is ready
-  if ((lane & 12) == 0 && slot < topk) {
-    const int r = rk[slot];
-    if (r >= 0) {
-      const int c = 4 * (lane & 3) + 2 * (int)b4;
-      ys[r * 16 + c] = k0;
-      ys[r * 16 + c + 1] = k1;
+  // the writes above come from this wave only; wait for them (and keep the
+  // compiler from moving the reads below above them)
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  if (live && g == 0) {
+    float4 y = *reinterpret_cast<const float4*>(rrow);
+    for (int gg = 1; gg < G2; ++gg) {
+      const float4 v = *reinterpret_cast<const float4*>(rrow + 16 * gg);
+      y.x += v.x;
+      y.y += v.y;
+      y.z += v.z;
+      y.w += v.w;
     }
+    *reinterpret_cast<float4*>(ys + rank * 16 + 4 * quad) = y;
   }
   __syncthreads();
   if (t < 16) {
@@ -705,21 +713,40 @@ static void launch_w2_t(const StageArgs& a, const uint16_t* act, const float* to
 // One 16-column tile per workgroup: groups of 2 or 4 adjacent tiles (longer
 // contiguous runs per expert) measured no faster, at 4 slower, on hot and
 // on cold weights.
+template <int RB, int SPW>
+static void launch_w2_seg(const StageArgs& a, const uint16_t* act, const float* topk_w, uint16_t* out,
+                          uint32_t md, hipStream_t stream) {
+  const int waves = (a.topk + SPW - 1) / SPW;
+  const dim3 grid(a.H / 16, a.M);
+  hipLaunchKernelGGL((w2_reduce_seg_kernel<RB, SPW>), grid, dim3(64 * waves), 0, stream, a.topk_ids, a.bank + a.w2_off,
+                     act, topk_w, out, (uint32_t)a.expert_bytes, md, pack_dims(a.H, a.I, a.topk, a.M), a.E);
+}
+
+template <int RB>
+static void launch_w2_seg_rb(const StageArgs& a, const uint16_t* act, const float* topk_w, uint16_t* out,
+                             uint32_t md, hipStream_t stream) {
+  // slots per wave: the largest instantiated SPW <= floor(64 / LS), LS = I/8 lanes per slot
+  const int spw = 64 / (a.I / 8);
+  if (spw >= 16) launch_w2_seg<RB, 16>(a, act, topk_w, out, md, stream);
+  else if (spw >= 8) launch_w2_seg<RB, 8>(a, act, topk_w, out, md, stream);
+  else if (spw >= 5) launch_w2_seg<RB, 5>(a, act, topk_w, out, md, stream);
+  else if (spw >= 4) launch_w2_seg<RB, 4>(a, act, topk_w, out, md, stream);
+  else if (spw >= 3) launch_w2_seg<RB, 3>(a, act, topk_w, out, md, stream);
+  else launch_w2_seg<RB, 2>(a, act, topk_w, out, md, stream);
+}
+
+// One 16-column tile per workgroup: groups of 2 or 4 adjacent tiles (longer
+// contiguous runs per expert) measured no faster, at 4 slower, on hot and
+// on cold weights.
 hipError_t launch_w2_reduce(const StageArgs& a, const uint16_t* act, const float* topk_w, uint16_t* out,
                             hipStream_t stream) {
   if (a.I <= 256) {
-    // one 32-lane half per slot, two slots per wave
-    const dim3 block(((a.topk * 32 + 63) / 64) * 64);
-    const dim3 grid(a.H / 16, a.M);
     const uint64_t md = a.w2_meta_off - a.w2_off;
     if (!fits32(a, md)) return hipErrorInvalidValue;
-    const uint32_t dims = pack_dims(a.H, a.I, a.topk, a.M);
     if (a.RB == 4)
-      hipLaunchKernelGGL(w2_reduce32_kernel<4>, grid, block, 0, stream, a.topk_ids, a.bank + a.w2_off, act, topk_w,
-                         out, (uint32_t)a.expert_bytes, (uint32_t)md, dims, a.E);
+      launch_w2_seg_rb<4>(a, act, topk_w, out, (uint32_t)md, stream);
     else
-      hipLaunchKernelGGL(w2_reduce32_kernel<3>, grid, block, 0, stream, a.topk_ids, a.bank + a.w2_off, act, topk_w,
-                         out, (uint32_t)a.expert_bytes, (uint32_t)md, dims, a.E);
+      launch_w2_seg_rb<3>(a, act, topk_w, out, (uint32_t)md, stream);
     return hipGetLastError();
   }
   if (a.RB == 4)

@@ -171,6 +171,9 @@ def test_decode_rank_shape(rb, M, mode):
     (16, 256, 32, 32, 8),      # top-k 32, 256 slots; 4 lanes per slot
     (6, 96, 64, 3, 5),         # hidden 96: 6 column tiles
     (12, 128, 96, 1, 3),       # top-k 1
+    (10, 512, 128, 7, 3),      # W2: 16 lanes per slot, 4 slots per wave
+    (9, 256, 256, 5, 2),       # W2: 32 lanes per slot, 2 slots per wave
+    (7, 160, 224, 3, 4),       # W2: 28 lanes per slot, 2 slots per wave, hidden 160
     (64, 2560, 160, 10, 8),    # a token whose ids are all invalid, next to valid ones
 ])
 def test_decode_other_shapes(E, H, I, k, M):
