@@ -393,6 +393,138 @@ __global__ __launch_bounds__(1024) void w13_swiglu_kernel(const int32_t* __restr
 }
 
 // ---------------------------------------------------------------------------
+// W13 + SwiGLU with each 32-value group split over a lane pair: the same
+// work as w13_swiglu_kernel on twice the lanes (ceil(H/4 / 64) waves, 10 at
+// H = 2560), each with half of every unit (an 8-byte load per column) and
+// half of the group's activations. With 5 waves a lone workgroup leaves one
+// SIMD of its CU with two waves' arithmetic; with 10 the busiest SIMD has
+// three half-waves' worth. Used when the grid has at most one workgroup per
+// CU (M = 1 at the rank shape: 3.68 -> 3.53 us on cold weights). Lane bits: 0 = half, 1..2 = quad, 3..5 = group
+// within the wave. The pair's and the wave's partial sums are combined by a
+// reduce-scatter over lane bits 0 and 3 and sums over bits 4 and 5, in a
+// fixed order, then the waves' sums in LDS in wave order.
+// ---------------------------------------------------------------------------
+// 16 fp16 activations of half a group as 8 packed pairs: px[4d + p] holds
+// (x[8d + 2p], x[8d + 2p + 1]) of the half's dword d (0, 1).
+struct Act16 {
+  uint32_t px[8];
+};
+
+__device__ __forceinline__ Act16 load_act16(const uint16_t* p) {
+  Act16 a;
+  const uint4* q = reinterpret_cast<const uint4*>(p);
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const uint4 v = q[i];
+    a.px[4 * i + 0] = v.x; a.px[4 * i + 1] = v.y; a.px[4 * i + 2] = v.z; a.px[4 * i + 3] = v.w;
+  }
+  return a;
+}
+
+// S and C of group_sums over the half's 16 values.
+__device__ __forceinline__ void half_group_sums(const Act16& a, float& S, float& C) {
+  const uint32_t one2 = 0x3C003C00u;  // fp16 (1.0, 1.0)
+  float s1024 = 0.f, s64 = 0.f;
+#pragma unroll
+  for (int d = 0; d < 2; ++d) {
+    s1024 = dot2(a.px[4 * d + 0], one2, s1024);
+    s64 = dot2(a.px[4 * d + 1], one2, s64);
+    s1024 = dot2(a.px[4 * d + 2], one2, s1024);
+    s64 = dot2(a.px[4 * d + 3], one2, s64);
+  }
+  S = s1024 + s64;
+  C = fmaf(1024.f, s1024, 64.f * s64);
+}
+
+// unit_dot over the half's two dwords.
+__device__ __forceinline__ float half_unit_dot(const uint2& w, const Act16& a, const Magic& mg) {
+  float acc = 0.f;
+  const uint32_t wd[2] = {w.x, w.y};
+#pragma unroll
+  for (int d = 0; d < 2; ++d) {
+    const uint32_t v = wd[d];
+    const uint32_t v8 = v >> 8;
+    acc = dot2(a.px[4 * d + 0], (v & kLoMask) | mg.m1024, acc);
+    acc = dot2(a.px[4 * d + 1], (v & kHiMask) | mg.m64, acc);
+    acc = dot2(a.px[4 * d + 2], (v8 & kLoMask) | mg.m1024, acc);
+    acc = dot2(a.px[4 * d + 3], (v8 & kHiMask) | mg.m64, acc);
+  }
+  return acc;
+}
+
+template <int RB>
+__global__ __launch_bounds__(1024) void w13_swiglu_pair_kernel(const int32_t* __restrict__ ids,
+                                                               const uint8_t* __restrict__ units_base,
+                                                               const uint16_t* __restrict__ x, uint8_t* __restrict__ ws,
+                                                               uint32_t expert_bytes, uint32_t meta_delta,
+                                                               uint32_t dims, int E) {
+  __shared__ float red[16][16];  // [wave][column]
+  const int nt = blockIdx.x, s = blockIdx.y;
+  const int e = ids[s];  // scalar load
+  const int G = dims_G(dims), I = 32 * dims_G2(dims), topk = dims_topk(dims);
+  const int H = 32 * G, L = 4 * G, nwaves = (2 * L + 63) >> 6;
+  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  const int tu = t >> 1, hf = t & 1;  // unit lane (4g + quad) and half
+  const int g = tu >> 2;
+  const bool status_wave = nt == 0 && s == 0 && wave == 0;
+  const int n = topk * dims_M(dims);  // <= 256 slots: four per lane of one wave
+  int sid[4];
+  if (status_wave) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) sid[q] = lane + 64 * q < n ? ids[lane + 64 * q] : 0;
+  }
+  Act16 av;
+  if (tu < L) av = load_act16(x + (uint64_t)(s / topk) * H + 32 * g + 16 * hf);
+  const bool live = e >= 0 && e < E;
+  const uint64_t eo = (uint64_t)(uint32_t)e * expert_bytes;
+  uint2 w[4];
+  RawRecords<RB> rraw;
+  if (live && tu < L) {
+    const uint8_t* units = units_base + eo + (uint64_t)nt * 256u * G + 8u * hf;
+    rraw = load_records_raw<RB>(units_base + eo + meta_delta + (uint64_t)nt * 16u * G * RB + (uint64_t)tu * 4u * RB);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) w[j] = *reinterpret_cast<const uint2*>(units + ((uint64_t)j * L + tu) * 16u);
+  }
+  if (status_wave) {
+    bool bad = false;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) bad |= lane + 64 * q < n && (sid[q] < 0 || sid[q] >= E);
+    const unsigned long long b = __ballot(bad);
+    if (lane == 0) *reinterpret_cast<uint32_t*>(ws + AWQ_MOE_KWS_STATUS_OFFSET) = b ? AWQ_MOE_STATUS_BAD_ID_BIT : 0u;
+  }
+  if (!live) return;  // invalid slot: no row (uniform over the workgroup)
+  float p0 = 0.f, p1 = 0.f, p2 = 0.f, p3 = 0.f;
+  if (tu < L) {
+    float S, Cs;
+    half_group_sums(av, S, Cs);
+    const Records<RB> rec = decode_records<RB>(rraw);
+    const Magic mg = make_magic();
+    p0 = rec.s[0] * (half_unit_dot(w[0], av, mg) - fmaf(rec.z[0], S, Cs));
+    p1 = rec.s[1] * (half_unit_dot(w[1], av, mg) - fmaf(rec.z[1], S, Cs));
+    p2 = rec.s[2] * (half_unit_dot(w[2], av, mg) - fmaf(rec.z[2], S, Cs));
+    p3 = rec.s[3] * (half_unit_dot(w[3], av, mg) - fmaf(rec.z[3], S, Cs));
+  }
+  // reduce-scatter over lane bit 0 (the pair): bit 0 keeps columns j = 2 b0, 2 b0 + 1
+  const bool b0 = lane & 1, b3 = (lane >> 3) & 1;
+  const float ka = (b0 ? p2 : p0) + dpp<kQuadSwap1>(b0 ? p0 : p2);
+  const float kb = (b0 ? p3 : p1) + dpp<kQuadSwap1>(b0 ? p1 : p3);
+  // over lane bit 3: keeps column j = 2 b0 + b3
+  float k = (b3 ? kb : ka) + dpp<kRowRor8>(b3 ? ka : kb);
+  // over lane bits 4 and 5
+  k += __shfl_xor(k, 16);
+  k += __shfl_xor(k, 32);
+  if (lane < 16) red[wave][4 * ((lane >> 1) & 3) + 2 * (int)b0 + (int)b3] = k;
+  __syncthreads();
+  if (t < 16) {
+    float h = 0.f;
+    for (int wv = 0; wv < nwaves; ++wv) h += red[wv][t];
+    const float other = __shfl_xor(h, 1);  // partner column: gate <-> up
+    uint16_t* act = reinterpret_cast<uint16_t*>(ws + AWQ_MOE_KWS_ACT_OFFSET);
+    if (!(t & 1)) act[(uint64_t)s * I + nt * 8 + (t >> 1)] = __builtin_bit_cast(uint16_t, (_Float16)silu_mul(h, other));
+  }
+}
+
+// ---------------------------------------------------------------------------
 // W2 + router-weighted reduction: grid (H/(16*TPW) column groups, M tokens).
 // The workgroup of (group, token) streams TPW adjacent 16-column W2 tiles
 // (one contiguous run per expert, all of K = I) of each of the token's
@@ -687,10 +819,23 @@ hipError_t launch_w13_swiglu(const StageArgs& a, const uint16_t* x, void* ws, hi
   const uint64_t md = a.w13_meta_off - a.w13_off;
   if (!fits32(a, md)) return hipErrorInvalidValue;
   const int L = 4 * (a.H / 32);
-  const dim3 block(((L + 63) / 64) * 64);
   const dim3 grid((2 * a.I) / 16, a.M * a.topk);
   const uint32_t dims = pack_dims(a.H, a.I, a.topk, a.M);
   uint8_t* w = static_cast<uint8_t*>(ws);
+  // Lane pairs when every workgroup has a CU to itself (MI355X: 256 CUs), where
+  // the busiest SIMD sets the time; with more workgroups the pair kernel's
+  // 8-byte loads cost more than it saves (M = 8: 7.6 -> 9.3 us).
+  if (2 * L <= 1024 && (uint64_t)grid.x * grid.y <= 256) {
+    const dim3 block(((2 * L + 63) / 64) * 64);
+    if (a.RB == 4)
+      hipLaunchKernelGGL(w13_swiglu_pair_kernel<4>, grid, block, 0, stream, a.topk_ids, a.bank + a.w13_off, x, w,
+                         (uint32_t)a.expert_bytes, (uint32_t)md, dims, a.E);
+    else
+      hipLaunchKernelGGL(w13_swiglu_pair_kernel<3>, grid, block, 0, stream, a.topk_ids, a.bank + a.w13_off, x, w,
+                         (uint32_t)a.expert_bytes, (uint32_t)md, dims, a.E);
+    return hipGetLastError();
+  }
+  const dim3 block(((L + 63) / 64) * 64);
   if (a.RB == 4)
     hipLaunchKernelGGL(w13_swiglu_kernel<4>, grid, block, 0, stream, a.topk_ids, a.bank + a.w13_off, x, w,
                        (uint32_t)a.expert_bytes, (uint32_t)md, dims, a.E);
