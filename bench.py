@@ -356,11 +356,26 @@ def cpu_baseline(bi, ids_calls, rng_seed, budget_s=12.0):
             "layer_us": round(dt / done * 1e6, 1)}
 
 
+def stage_kernel_names(M, H=H, I=I, topk=K_TOP, rb=4):
+    """Names of the W13 and W2 kernels the library launches for a shape (the
+    launchers' rules: lane pairs for W13 when every workgroup has a CU of its
+    own, W2 slot segments of I/8 lanes at inter <= 256)."""
+    pair = 2 * (H // 8) <= 1024 and (2 * I // 16) * M * topk <= 256
+    w13 = f"w13_swiglu_pair_kernel<{rb}>" if pair else f"w13_swiglu_kernel<{rb}>"
+    if I <= 256:
+        spw = 64 // (I // 8)
+        spw = max(v for v in (2, 3, 4, 5, 8, 16) if v <= spw)
+        w2 = f"w2_reduce_seg_kernel<{rb}, {spw}>"
+    else:
+        w2 = f"w2_reduce_kernel<{rb}, 1>"
+    return w13, w2
+
+
 def roofline(head):
     """HBM roofline of the longer of the two stage kernels at the headline workload."""
     k = "w2" if head["w2_us"] >= head["w13_us"] else "w13"
-    # at inter <= 256 the W2 launch is the two-slots-per-wave kernel
-    name = {"w13": "w13_swiglu_kernel<4>", "w2": "w2_reduce32_kernel<4>" if I <= 256 else "w2_reduce_kernel<4, 1>"}[k]
+    w13_name, w2_name = stage_kernel_names(head["M"])
+    name = {"w13": w13_name, "w2": w2_name}[k]
     gbs = head[k + "_gbs"]
     return {
         "bound": "hbm",
