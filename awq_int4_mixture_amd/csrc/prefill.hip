@@ -292,39 +292,57 @@ __device__ __forceinline__ void lds_operand(const uint32_t* __restrict__ wl, con
 
 // ---------------------------------------------------------------------------
 // W13 + SwiGLU: grid (2I/16 column tiles, work items), 4 waves. The tile is
-// staged in chunks of up to 40 groups (16-byte loads into LDS); within a
-// chunk wave w takes the groups gl = w, w + 4, ... in batches of kW13Batch:
+// staged in chunks of up to 80 groups (all of K at hidden 2560): the weight
+// runs go straight from the bank into LDS (global_load_lds_dwordx4, lane i
+// of a load at LDS base + 16 i; wave j copies run j), the records through
+// registers as dwords, and the workgroup waits once per chunk. Within a
+// chunk wave w takes the groups gl = w, w + 4, ... in batches (5 groups for
+// items of up to 16 rows, 2 for two-tile items):
 // a batch's activation loads are issued together (unconditionally, from
 // clamped groups) and then consumed, so a wave waits once per batch while
 // few registers stay live. Groups past the chunk get a zero scale. At the
 // end the waves' partial tiles are summed in LDS in wave order. Gate and up
 // of intermediate i are columns 2i and 2i + 1, i.e. neighbouring lanes.
 // ---------------------------------------------------------------------------
-constexpr int kW13Chunk = 40;
-constexpr int kW13Batch = 2;
+constexpr int kW13Chunk = 80;
 constexpr int kW13PerWave = kW13Chunk / 4;
-constexpr int kW13Pieces = (16 * kW13Chunk + 255) / 256;
+// Groups per batch of activation loads (one memory round trip per batch);
+// a single-tile item needs half the registers per group. The LDS of a
+// workgroup already limits a SIMD to 6 waves, so up to ~85 VGPRs are free
+// (5 and 2: 78 VGPRs; 5 and 4 measured no better, 10 and 5 take 125).
+constexpr int w13_batch(int nrt) { return nrt == 2 ? 2 : 5; }
 constexpr int kW13WlDw = 4 * run_stride(kW13Chunk);
-static_assert(kW13PerWave % kW13Batch == 0, "batches tile the wave's groups");
-static_assert(kW13Pieces <= 5 && kW13Chunk * 4 <= 256, "staging capacity (record quads: one per thread)");
+constexpr int kW13RecPieces = (4 * kW13Chunk + 255) / 256;  // record quads per thread
+static_assert(kW13PerWave % w13_batch(1) == 0 && kW13PerWave % w13_batch(2) == 0, "batches tile the wave's groups");
+static_assert(kW13RecPieces <= 2, "record staging capacity");
 static_assert(kW13WlDw >= 4 * 2 * 64 * 4, "the partial tiles reuse the weight buffer");
+
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef __attribute__((address_space(1))) const void glb_void_t;
+
+// 16 bytes per lane from global memory straight into LDS, lane i at
+// lds_base + 16 i (lds_base is the same for the whole wave).
+__device__ __forceinline__ void lds_direct16(const uint8_t* src, uint32_t* lds_base) {
+  __builtin_amdgcn_global_load_lds((glb_void_t*)src, (lds_void_t*)lds_base, 16, 0, 0);
+}
 
 template <int RB, int NRT>
 __device__ __forceinline__ void w13_chunk(const uint32_t* wl, const uint8_t* rl, const uint16_t* __restrict__ xr0,
                                           const uint16_t* __restrict__ xr1, int g0, int kc, int wave, int quad,
                                           int j, int kb, uint32_t m1024, f4_t& acc0, f4_t& acc1) {
   constexpr int rs = run_stride(kW13Chunk);
+  constexpr int kB = w13_batch(NRT);
 #pragma unroll 1
-  for (int i0 = 0; i0 < kW13PerWave; i0 += kW13Batch) {
-    h8_t a0[kW13Batch], a1[kW13Batch];
+  for (int i0 = 0; i0 < kW13PerWave; i0 += kB) {
+    h8_t a0[kB], a1[kB];
 #pragma unroll
-    for (int u = 0; u < kW13Batch; ++u) {
+    for (int u = 0; u < kB; ++u) {
       const int g = g0 + min(wave + 4 * (i0 + u), kc - 1);
       a0[u] = *reinterpret_cast<const h8_t*>(xr0 + 32 * g + 8 * kb);
       if constexpr (NRT == 2) a1[u] = *reinterpret_cast<const h8_t*>(xr1 + 32 * g + 8 * kb);
     }
 #pragma unroll
-    for (int u = 0; u < kW13Batch; ++u) {
+    for (int u = 0; u < kB; ++u) {
       const int gl = wave + 4 * (i0 + u);
       h8_t b;
       float sc;
@@ -363,15 +381,53 @@ __global__ __launch_bounds__(256) void prefill_w13_kernel(const int32_t* __restr
   const uint16_t* xr0 = x + (uint64_t)(row_slot[row0 + min(c, rows - 1)] / topk) * H;
   const uint16_t* xr1 = x + (uint64_t)(row_slot[row0 + min(16 + c, rows - 1)] / topk) * H;
   f4_t acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
-  // one chunk ahead: the next chunk's loads are in flight while this one is computed
-  Stager<RB, kW13Chunk, kW13Pieces> st;
-  st.issue(units, recs, G, 1, 0, min(kW13Chunk, G), 0, 0);
+  constexpr int rs = run_stride(kW13Chunk);
   for (int g0 = 0; g0 < G; g0 += kW13Chunk) {
     const int kc = min(kW13Chunk, G - g0);
     if (g0 > 0) __syncthreads();  // the previous chunk's LDS reads are done
-    st.store(wl, rl);
+    {
+      // run j = wave: 4 kc units of 16 bytes, 64 per load
+      const uint8_t* src = units + (uint64_t)wave * 64 * G + 64 * g0;
+      uint32_t* dst = wl + wave * rs;
+      for (int i = 0; 64 * i < 4 * kc; ++i) {
+        const int u = 64 * i + lane;
+        if (u < 4 * kc) lds_direct16(src + 16 * u, dst + 256 * i);
+      }
+    }
+    // records: every load is issued (a piece past the chunk rereads the run's
+    // first quad) before any is converted to dwords
+    typedef uint32_t u32x3 __attribute__((ext_vector_type(3), aligned(4)));
+    u32x3 rv[kW13RecPieces];
+    int rd[kW13RecPieces];
+#pragma unroll
+    for (int q = 0; q < kW13RecPieces; ++q) {
+      const Piece pc = record_piece<RB, kW13Chunk>((int)threadIdx.x + 256 * q, 1, G, g0, kc, 0);
+      rv[q] = *reinterpret_cast<const u32x3*>(recs + (pc.on ? pc.src : 0));
+      rd[q] = pc.on ? pc.dst : -1;
+    }
+    uint32_t rw[kW13RecPieces];  // the fourth dword of a 4-byte record quad
+    if constexpr (RB == 4) {
+#pragma unroll
+      for (int q = 0; q < kW13RecPieces; ++q) {
+        const Piece pc = record_piece<RB, kW13Chunk>((int)threadIdx.x + 256 * q, 1, G, g0, kc, 0);
+        rw[q] = *reinterpret_cast<const uint32_t*>(recs + (pc.on ? pc.src : 0) + 12);
+      }
+    }
+#pragma unroll
+    for (int q = 0; q < kW13RecPieces; ++q) {
+      if (rd[q] < 0) continue;
+      const u32x3 d = rv[q];
+      uint4 v;
+      if constexpr (RB == 4) {
+        v = make_uint4(d.x, d.y, d.z, rw[q]);
+      } else {
+        v = make_uint4(d.x & 0xFFFFFFu, (d.x >> 24) | ((d.y & 0xFFFFu) << 8), (d.y >> 16) | ((d.z & 0xFFu) << 16),
+                       d.z >> 8);
+      }
+      *reinterpret_cast<uint4*>(rl + rd[q]) = v;
+    }
+    // the barrier waits for every load of the workgroup, the LDS-direct ones included
     __syncthreads();
-    if (g0 + kW13Chunk < G) st.issue(units, recs, G, 1, g0 + kW13Chunk, min(kW13Chunk, G - g0 - kW13Chunk), 0, 0);
     if (nrt == 2)
       w13_chunk<RB, 2>(wl, rl, xr0, xr1, g0, kc, wave, quad, j, kb, m1024, acc0, acc1);
     else
