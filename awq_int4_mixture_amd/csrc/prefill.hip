@@ -176,8 +176,9 @@ __device__ __forceinline__ void item_of(const int32_t* __restrict__ items, int i
 
 // ---------------------------------------------------------------------------
 // Weight staging. A chunk of kc groups of T adjacent column tiles is copied
-// from the bank into LDS with 16-byte loads, all issued before the first LDS
-// write. In the bank a tile holds, for each j = column % 4, a run of 4G
+// from the bank straight into LDS (global_load_lds_dwordx4: 16 bytes per
+// lane, lane i at the wave's LDS base + 16 i), the records through registers
+// as dwords. In the bank a tile holds, for each j = column % 4, a run of 4G
 // units ordered (group, quad); the chunk is the units of groups
 // [g0, g0 + kc) of each run and the records of those groups, which are
 // contiguous. In LDS the runs are padded to a stride of 16 (mod 64) dwords,
@@ -186,25 +187,14 @@ __device__ __forceinline__ void item_of(const int32_t* __restrict__ items, int i
 // ---------------------------------------------------------------------------
 constexpr int run_stride(int kc) { return 16 * kc + ((16 - 16 * kc) % 64 + 64) % 64; }
 
-// Piece p of a chunk: 16 bytes of tile tt at bank offset src and LDS offset
-// dst. Pieces are numbered against the full chunk size KC (compile-time
-// divisors); a shorter last chunk leaves the pieces past kc groups off.
+// A record piece of a chunk: bank offset src and LDS offset dst. Pieces are
+// numbered against the full chunk size KC (compile-time divisors); a shorter
+// last chunk leaves the pieces past kc groups off.
 struct Piece {
   bool on;
   uint64_t src;
   int dst;
 };
-
-template <int KC>
-__device__ __forceinline__ Piece weight_piece(int p, int T, int G, int g0, int kc, int tile_dw) {
-  constexpr int kPerTile = 16 * KC, kRun = 4 * KC;
-  const int tt = p / kPerTile, rem = p - tt * kPerTile, j = rem / kRun, u = rem - j * kRun;
-  Piece r;
-  r.on = tt < T && u < 4 * kc;
-  r.src = (uint64_t)tt * 256 * G + (uint64_t)j * 64 * G + 64 * g0 + 16 * u;
-  r.dst = 4 * (tt * tile_dw + j * run_stride(KC) + 4 * u);  // bytes
-  return r;
-}
 
 // Record piece p: 4 consecutive records (12 or 16 bytes, 4-byte aligned) of
 // tile tt, stored in LDS as 4 dwords (a 3-byte record becomes its 4-byte
@@ -232,53 +222,6 @@ __device__ __forceinline__ uint4 load_records4(const uint8_t* __restrict__ base,
                       d.z >> 8);
   }
 }
-
-__device__ __forceinline__ uint4 load_piece(const uint8_t* __restrict__ base, const Piece& pc) {
-  return pc.on ? *reinterpret_cast<const uint4*>(base + pc.src) : make_uint4(0, 0, 0, 0);
-}
-
-// A chunk's staging in two halves: issue() requests up to 5 * 256 weight
-// pieces and 256 record pieces; store() writes them to LDS (and so waits for
-// them). Other work can run in between; only the LDS destinations (-1: no
-// piece) and the data stay in registers.
-template <int RB, int KC, int MAXW, int NTHREADS = 256>
-struct Stager {
-  int d0, d1, d2, d3, d4, dr;
-  uint4 v0, v1, v2, v3, v4, vr;
-
-  __device__ __forceinline__ static int fetch(const uint8_t* __restrict__ base, const Piece& pc, uint4& v) {
-    v = load_piece(base, pc);
-    return pc.on ? pc.dst : -1;
-  }
-
-  __device__ __forceinline__ void issue(const uint8_t* __restrict__ units, const uint8_t* __restrict__ recs, int G,
-                                        int T, int g0, int kc, int tile_dw, int tile_rb) {
-    static_assert(MAXW >= 1 && MAXW <= 5, "pieces per thread");
-    const int t = threadIdx.x;
-    d0 = fetch(units, weight_piece<KC>(t, T, G, g0, kc, tile_dw), v0);
-    if constexpr (MAXW > 1) d1 = fetch(units, weight_piece<KC>(t + NTHREADS, T, G, g0, kc, tile_dw), v1);
-    if constexpr (MAXW > 2) d2 = fetch(units, weight_piece<KC>(t + 2 * NTHREADS, T, G, g0, kc, tile_dw), v2);
-    if constexpr (MAXW > 3) d3 = fetch(units, weight_piece<KC>(t + 3 * NTHREADS, T, G, g0, kc, tile_dw), v3);
-    if constexpr (MAXW > 4) d4 = fetch(units, weight_piece<KC>(t + 4 * NTHREADS, T, G, g0, kc, tile_dw), v4);
-    const Piece prc = record_piece<RB, KC>(t, T, G, g0, kc, tile_rb);
-    vr = load_records4<RB>(recs, prc);
-    dr = prc.on ? prc.dst : -1;
-  }
-
-  __device__ __forceinline__ static void put(uint8_t* lds, int d, const uint4& v) {
-    if (d >= 0) *reinterpret_cast<uint4*>(lds + d) = v;
-  }
-
-  __device__ __forceinline__ void store(uint32_t* __restrict__ wl, uint8_t* __restrict__ rl) const {
-    uint8_t* wb = reinterpret_cast<uint8_t*>(wl);
-    put(wb, d0, v0);
-    if constexpr (MAXW > 1) put(wb, d1, v1);
-    if constexpr (MAXW > 2) put(wb, d2, v2);
-    if constexpr (MAXW > 3) put(wb, d3, v3);
-    if constexpr (MAXW > 4) put(wb, d4, v4);
-    put(rl, dr, vr);
-  }
-};
 
 // Operand of lane (column c = 4 quad + j, block kb) for chunk-local group gl.
 template <int RB>
@@ -458,11 +401,15 @@ __global__ __launch_bounds__(256) void prefill_w13_kernel(const int32_t* __restr
 // ---------------------------------------------------------------------------
 // W2: grid (ceil(H/16 / 8) column blocks, work items), 4 waves. The 8 tiles
 // of the block are staged in chunks of up to 5 groups (all of K at inter
-// 160), the activations of the chunk are requested first, and wave w takes
-// tiles w and w + 4 over the chunk's groups, writing fp32 row results.
+// 160) with LDS-direct loads, the activations of the chunk are requested
+// with them, and wave w takes tiles w and w + 4 over the chunk's groups,
+// writing fp32 row results.
 // ---------------------------------------------------------------------------
 constexpr int kW2Chunk = 5;
 constexpr int kW2TileDw = 4 * run_stride(kW2Chunk);
+constexpr int kW2TileUnits = 16 * kW2Chunk;                // 16-byte units of a staged tile
+constexpr int kW2Loads = (8 * kW2TileUnits + 63) / 64;     // 64-unit LDS-direct loads per block
+static_assert(run_stride(kW2Chunk) == 4 * 4 * kW2Chunk, "W2 runs are unpadded, so a block is one contiguous LDS run");
 
 template <int RB, int NRT>
 __device__ __forceinline__ void w2_block(const uint8_t* __restrict__ units, const uint8_t* __restrict__ recs,
@@ -474,8 +421,20 @@ __device__ __forceinline__ void w2_block(const uint8_t* __restrict__ units, cons
   constexpr int rs = run_stride(kW2Chunk);
   for (int g0 = 0; g0 < G; g0 += kW2Chunk) {
     const int kc = min(kW2Chunk, G - g0);
-    Stager<RB, kW2Chunk, 3> st;
-    st.issue(units, recs, G, T, g0, kc, kW2TileDw, 16 * kW2Chunk * 4);
+    if (g0 > 0) __syncthreads();  // the previous chunk's LDS reads are done
+    // weights: the chunk's 8 tiles x 4 runs x 4 kc units lie contiguously in
+    // LDS (the runs need no padding), 64 units per LDS-direct load, each lane
+    // with its own bank address
+#pragma unroll
+    for (int i = wave; i < kW2Loads; i += 4) {
+      const int up = 64 * i + lane;
+      const int tt = up / kW2TileUnits, rem = up - tt * kW2TileUnits;
+      const int jr = rem / (4 * kW2Chunk), u = rem - jr * (4 * kW2Chunk);
+      if (tt < T && u < 4 * kc)
+        lds_direct16(units + (uint64_t)tt * 256 * G + (uint64_t)jr * 64 * G + 64 * g0 + 16 * u, wl + 256 * i);
+    }
+    const Piece prc = record_piece<RB, kW2Chunk>((int)threadIdx.x, T, G, g0, kc, 16 * kW2Chunk * 4);
+    const uint4 vr = load_records4<RB>(recs, prc);
     h8_t a0[kW2Chunk], a1[kW2Chunk];
 #pragma unroll
     for (int i = 0; i < kW2Chunk; ++i) {
@@ -483,8 +442,8 @@ __device__ __forceinline__ void w2_block(const uint8_t* __restrict__ units, cons
       a0[i] = *reinterpret_cast<const h8_t*>(ar0 + 32 * g + 8 * kb);
       if constexpr (NRT == 2) a1[i] = *reinterpret_cast<const h8_t*>(ar1 + 32 * g + 8 * kb);
     }
-    if (g0 > 0) __syncthreads();
-    st.store(wl, rl);
+    if (prc.on) *reinterpret_cast<uint4*>(rl + prc.dst) = vr;
+    // the barrier waits for every load of the workgroup, the LDS-direct ones included
     __syncthreads();
 #pragma unroll
     for (int i = 0; i < kW2Chunk; ++i) {
