@@ -34,6 +34,7 @@ namespace awq_moe {
 typedef float f4_t __attribute__((ext_vector_type(4)));
 
 constexpr int kItemRows = 32;
+constexpr int kRouteBatch = 16;  // slot ids per thread in flight in the routing kernel
 
 // ---------------------------------------------------------------------------
 // routing: counts, row offsets per expert, work items, row of every slot.
@@ -53,12 +54,24 @@ __global__ __launch_bounds__(1024) void prefill_route_kernel(const int32_t* __re
   for (int e = t; e < E; e += 1024) cnt[e] = 0;
   if (t == 0) bad = 0;
   __syncthreads();
-  for (int s = t; s < n; s += 1024) {
-    const int e = ids[s];
-    if (e >= 0 && e < E)
-      atomicAdd(&cnt[e], 1);
-    else
-      bad = 1;
+  // The slots are read kRouteBatch per thread at a time, every load issued
+  // before the first is used: one memory round trip per batch, not per slot.
+  for (int s0 = t; s0 < n; s0 += kRouteBatch * 1024) {
+    int ev[kRouteBatch];
+#pragma unroll
+    for (int b = 0; b < kRouteBatch; ++b) {
+      const int s = s0 + 1024 * b;
+      ev[b] = s < n ? ids[s] : 0;
+    }
+#pragma unroll
+    for (int b = 0; b < kRouteBatch; ++b) {
+      if (s0 + 1024 * b >= n) break;
+      const int e = ev[b];
+      if (e >= 0 && e < E)
+        atomicAdd(&cnt[e], 1);
+      else
+        bad = 1;
+    }
   }
   __syncthreads();
   int c4[4], r4[4], i4[4], rs = 0, is = 0;
@@ -104,14 +117,25 @@ __global__ __launch_bounds__(1024) void prefill_route_kernel(const int32_t* __re
   if (t == 1023) *num_items = ib + is;
   if (t == 0) *status = bad ? AWQ_MOE_STATUS_BAD_ID_BIT : 0u;
   __syncthreads();
-  for (int s = t; s < n; s += 1024) {
-    const int e = ids[s];
-    if (e >= 0 && e < E) {
-      const int r = atomicAdd(&cur[e], 1);
-      slot_row[s] = r;
-      row_slot[r] = s;
-    } else {
-      slot_row[s] = -1;
+  for (int s0 = t; s0 < n; s0 += kRouteBatch * 1024) {
+    int ev[kRouteBatch];
+#pragma unroll
+    for (int b = 0; b < kRouteBatch; ++b) {
+      const int s = s0 + 1024 * b;
+      ev[b] = s < n ? ids[s] : 0;
+    }
+#pragma unroll
+    for (int b = 0; b < kRouteBatch; ++b) {
+      const int s = s0 + 1024 * b;
+      if (s >= n) break;
+      const int e = ev[b];
+      if (e >= 0 && e < E) {
+        const int r = atomicAdd(&cur[e], 1);
+        slot_row[s] = r;
+        row_slot[r] = s;
+      } else {
+        slot_row[s] = -1;
+      }
     }
   }
 }
