@@ -423,6 +423,128 @@ __global__ __launch_bounds__(256) void prefill_w13_kernel(const int32_t* __restr
 }
 
 // ---------------------------------------------------------------------------
+// W13 + SwiGLU for calls with many rows per expert: grid (ceil(NT/4) groups
+// of 4 column tiles, work items), 4 waves; wave w owns tile 4 q + w over
+// all of K, so an activation row staged once serves four tiles. Per chunk
+// of kMtChunk groups everything goes straight into LDS with LDS-direct
+// loads: the item's activations as [group][k block][row][16 B] (a load of
+// 64 lanes is 2 k blocks x 32 rows of one group, and an MFMA operand read
+// is 1 KB contiguous), the four tiles' weight runs at a stride of
+// kMtRun units (48 mod 64 dwords, so operand reads hit 64 banks; pad units
+// are lanes that load nothing), the records through registers as dwords.
+// Each wave keeps its tile's sums in registers to the end (no cross-wave
+// reduction), then applies SwiGLU.
+// ---------------------------------------------------------------------------
+constexpr int kMtChunk = 10;
+constexpr int kMtMinTokens = 512;  // calls from this many tokens take the multi-tile W13 kernel
+constexpr int kMtRun = 44;  // units per weight run in LDS (4 * kMtChunk = 40 used)
+constexpr int kMtAUnits = kMtChunk * 4 * 32;       // 16-byte activation units per chunk
+constexpr int kMtBUnits = 16 * kMtRun;             // 4 tiles x 4 runs
+constexpr int kMtBLoads = (kMtBUnits + 63) / 64;
+constexpr int kMtRecDw = 16 * kMtChunk;            // record dwords per tile and chunk
+static_assert((4 * kMtRun) % 64 == 48 && kMtRun >= 4 * kMtChunk, "weight runs: 64 banks, room for a chunk");
+static_assert(4 * 4 * kMtChunk <= 256, "record quads: one per thread");
+
+template <int RB>
+__global__ __launch_bounds__(256) void prefill_w13_mt_kernel(const int32_t* __restrict__ items,
+                                                             const int32_t* __restrict__ num_items,
+                                                             const int32_t* __restrict__ row_slot,
+                                                             const uint8_t* __restrict__ bank,
+                                                             const uint16_t* __restrict__ x, uint64_t expert_bytes,
+                                                             uint64_t units_off, uint64_t meta_off, int H, int I,
+                                                             int topk, uint16_t* __restrict__ act) {
+  __shared__ __attribute__((aligned(16))) uint32_t al[kMtAUnits * 4];
+  __shared__ __attribute__((aligned(16))) uint32_t bl[kMtBUnits * 4];
+  __shared__ __attribute__((aligned(16))) uint32_t rl[4 * kMtRecDw];
+  int it, tq;
+  xcd_item_tile(it, tq);
+  if (it >= *num_items) return;
+  int e, row0, rows;
+  item_of(items, it, e, row0, rows);
+  const int G = H >> 5, NT = (2 * I) >> 4;
+  const uint32_t m1024 = magic1024();
+  const int t = threadIdx.x, lane = t & 63, wave = __builtin_amdgcn_readfirstlane(t >> 6);
+  const int c = lane & 15, kb = lane >> 4, quad = c >> 2, j = c & 3;
+  const int nt0 = 4 * tq, T = min(4, NT - nt0);
+  const uint8_t* blk = bank + (uint64_t)e * expert_bytes;
+  const uint8_t* units = blk + units_off + (uint64_t)nt0 * 256 * G;
+  const uint8_t* recs = blk + meta_off + (uint64_t)nt0 * 16 * G * RB;
+  const int nrt = rows > 16 ? 2 : 1;
+  // the activation row this lane copies (row = lane & 31; rows past the item repeat its last row)
+  const int arow = lane & 31;
+  const uint16_t* xrow = x + (uint64_t)(row_slot[row0 + min(arow, rows - 1)] / topk) * H + 8 * (lane >> 5);
+  f4_t acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
+  for (int g0 = 0; g0 < G; g0 += kMtChunk) {
+    const int kc = min(kMtChunk, G - g0);
+    if (g0 > 0) __syncthreads();  // the previous chunk's LDS reads are done
+    // activations: load m = 2 gl + h covers k blocks 2h, 2h + 1 of group gl for rows 0..31
+    for (int m = wave; m < 2 * kc; m += 4) {
+      const int gl = m >> 1, h = m & 1;
+      if (arow < 16 * nrt)
+        lds_direct16(reinterpret_cast<const uint8_t*>(xrow + 32 * (g0 + gl) + 16 * h), al + 256 * m);
+    }
+    // weights: unit position p = (tile * 4 + j) * kMtRun + u
+#pragma unroll
+    for (int i = wave; i < kMtBLoads; i += 4) {
+      const int pos = 64 * i + lane;
+      const int tj = pos / kMtRun, u = pos - tj * kMtRun;
+      const int tt = tj >> 2, jr = tj & 3;
+      if (tt < T && u < 4 * kc)
+        lds_direct16(units + (uint64_t)tt * 256 * G + (uint64_t)jr * 64 * G + 64 * g0 + 16 * u, bl + 256 * i);
+    }
+    // records: quad r of tile tt (4 records of group r / 4), as dwords
+    {
+      const int tt = t / (4 * kMtChunk), rem = t - tt * (4 * kMtChunk);
+      const bool on = tt < T && rem < 4 * kc;
+      typedef uint32_t u32x3 __attribute__((ext_vector_type(3), aligned(4)));
+      const uint8_t* rp = recs + (on ? (uint64_t)tt * 16 * G * RB + (16 * g0 + 4 * rem) * RB : 0);
+      const u32x3 d = *reinterpret_cast<const u32x3*>(rp);
+      uint4 v;
+      if constexpr (RB == 4) {
+        v = make_uint4(d.x, d.y, d.z, *reinterpret_cast<const uint32_t*>(rp + 12));
+      } else {
+        v = make_uint4(d.x & 0xFFFFFFu, (d.x >> 24) | ((d.y & 0xFFFFu) << 8), (d.y >> 16) | ((d.z & 0xFFu) << 16),
+                       d.z >> 8);
+      }
+      if (on) *reinterpret_cast<uint4*>(rl + tt * kMtRecDw + 4 * rem) = v;
+    }
+    // the barrier waits for every load of the workgroup, the LDS-direct ones included
+    __syncthreads();
+    if (wave < T) {
+      const uint32_t* bw = bl + wave * 4 * kMtRun * 4;
+      const uint32_t* rw = rl + wave * kMtRecDw;
+      for (int gl = 0; gl < kc; ++gl) {
+        const uint32_t w = bw[(j * kMtRun + 4 * gl + quad) * 4 + kb];
+        const uint32_t r = rw[16 * gl + 4 * quad + j];
+        const float sc = (float)__builtin_bit_cast(_Float16, (uint16_t)(r & 0xFFFFu));
+        const h8_t b = qz_operand(w, (r >> 16) & 0xFFu, m1024);
+        const h8_t a0 = *reinterpret_cast<const h8_t*>(al + ((gl * 4 + kb) * 32 + c) * 4);
+        scale_add(acc0, sc, mfma16(a0, b));
+        if (nrt == 2) {
+          const h8_t a1 = *reinterpret_cast<const h8_t*>(al + ((gl * 4 + kb) * 32 + 16 + c) * 4);
+          scale_add(acc1, sc, mfma16(a1, b));
+        }
+      }
+    }
+  }
+  if (wave >= T) return;
+  const int nt = nt0 + wave;
+  for (int rt = 0; rt < nrt; ++rt) {
+    const f4_t d = rt == 0 ? acc0 : acc1;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float up = dpp<kQuadSwap1>(d[i]);  // column c ^ 1
+      const int row = 16 * rt + 4 * kb + i;
+      if (!(c & 1) && row < rows) {
+        const float g = d[i];
+        const float a = g / (1.0f + __expf(-g)) * up;
+        act[(uint64_t)(row0 + row) * I + nt * 8 + (c >> 1)] = __builtin_bit_cast(uint16_t, (_Float16)a);
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
 // W2: grid (ceil(H/16 / 8) column blocks, work items), 4 waves. The 8 tiles
 // of the block are staged in chunks of up to 5 groups (all of K at inter
 // 160) with LDS-direct loads, the activations of the chunk are requested
@@ -595,7 +717,16 @@ hipError_t launch_prefill(const StageArgs& a, const uint16_t* x, const float* to
   if (err != hipSuccess) return err;
   const int items8 = (max_items + 7) / 8 * 8;  // whole XCD rounds (see xcd_item_tile)
   const dim3 g13((2 * a.I) / 16, items8), g2(((a.H / 16) + 7) / 8, items8);
-  if (a.RB == 4) {
+  if (a.M >= kMtMinTokens) {
+    // many rows per expert: four tiles per workgroup share the staged activations
+    const dim3 g13m(((2 * a.I) / 16 + 3) / 4, items8);
+    if (a.RB == 4)
+      hipLaunchKernelGGL(prefill_w13_mt_kernel<4>, g13m, dim3(256), 0, stream, w.items, w.num_items, w.row_slot, a.bank,
+                         x, a.expert_bytes, a.w13_off, a.w13_meta_off, a.H, a.I, a.topk, w.act);
+    else
+      hipLaunchKernelGGL(prefill_w13_mt_kernel<3>, g13m, dim3(256), 0, stream, w.items, w.num_items, w.row_slot, a.bank,
+                         x, a.expert_bytes, a.w13_off, a.w13_meta_off, a.H, a.I, a.topk, w.act);
+  } else if (a.RB == 4) {
     hipLaunchKernelGGL(prefill_w13_kernel<4>, g13, dim3(256), 0, stream, w.items, w.num_items, w.row_slot, a.bank, x,
                        a.expert_bytes, a.w13_off, a.w13_meta_off, a.H, a.I, a.topk, w.act);
   } else {

@@ -45,6 +45,9 @@ def check(got, want, what):
     (64, 2560, 160, 10, 127, 3),   # rank shape with 64 experts, ~20 rows each
     (4, 8192, 32, 2, 9, 3),        # hidden 8192: 256 W13 groups, 64 per wave
     (16, 256, 32, 2, 4096, 3),     # the largest M: 8192 slots, ~512 rows per expert
+    (16, 352, 64, 4, 600, 4),      # four tiles per W13 workgroup: 11 groups (a chunk of 10 and one of 1), 2 tile groups
+    (40, 2560, 160, 10, 512, 3),   # four tiles per W13 workgroup at the rank shape: 8 chunks, ~128 rows per expert
+    (8, 8192, 32, 2, 520, 3),      # four tiles per W13 workgroup, hidden 8192: 26 chunks, the last of 6 groups
 ])
 def test_prefill_shapes(E, H, I, k, M, rb):
     dims, bank, bi = bank_case(60 + I, E, H, I, rb)
@@ -58,7 +61,7 @@ def test_prefill_shapes(E, H, I, k, M, rb):
 
 
 @pytest.mark.parametrize("rb", [3, 4])
-@pytest.mark.parametrize("M", [9, 128])
+@pytest.mark.parametrize("M", [9, 128, 512])
 def test_prefill_rank_shape_full_bank(rb, M):
     """The decode benchmark's layer (512 experts, hidden 2560, inter 160,
     top-k 10) with M tokens that pick their experts independently."""
