@@ -436,7 +436,7 @@ __global__ __launch_bounds__(256) void prefill_w13_kernel(const int32_t* __restr
 // reduction), then applies SwiGLU.
 // ---------------------------------------------------------------------------
 constexpr int kMtChunk = 10;
-constexpr int kMtMinTokens = 512;  // calls from this many tokens take the multi-tile W13 kernel
+constexpr int kMtMinTokens = 256;  // calls from this many tokens take the multi-tile W13 kernel (M = 128: 114 against 119 us; M = 256: even)
 constexpr int kMtRun = 44;  // units per weight run in LDS (4 * kMtChunk = 40 used)
 constexpr int kMtAUnits = kMtChunk * 4 * 32;       // 16-byte activation units per chunk
 constexpr int kMtBUnits = 16 * kMtRun;             // 4 tiles x 4 runs

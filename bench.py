@@ -45,7 +45,7 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=200)
     p.add_argument("--warmup", type=int, default=20)
-    p.add_argument("--only", default="", help="comma list of workloads: m1_hot,m1_cold,m8_pool,m8_distinct,p128,p1024,p4096,stack48,stack48_gemv")
+    p.add_argument("--only", default="", help="comma list of workloads: m1_hot,m1_cold,m8_pool,m8_distinct,p128,p256,p512,p1024,p4096,stack48,stack48_gemv")
     p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     return p.parse_args()
 
@@ -400,7 +400,7 @@ def main():
     from awq_int4_mixture_amd import abi
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     torch.cuda.set_device(0)
-    prefill_wls = {"p128": 128, "p1024": 1024, "p4096": 4096}
+    prefill_wls = {"p128": 128, "p256": 256, "p512": 512, "p1024": 1024, "p4096": 4096}
     only = set(filter(None, args.only.split(","))) or {"m1_hot", "m1_cold", "m8_pool", "m8_distinct", "stack48",
                                                        "stack48_gemv", *prefill_wls}
 
