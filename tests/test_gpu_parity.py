@@ -174,6 +174,8 @@ def test_decode_rank_shape(rb, M, mode):
     (10, 512, 128, 7, 3),      # W2: 16 lanes per slot, 4 slots per wave
     (9, 256, 256, 5, 2),       # W2: 32 lanes per slot, 2 slots per wave
     (7, 160, 224, 3, 4),       # W2: 28 lanes per slot, 2 slots per wave, hidden 160
+    (6, 4096, 64, 2, 1),       # W13 lane pairs at their largest block: 1024 threads, 16 waves
+    (5, 8192, 32, 3, 1),       # M = 1 but hidden 8192: pairs would need 2048 threads, single-lane W13
     (64, 2560, 160, 10, 8),    # a token whose ids are all invalid, next to valid ones
 ])
 def test_decode_other_shapes(E, H, I, k, M):
