@@ -160,9 +160,11 @@ __global__ __launch_bounds__(1024) void residual_rmsnorm_kernel(const uint16_t* 
   residual_finish(rr, delta != nullptr, H, eps, r_next + o, x + o);
 }
 
-// Both per-token steps between two stacked layers in one launch: the
-// residual rows' loads are issued first, the router runs while they are in
-// flight, then the norm finishes.
+// Both per-token steps between two stacked layers in one launch, as two
+// workgroups per token (blockIdx.y: 0 the router, 1 the residual update and
+// norm) so that the two chains run side by side. The block is the same for
+// both roles; the norm's extra waves add zero partial sums, so its result is
+// bit-identical to residual_rmsnorm_kernel's.
 __global__ __launch_bounds__(1024) void router_residual_kernel(const float* __restrict__ logits, int E, int k,
                                                                int32_t* __restrict__ ids, float* __restrict__ w,
                                                                const uint16_t* __restrict__ r,
@@ -170,10 +172,13 @@ __global__ __launch_bounds__(1024) void router_residual_kernel(const float* __re
                                                                uint16_t* __restrict__ r_next,
                                                                uint16_t* __restrict__ x) {
   const int tok = blockIdx.x;
-  const uint64_t o = (uint64_t)tok * H;
-  const ResRow rr = residual_load(r + o, delta ? delta + o : nullptr, H);
-  router_topk_row(logits + (uint64_t)tok * E, E, k, ids + tok * k, w + tok * k);
-  residual_finish(rr, delta != nullptr, H, eps, r_next + o, x + o);
+  if (blockIdx.y == 0) {
+    router_topk_row(logits + (uint64_t)tok * E, E, k, ids + tok * k, w + tok * k);
+  } else {
+    const uint64_t o = (uint64_t)tok * H;
+    const ResRow rr = residual_load(r + o, delta ? delta + o : nullptr, H);
+    residual_finish(rr, delta != nullptr, H, eps, r_next + o, x + o);
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -341,7 +346,7 @@ hipError_t launch_router_residual(const float* logits, int M, int E, int k, int3
   const int rt = ((H / 8 + 63) / 64) * 64;
   if (rt > threads) threads = rt;
   if (threads > 1024) threads = 1024;
-  hipLaunchKernelGGL(router_residual_kernel, dim3(M), dim3(threads), 0, stream, logits, E, k, ids, w, r, delta, H,
+  hipLaunchKernelGGL(router_residual_kernel, dim3(M, 2), dim3(threads), 0, stream, logits, E, k, ids, w, r, delta, H,
                      eps, r_next, x);
   return hipGetLastError();
 }
