@@ -345,11 +345,41 @@ def test_batch_independence_within_tolerance():
     say("batch-independent tokens (bit-equal)", same, "of", M)
 
 
-def test_graph_capture_replays_match_eager():
+def test_decode_back_to_back_on_one_workspace_equals_stage_pair():
+    """Calls in a row on one workspace with changing inputs (a stale act would
+    show): each equals the two stage entry points bit for bit and the oracle
+    within tolerance, with the status word set only by the call that has
+    invalid ids."""
+    H, I = RANK
+    E, k = 64, 10
+    dims, bank, bi = bank_case(7, E, H, I, 3)
+    dec = abi.Decoder(dims, bank, k)
+    for c in range(8):
+        rng = inputs.call_rng(14, c)
+        M = 1 if c % 2 == 0 else 3
+        x = inputs.activations(rng, M, H)
+        ids = inputs.ids_distinct(rng, M, k, E)
+        if c == 4:
+            ids[0, 2], ids[0, 6] = -1, E      # invalid ids: no row, status bit 0
+        if c == 6:
+            ids[0, :] = ids[0, 0]             # one expert in every slot
+        w = inputs.router_weights(rng, M, k)
+        say("back-to-back decode call", c, "M", M)
+        got = f16_to_np(dec(to_dev(x), to_dev(ids), to_dev(w)))
+        assert dec.status() == (abi.STATUS_BAD_ID if c == 4 else 0)
+        ws = abi.awq_moe_w13_swiglu(dims, bank, to_dev(x), to_dev(ids))
+        pair = abi.awq_moe_w2_reduce(dims, bank, to_dev(ids), to_dev(w), ws)
+        torch.cuda.synchronize()
+        assert got.view(np.uint16).tolist() == f16_to_np(pair).view(np.uint16).tolist(), c
+        check(got, R.moe_stage(x, ids, w, E, bi.expert), f"back-to-back call {c}")
+
+
+@pytest.mark.parametrize("M", [1, 2])
+def test_graph_capture_replays_match_eager(M):
     H, I = RANK
     dims, bank, bi = bank_case(7, 64, H, I, 3)
     rng = inputs.call_rng(13, 0)
-    M, k = 2, 10
+    k = 10
     x = to_dev(inputs.activations(rng, M, H))
     ids = to_dev(inputs.ids_shared_pool(rng, M, k, 64))
     w = to_dev(inputs.router_weights(rng, M, k))
