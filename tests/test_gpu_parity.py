@@ -194,6 +194,21 @@ def test_decode_other_shapes(E, H, I, k, M):
     check(got, want, f"shape E={E} H={H} I={I} k={k} M={M}")
 
 
+def test_decode_largest_hidden_and_inter_together():
+    """Hidden 8192 with inter 2048, the admitted maxima together, top-k 32
+    over 4 experts (each token routes to every expert several times), M = 2:
+    the single-lane W13 kernel at its 16 waves and the W2 kernel for
+    inter > 256 at their largest strides."""
+    E, H, I, k, M = 4, 8192, 2048, 32, 2
+    dims, bank, bi = bank_case(90, E, H, I, 3)
+    rng = inputs.call_rng(91, 0)
+    x = inputs.activations(rng, M, H)
+    ids = rng.integers(0, E, size=(M, k)).astype(np.int32)
+    w = inputs.router_weights(rng, M, k)
+    say("largest hidden and inter", E, H, I, k, M)
+    check(run_decode(dims, bank, x, ids, w), R.moe_stage(x, ids, w, E, bi.expert), "largest hidden and inter")
+
+
 def test_decode_full_bank_rank_shape_m1_and_m8():
     """The benchmark's layer: E=512, hidden 2560, inter 160, top-k 10, 3-byte records."""
     H, I = RANK

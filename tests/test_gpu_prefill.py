@@ -48,6 +48,7 @@ def check(got, want, what):
     (16, 352, 64, 4, 600, 4),      # four tiles per W13 workgroup: 11 groups (a chunk of 10 and one of 1), 2 tile groups
     (40, 2560, 160, 10, 512, 3),   # four tiles per W13 workgroup at the rank shape: 8 chunks, ~128 rows per expert
     (8, 8192, 32, 2, 520, 3),      # four tiles per W13 workgroup, hidden 8192: 26 chunks, the last of 6 groups
+    (4, 8192, 2048, 4, 9, 3),      # hidden 8192 with inter 2048 (the maxima together), single-tile W13
 ])
 def test_prefill_shapes(E, H, I, k, M, rb):
     dims, bank, bi = bank_case(60 + I, E, H, I, rb)
@@ -58,6 +59,23 @@ def test_prefill_shapes(E, H, I, k, M, rb):
     say("prefill shape", E, H, I, k, M, rb)
     check(run_prefill(dims, bank, x, ids, w), R.moe_stage(x, ids, w, E, bi.expert),
           f"prefill E={E} H={H} I={I} k={k} M={M} rb={rb}")
+
+
+def test_prefill_largest_hidden_and_inter_sampled():
+    """Hidden 8192 with inter 2048 at M = 300 (four tiles per W13
+    workgroup, ~300 rows per expert: ten items each, 26 chunks of groups):
+    the oracle on 12 sampled tokens, the first and last among them (a
+    token's result depends only on its own (id, weight) pairs)."""
+    E, H, I, k, M = 4, 8192, 2048, 4, 300
+    dims, bank, bi = bank_case(92, E, H, I, 4)
+    rng = inputs.call_rng(93, 0)
+    x = inputs.activations(rng, M, H)
+    ids = inputs.ids_distinct(rng, M, k, E)
+    w = inputs.router_weights(rng, M, k)
+    say("prefill largest hidden and inter", E, H, I, k, M)
+    got = run_prefill(dims, bank, x, ids, w)
+    sel = np.unique(np.concatenate([[0, M - 1], rng.choice(np.arange(1, M - 1), 10, replace=False)]))
+    check(got[sel], R.moe_stage(x[sel], ids[sel], w[sel], E, bi.expert), "prefill largest hidden and inter")
 
 
 @pytest.mark.parametrize("rb", [3, 4])
