@@ -430,19 +430,22 @@ __global__ __launch_bounds__(256) void prefill_w13_kernel(const int32_t* __restr
 // loads: the item's activations as [group][k block][row][16 B] (a load of
 // 64 lanes is 2 k blocks x 32 rows of one group, and an MFMA operand read
 // is 1 KB contiguous), the four tiles' weight runs at a stride of
-// kMtRun units (48 mod 64 dwords, so operand reads hit 64 banks; pad units
-// are lanes that load nothing), the records through registers as dwords.
+// kMtRun units (16 or 48 mod 64 dwords, so operand reads hit 64 banks; pad
+// units, if any, are lanes that load nothing), the records through
+// registers as dwords. Chunks of 8 groups keep the LDS at 27 KB, so five
+// workgroups fit on a CU (10 groups, 34 KB: four).
 // Each wave keeps its tile's sums in registers to the end (no cross-wave
 // reduction), then applies SwiGLU.
 // ---------------------------------------------------------------------------
-constexpr int kMtChunk = 10;
+constexpr int kMtChunk = 8;
 constexpr int kMtMinTokens = 256;  // calls from this many tokens take the multi-tile W13 kernel (M = 128: 114 against 119 us; M = 256: even)
-constexpr int kMtRun = 44;  // units per weight run in LDS (4 * kMtChunk = 40 used)
+constexpr int kMtRun = 36;  // units per weight run in LDS (4 * kMtChunk = 32 used)
 constexpr int kMtAUnits = kMtChunk * 4 * 32;       // 16-byte activation units per chunk
 constexpr int kMtBUnits = 16 * kMtRun;             // 4 tiles x 4 runs
 constexpr int kMtBLoads = (kMtBUnits + 63) / 64;
 constexpr int kMtRecDw = 16 * kMtChunk;            // record dwords per tile and chunk
-static_assert((4 * kMtRun) % 64 == 48 && kMtRun >= 4 * kMtChunk, "weight runs: 64 banks, room for a chunk");
+static_assert(((4 * kMtRun) % 64 == 16 || (4 * kMtRun) % 64 == 48) && kMtRun >= 4 * kMtChunk,
+              "weight runs: 64 banks, room for a chunk");
 static_assert(4 * 4 * kMtChunk <= 256, "record quads: one per thread");
 
 template <int RB>
