@@ -438,7 +438,10 @@ __global__ __launch_bounds__(256) void prefill_w13_kernel(const int32_t* __restr
 // reduction), then applies SwiGLU.
 // ---------------------------------------------------------------------------
 constexpr int kMtChunk = 8;
-constexpr int kMtMinTokens = 256;  // calls from this many tokens take the multi-tile W13 kernel (M = 128: 114 against 119 us; M = 256: even)
+// Calls from this many tokens take the multi-tile W13 kernel. Single-tile
+// against multi-tile, us per call: M = 32: 62.2 / 63.6, M = 64: 88.1 / 91.4,
+// M = 128: 113.8 / 112.9 (even); from M = 256 the multi-tile kernel is ahead.
+constexpr int kMtMinTokens = 256;
 constexpr int kMtRun = 36;  // units per weight run in LDS (4 * kMtChunk = 32 used)
 constexpr int kMtAUnits = kMtChunk * 4 * 32;       // 16-byte activation units per chunk
 constexpr int kMtBUnits = 16 * kMtRun;             // 4 tiles x 4 runs
