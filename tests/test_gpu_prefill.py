@@ -78,6 +78,22 @@ def test_prefill_largest_hidden_and_inter_sampled():
     check(got[sel], R.moe_stage(x[sel], ids[sel], w[sel], E, bi.expert), "prefill largest hidden and inter")
 
 
+def test_prefill_maximum_experts_topk_tokens_sampled():
+    """4096 experts, top-k 32 and 4096 tokens (131,072 slots, the admitted
+    maxima), hidden 256, inter 32: the oracle on 16 sampled tokens, the
+    first and last among them."""
+    E, H, I, k, M = 4096, 256, 32, 32, 4096
+    dims, bank, bi = bank_case(94, E, H, I, 3)
+    rng = inputs.call_rng(95, 0)
+    x = inputs.activations(rng, M, H)
+    ids = inputs.ids_distinct(rng, M, k, E)
+    w = inputs.router_weights(rng, M, k)
+    say("prefill maximum experts, top-k and tokens", E, k, M)
+    got = run_prefill(dims, bank, x, ids, w)
+    sel = np.unique(np.concatenate([[0, M - 1], rng.choice(np.arange(1, M - 1), 14, replace=False)]))
+    check(got[sel], R.moe_stage(x[sel], ids[sel], w[sel], E, bi.expert), "prefill maximum experts, top-k, tokens")
+
+
 @pytest.mark.parametrize("rb", [3, 4])
 @pytest.mark.parametrize("M", [9, 128, 512])
 def test_prefill_rank_shape_full_bank(rb, M):
@@ -194,7 +210,8 @@ def _pad256(b):
 
 
 @pytest.mark.parametrize("E,k,M,hot", [(16, 4, 128, False), (512, 10, 128, False), (8, 2, 300, True),
-                                       (64, 10, 9, False)])
+                                       (64, 10, 9, False),
+                                       (4096, 32, 4096, False)])  # the admitted maxima: 131,072 slots
 def test_prefill_routing_arrays(E, k, M, hot):
     """The routing arrays in the workspace (layout as documented in the
     header). Unique parts, bit-exact against the oracle's compaction: the
