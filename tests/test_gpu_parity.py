@@ -177,6 +177,7 @@ def test_decode_rank_shape(rb, M, mode):
     (6, 4096, 64, 2, 1),       # W13 lane pairs at their largest block: 1024 threads, 16 waves
     (5, 8192, 32, 3, 1),       # M = 1 but hidden 8192: pairs would need 2048 threads, single-lane W13
     (64, 2560, 160, 10, 8),    # a token whose ids are all invalid, next to valid ones
+    (4096, 256, 32, 32, 8),    # 4096 experts, top-k 32, M = 8: 256 slots, expert offsets past 32 MB
 ])
 def test_decode_other_shapes(E, H, I, k, M):
     dims, bank, bi = bank_case(40 + I, E, H, I, 3)
