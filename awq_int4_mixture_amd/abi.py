@@ -68,12 +68,12 @@ def _load() -> ctypes.CDLL:
         "awq_moe_prepare": [D, P, P, P, P, P, P, P, P, P, P, U64],
         "awq_moe_workspace_bytes": [D, I32, I32, ctypes.POINTER(ctypes.c_uint64)],
         "awq_moe_route_compact": [P, I32, I32, I32, P, P, P, P, P, V],
-        "awq_moe_decode": [D, P, P, P, P, I32, I32, P, P, U64, V],
+        "awq_moe_decode": [D, P, U64, P, P, P, I32, I32, P, P, U64, V],
         "awq_moe_prefill_workspace_bytes": [D, I32, I32, ctypes.POINTER(ctypes.c_uint64)],
-        "awq_moe_prefill": [D, P, P, P, P, I32, I32, P, P, U64, V],
-        "awq_moe_w13_swiglu": [D, P, P, P, I32, I32, P, U64, V],
-        "awq_moe_w2_reduce": [D, P, P, P, I32, I32, P, U64, P, V],
-        "awq_moe_dequant": [D, P, I32, I32, I32, P, V],
+        "awq_moe_prefill": [D, P, U64, P, P, P, I32, I32, P, P, U64, V],
+        "awq_moe_w13_swiglu": [D, P, U64, P, P, I32, I32, P, U64, V],
+        "awq_moe_w2_reduce": [D, P, U64, P, P, I32, I32, P, U64, P, V],
+        "awq_moe_dequant": [D, P, U64, I32, I32, I32, P, V],
         "awq_moe_router_topk": [P, I32, I32, I32, P, P, V],
         "awq_moe_residual_rmsnorm": [P, P, I32, I32, ctypes.c_float, P, P, V],
         "awq_moe_router_residual": [P, I32, I32, I32, P, P, P, P, I32, ctypes.c_float, P, P, V],
@@ -220,7 +220,8 @@ def awq_moe_decode(dims: awq_moe_dims, bank, x, topk_ids, topk_w, out=None, work
     if workspace is None:
         workspace = alloc_workspace(dims, M, k, x.device)
     _check(_lib.awq_moe_decode(
-        ctypes.byref(dims), _dev(bank, torch.uint8, name="bank"), _dev(x, torch.float16, (M, dims.hidden), "x"),
+        ctypes.byref(dims), _dev(bank, torch.uint8, name="bank"), bank.numel(),
+        _dev(x, torch.float16, (M, dims.hidden), "x"),
         _dev(topk_ids, torch.int32, (M, k), "topk_ids"), _dev(topk_w, torch.float32, (M, k), "topk_w"), M, k,
         _dev(out, torch.float16, (M, dims.hidden), "out"), _dev(workspace, torch.uint8, name="workspace"),
         workspace.numel(), _stream(stream)), "awq_moe_decode")
@@ -250,7 +251,8 @@ def awq_moe_prefill(dims: awq_moe_dims, bank, x, topk_ids, topk_w, out=None, wor
     if workspace is None:
         workspace = alloc_prefill_workspace(dims, M, k, x.device)
     _check(_lib.awq_moe_prefill(
-        ctypes.byref(dims), _dev(bank, torch.uint8, name="bank"), _dev(x, torch.float16, (M, dims.hidden), "x"),
+        ctypes.byref(dims), _dev(bank, torch.uint8, name="bank"), bank.numel(),
+        _dev(x, torch.float16, (M, dims.hidden), "x"),
         _dev(topk_ids, torch.int32, (M, k), "topk_ids"), _dev(topk_w, torch.float32, (M, k), "topk_w"), M, k,
         _dev(out, torch.float16, (M, dims.hidden), "out"), _dev(workspace, torch.uint8, name="workspace"),
         workspace.numel(), _stream(stream)), "awq_moe_prefill")
@@ -277,8 +279,8 @@ def awq_moe_w13_swiglu(dims: awq_moe_dims, bank, x, topk_ids, workspace=None, st
     if workspace is None:
         workspace = alloc_workspace(dims, M, k, x.device)
     _check(_lib.awq_moe_w13_swiglu(
-        ctypes.byref(dims), _dev(bank, torch.uint8, name="bank"), _dev(x, torch.float16, (M, dims.hidden), "x"),
-        _dev(topk_ids, torch.int32, (M, k), "topk_ids"), M, k,
+        ctypes.byref(dims), _dev(bank, torch.uint8, name="bank"), bank.numel(),
+        _dev(x, torch.float16, (M, dims.hidden), "x"), _dev(topk_ids, torch.int32, (M, k), "topk_ids"), M, k,
         _dev(workspace, torch.uint8, name="workspace"), workspace.numel(), _stream(stream)), "awq_moe_w13_swiglu")
     return workspace
 
@@ -290,7 +292,8 @@ def awq_moe_w2_reduce(dims: awq_moe_dims, bank, topk_ids, topk_w, workspace, out
     if out is None:
         out = torch.empty((M, dims.hidden), dtype=torch.float16, device=topk_w.device)
     _check(_lib.awq_moe_w2_reduce(
-        ctypes.byref(dims), _dev(bank, torch.uint8, name="bank"), _dev(topk_ids, torch.int32, (M, k), "topk_ids"),
+        ctypes.byref(dims), _dev(bank, torch.uint8, name="bank"), bank.numel(),
+        _dev(topk_ids, torch.int32, (M, k), "topk_ids"),
         _dev(topk_w, torch.float32, (M, k), "topk_w"), M, k, _dev(workspace, torch.uint8, name="workspace"),
         workspace.numel(), _dev(out, torch.float16, (M, dims.hidden), "out"), _stream(stream)), "awq_moe_w2_reduce")
     return out
@@ -301,7 +304,7 @@ def awq_moe_dequant(dims: awq_moe_dims, bank, expert_begin: int, expert_count: i
     K, N = (dims.hidden, 2 * dims.inter) if which == 0 else (dims.inter, dims.hidden)
     if out is None:
         out = torch.empty((expert_count, K, N), dtype=torch.float32, device=bank.device)
-    _check(_lib.awq_moe_dequant(ctypes.byref(dims), _dev(bank, torch.uint8, name="bank"), expert_begin,
+    _check(_lib.awq_moe_dequant(ctypes.byref(dims), _dev(bank, torch.uint8, name="bank"), bank.numel(), expert_begin,
                                 expert_count, which, _dev(out, torch.float32, (expert_count, K, N), "out"),
                                 _stream(stream)), "awq_moe_dequant")
     return out

@@ -140,6 +140,74 @@ int check_route_ptrs(const int32_t* ids, const int32_t* offsets, const int32_t* 
   return AWQ_MOE_OK;
 }
 
+int check_router_args(const float* logits, int32_t M, int32_t num_experts, int32_t topk, const int32_t* topk_ids,
+                      const float* topk_w) {
+  if (M < 1 || M > AWQ_MOE_MAX_TOKENS) return fail(AWQ_MOE_EINVAL, "M %d outside [1, %d]", M, AWQ_MOE_MAX_TOKENS);
+  if (num_experts < 1 || num_experts > AWQ_MOE_MAX_ROUTER_EXPERTS)
+    return fail(AWQ_MOE_EINVAL, "num_experts %d outside [1, %d]", num_experts, AWQ_MOE_MAX_ROUTER_EXPERTS);
+  if (topk < 1 || topk > AWQ_MOE_MAX_TOPK || topk > num_experts)
+    return fail(AWQ_MOE_EINVAL, "topk %d outside [1, min(%d, num_experts)]", topk, AWQ_MOE_MAX_TOPK);
+  if (!logits || !aligned(logits, 4)) return fail(AWQ_MOE_EINVAL, "logits null or misaligned");
+  if (!topk_ids || !aligned(topk_ids, 4)) return fail(AWQ_MOE_EINVAL, "topk_ids null or misaligned");
+  if (!topk_w || !aligned(topk_w, 4)) return fail(AWQ_MOE_EINVAL, "topk_w null or misaligned");
+  return AWQ_MOE_OK;
+}
+
+int check_residual_args(const uint16_t* r, const uint16_t* delta, int32_t M, int32_t hidden, float eps,
+                        const uint16_t* r_next, const uint16_t* x) {
+  if (M < 1 || M > AWQ_MOE_MAX_TOKENS) return fail(AWQ_MOE_EINVAL, "M %d outside [1, %d]", M, AWQ_MOE_MAX_TOKENS);
+  if (hidden < 8 || hidden > AWQ_MOE_MAX_HIDDEN || hidden % 8)
+    return fail(AWQ_MOE_EINVAL, "hidden %d: a multiple of 8 in [8, %d]", hidden, AWQ_MOE_MAX_HIDDEN);
+  if (!(eps > 0.f) || eps > 1.f) return fail(AWQ_MOE_EINVAL, "eps must be in (0, 1]");
+  if (!r || !r_next || !x || !aligned(r, 16) || !aligned(r_next, 16) || !aligned(x, 16) ||
+      (delta && !aligned(delta, 16)))
+    return fail(AWQ_MOE_EINVAL, "row pointer null or not 16-byte aligned");
+  const uint64_t nb = (uint64_t)M * hidden * 2;
+  auto overlap = [nb](const void* a, const void* b) {
+    const uintptr_t pa = reinterpret_cast<uintptr_t>(a), pb = reinterpret_cast<uintptr_t>(b);
+    return b && pa < pb + nb && pb < pa + nb;
+  };
+  if (overlap(r_next, r) || overlap(r_next, delta) || overlap(x, r) || overlap(x, delta) || overlap(x, r_next))
+    return fail(AWQ_MOE_EINVAL, "r_next and x must not overlap r, delta or each other");
+  return AWQ_MOE_OK;
+}
+
+// The bank must hold every expert block of dims: the kernels index experts
+// by id up to num_experts - 1 and never see the allocation's size.
+int check_bank(const awq_moe_dims* dims, const void* bank, uint64_t bank_bytes) {
+  if (!bank || !aligned(bank, 256)) return fail(AWQ_MOE_EINVAL, "bank null or not 256-byte aligned");
+  const uint64_t need = make_layout(dims).pub.total_bytes;
+  if (bank_bytes < need)
+    return fail(AWQ_MOE_ENOSPC, "bank_bytes %llu < %llu (the layout of dims)", (unsigned long long)bank_bytes,
+                (unsigned long long)need);
+  return AWQ_MOE_OK;
+}
+
+int check_stage(const awq_moe_dims* dims, const void* bank, uint64_t bank_bytes, int32_t M, int32_t topk,
+                const void* workspace, uint64_t workspace_bytes) {
+  int rc = check_dims(dims);
+  if (rc) return rc;
+  if ((rc = check_tokens(M, topk))) return rc;
+  if ((rc = check_bank(dims, bank, bank_bytes))) return rc;
+  if (!workspace || !aligned(workspace, 256)) return fail(AWQ_MOE_EINVAL, "workspace null or not 256-byte aligned");
+  const uint64_t need = ws_total(dims, M, topk);
+  if (workspace_bytes < need)
+    return fail(AWQ_MOE_ENOSPC, "workspace_bytes %llu < %llu", (unsigned long long)workspace_bytes,
+                (unsigned long long)need);
+  return AWQ_MOE_OK;
+}
+
+struct WsPtrs {
+  uint32_t* status;
+  uint16_t* act;
+};
+
+WsPtrs ws_ptrs(const void* workspace) {
+  uint8_t* ws = static_cast<uint8_t*>(const_cast<void*>(workspace));
+  return WsPtrs{reinterpret_cast<uint32_t*>(ws + AWQ_MOE_WS_STATUS_OFFSET),
+                reinterpret_cast<uint16_t*>(ws + AWQ_MOE_WS_ACT_OFFSET)};
+}
+
 }  // namespace
 
 extern "C" {
@@ -266,38 +334,6 @@ int awq_moe_route_compact(const int32_t* topk_ids, int32_t M, int32_t topk, int3
                     "route_compact launch");
 }
 
-int check_router_args(const float* logits, int32_t M, int32_t num_experts, int32_t topk, const int32_t* topk_ids,
-                      const float* topk_w) {
-  if (M < 1 || M > AWQ_MOE_MAX_TOKENS) return fail(AWQ_MOE_EINVAL, "M %d outside [1, %d]", M, AWQ_MOE_MAX_TOKENS);
-  if (num_experts < 1 || num_experts > AWQ_MOE_MAX_ROUTER_EXPERTS)
-    return fail(AWQ_MOE_EINVAL, "num_experts %d outside [1, %d]", num_experts, AWQ_MOE_MAX_ROUTER_EXPERTS);
-  if (topk < 1 || topk > AWQ_MOE_MAX_TOPK || topk > num_experts)
-    return fail(AWQ_MOE_EINVAL, "topk %d outside [1, min(%d, num_experts)]", topk, AWQ_MOE_MAX_TOPK);
-  if (!logits || !aligned(logits, 4)) return fail(AWQ_MOE_EINVAL, "logits null or misaligned");
-  if (!topk_ids || !aligned(topk_ids, 4)) return fail(AWQ_MOE_EINVAL, "topk_ids null or misaligned");
-  if (!topk_w || !aligned(topk_w, 4)) return fail(AWQ_MOE_EINVAL, "topk_w null or misaligned");
-  return AWQ_MOE_OK;
-}
-
-int check_residual_args(const uint16_t* r, const uint16_t* delta, int32_t M, int32_t hidden, float eps,
-                        const uint16_t* r_next, const uint16_t* x) {
-  if (M < 1 || M > AWQ_MOE_MAX_TOKENS) return fail(AWQ_MOE_EINVAL, "M %d outside [1, %d]", M, AWQ_MOE_MAX_TOKENS);
-  if (hidden < 8 || hidden > AWQ_MOE_MAX_HIDDEN || hidden % 8)
-    return fail(AWQ_MOE_EINVAL, "hidden %d: a multiple of 8 in [8, %d]", hidden, AWQ_MOE_MAX_HIDDEN);
-  if (!(eps > 0.f) || eps > 1.f) return fail(AWQ_MOE_EINVAL, "eps must be in (0, 1]");
-  if (!r || !r_next || !x || !aligned(r, 16) || !aligned(r_next, 16) || !aligned(x, 16) ||
-      (delta && !aligned(delta, 16)))
-    return fail(AWQ_MOE_EINVAL, "row pointer null or not 16-byte aligned");
-  const uint64_t nb = (uint64_t)M * hidden * 2;
-  auto overlap = [nb](const void* a, const void* b) {
-    const uintptr_t pa = reinterpret_cast<uintptr_t>(a), pb = reinterpret_cast<uintptr_t>(b);
-    return b && pa < pb + nb && pb < pa + nb;
-  };
-  if (overlap(r_next, r) || overlap(r_next, delta) || overlap(x, r) || overlap(x, delta) || overlap(x, r_next))
-    return fail(AWQ_MOE_EINVAL, "r_next and x must not overlap r, delta or each other");
-  return AWQ_MOE_OK;
-}
-
 int awq_moe_router_topk(const float* logits, int32_t M, int32_t num_experts, int32_t topk, int32_t* topk_ids,
                         float* topk_w, void* stream) {
   int rc = check_router_args(logits, M, num_experts, topk, topk_ids, topk_w);
@@ -345,34 +381,10 @@ int awq_moe_router_gemv(const uint16_t* r, const uint16_t* delta, int32_t M, int
                     "router_gemv launch");
 }
 
-int check_stage(const awq_moe_dims* dims, const void* bank, int32_t M, int32_t topk, const void* workspace,
-                uint64_t workspace_bytes) {
-  int rc = check_dims(dims);
-  if (rc) return rc;
-  if ((rc = check_tokens(M, topk))) return rc;
-  if (!bank || !aligned(bank, 256)) return fail(AWQ_MOE_EINVAL, "bank null or not 256-byte aligned");
-  if (!workspace || !aligned(workspace, 256)) return fail(AWQ_MOE_EINVAL, "workspace null or not 256-byte aligned");
-  const uint64_t need = ws_total(dims, M, topk);
-  if (workspace_bytes < need)
-    return fail(AWQ_MOE_ENOSPC, "workspace_bytes %llu < %llu", (unsigned long long)workspace_bytes,
-                (unsigned long long)need);
-  return AWQ_MOE_OK;
-}
-
-struct WsPtrs {
-  uint32_t* status;
-  uint16_t* act;
-};
-
-WsPtrs ws_ptrs(const void* workspace) {
-  uint8_t* ws = static_cast<uint8_t*>(const_cast<void*>(workspace));
-  return WsPtrs{reinterpret_cast<uint32_t*>(ws + AWQ_MOE_WS_STATUS_OFFSET),
-                reinterpret_cast<uint16_t*>(ws + AWQ_MOE_WS_ACT_OFFSET)};
-}
-
-int awq_moe_w13_swiglu(const awq_moe_dims* dims, const void* bank, const uint16_t* x, const int32_t* topk_ids,
-                       int32_t M, int32_t topk, void* workspace, uint64_t workspace_bytes, void* stream) {
-  int rc = check_stage(dims, bank, M, topk, workspace, workspace_bytes);
+int awq_moe_w13_swiglu(const awq_moe_dims* dims, const void* bank, uint64_t bank_bytes, const uint16_t* x,
+                       const int32_t* topk_ids, int32_t M, int32_t topk, void* workspace, uint64_t workspace_bytes,
+                       void* stream) {
+  int rc = check_stage(dims, bank, bank_bytes, M, topk, workspace, workspace_bytes);
   if (rc) return rc;
   if (!x || !aligned(x, 16)) return fail(AWQ_MOE_EINVAL, "x null or not 16-byte aligned");
   if (!topk_ids || !aligned(topk_ids, 4)) return fail(AWQ_MOE_EINVAL, "topk_ids null or misaligned");
@@ -382,10 +394,10 @@ int awq_moe_w13_swiglu(const awq_moe_dims* dims, const void* bank, const uint16_
                     "w13 launch");
 }
 
-int awq_moe_w2_reduce(const awq_moe_dims* dims, const void* bank, const int32_t* topk_ids, const float* topk_w,
-                      int32_t M, int32_t topk, const void* workspace, uint64_t workspace_bytes, uint16_t* out,
-                      void* stream) {
-  int rc = check_stage(dims, bank, M, topk, workspace, workspace_bytes);
+int awq_moe_w2_reduce(const awq_moe_dims* dims, const void* bank, uint64_t bank_bytes, const int32_t* topk_ids,
+                      const float* topk_w, int32_t M, int32_t topk, const void* workspace, uint64_t workspace_bytes,
+                      uint16_t* out, void* stream) {
+  int rc = check_stage(dims, bank, bank_bytes, M, topk, workspace, workspace_bytes);
   if (rc) return rc;
   if (!topk_ids || !aligned(topk_ids, 4)) return fail(AWQ_MOE_EINVAL, "topk_ids null or misaligned");
   if (!topk_w || !aligned(topk_w, 4)) return fail(AWQ_MOE_EINVAL, "topk_w null or misaligned");
@@ -445,12 +457,12 @@ int awq_moe_prefill_workspace_bytes(const awq_moe_dims* dims, int32_t max_tokens
   return ok();
 }
 
-int awq_moe_prefill(const awq_moe_dims* dims, const void* bank, const uint16_t* x, const int32_t* topk_ids,
-                    const float* topk_w, int32_t M, int32_t topk, uint16_t* out, void* workspace,
-                    uint64_t workspace_bytes, void* stream) {
+int awq_moe_prefill(const awq_moe_dims* dims, const void* bank, uint64_t bank_bytes, const uint16_t* x,
+                    const int32_t* topk_ids, const float* topk_w, int32_t M, int32_t topk, uint16_t* out,
+                    void* workspace, uint64_t workspace_bytes, void* stream) {
   int rc = check_prefill_shape(dims, M, topk);
   if (rc) return rc;
-  if (!bank || !aligned(bank, 256)) return fail(AWQ_MOE_EINVAL, "bank null or not 256-byte aligned");
+  if ((rc = check_bank(dims, bank, bank_bytes))) return rc;
   if (!workspace || !aligned(workspace, 256)) return fail(AWQ_MOE_EINVAL, "workspace null or not 256-byte aligned");
   const PrefillLayout L = prefill_layout(dims, M, topk);
   if (workspace_bytes < L.total)
@@ -475,10 +487,10 @@ int awq_moe_prefill(const awq_moe_dims* dims, const void* bank, const uint16_t* 
                     "prefill launch");
 }
 
-int awq_moe_decode(const awq_moe_dims* dims, const void* bank, const uint16_t* x, const int32_t* topk_ids,
-                   const float* topk_w, int32_t M, int32_t topk, uint16_t* out, void* workspace,
-                   uint64_t workspace_bytes, void* stream) {
-  int rc = check_stage(dims, bank, M, topk, workspace, workspace_bytes);
+int awq_moe_decode(const awq_moe_dims* dims, const void* bank, uint64_t bank_bytes, const uint16_t* x,
+                   const int32_t* topk_ids, const float* topk_w, int32_t M, int32_t topk, uint16_t* out,
+                   void* workspace, uint64_t workspace_bytes, void* stream) {
+  int rc = check_stage(dims, bank, bank_bytes, M, topk, workspace, workspace_bytes);
   if (rc) return rc;
   if (!x || !aligned(x, 16)) return fail(AWQ_MOE_EINVAL, "x null or not 16-byte aligned");
   if (!topk_ids || !aligned(topk_ids, 4)) return fail(AWQ_MOE_EINVAL, "topk_ids null or misaligned");
@@ -493,11 +505,11 @@ int awq_moe_decode(const awq_moe_dims* dims, const void* bank, const uint16_t* x
   return hip_status(awq_moe::launch_w2_reduce(a, w.act, topk_w, out, s), "w2 launch");
 }
 
-int awq_moe_dequant(const awq_moe_dims* dims, const void* bank, int32_t expert_begin, int32_t expert_count,
-                    int32_t which, float* out, void* stream) {
+int awq_moe_dequant(const awq_moe_dims* dims, const void* bank, uint64_t bank_bytes, int32_t expert_begin,
+                    int32_t expert_count, int32_t which, float* out, void* stream) {
   int rc = check_dims(dims);
   if (rc) return rc;
-  if (!bank || !aligned(bank, 256)) return fail(AWQ_MOE_EINVAL, "bank null or not 256-byte aligned");
+  if ((rc = check_bank(dims, bank, bank_bytes))) return rc;
   if (!out || !aligned(out, 4)) return fail(AWQ_MOE_EINVAL, "out null or misaligned");
   if (which != 0 && which != 1) return fail(AWQ_MOE_EINVAL, "which %d: 0 (W13) or 1 (W2)", which);
   if (expert_count < 1 || expert_begin < 0 || (int64_t)expert_begin + expert_count > dims->num_experts)

@@ -15,6 +15,12 @@ AWQ weights that are not available; the draws below stand in for them:
 * activations x = fp16(N(0,1))
 * router weights = fp32 softmax of N(0,1) logits over the k selected experts
 
+For parity over the whole record range the ABI admits there are also
+``expert_weights_wide`` (zeros U{0..255}; scales with a random sign that
+include +-0, subnormals and, in chosen K-groups, magnitudes in [32768, 65504];
+or subnormal scales only) and activations that are tiny in chosen groups or
+near the fp16 maximum (``activations_wide``, ``activations_near_max``).
+
 Every expert draws from its own stream, ``PCG64(SeedSequence([seed, e]))``,
 in the fixed order q_gate, q_up, q_down, s_gate, s_up, s_down, z_gate, z_up,
 z_down, so one expert can be regenerated without drawing the others.
@@ -98,8 +104,80 @@ class BankInputs:
 _FIELDS = ("q_gate", "q_up", "q_down", "s_gate", "s_up", "s_down", "z_gate", "z_up", "z_down")
 
 
-def bank_inputs(seed: int, num_experts: int, hidden: int, inter: int, **kw) -> BankInputs:
-    """Draw all experts of one layer (expert e from stream [seed, e])."""
+def fp16_wide_scales(rng: np.random.Generator, shape, std: float = 0.002, frac_zero: float = 0.05,
+                     frac_sub: float = 0.10) -> np.ndarray:
+    """fp16 scales spread over the finite range a record admits.
+
+    Every value gets a random sign bit (so +0 and -0 both occur). With
+    probability ``frac_zero`` the magnitude is 0, with probability
+    ``frac_sub`` it is a subnormal (exponent field 0, mantissa U{1..1023}),
+    otherwise fp16(|N(0,1)| * std). Draw order: class, sign, normal, mantissa.
+    """
+    u = rng.random(shape)
+    sign = (rng.integers(0, 2, size=shape).astype(np.uint16) << np.uint16(15)).astype(np.uint16)
+    normal = (np.abs(rng.standard_normal(shape)) * std).astype(np.float16).view(np.uint16)
+    sub = rng.integers(1, 1024, size=shape).astype(np.uint16)
+    mag = np.where(u < frac_zero, np.uint16(0), np.where(u < frac_zero + frac_sub, sub, normal)).astype(np.uint16)
+    return (mag | sign).view(np.float16)
+
+
+def fp16_big_scales(rng: np.random.Generator, shape) -> np.ndarray:
+    """fp16 scales at the top of the range: exponent field 30 (magnitudes
+    32768 .. 65504), mantissa U{0..1023}, random sign. Draw order: mantissa, sign."""
+    mant = rng.integers(0, 1024, size=shape).astype(np.uint16)
+    sign = (rng.integers(0, 2, size=shape).astype(np.uint16) << np.uint16(15)).astype(np.uint16)
+    return ((np.uint16(30 << 10) | mant) | sign).astype(np.uint16).view(np.float16)
+
+
+def fp16_tiny_scales(rng: np.random.Generator, shape, mant_hi: int = 4) -> np.ndarray:
+    """fp16 subnormal scales with mantissa U{1..mant_hi-1} (multiples of 2^-24)
+    and a random sign. Draw order: mantissa, sign."""
+    mant = rng.integers(1, mant_hi, size=shape).astype(np.uint16)
+    sign = (rng.integers(0, 2, size=shape).astype(np.uint16) << np.uint16(15)).astype(np.uint16)
+    return (mant | sign).astype(np.uint16).view(np.float16)
+
+
+def expert_weights_wide(seed: int, e: int, hidden: int, inter: int, kind: str = "wide", kind_w2: str | None = None,
+                        big_w13_groups=(), big_w2_groups=()) -> ExpertWeights:
+    """Expert ``e`` with records over the whole admitted range: zeros
+    U{0..255} and scales of both signs.
+
+    ``kind`` sets the W13 scales and ``kind_w2`` (default: the same) the W2
+    scales:
+      "wide": ``fp16_wide_scales``, except the K-groups listed in
+              ``big_w13_groups`` (W13) or ``big_w2_groups`` (W2), whose
+              scales (every column) come from ``fp16_big_scales``;
+      "tiny": ``fp16_tiny_scales`` (for activations near the fp16 maximum).
+    Draw order: q_gate, q_up, q_down, z_gate, z_up, z_down, then the scales
+    of gate, up and down (each: the base draw, then the big groups)."""
+    rng = _expert_rng(seed, e)
+    H, I = hidden, inter
+    q_gate = rng.integers(0, 16, size=(H, I), dtype=np.uint8)
+    q_up = rng.integers(0, 16, size=(H, I), dtype=np.uint8)
+    q_down = rng.integers(0, 16, size=(I, H), dtype=np.uint8)
+    z_gate = rng.integers(0, 256, size=(H // GROUP, I), dtype=np.uint8)
+    z_up = rng.integers(0, 256, size=(H // GROUP, I), dtype=np.uint8)
+    z_down = rng.integers(0, 256, size=(I // GROUP, H), dtype=np.uint8)
+    scales = []
+    kind_w2 = kind if kind_w2 is None else kind_w2
+    for shape, big, kd in (((H // GROUP, I), big_w13_groups, kind), ((H // GROUP, I), big_w13_groups, kind),
+                           ((I // GROUP, H), big_w2_groups, kind_w2)):
+        if kd == "tiny":
+            s = fp16_tiny_scales(rng, shape)
+        elif kd == "wide":
+            s = fp16_wide_scales(rng, shape)
+            for g in big:
+                s[g, :] = fp16_big_scales(rng, (shape[1],))
+        else:
+            raise ValueError(f"unknown kind {kd!r}")
+        scales.append(s)
+    return ExpertWeights(q_gate, q_up, q_down, scales[0], scales[1], scales[2], z_gate, z_up, z_down)
+
+
+def bank_inputs(seed: int, num_experts: int, hidden: int, inter: int, draw=None, **kw) -> BankInputs:
+    """Draw all experts of one layer (expert e from stream [seed, e]) with
+    ``draw`` (``expert_weights`` unless given) and its keyword arguments."""
+    draw = expert_weights if draw is None else draw
     E, H, I = num_experts, hidden, inter
     out = {
         "q_gate": np.empty((E, H, I), np.uint8), "q_up": np.empty((E, H, I), np.uint8),
@@ -110,7 +188,7 @@ def bank_inputs(seed: int, num_experts: int, hidden: int, inter: int, **kw) -> B
         "z_down": np.empty((E, I // GROUP, H), np.uint8),
     }
     for e in range(E):
-        w = expert_weights(seed, e, H, I, **kw)
+        w = draw(seed, e, H, I, **kw)
         for f in _FIELDS:
             out[f][e] = getattr(w, f)
     return BankInputs(**out)
@@ -119,6 +197,24 @@ def bank_inputs(seed: int, num_experts: int, hidden: int, inter: int, **kw) -> B
 def activations(rng: np.random.Generator, M: int, hidden: int) -> np.ndarray:
     """x = fp16(N(0,1)), shape [M][hidden]."""
     return rng.standard_normal((M, hidden)).astype(np.float16)
+
+
+def activations_wide(rng: np.random.Generator, M: int, hidden: int, tiny_groups=()) -> np.ndarray:
+    """x = fp16(N(0,1)), except the 32-value groups listed in ``tiny_groups``,
+    which get fp16(N(0,1) * 2^-22): mostly subnormals of a few units of 2^-24,
+    and zeros. Draw order: the normal matrix, then the tiny groups."""
+    x = rng.standard_normal((M, hidden))
+    for g in tiny_groups:
+        x[:, GROUP * g:GROUP * (g + 1)] = rng.standard_normal((M, GROUP)) * 2.0 ** -22
+    return x.astype(np.float16)
+
+
+def activations_near_max(rng: np.random.Generator, M: int, hidden: int) -> np.ndarray:
+    """x with |x| ~ U[2^14, 65504] rounded to fp16 and a random sign: the top
+    two binades of the fp16 range. Draw order: magnitudes, signs."""
+    mag = rng.uniform(2.0 ** 14, 65504.0, size=(M, hidden))
+    sign = np.where(rng.integers(0, 2, size=(M, hidden)) == 1, -1.0, 1.0)
+    return (mag * sign).astype(np.float16)
 
 
 def router_weights(rng: np.random.Generator, M: int, k: int) -> np.ndarray:

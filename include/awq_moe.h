@@ -26,6 +26,10 @@
  *    graph.
  *  - stream is a hipStream_t passed as void* (NULL = the null stream). Kernels
  *    run asynchronously on it; a launch failure returns AWQ_MOE_EHIP.
+ *  - Every call that reads a bank takes bank_bytes, the size of the caller's
+ *    allocation, and fails with AWQ_MOE_ENOSPC when it is smaller than the
+ *    layout of dims (so a bank packed for other dims is rejected before a
+ *    kernel could read past it).
  *  - Concurrent calls that share an output or workspace buffer race.
  *
  * Bank layout (version 1; also stated in oracle/layout.py):
@@ -141,7 +145,10 @@ int awq_moe_route_compact(const int32_t* topk_ids, int32_t M, int32_t topk, int3
 /* The whole stage for M = 1..8 tokens (PR #520 Purpose: 2 to 8 tokens; fork
  * PR #12 Purpose and stack: physical M = 1 with fp16 (1, hidden) x, int32
  * (1, k) ids and fp32 router weights).
- *   bank     device, 256-byte aligned, awq_moe_bank_layout_query(dims).total_bytes
+ *   bank     device, 256-byte aligned; bank_bytes, the size of the caller's
+ *            allocation, must be >= awq_moe_bank_layout_query(dims).total_bytes
+ *            (ENOSPC otherwise: the kernels address experts by id and cannot
+ *            see the allocation)
  *   x        device fp16 [M][H], 16-byte aligned
  *   topk_ids device int32 [M][topk]; topk_w device fp32 [M][topk] (used as given)
  *   out      device fp16 [M][H], 16-byte aligned, overwritten:
@@ -156,7 +163,7 @@ int awq_moe_route_compact(const int32_t* topk_ids, int32_t M, int32_t topk, int3
  * (token, 16-column tile) that sums the token's slots itself. Slots that
  * share an expert read its tiles at about the same moment and all but the
  * first read are served from cache, so no routing launch precedes them. */
-int awq_moe_decode(const awq_moe_dims* dims, const void* bank, const uint16_t* x,
+int awq_moe_decode(const awq_moe_dims* dims, const void* bank, uint64_t bank_bytes, const uint16_t* x,
                    const int32_t* topk_ids, const float* topk_w, int32_t M, int32_t topk,
                    uint16_t* out, void* workspace, uint64_t workspace_bytes, void* stream);
 
@@ -169,7 +176,7 @@ int awq_moe_decode(const awq_moe_dims* dims, const void* bank, const uint16_t* x
  * the status word and act into workspace: act[s] =
  * fp16(silu(x_t Wg_e) * (x_t Wu_e)) for each valid flat slot s = t*topk + j
  * (rows of invalid slots are not written). One launch. */
-int awq_moe_w13_swiglu(const awq_moe_dims* dims, const void* bank, const uint16_t* x,
+int awq_moe_w13_swiglu(const awq_moe_dims* dims, const void* bank, uint64_t bank_bytes, const uint16_t* x,
                        const int32_t* topk_ids, int32_t M, int32_t topk,
                        void* workspace, uint64_t workspace_bytes, void* stream);
 
@@ -178,7 +185,7 @@ int awq_moe_w13_swiglu(const awq_moe_dims* dims, const void* bank, const uint16_
  * workspace is only read). topk_ids device int32 [M][topk] and topk_w device
  * fp32 [M][topk] as for awq_moe_decode; out device fp16 [M][H], overwritten.
  * One launch. */
-int awq_moe_w2_reduce(const awq_moe_dims* dims, const void* bank, const int32_t* topk_ids,
+int awq_moe_w2_reduce(const awq_moe_dims* dims, const void* bank, uint64_t bank_bytes, const int32_t* topk_ids,
                       const float* topk_w, int32_t M, int32_t topk, const void* workspace,
                       uint64_t workspace_bytes, uint16_t* out, void* stream);
 
@@ -264,9 +271,9 @@ int awq_moe_router_gemv(const uint16_t* r, const uint16_t* delta, int32_t M, int
  * nothing is allocated and nothing synchronises, so the call can be
  * captured in a HIP graph. Calls that share a workspace must not overlap. */
 int awq_moe_prefill_workspace_bytes(const awq_moe_dims* dims, int32_t max_tokens, int32_t topk, uint64_t* out);
-int awq_moe_prefill(const awq_moe_dims* dims, const void* bank, const uint16_t* x, const int32_t* topk_ids,
-                    const float* topk_w, int32_t M, int32_t topk, uint16_t* out, void* workspace,
-                    uint64_t workspace_bytes, void* stream);
+int awq_moe_prefill(const awq_moe_dims* dims, const void* bank, uint64_t bank_bytes, const uint16_t* x,
+                    const int32_t* topk_ids, const float* topk_w, int32_t M, int32_t topk, uint16_t* out,
+                    void* workspace, uint64_t workspace_bytes, void* stream);
 
 /* Dequantise experts [expert_begin, expert_begin + expert_count) of the bank
  * into fp32 (diagnostic). Each value s * (q - z) is exact in fp32: q - z is an
@@ -275,7 +282,7 @@ int awq_moe_prefill(const awq_moe_dims* dims, const void* bank, const uint16_t* 
  *   which = 0: W13 [count][H][2I] (column 2i gate, 2i+1 up)
  *   which = 1: W2  [count][I][H]
  * out device fp32, C-contiguous. */
-int awq_moe_dequant(const awq_moe_dims* dims, const void* bank, int32_t expert_begin,
+int awq_moe_dequant(const awq_moe_dims* dims, const void* bank, uint64_t bank_bytes, int32_t expert_begin,
                     int32_t expert_count, int32_t which, float* out, void* stream);
 
 /* Message for the last error returned on the calling thread ("" if none). */

@@ -27,8 +27,6 @@ Readings where the pages are silent (each also listed in the design notes):
 
 from __future__ import annotations
 
-import math
-
 import numpy as np
 
 GROUP = 32
@@ -264,19 +262,3 @@ def within_gate(gpu: np.ndarray, ref: np.ndarray, max_rel: float = 4e-3, l2: flo
 def higham_gamma(n: int, u: float = 2.0 ** -24) -> float:
     """gamma_n = n u / (1 - n u), the standard bound for an n-term fp32 dot product."""
     return n * u / (1.0 - n * u)
-
-
-def fp16_round(v: np.ndarray) -> np.ndarray:
-    """Round-to-nearest-even into fp16 (values beyond the range become +-inf)."""
-    with np.errstate(over="ignore"):
-        return np.asarray(v, dtype=np.float64).astype(np.float16)
-
-
-def isclose_exact_fp32(v64: np.ndarray) -> bool:
-    """True when every float64 value is exactly representable in float32."""
-    v = np.asarray(v64, dtype=np.float64)
-    return bool(np.all(v.astype(np.float32).astype(np.float64) == v))
-
-
-def sigmoid_ref(g: float) -> float:
-    return 1.0 / (1.0 + math.exp(-g)) if g >= 0 else math.exp(g) / (1.0 + math.exp(g))

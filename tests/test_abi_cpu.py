@@ -49,6 +49,16 @@ def test_prepare_bytes_equal_oracle_pack(rb, E, H, I):
 
 
 @pytest.mark.parametrize("rb", [3, 4])
+def test_prepare_bytes_equal_oracle_pack_wide_records(rb):
+    """Zeros 0..255 and scales of both signs (+-0, subnormal, near 65504)."""
+    bi = inputs.bank_inputs(22, 3, 96, 64, draw=inputs.expert_weights_wide, big_w13_groups=(2,),
+                            big_w2_groups=(1,))
+    got = abi.prepare_from_inputs(abi.make_dims(3, 96, 64, rb), bi)
+    want = OL.pack_bank(OL.Dims(3, 96, 64, rb), bi)
+    assert got.tobytes() == want.tobytes()
+
+
+@pytest.mark.parametrize("rb", [3, 4])
 def test_prepare_worked_example(rb):
     from tests.test_oracle_layout import golden_entries, worked_example_weights
     w = worked_example_weights()
@@ -127,27 +137,29 @@ def test_device_calls_reject_bad_arguments_before_launch():
     ws_need = abi.awq_moe_workspace_bytes(d, 1, 10)
     pws_need = abi.awq_moe_prefill_workspace_bytes(d, 9, 10)
     d_big = abi.make_dims(4097, 256, 32, 3)
+    bb = abi.awq_moe_bank_layout_query(d).total_bytes          # the bank size the dims need
+    bb_big = abi.awq_moe_bank_layout_query(d_big).total_bytes
     cases = [
-        (lambda: lib.awq_moe_decode(ctypes.byref(d), p, p, p, p, 9, 10, p, p, ws_need, None), abi.EINVAL),
-        (lambda: lib.awq_moe_decode(ctypes.byref(d), p, p, p, p, 1, 10, p, p, ws_need - 1, None), abi.ENOSPC),
-        (lambda: lib.awq_moe_decode(ctypes.byref(d), mis, p, p, p, 1, 10, p, p, ws_need, None), abi.EINVAL),
-        (lambda: lib.awq_moe_decode(ctypes.byref(d), p, mis, p, p, 1, 10, p, p, ws_need, None), abi.EINVAL),
-        (lambda: lib.awq_moe_decode(ctypes.byref(d), p, p, None, p, 1, 10, p, p, ws_need, None), abi.EINVAL),
-        (lambda: lib.awq_moe_decode(ctypes.byref(d), p, p, p, p, 1, 10, mis, p, ws_need, None), abi.EINVAL),
-        (lambda: lib.awq_moe_decode(None, p, p, p, p, 1, 10, p, p, ws_need, None), abi.EINVAL),
+        (lambda: lib.awq_moe_decode(ctypes.byref(d), p, bb, p, p, p, 9, 10, p, p, ws_need, None), abi.EINVAL),
+        (lambda: lib.awq_moe_decode(ctypes.byref(d), p, bb, p, p, p, 1, 10, p, p, ws_need - 1, None), abi.ENOSPC),
+        (lambda: lib.awq_moe_decode(ctypes.byref(d), mis, bb, p, p, p, 1, 10, p, p, ws_need, None), abi.EINVAL),
+        (lambda: lib.awq_moe_decode(ctypes.byref(d), p, bb, mis, p, p, 1, 10, p, p, ws_need, None), abi.EINVAL),
+        (lambda: lib.awq_moe_decode(ctypes.byref(d), p, bb, p, None, p, 1, 10, p, p, ws_need, None), abi.EINVAL),
+        (lambda: lib.awq_moe_decode(ctypes.byref(d), p, bb, p, p, p, 1, 10, mis, p, ws_need, None), abi.EINVAL),
+        (lambda: lib.awq_moe_decode(None, p, bb, p, p, p, 1, 10, p, p, ws_need, None), abi.EINVAL),
         (lambda: lib.awq_moe_route_compact(p, 0, 10, 512, p, p, p, p, p, None), abi.EINVAL),
         (lambda: lib.awq_moe_route_compact(p, 1, 10, 0, p, p, p, p, p, None), abi.EINVAL),
         (lambda: lib.awq_moe_route_compact(p, 1, 10, 512, p, p, None, p, p, None), abi.EINVAL),
-        (lambda: lib.awq_moe_w13_swiglu(ctypes.byref(d), p, p, p, 1, 10, mis, ws_need, None), abi.EINVAL),
-        (lambda: lib.awq_moe_w13_swiglu(ctypes.byref(d), p, p, None, 1, 10, p, ws_need, None), abi.EINVAL),
-        (lambda: lib.awq_moe_w13_swiglu(ctypes.byref(d), p, p, p, 1, 10, p, ws_need - 1, None), abi.ENOSPC),
-        (lambda: lib.awq_moe_w2_reduce(ctypes.byref(d), p, p, p, 1, 10, p, ws_need, mis, None), abi.EINVAL),
-        (lambda: lib.awq_moe_w2_reduce(ctypes.byref(d), p, p, p, 9, 10, p, ws_need, p, None), abi.EINVAL),
-        (lambda: lib.awq_moe_w2_reduce(ctypes.byref(d), p, None, p, 1, 10, p, ws_need, p, None), abi.EINVAL),
-        (lambda: lib.awq_moe_w2_reduce(ctypes.byref(d), p, p, p, 1, 10, p, ws_need - 1, p, None), abi.ENOSPC),
-        (lambda: lib.awq_moe_w2_reduce(ctypes.byref(d), p, p, None, 1, 10, p, ws_need, p, None), abi.EINVAL),
-        (lambda: lib.awq_moe_dequant(ctypes.byref(d), p, 510, 3, 0, p, None), abi.EINVAL),
-        (lambda: lib.awq_moe_dequant(ctypes.byref(d), p, 0, 1, 2, p, None), abi.EINVAL),
+        (lambda: lib.awq_moe_w13_swiglu(ctypes.byref(d), p, bb, p, p, 1, 10, mis, ws_need, None), abi.EINVAL),
+        (lambda: lib.awq_moe_w13_swiglu(ctypes.byref(d), p, bb, p, None, 1, 10, p, ws_need, None), abi.EINVAL),
+        (lambda: lib.awq_moe_w13_swiglu(ctypes.byref(d), p, bb, p, p, 1, 10, p, ws_need - 1, None), abi.ENOSPC),
+        (lambda: lib.awq_moe_w2_reduce(ctypes.byref(d), p, bb, p, p, 1, 10, p, ws_need, mis, None), abi.EINVAL),
+        (lambda: lib.awq_moe_w2_reduce(ctypes.byref(d), p, bb, p, p, 9, 10, p, ws_need, p, None), abi.EINVAL),
+        (lambda: lib.awq_moe_w2_reduce(ctypes.byref(d), p, bb, None, p, 1, 10, p, ws_need, p, None), abi.EINVAL),
+        (lambda: lib.awq_moe_w2_reduce(ctypes.byref(d), p, bb, p, p, 1, 10, p, ws_need - 1, p, None), abi.ENOSPC),
+        (lambda: lib.awq_moe_w2_reduce(ctypes.byref(d), p, bb, p, None, 1, 10, p, ws_need, p, None), abi.EINVAL),
+        (lambda: lib.awq_moe_dequant(ctypes.byref(d), p, bb, 510, 3, 0, p, None), abi.EINVAL),
+        (lambda: lib.awq_moe_dequant(ctypes.byref(d), p, bb, 0, 1, 2, p, None), abi.EINVAL),
         (lambda: lib.awq_moe_router_topk(p, 0, 512, 10, p, p, None), abi.EINVAL),
         (lambda: lib.awq_moe_router_topk(p, 9, 512, 10, p, p, None), abi.EINVAL),
         (lambda: lib.awq_moe_router_topk(p, 1, 4097, 10, p, p, None), abi.EINVAL),
@@ -170,19 +182,27 @@ def test_device_calls_reject_bad_arguments_before_launch():
         (lambda: lib.awq_moe_router_gemv(p, None, 1, 256, 1e-6, None, 512, q1, q2, p, None), abi.EINVAL),
         (lambda: lib.awq_moe_router_gemv(p, None, 1, 256, 1e-6, p, 0, q1, q2, p, None), abi.EINVAL),
         (lambda: lib.awq_moe_router_gemv(p, None, 1, 256, 1e-6, p, 512, q1, q2, None, None), abi.EINVAL),
-        (lambda: lib.awq_moe_prefill(ctypes.byref(d), p, p, p, p, 8, 10, p, p, pws_need, None), abi.EINVAL),
-        (lambda: lib.awq_moe_prefill(ctypes.byref(d), p, p, p, p, 4097, 10, p, p, 1 << 62, None), abi.EINVAL),
-        (lambda: lib.awq_moe_prefill(ctypes.byref(d), p, p, p, p, 9, 33, p, p, 1 << 62, None), abi.EINVAL),
-        (lambda: lib.awq_moe_prefill(ctypes.byref(d), p, p, p, p, 9, 10, p, p, pws_need - 1, None), abi.ENOSPC),
-        (lambda: lib.awq_moe_prefill(ctypes.byref(d), mis, p, p, p, 9, 10, p, p, pws_need, None), abi.EINVAL),
-        (lambda: lib.awq_moe_prefill(ctypes.byref(d), p, mis, p, p, 9, 10, p, p, pws_need, None), abi.EINVAL),
-        (lambda: lib.awq_moe_prefill(ctypes.byref(d), p, p, None, p, 9, 10, p, p, pws_need, None), abi.EINVAL),
-        (lambda: lib.awq_moe_prefill(ctypes.byref(d), p, p, p, None, 9, 10, p, p, pws_need, None), abi.EINVAL),
-        (lambda: lib.awq_moe_prefill(ctypes.byref(d), p, p, p, p, 9, 10, mis, p, pws_need, None), abi.EINVAL),
-        (lambda: lib.awq_moe_prefill(ctypes.byref(d), p, p, p, p, 9, 10, p, mis, pws_need, None), abi.EINVAL),
-        (lambda: lib.awq_moe_prefill(ctypes.byref(d_big), p, p, p, p, 9, 10, p, p, 1 << 62, None),
+        (lambda: lib.awq_moe_prefill(ctypes.byref(d), p, bb, p, p, p, 8, 10, p, p, pws_need, None), abi.EINVAL),
+        (lambda: lib.awq_moe_prefill(ctypes.byref(d), p, bb, p, p, p, 4097, 10, p, p, 1 << 62, None), abi.EINVAL),
+        (lambda: lib.awq_moe_prefill(ctypes.byref(d), p, bb, p, p, p, 9, 33, p, p, 1 << 62, None), abi.EINVAL),
+        (lambda: lib.awq_moe_prefill(ctypes.byref(d), p, bb, p, p, p, 9, 10, p, p, pws_need - 1, None), abi.ENOSPC),
+        (lambda: lib.awq_moe_prefill(ctypes.byref(d), mis, bb, p, p, p, 9, 10, p, p, pws_need, None), abi.EINVAL),
+        (lambda: lib.awq_moe_prefill(ctypes.byref(d), p, bb, mis, p, p, 9, 10, p, p, pws_need, None), abi.EINVAL),
+        (lambda: lib.awq_moe_prefill(ctypes.byref(d), p, bb, p, None, p, 9, 10, p, p, pws_need, None), abi.EINVAL),
+        (lambda: lib.awq_moe_prefill(ctypes.byref(d), p, bb, p, p, None, 9, 10, p, p, pws_need, None), abi.EINVAL),
+        (lambda: lib.awq_moe_prefill(ctypes.byref(d), p, bb, p, p, p, 9, 10, mis, p, pws_need, None), abi.EINVAL),
+        (lambda: lib.awq_moe_prefill(ctypes.byref(d), p, bb, p, p, p, 9, 10, p, mis, pws_need, None), abi.EINVAL),
+        (lambda: lib.awq_moe_prefill(ctypes.byref(d_big), p, bb_big, p, p, p, 9, 10, p, p, 1 << 62, None),
          abi.EUNSUPPORTED),
-        (lambda: lib.awq_moe_prefill(None, p, p, p, p, 9, 10, p, p, pws_need, None), abi.EINVAL),
+        (lambda: lib.awq_moe_prefill(None, p, bb, p, p, p, 9, 10, p, p, pws_need, None), abi.EINVAL),
+        # a bank smaller than the layout of dims (e.g. packed for fewer experts or 3-byte records)
+        (lambda: lib.awq_moe_decode(ctypes.byref(d), p, bb - 1, p, p, p, 1, 10, p, p, ws_need, None), abi.ENOSPC),
+        (lambda: lib.awq_moe_w13_swiglu(ctypes.byref(d), p, bb - 256, p, p, 1, 10, p, ws_need, None), abi.ENOSPC),
+        (lambda: lib.awq_moe_w2_reduce(ctypes.byref(d), p, 0, p, p, 1, 10, p, ws_need, p, None), abi.ENOSPC),
+        (lambda: lib.awq_moe_prefill(ctypes.byref(d), p, bb - 1, p, p, p, 9, 10, p, p, pws_need, None), abi.ENOSPC),
+        (lambda: lib.awq_moe_dequant(ctypes.byref(d), p, bb - 1, 0, 1, 0, p, None), abi.ENOSPC),
+        (lambda: lib.awq_moe_decode(ctypes.byref(abi.make_dims(512, 2560, 160, 4)), p, bb, p, p, p, 1, 10, p, p,
+                                    1 << 40, None), abi.ENOSPC),
     ]
     for i, (call, code) in enumerate(cases):
         assert call() == code, (i, abi.awq_moe_last_error())

@@ -12,7 +12,7 @@ import pytest
 
 from awq_int4_mixture_amd import inputs
 from oracle import ref as R
-from tests.gpu_helpers import bank_case, f16_to_np, say, to_dev, torch_mod
+from tests.gpu_helpers import bank_case, exact_in_fp32, f16_to_np, say, to_dev, torch_mod
 
 pytestmark = pytest.mark.gpu
 
@@ -60,7 +60,7 @@ def test_dequant_bit_exact(rb, shape):
         for el in range(4):
             w = bi.expert(1 + el)
             want = R.w13_interleaved(w) if which == 0 else R.dequant(w.q_down, w.s_down, w.z_down)
-            assert R.isclose_exact_fp32(want)
+            assert exact_in_fp32(want)
             np.testing.assert_array_equal(got[el], want.astype(np.float32))
 
 

@@ -63,10 +63,14 @@ def test_worked_example_bytes(rb):
 
 
 @pytest.mark.parametrize("rb", [3, 4])
-@pytest.mark.parametrize("H,I", [(64, 32), (256, 32), (96, 64)])
-def test_round_trip(rb, H, I):
+@pytest.mark.parametrize("H,I,wide", [(64, 32, False), (256, 32, False), (96, 64, False), (96, 64, True)])
+def test_round_trip(rb, H, I, wide):
     d = OL.Dims(3, H, I, rb)
-    bi = inputs.bank_inputs(11, 3, H, I, zero_hi=256)
+    if wide:   # zeros 0..255, scales of both signs: +-0, subnormal, near 65504
+        bi = inputs.bank_inputs(11, 3, H, I, draw=inputs.expert_weights_wide, big_w13_groups=(0,),
+                                big_w2_groups=(1,))
+    else:
+        bi = inputs.bank_inputs(11, 3, H, I, zero_hi=256)
     bank = OL.pack_bank(d, bi)
     for e in range(3):
         w = bi.expert(e)

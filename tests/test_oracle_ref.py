@@ -30,6 +30,45 @@ def test_dequant_matches_scalar_loops():
         np.testing.assert_array_equal(got, want)
 
 
+def _wide_expert(seed=3, H=96, I=64):
+    """Records over the whole admitted range: zeros 0..255, scales of both
+    signs with +-0, subnormals, normals, and one K-group of scales near the
+    fp16 maximum in each matrix."""
+    return inputs.expert_weights_wide(seed, 0, H, I, big_w13_groups=(1,), big_w2_groups=(0,))
+
+
+def test_wide_record_draws_cover_every_class():
+    w = _wide_expert()
+    s = np.concatenate([w.s_gate.ravel(), w.s_up.ravel(), w.s_down.ravel()])
+    b = s.view(np.uint16)
+    assert (b == 0x0000).any() and (b == 0x8000).any()                 # +0 and -0
+    assert (((b & 0x7C00) == 0) & ((b & 0x03FF) != 0)).any()            # subnormals
+    assert (np.abs(s.astype(np.float64)) >= 32768).any()                # near the top of the range
+    assert (s < 0).any() and (s > 0).any()
+    assert w.z_gate.max() > 200 and w.z_down.max() > 200
+    assert np.isfinite(s.astype(np.float64)).all()
+    t = inputs.expert_weights_wide(3, 0, 64, 32, kind="tiny")
+    tb = t.s_gate.view(np.uint16) & 0x7FFF
+    assert ((tb >= 1) & (tb <= 3)).all()                                  # subnormal multiples of 2^-24
+    x = inputs.activations_near_max(np.random.default_rng(0), 2, 64).astype(np.float64)
+    assert (np.abs(x) >= 2.0 ** 14).all() and (np.abs(x) <= 65504).all() and (x < 0).any()
+
+
+def test_dequant_matches_scalar_loops_wide_records():
+    """The same pin over zeros 0..255 and scales of both signs, +-0,
+    subnormal and near 65504; each value is also exact in float32."""
+    w = _wide_expert()
+    for q, s, z in ((w.q_gate, w.s_gate, w.z_gate), (w.q_up, w.s_up, w.z_up), (w.q_down, w.s_down, w.z_down)):
+        got = R.dequant(q, s, z)
+        want = np.array(LP.dequant_loop(q.tolist(), s.astype(np.float64).tolist(), z.tolist()))
+        np.testing.assert_array_equal(got, want)
+        assert np.array_equal(got.astype(np.float32).astype(np.float64), got)
+        # the sign of a zero scale survives: (q - z) * (-0.0) is -0.0 for q > z
+        neg0 = (s.view(np.uint16) == 0x8000)[np.arange(q.shape[0]) // 32, :] & (q > z[np.arange(q.shape[0]) // 32, :])
+        if neg0.any():
+            assert np.signbit(got[neg0]).all() and (got[neg0] == 0).all()
+
+
 def test_dequant_closed_form_values():
     q = np.array([[0], [15], [7], [8]] * 8, np.uint8)          # K=32, N=1
     s = np.array([[0.5]], np.float16)
@@ -126,6 +165,29 @@ def test_stage_matches_scalar_loops_micro():
     want = np.array(LP.stage_loops(x.astype(np.float64).tolist(), ids.tolist(),
                                    w.astype(np.float64).tolist(), 4, bi.expert))
     assert np.abs(got - want).max() <= 1e-12 * np.abs(want).max()
+
+
+def test_stage_matches_scalar_loops_wide_records():
+    """E=3, H=96, I=64, k=2, M=3 with zeros 0..255, signed/zero/subnormal
+    scales, one W13 K-group of scales near 65504 whose activations are tiny
+    subnormals, and a second case with activations near the fp16 maximum and
+    subnormal W13 scales."""
+    E, H, I, M, k = 3, 96, 64, 3, 2
+    cases = (
+        (dict(big_w13_groups=(1,)), lambda rng: inputs.activations_wide(rng, M, H, tiny_groups=(1,))),
+        (dict(kind="tiny", kind_w2="wide"), lambda rng: inputs.activations_near_max(rng, M, H)),
+    )
+    for kw, xdraw in cases:
+        bi = inputs.bank_inputs(17, E, H, I, draw=inputs.expert_weights_wide, **kw)
+        rng = inputs.call_rng(17, 2)
+        x = xdraw(rng)
+        ids = inputs.ids_distinct(rng, M, k, E)
+        w = inputs.router_weights(rng, M, k)
+        got = R.moe_stage(x, ids, w, E, bi.expert)
+        want = np.array(LP.stage_loops(x.astype(np.float64).tolist(), ids.tolist(),
+                                       w.astype(np.float64).tolist(), E, bi.expert))
+        assert np.isfinite(got).all() and np.abs(got).max() > 1.0
+        assert np.abs(got - want).max() <= 1e-12 * np.abs(want).max(), kw
 
 
 def test_stage_with_duplicate_and_invalid_ids_matches_loops():
@@ -231,6 +293,15 @@ def test_topk_softmax_brute_force_and_ties():
         np.testing.assert_allclose(w[t], [a / sum(p) for a in p], rtol=1e-15)
     assert ids[0, :3].tolist() == [3, 9, 17]
     assert ids[1].tolist() == list(range(10))
+
+
+def test_higham_gamma_closed_form():
+    """gamma_n = n u / (1 - n u): n = 1 gives u / (1 - u), and it exceeds n u."""
+    u = 2.0 ** -24
+    assert R.higham_gamma(1) == u / (1.0 - u)
+    assert R.higham_gamma(1000) == 1000 * u / (1.0 - 1000 * u)
+    assert R.higham_gamma(1000) > 1000 * u
+    assert R.higham_gamma(0) == 0.0
 
 
 def test_gate_helper():
