@@ -21,12 +21,13 @@ LIB_PATH = os.path.join(HERE, "libawq_moe.so")
 OK, EINVAL, EUNSUPPORTED, ENOSPC, EHIP = 0, -1, -2, -3, -4
 MAX_TOKENS, MAX_TOPK = 8, 32
 STATUS_BAD_ID = 1
+NOALLOC_SCRATCH_BYTES = 256 + 512 * 1024
 WS_STATUS_OFFSET = 0
 WS_ACT_OFFSET = 256
 
 EXPORTED = (
     "awq_moe_bank_layout_query", "awq_moe_prepare", "awq_moe_workspace_bytes",
-    "awq_moe_route_compact", "awq_moe_decode", "awq_moe_w13_swiglu", "awq_moe_w2_reduce",
+    "awq_moe_route_compact", "awq_moe_decode", "awq_moe_decode_noalloc", "awq_moe_w13_swiglu", "awq_moe_w2_reduce",
     "awq_moe_dequant", "awq_moe_router_topk", "awq_moe_residual_rmsnorm", "awq_moe_router_residual",
     "awq_moe_router_gemv", "awq_moe_prefill_workspace_bytes", "awq_moe_prefill", "awq_moe_last_error",
 )
@@ -69,6 +70,7 @@ def _load() -> ctypes.CDLL:
         "awq_moe_workspace_bytes": [D, I32, I32, ctypes.POINTER(ctypes.c_uint64)],
         "awq_moe_route_compact": [P, I32, I32, I32, P, P, P, P, P, V],
         "awq_moe_decode": [D, P, U64, P, P, P, I32, I32, P, P, U64, V],
+        "awq_moe_decode_noalloc": [D, P, U64, P, P, P, I32, I32, P, P, V],
         "awq_moe_prefill_workspace_bytes": [D, I32, I32, ctypes.POINTER(ctypes.c_uint64)],
         "awq_moe_prefill": [D, P, U64, P, P, P, I32, I32, P, P, U64, V],
         "awq_moe_w13_swiglu": [D, P, U64, P, P, I32, I32, P, U64, V],
@@ -225,6 +227,23 @@ def awq_moe_decode(dims: awq_moe_dims, bank, x, topk_ids, topk_w, out=None, work
         _dev(topk_ids, torch.int32, (M, k), "topk_ids"), _dev(topk_w, torch.float32, (M, k), "topk_w"), M, k,
         _dev(out, torch.float16, (M, dims.hidden), "out"), _dev(workspace, torch.uint8, name="workspace"),
         workspace.numel(), _stream(stream)), "awq_moe_decode")
+    return out
+
+
+def awq_moe_decode_noalloc(dims: awq_moe_dims, bank, x, topk_ids, topk_w, out=None, status=None, stream=None):
+    """awq_moe_decode on the library's fixed scratch (no workspace argument).
+    ``status``: an int32 device tensor of one element, or None."""
+    torch = _torch()
+    M, H = x.shape
+    k = topk_ids.shape[1]
+    if out is None:
+        out = torch.empty((M, H), dtype=torch.float16, device=x.device)
+    sp = None if status is None else _dev(status, torch.int32, (1,), "status")
+    _check(_lib.awq_moe_decode_noalloc(
+        ctypes.byref(dims), _dev(bank, torch.uint8, name="bank"), bank.numel(),
+        _dev(x, torch.float16, (M, dims.hidden), "x"),
+        _dev(topk_ids, torch.int32, (M, k), "topk_ids"), _dev(topk_w, torch.float32, (M, k), "topk_w"), M, k,
+        _dev(out, torch.float16, (M, dims.hidden), "out"), sp, _stream(stream)), "awq_moe_decode_noalloc")
     return out
 
 

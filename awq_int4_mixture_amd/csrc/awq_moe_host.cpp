@@ -73,6 +73,8 @@ Layout make_layout(const awq_moe_dims* d) {
 
 // Workspace: [status u32 | pad] [fp16 act[n][I]].
 static_assert(AWQ_MOE_WS_ACT_OFFSET % 256 == 0, "act must stay 256-byte aligned");
+static_assert(AWQ_MOE_NOALLOC_SCRATCH_BYTES == AWQ_MOE_KNOALLOC_SCRATCH_BYTES,
+              "header and kernels agree on the fixed scratch size");
 static_assert(AWQ_MOE_WS_ACT_OFFSET == AWQ_MOE_KWS_ACT_OFFSET && AWQ_MOE_WS_STATUS_OFFSET == AWQ_MOE_KWS_STATUS_OFFSET,
               "kernels and header agree on the workspace layout");
 
@@ -503,6 +505,38 @@ int awq_moe_decode(const awq_moe_dims* dims, const void* bank, uint64_t bank_byt
   hipError_t e = awq_moe::launch_w13_swiglu(a, x, workspace, s);
   if (e != hipSuccess) return hip_status(e, "w13 launch");
   return hip_status(awq_moe::launch_w2_reduce(a, w.act, topk_w, out, s), "w2 launch");
+}
+
+int awq_moe_decode_noalloc(const awq_moe_dims* dims, const void* bank, uint64_t bank_bytes, const uint16_t* x,
+                           const int32_t* topk_ids, const float* topk_w, int32_t M, int32_t topk, uint16_t* out,
+                           uint32_t* status, void* stream) {
+  int rc = check_dims(dims);
+  if (rc) return rc;
+  if ((rc = check_tokens(M, topk))) return rc;
+  if ((rc = check_bank(dims, bank, bank_bytes))) return rc;
+  const uint64_t need = ws_total(dims, M, topk);
+  if (need > AWQ_MOE_NOALLOC_SCRATCH_BYTES)
+    return fail(AWQ_MOE_ENOSPC, "M*topk*inter = %lld needs %llu bytes of scratch; the library holds %llu",
+                (long long)M * topk * dims->inter, (unsigned long long)need,
+                (unsigned long long)AWQ_MOE_NOALLOC_SCRATCH_BYTES);
+  if (!x || !aligned(x, 16)) return fail(AWQ_MOE_EINVAL, "x null or not 16-byte aligned");
+  if (!topk_ids || !aligned(topk_ids, 4)) return fail(AWQ_MOE_EINVAL, "topk_ids null or misaligned");
+  if (!topk_w || !aligned(topk_w, 4)) return fail(AWQ_MOE_EINVAL, "topk_w null or misaligned");
+  if (!out || !aligned(out, 16)) return fail(AWQ_MOE_EINVAL, "out null or not 16-byte aligned");
+  if (status && !aligned(status, 4)) return fail(AWQ_MOE_EINVAL, "status misaligned");
+  if ((rc = check_device())) return rc;
+  void* ws = nullptr;
+  hipError_t e = awq_moe::noalloc_scratch(&ws);
+  if (e != hipSuccess) return hip_status(e, "scratch address");
+  const WsPtrs w = ws_ptrs(ws);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const awq_moe::StageArgs a = stage_args(dims, bank, topk_ids, M, topk);
+  e = awq_moe::launch_w13_swiglu(a, x, ws, s);
+  if (e != hipSuccess) return hip_status(e, "w13 launch");
+  e = awq_moe::launch_w2_reduce(a, w.act, topk_w, out, s);
+  if (e != hipSuccess) return hip_status(e, "w2 launch");
+  if (status) return hip_status(hipMemcpyAsync(status, w.status, 4, hipMemcpyDeviceToDevice, s), "status copy");
+  return ok();
 }
 
 int awq_moe_dequant(const awq_moe_dims* dims, const void* bank, uint64_t bank_bytes, int32_t expert_begin,

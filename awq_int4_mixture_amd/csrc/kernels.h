@@ -14,6 +14,8 @@
 // decode workspace: status word, then fp16 act [M*topk][I]
 #define AWQ_MOE_KWS_STATUS_OFFSET 0
 #define AWQ_MOE_KWS_ACT_OFFSET 256
+// fixed decode scratch of the no-allocation entry point: status word and act
+#define AWQ_MOE_KNOALLOC_SCRATCH_BYTES (256 + 512 * 1024)
 
 namespace awq_moe {
 
@@ -66,6 +68,10 @@ struct PrefillWs {
 int prefill_max_items(int n, int E);
 hipError_t launch_prefill(const StageArgs& a, const uint16_t* x, const float* topk_w, uint16_t* out,
                           const PrefillWs& w, hipStream_t stream);
+// Address of this device's copy of the library's fixed decode scratch (the
+// workspace of the no-allocation entry point), AWQ_MOE_KNOALLOC_SCRATCH_BYTES
+// bytes, 256-byte aligned. Taken once per device with that device current.
+hipError_t noalloc_scratch(void** ptr);
 hipError_t launch_dequant(const uint8_t* bank, uint64_t expert_bytes, uint64_t units_off,
                           uint64_t meta_off, int RB, int which, int H, int I, int expert_begin,
                           int expert_count, float* out, hipStream_t stream);

@@ -25,6 +25,9 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <atomic>
+#include <mutex>
+
 #include "device_util.h"
 #include "kernels.h"
 
@@ -796,6 +799,41 @@ __global__ void dequant_kernel(const uint8_t* __restrict__ bank, uint64_t expert
       const uint32_t q = (wd[d] >> (4 * (p >> 1) + 16 * (p & 1))) & 0xFu;
       o[(uint64_t)(32 * g + 8 * d + p) * N + n] = ((float)q - z) * s;
     }
+}
+
+// ---------------------------------------------------------------------------
+// Fixed decode scratch for callers that cannot allocate device memory: the
+// workspace (status word, fp16 act) of awq_moe_decode_noalloc. One copy per
+// device, held until the process ends. In host code the array's name only
+// stands for the symbol; kernels get the device address that
+// hipGetSymbolAddress returns for the current device.
+// ---------------------------------------------------------------------------
+static __device__ __attribute__((aligned(256))) uint8_t scratch[AWQ_MOE_KNOALLOC_SCRATCH_BYTES];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::atomic<void*> g_scratch_ptr[kMaxDevices];
+std::mutex g_scratch_mu;
+}  // namespace
+
+hipError_t noalloc_scratch(void** ptr) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  void* p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+  if (!p) {
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    p = g_scratch_ptr[dev].load(std::memory_order_relaxed);
+    if (!p) {
+      e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+      if (e != hipSuccess) return e;
+      if (!p || reinterpret_cast<uintptr_t>(p) % 256 != 0) return hipErrorInvalidSymbol;
+      g_scratch_ptr[dev].store(p, std::memory_order_release);
+    }
+  }
+  *ptr = p;
+  return hipSuccess;
 }
 
 // ---------------------------------------------------------------------------

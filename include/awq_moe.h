@@ -167,6 +167,24 @@ int awq_moe_decode(const awq_moe_dims* dims, const void* bank, uint64_t bank_byt
                    const int32_t* topk_ids, const float* topk_w, int32_t M, int32_t topk,
                    uint16_t* out, void* workspace, uint64_t workspace_bytes, void* stream);
 
+/* awq_moe_decode without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc). The workspace is a fixed scratch array
+ * inside the library, AWQ_MOE_NOALLOC_SCRATCH_BYTES bytes per device, held
+ * until the process ends; this call allocates nothing. Arguments, results and
+ * kernels are those of awq_moe_decode (outputs are bit-identical), except:
+ *   - ENOSPC when awq_moe_workspace_bytes(dims, M, topk) exceeds the scratch,
+ *     i.e. when 256 + M*topk*inter*2 (rounded up to 256) > the maximum;
+ *   - status: device uint32 [1] or NULL; when given, the status word of the
+ *     call (bit 0: some id outside [0, E)) is copied there on stream.
+ * Every call on one device shares that device's scratch (it keeps the last
+ * call's contents and needs no clearing: each call writes what it reads), so
+ * calls that overlap on one device race; serialise them on one stream. */
+#define AWQ_MOE_NOALLOC_SCRATCH_BYTES (256 + 512 * 1024)
+int awq_moe_decode_noalloc(const awq_moe_dims* dims, const void* bank, uint64_t bank_bytes, const uint16_t* x,
+                           const int32_t* topk_ids, const float* topk_w, int32_t M, int32_t topk,
+                           uint16_t* out, uint32_t* status, void* stream);
+
 /* --- stage exports, for stage-pair checks (fork PR #12, Numerical acceptance:
  * W2 checked on its own intermediate) and per-kernel timing. awq_moe_decode
  * is exactly awq_moe_w13_swiglu followed by awq_moe_w2_reduce on the same

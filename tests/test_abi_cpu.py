@@ -139,6 +139,8 @@ def test_device_calls_reject_bad_arguments_before_launch():
     d_big = abi.make_dims(4097, 256, 32, 3)
     bb = abi.awq_moe_bank_layout_query(d).total_bytes          # the bank size the dims need
     bb_big = abi.awq_moe_bank_layout_query(d_big).total_bytes
+    d_wide = abi.make_dims(4, 256, 2048, 3)                    # 8 x 32 x 2048 fp16 act: above the fixed scratch
+    bb_wide = abi.awq_moe_bank_layout_query(d_wide).total_bytes
     cases = [
         (lambda: lib.awq_moe_decode(ctypes.byref(d), p, bb, p, p, p, 9, 10, p, p, ws_need, None), abi.EINVAL),
         (lambda: lib.awq_moe_decode(ctypes.byref(d), p, bb, p, p, p, 1, 10, p, p, ws_need - 1, None), abi.ENOSPC),
@@ -203,11 +205,29 @@ def test_device_calls_reject_bad_arguments_before_launch():
         (lambda: lib.awq_moe_dequant(ctypes.byref(d), p, bb - 1, 0, 1, 0, p, None), abi.ENOSPC),
         (lambda: lib.awq_moe_decode(ctypes.byref(abi.make_dims(512, 2560, 160, 4)), p, bb, p, p, p, 1, 10, p, p,
                                     1 << 40, None), abi.ENOSPC),
+        # the no-allocation entry point: same checks, and a fixed scratch maximum
+        (lambda: lib.awq_moe_decode_noalloc(ctypes.byref(d), p, bb, p, p, p, 9, 10, p, None, None), abi.EINVAL),
+        (lambda: lib.awq_moe_decode_noalloc(ctypes.byref(d), p, bb - 1, p, p, p, 1, 10, p, None, None), abi.ENOSPC),
+        (lambda: lib.awq_moe_decode_noalloc(ctypes.byref(d), p, bb, mis, p, p, 1, 10, p, None, None), abi.EINVAL),
+        (lambda: lib.awq_moe_decode_noalloc(ctypes.byref(d), p, bb, p, p, p, 1, 10, mis, None, None), abi.EINVAL),
+        (lambda: lib.awq_moe_decode_noalloc(ctypes.byref(d), p, bb, p, p, p, 1, 10, p, mis, None), abi.EINVAL),
+        (lambda: lib.awq_moe_decode_noalloc(None, p, bb, p, p, p, 1, 10, p, None, None), abi.EINVAL),
+        (lambda: lib.awq_moe_decode_noalloc(ctypes.byref(d_wide), p, bb_wide, p, p, p, 8, 32, p, None, None),
+         abi.ENOSPC),
     ]
     for i, (call, code) in enumerate(cases):
         assert call() == code, (i, abi.awq_moe_last_error())
         assert abi.awq_moe_last_error() != ""
     assert bytes(buf) == bytes(4096)
+
+
+def test_noalloc_scratch_covers_the_rank_shape():
+    """The fixed scratch of the no-allocation entry point holds the decode
+    workspace of the rank shape at M = 8 and of every shape with
+    M * topk * inter <= 262144; one element more does not fit."""
+    assert abi.awq_moe_workspace_bytes(abi.make_dims(512, 2560, 160, 3), 8, 10) <= abi.NOALLOC_SCRATCH_BYTES
+    assert abi.awq_moe_workspace_bytes(abi.make_dims(4, 256, 2048, 3), 4, 32) == abi.NOALLOC_SCRATCH_BYTES
+    assert abi.awq_moe_workspace_bytes(abi.make_dims(4, 256, 2048, 3), 5, 32) > abi.NOALLOC_SCRATCH_BYTES
 
 
 def test_workspace_grows_with_tokens():
