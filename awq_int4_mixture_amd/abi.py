@@ -27,7 +27,8 @@ WS_ACT_OFFSET = 256
 
 EXPORTED = (
     "awq_moe_bank_layout_query", "awq_moe_prepare", "awq_moe_workspace_bytes",
-    "awq_moe_route_compact", "awq_moe_decode", "awq_moe_decode_noalloc", "awq_moe_w13_swiglu", "awq_moe_w2_reduce",
+    "awq_moe_route_compact", "awq_moe_decode", "awq_moe_decode_noalloc", "awq_moe_decode_rmsnorm_residual",
+    "awq_moe_w13_swiglu", "awq_moe_w2_reduce",
     "awq_moe_dequant", "awq_moe_router_topk", "awq_moe_residual_rmsnorm", "awq_moe_router_residual",
     "awq_moe_router_gemv", "awq_moe_prefill_workspace_bytes", "awq_moe_prefill", "awq_moe_last_error",
 )
@@ -71,6 +72,7 @@ def _load() -> ctypes.CDLL:
         "awq_moe_route_compact": [P, I32, I32, I32, P, P, P, P, P, V],
         "awq_moe_decode": [D, P, U64, P, P, P, I32, I32, P, P, U64, V],
         "awq_moe_decode_noalloc": [D, P, U64, P, P, P, I32, I32, P, P, V],
+        "awq_moe_decode_rmsnorm_residual": [D, P, U64, P, ctypes.c_float, P, P, I32, I32, P, P, U64, V],
         "awq_moe_prefill_workspace_bytes": [D, I32, I32, ctypes.POINTER(ctypes.c_uint64)],
         "awq_moe_prefill": [D, P, U64, P, P, P, I32, I32, P, P, U64, V],
         "awq_moe_w13_swiglu": [D, P, U64, P, P, I32, I32, P, U64, V],
@@ -245,6 +247,25 @@ def awq_moe_decode_noalloc(dims: awq_moe_dims, bank, x, topk_ids, topk_w, out=No
         _dev(topk_ids, torch.int32, (M, k), "topk_ids"), _dev(topk_w, torch.float32, (M, k), "topk_w"), M, k,
         _dev(out, torch.float16, (M, dims.hidden), "out"), sp, _stream(stream)), "awq_moe_decode_noalloc")
     return out
+
+
+def awq_moe_decode_rmsnorm_residual(dims: awq_moe_dims, bank, r, topk_ids, topk_w, eps: float = 1e-6, r_next=None,
+                                    workspace=None, stream=None):
+    """One stacked layer: r_next = fp16(r + stage(fp16(rms_norm(r)))). Returns r_next."""
+    torch = _torch()
+    M, H = r.shape
+    k = topk_ids.shape[1]
+    if r_next is None:
+        r_next = torch.empty_like(r)
+    if workspace is None:
+        workspace = alloc_workspace(dims, M, k, r.device)
+    _check(_lib.awq_moe_decode_rmsnorm_residual(
+        ctypes.byref(dims), _dev(bank, torch.uint8, name="bank"), bank.numel(),
+        _dev(r, torch.float16, (M, dims.hidden), "r"), eps,
+        _dev(topk_ids, torch.int32, (M, k), "topk_ids"), _dev(topk_w, torch.float32, (M, k), "topk_w"), M, k,
+        _dev(r_next, torch.float16, (M, dims.hidden), "r_next"), _dev(workspace, torch.uint8, name="workspace"),
+        workspace.numel(), _stream(stream)), "awq_moe_decode_rmsnorm_residual")
+    return r_next
 
 
 def awq_moe_prefill_workspace_bytes(dims: awq_moe_dims, max_tokens: int, topk: int) -> int:

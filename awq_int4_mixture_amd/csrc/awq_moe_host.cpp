@@ -143,8 +143,8 @@ int check_route_ptrs(const int32_t* ids, const int32_t* offsets, const int32_t* 
 }
 
 int check_router_args(const float* logits, int32_t M, int32_t num_experts, int32_t topk, const int32_t* topk_ids,
-                      const float* topk_w) {
-  if (M < 1 || M > AWQ_MOE_MAX_TOKENS) return fail(AWQ_MOE_EINVAL, "M %d outside [1, %d]", M, AWQ_MOE_MAX_TOKENS);
+                      const float* topk_w, int32_t max_rows = AWQ_MOE_MAX_TOKENS) {
+  if (M < 1 || M > max_rows) return fail(AWQ_MOE_EINVAL, "M %d outside [1, %d]", M, max_rows);
   if (num_experts < 1 || num_experts > AWQ_MOE_MAX_ROUTER_EXPERTS)
     return fail(AWQ_MOE_EINVAL, "num_experts %d outside [1, %d]", num_experts, AWQ_MOE_MAX_ROUTER_EXPERTS);
   if (topk < 1 || topk > AWQ_MOE_MAX_TOPK || topk > num_experts)
@@ -338,7 +338,7 @@ int awq_moe_route_compact(const int32_t* topk_ids, int32_t M, int32_t topk, int3
 
 int awq_moe_router_topk(const float* logits, int32_t M, int32_t num_experts, int32_t topk, int32_t* topk_ids,
                         float* topk_w, void* stream) {
-  int rc = check_router_args(logits, M, num_experts, topk, topk_ids, topk_w);
+  int rc = check_router_args(logits, M, num_experts, topk, topk_ids, topk_w, AWQ_MOE_MAX_ROUTER_ROWS);
   if (rc) return rc;
   if ((rc = check_device())) return rc;
   return hip_status(awq_moe::launch_router_topk(logits, M, num_experts, topk, topk_ids, topk_w,
@@ -391,7 +391,7 @@ int awq_moe_w13_swiglu(const awq_moe_dims* dims, const void* bank, uint64_t bank
   if (!x || !aligned(x, 16)) return fail(AWQ_MOE_EINVAL, "x null or not 16-byte aligned");
   if (!topk_ids || !aligned(topk_ids, 4)) return fail(AWQ_MOE_EINVAL, "topk_ids null or misaligned");
   if ((rc = check_device())) return rc;
-  return hip_status(awq_moe::launch_w13_swiglu(stage_args(dims, bank, topk_ids, M, topk), x, workspace,
+  return hip_status(awq_moe::launch_w13_swiglu(stage_args(dims, bank, topk_ids, M, topk), x, workspace, false, 0.f,
                                                static_cast<hipStream_t>(stream)),
                     "w13 launch");
 }
@@ -406,7 +406,7 @@ int awq_moe_w2_reduce(const awq_moe_dims* dims, const void* bank, uint64_t bank_
   if (!out || !aligned(out, 16)) return fail(AWQ_MOE_EINVAL, "out null or not 16-byte aligned");
   if ((rc = check_device())) return rc;
   const WsPtrs w = ws_ptrs(workspace);
-  return hip_status(awq_moe::launch_w2_reduce(stage_args(dims, bank, topk_ids, M, topk), w.act, topk_w, out,
+  return hip_status(awq_moe::launch_w2_reduce(stage_args(dims, bank, topk_ids, M, topk), w.act, topk_w, out, nullptr,
                                               static_cast<hipStream_t>(stream)),
                     "w2 launch");
 }
@@ -502,9 +502,32 @@ int awq_moe_decode(const awq_moe_dims* dims, const void* bank, uint64_t bank_byt
   const WsPtrs w = ws_ptrs(workspace);
   hipStream_t s = static_cast<hipStream_t>(stream);
   const awq_moe::StageArgs a = stage_args(dims, bank, topk_ids, M, topk);
-  hipError_t e = awq_moe::launch_w13_swiglu(a, x, workspace, s);
+  hipError_t e = awq_moe::launch_w13_swiglu(a, x, workspace, false, 0.f, s);
   if (e != hipSuccess) return hip_status(e, "w13 launch");
-  return hip_status(awq_moe::launch_w2_reduce(a, w.act, topk_w, out, s), "w2 launch");
+  return hip_status(awq_moe::launch_w2_reduce(a, w.act, topk_w, out, nullptr, s), "w2 launch");
+}
+
+int awq_moe_decode_rmsnorm_residual(const awq_moe_dims* dims, const void* bank, uint64_t bank_bytes,
+                                    const uint16_t* r, float eps, const int32_t* topk_ids, const float* topk_w,
+                                    int32_t M, int32_t topk, uint16_t* r_next, void* workspace,
+                                    uint64_t workspace_bytes, void* stream) {
+  int rc = check_stage(dims, bank, bank_bytes, M, topk, workspace, workspace_bytes);
+  if (rc) return rc;
+  if (!(eps > 0.f) || eps > 1.f) return fail(AWQ_MOE_EINVAL, "eps must be in (0, 1]");
+  if (!r || !r_next || !aligned(r, 16) || !aligned(r_next, 16))
+    return fail(AWQ_MOE_EINVAL, "r or r_next null or not 16-byte aligned");
+  const uint64_t nb = (uint64_t)M * dims->hidden * 2;
+  const uintptr_t pa = reinterpret_cast<uintptr_t>(r), pb = reinterpret_cast<uintptr_t>(r_next);
+  if (pa < pb + nb && pb < pa + nb) return fail(AWQ_MOE_EINVAL, "r_next must not overlap r");
+  if (!topk_ids || !aligned(topk_ids, 4)) return fail(AWQ_MOE_EINVAL, "topk_ids null or misaligned");
+  if (!topk_w || !aligned(topk_w, 4)) return fail(AWQ_MOE_EINVAL, "topk_w null or misaligned");
+  if ((rc = check_device())) return rc;
+  const WsPtrs w = ws_ptrs(workspace);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const awq_moe::StageArgs a = stage_args(dims, bank, topk_ids, M, topk);
+  hipError_t e = awq_moe::launch_w13_swiglu(a, r, workspace, true, eps, s);
+  if (e != hipSuccess) return hip_status(e, "w13 launch");
+  return hip_status(awq_moe::launch_w2_reduce(a, w.act, topk_w, r_next, r, s), "w2 launch");
 }
 
 int awq_moe_decode_noalloc(const awq_moe_dims* dims, const void* bank, uint64_t bank_bytes, const uint16_t* x,
@@ -531,9 +554,9 @@ int awq_moe_decode_noalloc(const awq_moe_dims* dims, const void* bank, uint64_t 
   const WsPtrs w = ws_ptrs(ws);
   hipStream_t s = static_cast<hipStream_t>(stream);
   const awq_moe::StageArgs a = stage_args(dims, bank, topk_ids, M, topk);
-  e = awq_moe::launch_w13_swiglu(a, x, ws, s);
+  e = awq_moe::launch_w13_swiglu(a, x, ws, false, 0.f, s);
   if (e != hipSuccess) return hip_status(e, "w13 launch");
-  e = awq_moe::launch_w2_reduce(a, w.act, topk_w, out, s);
+  e = awq_moe::launch_w2_reduce(a, w.act, topk_w, out, nullptr, s);
   if (e != hipSuccess) return hip_status(e, "w2 launch");
   if (status) return hip_status(hipMemcpyAsync(status, w.status, 4, hipMemcpyDeviceToDevice, s), "status copy");
   return ok();

@@ -40,9 +40,12 @@ struct RouteOut {
 
 hipError_t launch_route_compact(const int32_t* ids, int n, int E, const RouteOut& o, hipStream_t stream);
 // ws: the decode workspace (status word and act at the offsets above).
-hipError_t launch_w13_swiglu(const StageArgs& a, const uint16_t* x, void* ws, hipStream_t stream);
+// norm: x is a residual row r and the stage consumes fp16(rms_norm(r, eps)).
+hipError_t launch_w13_swiglu(const StageArgs& a, const uint16_t* x, void* ws, bool norm, float eps,
+                             hipStream_t stream);
+// resid non-null: out receives fp16(resid + fp16(result)).
 hipError_t launch_w2_reduce(const StageArgs& a, const uint16_t* act, const float* topk_w, uint16_t* out,
-                            hipStream_t stream);
+                            const uint16_t* resid, hipStream_t stream);
 hipError_t launch_router_topk(const float* logits, int M, int E, int k, int32_t* ids, float* w, hipStream_t stream);
 // r_next and x may not alias r or delta.
 hipError_t launch_residual_rmsnorm(const uint16_t* r, const uint16_t* delta, int M, int H, float eps,

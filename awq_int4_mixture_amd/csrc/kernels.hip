@@ -313,10 +313,76 @@ __global__ __launch_bounds__(1024) void route_compact_kernel(const int32_t* __re
 __host__ __device__ constexpr uint32_t pack_dims(int H, int I, int topk, int M) {
   return (uint32_t)(H >> 5) | ((uint32_t)(I >> 5) << 9) | ((uint32_t)topk << 16) | ((uint32_t)M << 22);
 }
-__device__ __forceinline__ int dims_G(uint32_t d) { return (int)(d & 0x1FFu); }
-__device__ __forceinline__ int dims_G2(uint32_t d) { return (int)((d >> 9) & 0x7Fu); }
-__device__ __forceinline__ int dims_topk(uint32_t d) { return (int)((d >> 16) & 0x3Fu); }
-__device__ __forceinline__ int dims_M(uint32_t d) { return (int)((d >> 22) & 0xFu); }
+__host__ __device__ __forceinline__ int dims_G(uint32_t d) { return (int)(d & 0x1FFu); }
+__host__ __device__ __forceinline__ int dims_G2(uint32_t d) { return (int)((d >> 9) & 0x7Fu); }
+__host__ __device__ __forceinline__ int dims_topk(uint32_t d) { return (int)((d >> 16) & 0x3Fu); }
+__host__ __device__ __forceinline__ int dims_M(uint32_t d) { return (int)((d >> 22) & 0xFu); }
+
+// The bank layout of one expert block, from the shape word and the record
+// size (the sections of the layout: W13 units, W13 records, W2 units, W2
+// records, each padded to 256 bytes). Unit sections are multiples of 256
+// already (1024 G G2 and 512 G G2 bytes). Kernels that compute it keep two
+// argument registers free; the launcher checks it against the host layout.
+struct ExpertGeometry {
+  uint32_t expert_bytes, w2_off, w2_meta_delta;
+};
+
+template <int RB>
+__host__ __device__ __forceinline__ ExpertGeometry expert_geometry(uint32_t d) {
+  const uint32_t G = (uint32_t)dims_G(d), G2 = (uint32_t)dims_G2(d);
+  const uint32_t w13_units = 1024u * G * G2, w13_meta = 64u * G * G2 * RB;
+  const uint32_t w2_units = 512u * G * G2, w2_meta = 32u * G * G2 * RB;
+  ExpertGeometry g;
+  g.w2_off = w13_units + ((w13_meta + 255u) & ~255u);
+  g.w2_meta_delta = w2_units;
+  g.expert_bytes = g.w2_off + w2_units + ((w2_meta + 255u) & ~255u);
+  return g;
+}
+
+// Sum of squares of a row of H fp16 values and 1/sqrt(mean + eps), in the
+// order of the residual/RMS-norm kernel: per run of 8 values (values
+// 8i .. 8i+7, run i) an fmaf chain; the runs of each 64-lane wave summed with
+// wave_sum_xor_order, run i in lane i; the waves' sums added in wave order.
+// run_ss holds run t's chain in lane t (0 for t >= H/8); part is 16 floats
+// of the caller's LDS. Every thread of the workgroup must call it (one
+// barrier).
+__device__ __forceinline__ float row_inv_rms(float run_ss, int H, float eps, float* part) {
+  const float s = wave_sum_xor_order(run_ss);
+  if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = s;
+  __syncthreads();
+  const int nw = ((H >> 3) + 63) >> 6;
+  float tot = 0.f;
+  for (int i = 0; i < nw; ++i) tot += part[i];
+  return 1.0f / sqrtf(tot / (float)H + eps);
+}
+
+// fmaf chain of the squares of the 8 fp16 values in 4 packed pairs.
+__device__ __forceinline__ float run_sumsq(uint32_t a, uint32_t b, uint32_t c, uint32_t d) {
+  const uint32_t px[4] = {a, b, c, d};
+  float ss = 0.f;
+#pragma unroll
+  for (int p = 0; p < 4; ++p) {
+    const h2_t v = as_h2(px[p]);
+    ss = fmaf((float)v.x, (float)v.x, ss);
+    ss = fmaf((float)v.y, (float)v.y, ss);
+  }
+  return ss;
+}
+
+// Pair p of run q (q = 0..3) of a group's 16 packed pairs, selected without
+// a dynamic index (which would place the array in memory).
+__device__ __forceinline__ uint32_t pick_run_pair(const Act32& a, int q, int p) {
+  return q == 0 ? a.px[p] : q == 1 ? a.px[4 + p] : q == 2 ? a.px[8 + p] : a.px[12 + p];
+}
+
+// A packed pair scaled and rounded as the norm does: fp16((float)v * inv).
+__device__ __forceinline__ uint32_t norm_pair(uint32_t v, float inv) {
+  const h2_t a = as_h2(v);
+  h2_t o;
+  o.x = (_Float16)((float)a.x * inv);
+  o.y = (_Float16)((float)a.y * inv);
+  return __builtin_bit_cast(uint32_t, o);
+}
 
 // ---------------------------------------------------------------------------
 // W13 + SwiGLU: grid (2I/16 column tiles, n slots), ceil(H/8 / 64) waves.
@@ -332,19 +398,24 @@ __device__ __forceinline__ int dims_M(uint32_t d) { return (int)((d >> 22) & 0xF
 // Wave 0 of workgroup (0, 0) also writes the status word; its id loads are
 // issued first and consumed after the weight loads are in flight.
 // ---------------------------------------------------------------------------
-template <int RB>
+// With NORM, x is a residual row r and the activations are
+// fp16(r / sqrt(mean(r^2) + eps)), computed by every workgroup of the token
+// from the row it loads anyway, bit-identical to the residual/RMS-norm
+// kernel's x: lane t (t = 4g + quad) holds values 32g .. 32g+31 and takes run
+// t (its quad's 8 values) for the sum of squares, as that kernel's thread t
+// does.
+template <int RB, bool NORM>
 __global__ __launch_bounds__(1024) void w13_swiglu_kernel(const int32_t* __restrict__ ids,
                                                           const uint8_t* __restrict__ units_base,
                                                           const uint16_t* __restrict__ x, uint8_t* __restrict__ ws,
                                                           uint32_t expert_bytes, uint32_t meta_delta, uint32_t dims,
-                                                          int E) {
+                                                          int E, float eps) {
   __shared__ float red[16][16];  // [wave][column]
   const int nt = blockIdx.x, s = blockIdx.y;
   const int e = ids[s];  // scalar load
   const int G = dims_G(dims), I = 32 * dims_G2(dims), topk = dims_topk(dims);
   const int H = 32 * G, L = 4 * G, nwaves = (L + 63) >> 6;
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
-  const int g = t >> 2;
   const bool status_wave = nt == 0 && s == 0 && wave == 0;
   const int n = topk * dims_M(dims);  // <= 256 slots: four per lane of one wave
   int sid[4];
@@ -352,18 +423,21 @@ __global__ __launch_bounds__(1024) void w13_swiglu_kernel(const int32_t* __restr
 #pragma unroll
     for (int q = 0; q < 4; ++q) sid[q] = lane + 64 * q < n ? ids[lane + 64 * q] : 0;
   }
-  Act32 av;
-  if (t < L) av = load_act32(x + (uint64_t)(s / topk) * H + 32 * g);
+  // Every load below is issued by every lane (lanes past L and invalid
+  // slots read valid addresses they do not use), so the code is
+  // straight-line and each wait covers exactly the loads its use needs.
+  const int tc = t < L ? t : 0;
+  Act32 av = load_act32(x + (uint64_t)(s / topk) * H + 32 * (tc >> 2));
+  // the activations are requested before the wait for the id
+  __builtin_amdgcn_sched_barrier(0);
   const bool live = e >= 0 && e < E;
-  const uint64_t eo = (uint64_t)(uint32_t)e * expert_bytes;
+  const uint64_t eo = (uint64_t)(uint32_t)(live ? e : 0) * expert_bytes;
+  const uint8_t* units = units_base + eo + (uint64_t)nt * 256u * G;
+  const RawRecords<RB> rraw =
+      load_records_raw<RB>(units_base + eo + meta_delta + (uint64_t)nt * 16u * G * RB + (uint64_t)tc * 4u * RB);
   uint4 w[4];
-  RawRecords<RB> rraw;
-  if (live && t < L) {
-    const uint8_t* units = units_base + eo + (uint64_t)nt * 256u * G;
-    rraw = load_records_raw<RB>(units_base + eo + meta_delta + (uint64_t)nt * 16u * G * RB + (uint64_t)t * 4u * RB);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) w[j] = *reinterpret_cast<const uint4*>(units + ((uint64_t)j * L + t) * 16u);
-  }
+  for (int j = 0; j < 4; ++j) w[j] = *reinterpret_cast<const uint4*>(units + ((uint64_t)j * L + tc) * 16u);
   if (status_wave) {
     bool bad = false;
 #pragma unroll
@@ -372,6 +446,19 @@ __global__ __launch_bounds__(1024) void w13_swiglu_kernel(const int32_t* __restr
     if (lane == 0) *reinterpret_cast<uint32_t*>(ws + AWQ_MOE_KWS_STATUS_OFFSET) = b ? AWQ_MOE_STATUS_BAD_ID_BIT : 0u;
   }
   if (!live) return;  // invalid slot: no row (uniform over the workgroup)
+  if constexpr (NORM) {
+    // after the weight loads: the norm must not delay them
+    __builtin_amdgcn_sched_barrier(0);
+    __shared__ float norm_part[16];
+    const int q = t & 3;
+    const float ss = run_sumsq(pick_run_pair(av, q, 0), pick_run_pair(av, q, 1), pick_run_pair(av, q, 2),
+                               pick_run_pair(av, q, 3));
+    const float inv = row_inv_rms(t < L ? ss : 0.f, H, eps, norm_part);
+    if (t < L) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) av.px[i] = norm_pair(av.px[i], inv);
+    }
+  }
   float part[4] = {0.f, 0.f, 0.f, 0.f};
   if (t < L) {
     float S, Cs;
@@ -455,12 +542,15 @@ __device__ __forceinline__ float half_unit_dot(const uint2& w, const Act16& a, c
   return acc;
 }
 
-template <int RB>
+// With NORM, as w13_swiglu_kernel: lane (tu = 4g + quad, half) holds runs
+// 4g + 2 half and 4g + 2 half + 1; the lanes with quad / 2 == half take run
+// tu, which an LDS exchange hands to lane tu for the ordered sum.
+template <int RB, bool NORM>
 __global__ __launch_bounds__(1024) void w13_swiglu_pair_kernel(const int32_t* __restrict__ ids,
                                                                const uint8_t* __restrict__ units_base,
                                                                const uint16_t* __restrict__ x, uint8_t* __restrict__ ws,
                                                                uint32_t expert_bytes, uint32_t meta_delta,
-                                                               uint32_t dims, int E) {
+                                                               uint32_t dims, int E, float eps) {
   __shared__ float red[16][16];  // [wave][column]
   const int nt = blockIdx.x, s = blockIdx.y;
   const int e = ids[s];  // scalar load
@@ -468,7 +558,6 @@ __global__ __launch_bounds__(1024) void w13_swiglu_pair_kernel(const int32_t* __
   const int H = 32 * G, L = 4 * G, nwaves = (2 * L + 63) >> 6;
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
   const int tu = t >> 1, hf = t & 1;  // unit lane (4g + quad) and half
-  const int g = tu >> 2;
   const bool status_wave = nt == 0 && s == 0 && wave == 0;
   const int n = topk * dims_M(dims);  // <= 256 slots: four per lane of one wave
   int sid[4];
@@ -476,18 +565,19 @@ __global__ __launch_bounds__(1024) void w13_swiglu_pair_kernel(const int32_t* __
 #pragma unroll
     for (int q = 0; q < 4; ++q) sid[q] = lane + 64 * q < n ? ids[lane + 64 * q] : 0;
   }
-  Act16 av;
-  if (tu < L) av = load_act16(x + (uint64_t)(s / topk) * H + 32 * g + 16 * hf);
+  // Every load below is issued by every lane (see w13_swiglu_kernel).
+  const int tuc = tu < L ? tu : 0;
+  Act16 av = load_act16(x + (uint64_t)(s / topk) * H + 32 * (tuc >> 2) + 16 * hf);
+  // the activations are requested before the wait for the id
+  __builtin_amdgcn_sched_barrier(0);
   const bool live = e >= 0 && e < E;
-  const uint64_t eo = (uint64_t)(uint32_t)e * expert_bytes;
+  const uint64_t eo = (uint64_t)(uint32_t)(live ? e : 0) * expert_bytes;
+  const uint8_t* units = units_base + eo + (uint64_t)nt * 256u * G + 8u * hf;
+  const RawRecords<RB> rraw =
+      load_records_raw<RB>(units_base + eo + meta_delta + (uint64_t)nt * 16u * G * RB + (uint64_t)tuc * 4u * RB);
   uint2 w[4];
-  RawRecords<RB> rraw;
-  if (live && tu < L) {
-    const uint8_t* units = units_base + eo + (uint64_t)nt * 256u * G + 8u * hf;
-    rraw = load_records_raw<RB>(units_base + eo + meta_delta + (uint64_t)nt * 16u * G * RB + (uint64_t)tu * 4u * RB);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) w[j] = *reinterpret_cast<const uint2*>(units + ((uint64_t)j * L + tu) * 16u);
-  }
+  for (int j = 0; j < 4; ++j) w[j] = *reinterpret_cast<const uint2*>(units + ((uint64_t)j * L + tuc) * 16u);
   if (status_wave) {
     bool bad = false;
 #pragma unroll
@@ -496,6 +586,23 @@ __global__ __launch_bounds__(1024) void w13_swiglu_pair_kernel(const int32_t* __
     if (lane == 0) *reinterpret_cast<uint32_t*>(ws + AWQ_MOE_KWS_STATUS_OFFSET) = b ? AWQ_MOE_STATUS_BAD_ID_BIT : 0u;
   }
   if (!live) return;  // invalid slot: no row (uniform over the workgroup)
+  if constexpr (NORM) {
+    // after the weight loads: the norm must not delay them
+    __builtin_amdgcn_sched_barrier(0);
+    __shared__ float runs[512];  // H <= 4096 here: at most 512 runs
+    const int quad = tu & 3;
+    const bool hi = quad & 1;
+    if (tu < L && (quad >> 1) == hf)
+      runs[tu] = run_sumsq(hi ? av.px[4] : av.px[0], hi ? av.px[5] : av.px[1], hi ? av.px[6] : av.px[2],
+                           hi ? av.px[7] : av.px[3]);
+    __syncthreads();
+    __shared__ float norm_part[16];
+    const float inv = row_inv_rms(t < L ? runs[t] : 0.f, H, eps, norm_part);
+    if (tu < L) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) av.px[i] = norm_pair(av.px[i], inv);
+    }
+  }
   float p0 = 0.f, p1 = 0.f, p2 = 0.f, p3 = 0.f;
   if (tu < L) {
     float S, Cs;
@@ -541,13 +648,15 @@ __global__ __launch_bounds__(1024) void w13_swiglu_pair_kernel(const int32_t* __
 // Wave 0 ranks the slots with lane shuffles while the weight loads are in
 // flight.
 // ---------------------------------------------------------------------------
-template <int RB, int TPW>
+// With RES, out receives fp16(resid + fp16(result)) (the residual update of
+// a stacked layer) instead of fp16(result).
+template <int RB, int TPW, bool RES>
 __global__ __launch_bounds__(1024) void w2_reduce_kernel(const int32_t* __restrict__ topk_ids,
                                                          const uint8_t* __restrict__ units_base,
                                                          const uint8_t* __restrict__ recs_base,
                                                          const uint16_t* __restrict__ act, uint64_t expert_bytes, int H,
                                                          int I, int topk, int E, const float* __restrict__ topk_w,
-                                                         uint16_t* __restrict__ out) {
+                                                         uint16_t* __restrict__ out, const uint16_t* __restrict__ resid) {
   constexpr int NC = 16 * TPW;                     // columns per workgroup
   __shared__ float red[4096];                      // [slot in pass][tile][g][16]; <= 4*blockDim
   __shared__ float ys[AWQ_MOE_KMAX_TOPK * NC];     // [rank][NC]: a valid slot's column results
@@ -628,8 +737,11 @@ __global__ __launch_bounds__(1024) void w2_reduce_kernel(const int32_t* __restri
     const int nv = nvalid_s;
     float acc = 0.f;
 #pragma unroll 4
-    for (int r = 0; r < nv; ++r) acc = fmaf(wr[r], ys[r * NC + t], acc);
-    out[(uint64_t)tok * H + nt0 * 16 + t] = __builtin_bit_cast(uint16_t, (_Float16)acc);
+    for (int rr = 0; rr < nv; ++rr) acc = fmaf(wr[rr], ys[rr * NC + t], acc);
+    const uint64_t o = (uint64_t)tok * H + nt0 * 16 + t;
+    _Float16 v = (_Float16)acc;
+    if constexpr (RES) v = (_Float16)((float)__builtin_bit_cast(_Float16, resid[o]) + (float)v);
+    out[o] = __builtin_bit_cast(uint16_t, v);
   }
 }
 
@@ -652,13 +764,18 @@ __global__ __launch_bounds__(1024) void w2_reduce_kernel(const int32_t* __restri
 // slot's 16 column results go to LDS at its rank; one barrier, then the
 // router-weighted sum in ascending (expert, slot) order.
 // ---------------------------------------------------------------------------
-template <int RB, int SPW>
+// With RES, out receives fp16(resid + fp16(result)) (the residual update of
+// a stacked layer); resid's value is requested at the start, off the id
+// chain. The expert stride and record offset come from the shape word
+// (expert_geometry), which keeps resid within the preloaded argument
+// registers.
+template <int RB, int SPW, bool RES>
 __global__ __launch_bounds__(1024) void w2_reduce_seg_kernel(const int32_t* __restrict__ topk_ids,
                                                              const uint8_t* __restrict__ units_base,
                                                              const uint16_t* __restrict__ act,
                                                              const float* __restrict__ topk_w,
-                                                             uint16_t* __restrict__ out, uint32_t expert_bytes,
-                                                             uint32_t meta_delta, uint32_t dims, int E) {
+                                                             uint16_t* __restrict__ out, uint32_t dims, int E,
+                                                             const uint16_t* __restrict__ resid) {
   __shared__ __attribute__((aligned(16))) float red[AWQ_MOE_KMAX_TOPK * 8 * 16];  // [slot][g][16]
   __shared__ __attribute__((aligned(16))) float ys[AWQ_MOE_KMAX_TOPK * 16];       // [rank][16]
   __shared__ float wr[AWQ_MOE_KMAX_TOPK];                                         // rank -> router weight
@@ -671,6 +788,10 @@ __global__ __launch_bounds__(1024) void w2_reduce_seg_kernel(const int32_t* __re
   const int t = threadIdx.x, lane = t & 63;
   const int s0 = __builtin_amdgcn_readfirstlane(t >> 6) * SPW;  // the wave's first slot
   const int32_t* ids = topk_ids + tok * topk;
+  const ExpertGeometry geo = expert_geometry<RB>(dims);
+  const uint32_t expert_bytes = geo.expert_bytes, meta_delta = geo.w2_meta_delta;
+  uint16_t rv = 0;
+  if constexpr (RES) rv = resid[(uint64_t)tok * H + nt * 16 + (t & 15)];  // used by t < 16
   // the wave's ids and router weights, indexes clamped into the token's slots
   int ek[SPW];
   float wk[SPW];
@@ -761,8 +882,10 @@ __global__ __launch_bounds__(1024) void w2_reduce_seg_kernel(const int32_t* __re
     const int nv = nvalid_s;
     float acc = 0.f;
 #pragma unroll 4
-    for (int r = 0; r < nv; ++r) acc = fmaf(wr[r], ys[r * 16 + t], acc);
-    out[(uint64_t)tok * H + nt * 16 + t] = __builtin_bit_cast(uint16_t, (_Float16)acc);
+    for (int rr = 0; rr < nv; ++rr) acc = fmaf(wr[rr], ys[rr * 16 + t], acc);
+    _Float16 v = (_Float16)acc;
+    if constexpr (RES) v = (_Float16)((float)__builtin_bit_cast(_Float16, rv) + (float)v);
+    out[(uint64_t)tok * H + nt * 16 + t] = __builtin_bit_cast(uint16_t, v);
   }
 }
 
@@ -853,90 +976,98 @@ static bool fits32(const StageArgs& a, uint64_t meta_delta) {
   return a.expert_bytes <= 0xFFFFFFFFull && meta_delta <= 0xFFFFFFFFull;
 }
 
-hipError_t launch_w13_swiglu(const StageArgs& a, const uint16_t* x, void* ws, hipStream_t stream) {
-  const uint64_t md = a.w13_meta_off - a.w13_off;
-  if (!fits32(a, md)) return hipErrorInvalidValue;
+template <int RB, bool NORM>
+static void launch_w13_t(const StageArgs& a, const uint16_t* x, uint8_t* w, uint32_t md, float eps, hipStream_t stream) {
   const int L = 4 * (a.H / 32);
   const dim3 grid((2 * a.I) / 16, a.M * a.topk);
   const uint32_t dims = pack_dims(a.H, a.I, a.topk, a.M);
-  uint8_t* w = static_cast<uint8_t*>(ws);
   // Lane pairs when every workgroup has a CU to itself (MI355X: 256 CUs), where
   // the busiest SIMD sets the time; with more workgroups the pair kernel's
   // 8-byte loads cost more than it saves (M = 8: 7.6 -> 9.3 us).
-  if (2 * L <= 1024 && (uint64_t)grid.x * grid.y <= 256) {
-    const dim3 block(((2 * L + 63) / 64) * 64);
-    if (a.RB == 4)
-      hipLaunchKernelGGL(w13_swiglu_pair_kernel<4>, grid, block, 0, stream, a.topk_ids, a.bank + a.w13_off, x, w,
-                         (uint32_t)a.expert_bytes, (uint32_t)md, dims, a.E);
-    else
-      hipLaunchKernelGGL(w13_swiglu_pair_kernel<3>, grid, block, 0, stream, a.topk_ids, a.bank + a.w13_off, x, w,
-                         (uint32_t)a.expert_bytes, (uint32_t)md, dims, a.E);
-    return hipGetLastError();
-  }
-  const dim3 block(((L + 63) / 64) * 64);
-  if (a.RB == 4)
-    hipLaunchKernelGGL(w13_swiglu_kernel<4>, grid, block, 0, stream, a.topk_ids, a.bank + a.w13_off, x, w,
-                       (uint32_t)a.expert_bytes, (uint32_t)md, dims, a.E);
+  if (2 * L <= 1024 && (uint64_t)grid.x * grid.y <= 256)
+    hipLaunchKernelGGL((w13_swiglu_pair_kernel<RB, NORM>), grid, dim3(((2 * L + 63) / 64) * 64), 0, stream,
+                       a.topk_ids, a.bank + a.w13_off, x, w, (uint32_t)a.expert_bytes, md, dims, a.E, eps);
   else
-    hipLaunchKernelGGL(w13_swiglu_kernel<3>, grid, block, 0, stream, a.topk_ids, a.bank + a.w13_off, x, w,
-                       (uint32_t)a.expert_bytes, (uint32_t)md, dims, a.E);
+    hipLaunchKernelGGL((w13_swiglu_kernel<RB, NORM>), grid, dim3(((L + 63) / 64) * 64), 0, stream, a.topk_ids,
+                       a.bank + a.w13_off, x, w, (uint32_t)a.expert_bytes, md, dims, a.E, eps);
+}
+
+hipError_t launch_w13_swiglu(const StageArgs& a, const uint16_t* x, void* ws, bool norm, float eps,
+                             hipStream_t stream) {
+  const uint64_t md = a.w13_meta_off - a.w13_off;
+  if (!fits32(a, md)) return hipErrorInvalidValue;
+  uint8_t* w = static_cast<uint8_t*>(ws);
+  if (a.RB == 4) {
+    if (norm) launch_w13_t<4, true>(a, x, w, (uint32_t)md, eps, stream);
+    else launch_w13_t<4, false>(a, x, w, (uint32_t)md, eps, stream);
+  } else {
+    if (norm) launch_w13_t<3, true>(a, x, w, (uint32_t)md, eps, stream);
+    else launch_w13_t<3, false>(a, x, w, (uint32_t)md, eps, stream);
+  }
   return hipGetLastError();
 }
 
-template <int RB, int TPW>
+template <int RB, int TPW, bool RES>
 static void launch_w2_t(const StageArgs& a, const uint16_t* act, const float* topk_w, uint16_t* out,
-                        hipStream_t stream) {
+                        const uint16_t* resid, hipStream_t stream) {
   const int lanes = a.topk * TPW * 4 * (a.I / 32);
   const dim3 block(lanes >= 1024 ? 1024 : ((lanes + 63) / 64) * 64);
   const dim3 grid(a.H / (16 * TPW), a.M);
-  hipLaunchKernelGGL((w2_reduce_kernel<RB, TPW>), grid, block, 0, stream, a.topk_ids, a.bank + a.w2_off,
-                     a.bank + a.w2_meta_off, act, a.expert_bytes, a.H, a.I, a.topk, a.E, topk_w, out);
+  hipLaunchKernelGGL((w2_reduce_kernel<RB, TPW, RES>), grid, block, 0, stream, a.topk_ids, a.bank + a.w2_off,
+                     a.bank + a.w2_meta_off, act, a.expert_bytes, a.H, a.I, a.topk, a.E, topk_w, out, resid);
 }
 
 // One 16-column tile per workgroup: groups of 2 or 4 adjacent tiles (longer
 // contiguous runs per expert) measured no faster, at 4 slower, on hot and
 // on cold weights.
-template <int RB, int SPW>
+template <int RB, int SPW, bool RES>
 static void launch_w2_seg(const StageArgs& a, const uint16_t* act, const float* topk_w, uint16_t* out,
-                          uint32_t md, hipStream_t stream) {
+                          const uint16_t* resid, hipStream_t stream) {
   const int waves = (a.topk + SPW - 1) / SPW;
   const dim3 grid(a.H / 16, a.M);
-  hipLaunchKernelGGL((w2_reduce_seg_kernel<RB, SPW>), grid, dim3(64 * waves), 0, stream, a.topk_ids, a.bank + a.w2_off,
-                     act, topk_w, out, (uint32_t)a.expert_bytes, md, pack_dims(a.H, a.I, a.topk, a.M), a.E);
+  hipLaunchKernelGGL((w2_reduce_seg_kernel<RB, SPW, RES>), grid, dim3(64 * waves), 0, stream, a.topk_ids,
+                     a.bank + a.w2_off, act, topk_w, out, pack_dims(a.H, a.I, a.topk, a.M), a.E, resid);
 }
 
-template <int RB>
+template <int RB, bool RES>
 static void launch_w2_seg_rb(const StageArgs& a, const uint16_t* act, const float* topk_w, uint16_t* out,
-                             uint32_t md, hipStream_t stream) {
+                             const uint16_t* resid, hipStream_t stream) {
   // slots per wave: the largest instantiated SPW <= floor(64 / LS), LS = I/8 lanes per slot
   const int spw = 64 / (a.I / 8);
-  if (spw >= 16) launch_w2_seg<RB, 16>(a, act, topk_w, out, md, stream);
-  else if (spw >= 8) launch_w2_seg<RB, 8>(a, act, topk_w, out, md, stream);
-  else if (spw >= 5) launch_w2_seg<RB, 5>(a, act, topk_w, out, md, stream);
-  else if (spw >= 4) launch_w2_seg<RB, 4>(a, act, topk_w, out, md, stream);
-  else if (spw >= 3) launch_w2_seg<RB, 3>(a, act, topk_w, out, md, stream);
-  else launch_w2_seg<RB, 2>(a, act, topk_w, out, md, stream);
+  if (spw >= 16) launch_w2_seg<RB, 16, RES>(a, act, topk_w, out, resid, stream);
+  else if (spw >= 8) launch_w2_seg<RB, 8, RES>(a, act, topk_w, out, resid, stream);
+  else if (spw >= 5) launch_w2_seg<RB, 5, RES>(a, act, topk_w, out, resid, stream);
+  else if (spw >= 4) launch_w2_seg<RB, 4, RES>(a, act, topk_w, out, resid, stream);
+  else if (spw >= 3) launch_w2_seg<RB, 3, RES>(a, act, topk_w, out, resid, stream);
+  else launch_w2_seg<RB, 2, RES>(a, act, topk_w, out, resid, stream);
 }
 
-// One 16-column tile per workgroup: groups of 2 or 4 adjacent tiles (longer
-// contiguous runs per expert) measured no faster, at 4 slower, on hot and
-// on cold weights.
-hipError_t launch_w2_reduce(const StageArgs& a, const uint16_t* act, const float* topk_w, uint16_t* out,
-                            hipStream_t stream) {
+template <bool RES>
+static hipError_t launch_w2_res(const StageArgs& a, const uint16_t* act, const float* topk_w, uint16_t* out,
+                                const uint16_t* resid, hipStream_t stream) {
   if (a.I <= 256) {
-    const uint64_t md = a.w2_meta_off - a.w2_off;
-    if (!fits32(a, md)) return hipErrorInvalidValue;
+    // the slot-segment kernel derives the expert geometry from the shape word
+    const ExpertGeometry g = a.RB == 4 ? expert_geometry<4>(pack_dims(a.H, a.I, a.topk, a.M))
+                                       : expert_geometry<3>(pack_dims(a.H, a.I, a.topk, a.M));
+    if (g.expert_bytes != a.expert_bytes || g.w2_off != a.w2_off || g.w2_meta_delta != a.w2_meta_off - a.w2_off)
+      return hipErrorInvalidValue;
     if (a.RB == 4)
-      launch_w2_seg_rb<4>(a, act, topk_w, out, (uint32_t)md, stream);
+      launch_w2_seg_rb<4, RES>(a, act, topk_w, out, resid, stream);
     else
-      launch_w2_seg_rb<3>(a, act, topk_w, out, (uint32_t)md, stream);
+      launch_w2_seg_rb<3, RES>(a, act, topk_w, out, resid, stream);
     return hipGetLastError();
   }
   if (a.RB == 4)
-    launch_w2_t<4, 1>(a, act, topk_w, out, stream);
+    launch_w2_t<4, 1, RES>(a, act, topk_w, out, resid, stream);
   else
-    launch_w2_t<3, 1>(a, act, topk_w, out, stream);
+    launch_w2_t<3, 1, RES>(a, act, topk_w, out, resid, stream);
   return hipGetLastError();
+}
+
+hipError_t launch_w2_reduce(const StageArgs& a, const uint16_t* act, const float* topk_w, uint16_t* out,
+                            const uint16_t* resid, hipStream_t stream) {
+  return resid ? launch_w2_res<true>(a, act, topk_w, out, resid, stream)
+               : launch_w2_res<false>(a, act, topk_w, out, nullptr, stream);
 }
 
 hipError_t launch_dequant(const uint8_t* bank, uint64_t expert_bytes, uint64_t units_off,

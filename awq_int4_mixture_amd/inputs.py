@@ -265,6 +265,35 @@ def rotating_ids(seed: int, calls: int, k: int, E: int) -> np.ndarray:
     return perm[: calls * k].reshape(calls, 1, k).astype(np.int32)
 
 
+def rotating_calls(seed: int, calls: int, M: int, k: int, E: int, banks: int, mode: str, frac: float = 0.6):
+    """Ids for ``calls`` consecutive calls that keep weights cold across banks.
+
+    Call j uses bank b = j % banks and the next window of P experts of that
+    bank's own seeded permutation (windows advance cyclically, so a window
+    comes back only after E / P calls on its bank, i.e. banks * E / P calls
+    in all). mode "distinct": P = M*k, the window shuffled into [M][k] (all
+    slots distinct); mode "pool": P = ceil(frac*M*k), each token draws k
+    distinct experts from the window (shared experts, as ``ids_shared_pool``).
+    Returns a list of (bank, ids int32 [M][k]). Draw order: the permutation of
+    each bank, then per call the shuffle or the tokens' draws."""
+    rng = np.random.Generator(np.random.PCG64(np.random.SeedSequence([int(seed), 0xD0, M, k])))
+    perms = [rng.permutation(E) for _ in range(banks)]
+    P = M * k if mode == "distinct" else max(k, min(E, int(math.ceil(frac * M * k))))
+    out = []
+    for j in range(calls):
+        b = j % banks
+        start = ((j // banks) * P) % E
+        win = perms[b][(start + np.arange(P)) % E]
+        if mode == "distinct":
+            ids = rng.permutation(win).reshape(M, k)
+        elif mode == "pool":
+            ids = np.stack([rng.choice(win, size=k, replace=False) for _ in range(M)])
+        else:
+            raise ValueError(f"unknown mode {mode!r}")
+        out.append((b, ids.astype(np.int32)))
+    return out
+
+
 def router_logits(rng: np.random.Generator, M: int, E: int) -> np.ndarray:
     """fp32 router logits ~ N(0,1), [M][E]."""
     return rng.standard_normal((M, E)).astype(np.float32)

@@ -1,21 +1,30 @@
 """Benchmark of the AWQ int4 MoE expert stage for small-batch decode on one MI355X.
 
 Headline workload: the 512-expert rank-share layer (hidden 2560, local
-intermediate 160, top-k 10, int4 group 32, 4-byte records), M = 1 token,
-the same 10 hot experts on every call, 48 calls per HIP-graph replay with a
-fresh fp16 x ~ N(0,1) and softmax router weights per call (PR #522,
-Operator results: 48 calls per graph replay). One *step* is one replay: 48
-awq_moe_decode calls (W13+SwiGLU, then W2+reduction; two launches each).
+intermediate 160, top-k 10, int4 group 32) with compact 3-byte records, M = 1
+token, cold weights: every call takes 10 experts that no call has touched
+within the last ~1.4 GB of weight traffic. Calls go round robin over four
+device copies of the layer bank (4 x 373.6 MB), each call taking the next
+window of its bank's own expert permutation, and the replays cycle through
+four graphs of 48 calls (PR #522 "Coalesce AWQ QPN W13 compact metadata
+loads...", Operator results: 48 calls per graph replay, hot and rotating
+experts), so nothing a call reads can still sit in the 256 MB MALL or the
+4 MB L2s. One *step* is one replay: 48 awq_moe_decode calls (W13+SwiGLU,
+then W2+reduction; two launches each).
 
 Printed: one JSON line with the layer's achieved weight bandwidth (touched
 weight + record bytes / layer time), per-kernel times from graphs of one
-kernel, the roofline of the dominant (longer) kernel from HIP events on its
-stream, side measurements (cold M=1 with 3-byte records over 480 rotating
-experts; M=8 with a shared expert pool and with 80 distinct experts), two
-live references (a 1 GiB streaming read and the per-launch floor of a
-graph of empty launches), and the CPU oracle timed on a bounded sample.
+kernel, the roofline of the dominant (longer) kernel with its duration on
+two clocks (HIP events on its stream, which ``frac`` uses, and the
+committed rocprofv3 kernel trace), M = 8 with a shared expert pool and with
+80 distinct experts (also cold), the same 10 hot experts on every call
+(4-byte records: cache-resident by construction, reported as effective
+bandwidth), the indexed prefill and the 48-layer stack, live references (a
+1 GiB copy, a 1 GiB streaming read, the per-launch floor), and the float64
+CPU oracle timed on the host (three configurations, all cores and one
+thread, median of 5).
 
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--only NAME] [--no-cpu]
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--only NAME,...] [--no-cpu]
 """
 
 from __future__ import annotations
@@ -36,6 +45,8 @@ from awq_int4_mixture_amd import inputs  # noqa: E402
 
 HBM_PEAK_GBS = 8000.0
 CALLS = 48
+COLD_BANKS = 4       # device copies of the 3-byte layer bank that cold calls rotate over
+COLD_GRAPHS = 4      # graphs of CALLS calls each; replays cycle through them
 SEED = 2026
 E, K_TOP, H, I = 512, 10, 2560, 160
 
@@ -45,67 +56,77 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=200)
     p.add_argument("--warmup", type=int, default=20)
-    p.add_argument("--only", default="", help="comma list of workloads: m1_hot,m1_cold,m8_pool,m8_distinct,p128,p256,p512,p1024,p4096,stack48,stack48_gemv")
+    p.add_argument("--only", default="", help="comma list of workloads: m1_cold,m1_hot,m8_pool,m8_distinct "
+                   "(any mN_pool / mN_distinct, N = 1..8),p128,p256,p512,p1024,p4096,stack48,stack48_gemv")
     p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     return p.parse_args()
 
 
 class Workload:
-    """48 calls of one configuration, all inputs resident on the device."""
+    """``graphs`` graphs of CALLS decode calls of one configuration, all inputs
+    resident on the device. ``calls[j] = (bank index, ids [M][k])`` for call
+    j = g * CALLS + c of graph g."""
 
-    def __init__(self, name, abi, torch, dims, bank, ids_calls, M, rng, per_expert):
-        self.name, self.dims, self.bank, self.M = name, dims, bank, M
-        dev = bank.device
-        self.x = [torch.from_numpy(inputs.activations(rng, M, H)).to(dev) for _ in range(CALLS)]
-        self.ids = [torch.from_numpy(np.ascontiguousarray(ids_calls[c])).to(dev) for c in range(CALLS)]
-        self.w = [torch.from_numpy(inputs.router_weights(rng, M, K_TOP)).to(dev) for _ in range(CALLS)]
+    def __init__(self, name, abi, torch, dims, banks, calls, M, rng, per_expert, graphs=1):
+        self.name, self.dims, self.banks, self.M, self.graphs = name, dims, banks, M, graphs
+        dev = banks[0].device
+        n = graphs * CALLS
+        assert len(calls) == n
+        self.bank_of = [banks[b] for b, _ in calls]
+        self.x = [torch.from_numpy(inputs.activations(rng, M, H)).to(dev) for _ in range(n)]
+        self.ids = [torch.from_numpy(np.ascontiguousarray(ids)).to(dev) for _, ids in calls]
+        self.w = [torch.from_numpy(inputs.router_weights(rng, M, K_TOP)).to(dev) for _ in range(n)]
         self.out = torch.empty((M, H), dtype=torch.float16, device=dev)
-        self.ws = [abi.alloc_workspace(dims, M, K_TOP, dev) for _ in range(CALLS)]
-        self.dec = abi.Decoder(dims, bank, K_TOP, max_tokens=M)
-        self.routes = [abi.alloc_route(M * K_TOP, dev) for _ in range(CALLS)]
-        self.ids_np = [np.asarray(ids_calls[c]) for c in range(CALLS)]
-        distinct = [len(np.unique(a)) for a in self.ids_np]
+        self.ws = [abi.alloc_workspace(dims, M, K_TOP, dev) for _ in range(n)]
+        self.routes = [abi.alloc_route(M * K_TOP, dev) for _ in range(n)]
+        distinct = [len(np.unique(ids)) for _, ids in calls]
         self.distinct_mean = float(np.mean(distinct))
         self.w13_bytes = [d * per_expert["w13"] for d in distinct]
         self.w2_bytes = [d * per_expert["w2"] for d in distinct]
+        self.bank_copies = len(banks)
 
 
 def measure_stack(abi, torch, steps, warmup, layers=48, M=8, router="given"):
-    """One decode step of a stack of 512-expert layers (3-byte records, banks
-    drawn on the device). Per layer, with router="given": residual update +
-    RMS norm and router top-k over fp32 N(0,1) logits (one launch), then the
-    stage (two launches). With router="gemv": residual update + RMS norm +
-    logits = x . Wr^T from fp16 router weights N(0,1)/sqrt(H) (one launch),
-    router top-k (one launch), then the stage. One graph replay = one step."""
+    """One decode step of a stack of 512-expert pre-norm layers (3-byte
+    records, banks drawn on the device): per layer r_{l+1} = fp16(r_l +
+    stage(fp16(rms_norm(r_l)))), one awq_moe_decode_rmsnorm_residual call
+    (two launches: the norm inside W13, the residual inside W2).
+    router="given": the fp32 N(0,1) logits of every layer are inputs of the
+    step, so the top-k of all layers is one launch at its start.
+    router="gemv": each layer's logits are x_l . Wr^T from fp16 router
+    weights N(0,1)/sqrt(H) (one launch, which also normalises r_l), then
+    top-k (one launch), then the layer: four launches per layer.
+    One graph replay = one step."""
     dims = abi.make_dims(E, H, I, 3)
     Lq = abi.awq_moe_bank_layout_query(dims)
     sections = [(int(Lq.w13_meta_off), (H // 32) * 2 * I), (int(Lq.w2_meta_off), (I // 32) * H)]
     banks = [inputs.device_bank(SEED + 9000 + l, E, sections, int(Lq.expert_bytes), 3) for l in range(layers)]
     rng = inputs.call_rng(SEED, 900)
+    ids_all = torch.empty((layers * M, K_TOP), dtype=torch.int32, device="cuda")
+    wts_all = torch.empty((layers * M, K_TOP), dtype=torch.float32, device="cuda")
+    ids = [ids_all[l * M:(l + 1) * M] for l in range(layers)]
+    wts = [wts_all[l * M:(l + 1) * M] for l in range(layers)]
     if router == "gemv":
         wr = [inputs.device_router_weights(SEED + 9500 + l, E, H) for l in range(layers)]
         logits = [torch.empty((M, E), dtype=torch.float32, device="cuda") for _ in range(layers)]
+        rcopy = torch.empty((M, H), dtype=torch.float16, device="cuda")
     else:
-        logits = [torch.from_numpy(inputs.router_logits(rng, M, E)).to("cuda") for _ in range(layers)]
+        logits_all = torch.from_numpy(inputs.router_logits(rng, layers * M, E)).to("cuda")
     r0 = torch.from_numpy(inputs.activations(rng, M, H)).to("cuda")
     rbuf = [torch.empty_like(r0) for _ in range(2)]
     xbuf = torch.empty_like(r0)
-    outs = [torch.empty_like(r0) for _ in range(layers)]
-    ids = [torch.empty((M, K_TOP), dtype=torch.int32, device="cuda") for _ in range(layers)]
-    wts = [torch.empty((M, K_TOP), dtype=torch.float32, device="cuda") for _ in range(layers)]
     ws = abi.alloc_workspace(dims, M, K_TOP, "cuda")
 
     def step():
+        if router != "gemv":
+            abi.awq_moe_router_topk(logits_all, K_TOP, ids=ids_all, w=wts_all)
         r = r0
         for l in range(layers):
             rn = rbuf[l % 2]
-            delta = None if l == 0 else outs[l - 1]
             if router == "gemv":
-                abi.awq_moe_router_gemv(r, wr[l], delta, r_next=rn, x=xbuf, logits=logits[l])
+                abi.awq_moe_router_gemv(r, wr[l], None, r_next=rcopy, x=xbuf, logits=logits[l])
                 abi.awq_moe_router_topk(logits[l], K_TOP, ids=ids[l], w=wts[l])
-            else:
-                abi.awq_moe_router_residual(logits[l], K_TOP, r, delta, ids=ids[l], w=wts[l], r_next=rn, x=xbuf)
-            abi.awq_moe_decode(dims, banks[l], xbuf, ids[l], wts[l], out=outs[l], workspace=ws)
+            abi.awq_moe_decode_rmsnorm_residual(dims, banks[l], r, ids[l], wts[l], r_next=rn, workspace=ws)
             r = rn
 
     step()
@@ -118,8 +139,8 @@ def measure_stack(abi, torch, steps, warmup, layers=48, M=8, router="given"):
     out = {"layers": layers, "M": M, "step_us": ms * 1e3, "layer_us": ms * 1e3 / layers,
            "distinct_experts_per_layer": float(np.mean(distinct)), "touched_bytes_per_step": touched,
            "gbs": touched / (ms * 1e6), "pct_peak": 100.0 * touched / (ms * 1e6) / HBM_PEAK_GBS,
-           "resident_bank_bytes": int(Lq.total_bytes) * layers, "launches_per_layer": 4 if router == "gemv" else 3,
-           "router": router}
+           "resident_bank_bytes": int(Lq.total_bytes) * layers,
+           "launches_per_layer": 4 if router == "gemv" else 2 + 1.0 / layers, "router": router}
     if router == "gemv":
         out["router_weight_bytes_per_step"] = layers * E * H * 2
         del wr
@@ -148,56 +169,71 @@ def capture(torch, fn):
 
 
 def time_graph(torch, g, reps, warmup):
-    """Mean ms per replay, from HIP events recorded on the replay stream."""
+    """Mean ms per replay of one graph, from HIP events recorded on the replay stream."""
+    return time_graphs(torch, [g], reps, warmup)
+
+
+def time_graphs(torch, gs, reps, warmup):
+    """Mean ms per replay when the graphs ``gs`` are replayed round robin
+    (reps rounded up to a multiple of len(gs)), from HIP events recorded on
+    the replay stream."""
     s = torch.cuda.current_stream()
-    for _ in range(warmup):
-        g.replay()
+    n = len(gs)
+    reps = -(-reps // n) * n
+    for i in range(max(warmup, n)):
+        gs[i % n].replay()
     torch.cuda.synchronize()
     t0 = torch.cuda.Event(enable_timing=True)
     t1 = torch.cuda.Event(enable_timing=True)
     t0.record(s)
-    for _ in range(reps):
-        g.replay()
+    for i in range(reps):
+        gs[i % n].replay()
     t1.record(s)
     t1.synchronize()
     return t0.elapsed_time(t1) / reps
 
 
 def measure(abi, torch, wl: Workload, steps, warmup):
-    def full():
-        for c in range(CALLS):
-            wl.dec(wl.x[c], wl.ids[c], wl.w[c], out=wl.out)
+    def calls_of(g):
+        return range(g * CALLS, (g + 1) * CALLS)
 
-    def route():
-        for c in range(CALLS):
+    def full(g):
+        for c in calls_of(g):
+            abi.awq_moe_decode(wl.dims, wl.bank_of[c], wl.x[c], wl.ids[c], wl.w[c], out=wl.out, workspace=wl.ws[c])
+
+    def route(g):
+        for c in calls_of(g):
             abi.awq_moe_route_compact(wl.ids[c], E, out=wl.routes[c])
 
-    def w13():
-        for c in range(CALLS):
-            abi.awq_moe_w13_swiglu(wl.dims, wl.bank, wl.x[c], wl.ids[c], workspace=wl.ws[c])
+    def w13(g):
+        for c in calls_of(g):
+            abi.awq_moe_w13_swiglu(wl.dims, wl.bank_of[c], wl.x[c], wl.ids[c], workspace=wl.ws[c])
 
-    def w2():
-        for c in range(CALLS):
-            abi.awq_moe_w2_reduce(wl.dims, wl.bank, wl.ids[c], wl.w[c], wl.ws[c], out=wl.out)
+    def w2(g):
+        for c in calls_of(g):
+            abi.awq_moe_w2_reduce(wl.dims, wl.bank_of[c], wl.ids[c], wl.w[c], wl.ws[c], out=wl.out)
 
-    route()
+    for g in range(wl.graphs):
+        route(g)
+        w13(g)
     torch.cuda.synchronize()
     res = {}
     # "layer" = awq_moe_decode (two launches, one workgroup per slot and tile);
     # "route" = the standalone awq_moe_route_compact kernel, not part of the layer.
-    graphs = {name: capture(torch, fn) for name, fn in (("layer", full), ("route", route), ("w13", w13), ("w2", w2))}
-    for name, g in graphs.items():
-        ms = time_graph(torch, g, steps, warmup)
+    graphs = {name: [capture(torch, lambda g=g, f=fn: f(g)) for g in range(wl.graphs)]
+              for name, fn in (("layer", full), ("route", route), ("w13", w13), ("w2", w2))}
+    for name, gs in graphs.items():
+        ms = time_graphs(torch, gs, steps, warmup)
         res[name + "_us"] = ms * 1e3 / CALLS
         if name == "layer":
             res["step_ms"] = ms
-    # 7 further samples per graph, in alternating (ABBA) order, for the median and the minimum
-    per_sample = max(steps // 7, 10)
+    # 7 further samples per graph set, in alternating (ABBA) order, for the median and the minimum
+    per_sample = max(steps // 7, 2 * wl.graphs)
     samples = {name: [] for name in graphs}
     names = list(graphs)
     for r in range(7):
         for name in (names if r % 2 == 0 else names[::-1]):
-            samples[name].append(time_graph(torch, graphs[name], per_sample, 2) * 1e3 / CALLS)
+            samples[name].append(time_graphs(torch, graphs[name], per_sample, wl.graphs) * 1e3 / CALLS)
     for name, v in samples.items():
         res[name + "_us_median7"] = float(np.median(v))
         res[name + "_us_min7"] = float(np.min(v))
@@ -205,8 +241,8 @@ def measure(abi, torch, wl: Workload, steps, warmup):
     w13b = float(np.mean(wl.w13_bytes))
     w2b = float(np.mean(wl.w2_bytes))
     res.update(
-        M=wl.M, distinct_experts_per_call=wl.distinct_mean,
-        w13_bytes_per_call=w13b, w2_bytes_per_call=w2b,
+        M=wl.M, distinct_experts_per_call=wl.distinct_mean, bank_copies=wl.bank_copies,
+        graphs=wl.graphs, w13_bytes_per_call=w13b, w2_bytes_per_call=w2b,
         w13_gbs=w13b / (res["w13_us"] * 1e3), w2_gbs=w2b / (res["w2_us"] * 1e3),
         layer_gbs=(w13b + w2b) / (res["layer_us"] * 1e3),
     )
@@ -262,7 +298,7 @@ def stage_source_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def recorded_traffic(kernel: str, summary: str = "pmc_traffic_m1_hot.txt"):
+def recorded_traffic(kernel: str, summary: str = "pmc_traffic_m1_cold.txt"):
     """HBM bytes per launch of ``kernel`` from the committed rocprofv3 counter summary
     (FETCH_SIZE and WRITE_SIZE, each scaled by a 1 GiB copy in the same run), or None
     when the summary is missing or the kernel source changed since it was taken."""
@@ -274,6 +310,22 @@ def recorded_traffic(kernel: str, summary: str = "pmc_traffic_m1_hot.txt"):
         parts = [p.strip() for p in line.split("|")]
         if len(parts) == 4 and parts[0] == "TRAFFIC" and kernel in parts[1] and parts[3] == f"source {h}":
             return float(parts[2].split()[0])
+    return None
+
+
+def recorded_trace(kernel: str, summary: str = "kernel_stats_m1_cold.txt"):
+    """(average ns, median ns) of ``kernel`` in the committed rocprofv3 kernel-trace
+    summary, or None when it is missing or the kernel source changed since."""
+    path = os.path.join(ROOT, "profiles", summary)
+    if not os.path.exists(path):
+        return None
+    text = open(path).read()
+    if f"sha256[:16] at collection: {stage_source_hash()}" not in text:
+        return None
+    for line in text.splitlines():
+        parts = [p.strip() for p in line.split("|")]
+        if len(parts) == 7 and parts[0].split("awq_moe::")[-1] == kernel:
+            return float(parts[2]), float(parts[3])
     return None
 
 
@@ -331,29 +383,63 @@ def launch_floor(torch, steps=50, warmup=5):
     return {"us_per_launch": ms * 1e3 / CALLS}
 
 
-def cpu_baseline(bi, ids_calls, rng_seed, budget_s=12.0):
-    """The float64 oracle on the headline workload's calls (cycling through the
-    48 expert sets with fresh inputs) for about budget_s seconds."""
+def cpu_baseline(bi, cold_calls, pool_calls, per_sample_s=0.6, samples=5):
+    """The float64 oracle (oracle.ref.moe_stage: dequantisation of the touched
+    experts, W13 + SwiGLU, W2, weighted sum; input generation excluded) on the
+    host, for the tiny layer (16 experts, hidden 256, inter 32, top-k 2,
+    4-byte records, M = 1), the cold M = 1 calls and the M = 8 shared-pool
+    calls of the rank layer. Each sample repeats calls for about
+    ``per_sample_s`` seconds; the median of ``samples`` samples is reported,
+    once with the BLAS thread pool at every core this process may use and
+    once at one thread (NumPy's elementwise dequantisation runs on one
+    thread either way)."""
     from threadpoolctl import threadpool_limits
 
     from oracle import ref as R
-    rng = inputs.call_rng(rng_seed, 77)
-    per_call = K_TOP * (409_600 + 102_400 + 204_800 + 51_200)
-    done = 0
-    with threadpool_limits(limits=1):
-        t0 = time.perf_counter()
-        while True:
-            x = inputs.activations(rng, 1, H)
-            w = inputs.router_weights(rng, 1, K_TOP)
-            R.moe_stage(x, ids_calls[done % CALLS], w, E, bi.expert)
-            done += 1
-            if time.perf_counter() - t0 > budget_s:
-                break
-        dt = time.perf_counter() - t0
-    return {"value": round(per_call * done / dt / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
-            "sample": f"{done} M=1 calls on the hot-expert sets (4-byte records), float64 NumPy on one "
-                      f"thread, dequantisation of the touched experts included, {dt:.1f} s",
-            "layer_us": round(dt / done * 1e6, 1)}
+    cores = len(os.sched_getaffinity(0))
+    tiny = inputs.bank_inputs(1, 16, 256, 32)
+    rng = inputs.call_rng(SEED, 77)
+    tiny_calls = [inputs.ids_distinct(rng, 1, 2, 16) for _ in range(64)]
+    cfgs = {
+        # name: (bank, experts, hidden, list of ids, bytes per distinct expert)
+        # tiny expert (4-byte records): W13 8,192 + 512 * 4 B, W2 4,096 + 256 * 4 B
+        "tiny_m1": (tiny, 16, 256, tiny_calls, (8192 + 512 * 4) + (4096 + 256 * 4)),
+        "m1_cold": (bi, E, H, [ids for _, ids in cold_calls], 729_600),
+        "m8_pool": (bi, E, H, [ids for _, ids in pool_calls], 729_600),
+    }
+    out = {"cores_all": cores}
+    for name, (bank, En, Hn, id_list, per_expert) in cfgs.items():
+        entry = {}
+        done = 0
+        for threads in (cores, 1):
+            per_sample = []
+            with threadpool_limits(limits=threads):
+                for _ in range(samples):
+                    n, byts, busy = 0, 0, 0.0
+                    while busy < per_sample_s:
+                        ids = id_list[done % len(id_list)]
+                        M = ids.shape[0]
+                        x = inputs.activations(rng, M, Hn)
+                        w = inputs.router_weights(rng, M, ids.shape[1])
+                        t0 = time.perf_counter()
+                        R.moe_stage(x, ids, w, En, bank.expert)
+                        busy += time.perf_counter() - t0
+                        n += 1
+                        done += 1
+                        byts += len(np.unique(ids)) * per_expert
+                    per_sample.append((busy / n, byts / n))
+            us = float(np.median([a for a, _ in per_sample])) * 1e6
+            byts = float(np.mean([b for _, b in per_sample]))
+            entry["threads_1" if threads == 1 else "threads_all"] = {
+                "threads": threads, "us_per_layer_median5": round(us, 1), "gbs": round(byts / (us * 1e3), 4)}
+        out[name] = entry
+    head = out["m1_cold"]["threads_all"]
+    return {"value": head["gbs"], "unit": "GB/s", "cores": cores, "kind": "oracle",
+            "sample": (f"float64 NumPy oracle on the host: the cold M=1 rank-layer calls (3-byte records, "
+                       f"10 experts per call), median of {samples} samples of ~{per_sample_s} s, BLAS threads = "
+                       f"{cores} (all cores this process may use); dequantisation of the touched experts "
+                       f"included, input generation excluded; also tiny M=1 and M=8 shared pool, and one thread"),
+            "layer_us": head["us_per_layer_median5"], "per_config": out}
 
 
 def stage_kernel_names(M, H=H, I=I, topk=K_TOP, rb=4):
@@ -371,13 +457,17 @@ def stage_kernel_names(M, H=H, I=I, topk=K_TOP, rb=4):
     return w13, w2
 
 
-def roofline(head):
-    """HBM roofline of the longer of the two stage kernels at the headline workload."""
+def roofline(head, rb):
+    """HBM roofline of the longer of the two stage kernels at the headline
+    workload. ``achieved`` and ``frac`` use the HIP-event clock (per-launch
+    period of a graph of 48 launches of that kernel alone); the committed
+    kernel-trace duration of the same kernel is carried next to it."""
     k = "w2" if head["w2_us"] >= head["w13_us"] else "w13"
-    w13_name, w2_name = stage_kernel_names(head["M"])
+    w13_name, w2_name = stage_kernel_names(head["M"], rb=rb)
     name = {"w13": w13_name, "w2": w2_name}[k]
     gbs = head[k + "_gbs"]
-    return {
+    algo = head[k + "_bytes_per_call"]
+    out = {
         "bound": "hbm",
         "kernel": name,
         "achieved": round(gbs, 2),
@@ -385,9 +475,31 @@ def roofline(head):
         "unit": "GB/s",
         "frac": round(gbs / HBM_PEAK_GBS, 4),
         "traffic": recorded_traffic(name),
-        "algorithmic_bytes_per_launch": head[k + "_bytes_per_call"],
+        "algorithmic_bytes_per_launch": algo,
+        "clock": "hip_events",
         "avg_launch_us": round(head[k + "_us"], 3),
     }
+    tr = recorded_trace(name)
+    if tr is not None:
+        out["trace_avg_us"] = round(tr[0] / 1e3, 3)
+        out["trace_median_us"] = round(tr[1] / 1e3, 3)
+        out["frac_trace_avg"] = round(algo / (tr[0] / 1e3) / 1e3 / HBM_PEAK_GBS, 4)
+    return out
+
+
+def decode_workloads(only):
+    """Names of the decode workloads asked for, in run order: (name, M, mode)."""
+    out = []
+    for name in sorted(only, key=lambda n: (n != "m1_cold", n)):
+        if name == "m1_hot":
+            out.append((name, 1, "hot"))
+            continue
+        if not name.startswith("m") or "_" not in name:
+            continue
+        m, mode = name[1:].split("_", 1)
+        if m.isdigit() and 1 <= int(m) <= 8 and mode in ("cold", "pool", "distinct"):
+            out.append((name, int(m), "distinct" if mode == "cold" else mode))
+    return out
 
 
 def main():
@@ -401,55 +513,47 @@ def main():
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     torch.cuda.set_device(0)
     prefill_wls = {"p128": 128, "p256": 256, "p512": 512, "p1024": 1024, "p4096": 4096}
-    only = set(filter(None, args.only.split(","))) or {"m1_hot", "m1_cold", "m8_pool", "m8_distinct", "stack48",
+    only = set(filter(None, args.only.split(","))) or {"m1_cold", "m1_hot", "m8_pool", "m8_distinct", "stack48",
                                                        "stack48_gemv", *prefill_wls}
+    decode_wls = decode_workloads(only)
+    cold_needed = any(mode != "hot" for _, _, mode in decode_wls) or bool(set(prefill_wls) & only)
 
     t_gen = time.perf_counter()
     bi = inputs.bank_inputs(SEED, E, H, I)
-    banks = {}
-    for rb in (4, 3):
-        if rb == 4 and "m1_hot" not in only:
-            continue
-        if rb == 3 and not ({"m1_cold", "m8_pool", "m8_distinct", *prefill_wls} & only):
-            continue
-        dims = abi.make_dims(E, H, I, rb)
-        banks[rb] = (dims, torch.from_numpy(abi.prepare_from_inputs(dims, bi)).to("cuda"))
+    dims3 = abi.make_dims(E, H, I, 3)
+    dims4 = abi.make_dims(E, H, I, 4)
+    banks3, bank4 = [], None
+    if cold_needed:
+        host3 = torch.from_numpy(abi.prepare_from_inputs(dims3, bi))
+        banks3 = [host3.to("cuda") for _ in range(COLD_BANKS)]   # physically distinct copies of one layer
+        del host3
+    if "m1_hot" in only:
+        bank4 = torch.from_numpy(abi.prepare_from_inputs(dims4, bi)).to("cuda")
     t_gen = time.perf_counter() - t_gen
 
     rng = inputs.call_rng(SEED, 1)
     hot = inputs.hot_experts(SEED, K_TOP, E)
-    hot_calls = [hot[None, :].copy() for _ in range(CALLS)]
-    results = {}
+    results, cold_calls = {}, {}
     stream = torch.cuda.Stream()
     with torch.cuda.stream(stream):
-        if "m1_hot" in only:
-            dims, bank = banks[4]
-            wl = Workload("m1_hot", abi, torch, dims, bank, hot_calls, 1, rng, per_expert_bytes(abi, dims))
-            results["m1_hot"] = measure(abi, torch, wl, args.steps, args.warmup)
-        if "m1_cold" in only:
-            dims, bank = banks[3]
-            rot = inputs.rotating_ids(SEED, CALLS, K_TOP, E)
-            wl = Workload("m1_cold", abi, torch, dims, bank, [rot[c] for c in range(CALLS)], 1, rng,
-                          per_expert_bytes(abi, dims))
-            results["m1_cold"] = measure(abi, torch, wl, args.steps, args.warmup)
-        if "m8_pool" in only:
-            dims, bank = banks[3]
-            ids = [inputs.ids_shared_pool(inputs.call_rng(SEED, 300 + c), 8, K_TOP, E) for c in range(CALLS)]
-            wl = Workload("m8_pool", abi, torch, dims, bank, ids, 8, rng, per_expert_bytes(abi, dims))
-            results["m8_pool"] = measure(abi, torch, wl, args.steps, args.warmup)
-        if "m8_distinct" in only:
-            dims, bank = banks[3]
-            ids = [inputs.ids_all_distinct(inputs.call_rng(SEED, 400 + c), 8, K_TOP, E) for c in range(CALLS)]
-            wl = Workload("m8_distinct", abi, torch, dims, bank, ids, 8, rng, per_expert_bytes(abi, dims))
-            results["m8_distinct"] = measure(abi, torch, wl, args.steps, args.warmup)
+        for name, M, mode in decode_wls:
+            if mode == "hot":
+                calls = [(0, hot[None, :].copy()) for _ in range(CALLS)]
+                wl = Workload(name, abi, torch, dims4, [bank4], calls, 1, rng, per_expert_bytes(abi, dims4))
+            else:
+                calls = inputs.rotating_calls(SEED + M, COLD_GRAPHS * CALLS, M, K_TOP, E, COLD_BANKS, mode)
+                cold_calls[name] = calls
+                wl = Workload(name, abi, torch, dims3, banks3, calls, M, rng, per_expert_bytes(abi, dims3),
+                              graphs=COLD_GRAPHS)
+            results[name] = measure(abi, torch, wl, args.steps, args.warmup)
+            del wl
         for name, Mp in prefill_wls.items():
             if name in only:
-                dims, bank = banks[3]
-                results[name] = measure_prefill(abi, torch, dims, bank, Mp, max(args.steps // 4, 10),
-                                                max(args.warmup // 4, 2), per_expert_bytes(abi, dims))
+                results[name] = measure_prefill(abi, torch, dims3, banks3[0], Mp, max(args.steps // 4, 10),
+                                                max(args.warmup // 4, 2), per_expert_bytes(abi, dims3))
         stack = stack_gemv = None
         if {"stack48", "stack48_gemv"} & only:
-            del banks
+            del banks3, bank4
             torch.cuda.empty_cache()
         if "stack48" in only:
             stack = measure_stack(abi, torch, max(args.steps // 4, 10), max(args.warmup // 4, 2))
@@ -463,7 +567,14 @@ def main():
     if not decode_results:
         print(json.dumps({"per_config": results, "stack48": stack, "stack48_gemv": stack_gemv}), flush=True)
         return
-    head = decode_results.get("m1_hot") or next(iter(decode_results.values()))
+    head_name = "m1_cold" if "m1_cold" in decode_results else next(iter(decode_results))
+    head = decode_results[head_name]
+    head_rb = 4 if head_name == "m1_hot" else 3
+
+    def brief(r):
+        return {k: round(r[k], 3) for k in ("layer_us", "w13_us", "w2_us", "layer_gbs", "layer_pct_peak",
+                                            "w13_pct_peak", "w2_pct_peak", "distinct_experts_per_call")}
+
     line = {
         "metric": "MoE layer decode µs and achieved weight HBM GB/s (% of peak) at M=1 and M=8",
         "value": round(head["layer_gbs"], 2),
@@ -478,12 +589,19 @@ def main():
         "dtype": "fp16 x int4 -> fp32 accumulate",
         "data": "synthetic (seeded int4 weights, fp16 scales |N(0,1)|*0.02, zeros U{0..15}, x ~ N(0,1))",
         "config": {
-            "workload": "AWQ int4 MoE expert stage, 512 experts, hidden 2560, inter 160, top-k 10, group 32, "
-                        "M=1, 4-byte records, same 10 hot experts on all 48 calls of a graph replay",
+            "workload": ("AWQ int4 MoE expert stage, 512 experts, hidden 2560, inter 160, top-k 10, group 32, "
+                         "M=1, 3-byte records, cold weights: calls rotate over 4 device copies of the layer "
+                         "bank and 4 graphs of 48 calls, every expert read at least 1.39 GB of weight traffic "
+                         "after its previous read") if head_name == "m1_cold" else head_name,
             "layer_us": round(head["layer_us"], 3),
             "calls_per_step": CALLS,
         },
-        "roofline": roofline(head),
+        "roofline": roofline(head, head_rb),
+        "m8_distinct": brief(results["m8_distinct"]) if "m8_distinct" in results else None,
+        "m8_pool": brief(results["m8_pool"]) if "m8_pool" in results else None,
+        "m1_hot_effective": (dict(brief(results["m1_hot"]), note="the same 10 experts on every call: "
+                                  "cache-resident, effective (not HBM) bandwidth")
+                             if "m1_hot" in results else None),
         "per_config": {k: {kk: (round(vv, 4) if isinstance(vv, float) else vv) for kk, vv in v.items()}
                        for k, v in results.items()},
         "stack48": stack,
@@ -493,8 +611,8 @@ def main():
         "launch_floor": floor,
         "setup_s": round(t_gen, 1),
     }
-    if not args.no_cpu and "m1_hot" in results:
-        line["cpu_baseline"] = cpu_baseline(bi, hot_calls, SEED)
+    if not args.no_cpu and "m1_cold" in cold_calls and "m8_pool" in cold_calls:
+        line["cpu_baseline"] = cpu_baseline(bi, cold_calls["m1_cold"], cold_calls["m8_pool"])
     print(json.dumps(line), flush=True)
 
 

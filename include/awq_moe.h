@@ -75,6 +75,7 @@ extern "C" {
 #define AWQ_MOE_MAX_HIDDEN 8192
 #define AWQ_MOE_MAX_INTER 2048
 #define AWQ_MOE_MAX_ROUTER_EXPERTS 4096
+#define AWQ_MOE_MAX_ROUTER_ROWS 4096  /* rows of logits per awq_moe_router_topk call */
 #define AWQ_MOE_STATUS_BAD_ID 1u
 #define AWQ_MOE_PREFILL_MIN_TOKENS 9      /* indexed prefill tokens per call, M in [9, 4096] */
 #define AWQ_MOE_PREFILL_MAX_TOKENS 4096
@@ -209,7 +210,9 @@ int awq_moe_w2_reduce(const awq_moe_dims* dims, const void* bank, uint64_t bank_
 
 /* --- support for a stack of MoE layers (not part of the stage itself) --- */
 
-/* Router top-k + softmax for M = 1..8 tokens. The pages leave the router
+/* Router top-k + softmax for M = 1..AWQ_MOE_MAX_ROUTER_ROWS rows of logits
+ * (tokens, or the tokens of several layers whose logits are all known). The
+ * pages leave the router
  * unchanged (fork PR #12, Purpose and stack); this is the library's reading:
  * per token, the topk largest fp32 logits, compared exactly (-0 == +0, NaN
  * below every number, ties to the lower expert id), listed by descending
@@ -221,6 +224,24 @@ int awq_moe_w2_reduce(const awq_moe_dims* dims, const void* bank, uint64_t bank_
  * num_experts)]. One launch (one wave per token). */
 int awq_moe_router_topk(const float* logits, int32_t M, int32_t num_experts, int32_t topk,
                         int32_t* topk_ids, float* topk_w, void* stream);
+
+/* One stacked pre-norm layer around the stage (the norm and the residual are
+ * not on the pages; fork PR #12, Purpose and stack, leaves the rest of the
+ * model unchanged): with x = fp16(r / sqrt(mean(r^2) + eps)) per row, as
+ * awq_moe_residual_rmsnorm computes it (bit-identical), and
+ * out = the fp16 result of awq_moe_decode(x, topk_ids, topk_w),
+ *   r_next = fp16(r + out)     (fp32 add, one rounding)
+ * which equals awq_moe_residual_rmsnorm(r, delta = out).r_next. Two launches,
+ * like awq_moe_decode: every W13 workgroup computes its token's norm from the
+ * row it loads anyway, and the W2 workgroups add the residual as they store,
+ * so no separate norm or residual launch sits between two layers.
+ *   r, r_next: device fp16 [M][hidden], 16-byte aligned, not overlapping;
+ *   eps in (0, 1]; the other arguments, the workspace and its contents
+ *   (status word, act) as for awq_moe_decode. */
+int awq_moe_decode_rmsnorm_residual(const awq_moe_dims* dims, const void* bank, uint64_t bank_bytes,
+                                    const uint16_t* r, float eps, const int32_t* topk_ids, const float* topk_w,
+                                    int32_t M, int32_t topk, uint16_t* r_next, void* workspace,
+                                    uint64_t workspace_bytes, void* stream);
 
 /* Residual update and parameter-free RMS norm between stacked layers (not on
  * the pages: fp16 residuals chained through many layers overflow without a

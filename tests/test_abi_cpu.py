@@ -163,7 +163,7 @@ def test_device_calls_reject_bad_arguments_before_launch():
         (lambda: lib.awq_moe_dequant(ctypes.byref(d), p, bb, 510, 3, 0, p, None), abi.EINVAL),
         (lambda: lib.awq_moe_dequant(ctypes.byref(d), p, bb, 0, 1, 2, p, None), abi.EINVAL),
         (lambda: lib.awq_moe_router_topk(p, 0, 512, 10, p, p, None), abi.EINVAL),
-        (lambda: lib.awq_moe_router_topk(p, 9, 512, 10, p, p, None), abi.EINVAL),
+        (lambda: lib.awq_moe_router_topk(p, 4097, 512, 10, p, p, None), abi.EINVAL),
         (lambda: lib.awq_moe_router_topk(p, 1, 4097, 10, p, p, None), abi.EINVAL),
         (lambda: lib.awq_moe_router_topk(p, 1, 8, 9, p, p, None), abi.EINVAL),
         (lambda: lib.awq_moe_router_topk(p, 1, 512, 33, p, p, None), abi.EINVAL),
@@ -205,6 +205,19 @@ def test_device_calls_reject_bad_arguments_before_launch():
         (lambda: lib.awq_moe_dequant(ctypes.byref(d), p, bb - 1, 0, 1, 0, p, None), abi.ENOSPC),
         (lambda: lib.awq_moe_decode(ctypes.byref(abi.make_dims(512, 2560, 160, 4)), p, bb, p, p, p, 1, 10, p, p,
                                     1 << 40, None), abi.ENOSPC),
+        # the fused stacked layer: the stage's checks plus eps and the two rows
+        (lambda: lib.awq_moe_decode_rmsnorm_residual(ctypes.byref(d), p, bb, q1, 0.0, p, p, 1, 10, q2, p, ws_need,
+                                                     None), abi.EINVAL),
+        (lambda: lib.awq_moe_decode_rmsnorm_residual(ctypes.byref(d), p, bb, q1, 1e-6, p, p, 1, 10, q1, p, ws_need,
+                                                     None), abi.EINVAL),
+        (lambda: lib.awq_moe_decode_rmsnorm_residual(ctypes.byref(d), p, bb, mis, 1e-6, p, p, 1, 10, q2, p, ws_need,
+                                                     None), abi.EINVAL),
+        (lambda: lib.awq_moe_decode_rmsnorm_residual(ctypes.byref(d), p, bb, q1, 1e-6, p, p, 9, 10, q2, p, ws_need,
+                                                     None), abi.EINVAL),
+        (lambda: lib.awq_moe_decode_rmsnorm_residual(ctypes.byref(d), p, bb - 1, q1, 1e-6, p, p, 1, 10, q2, p,
+                                                     ws_need, None), abi.ENOSPC),
+        (lambda: lib.awq_moe_decode_rmsnorm_residual(ctypes.byref(d), p, bb, q1, 1e-6, p, p, 1, 10, q2, p,
+                                                     ws_need - 1, None), abi.ENOSPC),
         # the no-allocation entry point: same checks, and a fixed scratch maximum
         (lambda: lib.awq_moe_decode_noalloc(ctypes.byref(d), p, bb, p, p, p, 9, 10, p, None, None), abi.EINVAL),
         (lambda: lib.awq_moe_decode_noalloc(ctypes.byref(d), p, bb - 1, p, p, p, 1, 10, p, None, None), abi.ENOSPC),

@@ -171,3 +171,90 @@ def test_stack_teacher_forced_four_layers():
         say("stack layer", layer, e)
         assert ok, (layer, e)
         r = r_next
+
+
+@pytest.mark.parametrize("E,H,I,k,M,rb", [
+    (64, 2560, 160, 10, 1, 3),     # W13 lane pairs with the norm (LDS run exchange), W2 slot segments
+    (64, 2560, 160, 10, 8, 4),     # single-lane W13 with the norm
+    (64, 2560, 160, 10, 3, 3),
+    (6, 8192, 32, 3, 2, 3),        # hidden 8192: 1024 runs over 16 waves
+    (8, 512, 2048, 4, 2, 3),       # the generic W2 kernel (inter > 256) with the residual
+    (12, 4096, 64, 2, 1, 4),       # lane pairs at their largest block (16 waves)
+])
+def test_decode_rmsnorm_residual_bit_identical_to_separate_calls(E, H, I, k, M, rb):
+    """awq_moe_decode_rmsnorm_residual(r) equals, bit for bit, the three
+    separate calls it replaces: x = residual_rmsnorm(r).x, out = decode(x),
+    r_next = residual_rmsnorm(r, delta = out).r_next (and its fp16 act equals
+    the separate W13 stage's act). r_next is also within the gate of the
+    float64 oracle, fp16(r + moe_stage(fp16(rms_norm(r))))."""
+    from tests.gpu_helpers import bank_case
+    dims, bank, bi = bank_case(510 + H, E, H, I, rb)
+    rng = inputs.call_rng(511, H + I + M)
+    r = (rng.standard_normal((M, H)) * 3).astype(np.float16)
+    ids = inputs.ids_shared_pool(rng, M, k, E) if k <= E else rng.integers(0, E, size=(M, k)).astype(np.int32)
+    w = inputs.router_weights(rng, M, k)
+    rd, idd, wd = to_dev(r), to_dev(ids), to_dev(w)
+    say("fused layer", E, H, I, k, M, rb)
+    ws_sep = abi.alloc_workspace(dims, M, k, "cuda")
+    _, x = abi.awq_moe_residual_rmsnorm(rd)
+    out = abi.awq_moe_decode(dims, bank, x, idd, wd, workspace=ws_sep)
+    want_rn, _ = abi.awq_moe_residual_rmsnorm(rd, out)
+    ws = abi.alloc_workspace(dims, M, k, "cuda")
+    rn = abi.awq_moe_decode_rmsnorm_residual(dims, bank, rd, idd, wd, workspace=ws)
+    torch.cuda.synchronize()
+    assert torch.equal(abi.workspace_act(ws, M, k, I).view(torch.int16),
+                       abi.workspace_act(ws_sep, M, k, I).view(torch.int16))
+    assert torch.equal(rn.view(torch.int16), want_rn.view(torch.int16))
+    x_ref = R.rms_norm(r).astype(np.float16)
+    want = (r.astype(np.float64) + R.moe_stage(x_ref, ids, w, E, bi.expert))
+    got = f16_to_np(rn).astype(np.float64)
+    ok, e = R.within_gate(got - r.astype(np.float64), want - r.astype(np.float64))
+    say("fused layer vs oracle (the update r_next - r)", e)
+    assert ok, e
+
+
+def test_router_rows_of_many_layers_in_one_call():
+    """The top-k of 48 layers x 8 tokens in one call (rows are independent)
+    equals the per-layer calls and the oracle."""
+    rng = inputs.call_rng(512, 0)
+    lg = inputs.router_logits(rng, 48 * 8, 512)
+    ids, w = abi.awq_moe_router_topk(to_dev(lg), 10)
+    torch.cuda.synchronize()
+    want_ids, want_w = R.topk_softmax(lg, 10)
+    np.testing.assert_array_equal(ids.cpu().numpy(), want_ids)
+    np.testing.assert_allclose(w.cpu().numpy().astype(np.float64), want_w, rtol=1e-5, atol=1e-7)
+    for layer in (0, 17, 47):
+        i1, w1 = abi.awq_moe_router_topk(to_dev(lg[8 * layer:8 * layer + 8]), 10)
+        torch.cuda.synchronize()
+        assert torch.equal(i1, ids[8 * layer:8 * layer + 8]) and torch.equal(w1, w[8 * layer:8 * layer + 8])
+
+
+def test_stack_fused_layers_teacher_forced():
+    """Four 512-expert layers, M = 8, 3-byte records, in the benchmark's
+    chain: every layer's top-k in one router call, then one fused layer call
+    per layer (norm in W13, residual in W2). Each layer is checked against
+    the oracle on the GPU's own residual input."""
+    E, H, I, K, M, RB, layers = 512, 2560, 160, 10, 8, 3, 4
+    dims = abi.make_dims(E, H, I, RB)
+    Lq = abi.awq_moe_bank_layout_query(dims)
+    sections = [(int(Lq.w13_meta_off), (H // 32) * 2 * I), (int(Lq.w2_meta_off), (I // 32) * H)]
+    d = OL.Dims(E, H, I, RB)
+    rng = inputs.call_rng(513, 0)
+    r = to_dev(inputs.activations(rng, M, H))
+    logits = inputs.router_logits(rng, layers * M, E)
+    ids_all, w_all = abi.awq_moe_router_topk(to_dev(logits), K)
+    ws = abi.alloc_workspace(dims, M, K, "cuda")
+    for layer in range(layers):
+        bank = inputs.device_bank(7100 + layer, E, sections, int(Lq.expert_bytes), RB)
+        ids, w = ids_all[layer * M:(layer + 1) * M], w_all[layer * M:(layer + 1) * M]
+        rn = abi.awq_moe_decode_rmsnorm_residual(dims, bank, r, ids, w, workspace=ws)
+        torch.cuda.synchronize()
+        r_np = f16_to_np(r)
+        want_ids, _ = R.topk_softmax(logits[layer * M:(layer + 1) * M], K)
+        np.testing.assert_array_equal(ids.cpu().numpy(), want_ids)
+        x_ref = R.rms_norm(r_np).astype(np.float16)
+        upd = R.moe_stage(x_ref, want_ids, w.cpu().numpy(), E, experts_from_bank(d, bank.cpu().numpy()))
+        ok, e = R.within_gate(f16_to_np(rn).astype(np.float64) - r_np.astype(np.float64), upd)
+        say("fused stack layer", layer, e)
+        assert ok, (layer, e)
+        r = rn
