@@ -339,49 +339,15 @@ __host__ __device__ __forceinline__ ExpertGeometry expert_geometry(uint32_t d) {
   return g;
 }
 
-// Sum of squares of a row of H fp16 values and 1/sqrt(mean + eps), in the
-// order of the residual/RMS-norm kernel: per run of 8 values (values
-// 8i .. 8i+7, run i) an fmaf chain; the runs of each 64-lane wave summed with
-// wave_sum_xor_order, run i in lane i; the waves' sums added in wave order.
-// run_ss holds run t's chain in lane t (0 for t >= H/8); part is 16 floats
-// of the caller's LDS. Every thread of the workgroup must call it (one
-// barrier).
-__device__ __forceinline__ float row_inv_rms(float run_ss, int H, float eps, float* part) {
-  const float s = wave_sum_xor_order(run_ss);
-  if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = s;
-  __syncthreads();
-  const int nw = ((H >> 3) + 63) >> 6;
-  float tot = 0.f;
-  for (int i = 0; i < nw; ++i) tot += part[i];
-  return 1.0f / sqrtf(tot / (float)H + eps);
-}
-
-// fmaf chain of the squares of the 8 fp16 values in 4 packed pairs.
-__device__ __forceinline__ float run_sumsq(uint32_t a, uint32_t b, uint32_t c, uint32_t d) {
-  const uint32_t px[4] = {a, b, c, d};
+// Sum of squares of the activations a lane holds (packed fp16 pairs), for the
+// in-kernel RMS norm: v_dot2 of each pair with itself (products exact in
+// fp32).
+template <int NP>
+__device__ __forceinline__ float pairs_sumsq(const uint32_t* px) {
   float ss = 0.f;
 #pragma unroll
-  for (int p = 0; p < 4; ++p) {
-    const h2_t v = as_h2(px[p]);
-    ss = fmaf((float)v.x, (float)v.x, ss);
-    ss = fmaf((float)v.y, (float)v.y, ss);
-  }
+  for (int i = 0; i < NP; ++i) ss = dot2(px[i], px[i], ss);
   return ss;
-}
-
-// Pair p of run q (q = 0..3) of a group's 16 packed pairs, selected without
-// a dynamic index (which would place the array in memory).
-__device__ __forceinline__ uint32_t pick_run_pair(const Act32& a, int q, int p) {
-  return q == 0 ? a.px[p] : q == 1 ? a.px[4 + p] : q == 2 ? a.px[8 + p] : a.px[12 + p];
-}
-
-// A packed pair scaled and rounded as the norm does: fp16((float)v * inv).
-__device__ __forceinline__ uint32_t norm_pair(uint32_t v, float inv) {
-  const h2_t a = as_h2(v);
-  h2_t o;
-  o.x = (_Float16)((float)a.x * inv);
-  o.y = (_Float16)((float)a.y * inv);
-  return __builtin_bit_cast(uint32_t, o);
 }
 
 // ---------------------------------------------------------------------------
@@ -398,12 +364,14 @@ __device__ __forceinline__ uint32_t norm_pair(uint32_t v, float inv) {
 // Wave 0 of workgroup (0, 0) also writes the status word; its id loads are
 // issued first and consumed after the weight loads are in flight.
 // ---------------------------------------------------------------------------
-// With NORM, x is a residual row r and the activations are
-// fp16(r / sqrt(mean(r^2) + eps)), computed by every workgroup of the token
-// from the row it loads anyway, bit-identical to the residual/RMS-norm
-// kernel's x: lane t (t = 4g + quad) holds values 32g .. 32g+31 and takes run
-// t (its quad's 8 values) for the sum of squares, as that kernel's thread t
-// does.
+// With NORM, x is a residual row r and the stage consumes r / rms(r), rms(r)
+// = sqrt(mean(r^2) + eps): the dot products run on r itself and each
+// column's fp32 sum is multiplied by 1/rms(r) before SwiGLU (the norm is a
+// per-row scale, so nothing is rounded in between). The sum of squares comes
+// from the row every workgroup of the token loads anyway: each wave sums its
+// lanes' squares (every group is held by the 4 lanes of a quad, so the
+// wave's sum is exactly 4 times the sum over its groups), the waves' sums
+// go through LDS with the column sums, and the one barrier serves both.
 template <int RB, bool NORM>
 __global__ __launch_bounds__(1024) void w13_swiglu_kernel(const int32_t* __restrict__ ids,
                                                           const uint8_t* __restrict__ units_base,
@@ -446,18 +414,10 @@ __global__ __launch_bounds__(1024) void w13_swiglu_kernel(const int32_t* __restr
     if (lane == 0) *reinterpret_cast<uint32_t*>(ws + AWQ_MOE_KWS_STATUS_OFFSET) = b ? AWQ_MOE_STATUS_BAD_ID_BIT : 0u;
   }
   if (!live) return;  // invalid slot: no row (uniform over the workgroup)
+  __shared__ float norm_part[16];  // [wave] sums of squares (NORM)
   if constexpr (NORM) {
-    // after the weight loads: the norm must not delay them
-    __builtin_amdgcn_sched_barrier(0);
-    __shared__ float norm_part[16];
-    const int q = t & 3;
-    const float ss = run_sumsq(pick_run_pair(av, q, 0), pick_run_pair(av, q, 1), pick_run_pair(av, q, 2),
-                               pick_run_pair(av, q, 3));
-    const float inv = row_inv_rms(t < L ? ss : 0.f, H, eps, norm_part);
-    if (t < L) {
-#pragma unroll
-      for (int i = 0; i < 16; ++i) av.px[i] = norm_pair(av.px[i], inv);
-    }
+    const float ss = wave_sum_xor_order(t < L ? pairs_sumsq<16>(av.px) : 0.f);
+    if (lane == 0) norm_part[wave] = ss;
   }
   float part[4] = {0.f, 0.f, 0.f, 0.f};
   if (t < L) {
@@ -476,6 +436,11 @@ __global__ __launch_bounds__(1024) void w13_swiglu_kernel(const int32_t* __restr
   if (t < 16) {
     float h = 0.f;
     for (int wv = 0; wv < nwaves; ++wv) h += red[wv][t];
+    if constexpr (NORM) {
+      float ss = 0.f;
+      for (int wv = 0; wv < nwaves; ++wv) ss += norm_part[wv];
+      h *= 1.0f / sqrtf(0.25f * ss / (float)H + eps);
+    }
     const float other = __shfl_xor(h, 1);  // partner column: gate <-> up
     uint16_t* act = reinterpret_cast<uint16_t*>(ws + AWQ_MOE_KWS_ACT_OFFSET);
     if (!(t & 1)) act[(uint64_t)s * I + nt * 8 + (t >> 1)] = __builtin_bit_cast(uint16_t, (_Float16)silu_mul(h, other));
@@ -542,9 +507,8 @@ __device__ __forceinline__ float half_unit_dot(const uint2& w, const Act16& a, c
   return acc;
 }
 
-// With NORM, as w13_swiglu_kernel: lane (tu = 4g + quad, half) holds runs
-// 4g + 2 half and 4g + 2 half + 1; the lanes with quad / 2 == half take run
-// tu, which an LDS exchange hands to lane tu for the ordered sum.
+// With NORM, as w13_swiglu_kernel (each half group is held by the 4 lanes of
+// its quad, so a wave's sum of squares is again exactly 4 times its groups').
 template <int RB, bool NORM>
 __global__ __launch_bounds__(1024) void w13_swiglu_pair_kernel(const int32_t* __restrict__ ids,
                                                                const uint8_t* __restrict__ units_base,
@@ -586,22 +550,10 @@ __global__ __launch_bounds__(1024) void w13_swiglu_pair_kernel(const int32_t* __
     if (lane == 0) *reinterpret_cast<uint32_t*>(ws + AWQ_MOE_KWS_STATUS_OFFSET) = b ? AWQ_MOE_STATUS_BAD_ID_BIT : 0u;
   }
   if (!live) return;  // invalid slot: no row (uniform over the workgroup)
+  __shared__ float norm_part[16];  // [wave] sums of squares (NORM)
   if constexpr (NORM) {
-    // after the weight loads: the norm must not delay them
-    __builtin_amdgcn_sched_barrier(0);
-    __shared__ float runs[512];  // H <= 4096 here: at most 512 runs
-    const int quad = tu & 3;
-    const bool hi = quad & 1;
-    if (tu < L && (quad >> 1) == hf)
-      runs[tu] = run_sumsq(hi ? av.px[4] : av.px[0], hi ? av.px[5] : av.px[1], hi ? av.px[6] : av.px[2],
-                           hi ? av.px[7] : av.px[3]);
-    __syncthreads();
-    __shared__ float norm_part[16];
-    const float inv = row_inv_rms(t < L ? runs[t] : 0.f, H, eps, norm_part);
-    if (tu < L) {
-#pragma unroll
-      for (int i = 0; i < 8; ++i) av.px[i] = norm_pair(av.px[i], inv);
-    }
+    const float ss = wave_sum_xor_order(tu < L ? pairs_sumsq<8>(av.px) : 0.f);
+    if (lane == 0) norm_part[wave] = ss;
   }
   float p0 = 0.f, p1 = 0.f, p2 = 0.f, p3 = 0.f;
   if (tu < L) {
@@ -628,6 +580,11 @@ __global__ __launch_bounds__(1024) void w13_swiglu_pair_kernel(const int32_t* __
   if (t < 16) {
     float h = 0.f;
     for (int wv = 0; wv < nwaves; ++wv) h += red[wv][t];
+    if constexpr (NORM) {
+      float ss = 0.f;
+      for (int wv = 0; wv < nwaves; ++wv) ss += norm_part[wv];
+      h *= 1.0f / sqrtf(0.25f * ss / (float)H + eps);
+    }
     const float other = __shfl_xor(h, 1);  // partner column: gate <-> up
     uint16_t* act = reinterpret_cast<uint16_t*>(ws + AWQ_MOE_KWS_ACT_OFFSET);
     if (!(t & 1)) act[(uint64_t)s * I + nt * 8 + (t >> 1)] = __builtin_bit_cast(uint16_t, (_Float16)silu_mul(h, other));

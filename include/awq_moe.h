@@ -227,14 +227,15 @@ int awq_moe_router_topk(const float* logits, int32_t M, int32_t num_experts, int
 
 /* One stacked pre-norm layer around the stage (the norm and the residual are
  * not on the pages; fork PR #12, Purpose and stack, leaves the rest of the
- * model unchanged): with x = fp16(r / sqrt(mean(r^2) + eps)) per row, as
- * awq_moe_residual_rmsnorm computes it (bit-identical), and
- * out = the fp16 result of awq_moe_decode(x, topk_ids, topk_w),
+ * model unchanged): with x = r / sqrt(mean(r^2) + eps) per row and
+ * out = the fp16 result of the stage on x (as awq_moe_decode computes it),
  *   r_next = fp16(r + out)     (fp32 add, one rounding)
- * which equals awq_moe_residual_rmsnorm(r, delta = out).r_next. Two launches,
- * like awq_moe_decode: every W13 workgroup computes its token's norm from the
- * row it loads anyway, and the W2 workgroups add the residual as they store,
- * so no separate norm or residual launch sits between two layers.
+ * Two launches, like awq_moe_decode: the W13 workgroups take their dot
+ * products on r and scale each column's fp32 sum by 1/sqrt(mean(r^2) + eps)
+ * (the norm is a per-row scale; x is never rounded to fp16, unlike the x of
+ * awq_moe_residual_rmsnorm), computing the mean from the row they load
+ * anyway; the W2 workgroups add the residual as they store. So no separate
+ * norm or residual launch sits between two layers.
  *   r, r_next: device fp16 [M][hidden], 16-byte aligned, not overlapping;
  *   eps in (0, 1]; the other arguments, the workspace and its contents
  *   (status word, act) as for awq_moe_decode. */
