@@ -21,6 +21,8 @@ LIB_PATH = os.path.join(HERE, "libawq_moe.so")
 OK, EINVAL, EUNSUPPORTED, ENOSPC, EHIP = 0, -1, -2, -3, -4
 MAX_TOKENS, MAX_TOPK = 8, 32
 STATUS_BAD_ID = 1
+W13_TABLE, W13_PAIR, W13_SINGLE, W13_SINGLE_TWO_TILES = 0, 1, 2, 3
+W2_TABLE, W2_SEG_MOST, W2_SEG_FEWER = 0, 1, 2
 NOALLOC_SCRATCH_BYTES = 256 + 512 * 1024
 WS_STATUS_OFFSET = 0
 WS_ACT_OFFSET = 256
@@ -28,6 +30,7 @@ WS_ACT_OFFSET = 256
 EXPORTED = (
     "awq_moe_bank_layout_query", "awq_moe_prepare", "awq_moe_workspace_bytes",
     "awq_moe_route_compact", "awq_moe_decode", "awq_moe_decode_noalloc", "awq_moe_decode_rmsnorm_residual",
+    "awq_moe_decode_table", "awq_moe_decode_forms",
     "awq_moe_w13_swiglu", "awq_moe_w2_reduce",
     "awq_moe_dequant", "awq_moe_router_topk", "awq_moe_residual_rmsnorm", "awq_moe_router_residual",
     "awq_moe_router_gemv", "awq_moe_prefill_workspace_bytes", "awq_moe_prefill", "awq_moe_last_error",
@@ -73,6 +76,8 @@ def _load() -> ctypes.CDLL:
         "awq_moe_decode": [D, P, U64, P, P, P, I32, I32, P, P, U64, V],
         "awq_moe_decode_noalloc": [D, P, U64, P, P, P, I32, I32, P, P, V],
         "awq_moe_decode_rmsnorm_residual": [D, P, U64, P, ctypes.c_float, P, P, I32, I32, P, P, U64, V],
+        "awq_moe_decode_table": [D, I32, I32, ctypes.POINTER(ctypes.c_int32), ctypes.POINTER(ctypes.c_int32)],
+        "awq_moe_decode_forms": [D, P, U64, P, P, P, I32, I32, P, P, U64, I32, I32, I32, V],
         "awq_moe_prefill_workspace_bytes": [D, I32, I32, ctypes.POINTER(ctypes.c_uint64)],
         "awq_moe_prefill": [D, P, U64, P, P, P, I32, I32, P, P, U64, V],
         "awq_moe_w13_swiglu": [D, P, U64, P, P, I32, I32, P, U64, V],
@@ -266,6 +271,35 @@ def awq_moe_decode_rmsnorm_residual(dims: awq_moe_dims, bank, r, topk_ids, topk_
         _dev(r_next, torch.float16, (M, dims.hidden), "r_next"), _dev(workspace, torch.uint8, name="workspace"),
         workspace.numel(), _stream(stream)), "awq_moe_decode_rmsnorm_residual")
     return r_next
+
+
+def awq_moe_decode_table(dims: awq_moe_dims, M: int, topk: int) -> tuple[int, int]:
+    """(W13 form, W2 form) the tactic table picks for (dims, M, topk)."""
+    a, b = ctypes.c_int32(), ctypes.c_int32()
+    _check(_lib.awq_moe_decode_table(ctypes.byref(dims), M, topk, ctypes.byref(a), ctypes.byref(b)),
+           "awq_moe_decode_table")
+    return a.value, b.value
+
+
+def awq_moe_decode_forms(dims: awq_moe_dims, bank, x, topk_ids, topk_w, w13_form: int, w2_form: int, stages: int = 3,
+                         out=None, workspace=None, stream=None):
+    """awq_moe_decode with forced kernel forms (0 = the table's). stages: 1 W13, 2 W2, 3 both."""
+    torch = _torch()
+    M, k = topk_ids.shape
+    H = dims.hidden
+    if out is None and stages & 2:
+        out = torch.empty((M, H), dtype=torch.float16, device=topk_ids.device)
+    if workspace is None:
+        workspace = alloc_workspace(dims, M, k, topk_ids.device)
+    xp = _dev(x, torch.float16, (M, H), "x") if stages & 1 else None
+    wp = _dev(topk_w, torch.float32, (M, k), "topk_w") if stages & 2 else None
+    op = _dev(out, torch.float16, (M, H), "out") if stages & 2 else None
+    _check(_lib.awq_moe_decode_forms(
+        ctypes.byref(dims), _dev(bank, torch.uint8, name="bank"), bank.numel(), xp,
+        _dev(topk_ids, torch.int32, (M, k), "topk_ids"), wp, M, k, op,
+        _dev(workspace, torch.uint8, name="workspace"), workspace.numel(), w13_form, w2_form, stages,
+        _stream(stream)), "awq_moe_decode_forms")
+    return out if stages & 2 else workspace
 
 
 def awq_moe_prefill_workspace_bytes(dims: awq_moe_dims, max_tokens: int, topk: int) -> int:

@@ -391,7 +391,7 @@ int awq_moe_w13_swiglu(const awq_moe_dims* dims, const void* bank, uint64_t bank
   if (!x || !aligned(x, 16)) return fail(AWQ_MOE_EINVAL, "x null or not 16-byte aligned");
   if (!topk_ids || !aligned(topk_ids, 4)) return fail(AWQ_MOE_EINVAL, "topk_ids null or misaligned");
   if ((rc = check_device())) return rc;
-  return hip_status(awq_moe::launch_w13_swiglu(stage_args(dims, bank, topk_ids, M, topk), x, workspace, false, 0.f,
+  return hip_status(awq_moe::launch_w13_swiglu(stage_args(dims, bank, topk_ids, M, topk), x, workspace, false, 0.f, 0,
                                                static_cast<hipStream_t>(stream)),
                     "w13 launch");
 }
@@ -406,7 +406,7 @@ int awq_moe_w2_reduce(const awq_moe_dims* dims, const void* bank, uint64_t bank_
   if (!out || !aligned(out, 16)) return fail(AWQ_MOE_EINVAL, "out null or not 16-byte aligned");
   if ((rc = check_device())) return rc;
   const WsPtrs w = ws_ptrs(workspace);
-  return hip_status(awq_moe::launch_w2_reduce(stage_args(dims, bank, topk_ids, M, topk), w.act, topk_w, out, nullptr,
+  return hip_status(awq_moe::launch_w2_reduce(stage_args(dims, bank, topk_ids, M, topk), w.act, topk_w, out, nullptr, 0,
                                               static_cast<hipStream_t>(stream)),
                     "w2 launch");
 }
@@ -502,9 +502,9 @@ int awq_moe_decode(const awq_moe_dims* dims, const void* bank, uint64_t bank_byt
   const WsPtrs w = ws_ptrs(workspace);
   hipStream_t s = static_cast<hipStream_t>(stream);
   const awq_moe::StageArgs a = stage_args(dims, bank, topk_ids, M, topk);
-  hipError_t e = awq_moe::launch_w13_swiglu(a, x, workspace, false, 0.f, s);
+  hipError_t e = awq_moe::launch_w13_swiglu(a, x, workspace, false, 0.f, 0, s);
   if (e != hipSuccess) return hip_status(e, "w13 launch");
-  return hip_status(awq_moe::launch_w2_reduce(a, w.act, topk_w, out, nullptr, s), "w2 launch");
+  return hip_status(awq_moe::launch_w2_reduce(a, w.act, topk_w, out, nullptr, 0, s), "w2 launch");
 }
 
 int awq_moe_decode_rmsnorm_residual(const awq_moe_dims* dims, const void* bank, uint64_t bank_bytes,
@@ -525,9 +525,52 @@ int awq_moe_decode_rmsnorm_residual(const awq_moe_dims* dims, const void* bank, 
   const WsPtrs w = ws_ptrs(workspace);
   hipStream_t s = static_cast<hipStream_t>(stream);
   const awq_moe::StageArgs a = stage_args(dims, bank, topk_ids, M, topk);
-  hipError_t e = awq_moe::launch_w13_swiglu(a, r, workspace, true, eps, s);
+  hipError_t e = awq_moe::launch_w13_swiglu(a, r, workspace, true, eps, 0, s);
   if (e != hipSuccess) return hip_status(e, "w13 launch");
-  return hip_status(awq_moe::launch_w2_reduce(a, w.act, topk_w, r_next, r, s), "w2 launch");
+  return hip_status(awq_moe::launch_w2_reduce(a, w.act, topk_w, r_next, r, 0, s), "w2 launch");
+}
+
+int awq_moe_decode_table(const awq_moe_dims* dims, int32_t M, int32_t topk, int32_t* w13_form, int32_t* w2_form) {
+  int rc = check_dims(dims);
+  if (rc) return rc;
+  if ((rc = check_tokens(M, topk))) return rc;
+  if (!w13_form || !w2_form) return fail(AWQ_MOE_EINVAL, "null output pointer");
+  int a = 0, b = 0;
+  awq_moe::decode_table(dims->hidden, dims->inter, topk, M, dims->meta_bytes, &a, &b);
+  *w13_form = a;
+  *w2_form = b;
+  return ok();
+}
+
+int awq_moe_decode_forms(const awq_moe_dims* dims, const void* bank, uint64_t bank_bytes, const uint16_t* x,
+                         const int32_t* topk_ids, const float* topk_w, int32_t M, int32_t topk, uint16_t* out,
+                         void* workspace, uint64_t workspace_bytes, int32_t w13_form, int32_t w2_form,
+                         int32_t stages, void* stream) {
+  int rc = check_stage(dims, bank, bank_bytes, M, topk, workspace, workspace_bytes);
+  if (rc) return rc;
+  if (stages < 1 || stages > 3) return fail(AWQ_MOE_EINVAL, "stages %d: 1 (W13), 2 (W2) or 3 (both)", stages);
+  if (w13_form < 0 || w13_form >= awq_moe::kW13FormCount || w2_form < 0 || w2_form >= awq_moe::kW2FormCount)
+    return fail(AWQ_MOE_EINVAL, "form out of range (w13 %d, w2 %d)", w13_form, w2_form);
+  if (w13_form && !awq_moe::w13_form_valid(w13_form, dims->hidden, dims->inter, topk, M))
+    return fail(AWQ_MOE_EUNSUPPORTED, "W13 form %d does not fit hidden %d", w13_form, dims->hidden);
+  if (w2_form && !awq_moe::w2_form_valid(w2_form, dims->hidden, dims->inter, topk, M))
+    return fail(AWQ_MOE_EUNSUPPORTED, "W2 form %d does not fit inter %d", w2_form, dims->inter);
+  if ((stages & 1) && (!x || !aligned(x, 16))) return fail(AWQ_MOE_EINVAL, "x null or not 16-byte aligned");
+  if (!topk_ids || !aligned(topk_ids, 4)) return fail(AWQ_MOE_EINVAL, "topk_ids null or misaligned");
+  if (stages & 2) {
+    if (!topk_w || !aligned(topk_w, 4)) return fail(AWQ_MOE_EINVAL, "topk_w null or misaligned");
+    if (!out || !aligned(out, 16)) return fail(AWQ_MOE_EINVAL, "out null or not 16-byte aligned");
+  }
+  if ((rc = check_device())) return rc;
+  const WsPtrs w = ws_ptrs(workspace);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const awq_moe::StageArgs a = stage_args(dims, bank, topk_ids, M, topk);
+  if (stages & 1) {
+    hipError_t e = awq_moe::launch_w13_swiglu(a, x, workspace, false, 0.f, w13_form, s);
+    if (e != hipSuccess) return hip_status(e, "w13 launch");
+  }
+  if (stages & 2) return hip_status(awq_moe::launch_w2_reduce(a, w.act, topk_w, out, nullptr, w2_form, s), "w2 launch");
+  return ok();
 }
 
 int awq_moe_decode_noalloc(const awq_moe_dims* dims, const void* bank, uint64_t bank_bytes, const uint16_t* x,
@@ -554,9 +597,9 @@ int awq_moe_decode_noalloc(const awq_moe_dims* dims, const void* bank, uint64_t 
   const WsPtrs w = ws_ptrs(ws);
   hipStream_t s = static_cast<hipStream_t>(stream);
   const awq_moe::StageArgs a = stage_args(dims, bank, topk_ids, M, topk);
-  e = awq_moe::launch_w13_swiglu(a, x, ws, false, 0.f, s);
+  e = awq_moe::launch_w13_swiglu(a, x, ws, false, 0.f, 0, s);
   if (e != hipSuccess) return hip_status(e, "w13 launch");
-  e = awq_moe::launch_w2_reduce(a, w.act, topk_w, out, nullptr, s);
+  e = awq_moe::launch_w2_reduce(a, w.act, topk_w, out, nullptr, 0, s);
   if (e != hipSuccess) return hip_status(e, "w2 launch");
   if (status) return hip_status(hipMemcpyAsync(status, w.status, 4, hipMemcpyDeviceToDevice, s), "status copy");
   return ok();

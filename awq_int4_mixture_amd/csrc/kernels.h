@@ -39,13 +39,22 @@ struct RouteOut {
 };
 
 hipError_t launch_route_compact(const int32_t* ids, int n, int E, const RouteOut& o, hipStream_t stream);
+// Kernel forms of the two decode stages. Form 0 lets the tactic table choose.
+enum W13Form : int { kW13Table = 0, kW13Pair = 1, kW13Single = 2, kW13Single2 = 3, kW13FormCount = 4 };
+enum W2Form : int { kW2Table = 0, kW2SegMost = 1, kW2SegFewer = 2, kW2FormCount = 3 };
+// The forms the table chooses for a shape (always valid for it).
+void decode_table(int H, int I, int topk, int M, int RB, int* w13_form, int* w2_form);
+// Whether a form (other than 0) can run a shape.
+bool w13_form_valid(int form, int H, int I, int topk, int M);
+bool w2_form_valid(int form, int H, int I, int topk, int M);
+
 // ws: the decode workspace (status word and act at the offsets above).
-// norm: x is a residual row r and the stage consumes fp16(rms_norm(r, eps)).
-hipError_t launch_w13_swiglu(const StageArgs& a, const uint16_t* x, void* ws, bool norm, float eps,
+// norm: x is a residual row r and the stage consumes r / rms(r) (eps).
+hipError_t launch_w13_swiglu(const StageArgs& a, const uint16_t* x, void* ws, bool norm, float eps, int form,
                              hipStream_t stream);
 // resid non-null: out receives fp16(resid + fp16(result)).
 hipError_t launch_w2_reduce(const StageArgs& a, const uint16_t* act, const float* topk_w, uint16_t* out,
-                            const uint16_t* resid, hipStream_t stream);
+                            const uint16_t* resid, int form, hipStream_t stream);
 hipError_t launch_router_topk(const float* logits, int M, int E, int k, int32_t* ids, float* w, hipStream_t stream);
 // r_next and x may not alias r or delta.
 hipError_t launch_residual_rmsnorm(const uint16_t* r, const uint16_t* delta, int M, int H, float eps,

@@ -372,19 +372,26 @@ __device__ __forceinline__ float pairs_sumsq(const uint32_t* px) {
 // lanes' squares (every group is held by the 4 lanes of a quad, so the
 // wave's sum is exactly 4 times the sum over its groups), the waves' sums
 // go through LDS with the column sums, and the one barrier serves both.
-template <int RB, bool NORM>
+// With TPB = 2 a workgroup takes two adjacent tiles of the slot (grid.x =
+// 2I/32), each on its own ceil(L/64) waves: one id load and one workgroup
+// per pair of tiles (a tactic for larger grids).
+template <int RB, bool NORM, int TPB>
 __global__ __launch_bounds__(1024) void w13_swiglu_kernel(const int32_t* __restrict__ ids,
                                                           const uint8_t* __restrict__ units_base,
                                                           const uint16_t* __restrict__ x, uint8_t* __restrict__ ws,
                                                           uint32_t expert_bytes, uint32_t meta_delta, uint32_t dims,
                                                           int E, float eps) {
+  static_assert(TPB == 1 || TPB == 2, "one or two tiles per workgroup");
   __shared__ float red[16][16];  // [wave][column]
-  const int nt = blockIdx.x, s = blockIdx.y;
+  const int s = blockIdx.y;
   const int e = ids[s];  // scalar load
   const int G = dims_G(dims), I = 32 * dims_G2(dims), topk = dims_topk(dims);
-  const int H = 32 * G, L = 4 * G, nwaves = (L + 63) >> 6;
-  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
-  const bool status_wave = nt == 0 && s == 0 && wave == 0;
+  const int H = 32 * G, L = 4 * G, nwaves = (L + 63) >> 6;  // waves per tile
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+  const int tile_i = (TPB == 2 && wave >= nwaves) ? 1 : 0;
+  const int nt = blockIdx.x * TPB + tile_i;
+  const int t = threadIdx.x - tile_i * 64 * nwaves;  // lane index within the tile
+  const bool status_wave = blockIdx.x == 0 && s == 0 && wave == 0;
   const int n = topk * dims_M(dims);  // <= 256 slots: four per lane of one wave
   int sid[4];
   if (status_wave) {
@@ -433,17 +440,21 @@ __global__ __launch_bounds__(1024) void w13_swiglu_kernel(const int32_t* __restr
   const float v = sum4_lane_bits_2to5(part[0], part[1], part[2], part[3]);
   if ((lane & 12) == 0) red[wave][4 * (lane & 3) + 2 * ((lane >> 4) & 1) + (lane >> 5)] = v;
   __syncthreads();
-  if (t < 16) {
+  if (threadIdx.x < 16 * TPB) {
+    const int ti = threadIdx.x >> 4, c = threadIdx.x & 15;  // tile of the workgroup, column
+    const int w0 = ti * nwaves;
     float h = 0.f;
-    for (int wv = 0; wv < nwaves; ++wv) h += red[wv][t];
+    for (int wv = w0; wv < w0 + nwaves; ++wv) h += red[wv][c];
     if constexpr (NORM) {
       float ss = 0.f;
-      for (int wv = 0; wv < nwaves; ++wv) ss += norm_part[wv];
+      for (int wv = w0; wv < w0 + nwaves; ++wv) ss += norm_part[wv];
       h *= 1.0f / sqrtf(0.25f * ss / (float)H + eps);
     }
     const float other = __shfl_xor(h, 1);  // partner column: gate <-> up
     uint16_t* act = reinterpret_cast<uint16_t*>(ws + AWQ_MOE_KWS_ACT_OFFSET);
-    if (!(t & 1)) act[(uint64_t)s * I + nt * 8 + (t >> 1)] = __builtin_bit_cast(uint16_t, (_Float16)silu_mul(h, other));
+    if (!(c & 1))
+      act[(uint64_t)s * I + (blockIdx.x * TPB + ti) * 8 + (c >> 1)] =
+          __builtin_bit_cast(uint16_t, (_Float16)silu_mul(h, other));
   }
 }
 
@@ -933,33 +944,110 @@ static bool fits32(const StageArgs& a, uint64_t meta_delta) {
   return a.expert_bytes <= 0xFFFFFFFFull && meta_delta <= 0xFFFFFFFFull;
 }
 
+// ---------------------------------------------------------------------------
+// Tactic table: the kernel form of each stage per token count M and record
+// size, measured on the rank layer (512 experts, hidden 2560, inter 160,
+// top-k 10; cold weights, shared expert pools for M >= 2, graphs of 48
+// calls). A form the shape cannot run falls back to the general rule: lane
+// pairs while the grid has at most one workgroup per CU (256), else single
+// lanes; for W2 the most slots per wave.
+// ---------------------------------------------------------------------------
+struct DecodeTactic {
+  int8_t w13, w2;
+};
+// [record bytes 3, 4][M - 1]. W13 us per launch, 3-byte records (lane pairs /
+// single lanes / two tiles per workgroup): M=1 3.78 / 3.93 / 4.16,
+// M=2 4.57 / 4.50 / 4.38, M=3 5.59 / 5.15 / 5.79, M=8 9.40 / 7.89 / 8.93;
+// 4-byte records rank the same. W2 with the most slots per wave wins at
+// every M (M=1 3.60 against 3.80, M=8 5.88 against 6.47).
+constexpr DecodeTactic kDecodeTable[2][AWQ_MOE_KMAX_TOKENS] = {
+    {{kW13Pair, kW2SegMost}, {kW13Single2, kW2SegMost}, {kW13Single, kW2SegMost}, {kW13Single, kW2SegMost},
+     {kW13Single, kW2SegMost}, {kW13Single, kW2SegMost}, {kW13Single, kW2SegMost}, {kW13Single, kW2SegMost}},
+    {{kW13Pair, kW2SegMost}, {kW13Single2, kW2SegMost}, {kW13Single, kW2SegMost}, {kW13Single, kW2SegMost},
+     {kW13Single, kW2SegMost}, {kW13Single, kW2SegMost}, {kW13Single, kW2SegMost}, {kW13Single, kW2SegMost}},
+};
+
+// The slot-segment W2 kernel's instantiated slots-per-wave values, descending.
+constexpr int kSpwChoices[] = {16, 8, 5, 4, 3, 2};
+
+static int w2_spw(int form, int I) {
+  const int cap = 64 / (I / 8);  // slots that fit a wave at I/8 lanes each
+  int most = -1;
+  for (int i = 0; i < (int)(sizeof kSpwChoices / sizeof kSpwChoices[0]); ++i)
+    if (kSpwChoices[i] <= cap) {
+      most = i;
+      break;
+    }
+  if (most < 0) return 0;
+  if (form == kW2SegFewer) return most + 1 < (int)(sizeof kSpwChoices / sizeof kSpwChoices[0]) ? kSpwChoices[most + 1] : 0;
+  return kSpwChoices[most];
+}
+
+bool w13_form_valid(int form, int H, int I, int topk, int M) {
+  const int L = 4 * (H / 32);
+  switch (form) {
+    case kW13Pair: return 2 * L <= 1024;
+    case kW13Single: return L <= 1024;
+    case kW13Single2: return 2 * ((L + 63) / 64) * 64 <= 1024 && ((2 * I) / 16) % 2 == 0;
+    default: return false;
+  }
+}
+
+bool w2_form_valid(int form, int H, int I, int topk, int M) {
+  if (I > 256) return form == kW2SegMost;  // the generic kernel (one form)
+  if (form == kW2SegMost) return w2_spw(form, I) > 0;
+  if (form == kW2SegFewer) return w2_spw(form, I) > 0;
+  return false;
+}
+
+void decode_table(int H, int I, int topk, int M, int RB, int* w13_form, int* w2_form) {
+  const DecodeTactic d = kDecodeTable[RB == 4 ? 1 : 0][M - 1];
+  int f13 = d.w13, f2 = d.w2;
+  const uint64_t grid = (uint64_t)((2 * I) / 16) * M * topk;
+  // the table's lane pairs are for grids of up to two workgroups per CU (its
+  // rank layer at M <= 2); other shapes take the general rule
+  if (!w13_form_valid(f13, H, I, topk, M) || (f13 == kW13Pair && grid > 512))
+    f13 = w13_form_valid(kW13Pair, H, I, topk, M) && grid <= 256 ? kW13Pair : kW13Single;
+  if (!w2_form_valid(f2, H, I, topk, M)) f2 = kW2SegMost;
+  *w13_form = f13;
+  *w2_form = f2;
+}
+
 template <int RB, bool NORM>
-static void launch_w13_t(const StageArgs& a, const uint16_t* x, uint8_t* w, uint32_t md, float eps, hipStream_t stream) {
+static void launch_w13_t(const StageArgs& a, const uint16_t* x, uint8_t* w, uint32_t md, float eps, int form,
+                         hipStream_t stream) {
   const int L = 4 * (a.H / 32);
   const dim3 grid((2 * a.I) / 16, a.M * a.topk);
   const uint32_t dims = pack_dims(a.H, a.I, a.topk, a.M);
-  // Lane pairs when every workgroup has a CU to itself (MI355X: 256 CUs), where
-  // the busiest SIMD sets the time; with more workgroups the pair kernel's
-  // 8-byte loads cost more than it saves (M = 8: 7.6 -> 9.3 us).
-  if (2 * L <= 1024 && (uint64_t)grid.x * grid.y <= 256)
+  const int bw = ((L + 63) / 64) * 64;  // threads per tile, single lanes
+  if (form == kW13Pair)
     hipLaunchKernelGGL((w13_swiglu_pair_kernel<RB, NORM>), grid, dim3(((2 * L + 63) / 64) * 64), 0, stream,
                        a.topk_ids, a.bank + a.w13_off, x, w, (uint32_t)a.expert_bytes, md, dims, a.E, eps);
+  else if (form == kW13Single2)
+    hipLaunchKernelGGL((w13_swiglu_kernel<RB, NORM, 2>), dim3(grid.x / 2, grid.y), dim3(2 * bw), 0, stream,
+                       a.topk_ids, a.bank + a.w13_off, x, w, (uint32_t)a.expert_bytes, md, dims, a.E, eps);
   else
-    hipLaunchKernelGGL((w13_swiglu_kernel<RB, NORM>), grid, dim3(((L + 63) / 64) * 64), 0, stream, a.topk_ids,
-                       a.bank + a.w13_off, x, w, (uint32_t)a.expert_bytes, md, dims, a.E, eps);
+    hipLaunchKernelGGL((w13_swiglu_kernel<RB, NORM, 1>), grid, dim3(bw), 0, stream, a.topk_ids, a.bank + a.w13_off,
+                       x, w, (uint32_t)a.expert_bytes, md, dims, a.E, eps);
 }
 
-hipError_t launch_w13_swiglu(const StageArgs& a, const uint16_t* x, void* ws, bool norm, float eps,
+hipError_t launch_w13_swiglu(const StageArgs& a, const uint16_t* x, void* ws, bool norm, float eps, int form,
                              hipStream_t stream) {
   const uint64_t md = a.w13_meta_off - a.w13_off;
   if (!fits32(a, md)) return hipErrorInvalidValue;
+  if (form == kW13Table) {
+    int f2;
+    decode_table(a.H, a.I, a.topk, a.M, a.RB, &form, &f2);
+  } else if (!w13_form_valid(form, a.H, a.I, a.topk, a.M)) {
+    return hipErrorInvalidValue;
+  }
   uint8_t* w = static_cast<uint8_t*>(ws);
   if (a.RB == 4) {
-    if (norm) launch_w13_t<4, true>(a, x, w, (uint32_t)md, eps, stream);
-    else launch_w13_t<4, false>(a, x, w, (uint32_t)md, eps, stream);
+    if (norm) launch_w13_t<4, true>(a, x, w, (uint32_t)md, eps, form, stream);
+    else launch_w13_t<4, false>(a, x, w, (uint32_t)md, eps, form, stream);
   } else {
-    if (norm) launch_w13_t<3, true>(a, x, w, (uint32_t)md, eps, stream);
-    else launch_w13_t<3, false>(a, x, w, (uint32_t)md, eps, stream);
+    if (norm) launch_w13_t<3, true>(a, x, w, (uint32_t)md, eps, form, stream);
+    else launch_w13_t<3, false>(a, x, w, (uint32_t)md, eps, form, stream);
   }
   return hipGetLastError();
 }
@@ -988,30 +1076,30 @@ static void launch_w2_seg(const StageArgs& a, const uint16_t* act, const float* 
 
 template <int RB, bool RES>
 static void launch_w2_seg_rb(const StageArgs& a, const uint16_t* act, const float* topk_w, uint16_t* out,
-                             const uint16_t* resid, hipStream_t stream) {
-  // slots per wave: the largest instantiated SPW <= floor(64 / LS), LS = I/8 lanes per slot
-  const int spw = 64 / (a.I / 8);
-  if (spw >= 16) launch_w2_seg<RB, 16, RES>(a, act, topk_w, out, resid, stream);
-  else if (spw >= 8) launch_w2_seg<RB, 8, RES>(a, act, topk_w, out, resid, stream);
-  else if (spw >= 5) launch_w2_seg<RB, 5, RES>(a, act, topk_w, out, resid, stream);
-  else if (spw >= 4) launch_w2_seg<RB, 4, RES>(a, act, topk_w, out, resid, stream);
-  else if (spw >= 3) launch_w2_seg<RB, 3, RES>(a, act, topk_w, out, resid, stream);
+                             const uint16_t* resid, int spw, hipStream_t stream) {
+  // spw: an instantiated slots-per-wave value that fits (I/8 lanes per slot)
+  if (spw == 16) launch_w2_seg<RB, 16, RES>(a, act, topk_w, out, resid, stream);
+  else if (spw == 8) launch_w2_seg<RB, 8, RES>(a, act, topk_w, out, resid, stream);
+  else if (spw == 5) launch_w2_seg<RB, 5, RES>(a, act, topk_w, out, resid, stream);
+  else if (spw == 4) launch_w2_seg<RB, 4, RES>(a, act, topk_w, out, resid, stream);
+  else if (spw == 3) launch_w2_seg<RB, 3, RES>(a, act, topk_w, out, resid, stream);
   else launch_w2_seg<RB, 2, RES>(a, act, topk_w, out, resid, stream);
 }
 
 template <bool RES>
 static hipError_t launch_w2_res(const StageArgs& a, const uint16_t* act, const float* topk_w, uint16_t* out,
-                                const uint16_t* resid, hipStream_t stream) {
+                                const uint16_t* resid, int form, hipStream_t stream) {
   if (a.I <= 256) {
     // the slot-segment kernel derives the expert geometry from the shape word
     const ExpertGeometry g = a.RB == 4 ? expert_geometry<4>(pack_dims(a.H, a.I, a.topk, a.M))
                                        : expert_geometry<3>(pack_dims(a.H, a.I, a.topk, a.M));
     if (g.expert_bytes != a.expert_bytes || g.w2_off != a.w2_off || g.w2_meta_delta != a.w2_meta_off - a.w2_off)
       return hipErrorInvalidValue;
+    const int spw = w2_spw(form, a.I);
     if (a.RB == 4)
-      launch_w2_seg_rb<4, RES>(a, act, topk_w, out, resid, stream);
+      launch_w2_seg_rb<4, RES>(a, act, topk_w, out, resid, spw, stream);
     else
-      launch_w2_seg_rb<3, RES>(a, act, topk_w, out, resid, stream);
+      launch_w2_seg_rb<3, RES>(a, act, topk_w, out, resid, spw, stream);
     return hipGetLastError();
   }
   if (a.RB == 4)
@@ -1022,9 +1110,15 @@ static hipError_t launch_w2_res(const StageArgs& a, const uint16_t* act, const f
 }
 
 hipError_t launch_w2_reduce(const StageArgs& a, const uint16_t* act, const float* topk_w, uint16_t* out,
-                            const uint16_t* resid, hipStream_t stream) {
-  return resid ? launch_w2_res<true>(a, act, topk_w, out, resid, stream)
-               : launch_w2_res<false>(a, act, topk_w, out, nullptr, stream);
+                            const uint16_t* resid, int form, hipStream_t stream) {
+  if (form == kW2Table) {
+    int f13;
+    decode_table(a.H, a.I, a.topk, a.M, a.RB, &f13, &form);
+  } else if (!w2_form_valid(form, a.H, a.I, a.topk, a.M)) {
+    return hipErrorInvalidValue;
+  }
+  return resid ? launch_w2_res<true>(a, act, topk_w, out, resid, form, stream)
+               : launch_w2_res<false>(a, act, topk_w, out, nullptr, form, stream);
 }
 
 hipError_t launch_dequant(const uint8_t* bank, uint64_t expert_bytes, uint64_t units_off,

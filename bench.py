@@ -59,6 +59,9 @@ def parse():
     p.add_argument("--only", default="", help="comma list of workloads: m1_cold,m1_hot,m8_pool,m8_distinct "
                    "(any mN_pool / mN_distinct, N = 1..8),p128,p256,p512,p1024,p4096,stack48,stack48_gemv")
     p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    p.add_argument("--tactics", action="store_true",
+                   help="time every kernel form of both stages for M = 1..8 and both record sizes (cold weights) "
+                        "and print that table instead of the benchmark line")
     return p.parse_args()
 
 
@@ -442,28 +445,30 @@ def cpu_baseline(bi, cold_calls, pool_calls, per_sample_s=0.6, samples=5):
             "layer_us": head["us_per_layer_median5"], "per_config": out}
 
 
-def stage_kernel_names(M, H=H, I=I, topk=K_TOP, rb=4):
-    """Names of the W13 and W2 kernels the library launches for a shape (the
-    launchers' rules: lane pairs for W13 when every workgroup has a CU of its
-    own, W2 slot segments of I/8 lanes at inter <= 256)."""
-    pair = 2 * (H // 8) <= 1024 and (2 * I // 16) * M * topk <= 256
-    w13 = f"w13_swiglu_pair_kernel<{rb}>" if pair else f"w13_swiglu_kernel<{rb}>"
+def stage_kernel_names(abi, M, rb, H=H, I=I, topk=K_TOP, E_=E):
+    """Names (as the kernel trace prints them) of the W13 and W2 kernels the
+    library's tactic table picks for a shape (awq_moe_decode_table)."""
+    f13, f2 = abi.awq_moe_decode_table(abi.make_dims(E_, H, I, rb), M, topk)
+    w13 = {abi.W13_PAIR: f"w13_swiglu_pair_kernel<{rb}, false>",
+           abi.W13_SINGLE: f"w13_swiglu_kernel<{rb}, false, 1>",
+           abi.W13_SINGLE_TWO_TILES: f"w13_swiglu_kernel<{rb}, false, 2>"}[f13]
     if I <= 256:
-        spw = 64 // (I // 8)
-        spw = max(v for v in (2, 3, 4, 5, 8, 16) if v <= spw)
-        w2 = f"w2_reduce_seg_kernel<{rb}, {spw}>"
+        cap = 64 // (I // 8)
+        choices = [v for v in (16, 8, 5, 4, 3, 2) if v <= cap]
+        spw = choices[0] if f2 == abi.W2_SEG_MOST else choices[1]
+        w2 = f"w2_reduce_seg_kernel<{rb}, {spw}, false>"
     else:
-        w2 = f"w2_reduce_kernel<{rb}, 1>"
+        w2 = f"w2_reduce_kernel<{rb}, 1, false>"
     return w13, w2
 
 
-def roofline(head, rb):
+def roofline(abi, head, rb):
     """HBM roofline of the longer of the two stage kernels at the headline
     workload. ``achieved`` and ``frac`` use the HIP-event clock (per-launch
     period of a graph of 48 launches of that kernel alone); the committed
     kernel-trace duration of the same kernel is carried next to it."""
     k = "w2" if head["w2_us"] >= head["w13_us"] else "w13"
-    w13_name, w2_name = stage_kernel_names(head["M"], rb=rb)
+    w13_name, w2_name = stage_kernel_names(abi, head["M"], rb)
     name = {"w13": w13_name, "w2": w2_name}[k]
     gbs = head[k + "_gbs"]
     algo = head[k + "_bytes_per_call"]
@@ -484,6 +489,64 @@ def roofline(head, rb):
         out["trace_avg_us"] = round(tr[0] / 1e3, 3)
         out["trace_median_us"] = round(tr[1] / 1e3, 3)
         out["frac_trace_avg"] = round(algo / (tr[0] / 1e3) / 1e3 / HBM_PEAK_GBS, 4)
+    return out
+
+
+def tactic_sweep(abi, torch, steps, rounds=3):
+    """Per record size and M = 1..8: every W13 form alone and every W2 form
+    alone, timed as graphs of 48 calls on cold weights (the headline's bank
+    rotation; M = 1 distinct experts, M >= 2 shared pools), in alternating
+    order over `rounds` rounds (minimum and median per form), next to the
+    forms the library's table picks."""
+    bi = inputs.bank_inputs(SEED, E, H, I)
+    out = {}
+    for rb in (3, 4):
+        dims = abi.make_dims(E, H, I, rb)
+        host = torch.from_numpy(abi.prepare_from_inputs(dims, bi))
+        banks = [host.to("cuda") for _ in range(COLD_BANKS)]
+        del host
+        per_expert = per_expert_bytes(abi, dims)
+        rng = inputs.call_rng(SEED, 5)
+        table = {}
+        for M in range(1, 9):
+            calls = inputs.rotating_calls(SEED + M, COLD_GRAPHS * CALLS, M, K_TOP, E, COLD_BANKS,
+                                          "distinct" if M == 1 else "pool")
+            wl = Workload(f"m{M}", abi, torch, dims, banks, calls, M, rng, per_expert, graphs=COLD_GRAPHS)
+            forms = {}
+            for f13 in (abi.W13_PAIR, abi.W13_SINGLE, abi.W13_SINGLE_TWO_TILES):
+                forms[("w13", f13)] = (f13, 0, 1)
+            for f2 in (abi.W2_SEG_MOST, abi.W2_SEG_FEWER):
+                forms[("w2", f2)] = (0, f2, 2)
+            graphs = {}
+            for key, (f13, f2, st) in forms.items():
+                def run(g, f13=f13, f2=f2, st=st):
+                    for c in range(g * CALLS, (g + 1) * CALLS):
+                        abi.awq_moe_decode_forms(wl.dims, wl.bank_of[c], wl.x[c], wl.ids[c], wl.w[c], f13, f2,
+                                                 stages=st, out=wl.out, workspace=wl.ws[c])
+                for g in range(COLD_GRAPHS):
+                    run(g)
+                graphs[key] = [capture(torch, lambda g=g, f=run: f(g)) for g in range(COLD_GRAPHS)]
+            samples = {key: [] for key in graphs}
+            keys = list(graphs)
+            for r in range(rounds):
+                for key in (keys if r % 2 == 0 else keys[::-1]):
+                    samples[key].append(time_graphs(torch, graphs[key], steps, COLD_GRAPHS) * 1e3 / CALLS)
+            del graphs
+            f13_t, f2_t = abi.awq_moe_decode_table(dims, M, K_TOP)
+            table[f"M{M}"] = {
+                "w13_us": {str(k[1]): round(float(np.min(v)), 3) for k, v in samples.items() if k[0] == "w13"},
+                "w13_us_median": {str(k[1]): round(float(np.median(v)), 3) for k, v in samples.items()
+                                  if k[0] == "w13"},
+                "w2_us": {str(k[1]): round(float(np.min(v)), 3) for k, v in samples.items() if k[0] == "w2"},
+                "w2_us_median": {str(k[1]): round(float(np.median(v)), 3) for k, v in samples.items()
+                                 if k[0] == "w2"},
+                "table": [f13_t, f2_t], "distinct_experts_per_call": wl.distinct_mean,
+            }
+            del wl
+            print(f"tactics rb={rb} M={M} {table[f'M{M}']}", flush=True)
+        out[f"rb{rb}"] = table
+        del banks
+        torch.cuda.empty_cache()
     return out
 
 
@@ -512,6 +575,11 @@ def main():
     from awq_int4_mixture_amd import abi
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     torch.cuda.set_device(0)
+    if args.tactics:
+        stream = torch.cuda.Stream()
+        with torch.cuda.stream(stream):
+            print(json.dumps({"tactics": tactic_sweep(abi, torch, max(args.steps // 4, 8))}), flush=True)
+        return
     prefill_wls = {"p128": 128, "p256": 256, "p512": 512, "p1024": 1024, "p4096": 4096}
     only = set(filter(None, args.only.split(","))) or {"m1_cold", "m1_hot", "m8_pool", "m8_distinct", "stack48",
                                                        "stack48_gemv", *prefill_wls}
@@ -596,7 +664,7 @@ def main():
             "layer_us": round(head["layer_us"], 3),
             "calls_per_step": CALLS,
         },
-        "roofline": roofline(head, head_rb),
+        "roofline": roofline(abi, head, head_rb),
         "m8_distinct": brief(results["m8_distinct"]) if "m8_distinct" in results else None,
         "m8_pool": brief(results["m8_pool"]) if "m8_pool" in results else None,
         "m1_hot_effective": (dict(brief(results["m1_hot"]), note="the same 10 experts on every call: "

@@ -186,6 +186,41 @@ int awq_moe_decode_noalloc(const awq_moe_dims* dims, const void* bank, uint64_t 
                            const int32_t* topk_ids, const float* topk_w, int32_t M, int32_t topk,
                            uint16_t* out, uint32_t* status, void* stream);
 
+/* --- the per-M tactic table (kernel forms) ---
+ * Each decode stage has several kernel forms; a constant table inside the
+ * library picks one per token count M and record size (measured on the
+ * rank layer; a form a shape cannot run falls back to a general rule).
+ * Forms: W13 + SwiGLU 1 = lane pairs (each group split over two lanes),
+ * 2 = single lanes (one 16-column tile per workgroup), 3 = single lanes,
+ * two tiles per workgroup; W2 + reduction 1 = slot segments with the most
+ * slots per wave, 2 = one instantiated step fewer (more waves). 0 = the
+ * table's choice. The pages' own tactic table (PR #520, Results: tile
+ * tactics and the small-shape autotune) is the model. */
+#define AWQ_MOE_W13_TABLE 0
+#define AWQ_MOE_W13_PAIR 1
+#define AWQ_MOE_W13_SINGLE 2
+#define AWQ_MOE_W13_SINGLE_TWO_TILES 3
+#define AWQ_MOE_W2_TABLE 0
+#define AWQ_MOE_W2_SEG_MOST 1
+#define AWQ_MOE_W2_SEG_FEWER 2
+
+/* The forms awq_moe_decode uses for (dims, M, topk) (host only). */
+int awq_moe_decode_table(const awq_moe_dims* dims, int32_t M, int32_t topk, int32_t* w13_form, int32_t* w2_form);
+
+/* awq_moe_decode with the forms given instead of the table's (diagnostic:
+ * per-form timing and parity). Arguments as for awq_moe_decode, plus
+ * w13_form, w2_form (0 = the table's) and stages: 1 runs W13 + SwiGLU only
+ * (topk_w and out unused), 2 runs W2 + reduction only, on the act the
+ * workspace holds (x unused), 3 runs both. EUNSUPPORTED when a form cannot
+ * run the shape. Every form gives the same result within the stage's
+ * rounding (the reduction orders differ between lane pairs and single
+ * lanes; two tiles per workgroup and the W2 forms are bit-identical to
+ * their one-tile / most-slots counterparts). */
+int awq_moe_decode_forms(const awq_moe_dims* dims, const void* bank, uint64_t bank_bytes, const uint16_t* x,
+                         const int32_t* topk_ids, const float* topk_w, int32_t M, int32_t topk, uint16_t* out,
+                         void* workspace, uint64_t workspace_bytes, int32_t w13_form, int32_t w2_form,
+                         int32_t stages, void* stream);
+
 /* --- stage exports, for stage-pair checks (fork PR #12, Numerical acceptance:
  * W2 checked on its own intermediate) and per-kernel timing. awq_moe_decode
  * is exactly awq_moe_w13_swiglu followed by awq_moe_w2_reduce on the same

@@ -141,6 +141,8 @@ def test_device_calls_reject_bad_arguments_before_launch():
     bb_big = abi.awq_moe_bank_layout_query(d_big).total_bytes
     d_wide = abi.make_dims(4, 256, 2048, 3)                    # 8 x 32 x 2048 fp16 act: above the fixed scratch
     bb_wide = abi.awq_moe_bank_layout_query(d_wide).total_bytes
+    d8k = abi.make_dims(4, 8192, 32, 3)                        # hidden 8192: no lane pairs (2048 threads)
+    bb8k = abi.awq_moe_bank_layout_query(d8k).total_bytes
     cases = [
         (lambda: lib.awq_moe_decode(ctypes.byref(d), p, bb, p, p, p, 9, 10, p, p, ws_need, None), abi.EINVAL),
         (lambda: lib.awq_moe_decode(ctypes.byref(d), p, bb, p, p, p, 1, 10, p, p, ws_need - 1, None), abi.ENOSPC),
@@ -218,6 +220,19 @@ def test_device_calls_reject_bad_arguments_before_launch():
                                                      ws_need, None), abi.ENOSPC),
         (lambda: lib.awq_moe_decode_rmsnorm_residual(ctypes.byref(d), p, bb, q1, 1e-6, p, p, 1, 10, q2, p,
                                                      ws_need - 1, None), abi.ENOSPC),
+        # forced kernel forms: the stage's checks, then the forms and stages
+        (lambda: lib.awq_moe_decode_forms(ctypes.byref(d), p, bb, p, p, p, 1, 10, p, p, ws_need, 4, 0, 3, None),
+         abi.EINVAL),
+        (lambda: lib.awq_moe_decode_forms(ctypes.byref(d), p, bb, p, p, p, 1, 10, p, p, ws_need, 0, 3, 3, None),
+         abi.EINVAL),
+        (lambda: lib.awq_moe_decode_forms(ctypes.byref(d), p, bb, p, p, p, 1, 10, p, p, ws_need, 0, 0, 0, None),
+         abi.EINVAL),
+        (lambda: lib.awq_moe_decode_forms(ctypes.byref(d), p, bb, p, p, p, 9, 10, p, p, ws_need, 0, 0, 3, None),
+         abi.EINVAL),
+        (lambda: lib.awq_moe_decode_forms(ctypes.byref(d8k), p, bb8k, p, p, p, 1, 2, p, p, 1 << 30, 1, 0, 3, None),
+         abi.EUNSUPPORTED),
+        (lambda: lib.awq_moe_decode_forms(ctypes.byref(d_wide), p, bb_wide, p, p, p, 1, 2, p, p, 1 << 30, 0, 2, 3,
+                                          None), abi.EUNSUPPORTED),
         # the no-allocation entry point: same checks, and a fixed scratch maximum
         (lambda: lib.awq_moe_decode_noalloc(ctypes.byref(d), p, bb, p, p, p, 9, 10, p, None, None), abi.EINVAL),
         (lambda: lib.awq_moe_decode_noalloc(ctypes.byref(d), p, bb - 1, p, p, p, 1, 10, p, None, None), abi.ENOSPC),
@@ -232,6 +247,22 @@ def test_device_calls_reject_bad_arguments_before_launch():
         assert call() == code, (i, abi.awq_moe_last_error())
         assert abi.awq_moe_last_error() != ""
     assert bytes(buf) == bytes(4096)
+
+
+def test_tactic_table_forms_are_valid_for_every_admitted_token_count():
+    """The table answers for every M and record size, and only with forms
+    that fit the shape (lane pairs need hidden <= 4096; the generic W2
+    kernel for inter > 256 has one form)."""
+    for dims in (abi.make_dims(512, 2560, 160, 3), abi.make_dims(512, 2560, 160, 4), abi.make_dims(4, 8192, 32, 3),
+                 abi.make_dims(8, 512, 2048, 3), abi.make_dims(16, 96, 64, 4)):
+        for M in range(1, 9):
+            f13, f2 = abi.awq_moe_decode_table(dims, M, 10)
+            assert f13 in (abi.W13_PAIR, abi.W13_SINGLE, abi.W13_SINGLE_TWO_TILES)
+            assert f2 in (abi.W2_SEG_MOST, abi.W2_SEG_FEWER)
+            if dims.hidden > 4096:
+                assert f13 == abi.W13_SINGLE
+            if dims.inter > 256:
+                assert f2 == abi.W2_SEG_MOST
 
 
 def test_noalloc_scratch_covers_the_rank_shape():

@@ -417,3 +417,63 @@ def test_graph_capture_replays_match_eager(M):
         g.replay()
         torch.cuda.synchronize()
         assert torch.equal(out, eager), rep
+
+
+# ---------------------------------------------------------------------------
+# every kernel form of the tactic table
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("rb", [3, 4])
+@pytest.mark.parametrize("M", [1, 2, 8])
+def test_every_decode_form_against_oracle(rb, M):
+    """Each W13 form (lane pairs, single lanes, single lanes with two tiles
+    per workgroup) and each W2 form (most slots per wave, one step fewer) is
+    within the gate of the oracle; two tiles per workgroup is bit-identical
+    to one, and the W2 forms are bit-identical to each other (same per-lane
+    work, same reduction order); the table's forms equal awq_moe_decode."""
+    H, I, E, k = 2560, 160, 64, 10
+    dims, bank, bi = bank_case(7, E, H, I, rb)
+    rng = inputs.call_rng(70, M)
+    x = inputs.activations(rng, M, H)
+    ids = inputs.ids_shared_pool(rng, M, k, E) if M > 1 else inputs.ids_distinct(rng, 1, k, E)
+    w = inputs.router_weights(rng, M, k)
+    want = R.moe_stage(x, ids, w, E, bi.expert)
+    xd, idd, wd = to_dev(x), to_dev(ids), to_dev(w)
+    outs = {}
+    for f13 in (abi.W13_PAIR, abi.W13_SINGLE, abi.W13_SINGLE_TWO_TILES):
+        for f2 in (abi.W2_SEG_MOST, abi.W2_SEG_FEWER):
+            say("decode forms", M, rb, f13, f2)
+            out = abi.awq_moe_decode_forms(dims, bank, xd, idd, wd, f13, f2)
+            torch.cuda.synchronize()
+            outs[(f13, f2)] = f16_to_np(out)
+            check(outs[(f13, f2)], want, f"forms w13={f13} w2={f2} M={M} rb={rb}")
+    bits = {key: v.view(np.uint16).tolist() for key, v in outs.items()}
+    for f2 in (abi.W2_SEG_MOST, abi.W2_SEG_FEWER):
+        assert bits[(abi.W13_SINGLE, f2)] == bits[(abi.W13_SINGLE_TWO_TILES, f2)]
+    for f13 in (abi.W13_PAIR, abi.W13_SINGLE, abi.W13_SINGLE_TWO_TILES):
+        assert bits[(f13, abi.W2_SEG_MOST)] == bits[(f13, abi.W2_SEG_FEWER)]
+    table = abi.awq_moe_decode_table(dims, M, k)
+    assert run_decode(dims, bank, x, ids, w).view(np.uint16).tolist() == bits[table]
+
+
+def test_forms_on_other_shapes_and_stage_split():
+    """Forms at shapes that change their geometry (hidden 96: lanes past L;
+    inter 32: 16 slots per wave; hidden 4096: 16-wave two-tile blocks), and
+    the W13-only / W2-only stages of the forms composing to the full call."""
+    for (E, H, I, k, M) in ((6, 96, 64, 3, 5), (16, 256, 32, 8, 3), (6, 4096, 64, 2, 2)):
+        dims, bank, bi = bank_case(80 + H, E, H, I, 3)
+        rng = inputs.call_rng(81, H)
+        x = inputs.activations(rng, M, H)
+        ids = inputs.ids_shared_pool(rng, M, k, E)
+        w = inputs.router_weights(rng, M, k)
+        want = R.moe_stage(x, ids, w, E, bi.expert)
+        xd, idd, wd = to_dev(x), to_dev(ids), to_dev(w)
+        for f13 in (abi.W13_PAIR, abi.W13_SINGLE, abi.W13_SINGLE_TWO_TILES):
+            for f2 in (abi.W2_SEG_MOST, abi.W2_SEG_FEWER):
+                say("forms other shape", E, H, I, k, M, f13, f2)
+                full = abi.awq_moe_decode_forms(dims, bank, xd, idd, wd, f13, f2)
+                ws = abi.awq_moe_decode_forms(dims, bank, xd, idd, wd, f13, 0, stages=1)
+                split = abi.awq_moe_decode_forms(dims, bank, xd, idd, wd, 0, f2, stages=2, workspace=ws)
+                torch.cuda.synchronize()
+                check(f16_to_np(full), want, f"forms E={E} H={H} I={I} w13={f13} w2={f2}")
+                assert f16_to_np(full).view(np.uint16).tolist() == f16_to_np(split).view(np.uint16).tolist()
