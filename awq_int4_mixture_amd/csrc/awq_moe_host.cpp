@@ -414,20 +414,28 @@ int awq_moe_w2_reduce(const awq_moe_dims* dims, const void* bank, uint64_t bank_
 namespace {
 
 struct PrefillLayout {
-  uint64_t slot_row, row_slot, items, act, y, total;
+  uint64_t slot_row, row_slot, items, witems, route_cnt, route_bad, act, y, total;
 };
 
 PrefillLayout prefill_layout(const awq_moe_dims* d, int M, int topk) {
   const uint64_t n = (uint64_t)M * (uint64_t)topk;
   const uint64_t mi = (uint64_t)awq_moe::prefill_max_items((int)n, d->num_experts);
+  const uint64_t mw = (uint64_t)awq_moe::prefill_max_wide_items((int)n, d->num_experts);
   PrefillLayout L;
-  uint64_t off = 256;  // status u32 at 0, num_items i32 at 4
+  uint64_t off = 256;  // status u32 at 0, num_items i32 at 4, num wide items i32 at 8
   L.slot_row = off;
   off += pad256(n * 4);
   L.row_slot = off;
   off += pad256(n * 4);
   L.items = off;
   off += pad256(mi * 8);
+  L.witems = off;
+  off += pad256(mw * 8);
+  const uint64_t nb = (uint64_t)awq_moe::prefill_route_blocks((int)n, d->num_experts);
+  L.route_cnt = off;
+  off += pad256(nb * (uint64_t)d->num_experts * 4);
+  L.route_bad = off;
+  off += pad256(nb * 4);
   L.act = off;
   off += pad256(n * (uint64_t)d->inter * 2);
   L.y = off;
@@ -482,6 +490,10 @@ int awq_moe_prefill(const awq_moe_dims* dims, const void* bank, uint64_t bank_by
   w.slot_row = reinterpret_cast<int32_t*>(ws + L.slot_row);
   w.row_slot = reinterpret_cast<int32_t*>(ws + L.row_slot);
   w.items = reinterpret_cast<int32_t*>(ws + L.items);
+  w.num_witems = reinterpret_cast<int32_t*>(ws + 8);
+  w.witems = reinterpret_cast<int32_t*>(ws + L.witems);
+  w.route_cnt = reinterpret_cast<int32_t*>(ws + L.route_cnt);
+  w.route_bad = reinterpret_cast<int32_t*>(ws + L.route_bad);
   w.act = reinterpret_cast<uint16_t*>(ws + L.act);
   w.y = reinterpret_cast<float*>(ws + L.y);
   return hip_status(awq_moe::launch_prefill(stage_args(dims, bank, topk_ids, M, topk), x, topk_w, out, w,

@@ -72,12 +72,20 @@ struct PrefillWs {
   int32_t* num_items;
   int32_t* slot_row;  // [n] row of each slot, -1 for an invalid id
   int32_t* row_slot;  // [n] slot of each row
-  int32_t* items;     // [max_items][2] {expert, row0 | rows << 24}
+  int32_t* items;     // [max_items][2] {expert, row0 | rows << 24}, rows <= 32
+  int32_t* num_witems;
+  int32_t* witems;    // [max_wide_items][2] the same with rows <= 64
+  int32_t* route_cnt;  // [route blocks][E] slots per expert in each routing workgroup's slice
+  int32_t* route_bad;  // [route blocks] the slice holds an id outside [0, E)
   uint16_t* act;      // fp16 [n][I] by row
   float* y;           // fp32 [n][H] by row
 };
 // Upper bound on the number of work items (expert row chunks of 32) for n slots.
 int prefill_max_items(int n, int E);
+// The same for wide work items (chunks of 64 rows).
+int prefill_max_wide_items(int n, int E);
+// Workgroups of the routing launches for n slots and E experts.
+int prefill_route_blocks(int n, int E);
 hipError_t launch_prefill(const StageArgs& a, const uint16_t* x, const float* topk_w, uint16_t* out,
                           const PrefillWs& w, hipStream_t stream);
 // Address of this device's copy of the library's fixed decode scratch (the

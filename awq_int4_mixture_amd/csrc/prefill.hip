@@ -6,15 +6,16 @@
 // With many tokens an expert serves several rows, so the work is expert-major
 // and the products run on the matrix cores:
 //
-//  * route: one workgroup counts the slots per expert, lays the experts'
-//    rows out in ascending expert order and cuts each expert's rows into
-//    work items of at most 32 rows (two 16-row MFMA tiles);
-//  * W13 + SwiGLU: one workgroup per (work item, 16-column tile); each
-//    group of 32 K values is one v_mfma_f32_16x16x32_f16 whose B operand is
-//    the exact integer (q - z) in fp16 (|q - z| <= 255), so the dequantised
-//    weight is never rounded; the group's fp32 result is scaled by s and
-//    accumulated in fp32;
-//  * W2: the same per (work item, 8 column tiles), writing fp32 row results;
+//  * route (two launches over slices of the slots): counts per expert, the
+//    experts' rows laid out in ascending expert order, each expert's rows
+//    cut into work items of at most 32 rows and wide items of at most 64;
+//  * below 256 tokens, W13 + SwiGLU per (work item, 16-column tile) and W2
+//    per (work item, 8 column tiles); from 256 tokens the wide kernels, per
+//    (wide item, 20 column tiles), for both products. Each group of 32 K
+//    values is one v_mfma_f32_16x16x32_f16 whose B operand is the exact
+//    integer (q - z) in fp16 (|q - z| <= 255), so the dequantised weight is
+//    never rounded; the group's fp32 result is scaled by s and accumulated
+//    in fp32. W2 writes fp32 row results;
 //  * reduce: per token, the router-weighted fp32 sum of its rows in
 //    ascending (expert id, slot) order, rounded once to fp16, as the decode
 //    stage does.
@@ -26,118 +27,186 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "device_util.h"
 #include "kernels.h"
 
 namespace awq_moe {
 
 typedef float f4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 
 constexpr int kItemRows = 32;
-constexpr int kRouteBatch = 16;  // slot ids per thread in flight in the routing kernel
+constexpr int kWideRows = 64;  // rows of a wide work item (the many-rows W13 kernel), a multiple of 16
+constexpr int kRouteBatch = 16;           // slot ids per thread in flight in the routing kernels
+constexpr int kRouteSlotsPerBlock = 2048;  // slots per routing workgroup (when E allows)
+constexpr int kRouteCountCap = 65536;      // workgroups x experts of the per-workgroup counts
 
 // ---------------------------------------------------------------------------
-// routing: counts, row offsets per expert, work items, row of every slot.
-// Thread t owns experts [4t, 4t + 4) in the scans (E <= 4096).
+// routing, in two launches over B workgroups that each own a contiguous
+// slice of the slots (B from prefill_route_blocks):
+//  * count: the slice's slots per expert (LDS atomics), written to
+//    cnt[b][E], and whether the slice holds an id outside [0, E);
+//  * place: every workgroup sums cnt over the workgroups for each expert
+//    (the total, and the part of the workgroups before it), scans the totals
+//    over experts (rows, 32-row items, wide items; thread t owns experts
+//    [4t, 4t + 4), E <= 4096), and gives each of its slots the next row of its
+//    expert's range after the rows of the lower experts and of the earlier
+//    workgroups (LDS atomics: the order inside a workgroup's share of an
+//    expert is unspecified). Workgroup 0 writes the items, their numbers and
+//    the status word.
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(1024) void prefill_route_kernel(const int32_t* __restrict__ ids, int n, int E,
+int prefill_route_blocks(int n, int E) {
+  int b = (n + kRouteSlotsPerBlock - 1) / kRouteSlotsPerBlock;
+  b = min(b, kRouteCountCap / E);
+  return max(b, 1);
+}
+
+// The slots [s0, s1) of this workgroup, kRouteBatch per thread in flight:
+// f(slot, id) for each.
+template <class F>
+__device__ __forceinline__ void for_slots(const int32_t* __restrict__ ids, int s0, int s1, F&& f) {
+  for (int sb = s0 + (int)threadIdx.x; sb < s1; sb += kRouteBatch * 1024) {
+    int ev[kRouteBatch];
+#pragma unroll
+    for (int b = 0; b < kRouteBatch; ++b) {
+      const int s = sb + 1024 * b;
+      ev[b] = s < s1 ? ids[s] : 0;
+    }
+#pragma unroll
+    for (int b = 0; b < kRouteBatch; ++b) {
+      const int s = sb + 1024 * b;
+      if (s >= s1) break;
+      f(s, ev[b]);
+    }
+  }
+}
+
+__global__ __launch_bounds__(1024) void prefill_count_kernel(const int32_t* __restrict__ ids, int n, int E, int per,
+                                                             int32_t* __restrict__ cnt, int32_t* __restrict__ bad) {
+  __shared__ int c[AWQ_MOE_KMAX_ROUTER_E];
+  __shared__ int any_bad;
+  const int t = threadIdx.x, b = blockIdx.x;
+  for (int e = t; e < E; e += 1024) c[e] = 0;
+  if (t == 0) any_bad = 0;
+  __syncthreads();
+  const int s0 = b * per, s1 = min(n, s0 + per);
+  for_slots(ids, s0, s1, [&](int, int e) {
+    if (e >= 0 && e < E)
+      atomicAdd(&c[e], 1);
+    else
+      any_bad = 1;
+  });
+  __syncthreads();
+  for (int e = t; e < E; e += 1024) cnt[(uint64_t)b * E + e] = c[e];
+  if (t == 0) bad[b] = any_bad;
+}
+
+__global__ __launch_bounds__(1024) void prefill_place_kernel(const int32_t* __restrict__ ids, int n, int E, int per,
+                                                             int nb, const int32_t* __restrict__ cnt,
+                                                             const int32_t* __restrict__ bad,
                                                              int32_t* __restrict__ slot_row,
                                                              int32_t* __restrict__ row_slot,
                                                              int32_t* __restrict__ items,
                                                              int32_t* __restrict__ num_items,
+                                                             int32_t* __restrict__ witems,
+                                                             int32_t* __restrict__ num_witems,
                                                              uint32_t* __restrict__ status) {
-  __shared__ int cnt[AWQ_MOE_KMAX_ROUTER_E];
+  __shared__ int tot[AWQ_MOE_KMAX_ROUTER_E];
   __shared__ int cur[AWQ_MOE_KMAX_ROUTER_E];
-  __shared__ int wsum[16][2];
-  __shared__ int bad;
-  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
-  for (int e = t; e < E; e += 1024) cnt[e] = 0;
-  if (t == 0) bad = 0;
-  __syncthreads();
-  // The slots are read kRouteBatch per thread at a time, every load issued
-  // before the first is used: one memory round trip per batch, not per slot.
-  for (int s0 = t; s0 < n; s0 += kRouteBatch * 1024) {
-    int ev[kRouteBatch];
+  __shared__ int wsum[16][3];
+  const int t = threadIdx.x, lane = t & 63, wave = t >> 6, b = blockIdx.x;
+  // totals per expert and the share of the workgroups before this one
+  for (int e = t; e < E; e += 1024) {
+    int all = 0, before = 0;
+    for (int w0 = 0; w0 < nb; w0 += 8) {
+      int v[8];
 #pragma unroll
-    for (int b = 0; b < kRouteBatch; ++b) {
-      const int s = s0 + 1024 * b;
-      ev[b] = s < n ? ids[s] : 0;
-    }
+      for (int u = 0; u < 8; ++u) v[u] = w0 + u < nb ? cnt[(uint64_t)(w0 + u) * E + e] : 0;  // 8 requests in flight
 #pragma unroll
-    for (int b = 0; b < kRouteBatch; ++b) {
-      if (s0 + 1024 * b >= n) break;
-      const int e = ev[b];
-      if (e >= 0 && e < E)
-        atomicAdd(&cnt[e], 1);
-      else
-        bad = 1;
+      for (int u = 0; u < 8; ++u) {
+        all += v[u];
+        before += w0 + u < b ? v[u] : 0;
+      }
     }
+    tot[e] = all;
+    cur[e] = before;
   }
   __syncthreads();
-  int c4[4], r4[4], i4[4], rs = 0, is = 0;
+  int c4[4], r4[4], i4[4], w4[4], rs = 0, is = 0, ws = 0;
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
     const int e = 4 * t + q;
-    c4[q] = e < E ? cnt[e] : 0;
+    c4[q] = e < E ? tot[e] : 0;
     r4[q] = rs;
     i4[q] = is;
+    w4[q] = ws;
     rs += c4[q];
     is += (c4[q] + kItemRows - 1) / kItemRows;
+    ws += (c4[q] + kWideRows - 1) / kWideRows;
   }
-  int ri = rs, ii = is;
+  int ri = rs, ii = is, wi = ws;
 #pragma unroll
   for (int off = 1; off < 64; off <<= 1) {
-    const int a = __shfl_up(ri, off), b = __shfl_up(ii, off);
+    const int a = __shfl_up(ri, off), bb = __shfl_up(ii, off), d = __shfl_up(wi, off);
     if (lane >= off) {
       ri += a;
-      ii += b;
+      ii += bb;
+      wi += d;
     }
   }
   if (lane == 63) {
     wsum[wave][0] = ri;
     wsum[wave][1] = ii;
+    wsum[wave][2] = wi;
   }
   __syncthreads();
-  int rb = ri - rs, ib = ii - is;  // exclusive bases of this thread
+  int rb = ri - rs, ib = ii - is, wb = wi - ws;  // exclusive bases of this thread
   for (int w = 0; w < wave; ++w) {
     rb += wsum[w][0];
     ib += wsum[w][1];
+    wb += wsum[w][2];
   }
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
     const int e = 4 * t + q;
     if (e >= E) break;
-    const int row0 = rb + r4[q], it0 = ib + i4[q];
-    cur[e] = row0;
+    const int row0 = rb + r4[q], it0 = ib + i4[q], wt0 = wb + w4[q];
+    cur[e] += row0;  // this workgroup's first row of expert e
+    if (b != 0) continue;
     for (int p = 0; p * kItemRows < c4[q]; ++p) {
       items[2 * (it0 + p)] = e;
       items[2 * (it0 + p) + 1] = (row0 + kItemRows * p) | (min(kItemRows, c4[q] - kItemRows * p) << 24);
     }
+    // wide items: ceil(c / 64) of them, the rows shared out in multiples of 16
+    const int nw = (c4[q] + kWideRows - 1) / kWideRows;
+    const int pw = nw ? ((c4[q] + nw - 1) / nw + 15) / 16 * 16 : 0;
+    for (int p = 0; p < nw; ++p) {
+      witems[2 * (wt0 + p)] = e;
+      witems[2 * (wt0 + p) + 1] = (row0 + pw * p) | (min(pw, c4[q] - pw * p) << 24);
+    }
   }
-  if (t == 1023) *num_items = ib + is;
-  if (t == 0) *status = bad ? AWQ_MOE_STATUS_BAD_ID_BIT : 0u;
+  if (b == 0 && t == 1023) {
+    *num_items = ib + is;
+    *num_witems = wb + ws;
+  }
+  if (b == 0 && t == 0) {
+    int any = 0;
+    for (int w = 0; w < nb; ++w) any |= bad[w];
+    *status = any ? AWQ_MOE_STATUS_BAD_ID_BIT : 0u;
+  }
   __syncthreads();
-  for (int s0 = t; s0 < n; s0 += kRouteBatch * 1024) {
-    int ev[kRouteBatch];
-#pragma unroll
-    for (int b = 0; b < kRouteBatch; ++b) {
-      const int s = s0 + 1024 * b;
-      ev[b] = s < n ? ids[s] : 0;
+  const int s0 = b * per, s1 = min(n, s0 + per);
+  for_slots(ids, s0, s1, [&](int s, int e) {
+    if (e >= 0 && e < E) {
+      const int r = atomicAdd(&cur[e], 1);
+      slot_row[s] = r;
+      row_slot[r] = s;
+    } else {
+      slot_row[s] = -1;
     }
-#pragma unroll
-    for (int b = 0; b < kRouteBatch; ++b) {
-      const int s = s0 + 1024 * b;
-      if (s >= n) break;
-      const int e = ev[b];
-      if (e >= 0 && e < E) {
-        const int r = atomicAdd(&cur[e], 1);
-        slot_row[s] = r;
-        row_slot[r] = s;
-      } else {
-        slot_row[s] = -1;
-      }
-    }
-  }
+  });
 }
 
 // ---------------------------------------------------------------------------
@@ -431,132 +500,331 @@ __global__ __launch_bounds__(256) void prefill_w13_kernel(const int32_t* __restr
   }
 }
 
-// ---------------------------------------------------------------------------
-// W13 + SwiGLU for calls with many rows per expert: grid (ceil(NT/4) groups
-// of 4 column tiles, work items), 4 waves; wave w owns tile 4 q + w over
-// all of K, so an activation row staged once serves four tiles. Per chunk
-// of kMtChunk groups everything goes straight into LDS with LDS-direct
-// loads: the item's activations as [group][k block][row][16 B] (a load of
-// 64 lanes is 2 k blocks x 32 rows of one group, and an MFMA operand read
-// is 1 KB contiguous), the four tiles' weight runs at a stride of
-// kMtRun units (16 or 48 mod 64 dwords, so operand reads hit 64 banks; pad
-// units, if any, are lanes that load nothing), the records through
-// registers as dwords. Chunks of 8 groups keep the LDS at 27 KB, so five
-// workgroups fit on a CU (10 groups, 34 KB: four).
-// Each wave keeps its tile's sums in registers to the end (no cross-wave
-// reduction), then applies SwiGLU.
-// ---------------------------------------------------------------------------
-constexpr int kMtChunk = 8;
-// Calls from this many tokens take the multi-tile W13 kernel. Single-tile
-// against multi-tile, us per call: M = 32: 62.2 / 63.6, M = 64: 88.1 / 91.4,
-// M = 128: 113.8 / 112.9 (even); from M = 256 the multi-tile kernel is ahead.
-constexpr int kMtMinTokens = 256;
-constexpr int kMtRun = 36;  // units per weight run in LDS (4 * kMtChunk = 32 used)
-constexpr int kMtAUnits = kMtChunk * 4 * 32;       // 16-byte activation units per chunk
-constexpr int kMtBUnits = 16 * kMtRun;             // 4 tiles x 4 runs
-constexpr int kMtBLoads = (kMtBUnits + 63) / 64;
-constexpr int kMtRecDw = 16 * kMtChunk;            // record dwords per tile and chunk
-static_assert(((4 * kMtRun) % 64 == 16 || (4 * kMtRun) % 64 == 48) && kMtRun >= 4 * kMtChunk,
-              "weight runs: 64 banks, room for a chunk");
-static_assert(4 * 4 * kMtChunk <= 256, "record quads: one per thread");
+// Calls from this many tokens take the wide kernels (items of up to 64 rows,
+// 20 column tiles per workgroup); below, the per-tile kernels above.
+constexpr int kWideMinTokens = 256;
 
-template <int RB>
-__global__ __launch_bounds__(256) void prefill_w13_mt_kernel(const int32_t* __restrict__ items,
-                                                             const int32_t* __restrict__ num_items,
-                                                             const int32_t* __restrict__ row_slot,
-                                                             const uint8_t* __restrict__ bank,
-                                                             const uint16_t* __restrict__ x, uint64_t expert_bytes,
-                                                             uint64_t units_off, uint64_t meta_off, int H, int I,
-                                                             int topk, uint16_t* __restrict__ act, int run_log2) {
-  __shared__ __attribute__((aligned(16))) uint32_t al[kMtAUnits * 4];
-  __shared__ __attribute__((aligned(16))) uint32_t bl[kMtBUnits * 4];
-  __shared__ __attribute__((aligned(16))) uint32_t rl[4 * kMtRecDw];
-  int it, tq;
-  xcd_item_tile(run_log2, it, tq);
-  if (it >= *num_items) return;
-  int e, row0, rows;
-  item_of(items, it, e, row0, rows);
-  const int G = H >> 5, NT = (2 * I) >> 4;
-  const uint32_t m1024 = magic1024();
+// ---------------------------------------------------------------------------
+// Both products for calls with many rows per expert ("wide" kernels): work
+// items of up to 64 rows of one expert (wide items), grid (ceil(NT / (4 CT))
+// blocks of 4 CT column tiles, wide items), 4 waves. Wave w owns the CT
+// consecutive tiles CT w .. CT w + CT - 1 of its block over all of K and all
+// RT 16-row tiles of the item, so one (q - z) operand feeds RT matrix-core
+// products and the item's rows, staged in LDS, serve all 4 CT tiles.
+//   W13: A = the item's token rows of x (gathered), K = hidden, N = 2 inter,
+//        SwiGLU into act (fp16, by row), chunks of 4 groups, CT = 5;
+//   W2:  A = the item's rows of act, K = inter, N = hidden, fp32 row
+//        results y (by row), chunks of 5 groups (all of K at inter 160),
+//        CT = 5.
+//
+// Data flow per chunk of CG groups: the item's A units (16 bytes each,
+// [group][k block][row] in LDS so that an operand read is 1 KB contiguous;
+// the row is XOR-swizzled inside its 16-row tile with (4 group + k block) so
+// that the staging writes spread over the banks) and the block's records are
+// requested one chunk ahead into registers and written to LDS at the chunk
+// boundary, the records decoded once there into {fp32 scale (zero for a
+// group past K), the two packed fp16 offsets the operand subtracts}. The
+// weights take one of two ways (wx_ring):
+//   * LDS (W2): the block's weights of the chunk go the same way as A, 16
+//     bytes per lane, so a load covers contiguous runs of 64 CG bytes; each
+//     lane then reads its operand dword (dword kb of column c's unit) from
+//     LDS;
+//   * register ring (W13): each lane requests its operand dwords of its
+//     wave's tiles straight into registers CG groups ahead of their use.
+// Loads are unconditional, their addresses clamped into K, into the block's
+// tiles and into the item's rows; a group past K meets a zero scale.
+// Addresses are a uniform base (scalar registers) plus a 32-bit lane offset,
+// so the loads take the scalar-base form.
+// ---------------------------------------------------------------------------
+constexpr int kWxRows = 64;                 // A rows of an LDS chunk (room for 4 row tiles)
+constexpr int kWxRT = kWideRows / 16;       // 16-row tiles of the largest wide item
+constexpr int kWxCT13 = 5, kWxCT2 = 5;      // column tiles per wave of the two stages
+constexpr int kWxCG13 = 4, kWxCG2 = 5;      // groups per chunk of the two stages
+// LDS dwords of a stage's A chunk, decoded records of a chunk and weights of a chunk
+constexpr int wx_a_dw(int cg) { return cg * 4 * kWxRows * 4; }
+constexpr int wx_r_dw(int ct, int cg) { return 4 * ct * cg * 16 * 2; }
+// weight runs in LDS: a run of a chunk is 16 CG dwords, padded to a stride of
+// 16 or 48 (mod 64) dwords so that the 64 lanes of an operand read (column
+// c = 4 quad + j, dword kb) hit 64 different banks
+constexpr int wx_run_stride(int cg) { return 16 * cg + ((16 - 16 * cg) % 64 + 64) % 64; }
+constexpr int wx_b_dw(int ct, int cg) { return 4 * ct * 4 * wx_run_stride(cg); }
+static_assert(kWideRows % 16 == 0 && kWxRT >= 1 && kWxRT <= 4, "wide items of 1 to 4 row tiles");
+enum WideStage { kWideW13 = 0, kWideW2 = 1 };
+// Where a stage's weights go: W13 keeps a register ring per wave (each lane's
+// operand dwords requested CG groups ahead; measured faster than LDS staging
+// at 4096 tokens, equal at 1024), W2 stages them in LDS (its K is short, so
+// the whole chunk is requested at once in contiguous runs; measured faster).
+constexpr bool wx_ring(int stage) { return stage == 0; }
+
+// f(std::integral_constant<int, i>) for i = 0 .. N - 1, each a separate
+// instantiation, so that indices derived from i are compile-time constants.
+template <int N, int I = 0, class F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (I < N) {
+    f(std::integral_constant<int, I>{});
+    static_for<N, I + 1>(f);
+  }
+}
+
+// Keeps the memory requests above where they are: neither the IR passes
+// (the empty asm is a compiler memory barrier) nor the machine scheduler
+// (sched_barrier) move them past this point towards their first use. The
+// pointers of the kernels that rely on it carry no __restrict__: a load
+// through a no-alias pointer may legally cross the compiler barrier.
+__device__ __forceinline__ void issue_here() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+__device__ __forceinline__ uint32_t magic64() {
+  uint32_t m;
+  asm volatile("v_mov_b32 %0, 0x54005400" : "=v"(m));
+  return m;
+}
+
+// Eight (q - z) values in fp16 from one dword of a unit (value p at bits
+// 4*(p/2) + 16*(p%2)). The nibbles at bits 0..3 of a half OR-ed into the
+// mantissa of 1024.0 give 1024 + q; those at bits 4..7 OR-ed into the
+// mantissa of 64.0 (whose last mantissa bit is worth 1/16) give 64 + q, so
+// two of the four pairs need no shift. czz holds -(1024 + z) in its low half
+// and -(64 + z) in its high half; every sum is an exact integer.
+__device__ __forceinline__ h8_t qz_operand64(uint32_t w, uint32_t czz, uint32_t m1024, uint32_t m64) {
+  const h2_t c = as_h2(czz);
+  const h2_t c1024 = __builtin_shufflevector(c, c, 0, 0), c64 = __builtin_shufflevector(c, c, 1, 1);
+  const uint32_t w8 = w >> 8;
+  const h2_t p0 = as_h2((w & 0x000F000Fu) | m1024) + c1024;
+  const h2_t p1 = as_h2((w & 0x00F000F0u) | m64) + c64;
+  const h2_t p2 = as_h2((w8 & 0x000F000Fu) | m1024) + c1024;
+  const h2_t p3 = as_h2((w8 & 0x00F000F0u) | m64) + c64;
+  return __builtin_bit_cast(h8_t, make_uint4(__builtin_bit_cast(uint32_t, p0), __builtin_bit_cast(uint32_t, p1),
+                                             __builtin_bit_cast(uint32_t, p2), __builtin_bit_cast(uint32_t, p3)));
+}
+
+// A decoded record: {the scale in fp32 (0 when not live), czz as above}.
+__device__ __forceinline__ uint2 decode_record(uint32_t r, bool live) {
+  const float s = (float)__builtin_bit_cast(_Float16, (uint16_t)(r & 0xFFFFu));
+  const uint32_t z = (r >> 16) & 0xFFu;
+  const _Float16 m64z = (_Float16)(-64.0f - (float)z);  // exact: 64 + z <= 319
+  return make_uint2(live ? __builtin_bit_cast(uint32_t, s) : 0u,
+                    (0xE400u + z) | ((uint32_t)__builtin_bit_cast(uint16_t, m64z) << 16));
+}
+
+// One wide item of one column block. K = 32 G; the A rows are K fp16 long.
+template <int RB, int RT, int CG, int CT, int STAGE>
+__device__ __forceinline__ void wide_item(const uint8_t* units, const uint8_t* recs, const uint16_t* a_src,
+                                          const int32_t* row_slot, int row0, int rows, int topk, int G, int NT,
+                                          int nb0, void* out, int out_stride, uint32_t* al, uint32_t* rl,
+                                          uint32_t* bl) {
+  typedef uint32_t u32x3 __attribute__((ext_vector_type(3), aligned(4)));
+  constexpr int kNU = (RT * CG + 3) / 4;           // A units per thread and chunk
+  constexpr int kUnits = 16 * RT * CG * 4;         // A units of a chunk
+  constexpr int kWxTiles = 4 * CT;                 // column tiles of the block
+  constexpr int kQuads = kWxTiles * CG * 4;        // record quads of a chunk
+  constexpr int kNQ = (kQuads + 255) / 256;        // record quads per thread and chunk
   const int t = threadIdx.x, lane = t & 63, wave = __builtin_amdgcn_readfirstlane(t >> 6);
   const int c = lane & 15, kb = lane >> 4, quad = c >> 2, j = c & 3;
-  const int nt0 = 4 * tq, T = min(4, NT - nt0);
-  const uint8_t* blk = bank + (uint64_t)e * expert_bytes;
-  const uint8_t* units = blk + units_off + (uint64_t)nt0 * 256 * G;
-  const uint8_t* recs = blk + meta_off + (uint64_t)nt0 * 16 * G * RB;
-  const int nrt = rows > 16 ? 2 : 1;
-  // the activation row this lane copies (row = lane & 31; rows past the item repeat its last row)
-  const int arow = lane & 31;
-  const uint16_t* xrow = x + (uint64_t)(row_slot[row0 + min(arow, rows - 1)] / topk) * H + 8 * (lane >> 5);
-  f4_t acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
-  for (int g0 = 0; g0 < G; g0 += kMtChunk) {
-    const int kc = min(kMtChunk, G - g0);
-    if (g0 > 0) __syncthreads();  // the previous chunk's LDS reads are done
-    // activations: load m = 2 gl + h covers k blocks 2h, 2h + 1 of group gl for rows 0..31
-    for (int m = wave; m < 2 * kc; m += 4) {
-      const int gl = m >> 1, h = m & 1;
-      if (arow < 16 * nrt)
-        lds_direct16(reinterpret_cast<const uint8_t*>(xrow + 32 * (g0 + gl) + 16 * h), al + 256 * m);
-    }
-    // weights: unit position p = (tile * 4 + j) * kMtRun + u
+  const uint32_t m1024 = magic1024(), m64 = magic64();
+  const int Tb = min(kWxTiles, NT - nb0);  // tiles of this block
+  // A units of this thread: u = t + 256 i is k block u & 3 of group
+  // (u >> 2) % CG of row (u >> 2) / CG
+  const uint8_t* ab = reinterpret_cast<const uint8_t*>(a_src);
+  uint32_t ao[kNU];  // byte offset of the unit's k block in its row
+  int agl[kNU], adst[kNU];
 #pragma unroll
-    for (int i = wave; i < kMtBLoads; i += 4) {
-      const int pos = 64 * i + lane;
-      const int tj = pos / kMtRun, u = pos - tj * kMtRun;
-      const int tt = tj >> 2, jr = tj & 3;
-      if (tt < T && u < 4 * kc)
-        lds_direct16(units + (uint64_t)tt * 256 * G + (uint64_t)jr * 64 * G + 64 * g0 + 16 * u, bl + 256 * i);
+  for (int i = 0; i < kNU; ++i) {
+    const int u = t + 256 * i, gl = (u >> 2) % CG, row = (u >> 2) / CG, akb = u & 3;
+    const int r = row0 + min(row, rows - 1);
+    const uint32_t arow = STAGE == kWideW13 ? (uint32_t)(row_slot[r] / topk) : (uint32_t)r;
+    ao[i] = arow * (uint32_t)G * 64u + 16u * akb;
+    agl[i] = gl;
+    const int h = (4 * gl + akb) & 15;
+    adst[i] = u < kUnits ? ((gl * 4 + akb) * kWxRows + (row & ~15) + ((row & 15) ^ h)) * 4 : -1;
+  }
+  // record quads of this thread: u = t + 256 q is records 4 (u & 3) .. + 3 of
+  // group (u >> 2) % CG of the chunk, tile u / (4 CG) of the block
+  uint32_t ro[kNQ];
+  int rgl[kNQ], rdst[kNQ];
+#pragma unroll
+  for (int q = 0; q < kNQ; ++q) {
+    const int u = min(t + 256 * q, kQuads - 1);
+    ro[q] = (uint32_t)min(u / (4 * CG), Tb - 1) * 16u * G * RB + 4u * (u & 3) * RB;
+    rgl[q] = (u >> 2) % CG;
+    rdst[q] = t + 256 * q < kQuads ? 8 * u : -1;  // dword offset of its 4 decoded records
+  }
+  // weight units of this thread: u = t + 256 i is unit u % (4 CG) (group
+  // (u % (4 CG)) / 4, quad u % 4) of run (u / (4 CG)) % 4 of tile u / (16 CG)
+  constexpr bool RING = wx_ring(STAGE);
+  constexpr int kRS = wx_run_stride(CG);
+  constexpr int kBU = RING ? 0 : kWxTiles * 4 * 4 * CG;  // weight units of a chunk staged in LDS
+  constexpr int kNB = kBU ? (kBU + 255) / 256 : 1;       // weight units per thread and chunk (1 unused with RING)
+  uint32_t bo[kNB];
+  int bgl[kNB], bdst[kNB];
+#pragma unroll
+  for (int i = 0; i < kNB; ++i) {
+    const int u = min(t + 256 * i, kBU - 1), ur = u % (4 * CG), run = u / (4 * CG);
+    const int tt = run >> 2, jr = run & 3;
+    bo[i] = (uint32_t)min(tt, Tb - 1) * 256u * G + (uint32_t)jr * 64u * G + 16u * (ur & 3);
+    bgl[i] = ur >> 2;
+    bdst[i] = t + 256 * i < kBU ? run * kRS + 4 * ur : -1;
+  }
+  // plain loads: an expert's second item finds its weights in the caches
+  // (non-temporal loads measured slower here, while they speed up the
+  // reduce's read-once rows)
+  auto ld_b = [&](int i, int g0) {
+    return *reinterpret_cast<const u32x4_t*>(units + 64 * min(g0 + bgl[i], G - 1) + bo[i]);
+  };
+  // the register ring (RING): this lane's operand dword of tile CT wave + ct
+  // (clamped into the block), group g
+  const uint32_t bor = (uint32_t)j * 64u * G + 16u * quad + 4u * kb;
+  const uint8_t* tbase[CT];
+#pragma unroll
+  for (int ct = 0; ct < CT; ++ct) tbase[ct] = units + (uint64_t)min(CT * wave + ct, Tb - 1) * 256 * G;
+  auto ld_r = [&](int ct, int g) { return *reinterpret_cast<const uint32_t*>(tbase[ct] + 64 * min(g, G - 1) + bor); };
+  auto ld_a = [&](int i, int g0) { return *reinterpret_cast<const u32x4_t*>(ab + 64 * min(g0 + agl[i], G - 1) + ao[i]); };
+  auto rsrc = [&](int q, int g0) { return recs + 16 * RB * min(g0 + rgl[q], G - 1) + ro[q]; };
+  u32x4_t av[kNU], bv[kNB];
+  u32x3 rv[kNQ];
+  uint32_t rw[kNQ];  // the fourth record of a 4-byte quad
+  auto load_chunk = [&](int g0) {
+#pragma unroll
+    for (int i = 0; i < kNB; ++i)
+      if constexpr (!RING) bv[i] = ld_b(i, g0);
+#pragma unroll
+    for (int i = 0; i < kNU; ++i) av[i] = ld_a(i, g0);
+#pragma unroll
+    for (int q = 0; q < kNQ; ++q) {
+      const uint8_t* src = rsrc(q, g0);
+      rv[q] = *reinterpret_cast<const u32x3*>(src);
+      if constexpr (RB == 4) rw[q] = *reinterpret_cast<const uint32_t*>(src + 12);
     }
-    // records: quad r of tile tt (4 records of group r / 4), as dwords
-    {
-      const int tt = t / (4 * kMtChunk), rem = t - tt * (4 * kMtChunk);
-      const bool on = tt < T && rem < 4 * kc;
-      typedef uint32_t u32x3 __attribute__((ext_vector_type(3), aligned(4)));
-      const uint8_t* rp = recs + (on ? (uint64_t)tt * 16 * G * RB + (16 * g0 + 4 * rem) * RB : 0);
-      const u32x3 d = *reinterpret_cast<const u32x3*>(rp);
-      uint4 v;
+  };
+  load_chunk(0);
+  uint32_t bq[RING ? CG : 1][CT];
+  if constexpr (RING) {
+    // chunk requests before ring requests, in the same order as in the loop,
+    // so that the first chunk's wait leaves the ring in flight
+    issue_here();
+#pragma unroll
+    for (int g = 0; g < CG; ++g) {
+#pragma unroll
+      for (int ct = 0; ct < CT; ++ct) bq[g][ct] = ld_r(ct, g);
+      issue_here();
+    }
+  }
+  f4_t acc[CT][RT];
+#pragma unroll
+  for (int ct = 0; ct < CT; ++ct)
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt) acc[ct][rt] = f4_t{0.f, 0.f, 0.f, 0.f};
+  for (int g0 = 0; g0 < G; g0 += CG) {
+    if (g0 > 0) __syncthreads();  // every wave is done with the previous chunk's LDS
+#pragma unroll
+    for (int i = 0; i < kNB; ++i)
+      if (!RING && bdst[i] >= 0) *reinterpret_cast<u32x4_t*>(bl + bdst[i]) = bv[i];
+#pragma unroll
+    for (int i = 0; i < kNU; ++i)
+      if (adst[i] >= 0) *reinterpret_cast<u32x4_t*>(al + adst[i]) = av[i];
+#pragma unroll
+    for (int q = 0; q < kNQ; ++q) {
+      if (rdst[q] < 0) continue;
+      const u32x3 d = rv[q];
+      uint32_t r4[4];
       if constexpr (RB == 4) {
-        v = make_uint4(d.x, d.y, d.z, *reinterpret_cast<const uint32_t*>(rp + 12));
+        r4[0] = d.x, r4[1] = d.y, r4[2] = d.z, r4[3] = rw[q];
       } else {
-        v = make_uint4(d.x & 0xFFFFFFu, (d.x >> 24) | ((d.y & 0xFFFFu) << 8), (d.y >> 16) | ((d.z & 0xFFu) << 16),
-                       d.z >> 8);
+        r4[0] = d.x, r4[1] = (d.x >> 24) | (d.y << 8), r4[2] = (d.y >> 16) | (d.z << 16), r4[3] = d.z >> 8;
       }
-      if (on) *reinterpret_cast<uint4*>(rl + tt * kMtRecDw + 4 * rem) = v;
+      const bool live = g0 + rgl[q] < G;
+      const uint2 d0 = decode_record(r4[0], live), d1 = decode_record(r4[1], live);
+      const uint2 d2 = decode_record(r4[2], live), d3 = decode_record(r4[3], live);
+      const u32x4_t lo = {d0.x, d0.y, d1.x, d1.y}, hi = {d2.x, d2.y, d3.x, d3.y};
+      *reinterpret_cast<u32x4_t*>(rl + rdst[q]) = lo;
+      *reinterpret_cast<u32x4_t*>(rl + rdst[q] + 4) = hi;
     }
-    // the barrier waits for every load of the workgroup, the LDS-direct ones included
     __syncthreads();
-    if (wave < T) {
-      const uint32_t* bw = bl + wave * 4 * kMtRun * 4;
-      const uint32_t* rw = rl + wave * kMtRecDw;
-      for (int gl = 0; gl < kc; ++gl) {
-        const uint32_t w = bw[(j * kMtRun + 4 * gl + quad) * 4 + kb];
-        const uint32_t r = rw[16 * gl + 4 * quad + j];
-        const float sc = (float)__builtin_bit_cast(_Float16, (uint16_t)(r & 0xFFFFu));
-        const h8_t b = qz_operand(w, (r >> 16) & 0xFFu, m1024);
-        const h8_t a0 = *reinterpret_cast<const h8_t*>(al + ((gl * 4 + kb) * 32 + c) * 4);
-        scale_add(acc0, sc, mfma16(a0, b));
-        if (nrt == 2) {
-          const h8_t a1 = *reinterpret_cast<const h8_t*>(al + ((gl * 4 + kb) * 32 + 16 + c) * 4);
-          scale_add(acc1, sc, mfma16(a1, b));
+    load_chunk(g0 + CG);  // the next chunk (clamped past K: loaded, never used)
+    issue_here();
+#pragma unroll
+    for (int gl = 0; gl < CG; ++gl) {
+      const int cs = c ^ ((4 * gl + kb) & 15);  // the swizzled row of lane c in its tile
+      h8_t a[RT];
+#pragma unroll
+      for (int rt = 0; rt < RT; ++rt)
+        a[rt] = *reinterpret_cast<const h8_t*>(al + ((gl * 4 + kb) * kWxRows + 16 * rt + cs) * 4);
+#pragma unroll
+      for (int ct = 0; ct < CT; ++ct) {
+        const int tb = min(CT * wave + ct, Tb - 1);
+        const uint2 sc = *reinterpret_cast<const uint2*>(rl + ((tb * CG + gl) * 16 + c) * 2);
+        const uint32_t wq = RING ? bq[RING ? gl : 0][ct] : bl[(tb * 4 + j) * kRS + (4 * gl + quad) * 4 + kb];
+        const h8_t b = qz_operand64(wq, sc.y, m1024, m64);
+        const float s = __builtin_bit_cast(float, sc.x);
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt) scale_add(acc[ct][rt], s, mfma16(a[rt], b));
+      }
+      if constexpr (RING) {
+#pragma unroll
+        for (int ct = 0; ct < CT; ++ct) bq[gl][ct] = ld_r(ct, g0 + gl + CG);
+        issue_here();  // the same for the weight ring
+      }
+    }
+  }
+#pragma unroll
+  for (int ct = 0; ct < CT; ++ct) {
+    const int tb = CT * wave + ct;
+    if (tb >= Tb) break;
+    const int nt = nb0 + tb;
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float d = acc[ct][rt][i];
+        const int row = 16 * rt + 4 * kb + i;
+        if constexpr (STAGE == kWideW13) {
+          const float up = dpp<kQuadSwap1>(d);  // column c ^ 1
+          if (!(c & 1) && row < rows) {
+            const float a = d / (1.0f + __expf(-d)) * up;
+            static_cast<uint16_t*>(out)[(uint64_t)(row0 + row) * out_stride + nt * 8 + (c >> 1)] =
+                __builtin_bit_cast(uint16_t, (_Float16)a);
+          }
+        } else {
+          if (row < rows) static_cast<float*>(out)[(uint64_t)(row0 + row) * out_stride + nt * 16 + c] = d;
         }
       }
     }
   }
-  if (wave >= T) return;
-  const int nt = nt0 + wave;
-  for (int rt = 0; rt < nrt; ++rt) {
-    const f4_t d = rt == 0 ? acc0 : acc1;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const float up = dpp<kQuadSwap1>(d[i]);  // column c ^ 1
-      const int row = 16 * rt + 4 * kb + i;
-      if (!(c & 1) && row < rows) {
-        const float g = d[i];
-        const float a = g / (1.0f + __expf(-g)) * up;
-        act[(uint64_t)(row0 + row) * I + nt * 8 + (c >> 1)] = __builtin_bit_cast(uint16_t, (_Float16)a);
-      }
-    }
-  }
+}
+
+// STAGE kWideW13: a = x, out = act (stride inter); kWideW2: a = act, out = y
+// (stride hidden).
+template <int RB, int STAGE>
+__global__ __launch_bounds__(256, 2) void prefill_wide_kernel(const int32_t* items, const int32_t* num_items,
+                                                              const int32_t* row_slot, const uint8_t* bank,
+                                                              const uint16_t* a, uint64_t expert_bytes,
+                                                              uint64_t units_off, uint64_t meta_off, int H, int I,
+                                                              int topk, void* out, int run_log2) {
+  constexpr int CG = STAGE == kWideW13 ? kWxCG13 : kWxCG2;
+  constexpr int CT = STAGE == kWideW13 ? kWxCT13 : kWxCT2;
+  __shared__ __attribute__((aligned(16))) uint32_t al[wx_a_dw(CG)];
+  __shared__ __attribute__((aligned(16))) uint32_t rl[wx_r_dw(CT, CG)];
+  __shared__ __attribute__((aligned(16))) uint32_t bl[wx_ring(STAGE) ? 4 : wx_b_dw(CT, CG)];
+  constexpr int kWxTiles = 4 * CT;
+  int it, bx;
+  xcd_item_tile(run_log2, it, bx);
+  if (it >= *num_items) return;
+  int e, row0, rows;
+  item_of(items, it, e, row0, rows);
+  const int G = (STAGE == kWideW13 ? H : I) >> 5, NT = (STAGE == kWideW13 ? 2 * I : H) >> 4;
+  const int nb0 = kWxTiles * bx, out_stride = STAGE == kWideW13 ? I : H;
+  const uint8_t* blk = bank + (uint64_t)e * expert_bytes;
+  const uint8_t* units = blk + units_off + (uint64_t)nb0 * 256 * G;
+  const uint8_t* recs = blk + meta_off + (uint64_t)nb0 * 16 * G * RB;
+  const int rt = (rows + 15) >> 4;  // 1 .. kWxRT
+  static_for<kWxRT>([&](auto i_c) {
+    constexpr int RT = decltype(i_c)::value + 1;
+    if (rt == RT)
+      wide_item<RB, RT, CG, CT, STAGE>(units, recs, a, row_slot, row0, rows, topk, G, NT, nb0, out, out_stride, al,
+                                       rl, bl);
+  });
 }
 
 // ---------------------------------------------------------------------------
@@ -673,8 +941,11 @@ __global__ __launch_bounds__(256) void prefill_w2_kernel(const int32_t* __restri
 // reduce: grid (ceil(H/512), M), one wave; lane l sums columns 8l .. 8l + 7 of
 // a 512-column block. The token's valid slots are ranked by (expert id,
 // slot) with lane reads, then summed in that order: acc = fma(w, y, acc)
-// from +0, rounded once to fp16.
+// from +0, rounded once to fp16. The rows are requested kRedBatch at a time
+// before any is summed (one memory round trip per batch).
 // ---------------------------------------------------------------------------
+constexpr int kRedBatch = 8;
+
 __global__ __launch_bounds__(64) void prefill_reduce_kernel(const int32_t* __restrict__ ids,
                                                             const float* __restrict__ topk_w,
                                                             const int32_t* __restrict__ slot_row,
@@ -698,19 +969,25 @@ __global__ __launch_bounds__(64) void prefill_reduce_kernel(const int32_t* __res
   const int col = blockIdx.x * 512 + 8 * lane;
   if (col >= H) return;
   float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-  for (int r = 0; r < nvalid; ++r) {
-    const float w = order_w[r];
-    const float* yr = y + (uint64_t)order_row[r] * H + col;
-    const float4 v0 = *reinterpret_cast<const float4*>(yr);
-    const float4 v1 = *reinterpret_cast<const float4*>(yr + 4);
-    acc[0] = fmaf(w, v0.x, acc[0]);
-    acc[1] = fmaf(w, v0.y, acc[1]);
-    acc[2] = fmaf(w, v0.z, acc[2]);
-    acc[3] = fmaf(w, v0.w, acc[3]);
-    acc[4] = fmaf(w, v1.x, acc[4]);
-    acc[5] = fmaf(w, v1.y, acc[5]);
-    acc[6] = fmaf(w, v1.z, acc[6]);
-    acc[7] = fmaf(w, v1.w, acc[7]);
+  for (int r0 = 0; r0 < nvalid; r0 += kRedBatch) {
+    f4_t v[kRedBatch][2];
+#pragma unroll
+    for (int b = 0; b < kRedBatch; ++b) {
+      // rows past the token's last are requested again from its first (never summed)
+      const float* yr = y + (uint64_t)order_row[r0 + b < nvalid ? r0 + b : 0] * H + col;
+      v[b][0] = __builtin_nontemporal_load(reinterpret_cast<const f4_t*>(yr));  // read once: streamed
+      v[b][1] = __builtin_nontemporal_load(reinterpret_cast<const f4_t*>(yr + 4));
+    }
+#pragma unroll
+    for (int b = 0; b < kRedBatch; ++b) {
+      if (r0 + b >= nvalid) break;
+      const float w = order_w[r0 + b];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        acc[i] = fmaf(w, v[b][0][i], acc[i]);
+        acc[4 + i] = fmaf(w, v[b][1][i], acc[4 + i]);
+      }
+    }
   }
   h8_t o;
 #pragma unroll
@@ -722,29 +999,40 @@ __global__ __launch_bounds__(64) void prefill_reduce_kernel(const int32_t* __res
 // launchers
 // ---------------------------------------------------------------------------
 int prefill_max_items(int n, int E) { return (n + kItemRows - 1) / kItemRows + (E < n ? E : n); }
+int prefill_max_wide_items(int n, int E) { return (n + kWideRows - 1) / kWideRows + (E < n ? E : n); }
 
 hipError_t launch_prefill(const StageArgs& a, const uint16_t* x, const float* topk_w, uint16_t* out,
                           const PrefillWs& w, hipStream_t stream) {
   const int n = a.M * a.topk;
   const int max_items = prefill_max_items(n, a.E);
-  hipLaunchKernelGGL(prefill_route_kernel, dim3(1), dim3(1024), 0, stream, a.topk_ids, n, a.E, w.slot_row,
-                     w.row_slot, w.items, w.num_items, w.status);
+  const int nb = prefill_route_blocks(n, a.E), per = (n + nb - 1) / nb;
+  hipLaunchKernelGGL(prefill_count_kernel, dim3(nb), dim3(1024), 0, stream, a.topk_ids, n, a.E, per, w.route_cnt,
+                     w.route_bad);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
+  hipLaunchKernelGGL(prefill_place_kernel, dim3(nb), dim3(1024), 0, stream, a.topk_ids, n, a.E, per, nb, w.route_cnt,
+                     w.route_bad, w.slot_row, w.row_slot, w.items, w.num_items, w.witems, w.num_witems, w.status);
+  if ((err = hipGetLastError()) != hipSuccess) return err;
   // runs of 8 items per XCD from 64 rows per expert on average (2 items or more each)
   const int run_log2 = n >= 64 * a.E ? 3 : 0;
   const int round = 8 << run_log2;
   const int items8 = (max_items + round - 1) / round * round;  // whole XCD rounds (see xcd_item_tile)
   const dim3 g13((2 * a.I) / 16, items8), g2(((a.H / 16) + 7) / 8, items8);
-  if (a.M >= kMtMinTokens) {
-    // many rows per expert: four tiles per workgroup share the staged activations
-    const dim3 g13m(((2 * a.I) / 16 + 3) / 4, items8);
+  const bool wide = a.M >= kWideMinTokens;
+  const int wrun_log2 = n >= 64 * a.E ? 1 : 0;
+  const int wround = 8 << wrun_log2;
+  const int witems8 = (prefill_max_wide_items(n, a.E) + wround - 1) / wround * wround;
+  if (wide) {
+    // many rows per expert: wide items, 20 column tiles per workgroup
+    const dim3 g13w(((2 * a.I) / 16 + 4 * kWxCT13 - 1) / (4 * kWxCT13), witems8);
     if (a.RB == 4)
-      hipLaunchKernelGGL(prefill_w13_mt_kernel<4>, g13m, dim3(256), 0, stream, w.items, w.num_items, w.row_slot, a.bank,
-                         x, a.expert_bytes, a.w13_off, a.w13_meta_off, a.H, a.I, a.topk, w.act, run_log2);
+      hipLaunchKernelGGL((prefill_wide_kernel<4, kWideW13>), g13w, dim3(256), 0, stream, w.witems, w.num_witems,
+                         w.row_slot, a.bank, x, a.expert_bytes, a.w13_off, a.w13_meta_off, a.H, a.I, a.topk,
+                         (void*)w.act, wrun_log2);
     else
-      hipLaunchKernelGGL(prefill_w13_mt_kernel<3>, g13m, dim3(256), 0, stream, w.items, w.num_items, w.row_slot, a.bank,
-                         x, a.expert_bytes, a.w13_off, a.w13_meta_off, a.H, a.I, a.topk, w.act, run_log2);
+      hipLaunchKernelGGL((prefill_wide_kernel<3, kWideW13>), g13w, dim3(256), 0, stream, w.witems, w.num_witems,
+                         w.row_slot, a.bank, x, a.expert_bytes, a.w13_off, a.w13_meta_off, a.H, a.I, a.topk,
+                         (void*)w.act, wrun_log2);
   } else if (a.RB == 4) {
     hipLaunchKernelGGL(prefill_w13_kernel<4>, g13, dim3(256), 0, stream, w.items, w.num_items, w.row_slot, a.bank, x,
                        a.expert_bytes, a.w13_off, a.w13_meta_off, a.H, a.I, a.topk, w.act, run_log2);
@@ -753,7 +1041,17 @@ hipError_t launch_prefill(const StageArgs& a, const uint16_t* x, const float* to
                        a.expert_bytes, a.w13_off, a.w13_meta_off, a.H, a.I, a.topk, w.act, run_log2);
   }
   if ((err = hipGetLastError()) != hipSuccess) return err;
-  if (a.RB == 4) {
+  if (wide) {
+    const dim3 g2w(((a.H / 16) + 4 * kWxCT2 - 1) / (4 * kWxCT2), witems8);
+    if (a.RB == 4)
+      hipLaunchKernelGGL((prefill_wide_kernel<4, kWideW2>), g2w, dim3(256), 0, stream, w.witems, w.num_witems,
+                         w.row_slot, a.bank, w.act, a.expert_bytes, a.w2_off, a.w2_meta_off, a.H, a.I, a.topk,
+                         (void*)w.y, wrun_log2);
+    else
+      hipLaunchKernelGGL((prefill_wide_kernel<3, kWideW2>), g2w, dim3(256), 0, stream, w.witems, w.num_witems,
+                         w.row_slot, a.bank, w.act, a.expert_bytes, a.w2_off, a.w2_meta_off, a.H, a.I, a.topk,
+                         (void*)w.y, wrun_log2);
+  } else if (a.RB == 4) {
     hipLaunchKernelGGL(prefill_w2_kernel<4>, g2, dim3(256), 0, stream, w.items, w.num_items, a.bank, a.expert_bytes,
                        a.w2_off, a.w2_meta_off, a.H, a.I, w.act, w.y, run_log2);
   } else {

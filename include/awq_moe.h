@@ -328,16 +328,23 @@ int awq_moe_router_gemv(const uint16_t* r, const uint16_t* delta, int32_t M, int
  *
  * Arguments as in awq_moe_decode, with num_experts <= 4096 and
  * workspace_bytes >= awq_moe_prefill_workspace_bytes(dims, M, topk).
- * Workspace layout, with n = M*topk, X = ceil(n/32) + min(E, n) and P(b) =
- * b rounded up to a multiple of 256, each part starting where the previous
- * one ends:
+ * Workspace layout, with n = M*topk, X = ceil(n/32) + min(E, n),
+ * W = ceil(n/64) + min(E, n) and P(b) = b rounded up to a multiple of 256,
+ * each part starting where the previous one ends:
  *   [0, 256)   status u32 at 0 (bit 0: an id outside [0, E); its slot
- *              contributes 0), number of work items i32 at 4;
+ *              contributes 0), number of work items i32 at 4, number of
+ *              wide work items i32 at 8;
  *   P(4n)      slot_row i32[n]: row of each slot, -1 for an invalid id;
  *   P(4n)      row_slot i32[n]: slot of each row (rows 0 .. valid slots - 1);
  *   P(8X)      work items i32[X][2]: {expert, first row | rows << 24}, rows
  *              <= 32, in ascending expert order, each expert's rows cut
  *              into chunks of 32 from its first row;
+ *   P(8W)      wide work items i32[W][2]: the same format, ceil(c/64)
+ *              items for an expert of c rows, each but the last of
+ *              16*ceil(ceil(c/items)/16) rows;
+ *   P(4BE), P(4B)  routing counts: with B = max(1, min(ceil(n/2048),
+ *              65536/E)) workgroups, each slice's slots per expert i32[B][E]
+ *              and a flag per slice (working state of the routing);
  *   P(2n*I)    fp16 act [n][inter] by row;  P(4n*H) fp32 y [n][hidden] by row.
  * The rows of expert e are the contiguous range after the rows of all
  * lower experts (ascending expert order, as route_compact's segments); the

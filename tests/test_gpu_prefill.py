@@ -49,6 +49,8 @@ def check(got, want, what):
     (40, 2560, 160, 10, 512, 3),   # four tiles per W13 workgroup at the rank shape: 8 chunks, ~128 rows per expert
     (8, 8192, 32, 2, 520, 3),      # four tiles per W13 workgroup, hidden 8192: 26 chunks, the last of 6 groups
     (4, 8192, 2048, 4, 9, 3),      # hidden 8192 with inter 2048 (the maxima together), single-tile W13
+    (6, 96, 64, 3, 300, 3),        # wide items with 3 groups: one chunk, shorter than the weight ring
+    (6, 96, 64, 3, 300, 4),        # the same with 4-byte records
 ])
 def test_prefill_shapes(E, H, I, k, M, rb):
     dims, bank, bi = bank_case(60 + I, E, H, I, rb)
@@ -234,13 +236,16 @@ def test_prefill_routing_arrays(E, k, M, hot):
     raw = ws.cpu().numpy()
     n = M * k
     X = (n + 31) // 32 + min(E, n)
+    W = (n + 63) // 64 + min(E, n)
     o_slot_row = 256
     o_row_slot = o_slot_row + _pad256(4 * n)
     o_items = o_row_slot + _pad256(4 * n)
-    status, n_items = raw[:8].view(np.int32)
+    o_witems = o_items + _pad256(8 * X)
+    status, n_items, n_witems = raw[:12].view(np.int32)
     slot_row = raw[o_slot_row:o_slot_row + 4 * n].view(np.int32)
     row_slot = raw[o_row_slot:o_row_slot + 4 * n].view(np.int32)
     items = raw[o_items:o_items + 8 * X].view(np.int32).reshape(X, 2)
+    witems = raw[o_witems:o_witems + 8 * W].view(np.int32).reshape(W, 2)
 
     ro = R.route_compact(ids, E)
     flat = ids.reshape(-1)
@@ -256,6 +261,16 @@ def test_prefill_routing_arrays(E, k, M, hot):
             want_items.append((e, r0 | (min(32, hi - r0) << 24)))
     assert n_items == len(want_items)
     assert [tuple(v) for v in items[:n_items].tolist()] == want_items
+    # wide items: ceil(c / 64) per expert, rows shared out in multiples of 16
+    want_witems = []
+    for e, (lo, hi) in sorted(seg.items()):
+        c = hi - lo
+        nw = -(-c // 64)
+        per = -(-(-(-c // nw)) // 16) * 16
+        for p in range(nw):
+            want_witems.append((e, (lo + per * p) | (min(per, c - per * p) << 24)))
+    assert n_witems == len(want_witems) <= W
+    assert [tuple(v) for v in witems[:n_witems].tolist()] == want_witems
     # rows (valid placement): bijection, each slot inside its expert's segment
     assert (slot_row[~valid] == -1).all()
     rows_of_valid = slot_row[valid]
