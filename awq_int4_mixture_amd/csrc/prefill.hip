@@ -503,6 +503,10 @@ __global__ __launch_bounds__(256) void prefill_w13_kernel(const int32_t* __restr
 // Calls from this many tokens take the wide kernels (items of up to 64 rows,
 // 20 column tiles per workgroup); below, the per-tile kernels above.
 constexpr int kWideMinTokens = 256;
+// Slots from which W2 takes the wide items (below: the 32-row items, where
+// experts have few rows: M = 1024, 154.8 against 160.1 us per call; M =
+// 4096, 404.8 against 399.0).
+constexpr int kW2WideItemsFrom = 16384;
 
 // ---------------------------------------------------------------------------
 // Both products for calls with many rows per expert ("wide" kernels): work
@@ -538,7 +542,10 @@ constexpr int kWideMinTokens = 256;
 // ---------------------------------------------------------------------------
 constexpr int kWxRows = 64;                 // A rows of an LDS chunk (room for 4 row tiles)
 constexpr int kWxRT = kWideRows / 16;       // 16-row tiles of the largest wide item
-constexpr int kWxCT13 = 5, kWxCT2 = 5;      // column tiles per wave of the two stages
+// column tiles per wave: W13 5; W2 5 over wide items, 4 over 32-row items
+// (a register budget for three workgroups per CU)
+constexpr int kWxCT13 = 5, kWxCT2 = 5, kWxCT2Narrow = 4;
+constexpr int wx_ct(int stage, int rtmax) { return stage == 0 ? kWxCT13 : rtmax <= 2 ? kWxCT2Narrow : kWxCT2; }
 constexpr int kWxCG13 = 4, kWxCG2 = 5;      // groups per chunk of the two stages
 // LDS dwords of a stage's A chunk, decoded records of a chunk and weights of a chunk
 constexpr int wx_a_dw(int cg) { return cg * 4 * kWxRows * 4; }
@@ -796,14 +803,14 @@ __device__ __forceinline__ void wide_item(const uint8_t* units, const uint8_t* r
 
 // STAGE kWideW13: a = x, out = act (stride inter); kWideW2: a = act, out = y
 // (stride hidden).
-template <int RB, int STAGE>
-__global__ __launch_bounds__(256, 2) void prefill_wide_kernel(const int32_t* items, const int32_t* num_items,
+template <int RB, int STAGE, int RTMAX>
+__global__ __launch_bounds__(256, RTMAX <= 2 ? 3 : 2) void prefill_wide_kernel(const int32_t* items, const int32_t* num_items,
                                                               const int32_t* row_slot, const uint8_t* bank,
                                                               const uint16_t* a, uint64_t expert_bytes,
                                                               uint64_t units_off, uint64_t meta_off, int H, int I,
                                                               int topk, void* out, int run_log2) {
   constexpr int CG = STAGE == kWideW13 ? kWxCG13 : kWxCG2;
-  constexpr int CT = STAGE == kWideW13 ? kWxCT13 : kWxCT2;
+  constexpr int CT = wx_ct(STAGE, RTMAX);
   __shared__ __attribute__((aligned(16))) uint32_t al[wx_a_dw(CG)];
   __shared__ __attribute__((aligned(16))) uint32_t rl[wx_r_dw(CT, CG)];
   __shared__ __attribute__((aligned(16))) uint32_t bl[wx_ring(STAGE) ? 4 : wx_b_dw(CT, CG)];
@@ -818,8 +825,8 @@ __global__ __launch_bounds__(256, 2) void prefill_wide_kernel(const int32_t* ite
   const uint8_t* blk = bank + (uint64_t)e * expert_bytes;
   const uint8_t* units = blk + units_off + (uint64_t)nb0 * 256 * G;
   const uint8_t* recs = blk + meta_off + (uint64_t)nb0 * 16 * G * RB;
-  const int rt = (rows + 15) >> 4;  // 1 .. kWxRT
-  static_for<kWxRT>([&](auto i_c) {
+  const int rt = (rows + 15) >> 4;  // 1 .. RTMAX
+  static_for<RTMAX>([&](auto i_c) {
     constexpr int RT = decltype(i_c)::value + 1;
     if (rt == RT)
       wide_item<RB, RT, CG, CT, STAGE>(units, recs, a, row_slot, row0, rows, topk, G, NT, nb0, out, out_stride, al,
@@ -938,50 +945,57 @@ __global__ __launch_bounds__(256) void prefill_w2_kernel(const int32_t* __restri
 }
 
 // ---------------------------------------------------------------------------
-// reduce: grid (ceil(H/512), M), one wave; lane l sums columns 8l .. 8l + 7 of
-// a 512-column block. The token's valid slots are ranked by (expert id,
-// slot) with lane reads, then summed in that order: acc = fma(w, y, acc)
-// from +0, rounded once to fp16. The rows are requested kRedBatch at a time
-// before any is summed (one memory round trip per batch).
+// reduce: grid (ceil(H/512), ceil(M/4)), four waves, wave w taking token
+// 4 blockIdx.y + w (four-wave workgroups: one-wave workgroups left CUs short
+// of waves); lane l sums columns 4l .. 4l + 3 and 256 + 4l .. 256 + 4l + 3 of
+// a 512-column block (each of the two loads of a row covers 1 KB). The
+// token's valid slots are ranked by (expert id, slot) with lane reads, then
+// summed in that order: acc = fma(w, y, acc) from +0, rounded once to fp16.
+// The rows are requested kRedBatch at a time before any is summed (one
+// memory round trip per batch), with non-temporal loads (each row is read
+// once).
 // ---------------------------------------------------------------------------
 constexpr int kRedBatch = 8;
 
-__global__ __launch_bounds__(64) void prefill_reduce_kernel(const int32_t* __restrict__ ids,
-                                                            const float* __restrict__ topk_w,
-                                                            const int32_t* __restrict__ slot_row,
-                                                            const float* __restrict__ y, int H, int topk, int E,
-                                                            uint16_t* __restrict__ out) {
-  __shared__ int order_row[AWQ_MOE_KMAX_TOPK];
-  __shared__ float order_w[AWQ_MOE_KMAX_TOPK];
-  const int tok = blockIdx.y, lane = threadIdx.x;
-  const int s = tok * topk + lane;
-  int id = lane < topk ? ids[s] : -1;
-  const bool valid = lane < topk && id >= 0 && id < E;
+__global__ __launch_bounds__(256) void prefill_reduce_kernel(const int32_t* __restrict__ ids,
+                                                             const float* __restrict__ topk_w,
+                                                             const int32_t* __restrict__ slot_row,
+                                                             const float* __restrict__ y, int M, int H, int topk,
+                                                             int E, uint16_t* __restrict__ out) {
+  __shared__ int order_row[4][AWQ_MOE_KMAX_TOPK];
+  __shared__ float order_w[4][AWQ_MOE_KMAX_TOPK];
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int tok = blockIdx.y * 4 + wave;
+  const bool live_tok = tok < M;
+  const int s = (live_tok ? tok : 0) * topk + lane;
+  const int id = lane < topk ? ids[s] : -1;
+  const bool valid = live_tok && lane < topk && id >= 0 && id < E;
   const int key = valid ? id * 32 + lane : 0x7FFFFFFF;
   int rank = 0;
   for (int jj = 0; jj < topk; ++jj) rank += __builtin_amdgcn_readlane(key, jj) < key;
   if (valid) {
-    order_row[rank] = slot_row[s];
-    order_w[rank] = topk_w[s];
+    order_row[wave][rank] = slot_row[s];
+    order_w[wave][rank] = topk_w[s];
   }
   const int nvalid = __popcll(__ballot(valid));
   __syncthreads();
-  const int col = blockIdx.x * 512 + 8 * lane;
-  if (col >= H) return;
+  const int col = blockIdx.x * 512 + 4 * lane;  // and col + 256
+  if (!live_tok || col >= H) return;
+  const bool hi_half = col + 256 < H;
   float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
   for (int r0 = 0; r0 < nvalid; r0 += kRedBatch) {
     f4_t v[kRedBatch][2];
 #pragma unroll
     for (int b = 0; b < kRedBatch; ++b) {
       // rows past the token's last are requested again from its first (never summed)
-      const float* yr = y + (uint64_t)order_row[r0 + b < nvalid ? r0 + b : 0] * H + col;
-      v[b][0] = __builtin_nontemporal_load(reinterpret_cast<const f4_t*>(yr));  // read once: streamed
-      v[b][1] = __builtin_nontemporal_load(reinterpret_cast<const f4_t*>(yr + 4));
+      const float* yr = y + (uint64_t)order_row[wave][r0 + b < nvalid ? r0 + b : 0] * H + col;
+      v[b][0] = __builtin_nontemporal_load(reinterpret_cast<const f4_t*>(yr));
+      v[b][1] = __builtin_nontemporal_load(reinterpret_cast<const f4_t*>(yr + (hi_half ? 256 : 0)));
     }
 #pragma unroll
     for (int b = 0; b < kRedBatch; ++b) {
       if (r0 + b >= nvalid) break;
-      const float w = order_w[r0 + b];
+      const float w = order_w[wave][r0 + b];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         acc[i] = fmaf(w, v[b][0][i], acc[i]);
@@ -989,10 +1003,15 @@ __global__ __launch_bounds__(64) void prefill_reduce_kernel(const int32_t* __res
       }
     }
   }
-  h8_t o;
+  typedef _Float16 h4_t __attribute__((ext_vector_type(4)));
+  h4_t o0, o1;
 #pragma unroll
-  for (int i = 0; i < 8; ++i) o[i] = (_Float16)acc[i];
-  *reinterpret_cast<h8_t*>(out + (uint64_t)tok * H + col) = o;
+  for (int i = 0; i < 4; ++i) {
+    o0[i] = (_Float16)acc[i];
+    o1[i] = (_Float16)acc[4 + i];
+  }
+  *reinterpret_cast<h4_t*>(out + (uint64_t)tok * H + col) = o0;
+  if (hi_half) *reinterpret_cast<h4_t*>(out + (uint64_t)tok * H + col + 256) = o1;
 }
 
 // ---------------------------------------------------------------------------
@@ -1026,11 +1045,11 @@ hipError_t launch_prefill(const StageArgs& a, const uint16_t* x, const float* to
     // many rows per expert: wide items, 20 column tiles per workgroup
     const dim3 g13w(((2 * a.I) / 16 + 4 * kWxCT13 - 1) / (4 * kWxCT13), witems8);
     if (a.RB == 4)
-      hipLaunchKernelGGL((prefill_wide_kernel<4, kWideW13>), g13w, dim3(256), 0, stream, w.witems, w.num_witems,
+      hipLaunchKernelGGL((prefill_wide_kernel<4, kWideW13, kWxRT>), g13w, dim3(256), 0, stream, w.witems, w.num_witems,
                          w.row_slot, a.bank, x, a.expert_bytes, a.w13_off, a.w13_meta_off, a.H, a.I, a.topk,
                          (void*)w.act, wrun_log2);
     else
-      hipLaunchKernelGGL((prefill_wide_kernel<3, kWideW13>), g13w, dim3(256), 0, stream, w.witems, w.num_witems,
+      hipLaunchKernelGGL((prefill_wide_kernel<3, kWideW13, kWxRT>), g13w, dim3(256), 0, stream, w.witems, w.num_witems,
                          w.row_slot, a.bank, x, a.expert_bytes, a.w13_off, a.w13_meta_off, a.H, a.I, a.topk,
                          (void*)w.act, wrun_log2);
   } else if (a.RB == 4) {
@@ -1041,14 +1060,26 @@ hipError_t launch_prefill(const StageArgs& a, const uint16_t* x, const float* to
                        a.expert_bytes, a.w13_off, a.w13_meta_off, a.H, a.I, a.topk, w.act, run_log2);
   }
   if ((err = hipGetLastError()) != hipSuccess) return err;
-  if (wide) {
+  if (wide && n < kW2WideItemsFrom) {
+    // W2 over the 32-row work items (two row tiles at most): a smaller
+    // register budget, three workgroups per CU
+    const dim3 g2n(((a.H / 16) + 4 * kWxCT2Narrow - 1) / (4 * kWxCT2Narrow), items8);
+    if (a.RB == 4)
+      hipLaunchKernelGGL((prefill_wide_kernel<4, kWideW2, 2>), g2n, dim3(256), 0, stream, w.items, w.num_items,
+                         w.row_slot, a.bank, w.act, a.expert_bytes, a.w2_off, a.w2_meta_off, a.H, a.I, a.topk,
+                         (void*)w.y, run_log2);
+    else
+      hipLaunchKernelGGL((prefill_wide_kernel<3, kWideW2, 2>), g2n, dim3(256), 0, stream, w.items, w.num_items,
+                         w.row_slot, a.bank, w.act, a.expert_bytes, a.w2_off, a.w2_meta_off, a.H, a.I, a.topk,
+                         (void*)w.y, run_log2);
+  } else if (wide) {
     const dim3 g2w(((a.H / 16) + 4 * kWxCT2 - 1) / (4 * kWxCT2), witems8);
     if (a.RB == 4)
-      hipLaunchKernelGGL((prefill_wide_kernel<4, kWideW2>), g2w, dim3(256), 0, stream, w.witems, w.num_witems,
+      hipLaunchKernelGGL((prefill_wide_kernel<4, kWideW2, kWxRT>), g2w, dim3(256), 0, stream, w.witems, w.num_witems,
                          w.row_slot, a.bank, w.act, a.expert_bytes, a.w2_off, a.w2_meta_off, a.H, a.I, a.topk,
                          (void*)w.y, wrun_log2);
     else
-      hipLaunchKernelGGL((prefill_wide_kernel<3, kWideW2>), g2w, dim3(256), 0, stream, w.witems, w.num_witems,
+      hipLaunchKernelGGL((prefill_wide_kernel<3, kWideW2, kWxRT>), g2w, dim3(256), 0, stream, w.witems, w.num_witems,
                          w.row_slot, a.bank, w.act, a.expert_bytes, a.w2_off, a.w2_meta_off, a.H, a.I, a.topk,
                          (void*)w.y, wrun_log2);
   } else if (a.RB == 4) {
@@ -1059,8 +1090,8 @@ hipError_t launch_prefill(const StageArgs& a, const uint16_t* x, const float* to
                        a.w2_off, a.w2_meta_off, a.H, a.I, w.act, w.y, run_log2);
   }
   if ((err = hipGetLastError()) != hipSuccess) return err;
-  hipLaunchKernelGGL(prefill_reduce_kernel, dim3((a.H + 511) / 512, a.M), dim3(64), 0, stream, a.topk_ids, topk_w,
-                     w.slot_row, w.y, a.H, a.topk, a.E, out);
+  hipLaunchKernelGGL(prefill_reduce_kernel, dim3((a.H + 511) / 512, (a.M + 3) / 4), dim3(256), 0, stream, a.topk_ids,
+                     topk_w, w.slot_row, w.y, a.M, a.H, a.topk, a.E, out);
   return hipGetLastError();
 }
 

@@ -80,6 +80,24 @@ def test_prefill_largest_hidden_and_inter_sampled():
     check(got[sel], R.moe_stage(x[sel], ids[sel], w[sel], E, bi.expert), "prefill largest hidden and inter")
 
 
+@pytest.mark.parametrize("rb", [3, 4])
+def test_prefill_rank_shape_wide_items_sampled(rb):
+    """Hidden 2560, inter 160, 64 experts, top-k 10, M = 2048 (20,480 slots,
+    about 320 rows per expert): W2 takes the wide items (five 64-row items
+    per expert), W13 the wide items throughout; the oracle on 16 sampled
+    tokens, the first and last among them."""
+    E, H, I, k, M = 64, 2560, 160, 10, 2048
+    dims, bank, bi = bank_case(96, E, H, I, rb)
+    rng = inputs.call_rng(97, rb)
+    x = inputs.activations(rng, M, H)
+    ids = inputs.ids_distinct(rng, M, k, E)
+    w = inputs.router_weights(rng, M, k)
+    say("prefill rank shape wide items", M, rb)
+    got = run_prefill(dims, bank, x, ids, w)
+    sel = np.unique(np.concatenate([[0, M - 1], rng.choice(np.arange(1, M - 1), 14, replace=False)]))
+    check(got[sel], R.moe_stage(x[sel], ids[sel], w[sel], E, bi.expert), f"prefill rank shape wide items rb={rb}")
+
+
 def test_prefill_maximum_experts_topk_tokens_sampled():
     """4096 experts, top-k 32 and 4096 tokens (131,072 slots, the admitted
     maxima), hidden 256, inter 32: the oracle on 16 sampled tokens, the
