@@ -44,8 +44,9 @@ constexpr int kRouteSlotsPerBlock = 2048;  // slots per routing workgroup (when 
 constexpr int kRouteCountCap = 65536;      // workgroups x experts of the per-workgroup counts
 
 // ---------------------------------------------------------------------------
-// routing, in two launches over B workgroups that each own a contiguous
-// slice of the slots (B from prefill_route_blocks):
+// routing. Up to kRouteBatch * 1024 slots, one workgroup does all of it in
+// one launch (place with SINGLE). Beyond, two launches over B workgroups
+// that each own a contiguous slice of the slots (B from prefill_route_blocks):
 //  * count: the slice's slots per expert (LDS atomics), written to
 //    cnt[b][E], and whether the slice holds an id outside [0, E);
 //  * place: every workgroup sums cnt over the workgroups for each expert
@@ -103,6 +104,10 @@ __global__ __launch_bounds__(1024) void prefill_count_kernel(const int32_t* __re
   if (t == 0) bad[b] = any_bad;
 }
 
+// SINGLE (n <= kRouteBatch * 1024 slots, one workgroup): the count is taken
+// here from the ids held in registers, which then also serve the placement
+// (one launch, one read of the ids).
+template <bool SINGLE>
 __global__ __launch_bounds__(1024) void prefill_place_kernel(const int32_t* __restrict__ ids, int n, int E, int per,
                                                              int nb, const int32_t* __restrict__ cnt,
                                                              const int32_t* __restrict__ bad,
@@ -116,9 +121,27 @@ __global__ __launch_bounds__(1024) void prefill_place_kernel(const int32_t* __re
   __shared__ int tot[AWQ_MOE_KMAX_ROUTER_E];
   __shared__ int cur[AWQ_MOE_KMAX_ROUTER_E];
   __shared__ int wsum[16][3];
+  __shared__ int any_bad;
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6, b = blockIdx.x;
+  int ev[kRouteBatch];  // SINGLE: the ids of slots t + 1024 q
+  if constexpr (SINGLE) {
+#pragma unroll
+    for (int q = 0; q < kRouteBatch; ++q) ev[q] = t + 1024 * q < n ? ids[t + 1024 * q] : 0;  // all in flight
+    for (int e = t; e < E; e += 1024) tot[e] = cur[e] = 0;
+    if (t == 0) any_bad = 0;
+    __syncthreads();
+#pragma unroll
+    for (int q = 0; q < kRouteBatch; ++q) {
+      if (t + 1024 * q >= n) break;
+      if (ev[q] >= 0 && ev[q] < E)
+        atomicAdd(&tot[ev[q]], 1);
+      else
+        any_bad = 1;
+    }
+    __syncthreads();
+  }
   // totals per expert and the share of the workgroups before this one
-  for (int e = t; e < E; e += 1024) {
+  for (int e = t; !SINGLE && e < E; e += 1024) {
     int all = 0, before = 0;
     for (int w0 = 0; w0 < nb; w0 += 8) {
       int v[8];
@@ -192,11 +215,27 @@ __global__ __launch_bounds__(1024) void prefill_place_kernel(const int32_t* __re
     *num_witems = wb + ws;
   }
   if (b == 0 && t == 0) {
-    int any = 0;
-    for (int w = 0; w < nb; ++w) any |= bad[w];
+    int any = SINGLE ? any_bad : 0;
+    for (int w = 0; !SINGLE && w < nb; ++w) any |= bad[w];
     *status = any ? AWQ_MOE_STATUS_BAD_ID_BIT : 0u;
   }
   __syncthreads();
+  if constexpr (SINGLE) {
+#pragma unroll
+    for (int q = 0; q < kRouteBatch; ++q) {
+      const int s = t + 1024 * q;
+      if (s >= n) break;
+      const int e = ev[q];
+      if (e >= 0 && e < E) {
+        const int r = atomicAdd(&cur[e], 1);
+        slot_row[s] = r;
+        row_slot[r] = s;
+      } else {
+        slot_row[s] = -1;
+      }
+    }
+    return;
+  }
   const int s0 = b * per, s1 = min(n, s0 + per);
   for_slots(ids, s0, s1, [&](int s, int e) {
     if (e >= 0 && e < E) {
@@ -1024,13 +1063,20 @@ hipError_t launch_prefill(const StageArgs& a, const uint16_t* x, const float* to
                           const PrefillWs& w, hipStream_t stream) {
   const int n = a.M * a.topk;
   const int max_items = prefill_max_items(n, a.E);
-  const int nb = prefill_route_blocks(n, a.E), per = (n + nb - 1) / nb;
-  hipLaunchKernelGGL(prefill_count_kernel, dim3(nb), dim3(1024), 0, stream, a.topk_ids, n, a.E, per, w.route_cnt,
-                     w.route_bad);
-  hipError_t err = hipGetLastError();
-  if (err != hipSuccess) return err;
-  hipLaunchKernelGGL(prefill_place_kernel, dim3(nb), dim3(1024), 0, stream, a.topk_ids, n, a.E, per, nb, w.route_cnt,
-                     w.route_bad, w.slot_row, w.row_slot, w.items, w.num_items, w.witems, w.num_witems, w.status);
+  hipError_t err;
+  if (n <= kRouteBatch * 1024) {
+    hipLaunchKernelGGL(prefill_place_kernel<true>, dim3(1), dim3(1024), 0, stream, a.topk_ids, n, a.E, n, 1,
+                       w.route_cnt, w.route_bad, w.slot_row, w.row_slot, w.items, w.num_items, w.witems, w.num_witems,
+                       w.status);
+  } else {
+    const int nb = prefill_route_blocks(n, a.E), per = (n + nb - 1) / nb;
+    hipLaunchKernelGGL(prefill_count_kernel, dim3(nb), dim3(1024), 0, stream, a.topk_ids, n, a.E, per, w.route_cnt,
+                       w.route_bad);
+    if ((err = hipGetLastError()) != hipSuccess) return err;
+    hipLaunchKernelGGL(prefill_place_kernel<false>, dim3(nb), dim3(1024), 0, stream, a.topk_ids, n, a.E, per, nb,
+                       w.route_cnt, w.route_bad, w.slot_row, w.row_slot, w.items, w.num_items, w.witems, w.num_witems,
+                       w.status);
+  }
   if ((err = hipGetLastError()) != hipSuccess) return err;
   // runs of 8 items per XCD from 64 rows per expert on average (2 items or more each)
   const int run_log2 = n >= 64 * a.E ? 3 : 0;
