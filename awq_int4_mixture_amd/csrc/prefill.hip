@@ -6,12 +6,14 @@
 // With many tokens an expert serves several rows, so the work is expert-major
 // and the products run on the matrix cores:
 //
-//  * route (two launches over slices of the slots): counts per expert, the
-//    experts' rows laid out in ascending expert order, each expert's rows
-//    cut into work items of at most 32 rows and wide items of at most 64;
-//  * below 256 tokens, W13 + SwiGLU per (work item, 16-column tile) and W2
-//    per (work item, 8 column tiles); from 256 tokens the wide kernels, per
-//    (wide item, 20 column tiles), for both products. Each group of 32 K
+//  * route (one workgroup up to 16,384 slots, else two launches over slices
+//    of the slots): counts per expert, the experts' rows laid out in
+//    ascending expert order, each expert's rows cut into work items of at
+//    most 32 rows and wide items of at most 64;
+//  * below 128 tokens, W13 + SwiGLU per (work item, 16-column tile) and W2
+//    per (work item, 8 column tiles); from 128 tokens the wide kernels, per
+//    (wide item, 20 column tiles) for W13 and per (work item or wide item,
+//    16 or 20 column tiles) for W2. Each group of 32 K
 //    values is one v_mfma_f32_16x16x32_f16 whose B operand is the exact
 //    integer (q - z) in fp16 (|q - z| <= 255), so the dequantised weight is
 //    never rounded; the group's fp32 result is scaled by s and accumulated
@@ -540,8 +542,10 @@ __global__ __launch_bounds__(256) void prefill_w13_kernel(const int32_t* __restr
 }
 
 // Calls from this many tokens take the wide kernels (items of up to 64 rows,
-// 20 column tiles per workgroup); below, the per-tile kernels above.
-constexpr int kWideMinTokens = 256;
+// 20 column tiles per workgroup); below, the per-tile kernels above (M = 128:
+// 108.1 against 95.6 us per call with the wide kernels; M = 64: 83.6 against
+// 86.0).
+constexpr int kWideMinTokens = 128;
 // Slots from which W2 takes the wide items (below: the 32-row items, where
 // experts have few rows: M = 1024, 154.8 against 160.1 us per call; M =
 // 4096, 404.8 against 399.0).
@@ -601,6 +605,14 @@ enum WideStage { kWideW13 = 0, kWideW2 = 1 };
 // at 4096 tokens, equal at 1024), W2 stages them in LDS (its K is short, so
 // the whole chunk is requested at once in contiguous runs; measured faster).
 constexpr bool wx_ring(int stage) { return stage == 0; }
+// The ring's two forms: per group, each lane requests its operand dword (four
+// 64-byte pieces per request) as soon as the group before is used; per chunk,
+// each lane requests a whole 16-byte unit (256 contiguous bytes per run) and
+// a transpose across the wave's lane rows rebuilds the operands. Items of up
+// to two row tiles are load-bound and take the second (W13 at M = 256: 59.8
+// -> 48.8 us, M = 512: 62.9 -> 56.6 us); with more row tiles the extra moves
+// and swaps cost more than the longer runs save (M = 4096: 145 -> 155 us).
+constexpr bool wx_ring_units(int stage, int rt) { return wx_ring(stage) && rt <= 2; }
 
 // f(std::integral_constant<int, i>) for i = 0 .. N - 1, each a separate
 // instantiation, so that indices derived from i are compile-time constants.
@@ -653,6 +665,18 @@ __device__ __forceinline__ uint2 decode_record(uint32_t r, bool live) {
   const _Float16 m64z = (_Float16)(-64.0f - (float)z);  // exact: 64 + z <= 319
   return make_uint2(live ? __builtin_bit_cast(uint32_t, s) : 0u,
                     (0xE400u + z) | ((uint32_t)__builtin_bit_cast(uint16_t, m64z) << 16));
+}
+
+// 4 x 4 transpose across the four 16-lane rows of a wave: on entry lane row r
+// holds m[r][0..3] in v[0..3], on exit m[0..3][r]. The 32-lane swaps exchange
+// rows {2, 3} of v[0], v[1] with rows {0, 1} of v[2], v[3]; the 16-lane swaps
+// then exchange the odd rows of v[0], v[2] with the even rows of v[1], v[3].
+__device__ __forceinline__ void rows_transpose4(uint32_t (&v)[4]) {
+  const auto s02 = __builtin_amdgcn_permlane32_swap(v[0], v[2], false, false);
+  const auto s13 = __builtin_amdgcn_permlane32_swap(v[1], v[3], false, false);
+  const auto s01 = __builtin_amdgcn_permlane16_swap(s02[0], s13[0], false, false);
+  const auto s23 = __builtin_amdgcn_permlane16_swap(s02[1], s13[1], false, false);
+  v[0] = s01[0], v[1] = s01[1], v[2] = s23[0], v[3] = s23[1];
 }
 
 // One wide item of one column block. K = 32 G; the A rows are K fp16 long.
@@ -719,13 +743,24 @@ __device__ __forceinline__ void wide_item(const uint8_t* units, const uint8_t* r
   auto ld_b = [&](int i, int g0) {
     return *reinterpret_cast<const u32x4_t*>(units + 64 * min(g0 + bgl[i], G - 1) + bo[i]);
   };
-  // the register ring (RING): this lane's operand dword of tile CT wave + ct
-  // (clamped into the block), group g
-  const uint32_t bor = (uint32_t)j * 64u * G + 16u * quad + 4u * kb;
+  // the register ring (RING), tile CT wave + ct clamped into the block:
+  //  * per group (!RU): this lane's operand dword of group g;
+  //  * per chunk (RU): lane (c, kb) requests the whole unit of column c,
+  //    group g0 + kb (clamped into K), so the 16 lanes of a run j read the
+  //    run's 256 contiguous bytes of the chunk; rows_transpose4 then hands
+  //    lane (c, kb) dword kb of column c's unit of each of the chunk's groups.
+  constexpr bool RU = wx_ring_units(STAGE, RT);
+  static_assert(!RU || CG == 4, "the ring's transpose takes chunks of 4 groups");
+  const uint32_t bor = (uint32_t)j * 64u * G + 16u * quad + (RU ? 0u : 4u * kb);
   const uint8_t* tbase[CT];
 #pragma unroll
   for (int ct = 0; ct < CT; ++ct) tbase[ct] = units + (uint64_t)min(CT * wave + ct, Tb - 1) * 256 * G;
   auto ld_r = [&](int ct, int g) { return *reinterpret_cast<const uint32_t*>(tbase[ct] + 64 * min(g, G - 1) + bor); };
+  auto ld_ru = [&](int ct, int g0) {  // group min(g0 + kb, G - 1) as a uniform part plus a lane part
+    const int gu = min(g0, G - 1);
+    const uint32_t lo = 64u * (uint32_t)min(kb, G - 1 - gu) + bor;
+    return *reinterpret_cast<const u32x4_t*>(tbase[ct] + 64 * gu + lo);
+  };
   auto ld_a = [&](int i, int g0) { return *reinterpret_cast<const u32x4_t*>(ab + 64 * min(g0 + agl[i], G - 1) + ao[i]); };
   auto rsrc = [&](int q, int g0) { return recs + 16 * RB * min(g0 + rgl[q], G - 1) + ro[q]; };
   u32x4_t av[kNU], bv[kNB];
@@ -745,10 +780,11 @@ __device__ __forceinline__ void wide_item(const uint8_t* units, const uint8_t* r
     }
   };
   load_chunk(0);
-  uint32_t bq[RING ? CG : 1][CT];
-  if constexpr (RING) {
-    // chunk requests before ring requests, in the same order as in the loop,
-    // so that the first chunk's wait leaves the ring in flight
+  // chunk requests before ring requests, in the same order as in the loop,
+  // so that the wait for the chunk's A and records leaves the ring in flight
+  uint32_t bq[RING && !RU ? CG : 1][CT];  // per group: [group of the chunk][tile]
+  u32x4_t braw[RU ? CT : 1];              // per chunk: the next chunk's units
+  if constexpr (RING && !RU) {
     issue_here();
 #pragma unroll
     for (int g = 0; g < CG; ++g) {
@@ -756,6 +792,12 @@ __device__ __forceinline__ void wide_item(const uint8_t* units, const uint8_t* r
       for (int ct = 0; ct < CT; ++ct) bq[g][ct] = ld_r(ct, g);
       issue_here();
     }
+  }
+  if constexpr (RU) {
+    issue_here();
+#pragma unroll
+    for (int ct = 0; ct < CT; ++ct) braw[ct] = ld_ru(ct, 0);
+    issue_here();
   }
   f4_t acc[CT][RT];
 #pragma unroll
@@ -788,7 +830,19 @@ __device__ __forceinline__ void wide_item(const uint8_t* units, const uint8_t* r
       *reinterpret_cast<u32x4_t*>(rl + rdst[q] + 4) = hi;
     }
     __syncthreads();
+    // RU: this chunk's units, transposed into bt[tile][group of the chunk]
+    // where a tile is first used, so that each waits only for its own load
+    u32x4_t bcur[RU ? CT : 1];
+    uint32_t bt[RU ? CT : 1][4];
+    if constexpr (RU) {
+#pragma unroll
+      for (int ct = 0; ct < CT; ++ct) bcur[ct] = braw[ct];
+    }
     load_chunk(g0 + CG);  // the next chunk (clamped past K: loaded, never used)
+    if constexpr (RU) {
+#pragma unroll
+      for (int ct = 0; ct < CT; ++ct) braw[ct] = ld_ru(ct, g0 + CG);
+    }
     issue_here();
 #pragma unroll
     for (int gl = 0; gl < CG; ++gl) {
@@ -799,15 +853,23 @@ __device__ __forceinline__ void wide_item(const uint8_t* units, const uint8_t* r
         a[rt] = *reinterpret_cast<const h8_t*>(al + ((gl * 4 + kb) * kWxRows + 16 * rt + cs) * 4);
 #pragma unroll
       for (int ct = 0; ct < CT; ++ct) {
+        if constexpr (RU) {
+          if (gl == 0) {
+            bt[ct][0] = bcur[ct].x, bt[ct][1] = bcur[ct].y, bt[ct][2] = bcur[ct].z, bt[ct][3] = bcur[ct].w;
+            rows_transpose4(bt[ct]);
+          }
+        }
         const int tb = min(CT * wave + ct, Tb - 1);
         const uint2 sc = *reinterpret_cast<const uint2*>(rl + ((tb * CG + gl) * 16 + c) * 2);
-        const uint32_t wq = RING ? bq[RING ? gl : 0][ct] : bl[(tb * 4 + j) * kRS + (4 * gl + quad) * 4 + kb];
+        const uint32_t wq = RU     ? bt[RU ? ct : 0][gl]
+                            : RING ? bq[RING ? gl : 0][ct]
+                                   : bl[(tb * 4 + j) * kRS + (4 * gl + quad) * 4 + kb];
         const h8_t b = qz_operand64(wq, sc.y, m1024, m64);
         const float s = __builtin_bit_cast(float, sc.x);
 #pragma unroll
         for (int rt = 0; rt < RT; ++rt) scale_add(acc[ct][rt], s, mfma16(a[rt], b));
       }
-      if constexpr (RING) {
+      if constexpr (RING && !RU) {
 #pragma unroll
         for (int ct = 0; ct < CT; ++ct) bq[gl][ct] = ld_r(ct, g0 + gl + CG);
         issue_here();  // the same for the weight ring

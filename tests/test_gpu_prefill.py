@@ -38,19 +38,21 @@ def check(got, want, what):
 
 @pytest.mark.parametrize("E,H,I,k,M,rb", [
     (16, 256, 32, 2, 9, 3),        # the admission boundary, tiny shape
-    (16, 256, 32, 4, 128, 4),      # 32 rows per expert on average: several items, two 16-row tiles
+    (16, 256, 32, 4, 128, 4),      # wide kernels, 32 rows per expert on average: items of two or three row tiles
     (6, 96, 64, 3, 17, 3),         # hidden 96: 6 W2 column tiles in one block; 3 W13 groups for 4 waves
     (16, 512, 2048, 10, 40, 3),    # inter 2048: 256 W13 column tiles, 64 W2 groups
     (12, 128, 96, 1, 33, 4),       # top-k 1
     (64, 2560, 160, 10, 127, 3),   # rank shape with 64 experts, ~20 rows each
     (4, 8192, 32, 2, 9, 3),        # hidden 8192: 256 W13 groups, 64 per wave
     (16, 256, 32, 2, 4096, 3),     # the largest M: 8192 slots, ~512 rows per expert
-    (16, 352, 64, 4, 600, 4),      # four tiles per W13 workgroup: 11 groups (a chunk of 10 and one of 1), 2 tile groups
-    (40, 2560, 160, 10, 512, 3),   # four tiles per W13 workgroup at the rank shape: 8 chunks, ~128 rows per expert
-    (8, 8192, 32, 2, 520, 3),      # four tiles per W13 workgroup, hidden 8192: 26 chunks, the last of 6 groups
+    (16, 352, 64, 4, 600, 4),      # wide kernels: 11 groups (W13 chunks of 4, 4, 3), ~150 rows per expert
+    (40, 2560, 160, 10, 512, 3),   # wide kernels at the rank shape, ~128 rows per expert: 64-row items
+    (8, 8192, 32, 2, 520, 3),      # wide kernels, hidden 8192: 64 W13 chunks, ~130 rows per expert
     (4, 8192, 2048, 4, 9, 3),      # hidden 8192 with inter 2048 (the maxima together), single-tile W13
     (6, 96, 64, 3, 300, 3),        # wide items with 3 groups: one chunk, shorter than the weight ring
     (6, 96, 64, 3, 300, 4),        # the same with 4-byte records
+    (24, 96, 64, 3, 128, 3),       # wide items of one or two row tiles (the unit ring) with 3 groups: clamped units
+    (44, 352, 64, 4, 160, 4),      # the unit ring over 11 groups (chunks of 4, 4, 3), ~15 rows per expert
 ])
 def test_prefill_shapes(E, H, I, k, M, rb):
     dims, bank, bi = bank_case(60 + I, E, H, I, rb)

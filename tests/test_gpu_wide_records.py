@@ -12,7 +12,8 @@ records:
     one workgroup per CU) and single lanes (M = 8);
   * decode W2 + reduction in both forms: slot segments (inter 160) and the
     generic kernel (inter 2048);
-  * prefill W13 single-tile (M < 256) and multi-tile (M >= 256), and W2;
+  * prefill: the per-tile kernels (M < 128) and the wide kernels (from 128
+    tokens) with both forms of the W13 weight ring, and W2;
   * 3-byte and 4-byte records (byte-identical outputs).
 
 Two input families:
@@ -177,13 +178,15 @@ def test_w2_stage_scales_near_fp16_max_on_given_act(rb, M):
 
 
 @pytest.mark.parametrize("family", ["wide", "xmax"])
-@pytest.mark.parametrize("M", [40, 300])
+@pytest.mark.parametrize("M", [40, 128, 300])
 @pytest.mark.parametrize("rb", [3, 4])
 def test_prefill_wide_records(rb, M, family):
-    """Indexed prefill with wide records: single-tile W13 at M = 40 (about 6
-    rows per expert), multi-tile W13 at M = 300 (about 47 rows per expert,
-    two work items each), the matrix-core B operand (q - z) over zeros
-    0..255, and W2 with signed/zero/subnormal scales."""
+    """Indexed prefill with wide records: the per-tile kernels at M = 40
+    (about 6 rows per expert), the wide kernels at M = 128 (about 20 rows:
+    items of one or two row tiles, whose W13 weights take the unit ring) and
+    M = 300 (about 47 rows: three row tiles, the per-group ring), the
+    matrix-core B operand (q - z) over zeros 0..255, and W2 with
+    signed/zero/subnormal scales."""
     E, k = 64, 10
     dims, bank, bi = bank_case(301, E, H, I, rb, wide=FAMILIES[family])
     rng = inputs.call_rng(308, M + len(family))
