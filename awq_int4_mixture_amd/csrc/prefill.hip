@@ -679,8 +679,18 @@ __device__ __forceinline__ void rows_transpose4(uint32_t (&v)[4]) {
   v[0] = s01[0], v[1] = s01[1], v[2] = s23[0], v[3] = s23[1];
 }
 
+// The LDS dword offset of unit (16-row tile slot row', group g, k block kb)
+// of a staged A chunk of kWxRows rows: [group][k block][row], the row
+// XOR-swizzled inside its 16-row tile with (4 g + kb).
+__device__ __forceinline__ int wx_a_unit(int g, int kb, int row) {
+  return ((g * 4 + kb) * 64 + (row & ~15) + ((row & 15) ^ ((4 * g + kb) & 15))) * 4;
+}
+
 // One wide item of one column block. K = 32 G; the A rows are K fp16 long.
-template <int RB, int RT, int CG, int CT, int STAGE>
+// TO_LDS (W13 only): act goes to LDS at `out` in the A layout of a W2 chunk
+// (every row of the item's row tiles, padding rows included) instead of to
+// global memory.
+template <int RB, int RT, int CG, int CT, int STAGE, bool TO_LDS = false>
 __device__ __forceinline__ void wide_item(const uint8_t* units, const uint8_t* recs, const uint16_t* a_src,
                                           const int32_t* row_slot, int row0, int rows, int topk, int G, int NT,
                                           int nb0, void* out, int out_stride, uint32_t* al, uint32_t* rl,
@@ -887,7 +897,15 @@ __device__ __forceinline__ void wide_item(const uint8_t* units, const uint8_t* r
       for (int i = 0; i < 4; ++i) {
         const float d = acc[ct][rt][i];
         const int row = 16 * rt + 4 * kb + i;
-        if constexpr (STAGE == kWideW13) {
+        if constexpr (STAGE == kWideW13 && TO_LDS) {
+          const float up = dpp<kQuadSwap1>(d);  // column c ^ 1
+          if (!(c & 1)) {
+            const float a = d / (1.0f + __expf(-d)) * up;
+            const int ac = nt * 8 + (c >> 1);  // act column: group ac / 32, k block (ac / 8) % 4
+            static_cast<uint16_t*>(out)[2 * wx_a_unit(ac >> 5, (ac >> 3) & 3, row) + (ac & 7)] =
+                __builtin_bit_cast(uint16_t, (_Float16)a);
+          }
+        } else if constexpr (STAGE == kWideW13) {
           const float up = dpp<kQuadSwap1>(d);  // column c ^ 1
           if (!(c & 1) && row < rows) {
             const float a = d / (1.0f + __expf(-d)) * up;
@@ -932,6 +950,190 @@ __global__ __launch_bounds__(256, RTMAX <= 2 ? 3 : 2) void prefill_wide_kernel(c
     if (rt == RT)
       wide_item<RB, RT, CG, CT, STAGE>(units, recs, a, row_slot, row0, rows, topk, G, NT, nb0, out, out_stride, al,
                                        rl, bl);
+  });
+}
+
+// ---------------------------------------------------------------------------
+// Both products of one wide item in one workgroup (inter <= 160, so that the
+// item's act rows, all of W2's K, fit one LDS chunk and W13's 2 inter / 16
+// column tiles one block of 20): W13 + SwiGLU as in prefill_wide_kernel with
+// act written to LDS in the A layout of a W2 chunk, then W2 over every block
+// of 20 column tiles with that A resident. The next block's weights and
+// records are requested before the current block computes. One launch less
+// than the two wide kernels, and no act round trip through global memory;
+// the arithmetic and its order are the same, so the results are too.
+// ---------------------------------------------------------------------------
+constexpr int kFusedMaxInter = 32 * kWxCG2;  // 160
+
+template <int RB, int RT, int CT>
+__device__ __forceinline__ void w2_resident(const uint8_t* units, const uint8_t* recs, const uint32_t* al, int G,
+                                            int NT, int row0, int rows, float* y, int H, uint32_t* rl,
+                                            uint32_t* bl) {
+  typedef uint32_t u32x3 __attribute__((ext_vector_type(3), aligned(4)));
+  constexpr int CG = kWxCG2;                       // all of K (G <= CG) in the one chunk
+  constexpr int kWxTiles = 4 * CT;                 // column tiles of a block
+  constexpr int kQuads = kWxTiles * CG * 4;        // record quads of a block
+  constexpr int kNQ = (kQuads + 255) / 256;
+  constexpr int kRS = wx_run_stride(CG);
+  constexpr int kBU = kWxTiles * 4 * 4 * CG;       // weight units of a block
+  constexpr int kNB = (kBU + 255) / 256;
+  // an opaque copy of the thread index, so that this phase's per-thread
+  // offsets are computed here and do not stay live through the phase before
+  int t;
+  asm volatile("v_mov_b32 %0, %1" : "=v"(t) : "v"((int)threadIdx.x));
+  const int lane = t & 63, wave = __builtin_amdgcn_readfirstlane(t >> 6);
+  const int c = lane & 15, kb = lane >> 4, quad = c >> 2, j = c & 3;
+  const uint32_t m1024 = magic1024(), m64 = magic64();
+  const int nblk = (NT + kWxTiles - 1) / kWxTiles;
+  // this thread's weight units and record quads of a block, as in wide_item:
+  // the tile within the block and the offset inside the tile (group clamped
+  // into K); a block's requests are its uniform base plus 32-bit lane offsets
+  uint32_t bo[kNB];
+  int btl[kNB], bdst[kNB];
+#pragma unroll
+  for (int i = 0; i < kNB; ++i) {
+    const int u = min(t + 256 * i, kBU - 1), ur = u % (4 * CG), run = u / (4 * CG);
+    btl[i] = run >> 2;
+    bo[i] = (uint32_t)(run & 3) * 64u * G + 16u * (ur & 3) + 64u * (uint32_t)min(ur >> 2, G - 1);
+    bdst[i] = t + 256 * i < kBU ? run * kRS + 4 * ur : -1;
+  }
+  uint32_t ro[kNQ];
+  int rtl[kNQ], rgl[kNQ], rdst[kNQ];
+#pragma unroll
+  for (int q = 0; q < kNQ; ++q) {
+    const int u = min(t + 256 * q, kQuads - 1);
+    rtl[q] = u / (4 * CG);
+    rgl[q] = (u >> 2) % CG;
+    ro[q] = 4u * (u & 3) * RB + 16u * RB * (uint32_t)min(rgl[q], G - 1);
+    rdst[q] = t + 256 * q < kQuads ? 8 * u : -1;
+  }
+  u32x4_t bv[kNB];
+  u32x3 rv[kNQ];
+  uint32_t rw[kNQ];
+  const uint32_t tile_b = 256u * G, tile_r = 16u * G * RB;  // bytes of a tile's weights and records
+  auto load_block = [&](int b) {  // clamped into the blocks, the block's tiles and K
+    const int nb0 = kWxTiles * min(b, nblk - 1), Tb = min(kWxTiles, NT - nb0);
+    const uint8_t* ub = units + (uint64_t)nb0 * tile_b;
+    const uint8_t* rb = recs + (uint64_t)nb0 * tile_r;
+#pragma unroll
+    for (int i = 0; i < kNB; ++i)
+      bv[i] = *reinterpret_cast<const u32x4_t*>(ub + ((uint32_t)min(btl[i], Tb - 1) * tile_b + bo[i]));
+#pragma unroll
+    for (int q = 0; q < kNQ; ++q) {
+      const uint8_t* src = rb + ((uint32_t)min(rtl[q], Tb - 1) * tile_r + ro[q]);
+      rv[q] = *reinterpret_cast<const u32x3*>(src);
+      if constexpr (RB == 4) rw[q] = *reinterpret_cast<const uint32_t*>(src + 12);
+    }
+  };
+  load_block(0);
+#pragma unroll 1
+  for (int b = 0; b < nblk; ++b) {
+    const int nb0 = kWxTiles * b, Tb = min(kWxTiles, NT - nb0);
+    if (b > 0) __syncthreads();  // every wave is done with the previous block's LDS
+#pragma unroll
+    for (int i = 0; i < kNB; ++i)
+      if (bdst[i] >= 0) *reinterpret_cast<u32x4_t*>(bl + bdst[i]) = bv[i];
+#pragma unroll
+    for (int q = 0; q < kNQ; ++q) {
+      if (rdst[q] < 0) continue;
+      const u32x3 dr = rv[q];
+      uint32_t r4[4];
+      if constexpr (RB == 4) {
+        r4[0] = dr.x, r4[1] = dr.y, r4[2] = dr.z, r4[3] = rw[q];
+      } else {
+        r4[0] = dr.x, r4[1] = (dr.x >> 24) | (dr.y << 8), r4[2] = (dr.y >> 16) | (dr.z << 16), r4[3] = dr.z >> 8;
+      }
+      const bool live = rgl[q] < G;
+      const uint2 d0 = decode_record(r4[0], live), d1 = decode_record(r4[1], live);
+      const uint2 d2 = decode_record(r4[2], live), d3 = decode_record(r4[3], live);
+      const u32x4_t lo = {d0.x, d0.y, d1.x, d1.y}, hi = {d2.x, d2.y, d3.x, d3.y};
+      *reinterpret_cast<u32x4_t*>(rl + rdst[q]) = lo;
+      *reinterpret_cast<u32x4_t*>(rl + rdst[q] + 4) = hi;
+    }
+    __syncthreads();
+    load_block(b + 1);  // the next block (past the last: the last again, never used)
+    issue_here();
+    f4_t acc[CT][RT];
+#pragma unroll
+    for (int ct = 0; ct < CT; ++ct)
+#pragma unroll
+      for (int rt = 0; rt < RT; ++rt) acc[ct][rt] = f4_t{0.f, 0.f, 0.f, 0.f};
+    // Compile-time LDS offsets throughout: the act groups past K hold zeros,
+    // and the staged tile slots past the block's last hold copies of it.
+#pragma unroll
+    for (int gl = 0; gl < CG; ++gl) {
+      h8_t a[RT];  // the item's act rows (resident)
+#pragma unroll
+      for (int rt = 0; rt < RT; ++rt)
+        a[rt] = *reinterpret_cast<const h8_t*>(al + wx_a_unit(gl, kb, 16 * rt + c));
+#pragma unroll
+      for (int ct = 0; ct < CT; ++ct) {
+        const int tb = CT * wave + ct;
+        const uint2 sc = *reinterpret_cast<const uint2*>(rl + ((tb * CG + gl) * 16 + c) * 2);
+        const h8_t bq = qz_operand64(bl[(tb * 4 + j) * kRS + (4 * gl + quad) * 4 + kb], sc.y, m1024, m64);
+        const float sf = __builtin_bit_cast(float, sc.x);
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt) {
+          scale_add(acc[ct][rt], sf, mfma16(a[rt], bq));
+          // the sum is formed here: left alone, the compiler sinks every
+          // scale-add to the stores and keeps all the groups' products live
+          asm volatile("" : "+v"(acc[ct][rt]));
+        }
+      }
+    }
+    // A wave's tiles past the block's last are clamped to it, as in the
+    // products: those waves store the same values to the same place again,
+    // which keeps the stores out of branches (and the registers unspilled).
+    float* yb = y + (uint64_t)row0 * H + nb0 * 16;  // uniform; the lanes add 32-bit offsets
+#pragma unroll
+    for (int ct = 0; ct < CT; ++ct) {
+      const int tb = min(CT * wave + ct, Tb - 1);
+#pragma unroll
+      for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int row = 16 * rt + 4 * kb + i;
+          if (row < rows) yb[(uint32_t)(row * H + tb * 16 + c)] = acc[ct][rt][i];
+        }
+    }
+  }
+}
+
+template <int RB, int RTMAX>
+__global__ __launch_bounds__(256, 2) void prefill_fused_kernel(const int32_t* items, const int32_t* num_items,
+                                                               const int32_t* row_slot, const uint8_t* bank,
+                                                               const uint16_t* x, uint64_t expert_bytes,
+                                                               uint64_t w13_off, uint64_t w13_meta_off,
+                                                               uint64_t w2_off, uint64_t w2_meta_off, int H, int I,
+                                                               int topk, float* y, int run_log2) {
+  constexpr int CT = kWxCT13;
+  static_assert(kWxCT2 == CT, "one block width for both products");
+  // act (the W2 A chunk) stays for the whole item; W13's staging and W2's
+  // weights and records share the rest
+  constexpr int kW13Dw = wx_a_dw(kWxCG13) + wx_r_dw(CT, kWxCG13);
+  constexpr int kW2Dw = wx_r_dw(CT, kWxCG2) + wx_b_dw(CT, kWxCG2);
+  __shared__ __attribute__((aligned(16))) uint32_t act[wx_a_dw(kWxCG2)];
+  __shared__ __attribute__((aligned(16))) uint32_t lds[kW13Dw > kW2Dw ? kW13Dw : kW2Dw];
+  __shared__ __attribute__((aligned(16))) uint32_t ring[4];  // unused (W13 keeps its weights in registers)
+  int it, bx;
+  xcd_item_tile(run_log2, it, bx);
+  if (it >= *num_items) return;
+  int e, row0, rows;
+  item_of(items, it, e, row0, rows);
+  const uint8_t* blk = bank + (uint64_t)e * expert_bytes;
+  const int G13 = H >> 5, NT13 = (2 * I) >> 4, G2 = I >> 5, NT2 = H >> 4;
+  const int rt = (rows + 15) >> 4;  // 1 .. RTMAX
+  // the act groups past K (inter < 160) are zeros for the W2 products
+  for (int d = G2 * 1024 + (int)threadIdx.x; d < kWxCG2 * 1024; d += 256) act[d] = 0u;
+  static_for<RTMAX>([&](auto i_c) {
+    constexpr int RT = decltype(i_c)::value + 1;
+    if (rt == RT) {
+      wide_item<RB, RT, kWxCG13, CT, kWideW13, true>(blk + w13_off, blk + w13_meta_off, x, row_slot, row0, rows,
+                                                     topk, G13, NT13, 0, act, 0, lds, lds + wx_a_dw(kWxCG13), ring);
+      __syncthreads();  // act complete; W13's LDS free
+      w2_resident<RB, RT, CT>(blk + w2_off, blk + w2_meta_off, act, G2, NT2, row0, rows, y, H, lds,
+                              lds + wx_r_dw(CT, kWxCG2));
+    }
   });
 }
 
@@ -1149,7 +1351,18 @@ hipError_t launch_prefill(const StageArgs& a, const uint16_t* x, const float* to
   const int wrun_log2 = n >= 64 * a.E ? 1 : 0;
   const int wround = 8 << wrun_log2;
   const int witems8 = (prefill_max_wide_items(n, a.E) + wround - 1) / wround * wround;
-  if (wide) {
+  if (wide && a.I <= kFusedMaxInter) {
+    // both products per wide item in one launch
+    const dim3 gf(1, witems8);
+    if (a.RB == 4)
+      hipLaunchKernelGGL((prefill_fused_kernel<4, kWxRT>), gf, dim3(256), 0, stream, w.witems, w.num_witems,
+                         w.row_slot, a.bank, x, a.expert_bytes, a.w13_off, a.w13_meta_off, a.w2_off,
+                         a.w2_meta_off, a.H, a.I, a.topk, w.y, wrun_log2);
+    else
+      hipLaunchKernelGGL((prefill_fused_kernel<3, kWxRT>), gf, dim3(256), 0, stream, w.witems, w.num_witems,
+                         w.row_slot, a.bank, x, a.expert_bytes, a.w13_off, a.w13_meta_off, a.w2_off,
+                         a.w2_meta_off, a.H, a.I, a.topk, w.y, wrun_log2);
+  } else if (wide) {
     // many rows per expert: wide items, 20 column tiles per workgroup
     const dim3 g13w(((2 * a.I) / 16 + 4 * kWxCT13 - 1) / (4 * kWxCT13), witems8);
     if (a.RB == 4)
@@ -1168,7 +1381,9 @@ hipError_t launch_prefill(const StageArgs& a, const uint16_t* x, const float* to
                        a.expert_bytes, a.w13_off, a.w13_meta_off, a.H, a.I, a.topk, w.act, run_log2);
   }
   if ((err = hipGetLastError()) != hipSuccess) return err;
-  if (wide && n < kW2WideItemsFrom) {
+  if (wide && a.I <= kFusedMaxInter) {
+    // W2 ran in the fused launch
+  } else if (wide && n < kW2WideItemsFrom) {
     // W2 over the 32-row work items (two row tiles at most): a smaller
     // register budget, three workgroups per CU
     const dim3 g2n(((a.H / 16) + 4 * kWxCT2Narrow - 1) / (4 * kWxCT2Narrow), items8);
