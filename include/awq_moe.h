@@ -345,13 +345,17 @@ int awq_moe_router_gemv(const uint16_t* r, const uint16_t* delta, int32_t M, int
  *   P(4BE), P(4B)  routing counts: with B = max(1, min(ceil(n/2048),
  *              65536/E)) workgroups, each slice's slots per expert i32[B][E]
  *              and a flag per slice (working state of the routing);
- *   P(2n*I)    fp16 act [n][inter] by row;  P(4n*H) fp32 y [n][hidden] by row.
+ *   P(2n*I)    fp16 act [n][inter] by row (not written when both products
+ *              run in one launch: M >= 128 and inter <= 160);
+ *   P(4n*H)    fp32 y [n][hidden] by row.
  * The rows of expert e are the contiguous range after the rows of all
  * lower experts (ascending expert order, as route_compact's segments); the
  * order of the rows inside that range is unspecified and no output depends
- * on it. The workspace needs no initialisation. Four launches on `stream`;
- * nothing is allocated and nothing synchronises, so the call can be
- * captured in a HIP graph. Calls that share a workspace must not overlap. */
+ * on it. The workspace needs no initialisation. Three or four launches on
+ * `stream` (routing, W13 and W2 (one launch for both at M >= 128 and inter
+ * <= 160), reduce; the routing takes two above 16,384 slots); nothing is
+ * allocated and nothing synchronises, so the call can be captured in a HIP
+ * graph. Calls that share a workspace must not overlap. */
 int awq_moe_prefill_workspace_bytes(const awq_moe_dims* dims, int32_t max_tokens, int32_t topk, uint64_t* out);
 int awq_moe_prefill(const awq_moe_dims* dims, const void* bank, uint64_t bank_bytes, const uint16_t* x,
                     const int32_t* topk_ids, const float* topk_w, int32_t M, int32_t topk, uint16_t* out,
