@@ -53,6 +53,8 @@ def check(got, want, what):
     (6, 96, 64, 3, 300, 4),        # the same with 4-byte records
     (24, 96, 64, 3, 128, 3),       # wide items of one or two row tiles (the unit ring) with 3 groups: clamped units
     (44, 352, 64, 4, 160, 4),      # the unit ring over 11 groups (chunks of 4, 4, 3), ~15 rows per expert
+    (32, 512, 96, 6, 256, 3),      # inter 96 in one launch: 3 act groups (2 zero groups), 12 W13 tiles
+    (16, 1024, 128, 4, 384, 4),    # inter 128 in one launch: 4 act groups, 16 W13 tiles, 4 W2 column blocks
     (16, 512, 256, 4, 160, 3),     # inter 256: the two wide kernels (no single-launch form), W2 on 32-row items
     (16, 256, 192, 8, 2048, 4),    # inter 192 at 16,384 slots: the two wide kernels, W2 on the wide items
 ])
