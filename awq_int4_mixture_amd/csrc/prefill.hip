@@ -555,9 +555,10 @@ __global__ __launch_bounds__(256) void prefill_w13_kernel(const int32_t* __restr
 }
 
 // Calls from this many tokens take the wide kernels (items of up to 64 rows,
-// 20 column tiles per workgroup); below, the per-tile kernels above (M = 128:
-// 108.1 against 95.6 us per call with the wide kernels; M = 64: 83.6 against
-// 86.0).
+// 20 column tiles per workgroup; both products in one launch at inter <=
+// 160); below, the per-tile kernels above (M = 128: 108.1 against 95.6 us per
+// call with the two wide kernels; M = 64: 83.4 against 90.0 with the one
+// launch, whose 369 items leave CUs idle).
 constexpr int kWideMinTokens = 128;
 // Slots from which W2 takes the wide items (below: the 32-row items, where
 // experts have few rows: M = 1024, 154.8 against 160.1 us per call; M =
