@@ -305,7 +305,7 @@ __global__ __launch_bounds__(1024) void route_compact_kernel(const int32_t* __re
 
 // ---------------------------------------------------------------------------
 // Shape word of the decode kernels: G = H/32 in bits 0..8, G2 = I/32 in bits
-// 9..15, topk in bits 16..21, M in bits 22..25. Together with 32-bit expert
+// 9..15, topk in bits 16..21, M in bits 22..27. Together with 32-bit expert
 // strides it keeps every argument a kernel needs before its first weight
 // load inside the 14 dwords that arrive preloaded in SGPRs, so no wave waits
 // on a kernel-argument load.
@@ -316,7 +316,7 @@ __host__ __device__ constexpr uint32_t pack_dims(int H, int I, int topk, int M) 
 __host__ __device__ __forceinline__ int dims_G(uint32_t d) { return (int)(d & 0x1FFu); }
 __host__ __device__ __forceinline__ int dims_G2(uint32_t d) { return (int)((d >> 9) & 0x7Fu); }
 __host__ __device__ __forceinline__ int dims_topk(uint32_t d) { return (int)((d >> 16) & 0x3Fu); }
-__host__ __device__ __forceinline__ int dims_M(uint32_t d) { return (int)((d >> 22) & 0xFu); }
+__host__ __device__ __forceinline__ int dims_M(uint32_t d) { return (int)((d >> 22) & 0x3Fu); }
 
 // The bank layout of one expert block, from the shape word and the record
 // size (the sections of the layout: W13 units, W13 records, W2 units, W2
@@ -392,7 +392,7 @@ __global__ __launch_bounds__(1024) void w13_swiglu_kernel(const int32_t* __restr
   const int nt = blockIdx.x * TPB + tile_i;
   const int t = threadIdx.x - tile_i * 64 * nwaves;  // lane index within the tile
   const bool status_wave = blockIdx.x == 0 && s == 0 && wave == 0;
-  const int n = topk * dims_M(dims);  // <= 256 slots: four per lane of one wave
+  const int n = topk * dims_M(dims);  // the first 256 slots four per lane of one wave, then the rest
   int sid[4];
   if (status_wave) {
 #pragma unroll
@@ -417,6 +417,10 @@ __global__ __launch_bounds__(1024) void w13_swiglu_kernel(const int32_t* __restr
     bool bad = false;
 #pragma unroll
     for (int q = 0; q < 4; ++q) bad |= lane + 64 * q < n && (sid[q] < 0 || sid[q] >= E);
+    for (int b0 = 256; b0 < n; b0 += 64) {  // more than 256 slots (calls of the indexed prefill)
+      const int id = b0 + lane < n ? ids[b0 + lane] : 0;
+      bad |= id < 0 || id >= E;
+    }
     const unsigned long long b = __ballot(bad);
     if (lane == 0) *reinterpret_cast<uint32_t*>(ws + AWQ_MOE_KWS_STATUS_OFFSET) = b ? AWQ_MOE_STATUS_BAD_ID_BIT : 0u;
   }
@@ -534,7 +538,7 @@ __global__ __launch_bounds__(1024) void w13_swiglu_pair_kernel(const int32_t* __
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
   const int tu = t >> 1, hf = t & 1;  // unit lane (4g + quad) and half
   const bool status_wave = nt == 0 && s == 0 && wave == 0;
-  const int n = topk * dims_M(dims);  // <= 256 slots: four per lane of one wave
+  const int n = topk * dims_M(dims);  // the first 256 slots four per lane of one wave, then the rest
   int sid[4];
   if (status_wave) {
 #pragma unroll
@@ -557,6 +561,10 @@ __global__ __launch_bounds__(1024) void w13_swiglu_pair_kernel(const int32_t* __
     bool bad = false;
 #pragma unroll
     for (int q = 0; q < 4; ++q) bad |= lane + 64 * q < n && (sid[q] < 0 || sid[q] >= E);
+    for (int b0 = 256; b0 < n; b0 += 64) {  // more than 256 slots (calls of the indexed prefill)
+      const int id = b0 + lane < n ? ids[b0 + lane] : 0;
+      bad |= id < 0 || id >= E;
+    }
     const unsigned long long b = __ballot(bad);
     if (lane == 0) *reinterpret_cast<uint32_t*>(ws + AWQ_MOE_KWS_STATUS_OFFSET) = b ? AWQ_MOE_STATUS_BAD_ID_BIT : 0u;
   }
@@ -1001,7 +1009,10 @@ bool w2_form_valid(int form, int H, int I, int topk, int M) {
 }
 
 void decode_table(int H, int I, int topk, int M, int RB, int* w13_form, int* w2_form) {
-  const DecodeTactic d = kDecodeTable[RB == 4 ? 1 : 0][M - 1];
+  // past the table (the indexed prefill's smallest calls): single lanes, the
+  // most slots per wave
+  const DecodeTactic d = M <= AWQ_MOE_KMAX_TOKENS ? kDecodeTable[RB == 4 ? 1 : 0][M - 1]
+                                                  : DecodeTactic{kW13Single, kW2SegMost};
   int f13 = d.w13, f2 = d.w2;
   const uint64_t grid = (uint64_t)((2 * I) / 16) * M * topk;
   // the table's lane pairs are for grids of up to two workgroups per CU (its

@@ -554,12 +554,16 @@ __global__ __launch_bounds__(256) void prefill_w13_kernel(const int32_t* __restr
   }
 }
 
-// Calls from this many tokens take the wide kernels (items of up to 64 rows,
-// 20 column tiles per workgroup; both products in one launch at inter <=
-// 160); below, the per-tile kernels above (M = 128: 108.1 against 95.6 us per
-// call with the two wide kernels; M = 64: 83.4 against 90.0 with the one
-// launch, whose 369 items leave CUs idle).
-constexpr int kWideMinTokens = 128;
+// Calls of up to kDecodeFormMaxTokens tokens and kDecodeFormMaxSlots slots
+// run the decode kernels (per slot and tile, per token and tile: no routing,
+// no row results; M = 9: 39.4 -> 19.2 us per call, 16: 45.5 -> 24.4, 32: 60.4
+// -> 38.9, 48: 73.0 -> 51.8, 64: 82.4 -> 66.3 against the per-tile kernels).
+// From kWideMinTokens the wide kernels (items of up to 64 rows, 20 column
+// tiles per workgroup; both products in one launch at inter <= 160: M = 96
+// 89.6 against 95.7 per-tile and 96.0 in the decode form; M = 128 90.2
+// against 108.1 per-tile). Between (more slots), the per-tile kernels above.
+constexpr int kDecodeFormMaxTokens = 64, kDecodeFormMaxSlots = 1024;
+constexpr int kWideMinTokens = kDecodeFormMaxTokens + 1;
 // Slots from which W2 takes the wide items (below: the 32-row items, where
 // experts have few rows: M = 1024, 154.8 against 160.1 us per call; M =
 // 4096, 404.8 against 399.0).
@@ -1342,6 +1346,17 @@ int prefill_max_wide_items(int n, int E) { return (n + kWideRows - 1) / kWideRow
 hipError_t launch_prefill(const StageArgs& a, const uint16_t* x, const float* topk_w, uint16_t* out,
                           const PrefillWs& w, hipStream_t stream) {
   const int n = a.M * a.topk;
+  if (a.M <= kDecodeFormMaxTokens && n <= kDecodeFormMaxSlots) {
+    // few tokens: the decode kernels (W13 per slot and tile, W2 per token
+    // and tile, the token's slots summed in ascending (expert, slot) order),
+    // on the workspace's first bytes in the decode layout (status word at 0,
+    // act at 256); no routing and no row results
+    uint8_t* ws0 = reinterpret_cast<uint8_t*>(w.status);
+    hipError_t e = launch_w13_swiglu(a, x, ws0, false, 0.f, kW13Table, stream);
+    if (e != hipSuccess) return e;
+    return launch_w2_reduce(a, reinterpret_cast<const uint16_t*>(ws0 + AWQ_MOE_KWS_ACT_OFFSET), topk_w, out,
+                            nullptr, kW2Table, stream);
+  }
   const int max_items = prefill_max_items(n, a.E);
   hipError_t err;
   if (n <= kRouteBatch * 1024) {

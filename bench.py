@@ -57,7 +57,7 @@ def parse():
     p.add_argument("--steps", type=int, default=200)
     p.add_argument("--warmup", type=int, default=20)
     p.add_argument("--only", default="", help="comma list of workloads: m1_cold,m1_hot,m8_pool,m8_distinct "
-                   "(any mN_pool / mN_distinct, N = 1..8),p32,p64,p128,p256,p512,p1024,p4096,stack48,stack48_gemv")
+                   "(any mN_pool / mN_distinct, N = 1..8),p9,p16,p32,p48,p64,p96,p128,p256,p512,p1024,p4096,stack48,stack48_gemv")
     p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     p.add_argument("--tactics", action="store_true",
                    help="time every kernel form of both stages for M = 1..8 and both record sizes (cold weights) "
@@ -580,7 +580,7 @@ def main():
         with torch.cuda.stream(stream):
             print(json.dumps({"tactics": tactic_sweep(abi, torch, max(args.steps // 4, 8))}), flush=True)
         return
-    prefill_wls = {"p32": 32, "p64": 64, "p128": 128, "p256": 256, "p512": 512, "p1024": 1024, "p4096": 4096}
+    prefill_wls = {"p9": 9, "p16": 16, "p32": 32, "p48": 48, "p64": 64, "p96": 96, "p128": 128, "p256": 256, "p512": 512, "p1024": 1024, "p4096": 4096}
     only = set(filter(None, args.only.split(","))) or {"m1_cold", "m1_hot", "m8_pool", "m8_distinct", "stack48",
                                                        "stack48_gemv", *prefill_wls}
     decode_wls = decode_workloads(only)

@@ -318,13 +318,17 @@ int awq_moe_router_gemv(const uint16_t* r, const uint16_t* delta, int32_t M, int
  * admission (boundary cases 8 and 9 tokens), so M <= 8 is EINVAL here and
  * M >= 9 is EINVAL in awq_moe_decode.
  *
- * Work is expert-major: each distinct expert's weights are read once per
- * call and applied to all of its rows with matrix-core products, the
- * dequantised weight kept exact as the integer (q - z) and the group scale
- * applied to the fp32 group result. Row results go to an fp32 workspace and
- * each token's rows are summed in ascending (expert id, slot) order, so the
- * output is deterministic, bit-invariant to permuting a token's (id, weight)
- * pairs, and independent of which other tokens share the call.
+ * Up to 64 tokens and 1,024 slots the call runs the decode kernels on all
+ * of its tokens (two launches: W13 + SwiGLU per slot and tile, W2 per token
+ * and tile), so it returns the bytes that awq_moe_decode gives on any split
+ * of the tokens into calls of at most 8. Beyond, work is expert-major: each
+ * distinct expert's weights are read once per call and applied to all of
+ * its rows with matrix-core products, the dequantised weight kept exact as
+ * the integer (q - z) and the group scale applied to the fp32 group result.
+ * Row results go to an fp32 workspace and each token's rows are summed in
+ * ascending (expert id, slot) order. Either way the output is
+ * deterministic, bit-invariant to permuting a token's (id, weight) pairs,
+ * and independent of which other tokens share the call.
  *
  * Arguments as in awq_moe_decode, with num_experts <= 4096 and
  * workspace_bytes >= awq_moe_prefill_workspace_bytes(dims, M, topk).
@@ -346,16 +350,19 @@ int awq_moe_router_gemv(const uint16_t* r, const uint16_t* delta, int32_t M, int
  *              65536/E)) workgroups, each slice's slots per expert i32[B][E]
  *              and a flag per slice (working state of the routing);
  *   P(2n*I)    fp16 act [n][inter] by row (not written when both products
- *              run in one launch: M >= 128 and inter <= 160);
+ *              run in one launch: M >= 65 and inter <= 160);
  *   P(4n*H)    fp32 y [n][hidden] by row.
  * The rows of expert e are the contiguous range after the rows of all
  * lower experts (ascending expert order, as route_compact's segments); the
  * order of the rows inside that range is unspecified and no output depends
- * on it. The workspace needs no initialisation. Three or four launches on
- * `stream` (routing, W13 and W2 (one launch for both at M >= 128 and inter
- * <= 160), reduce; the routing takes two above 16,384 slots); nothing is
- * allocated and nothing synchronises, so the call can be captured in a HIP
- * graph. Calls that share a workspace must not overlap. */
+ * on it. The calls that run the decode kernels use the workspace in the
+ * decode layout instead (status word at 0, act at 256) and write no routing
+ * arrays. The workspace needs no initialisation. Two launches on `stream`
+ * in the decode form; otherwise routing, W13 and W2 (one launch for both
+ * from 65 tokens at inter <= 160), reduce, the routing taking two launches
+ * above 16,384 slots; nothing is allocated and nothing synchronises, so the
+ * call can be captured in a HIP graph. Calls that share a workspace must
+ * not overlap. */
 int awq_moe_prefill_workspace_bytes(const awq_moe_dims* dims, int32_t max_tokens, int32_t topk, uint64_t* out);
 int awq_moe_prefill(const awq_moe_dims* dims, const void* bank, uint64_t bank_bytes, const uint16_t* x,
                     const int32_t* topk_ids, const float* topk_w, int32_t M, int32_t topk, uint16_t* out,

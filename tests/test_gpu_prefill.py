@@ -37,18 +37,24 @@ def check(got, want, what):
 
 
 @pytest.mark.parametrize("E,H,I,k,M,rb", [
-    (16, 256, 32, 2, 9, 3),        # the admission boundary, tiny shape
+    (16, 256, 32, 2, 9, 3),        # the admission boundary, tiny shape (decode kernels)
     (16, 256, 32, 4, 128, 4),      # wide kernels, 32 rows per expert on average: items of two or three row tiles
-    (6, 96, 64, 3, 17, 3),         # hidden 96: 6 W2 column tiles in one block; 3 W13 groups for 4 waves
-    (16, 512, 2048, 10, 40, 3),    # inter 2048: 256 W13 column tiles, 64 W2 groups
+    (6, 96, 64, 3, 17, 3),         # hidden 96 in the decode kernels
+    (16, 512, 2048, 10, 40, 3),    # inter 2048 in the decode kernels (the generic W2 kernel)
     (12, 128, 96, 1, 33, 4),       # top-k 1
+    (64, 2560, 160, 10, 64, 3),    # rank shape with 64 experts at the decode kernels' last token count
+    (64, 2560, 160, 10, 65, 4),    # ... and one token more: the wide kernels in one launch
     (64, 2560, 160, 10, 127, 3),   # rank shape with 64 experts, ~20 rows each
     (4, 8192, 32, 2, 9, 3),        # hidden 8192: 256 W13 groups, 64 per wave
+    (32, 256, 64, 32, 40, 3),      # top-k 32, 1,280 slots: the per-tile kernels (more slots than the decode form)
+    (64, 2560, 160, 20, 60, 4),    # the per-tile kernels at the rank shape, 1,200 slots
+    (32, 512, 2048, 17, 64, 3),    # the per-tile kernels with inter 2048, 1,088 slots
+    (96, 256, 32, 24, 48, 3),      # 1,152 slots over 96 experts: per-tile items of one to three rows
     (16, 256, 32, 2, 4096, 3),     # the largest M: 8192 slots, ~512 rows per expert
     (16, 352, 64, 4, 600, 4),      # wide kernels: 11 groups (W13 chunks of 4, 4, 3), ~150 rows per expert
     (40, 2560, 160, 10, 512, 3),   # wide kernels at the rank shape, ~128 rows per expert: 64-row items
     (8, 8192, 32, 2, 520, 3),      # wide kernels, hidden 8192: 64 W13 chunks, ~130 rows per expert
-    (4, 8192, 2048, 4, 9, 3),      # hidden 8192 with inter 2048 (the maxima together), single-tile W13
+    (4, 8192, 2048, 4, 9, 3),      # hidden 8192 with inter 2048 (the maxima together), decode kernels
     (6, 96, 64, 3, 300, 3),        # wide items with 3 groups: one chunk, shorter than the weight ring
     (6, 96, 64, 3, 300, 4),        # the same with 4-byte records
     (24, 96, 64, 3, 128, 3),       # wide items of one or two row tiles (the unit ring) with 3 groups: clamped units
@@ -135,11 +141,12 @@ def test_prefill_rank_shape_full_bank(rb, M):
     check(run_prefill(dims, bank, x, ids, w), R.moe_stage(x, ids, w, 512, bi.expert), f"prefill rank M={M} rb={rb}")
 
 
-def test_prefill_invalid_and_duplicate_ids():
+@pytest.mark.parametrize("M", [20, 130])  # the decode kernels, the wide kernels (routed)
+def test_prefill_invalid_and_duplicate_ids(M):
     """Ids outside [0, E) set status bit 0 and contribute nothing; a token
     may route to one expert twice (two rows); a token with no valid id gives
     an all-zero row."""
-    E, H, I, k, M = 16, 256, 32, 4, 20
+    E, H, I, k = 16, 256, 32, 4
     dims, bank, bi = bank_case(62, E, H, I, 3)
     rng = inputs.call_rng(63, 0)
     x = inputs.activations(rng, M, H)
@@ -159,19 +166,21 @@ def test_prefill_invalid_and_duplicate_ids():
     assert int(ws[:4].view(torch.int32).cpu()[0]) == 0
 
 
-def test_prefill_bit_exact_invariants():
+@pytest.mark.parametrize("E,k,M,Msub", [(24, 6, 40, 9),      # the decode kernels
+                                       (64, 32, 40, 36),    # the per-tile kernels (1,280 and 1,152 slots)
+                                       (24, 6, 200, 130)])  # the wide kernels (one launch at inter 64)
+def test_prefill_bit_exact_invariants(E, k, M, Msub):
     """Each token's result depends only on its own (id, weight) pairs: two
     calls give identical bytes; permuting a token's pairs gives identical
     bytes (ascending (expert, slot) summation); a token gives identical bytes
-    inside a 9-token call and inside a 40-token call with other tokens
-    (a row's matrix-core result does not depend on the rows sharing its
-    tile); router weights scaled by 2 give exactly twice the output."""
-    E, H, I, k = 24, 512, 64, 6
+    inside a call of its first Msub tokens and inside the M-token call (a
+    row's matrix-core result does not depend on the rows sharing its tile);
+    router weights scaled by 2 give exactly twice the output."""
+    H, I = 512, 64
     dims, bank, bi = bank_case(64, E, H, I, 3)
-    rng = inputs.call_rng(65, 0)
-    M = 40
+    rng = inputs.call_rng(65, M)
     x = inputs.activations(rng, M, H)
-    ids = inputs.ids_shared_pool(rng, M, k, E, frac=0.3)
+    ids = inputs.ids_shared_pool(rng, M, k, E, frac=0.3) if k < E // 2 else inputs.ids_distinct(rng, M, k, E)
     w = inputs.router_weights(rng, M, k)
     a = run_prefill(dims, bank, x, ids, w)
     b = run_prefill(dims, bank, x, ids, w)
@@ -181,33 +190,53 @@ def test_prefill_bit_exact_invariants():
     w_p = np.take_along_axis(w, perm, 1)
     c = run_prefill(dims, bank, x, ids_p, w_p)
     assert a.tobytes() == c.tobytes()
-    sub = run_prefill(dims, bank, x[:9], ids[:9], w[:9])
-    assert sub.tobytes() == a[:9].tobytes()
+    sub = run_prefill(dims, bank, x[:Msub], ids[:Msub], w[:Msub])
+    assert sub.tobytes() == a[:Msub].tobytes()
     d = run_prefill(dims, bank, x, ids, (w * 2).astype(np.float32))
     mag = np.abs(a.astype(np.float64))
     normal = (mag >= 2.0 ** -14) & (mag < 3e4)  # doubling is exact there, subnormals excluded
     assert np.array_equal(d[normal].astype(np.float64), 2.0 * a[normal].astype(np.float64))
-    check(a, R.moe_stage(x, ids, w, E, bi.expert), "prefill invariants case")
+    check(a, R.moe_stage(x, ids, w, E, bi.expert), f"prefill invariants M={M} k={k}")
 
 
-def test_prefill_close_to_decode():
-    """The prefill and decode paths compute the same stage: 16 tokens in one
-    prefill call against two 8-token decode calls, within the gate."""
+def test_prefill_decode_form_equals_decode_calls():
+    """Up to 64 tokens (and 1,024 slots) the prefill runs the decode kernels
+    on the whole call; each token's work is its own, so 24 tokens in one
+    prefill call give the same bytes as three 8-token decode calls."""
     H, I = 2560, 160
     dims, bank, bi = bank_case(7, 128, H, I, 3)
     rng = inputs.call_rng(66, 0)
-    x = inputs.activations(rng, 16, H)
-    ids = inputs.ids_shared_pool(rng, 16, 10, 128)
-    w = inputs.router_weights(rng, 16, 10)
+    x = inputs.activations(rng, 24, H)
+    ids = inputs.ids_shared_pool(rng, 24, 10, 128)
+    w = inputs.router_weights(rng, 24, 10)
     p = run_prefill(dims, bank, x, ids, w)
     d = np.concatenate([f16_to_np(abi.awq_moe_decode(dims, bank, to_dev(x[h:h + 8]), to_dev(ids[h:h + 8]),
-                                                     to_dev(w[h:h + 8]))) for h in (0, 8)])
+                                                     to_dev(w[h:h + 8]))) for h in (0, 8, 16)])
+    torch.cuda.synchronize()
+    assert p.tobytes() == d.tobytes()
+    check(p, R.moe_stage(x, ids, w, 128, bi.expert), "prefill decode form")
+
+
+def test_prefill_close_to_decode():
+    """The matrix-core path and the decode path compute the same stage: 96
+    tokens in one prefill call (the wide kernels) against twelve 8-token
+    decode calls, within the gate."""
+    H, I = 2560, 160
+    dims, bank, bi = bank_case(7, 128, H, I, 3)
+    rng = inputs.call_rng(66, 1)
+    x = inputs.activations(rng, 96, H)
+    ids = inputs.ids_shared_pool(rng, 96, 10, 128)
+    w = inputs.router_weights(rng, 96, 10)
+    p = run_prefill(dims, bank, x, ids, w)
+    d = np.concatenate([f16_to_np(abi.awq_moe_decode(dims, bank, to_dev(x[h:h + 8]), to_dev(ids[h:h + 8]),
+                                                     to_dev(w[h:h + 8]))) for h in range(0, 96, 8)])
     torch.cuda.synchronize()
     check(p, d.astype(np.float64), "prefill vs decode")
 
 
-def test_prefill_graph_capture_replays_match_eager():
-    E, H, I, k, M = 32, 256, 64, 4, 64
+@pytest.mark.parametrize("M", [64, 130])  # the decode kernels, the wide kernels
+def test_prefill_graph_capture_replays_match_eager(M):
+    E, H, I, k = 32, 256, 64, 4
     dims, bank, bi = bank_case(67, E, H, I, 4)
     rng = inputs.call_rng(68, 0)
     x = to_dev(inputs.activations(rng, M, H))
@@ -236,7 +265,7 @@ def _pad256(b):
 
 
 @pytest.mark.parametrize("E,k,M,hot", [(16, 4, 128, False), (512, 10, 128, False), (8, 2, 300, True),
-                                       (64, 10, 9, False),
+                                       (64, 10, 65, False),  # the smallest routed call
                                        (4096, 32, 4096, False)])  # the admitted maxima: 131,072 slots
 def test_prefill_routing_arrays(E, k, M, hot):
     """The routing arrays in the workspace (layout as documented in the

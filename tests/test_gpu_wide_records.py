@@ -12,8 +12,9 @@ records:
     one workgroup per CU) and single lanes (M = 8);
   * decode W2 + reduction in both forms: slot segments (inter 160) and the
     generic kernel (inter 2048);
-  * prefill: the per-tile kernels (M < 128) and the wide kernels (from 128
-    tokens) with both forms of the W13 weight ring, and W2;
+  * prefill: the decode kernels (up to 64 tokens), the per-tile kernels
+    (more than 1,024 slots at up to 64 tokens) and the wide kernels with
+    both forms of the W13 weight ring;
   * 3-byte and 4-byte records (byte-identical outputs).
 
 Two input families:
@@ -178,24 +179,24 @@ def test_w2_stage_scales_near_fp16_max_on_given_act(rb, M):
 
 
 @pytest.mark.parametrize("family", ["wide", "xmax"])
-@pytest.mark.parametrize("M", [40, 128, 300])
+@pytest.mark.parametrize("M,k", [(40, 10), (40, 30), (128, 10), (300, 10)])
 @pytest.mark.parametrize("rb", [3, 4])
-def test_prefill_wide_records(rb, M, family):
-    """Indexed prefill with wide records: the per-tile kernels at M = 40
-    (about 6 rows per expert), the wide kernels at M = 128 (about 20 rows:
-    items of one or two row tiles, whose W13 weights take the unit ring) and
-    M = 300 (about 47 rows: three row tiles, the per-group ring), the
-    matrix-core B operand (q - z) over zeros 0..255, and W2 with
-    signed/zero/subnormal scales."""
-    E, k = 64, 10
+def test_prefill_wide_records(rb, M, k, family):
+    """Indexed prefill with wide records: the decode kernels at M = 40, the
+    per-tile kernels at M = 40 with top-k 30 (1,200 slots, about 19 rows per
+    expert), the wide kernels at M = 128 (about 20 rows: items of one or two
+    row tiles, whose W13 weights take the unit ring) and M = 300 (about 47
+    rows: three row tiles, the per-group ring), the matrix-core B operand
+    (q - z) over zeros 0..255, and W2 with signed/zero/subnormal scales."""
+    E = 64
     dims, bank, bi = bank_case(301, E, H, I, rb, wide=FAMILIES[family])
-    rng = inputs.call_rng(308, M + len(family))
+    rng = inputs.call_rng(308, M + len(family) + (1000 * k if k != 10 else 0))
     x = draw_x(family, rng, M, H)
     ids = inputs.ids_distinct(rng, M, k, E)
     w = inputs.router_weights(rng, M, k)
-    say("prefill wide records", family, "M", M, "rb", rb)
+    say("prefill wide records", family, "M", M, "k", k, "rb", rb)
     out_ref = R.moe_stage(x, ids, w, E, bi.expert)
     assert np.abs(out_ref).max() < FINITE_MARGIN
     out = abi.awq_moe_prefill(dims, bank, to_dev(x), to_dev(ids), to_dev(w))
     torch.cuda.synchronize()
-    check(f16_to_np(out), out_ref, f"prefill {family} M={M} rb={rb}")
+    check(f16_to_np(out), out_ref, f"prefill {family} M={M} k={k} rb={rb}")
