@@ -50,6 +50,8 @@ def check(got, want, what):
     (64, 2560, 160, 20, 60, 4),    # the per-tile kernels at the rank shape, 1,200 slots
     (32, 512, 2048, 17, 64, 3),    # the per-tile kernels with inter 2048, 1,088 slots
     (96, 256, 32, 24, 48, 3),      # 1,152 slots over 96 experts: per-tile items of one to three rows
+    (64, 256, 32, 32, 32, 4),      # top-k 32 at 1,024 slots: the decode kernels' largest call (status over 1,024 ids)
+    (4096, 256, 32, 8, 16, 3),     # 4096 experts in the decode kernels
     (16, 256, 32, 2, 4096, 3),     # the largest M: 8192 slots, ~512 rows per expert
     (16, 352, 64, 4, 600, 4),      # wide kernels: 11 groups (W13 chunks of 4, 4, 3), ~150 rows per expert
     (40, 2560, 160, 10, 512, 3),   # wide kernels at the rank shape, ~128 rows per expert: 64-row items
