@@ -3,17 +3,19 @@
 // Qwen3.8 AWQ active grouped decode", Tests: indexed prefill is admitted
 // from 9 tokens, disjoint from the grouped decode's 1..8).
 //
-// With many tokens an expert serves several rows, so the work is expert-major
-// and the products run on the matrix cores:
+// Calls of up to 64 tokens and 1,024 slots run the decode kernels on all of
+// their tokens (launch_prefill). With more, an expert serves several rows,
+// so the work is expert-major and the products run on the matrix cores:
 //
 //  * route (one workgroup up to 16,384 slots, else two launches over slices
 //    of the slots): counts per expert, the experts' rows laid out in
 //    ascending expert order, each expert's rows cut into work items of at
 //    most 32 rows and wide items of at most 64;
-//  * below 128 tokens, W13 + SwiGLU per (work item, 16-column tile) and W2
-//    per (work item, 8 column tiles); from 128 tokens the wide kernels, per
-//    (wide item, 20 column tiles) for W13 and per (work item or wide item,
-//    16 or 20 column tiles) for W2. Each group of 32 K
+//  * up to 64 tokens, W13 + SwiGLU per (work item, 16-column tile) and W2
+//    per (work item, 8 column tiles); from 65 tokens the wide kernels: both
+//    products of a wide item in one workgroup at inter <= 160, else W13 per
+//    (wide item, 20 column tiles) and W2 per (work item or wide item, 16 or
+//    20 column tiles). Each group of 32 K
 //    values is one v_mfma_f32_16x16x32_f16 whose B operand is the exact
 //    integer (q - z) in fp16 (|q - z| <= 255), so the dequantised weight is
 //    never rounded; the group's fp32 result is scaled by s and accumulated
