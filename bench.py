@@ -255,7 +255,7 @@ def measure(abi, torch, wl: Workload, steps, warmup):
 
 
 def measure_prefill(abi, torch, dims, bank, M, steps, warmup, per_expert, calls=8):
-    """Indexed prefill of M tokens (awq_moe_prefill, four launches) on the
+    """Indexed prefill of M tokens (awq_moe_prefill, two to five launches) on the
     512-expert rank layer: each token picks 10 distinct experts uniformly.
     One graph replays `calls` calls with different inputs; reported per call."""
     dev = bank.device
