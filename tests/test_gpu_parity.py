@@ -456,6 +456,32 @@ def test_every_decode_form_against_oracle(rb, M):
     assert run_decode(dims, bank, x, ids, w).view(np.uint16).tolist() == bits[table]
 
 
+@pytest.mark.parametrize("f13", ["single", "single_two_tiles"])
+@pytest.mark.parametrize("rb", [3, 4])
+def test_w13_plain_and_non_temporal_weight_loads_agree(f13, rb):
+    """W13 reads its weights with non-temporal loads when its whole grid fits
+    the chip at once and with plain loads otherwise. Eight tokens at top-k 32
+    (20 tiles x 256 slots x 5 waves, past 8192 waves) take plain loads; the
+    same tokens in calls of two (5 x 1,280 waves) take non-temporal ones.
+    Rows are independent, so both give the same bytes, within the gate of
+    the oracle."""
+    form = abi.W13_SINGLE if f13 == "single" else abi.W13_SINGLE_TWO_TILES
+    E, (H, I), k, M = 64, RANK, 32, 8
+    dims, bank, bi = bank_case(90 + rb, E, H, I, rb)
+    rng = inputs.call_rng(91, rb)
+    x = inputs.activations(rng, M, H)
+    ids = inputs.ids_distinct(rng, M, k, E)
+    w = inputs.router_weights(rng, M, k)
+    say("w13 plain vs non-temporal loads", f13, rb)
+    full = abi.awq_moe_decode_forms(dims, bank, to_dev(x), to_dev(ids), to_dev(w), form, abi.W2_SEG_MOST)
+    parts = [abi.awq_moe_decode_forms(dims, bank, to_dev(x[i:i + 2]), to_dev(ids[i:i + 2]), to_dev(w[i:i + 2]),
+                                      form, abi.W2_SEG_MOST) for i in range(0, M, 2)]
+    torch.cuda.synchronize()
+    got = f16_to_np(full)
+    assert got.view(np.uint16).tolist() == np.concatenate([f16_to_np(p) for p in parts]).view(np.uint16).tolist()
+    check(got, R.moe_stage(x, ids, w, E, bi.expert), f"w13 {f13} rb={rb} top-k 32")
+
+
 def test_forms_on_other_shapes_and_stage_split():
     """Forms at shapes that change their geometry (hidden 96: lanes past L;
     inter 32: 16 slots per wave; hidden 4096: 16-wave two-tile blocks), and
