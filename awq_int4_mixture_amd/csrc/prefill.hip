@@ -41,6 +41,16 @@ namespace awq_moe {
 typedef float f4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 
+// 16 bytes of the bank; NT marks the load non-temporal (data that no other
+// workgroup of the launch will read soon, so the caches need not keep it).
+template <bool NT>
+__device__ __forceinline__ u32x4_t load16(const uint8_t* p) {
+  if constexpr (NT)
+    return __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
+  else
+    return *reinterpret_cast<const u32x4_t*>(p);
+}
+
 constexpr int kItemRows = 32;
 constexpr int kWideRows = 64;  // rows of a wide work item (the many-rows W13 kernel), a multiple of 16
 constexpr int kRouteBatch = 16;           // slot ids per thread in flight in the routing kernels
@@ -709,8 +719,8 @@ __device__ __forceinline__ int wx_a_unit(int g, int kb, int row) {
 // One wide item of one column block. K = 32 G; the A rows are K fp16 long.
 // TO_LDS (W13 only): act goes to LDS at `out` in the A layout of a W2 chunk
 // (every row of the item's row tiles, padding rows included) instead of to
-// global memory.
-template <int RB, int RT, int CG, int CT, int STAGE, bool TO_LDS = false>
+// global memory. NTW: the whole-unit ring's weight loads are non-temporal.
+template <int RB, int RT, int CG, int CT, int STAGE, bool TO_LDS = false, bool NTW = false>
 __device__ __forceinline__ void wide_item(const uint8_t* units, const uint8_t* recs, const uint16_t* a_src,
                                           const int32_t* row_slot, int row0, int rows, int topk, int G, int NT,
                                           int nb0, void* out, int out_stride, uint32_t* al, uint32_t* rl,
@@ -789,7 +799,7 @@ __device__ __forceinline__ void wide_item(const uint8_t* units, const uint8_t* r
   auto ld_ru = [&](int ct, int g0) {  // group min(g0 + kb, G - 1) as a uniform part plus a lane part
     const int gu = min(g0, G - 1);
     const uint32_t lo = 64u * (uint32_t)min(kb, G - 1 - gu) + bor;
-    return *reinterpret_cast<const u32x4_t*>(tbase[ct] + 64 * gu + lo);
+    return load16<NTW>(tbase[ct] + 64 * gu + lo);
   };
   auto ld_a = [&](int i, int g0) { return *reinterpret_cast<const u32x4_t*>(ab + 64 * min(g0 + agl[i], G - 1) + ao[i]); };
   auto rsrc = [&](int q, int g0) { return recs + 16 * RB * min(g0 + rgl[q], G - 1) + ro[q]; };
@@ -985,7 +995,7 @@ __global__ __launch_bounds__(256, RTMAX <= 2 ? 3 : 2) void prefill_wide_kernel(c
 // ---------------------------------------------------------------------------
 constexpr int kFusedMaxInter = 32 * kWxCG2;  // 160
 
-template <int RB, int RT, int CT>
+template <int RB, int RT, int CT, bool NTW>
 __device__ __forceinline__ void w2_resident(const uint8_t* units, const uint8_t* recs, const uint32_t* al, int G,
                                             int NT, int row0, int rows, float* y, int H, uint32_t* rl,
                                             uint32_t* bl) {
@@ -1037,7 +1047,7 @@ __device__ __forceinline__ void w2_resident(const uint8_t* units, const uint8_t*
     const uint8_t* rb = recs + (uint64_t)nb0 * tile_r;
 #pragma unroll
     for (int i = 0; i < kNB; ++i)
-      bv[i] = *reinterpret_cast<const u32x4_t*>(ub + ((uint32_t)min(btl[i], Tb - 1) * tile_b + bo[i]));
+      bv[i] = load16<NTW>(ub + ((uint32_t)min(btl[i], Tb - 1) * tile_b + bo[i]));
 #pragma unroll
     for (int q = 0; q < kNQ; ++q) {
       const uint8_t* src = rb + ((uint32_t)min(rtl[q], Tb - 1) * tile_r + ro[q]);
@@ -1121,7 +1131,9 @@ __device__ __forceinline__ void w2_resident(const uint8_t* units, const uint8_t*
   }
 }
 
-template <int RB, int RTMAX>
+// NT13 / NT2: non-temporal weight loads in the W13 ring (items of one or two
+// row tiles) and in W2.
+template <int RB, int RTMAX, bool NT13, bool NT2>
 __global__ __launch_bounds__(256, 2) void prefill_fused_kernel(const int32_t* items, const int32_t* num_items,
                                                                const int32_t* row_slot, const uint8_t* bank,
                                                                const uint16_t* x, uint64_t expert_bytes,
@@ -1143,18 +1155,19 @@ __global__ __launch_bounds__(256, 2) void prefill_fused_kernel(const int32_t* it
   int e, row0, rows;
   item_of(items, it, e, row0, rows);
   const uint8_t* blk = bank + (uint64_t)e * expert_bytes;
-  const int G13 = H >> 5, NT13 = (2 * I) >> 4, G2 = I >> 5, NT2 = H >> 4;
+  const int G13 = H >> 5, NT13c = (2 * I) >> 4, G2 = I >> 5, NT2c = H >> 4;  // groups and column tiles
   const int rt = (rows + 15) >> 4;  // 1 .. RTMAX
   // the act groups past K (inter < 160) are zeros for the W2 products
   for (int d = G2 * 1024 + (int)threadIdx.x; d < kWxCG2 * 1024; d += 256) act[d] = 0u;
   static_for<RTMAX>([&](auto i_c) {
     constexpr int RT = decltype(i_c)::value + 1;
     if (rt == RT) {
-      wide_item<RB, RT, kWxCG13, CT, kWideW13, true>(blk + w13_off, blk + w13_meta_off, x, row_slot, row0, rows,
-                                                     topk, G13, NT13, 0, act, 0, lds, lds + wx_a_dw(kWxCG13), ring);
+      wide_item<RB, RT, kWxCG13, CT, kWideW13, true, NT13>(blk + w13_off, blk + w13_meta_off, x, row_slot, row0,
+                                                           rows, topk, G13, NT13c, 0, act, 0, lds,
+                                                           lds + wx_a_dw(kWxCG13), ring);
       __syncthreads();  // act complete; W13's LDS free
-      w2_resident<RB, RT, CT>(blk + w2_off, blk + w2_meta_off, act, G2, NT2, row0, rows, y, H, lds,
-                              lds + wx_r_dw(CT, kWxCG2));
+      w2_resident<RB, RT, CT, NT2>(blk + w2_off, blk + w2_meta_off, act, G2, NT2c, row0, rows, y, H, lds,
+                                   lds + wx_r_dw(CT, kWxCG2));
     }
   });
 }
@@ -1345,6 +1358,34 @@ __global__ __launch_bounds__(256) void prefill_reduce_kernel(const int32_t* __re
 int prefill_max_items(int n, int E) { return (n + kItemRows - 1) / kItemRows + (E < n ? E : n); }
 int prefill_max_wide_items(int n, int E) { return (n + kWideRows - 1) / kWideRows + (E < n ? E : n); }
 
+template <int RB, bool NT13, bool NT2>
+static void launch_fused(const StageArgs& a, const uint16_t* x, const PrefillWs& w, int witems8, int wrun_log2,
+                         hipStream_t stream) {
+  hipLaunchKernelGGL((prefill_fused_kernel<RB, kWxRT, NT13, NT2>), dim3(1, witems8), dim3(256), 0, stream, w.witems,
+                     w.num_witems, w.row_slot, a.bank, x, a.expert_bytes, a.w13_off, a.w13_meta_off, a.w2_off,
+                     a.w2_meta_off, a.H, a.I, a.topk, w.y, wrun_log2);
+}
+
+// Non-temporal weight loads in the one-launch kernel, by the mean rows per
+// expert r = n / E (n slots): W13's whole-unit ring when r <= 32 (an
+// expert then mostly has one item, and no other workgroup reads its
+// weights), W2 when r >= 16. Per call at the rank layer (µs, one run of
+// each under the kernel trace; plain / W13 / W2 / both): 128 tokens
+// (r = 2.5) 91.9 / 89.4 / 93.1 / 92.2, 1024 (r = 20) 142.1 / 139.8 / 140.4 /
+// 137.7, 4096 (r = 80) 359.7 / 362.3 / 354.1 / 355.2.
+template <int RB>
+static void launch_fused_rb(const StageArgs& a, const uint16_t* x, const PrefillWs& w, int witems8, int wrun_log2,
+                            hipStream_t stream) {
+  const uint64_t n = (uint64_t)a.M * a.topk;
+  const bool nt13 = n <= 32ull * a.E, nt2 = n >= 16ull * a.E;
+  if (nt13 && nt2)
+    launch_fused<RB, true, true>(a, x, w, witems8, wrun_log2, stream);
+  else if (nt13)
+    launch_fused<RB, true, false>(a, x, w, witems8, wrun_log2, stream);
+  else
+    launch_fused<RB, false, true>(a, x, w, witems8, wrun_log2, stream);
+}
+
 hipError_t launch_prefill(const StageArgs& a, const uint16_t* x, const float* topk_w, uint16_t* out,
                           const PrefillWs& w, hipStream_t stream) {
   const int n = a.M * a.topk;
@@ -1386,15 +1427,10 @@ hipError_t launch_prefill(const StageArgs& a, const uint16_t* x, const float* to
   const int witems8 = (prefill_max_wide_items(n, a.E) + wround - 1) / wround * wround;
   if (wide && a.I <= kFusedMaxInter) {
     // both products per wide item in one launch
-    const dim3 gf(1, witems8);
     if (a.RB == 4)
-      hipLaunchKernelGGL((prefill_fused_kernel<4, kWxRT>), gf, dim3(256), 0, stream, w.witems, w.num_witems,
-                         w.row_slot, a.bank, x, a.expert_bytes, a.w13_off, a.w13_meta_off, a.w2_off,
-                         a.w2_meta_off, a.H, a.I, a.topk, w.y, wrun_log2);
+      launch_fused_rb<4>(a, x, w, witems8, wrun_log2, stream);
     else
-      hipLaunchKernelGGL((prefill_fused_kernel<3, kWxRT>), gf, dim3(256), 0, stream, w.witems, w.num_witems,
-                         w.row_slot, a.bank, x, a.expert_bytes, a.w13_off, a.w13_meta_off, a.w2_off,
-                         a.w2_meta_off, a.H, a.I, a.topk, w.y, wrun_log2);
+      launch_fused_rb<3>(a, x, w, witems8, wrun_log2, stream);
   } else if (wide) {
     // many rows per expert: wide items, 20 column tiles per workgroup
     const dim3 g13w(((2 * a.I) / 16 + 4 * kWxCT13 - 1) / (4 * kWxCT13), witems8);
