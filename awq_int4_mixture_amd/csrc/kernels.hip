@@ -942,7 +942,23 @@ namespace {
 constexpr int kMaxDevices = 64;
 std::atomic<void*> g_scratch_ptr[kMaxDevices];
 std::mutex g_scratch_mu;
+std::atomic<int> g_resident_waves[kMaxDevices];  // 0: not asked yet
 }  // namespace
+
+// Waves the current device holds at once at 8 per SIMD (4 SIMDs per CU):
+// 8,192 on a whole MI355X, fewer on a partition of it. Asked once per device.
+static int resident_waves() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return 256 * 32;
+  int w = g_resident_waves[dev].load(std::memory_order_relaxed);
+  if (w == 0) {
+    int cus = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) cus = 256;
+    w = 32 * cus;
+    g_resident_waves[dev].store(w, std::memory_order_relaxed);
+  }
+  return w;
+}
 
 hipError_t noalloc_scratch(void** ptr) {
   int dev = 0;
@@ -1061,9 +1077,9 @@ static void launch_w13_t(const StageArgs& a, const uint16_t* x, uint8_t* w, uint
   const uint32_t dims = pack_dims(a.H, a.I, a.topk, a.M);
   const int bw = ((L + 63) / 64) * 64;  // threads per tile, single lanes
   // non-temporal weights when the whole grid can be resident at once (its
-  // waves within 256 CUs x 4 SIMDs x 8): slots that share an expert then
+  // waves within the CUs x 4 SIMDs x 8): slots that share an expert then
   // request its tiles together (the same count for two tiles per workgroup)
-  const bool nt = (uint64_t)grid.x * grid.y * (bw / 64) <= 8192;
+  const bool nt = (uint64_t)grid.x * grid.y * (bw / 64) <= (uint64_t)resident_waves();
   if (form == kW13Pair)
     hipLaunchKernelGGL((w13_swiglu_pair_kernel<RB, NORM>), grid, dim3(((2 * L + 63) / 64) * 64), 0, stream,
                        a.topk_ids, a.bank + a.w13_off, x, w, (uint32_t)a.expert_bytes, md, dims, a.E, eps);
