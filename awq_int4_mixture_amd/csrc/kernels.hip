@@ -384,10 +384,12 @@ __device__ __forceinline__ float pairs_sumsq(const uint32_t* px) {
 // token's activations are requested before that load returns, and the
 // expert's 16-column tile (all of K) right after it, so the slot's chain is
 // two memory round trips. It then writes act[s] for that tile. Slots that
-// share an expert read the same tile; the second and later reads are served
-// by L2 or the MALL (all of them request it within the same few hundred
-// nanoseconds), which measured faster than first electing one workgroup per
-// expert from the routed ids.
+// share an expert read the same tile within the same few hundred
+// nanoseconds: a later read hits the L2 when it runs on the same XCD and
+// otherwise goes to the MALL or HBM (with 8 tokens drawing from shared
+// pools, about 1.4 times the distinct bytes are fetched), which still
+// measured faster than first electing one workgroup per expert from the
+// routed ids.
 // The workspace holds the status word at offset 0 and act at offset 256.
 // Wave 0 of workgroup (0, 0) also writes the status word; its id loads are
 // issued first and consumed after the weight loads are in flight.
@@ -1009,12 +1011,13 @@ struct DecodeTactic {
   int8_t w13, w2;
 };
 // [record bytes 3, 4][M - 1]. W13 us per launch, 3-byte records (lane pairs /
-// single lanes / two tiles per workgroup): M=1 3.78 / 3.93 / 4.16,
-// M=2 4.57 / 4.50 / 4.38, M=3 5.59 / 5.15 / 5.79, M=8 9.40 / 7.89 / 8.93;
-// 4-byte records rank the same. W2 with the most slots per wave wins at
-// every M (M=1 3.60 against 3.80, M=8 5.88 against 6.47).
+// single lanes / two tiles per workgroup): M=1 3.51 / 3.61 / 3.91,
+// M=2 4.44 / 4.25 / 4.31, M=3 5.50 / 4.84 / 5.64, M=8 9.61 / 8.07 / 9.03;
+// 4-byte records rank the same except at M=2 (4.49 / 4.43 / 4.36). W2 with
+// the most slots per wave wins at every M (M=1 3.42 against 3.63, M=8 5.69
+// against 6.26).
 constexpr DecodeTactic kDecodeTable[2][AWQ_MOE_KMAX_TOKENS] = {
-    {{kW13Pair, kW2SegMost}, {kW13Single2, kW2SegMost}, {kW13Single, kW2SegMost}, {kW13Single, kW2SegMost},
+    {{kW13Pair, kW2SegMost}, {kW13Single, kW2SegMost}, {kW13Single, kW2SegMost}, {kW13Single, kW2SegMost},
      {kW13Single, kW2SegMost}, {kW13Single, kW2SegMost}, {kW13Single, kW2SegMost}, {kW13Single, kW2SegMost}},
     {{kW13Pair, kW2SegMost}, {kW13Single2, kW2SegMost}, {kW13Single, kW2SegMost}, {kW13Single, kW2SegMost},
      {kW13Single, kW2SegMost}, {kW13Single, kW2SegMost}, {kW13Single, kW2SegMost}, {kW13Single, kW2SegMost}},

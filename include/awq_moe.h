@@ -162,8 +162,10 @@ int awq_moe_route_compact(const int32_t* topk_ids, int32_t M, int32_t topk, int3
  * Launches two kernels on stream: W13 + SwiGLU with one workgroup per
  * (slot, 16-column tile), then W2 + reduction with one workgroup per
  * (token, 16-column tile) that sums the token's slots itself. Slots that
- * share an expert read its tiles at about the same moment and all but the
- * first read are served from cache, so no routing launch precedes them. */
+ * share an expert read its tiles at about the same moment, so no routing
+ * launch precedes them: a second read hits the L2 when it runs on the same
+ * XCD and otherwise goes to the MALL or HBM (with 8 tokens drawing from
+ * shared pools, W13 fetches about 1.4 times the distinct experts' bytes). */
 int awq_moe_decode(const awq_moe_dims* dims, const void* bank, uint64_t bank_bytes, const uint16_t* x,
                    const int32_t* topk_ids, const float* topk_w, int32_t M, int32_t topk,
                    uint16_t* out, void* workspace, uint64_t workspace_bytes, void* stream);
