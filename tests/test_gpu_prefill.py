@@ -201,6 +201,30 @@ def test_prefill_bit_exact_invariants(E, k, M, Msub):
     check(a, R.moe_stage(x, ids, w, E, bi.expert), f"prefill invariants M={M} k={k}")
 
 
+@pytest.mark.parametrize("rb", [3, 4])
+def test_prefill_rows_identical_across_cache_policies(rb):
+    """At the rank layer the one-launch kernel picks its weight loads' cache
+    policy from the mean rows per expert: 128 tokens (2.5 rows per expert)
+    non-temporal W13 only, 1024 tokens (20) both, 4096 tokens (80) W2 only,
+    and the items hold one, two or four row tiles. The first 128 tokens give
+    the same bytes in all three calls, and the first 1024 in the last two,
+    and 8 sampled tokens of the largest call are within the gate of the
+    oracle."""
+    E, H, I, k = 512, 2560, 160, 10
+    dims, bank, bi = bank_case(2026, E, H, I, rb)
+    rng = inputs.call_rng(2029, rb)
+    M = 4096
+    x = inputs.activations(rng, M, H)
+    ids = inputs.ids_distinct(rng, M, k, E)
+    w = inputs.router_weights(rng, M, k)
+    say("prefill rows across cache policies", rb)
+    outs = {m: run_prefill(dims, bank, x[:m], ids[:m], w[:m]) for m in (128, 1024, 4096)}
+    assert outs[128].tobytes() == outs[1024][:128].tobytes() == outs[4096][:128].tobytes()
+    assert outs[1024].tobytes() == outs[4096][:1024].tobytes()
+    sel = np.unique(np.concatenate([[0, M - 1], rng.choice(np.arange(1, M - 1), 6, replace=False)]))
+    check(outs[4096][sel], R.moe_stage(x[sel], ids[sel], w[sel], E, bi.expert), f"prefill rows across policies rb={rb}")
+
+
 def test_prefill_decode_form_equals_decode_calls():
     """Up to 64 tokens (and 1,024 slots) the prefill runs the decode kernels
     on the whole call; each token's work is its own, so 24 tokens in one
