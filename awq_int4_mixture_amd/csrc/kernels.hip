@@ -753,12 +753,13 @@ __global__ __launch_bounds__(1024) void w2_reduce_kernel(const int32_t* __restri
 }
 
 // ---------------------------------------------------------------------------
-// W2 + router-weighted reduction for I <= 256: grid (H/16 tiles, M tokens)
-// as above. A slot owns LS = 4*I/32 <= 32 adjacent lanes of a wave (lane =
+// W2 + router-weighted reduction for I <= 512: grid (H/16 tiles, M tokens)
+// as above. A slot owns LS = 4*I/32 <= 64 adjacent lanes of a wave (lane =
 // 4g + quad inside its segment), and a wave holds SPW = floor(64 / LS)
-// slots, so a token's slots take ceil(topk / SPW) waves: 4 at I = 160 and
-// top-k 10, one per SIMD of the CU (with 5 waves one SIMD runs two, and at
-// M = 1, one workgroup per CU, that SIMD sets the kernel's time).
+// slots, so a token's slots take ceil(topk / SPW) waves (at most 16): 4 at
+// I = 160 and top-k 10, one per SIMD of the CU (with 5 waves one SIMD runs
+// two, and at M = 1, one workgroup per CU, that SIMD sets the kernel's
+// time); one slot per wave from I = 288 (LS > 32).
 // The wave's ids and router weights arrive as scalar loads; the token's
 // ids (for the ranking) and the activations are requested before they
 // return, and every load is unconditional with clamped indexes, so the
@@ -783,11 +784,15 @@ __global__ __launch_bounds__(1024) void w2_reduce_seg_kernel(const int32_t* __re
                                                              const float* __restrict__ topk_w,
                                                              uint16_t* __restrict__ out, uint32_t dims, int E,
                                                              const uint16_t* __restrict__ resid) {
-  __shared__ __attribute__((aligned(16))) float red[AWQ_MOE_KMAX_TOPK * 8 * 16];  // [slot][g][16]
+  // [slot][g][16]: up to 8 groups of 32 slots, or with one slot per wave
+  // (at most 16 waves) up to 16 groups of 16 slots
+  constexpr int kG2Max = SPW == 1 ? 16 : 8;
+  constexpr int kSlots = SPW == 1 ? 16 : AWQ_MOE_KMAX_TOPK;
+  __shared__ __attribute__((aligned(16))) float red[kSlots * kG2Max * 16];
   __shared__ __attribute__((aligned(16))) float ys[AWQ_MOE_KMAX_TOPK * 16];       // [rank][16]
   __shared__ float wr[AWQ_MOE_KMAX_TOPK];                                         // rank -> router weight
   __shared__ int nvalid_s;
-  const int G2 = dims_G2(dims), LS = 4 * G2;  // LS <= 32, SPW * LS <= 64
+  const int G2 = dims_G2(dims), LS = 4 * G2;  // SPW * LS <= 64
   const int H = 32 * dims_G(dims), I = 32 * G2, topk = dims_topk(dims);
   const int T2 = H >> 4;
   const int nt = (T2 & 7) ? (int)blockIdx.x : (int)((blockIdx.x & 7) * (T2 >> 3) + (blockIdx.x >> 3));
@@ -814,7 +819,10 @@ __global__ __launch_bounds__(1024) void w2_reduce_seg_kernel(const int32_t* __re
   int kk = 0;
 #pragma unroll
   for (int k = 1; k <= SPW; ++k) kk += lane >= k * LS;
-  const int tl = lane - kk * LS;  // in [0, LS) for every lane
+  // in [0, LS) for every lane: a lane past the segments is clamped to the
+  // segment's last, so that its (unused) loads stay inside the tile, the
+  // expert's records and the slot's act row also when SPW * LS + LS < 64
+  const int tl = min(lane - kk * LS, LS - 1);
   const int slot = s0 + kk;
   const bool lane_on = kk < SPW && slot < topk;
   const int slotc = slot < topk ? slot : topk - 1;
@@ -857,7 +865,7 @@ __global__ __launch_bounds__(1024) void w2_reduce_seg_kernel(const int32_t* __re
   av.px[4] = quad_bcast<1>(araw.x); av.px[5] = quad_bcast<1>(araw.y); av.px[6] = quad_bcast<1>(araw.z); av.px[7] = quad_bcast<1>(araw.w);
   av.px[8] = quad_bcast<2>(araw.x); av.px[9] = quad_bcast<2>(araw.y); av.px[10] = quad_bcast<2>(araw.z); av.px[11] = quad_bcast<2>(araw.w);
   av.px[12] = quad_bcast<3>(araw.x); av.px[13] = quad_bcast<3>(araw.y); av.px[14] = quad_bcast<3>(araw.z); av.px[15] = quad_bcast<3>(araw.w);
-  float* rrow = red + (slotc * 8) * 16 + 4 * quad;  // + 16 g: this lane's four columns in group g
+  float* rrow = red + (slotc * kG2Max) * 16 + 4 * quad;  // + 16 g: this lane's four columns in group g
   if (live) {
     float S, Cs;
     group_sums(av, S, Cs);
@@ -1024,7 +1032,7 @@ constexpr DecodeTactic kDecodeTable[2][AWQ_MOE_KMAX_TOKENS] = {
 };
 
 // The slot-segment W2 kernel's instantiated slots-per-wave values, descending.
-constexpr int kSpwChoices[] = {16, 8, 5, 4, 3, 2};
+constexpr int kSpwChoices[] = {16, 8, 5, 4, 3, 2, 1};
 
 static int w2_spw(int form, int I) {
   const int cap = 64 / (I / 8);  // slots that fit a wave at I/8 lanes each
@@ -1049,11 +1057,15 @@ bool w13_form_valid(int form, int H, int I, int topk, int M) {
   }
 }
 
+// The slot-segment kernel runs a form when the form's slots per wave fit the
+// inter size and the token's slots fit 16 waves; otherwise the generic
+// kernel (inter > 512, or one slot per wave with top-k above 16) serves the
+// shape with its one form.
+static bool w2_seg_fits(int spw, int topk) { return spw > 0 && (topk + spw - 1) / spw <= 16; }
+
 bool w2_form_valid(int form, int H, int I, int topk, int M) {
-  if (I > 256) return form == kW2SegMost;  // the generic kernel (one form)
-  if (form == kW2SegMost) return w2_spw(form, I) > 0;
-  if (form == kW2SegFewer) return w2_spw(form, I) > 0;
-  return false;
+  if (form != kW2SegMost && form != kW2SegFewer) return false;
+  return w2_seg_fits(w2_spw(form, I), topk) || form == kW2SegMost;
 }
 
 void decode_table(int H, int I, int topk, int M, int RB, int* w13_form, int* w2_form) {
@@ -1152,19 +1164,20 @@ static void launch_w2_seg_rb(const StageArgs& a, const uint16_t* act, const floa
   else if (spw == 5) launch_w2_seg<RB, 5, RES>(a, act, topk_w, out, resid, stream);
   else if (spw == 4) launch_w2_seg<RB, 4, RES>(a, act, topk_w, out, resid, stream);
   else if (spw == 3) launch_w2_seg<RB, 3, RES>(a, act, topk_w, out, resid, stream);
-  else launch_w2_seg<RB, 2, RES>(a, act, topk_w, out, resid, stream);
+  else if (spw == 2) launch_w2_seg<RB, 2, RES>(a, act, topk_w, out, resid, stream);
+  else launch_w2_seg<RB, 1, RES>(a, act, topk_w, out, resid, stream);
 }
 
 template <bool RES>
 static hipError_t launch_w2_res(const StageArgs& a, const uint16_t* act, const float* topk_w, uint16_t* out,
                                 const uint16_t* resid, int form, hipStream_t stream) {
-  if (a.I <= 256) {
+  const int spw = w2_spw(form, a.I);
+  if (w2_seg_fits(spw, a.topk)) {
     // the slot-segment kernel derives the expert geometry from the shape word
     const ExpertGeometry g = a.RB == 4 ? expert_geometry<4>(pack_dims(a.H, a.I, a.topk, a.M))
                                        : expert_geometry<3>(pack_dims(a.H, a.I, a.topk, a.M));
     if (g.expert_bytes != a.expert_bytes || g.w2_off != a.w2_off || g.w2_meta_delta != a.w2_meta_off - a.w2_off)
       return hipErrorInvalidValue;
-    const int spw = w2_spw(form, a.I);
     if (a.RB == 4)
       launch_w2_seg_rb<4, RES>(a, act, topk_w, out, resid, spw, stream);
     else

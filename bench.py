@@ -449,13 +449,16 @@ def stage_kernel_names(abi, M, rb, H=H, I=I, topk=K_TOP, E_=E):
     """Names (as the kernel trace prints them) of the W13 and W2 kernels the
     library's tactic table picks for a shape (awq_moe_decode_table)."""
     f13, f2 = abi.awq_moe_decode_table(abi.make_dims(E_, H, I, rb), M, topk)
+    # single lanes read their weights non-temporally when the grid's waves
+    # fit the chip at once (256 CUs x 4 SIMDs x 8)
+    nt = "true" if (2 * I // 16) * M * topk * ((4 * (H // 32) + 63) // 64) <= 256 * 32 else "false"
     w13 = {abi.W13_PAIR: f"w13_swiglu_pair_kernel<{rb}, false>",
-           abi.W13_SINGLE: f"w13_swiglu_kernel<{rb}, false, 1>",
-           abi.W13_SINGLE_TWO_TILES: f"w13_swiglu_kernel<{rb}, false, 2>"}[f13]
-    if I <= 256:
-        cap = 64 // (I // 8)
-        choices = [v for v in (16, 8, 5, 4, 3, 2) if v <= cap]
-        spw = choices[0] if f2 == abi.W2_SEG_MOST else choices[1]
+           abi.W13_SINGLE: f"w13_swiglu_kernel<{rb}, false, 1, {nt}>",
+           abi.W13_SINGLE_TWO_TILES: f"w13_swiglu_kernel<{rb}, false, 2, {nt}>"}[f13]
+    choices = [v for v in (16, 8, 5, 4, 3, 2, 1) if v <= 64 // (I // 8)]  # slots per wave that fit
+    pick = 0 if f2 == abi.W2_SEG_MOST else 1
+    spw = choices[pick] if pick < len(choices) else 0
+    if spw and (topk + spw - 1) // spw <= 16:
         w2 = f"w2_reduce_seg_kernel<{rb}, {spw}, false>"
     else:
         w2 = f"w2_reduce_kernel<{rb}, 1, false>"

@@ -178,6 +178,12 @@ def test_decode_rank_shape(rb, M, mode):
     (5, 8192, 32, 3, 1),       # M = 1 but hidden 8192: pairs would need 2048 threads, single-lane W13
     (64, 2560, 160, 10, 8),    # a token whose ids are all invalid, next to valid ones
     (4096, 256, 32, 32, 8),    # 4096 experts, top-k 32, M = 8: 256 slots, expert offsets past 32 MB
+    (24, 2560, 320, 10, 8),    # W2: 40 lanes per slot, one slot per wave (inter 320)
+    (24, 2560, 320, 10, 1),
+    (12, 512, 512, 16, 3),     # W2: 64 lanes per slot, one per wave, 16 waves (its largest block)
+    (12, 512, 512, 17, 2),     # ... one slot more than 16 waves hold: the generic W2 kernel
+    (10, 256, 288, 4, 5),      # W2: 36 lanes per slot (nine groups), one per wave
+    (8, 512, 640, 6, 3),       # inter 640: 80 lanes per slot, the generic W2 kernel
 ])
 def test_decode_other_shapes(E, H, I, k, M):
     dims, bank, bi = bank_case(40 + I, E, H, I, 3)
@@ -454,6 +460,31 @@ def test_every_decode_form_against_oracle(rb, M):
         assert bits[(f13, abi.W2_SEG_MOST)] == bits[(f13, abi.W2_SEG_FEWER)]
     table = abi.awq_moe_decode_table(dims, M, k)
     assert run_decode(dims, bank, x, ids, w).view(np.uint16).tolist() == bits[table]
+
+
+@pytest.mark.parametrize("I", [64, 96, 160, 192, 256])
+def test_w2_fewer_slots_per_wave_lanes_past_the_segments(I):
+    """The W2 form with one step fewer slots per wave leaves lanes past the
+    wave's segments (at inter 64, 96 and 160 more than one segment's worth;
+    at 192 and 256 it is one slot per wave): their loads are clamped into
+    the tile, so the last expert's last tile reads nothing past its block.
+    The form equals the most-slots form bit for bit, with every slot on the
+    bank's last expert in one token, and is within the gate of the
+    oracle."""
+    E, H, k, M = 6, 512, 6, 2
+    dims, bank, bi = bank_case(700 + I, E, H, I, 3)
+    rng = inputs.call_rng(701, I)
+    x = inputs.activations(rng, M, H)
+    ids = inputs.ids_distinct(rng, M, k, E)
+    ids[0, :] = E - 1                      # every slot of token 0 on the last expert
+    w = inputs.router_weights(rng, M, k)
+    xd, idd, wd = to_dev(x), to_dev(ids), to_dev(w)
+    say("w2 fewer slots per wave", I)
+    most = abi.awq_moe_decode_forms(dims, bank, xd, idd, wd, abi.W13_SINGLE, abi.W2_SEG_MOST)
+    fewer = abi.awq_moe_decode_forms(dims, bank, xd, idd, wd, abi.W13_SINGLE, abi.W2_SEG_FEWER)
+    torch.cuda.synchronize()
+    assert f16_to_np(most).view(np.uint16).tolist() == f16_to_np(fewer).view(np.uint16).tolist()
+    check(f16_to_np(fewer), R.moe_stage(x, ids, w, E, bi.expert), f"w2 fewer slots per wave I={I}")
 
 
 @pytest.mark.parametrize("f13", ["single", "single_two_tiles"])

@@ -65,6 +65,7 @@ def check(got, want, what):
     (16, 1024, 128, 4, 384, 4),    # inter 128 in one launch: 4 act groups, 16 W13 tiles, 4 W2 column blocks
     (16, 512, 256, 4, 160, 3),     # inter 256: the two wide kernels (no single-launch form), W2 on 32-row items
     (16, 256, 192, 8, 2048, 4),    # inter 192 at 16,384 slots: the two wide kernels, W2 on the wide items
+    (24, 1024, 320, 10, 40, 3),    # inter 320 in the decode kernels: W2 with one slot per wave
 ])
 def test_prefill_shapes(E, H, I, k, M, rb):
     dims, bank, bi = bank_case(60 + I, E, H, I, rb)
