@@ -904,6 +904,131 @@ __global__ __launch_bounds__(1024) void w2_reduce_seg_kernel(const int32_t* __re
   }
 }
 
+// The slot-segment W2 for inter 544 to 1024 (at most 16 slots): the work
+// of w2_reduce_seg_kernel with one slot per wave, whose 64 lanes each take
+// group g = lane / 4 and, below G2, group g + 16 as well; the groups are
+// summed in the same ascending order, so the result equals the generic
+// kernel's. (A kernel of its own, so that the rank shape's kernel keeps its
+// code.)
+template <int RB, bool RES>
+__global__ __launch_bounds__(1024) void w2_reduce_seg2_kernel(const int32_t* __restrict__ topk_ids,
+                                                              const uint8_t* __restrict__ units_base,
+                                                              const uint16_t* __restrict__ act,
+                                                              const float* __restrict__ topk_w,
+                                                              uint16_t* __restrict__ out, uint32_t dims, int E,
+                                                              const uint16_t* __restrict__ resid) {
+  __shared__ __attribute__((aligned(16))) float red[16 * 32 * 16];  // [slot][g][16]
+  __shared__ __attribute__((aligned(16))) float ys[16 * 16];        // [rank][16]
+  __shared__ float wr[16];                                           // rank -> router weight
+  __shared__ int nvalid_s;
+  const int G2 = dims_G2(dims), LS = 4 * G2;  // lanes of a tile row (4 per group): 68 .. 128
+  const int H = 32 * dims_G(dims), I = 32 * G2, topk = dims_topk(dims);
+  const int T2 = H >> 4;
+  const int nt = (T2 & 7) ? (int)blockIdx.x : (int)((blockIdx.x & 7) * (T2 >> 3) + (blockIdx.x >> 3));
+  const int tok = blockIdx.y;
+  const int t = threadIdx.x, lane = t & 63;
+  const int slot = __builtin_amdgcn_readfirstlane(t >> 6);  // the wave's slot (< topk <= 16)
+  const int32_t* ids = topk_ids + tok * topk;
+  const ExpertGeometry geo = expert_geometry<RB>(dims);
+  const uint32_t expert_bytes = geo.expert_bytes, meta_delta = geo.w2_meta_delta;
+  uint16_t rv = 0;
+  if constexpr (RES) rv = resid[(uint64_t)tok * H + nt * 16 + (t & 15)];  // used by t < 16
+  const int e = ids[slot];
+  const float we = topk_w[tok * topk + slot];
+  const int rid = ids[lane < topk ? lane : topk - 1];  // ranking input: lane j holds slot j's id
+  // lane tl takes group g = tl / 4 and, below G2, group g2 = g + 16 (its
+  // lane index clamped into the tile row, so the unused loads stay inside)
+  const int tl = lane, g = tl >> 2, quad = tl & 3;
+  const int tl2 = min(tl + 64, LS - 1), g2 = tl2 >> 2;
+  const bool on2 = tl + 64 < LS;
+  const uint16_t* arow = act + (uint64_t)(tok * topk + slot) * I + 8 * quad;
+  const uint4 araw = *reinterpret_cast<const uint4*>(arow + 32 * g);
+  const uint4 araw2 = *reinterpret_cast<const uint4*>(arow + 32 * g2);
+  const bool live = e >= 0 && e < E;
+  const uint64_t eo = (uint64_t)(uint32_t)(live ? e : 0) * expert_bytes;
+  const uint8_t* units = units_base + eo + (uint64_t)nt * 256u * G2;
+  const uint8_t* recs = units_base + eo + meta_delta + (uint64_t)nt * 16u * G2 * RB;
+  const RawRecords<RB> rraw = load_records_raw<RB>(recs + (uint64_t)tl * 4u * RB);
+  const RawRecords<RB> rraw2 = load_records_raw<RB>(recs + (uint64_t)tl2 * 4u * RB);
+  uint4 w[4], wb[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) w[j] = load_unit16<true>(units + ((uint64_t)j * LS + tl) * 16u);
+#pragma unroll
+  for (int j = 0; j < 4; ++j) wb[j] = load_unit16<true>(units + ((uint64_t)j * LS + tl2) * 16u);
+  // Keep the ranking below the weight loads: it runs while they are in flight.
+  __builtin_amdgcn_sched_barrier(0);
+  // The slot's rank among the token's valid slots by (id, slot).
+  const bool vj = lane < topk && rid >= 0 && rid < E;
+  const int rank = (int)__popcll(__ballot(vj && (rid < e || (rid == e && lane < slot))));
+  const unsigned long long bv = __ballot(vj);
+  if (lane == 0) {
+    if (live) wr[rank] = we;
+    if (slot == 0) nvalid_s = (int)__popcll(bv);
+  }
+  // the quad's four 16-byte quarters of the group's activations, to every
+  // lane of the quad (the second group's after the first group's products,
+  // so that the two are not live together)
+  Act32 av;
+  av.px[0] = quad_bcast<0>(araw.x); av.px[1] = quad_bcast<0>(araw.y); av.px[2] = quad_bcast<0>(araw.z); av.px[3] = quad_bcast<0>(araw.w);
+  av.px[4] = quad_bcast<1>(araw.x); av.px[5] = quad_bcast<1>(araw.y); av.px[6] = quad_bcast<1>(araw.z); av.px[7] = quad_bcast<1>(araw.w);
+  av.px[8] = quad_bcast<2>(araw.x); av.px[9] = quad_bcast<2>(araw.y); av.px[10] = quad_bcast<2>(araw.z); av.px[11] = quad_bcast<2>(araw.w);
+  av.px[12] = quad_bcast<3>(araw.x); av.px[13] = quad_bcast<3>(araw.y); av.px[14] = quad_bcast<3>(araw.z); av.px[15] = quad_bcast<3>(araw.w);
+  float* rrow = red + (slot * 32) * 16 + 4 * quad;  // + 16 g: this lane's four columns in group g
+  if (live) {
+    float S, Cs;
+    group_sums(av, S, Cs);
+    const Records<RB> rec = decode_records<RB>(rraw);
+    const Magic mg = make_magic();
+    float4 part;
+    part.x = rec.s[0] * (unit_dot(w[0], av, mg) - fmaf(rec.z[0], S, Cs));
+    part.y = rec.s[1] * (unit_dot(w[1], av, mg) - fmaf(rec.z[1], S, Cs));
+    part.z = rec.s[2] * (unit_dot(w[2], av, mg) - fmaf(rec.z[2], S, Cs));
+    part.w = rec.s[3] * (unit_dot(w[3], av, mg) - fmaf(rec.z[3], S, Cs));
+    *reinterpret_cast<float4*>(rrow + 16 * g) = part;
+  }
+  Act32 av2;
+  av2.px[0] = quad_bcast<0>(araw2.x); av2.px[1] = quad_bcast<0>(araw2.y); av2.px[2] = quad_bcast<0>(araw2.z); av2.px[3] = quad_bcast<0>(araw2.w);
+  av2.px[4] = quad_bcast<1>(araw2.x); av2.px[5] = quad_bcast<1>(araw2.y); av2.px[6] = quad_bcast<1>(araw2.z); av2.px[7] = quad_bcast<1>(araw2.w);
+  av2.px[8] = quad_bcast<2>(araw2.x); av2.px[9] = quad_bcast<2>(araw2.y); av2.px[10] = quad_bcast<2>(araw2.z); av2.px[11] = quad_bcast<2>(araw2.w);
+  av2.px[12] = quad_bcast<3>(araw2.x); av2.px[13] = quad_bcast<3>(araw2.y); av2.px[14] = quad_bcast<3>(araw2.z); av2.px[15] = quad_bcast<3>(araw2.w);
+  if (live && on2) {
+    float S, Cs;
+    group_sums(av2, S, Cs);
+    const Records<RB> rec = decode_records<RB>(rraw2);
+    const Magic mg = make_magic();
+    float4 part;
+    part.x = rec.s[0] * (unit_dot(wb[0], av2, mg) - fmaf(rec.z[0], S, Cs));
+    part.y = rec.s[1] * (unit_dot(wb[1], av2, mg) - fmaf(rec.z[1], S, Cs));
+    part.z = rec.s[2] * (unit_dot(wb[2], av2, mg) - fmaf(rec.z[2], S, Cs));
+    part.w = rec.s[3] * (unit_dot(wb[3], av2, mg) - fmaf(rec.z[3], S, Cs));
+    *reinterpret_cast<float4*>(rrow + 16 * g2) = part;
+  }
+  // the writes above come from this wave only; wait for them (and keep the
+  // compiler from moving the reads below above them)
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  if (live && g == 0) {
+    float4 y = *reinterpret_cast<const float4*>(rrow);
+    for (int gg = 1; gg < G2; ++gg) {
+      const float4 v = *reinterpret_cast<const float4*>(rrow + 16 * gg);
+      y.x += v.x;
+      y.y += v.y;
+      y.z += v.z;
+      y.w += v.w;
+    }
+    *reinterpret_cast<float4*>(ys + rank * 16 + 4 * quad) = y;
+  }
+  __syncthreads();
+  if (t < 16) {
+    const int nv = nvalid_s;
+    float acc = 0.f;
+#pragma unroll 4
+    for (int rr = 0; rr < nv; ++rr) acc = fmaf(wr[rr], ys[rr * 16 + t], acc);
+    _Float16 v = (_Float16)acc;
+    if constexpr (RES) v = (_Float16)((float)__builtin_bit_cast(_Float16, rv) + (float)v);
+    out[(uint64_t)tok * H + nt * 16 + t] = __builtin_bit_cast(uint16_t, v);
+  }
+}
+
 // ---------------------------------------------------------------------------
 // dequantisation (diagnostic): one thread per unit, writes 32 fp32 values
 // ---------------------------------------------------------------------------
@@ -1058,9 +1183,10 @@ bool w13_form_valid(int form, int H, int I, int topk, int M) {
 }
 
 // The slot-segment kernel runs a form when the form's slots per wave fit the
-// inter size and the token's slots fit 16 waves; otherwise the generic
-// kernel (inter > 512, or one slot per wave with top-k above 16) serves the
-// shape with its one form.
+// inter size and the token's slots fit 16 waves (from inter 544 to 1024 the
+// most-slots form is its two-groups-per-lane variant); otherwise the
+// generic kernel (inter > 1024, or more than 16 waves) serves the shape with
+// its one form.
 static bool w2_seg_fits(int spw, int topk) { return spw > 0 && (topk + spw - 1) / spw <= 16; }
 
 bool w2_form_valid(int form, int H, int I, int topk, int M) {
@@ -1155,6 +1281,17 @@ static void launch_w2_seg(const StageArgs& a, const uint16_t* act, const float* 
                      a.bank + a.w2_off, act, topk_w, out, pack_dims(a.H, a.I, a.topk, a.M), a.E, resid);
 }
 
+// Inter 544 to 1024 with at most 16 slots: one slot per wave, two groups per lane.
+static bool w2_seg2_fits(int I, int topk) { return I > 512 && I <= 1024 && topk <= 16; }
+
+template <int RB, bool RES>
+static void launch_w2_seg2(const StageArgs& a, const uint16_t* act, const float* topk_w, uint16_t* out,
+                           const uint16_t* resid, hipStream_t stream) {
+  const dim3 grid(a.H / 16, a.M);
+  hipLaunchKernelGGL((w2_reduce_seg2_kernel<RB, RES>), grid, dim3(64 * a.topk), 0, stream, a.topk_ids,
+                     a.bank + a.w2_off, act, topk_w, out, pack_dims(a.H, a.I, a.topk, a.M), a.E, resid);
+}
+
 template <int RB, bool RES>
 static void launch_w2_seg_rb(const StageArgs& a, const uint16_t* act, const float* topk_w, uint16_t* out,
                              const uint16_t* resid, int spw, hipStream_t stream) {
@@ -1172,13 +1309,18 @@ template <bool RES>
 static hipError_t launch_w2_res(const StageArgs& a, const uint16_t* act, const float* topk_w, uint16_t* out,
                                 const uint16_t* resid, int form, hipStream_t stream) {
   const int spw = w2_spw(form, a.I);
-  if (w2_seg_fits(spw, a.topk)) {
-    // the slot-segment kernel derives the expert geometry from the shape word
+  const bool seg2 = spw == 0 && form == kW2SegMost && w2_seg2_fits(a.I, a.topk);
+  if (w2_seg_fits(spw, a.topk) || seg2) {
+    // the slot-segment kernels derive the expert geometry from the shape word
     const ExpertGeometry g = a.RB == 4 ? expert_geometry<4>(pack_dims(a.H, a.I, a.topk, a.M))
                                        : expert_geometry<3>(pack_dims(a.H, a.I, a.topk, a.M));
     if (g.expert_bytes != a.expert_bytes || g.w2_off != a.w2_off || g.w2_meta_delta != a.w2_meta_off - a.w2_off)
       return hipErrorInvalidValue;
-    if (a.RB == 4)
+    if (seg2 && a.RB == 4)
+      launch_w2_seg2<4, RES>(a, act, topk_w, out, resid, stream);
+    else if (seg2)
+      launch_w2_seg2<3, RES>(a, act, topk_w, out, resid, stream);
+    else if (a.RB == 4)
       launch_w2_seg_rb<4, RES>(a, act, topk_w, out, resid, spw, stream);
     else
       launch_w2_seg_rb<3, RES>(a, act, topk_w, out, resid, spw, stream);

@@ -183,7 +183,10 @@ def test_decode_rank_shape(rb, M, mode):
     (12, 512, 512, 16, 3),     # W2: 64 lanes per slot, one per wave, 16 waves (its largest block)
     (12, 512, 512, 17, 2),     # ... one slot more than 16 waves hold: the generic W2 kernel
     (10, 256, 288, 4, 5),      # W2: 36 lanes per slot (nine groups), one per wave
-    (8, 512, 640, 6, 3),       # inter 640: 80 lanes per slot, the generic W2 kernel
+    (8, 512, 640, 6, 3),       # inter 640: one slot per wave, two groups on the first 16 lanes
+    (6, 256, 544, 5, 3),       # inter 544: 17 groups, a second group on 4 lanes only
+    (8, 512, 1024, 16, 2),     # inter 1024: two groups on every lane, 16 waves
+    (8, 512, 1024, 17, 2),     # ... one slot more: the generic W2 kernel
 ])
 def test_decode_other_shapes(E, H, I, k, M):
     dims, bank, bi = bank_case(40 + I, E, H, I, 3)

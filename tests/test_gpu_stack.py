@@ -181,6 +181,7 @@ def test_stack_teacher_forced_four_layers():
     (8, 512, 2048, 4, 2, 3),       # the generic W2 kernel (inter > 256) with the residual
     (12, 4096, 64, 2, 1, 4),       # lane pairs at their largest block (16 waves)
     (12, 1024, 320, 6, 3, 3),      # W2 with one slot per wave (inter 320) with the residual
+    (8, 512, 768, 4, 2, 4),        # W2 with two groups per lane (inter 768) with the residual
 ])
 def test_decode_rmsnorm_residual_against_oracle_and_separate_calls(E, H, I, k, M, rb):
     """awq_moe_decode_rmsnorm_residual(r): the update r_next - r is within
