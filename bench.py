@@ -460,6 +460,8 @@ def stage_kernel_names(abi, M, rb, H=H, I=I, topk=K_TOP, E_=E):
     spw = choices[pick] if pick < len(choices) else 0
     if spw and (topk + spw - 1) // spw <= 16:
         w2 = f"w2_reduce_seg_kernel<{rb}, {spw}, false>"
+    elif f2 == abi.W2_SEG_MOST and 512 < I <= 1024 and topk <= 16:
+        w2 = f"w2_reduce_seg2_kernel<{rb}, false>"
     else:
         w2 = f"w2_reduce_kernel<{rb}, 1, false>"
     return w13, w2
