@@ -195,11 +195,12 @@ int awq_moe_decode_noalloc(const awq_moe_dims* dims, const void* bank, uint64_t 
  * Forms: W13 + SwiGLU 1 = lane pairs (each group split over two lanes),
  * 2 = single lanes (one 16-column tile per workgroup), 3 = single lanes,
  * two tiles per workgroup; W2 + reduction 1 = slot segments with the most
- * slots per wave, 2 = one instantiated step fewer (more waves). Form 1 is
- * the segment kernel up to inter 512 (one slot per wave from inter 288),
- * two groups per lane from inter 544 to 1024 (top-k <= 16 there and from
- * inter 288), and beyond that the generic kernel; form 2 exists where one
- * step fewer still fits 16 waves. 0 = the table's choice. The pages' own tactic table (PR #520, Results: tile
+ * slots per wave, 2 = one instantiated step fewer (more waves). Form 1
+ * runs the slot-segment kernel (one slot per wave from inter 288, which
+ * needs top-k <= 16), from inter 544 to 1024 its two-groups-per-lane
+ * variant (top-k <= 16), and otherwise a generic kernel; form 2 exists
+ * where one step fewer slots per wave still fits 16 waves. 0 = the table's
+ * choice. The pages' own tactic table (PR #520, Results: tile
  * tactics and the small-shape autotune) is the model. */
 #define AWQ_MOE_W13_TABLE 0
 #define AWQ_MOE_W13_PAIR 1
