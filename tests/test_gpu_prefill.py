@@ -65,6 +65,8 @@ def check(got, want, what):
     (16, 1024, 128, 4, 384, 4),    # inter 128 in one launch: 4 act groups, 16 W13 tiles, 4 W2 column blocks
     (16, 512, 256, 4, 160, 3),     # inter 256: the two wide kernels (no single-launch form), W2 on 32-row items
     (16, 256, 192, 8, 2048, 4),    # inter 192 at 16,384 slots: the two wide kernels, W2 on the wide items
+    (24, 1024, 320, 6, 200, 4),    # inter 320 on the two wide kernels: two W13 column blocks, 10 W2 K groups
+    (12, 512, 352, 4, 300, 3),     # inter 352: 22 W13 tiles (a 2-tile second block), 11 W2 K groups
     (24, 1024, 320, 10, 40, 3),    # inter 320 in the decode kernels: W2 with one slot per wave
 ])
 def test_prefill_shapes(E, H, I, k, M, rb):
