@@ -252,16 +252,17 @@ def test_device_calls_reject_bad_arguments_before_launch():
 def test_tactic_table_forms_are_valid_for_every_admitted_token_count():
     """The table answers for every M and record size, and only with forms
     that fit the shape (lane pairs need hidden <= 4096; the generic W2
-    kernel for inter > 256 has one form)."""
+    kernel, past inter 1024, has one form)."""
     for dims in (abi.make_dims(512, 2560, 160, 3), abi.make_dims(512, 2560, 160, 4), abi.make_dims(4, 8192, 32, 3),
-                 abi.make_dims(8, 512, 2048, 3), abi.make_dims(16, 96, 64, 4)):
+                 abi.make_dims(8, 512, 2048, 3), abi.make_dims(16, 96, 64, 4), abi.make_dims(64, 2560, 320, 3),
+                 abi.make_dims(64, 2560, 640, 4)):
         for M in range(1, 9):
             f13, f2 = abi.awq_moe_decode_table(dims, M, 10)
             assert f13 in (abi.W13_PAIR, abi.W13_SINGLE, abi.W13_SINGLE_TWO_TILES)
             assert f2 in (abi.W2_SEG_MOST, abi.W2_SEG_FEWER)
             if dims.hidden > 4096:
                 assert f13 == abi.W13_SINGLE
-            if dims.inter > 256:
+            if dims.inter > 1024:
                 assert f2 == abi.W2_SEG_MOST
 
 

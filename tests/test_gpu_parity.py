@@ -208,7 +208,7 @@ def test_decode_largest_hidden_and_inter_together():
     """Hidden 8192 with inter 2048, the admitted maxima together, top-k 32
     over 4 experts (each token routes to every expert several times), M = 2:
     the single-lane W13 kernel at its 16 waves and the W2 kernel for
-    inter > 256 at their largest strides."""
+    inter > 1024 at their largest strides."""
     E, H, I, k, M = 4, 8192, 2048, 32, 2
     dims, bank, bi = bank_case(90, E, H, I, 3)
     rng = inputs.call_rng(91, 0)

@@ -178,7 +178,7 @@ def test_stack_teacher_forced_four_layers():
     (64, 2560, 160, 10, 8, 4),     # single-lane W13 with the norm
     (64, 2560, 160, 10, 3, 3),
     (6, 8192, 32, 3, 2, 3),        # hidden 8192: 16 waves of squares
-    (8, 512, 2048, 4, 2, 3),       # the generic W2 kernel (inter > 256) with the residual
+    (8, 512, 2048, 4, 2, 3),       # the generic W2 kernel (inter > 1024) with the residual
     (12, 4096, 64, 2, 1, 4),       # lane pairs at their largest block (16 waves)
     (12, 1024, 320, 6, 3, 3),      # W2 with one slot per wave (inter 320) with the residual
     (8, 512, 768, 4, 2, 4),        # W2 with two groups per lane (inter 768) with the residual

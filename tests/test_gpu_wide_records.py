@@ -126,7 +126,7 @@ def test_decode_wide_records_three_and_four_byte_identical(family):
 
 @pytest.mark.parametrize("M", [1, 2])
 def test_decode_wide_records_inter_2048(M):
-    """The generic W2 kernel (inter > 256: 64 K-groups, slots in passes) and
+    """The generic W2 kernel (inter > 1024: 64 K-groups, slots in passes) and
     the single-lane W13 kernel with wide records."""
     E, Hs, Is, k = 8, 512, 2048, 4
     big = (5,)
