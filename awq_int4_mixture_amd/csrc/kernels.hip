@@ -205,8 +205,12 @@ __device__ __forceinline__ float unit_dot(const uint4& w, const Act32& a, const 
   return acc;
 }
 
+// silu(g) * u = g / (1 + e^-g) * u. The division is the hardware reciprocal
+// (about 1 ulp of fp32, far below the fp16 rounding of the result): it is
+// the last step before each workgroup's store, and the IEEE division there
+// measured 0.02-0.05 us per W13 launch.
 __device__ __forceinline__ float silu_mul(float g, float u) {
-  return g / (1.0f + __expf(-g)) * u;
+  return g * __builtin_amdgcn_rcpf(1.0f + __expf(-g)) * u;
 }
 
 // ---------------------------------------------------------------------------
