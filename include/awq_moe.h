@@ -273,7 +273,9 @@ int awq_moe_router_topk(const float* logits, int32_t M, int32_t num_experts, int
  *   r_next = fp16(r + out)     (fp32 add, one rounding)
  * Two launches, like awq_moe_decode: the W13 workgroups take their dot
  * products on r and scale each column's fp32 sum by 1/sqrt(mean(r^2) + eps)
- * (the norm is a per-row scale; x is never rounded to fp16, unlike the x of
+ * (formed with the hardware reciprocal and reciprocal square root, within
+ * about 2 ulp of fp32; the norm is a per-row scale; x is never rounded to
+ * fp16, unlike the x of
  * awq_moe_residual_rmsnorm), computing the mean from the row they load
  * anyway; the W2 workgroups add the residual as they store. So no separate
  * norm or residual launch sits between two layers.
@@ -290,6 +292,10 @@ int awq_moe_decode_rmsnorm_residual(const awq_moe_dims* dims, const void* bank, 
  * norm). Per row t of M = 1..8 rows, in fp32:
  *   r_next[t] = fp16_rne(r[t] + delta[t])      (delta NULL: r_next[t] = r[t])
  *   x[t]      = fp16_rne(r_next[t] / sqrt(mean(r_next[t]^2) + eps))
+ * where 1/sqrt(...) is formed with the hardware reciprocal and reciprocal
+ * square root (within about 2 ulp of fp32), so an x value may sit one fp16
+ * ulp from the correctly rounded quotient; awq_moe_router_gemv forms its x
+ * with the same formula, bit for bit.
  * r, delta, r_next, x: device fp16 [M][hidden], 16-byte aligned; hidden a
  * multiple of 8 in [8, AWQ_MOE_MAX_HIDDEN]; r_next and x must not overlap r,
  * delta or each other. eps in (0, 1]. One launch. */
