@@ -2,6 +2,7 @@
 // (fail closed before any write or launch), the bank packer, layout and
 // workspace queries, and the kernel launch sequence of the decode stage.
 
+#include <cfloat>
 #include <hip/hip_runtime.h>
 
 #include <atomic>
@@ -160,7 +161,9 @@ int check_residual_args(const uint16_t* r, const uint16_t* delta, int32_t M, int
   if (M < 1 || M > AWQ_MOE_MAX_TOKENS) return fail(AWQ_MOE_EINVAL, "M %d outside [1, %d]", M, AWQ_MOE_MAX_TOKENS);
   if (hidden < 8 || hidden > AWQ_MOE_MAX_HIDDEN || hidden % 8)
     return fail(AWQ_MOE_EINVAL, "hidden %d: a multiple of 8 in [8, %d]", hidden, AWQ_MOE_MAX_HIDDEN);
-  if (!(eps > 0.f) || eps > 1.f) return fail(AWQ_MOE_EINVAL, "eps must be in (0, 1]");
+  // a normal float: 1/sqrt(mean + eps) is formed with the hardware
+  // reciprocal square root, whose argument is then never subnormal
+  if (!(eps >= FLT_MIN) || eps > 1.f) return fail(AWQ_MOE_EINVAL, "eps must be a normal float in [2^-126, 1]");
   if (!r || !r_next || !x || !aligned(r, 16) || !aligned(r_next, 16) || !aligned(x, 16) ||
       (delta && !aligned(delta, 16)))
     return fail(AWQ_MOE_EINVAL, "row pointer null or not 16-byte aligned");
@@ -525,7 +528,9 @@ int awq_moe_decode_rmsnorm_residual(const awq_moe_dims* dims, const void* bank, 
                                     uint64_t workspace_bytes, void* stream) {
   int rc = check_stage(dims, bank, bank_bytes, M, topk, workspace, workspace_bytes);
   if (rc) return rc;
-  if (!(eps > 0.f) || eps > 1.f) return fail(AWQ_MOE_EINVAL, "eps must be in (0, 1]");
+  // a normal float: 1/sqrt(mean + eps) is formed with the hardware
+  // reciprocal square root, whose argument is then never subnormal
+  if (!(eps >= FLT_MIN) || eps > 1.f) return fail(AWQ_MOE_EINVAL, "eps must be a normal float in [2^-126, 1]");
   if (!r || !r_next || !aligned(r, 16) || !aligned(r_next, 16))
     return fail(AWQ_MOE_EINVAL, "r or r_next null or not 16-byte aligned");
   const uint64_t nb = (uint64_t)M * dims->hidden * 2;

@@ -280,7 +280,7 @@ int awq_moe_router_topk(const float* logits, int32_t M, int32_t num_experts, int
  * anyway; the W2 workgroups add the residual as they store. So no separate
  * norm or residual launch sits between two layers.
  *   r, r_next: device fp16 [M][hidden], 16-byte aligned, not overlapping;
- *   eps in (0, 1]; the other arguments, the workspace and its contents
+ *   eps a normal float in [2^-126, 1]; the other arguments, the workspace and its contents
  *   (status word, act) as for awq_moe_decode. */
 int awq_moe_decode_rmsnorm_residual(const awq_moe_dims* dims, const void* bank, uint64_t bank_bytes,
                                     const uint16_t* r, float eps, const int32_t* topk_ids, const float* topk_w,
@@ -298,7 +298,8 @@ int awq_moe_decode_rmsnorm_residual(const awq_moe_dims* dims, const void* bank, 
  * with the same formula, bit for bit.
  * r, delta, r_next, x: device fp16 [M][hidden], 16-byte aligned; hidden a
  * multiple of 8 in [8, AWQ_MOE_MAX_HIDDEN]; r_next and x must not overlap r,
- * delta or each other. eps in (0, 1]. One launch. */
+ * delta or each other. eps a normal float in [2^-126, 1] (AWQ_MOE_EINVAL
+ * otherwise). One launch. */
 int awq_moe_residual_rmsnorm(const uint16_t* r, const uint16_t* delta, int32_t M, int32_t hidden,
                              float eps, uint16_t* r_next, uint16_t* x, void* stream);
 

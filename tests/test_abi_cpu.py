@@ -172,6 +172,7 @@ def test_device_calls_reject_bad_arguments_before_launch():
         (lambda: lib.awq_moe_router_topk(None, 1, 512, 10, p, p, None), abi.EINVAL),
         (lambda: lib.awq_moe_router_topk(mis, 1, 512, 10, p, p, None), abi.EINVAL),
         (lambda: lib.awq_moe_residual_rmsnorm(p, None, 1, 2560, 0.0, q1, q2, None), abi.EINVAL),
+        (lambda: lib.awq_moe_residual_rmsnorm(p, None, 1, 2560, 1e-40, q1, q2, None), abi.EINVAL),  # subnormal eps
         (lambda: lib.awq_moe_residual_rmsnorm(p, None, 9, 256, 1e-6, q1, q2, None), abi.EINVAL),
         (lambda: lib.awq_moe_residual_rmsnorm(p, None, 1, 256, 1e-6, p, q2, None), abi.EINVAL),
         (lambda: lib.awq_moe_residual_rmsnorm(p, q2, 1, 256, 1e-6, q1, q2, None), abi.EINVAL),
@@ -209,6 +210,8 @@ def test_device_calls_reject_bad_arguments_before_launch():
                                     1 << 40, None), abi.ENOSPC),
         # the fused stacked layer: the stage's checks plus eps and the two rows
         (lambda: lib.awq_moe_decode_rmsnorm_residual(ctypes.byref(d), p, bb, q1, 0.0, p, p, 1, 10, q2, p, ws_need,
+                                                     None), abi.EINVAL),
+        (lambda: lib.awq_moe_decode_rmsnorm_residual(ctypes.byref(d), p, bb, q1, 1e-40, p, p, 1, 10, q2, p, ws_need,
                                                      None), abi.EINVAL),
         (lambda: lib.awq_moe_decode_rmsnorm_residual(ctypes.byref(d), p, bb, q1, 1e-6, p, p, 1, 10, q1, p, ws_need,
                                                      None), abi.EINVAL),
