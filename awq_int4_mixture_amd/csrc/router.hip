@@ -121,6 +121,15 @@ __device__ __forceinline__ ResRow residual_load(const uint16_t* __restrict__ r, 
   return rr;
 }
 
+// 1/sqrt(tot / H + eps) with the hardware reciprocal and reciprocal square
+// root (about 1 ulp each): the step sits between the row's last barrier and
+// its first use, where an IEEE division and square root lengthen every
+// workgroup's critical path. Both kernels that normalise a row use it, so
+// their x agree bit for bit.
+__device__ __forceinline__ float inv_rms_row(float tot, int H, float eps) {
+  return __builtin_amdgcn_rsqf(fmaf(tot, __builtin_amdgcn_rcpf((float)H), eps));
+}
+
 __device__ void residual_finish(const ResRow& rr, bool has_delta, int H, float eps, uint16_t* __restrict__ r_next,
                                 uint16_t* __restrict__ x) {
   __shared__ float part[16];
@@ -142,7 +151,7 @@ __device__ void residual_finish(const ResRow& rr, bool has_delta, int H, float e
   __syncthreads();
   float tot = 0.f;
   for (int i = 0; i < (int)(blockDim.x >> 6); ++i) tot += part[i];
-  const float inv = 1.0f / sqrtf(tot / (float)H + eps);
+  const float inv = inv_rms_row(tot, H, eps);
   if (on) {
     h8_t o;
 #pragma unroll
@@ -284,7 +293,7 @@ __global__ __launch_bounds__(1024) void router_gemv_kernel(const uint16_t* __res
   __syncthreads();
   float tot = 0.f;
   for (int i = 0; i < nwaves; ++i) tot += part[i];
-  const float inv = 1.0f / sqrtf(tot / (float)H + eps);
+  const float inv = inv_rms_row(tot, H, eps);
   h8_t xo;
 #pragma unroll
   for (int e = 0; e < 8; ++e) xo[e] = (_Float16)((float)a[e] * inv);
