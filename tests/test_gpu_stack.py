@@ -265,3 +265,34 @@ def test_stack_fused_layers_teacher_forced():
         say("fused stack layer", layer, e)
         assert ok, (layer, e)
         r = rn
+
+
+@pytest.mark.parametrize("M", [1, 8])   # W13 lane pairs / single lanes with the norm
+def test_norm_zero_row_at_the_smallest_eps(M):
+    """eps = 2^-126, the smallest the entry points admit, on a row of zeros:
+    1/rms comes from the hardware reciprocal square root of eps itself, so
+    the row's update is exactly zero (no inf or NaN); the other rows match
+    the oracle with the same eps, and awq_moe_residual_rmsnorm gives x = 0
+    for the zero row."""
+    from tests.gpu_helpers import bank_case
+    E, H, I, k, rb = 64, 2560, 160, 10, 3
+    eps = 2.0 ** -126
+    dims, bank, bi = bank_case(530 + M, E, H, I, rb)
+    rng = inputs.call_rng(531, M)
+    r = (rng.standard_normal((M, H)) * 3).astype(np.float16)
+    r[0] = 0
+    ids = inputs.ids_shared_pool(rng, M, k, E)
+    w = inputs.router_weights(rng, M, k)
+    say("zero row, eps 2^-126", M)
+    rn = abi.awq_moe_decode_rmsnorm_residual(dims, bank, to_dev(r), to_dev(ids), to_dev(w), eps=eps)
+    r2, x = abi.awq_moe_residual_rmsnorm(to_dev(r), eps=eps)
+    torch.cuda.synchronize()
+    got = f16_to_np(rn)
+    assert np.all(np.isfinite(got))
+    assert not got[0].any()
+    assert not f16_to_np(x)[0].any() and np.all(np.isfinite(f16_to_np(x)))
+    if M > 1:
+        upd = got[1:].astype(np.float64) - r[1:].astype(np.float64)
+        want = R.moe_stage(R.rms_norm(r[1:], eps=eps), ids[1:], w[1:], E, bi.expert)
+        ok, e = R.within_gate(upd, want)
+        assert ok, e
